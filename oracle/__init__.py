@@ -1,0 +1,28 @@
+"""CPU oracle for the SS2D path: TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, fp64 implementations of what the GPU path computes, written from
+the method's definitions so that a reader can check them against the pages by
+eye.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import anything from here; the product package never does,
+and the two share no code.
+
+Functions (see ``oracle/ss2d_oracle.py`` for the citations):
+  cross_scan, cross_merge        exact index permutations (numpy)
+  ss_fwd, ss_bwd                 the selective scan and its exact gradient (C, fp64)
+  ss2d_fwd, ss2d_bwd             cross-scan -> selective scan -> cross-merge (+ gate)
+
+Pins: every function here is checked by ``tests/test_oracle_*.py`` against
+closed forms, invariants, a brute-force semiseparable-matrix formulation and
+finite differences; none of them is "parity unpinned".
+"""
+from .ss2d_oracle import (  # noqa: F401
+    build_oracle_lib,
+    cross_merge,
+    cross_scan,
+    perm_indices,
+    softplus,
+    ss2d_bwd,
+    ss2d_fwd,
+    ss_bwd,
+    ss_fwd,
+)
