@@ -1,0 +1,236 @@
+/*
+ * ss2d.h -- C ABI of the SS2D library (cross-scan -> selective scan S6 -> cross-merge)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are defined on these pages:
+ *   [VMamba]  "VMamba: Visual State Space Model" (Chinese translation, blog.csdn.net):
+ *             section "2-D selective scan (SS2D) for visual data" and the Fig. 2 caption --
+ *             SS2D unfolds the map along four routes (cross-scan), runs one S6 scan per
+ *             route, and merges the results back onto the map (cross-merge).
+ *   [S6]      "Vision Mamba structure and principle" (freeymw.com), section 1 (the merge
+ *             adds the routes) and section 2: `selective_scan_fn`, `SelectiveScanFn`
+ *             (forward/backward interface) and `selective_scan_ref` (the semantics).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  * Pointers are DEVICE pointers to dense, contiguous buffers (last index fastest),
+ *    owned by the caller.  The library never allocates, frees or synchronises device
+ *    memory; scratch space comes in through an explicit workspace argument whose size
+ *    is given by the matching *_workspace_bytes query.
+ *  * Every call enqueues its kernels on `stream` and returns; SS2D_OK means "enqueued".
+ *    Device-side faults surface at the caller's next synchronisation.
+ *  * Arguments are validated before anything is launched; on an error nothing is
+ *    enqueued and no output is touched.
+ *  * I/O tensors use `dtype` (SS2D_DTYPE_F32 or SS2D_DTYPE_BF16).  Parameters A, D,
+ *    delta_bias and the gradients dA, dD, ddelta_bias are always fp32.  The scan state
+ *    and all accumulation are fp32.
+ *  * Sizes of 0 (empty batch, no channels, empty sequence) are valid and do nothing
+ *    except write zeros to gradients that are sums over an empty set.
+ *  * The library keeps no global state; calls on different streams may run
+ *    concurrently as long as their workspaces do not overlap.
+ */
+#ifndef SS2D_H_
+#define SS2D_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SS2D_ABI_VERSION 1
+
+/* Status codes returned by every entry point. */
+enum {
+  SS2D_OK = 0,
+  SS2D_ERR_INVALID_ARGUMENT = 1, /* null required pointer, negative size, dim % ngroups != 0,
+                                    workspace missing or too small, misaligned pointer */
+  SS2D_ERR_UNSUPPORTED = 2,      /* dtype not F32/BF16, dstate outside [1, 64] */
+  SS2D_ERR_HIP = 3               /* a kernel launch reported an error */
+};
+
+/* I/O element types. */
+enum { SS2D_DTYPE_F32 = 0, SS2D_DTYPE_BF16 = 1 };
+
+/* Version of this ABI (SS2D_ABI_VERSION of the build). */
+int ss2d_abi_version(void);
+
+/* Static, never-freed description of a status code. */
+const char* ss2d_status_string(int status);
+
+/* ---------------------------------------------------------------------------------
+ * Cross-scan [VMamba, Fig. 2 caption]: unfold a map along the four routes.
+ *   x  : (batch, channels, height, width)           dtype
+ *   xs : (batch, 4, channels, L), L = height*width   dtype
+ * Route k visits pixel (h, w) at step pi_k(h, w):
+ *   pi_0 = h*width + w      (row-major)        pi_2 = L-1-pi_0
+ *   pi_1 = w*height + h     (column-major)     pi_3 = L-1-pi_1
+ * xs[b, k, c, pi_k(h, w)] = x[b, c, h, w]: a bit-exact copy.
+ * ------------------------------------------------------------------------------- */
+int ss2d_cross_scan(const void* x, void* xs, int64_t batch, int64_t channels, int64_t height,
+                    int64_t width, int dtype, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * Cross-merge [S6 page, section 1: the four routes are added and merged back]:
+ *   ys : (batch, 4, channels, L)   dtype
+ *   y  : (batch, channels, height, width)  dtype
+ * y[b, c, h, w] = ((ys0[pi_0] + ys1[pi_1]) + ys2[pi_2]) + ys3[pi_3], summed in fp32 in
+ * that order and rounded once to dtype (round to nearest even).
+ * ------------------------------------------------------------------------------- */
+int ss2d_cross_merge(const void* ys, void* y, int64_t batch, int64_t channels, int64_t height,
+                     int64_t width, int dtype, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * Selective scan S6 [S6 page, section 2, `selective_scan_ref`]:
+ *   delta_t = softplus(delta_raw_t + delta_bias[d])   (bias/softplus optional)
+ *   h_t[n]  = exp(delta_t*A[d, n]) * h_{t-1}[n] + delta_t * B[b, g, n, t] * u_t,  h_{-1} = 0
+ *   y_t     = sum_n C[b, g, n, t] * h_t[n] + D[d]*u_t,  out_t = y_t * silu(z_t) (z optional)
+ * with channel d reading group g = d / (dim / ngroups).
+ * Layouts:  u, delta, z, out : (batch, dim, seqlen)          dtype
+ *           A                : (dim, dstate)                  fp32
+ *           Bm, Cm           : (batch, ngroups, dstate, seqlen) dtype
+ *           Dskip, delta_bias: (dim)                           fp32, may be NULL
+ *           last_state       : (batch, dim, dstate)            fp32, may be NULL
+ * The workspace (optional for the forward) receives the scan state at every
+ * checkpoint (every 64 steps) so that the backward need not recompute it, and lets the
+ * forward split long sequences across wavefronts when there are few rows.
+ * ------------------------------------------------------------------------------- */
+size_t selective_scan_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                      int64_t ngroups);
+
+typedef struct ss_fwd_args {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;      /* may be NULL */
+  const void* z;           /* may be NULL */
+  const float* delta_bias; /* may be NULL */
+  void* out;
+  float* last_state;       /* may be NULL */
+  void* workspace;         /* may be NULL; else >= selective_scan_workspace_bytes(...) */
+  size_t workspace_bytes;
+  int64_t batch, dim, dstate, seqlen, ngroups;
+  int dtype;
+  int delta_softplus;
+} ss_fwd_args;
+
+int selective_scan_fwd(const ss_fwd_args* args, hipStream_t stream);
+
+/* Backward of selective_scan_fwd [S6 page, section 2, `SelectiveScanFn.backward`]:
+ * given dout = dLoss/dout, writes
+ *   du, ddelta, dz : (batch, dim, seqlen)  dtype   (ddelta is w.r.t. the RAW delta,
+ *                                                   before bias and softplus)
+ *   dBm, dCm       : (batch, ngroups, dstate, seqlen) dtype (fp32 sums, rounded once)
+ *   dA             : (dim, dstate) fp32;  dDskip, ddelta_bias : (dim) fp32
+ * All outputs are overwritten, never accumulated into.  dz is written iff z != NULL,
+ * dDskip iff Dskip != NULL, ddelta_bias iff delta_bias != NULL.
+ * The workspace is required (>= selective_scan_workspace_bytes(...)).  If
+ * workspace_has_states != 0 it must hold what selective_scan_fwd wrote into it for the
+ * same inputs; otherwise the backward recomputes the states itself. */
+typedef struct ss_bwd_args {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;
+  const void* z;
+  const float* delta_bias;
+  const void* dout;
+  void* du;
+  void* ddelta;
+  float* dA;
+  void* dBm;
+  void* dCm;
+  float* dDskip;
+  void* dz;
+  float* ddelta_bias;
+  void* workspace;
+  size_t workspace_bytes;
+  int workspace_has_states;
+  int64_t batch, dim, dstate, seqlen, ngroups;
+  int dtype;
+  int delta_softplus;
+} ss_bwd_args;
+
+int selective_scan_bwd(const ss_bwd_args* args, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * Fused SS2D forward [VMamba, SS2D section]: equivalent, up to fp32 rounding order, to
+ *   cross_merge(selective_scan_fwd(cross_scan(x), delta, A, B, C, D, delta_bias,
+ *               softplus, ngroups = 4))  then  * silu(z)  per pixel (z optional)
+ * Layouts:  x, z, out  : (batch, dim, height, width)      dtype   (grid)
+ *           delta      : (batch, 4, dim, L)               dtype   (route k in its own order)
+ *           Bm, Cm     : (batch, 4, dstate, L)            dtype   (shared by the dim channels
+ *                                                                  of route k)
+ *           A          : (4, dim, dstate) fp32;  Dskip, delta_bias : (4, dim) fp32 (may be NULL)
+ * The gate is applied once per pixel after the merge, which equals gating every route
+ * with the cross-scanned z and merging (silu(z) is the same factor on all four).
+ * The workspace is required (>= ss2d_workspace_bytes(...)).
+ * ------------------------------------------------------------------------------- */
+size_t ss2d_workspace_bytes(int64_t batch, int64_t dim, int64_t height, int64_t width,
+                            int64_t dstate, int dtype);
+
+typedef struct ss2d_fwd_args {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;      /* may be NULL */
+  const float* delta_bias; /* may be NULL */
+  const void* z;           /* may be NULL */
+  void* out;
+  void* workspace;
+  size_t workspace_bytes;
+  int64_t batch, dim, height, width, dstate;
+  int dtype;
+  int delta_softplus;
+} ss2d_fwd_args;
+
+int ss2d_fwd(const ss2d_fwd_args* args, hipStream_t stream);
+
+/* Backward of ss2d_fwd: given dout (batch, dim, height, width), writes
+ *   dx, dz     : (batch, dim, height, width)  dtype  (dz iff z != NULL)
+ *   ddelta     : (batch, 4, dim, L) dtype (w.r.t. the raw delta);
+ *   dBm, dCm   : (batch, 4, dstate, L) dtype;
+ *   dA         : (4, dim, dstate) fp32;  dDskip, ddelta_bias : (4, dim) fp32 (iff given)
+ * Everything is overwritten.  The forward states are recomputed inside (the workspace,
+ * >= ss2d_workspace_bytes(...), holds them). */
+typedef struct ss2d_bwd_args {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;
+  const float* delta_bias;
+  const void* z;
+  const void* dout;
+  void* dx;
+  void* ddelta;
+  float* dA;
+  void* dBm;
+  void* dCm;
+  float* dDskip;
+  float* ddelta_bias;
+  void* dz;
+  void* workspace;
+  size_t workspace_bytes;
+  int64_t batch, dim, height, width, dstate;
+  int dtype;
+  int delta_softplus;
+} ss2d_bwd_args;
+
+int ss2d_bwd(const ss2d_bwd_args* args, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS2D_H_ */

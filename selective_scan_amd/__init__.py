@@ -1,0 +1,18 @@
+"""SS2D on AMD Instinct MI355X: cross-scan -> selective scan (S6) -> cross-merge.
+
+The computation runs in hand-written HIP kernels for gfx950 behind the C ABI in
+include/ss2d.h (libss2d.so, built in-tree by __graft_entry__.build()).  This package
+is the thin Python binding over that ABI; its functions carry the C entry points' names.
+"""
+from ._binding import (  # noqa: F401
+    SS2DError,
+    lib,
+    selective_scan_bwd,
+    selective_scan_fwd,
+    selective_scan_workspace_bytes,
+    ss2d_bwd,
+    ss2d_cross_merge,
+    ss2d_cross_scan,
+    ss2d_fwd,
+    ss2d_workspace_bytes,
+)

@@ -1,0 +1,279 @@
+"""ctypes binding of libss2d.so (include/ss2d.h).  Argument marshalling only.
+
+Each function here has the name of the C entry point it calls, takes torch tensors that
+already live on a ROCm device, allocates the outputs (and, when not given, the workspace)
+with torch, and enqueues the library call on torch's current stream of that device.  Every
+step of the computation runs in the library's HIP kernels; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libss2d.so")
+
+SS2D_OK, SS2D_ERR_INVALID_ARGUMENT, SS2D_ERR_UNSUPPORTED, SS2D_ERR_HIP = 0, 1, 2, 3
+DTYPE_F32, DTYPE_BF16 = 0, 1
+ABI_VERSION = 1
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_sz = ctypes.c_size_t
+
+
+class SsFwdArgs(ctypes.Structure):
+    _fields_ = [(n, _p) for n in ("u", "delta", "A", "Bm", "Cm", "Dskip", "z", "delta_bias", "out",
+                                  "last_state", "workspace")] + [
+        ("workspace_bytes", _sz), ("batch", _i64), ("dim", _i64), ("dstate", _i64), ("seqlen", _i64),
+        ("ngroups", _i64), ("dtype", _int), ("delta_softplus", _int)]
+
+
+class SsBwdArgs(ctypes.Structure):
+    _fields_ = [(n, _p) for n in ("u", "delta", "A", "Bm", "Cm", "Dskip", "z", "delta_bias", "dout", "du",
+                                  "ddelta", "dA", "dBm", "dCm", "dDskip", "dz", "ddelta_bias", "workspace")] + [
+        ("workspace_bytes", _sz), ("workspace_has_states", _int), ("batch", _i64), ("dim", _i64),
+        ("dstate", _i64), ("seqlen", _i64), ("ngroups", _i64), ("dtype", _int), ("delta_softplus", _int)]
+
+
+class SS2DFwdArgs(ctypes.Structure):
+    _fields_ = [(n, _p) for n in ("x", "delta", "A", "Bm", "Cm", "Dskip", "delta_bias", "z", "out",
+                                  "workspace")] + [
+        ("workspace_bytes", _sz), ("batch", _i64), ("dim", _i64), ("height", _i64), ("width", _i64),
+        ("dstate", _i64), ("dtype", _int), ("delta_softplus", _int)]
+
+
+class SS2DBwdArgs(ctypes.Structure):
+    _fields_ = [(n, _p) for n in ("x", "delta", "A", "Bm", "Cm", "Dskip", "delta_bias", "z", "dout", "dx",
+                                  "ddelta", "dA", "dBm", "dCm", "dDskip", "ddelta_bias", "dz", "workspace")] + [
+        ("workspace_bytes", _sz), ("batch", _i64), ("dim", _i64), ("height", _i64), ("width", _i64),
+        ("dstate", _i64), ("dtype", _int), ("delta_softplus", _int)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libss2d.so (built by __graft_entry__.build()); fail loudly if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.ss2d_abi_version.restype = _int
+        L.ss2d_abi_version.argtypes = []
+        L.ss2d_status_string.restype = ctypes.c_char_p
+        L.ss2d_status_string.argtypes = [_int]
+        for name in ("ss2d_cross_scan", "ss2d_cross_merge"):
+            f = getattr(L, name)
+            f.restype = _int
+            f.argtypes = [_p, _p, _i64, _i64, _i64, _i64, _int, _p]
+        L.selective_scan_workspace_bytes.restype = _sz
+        L.selective_scan_workspace_bytes.argtypes = [_i64] * 5
+        L.ss2d_workspace_bytes.restype = _sz
+        L.ss2d_workspace_bytes.argtypes = [_i64] * 5 + [_int]
+        for name, st in (("selective_scan_fwd", SsFwdArgs), ("selective_scan_bwd", SsBwdArgs),
+                         ("ss2d_fwd", SS2DFwdArgs), ("ss2d_bwd", SS2DBwdArgs)):
+            f = getattr(L, name)
+            f.restype = _int
+            f.argtypes = [ctypes.POINTER(st), _p]
+        if L.ss2d_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"libss2d ABI {L.ss2d_abi_version()} != binding ABI {ABI_VERSION}")
+        _lib = L
+    return _lib
+
+
+class SS2DError(RuntimeError):
+    pass
+
+
+def _check(status: int, what: str):
+    if status != SS2D_OK:
+        raise SS2DError(f"{what}: {lib().ss2d_status_string(status).decode()} (status {status})")
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return DTYPE_F32
+    if t == torch.bfloat16:
+        return DTYPE_BF16
+    raise SS2DError(f"unsupported I/O dtype {t}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t: torch.Tensor) -> torch.device:
+    if not t.is_cuda:
+        raise SS2DError("tensors must live on a ROCm device")
+    return t.device
+
+
+def _c(t, dtype=None):
+    """Contiguous (as the pages' wrapper does for every input), optionally cast (fp32 params)."""
+    if t is None:
+        return None
+    if dtype is not None and t.dtype != dtype:
+        t = t.to(dtype)
+    return t.contiguous()
+
+
+def _workspace(nbytes: int, device, workspace=None):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise SS2DError("workspace too small")
+        return workspace
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------------------------
+def ss2d_cross_scan(x: torch.Tensor) -> torch.Tensor:
+    x = _c(x)
+    B, C, H, W = x.shape
+    xs = torch.empty((B, 4, C, H * W), dtype=x.dtype, device=_dev(x))
+    _check(lib().ss2d_cross_scan(_ptr(x), _ptr(xs), B, C, H, W, _dtype_code(x.dtype), _stream(x.device)),
+           "ss2d_cross_scan")
+    return xs
+
+
+def ss2d_cross_merge(ys: torch.Tensor, height: int, width: int) -> torch.Tensor:
+    ys = _c(ys)
+    B, K, C, L = ys.shape
+    if K != 4 or L != height * width:
+        raise SS2DError("ys must be (batch, 4, channels, height*width)")
+    y = torch.empty((B, C, height, width), dtype=ys.dtype, device=_dev(ys))
+    _check(lib().ss2d_cross_merge(_ptr(ys), _ptr(y), B, C, height, width, _dtype_code(ys.dtype),
+                                  _stream(ys.device)), "ss2d_cross_merge")
+    return y
+
+
+def selective_scan_workspace_bytes(batch, dim, dstate, seqlen, ngroups) -> int:
+    return int(lib().selective_scan_workspace_bytes(batch, dim, dstate, seqlen, ngroups))
+
+
+def ss2d_workspace_bytes(batch, dim, height, width, dstate, dtype: torch.dtype) -> int:
+    return int(lib().ss2d_workspace_bytes(batch, dim, height, width, dstate, _dtype_code(dtype)))
+
+
+def _bc4(Bm):
+    return Bm.unsqueeze(1) if Bm.dim() == 3 else Bm  # (batch, N, L) is read as one group
+
+
+def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+                       return_last_state=False, workspace=None):
+    """Forward of the selective scan (`selective_scan_fn` shapes).  Returns out, and
+    last_state when asked.  A caller-provided `workspace` (uint8 tensor of at least
+    selective_scan_workspace_bytes) keeps the checkpoint states that selective_scan_bwd can
+    reuse (workspace_has_states=True); without one a temporary workspace is allocated."""
+    u, delta = _c(u), _c(delta)
+    dev = _dev(u)
+    B, C = _c(_bc4(B)), _c(_bc4(C))
+    A = _c(A, torch.float32)
+    D = _c(D, torch.float32)
+    delta_bias = _c(delta_bias, torch.float32)
+    z = _c(z)
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    G = B.shape[1]
+    out = torch.empty_like(u)
+    last = torch.empty((batch, dim, N), dtype=torch.float32, device=dev) if return_last_state else None
+    ws = _workspace(selective_scan_workspace_bytes(batch, dim, N, L, G), dev, workspace)
+    a = SsFwdArgs(u=_ptr(u), delta=_ptr(delta), A=_ptr(A), Bm=_ptr(B), Cm=_ptr(C), Dskip=_ptr(D), z=_ptr(z),
+                  delta_bias=_ptr(delta_bias), out=_ptr(out), last_state=_ptr(last), workspace=_ptr(ws),
+                  workspace_bytes=ws.numel() * ws.element_size(),
+                  batch=batch, dim=dim, dstate=N, seqlen=L, ngroups=G, dtype=_dtype_code(u.dtype),
+                  delta_softplus=int(bool(delta_softplus)))
+    _check(lib().selective_scan_fwd(ctypes.byref(a), _stream(dev)), "selective_scan_fwd")
+    return (out, last) if return_last_state else out
+
+
+def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dout=None, delta_softplus=False,
+                       workspace=None, workspace_has_states=False):
+    """Backward of selective_scan_fwd.  Returns a dict of gradients (None for absent inputs)."""
+    u, delta, dout = _c(u), _c(delta), _c(dout)
+    dev = _dev(u)
+    squeeze = B.dim() == 3
+    B, C = _c(_bc4(B)), _c(_bc4(C))
+    A = _c(A, torch.float32)
+    D = _c(D, torch.float32)
+    delta_bias = _c(delta_bias, torch.float32)
+    z = _c(z)
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    G = B.shape[1]
+    du, ddelta = torch.empty_like(u), torch.empty_like(u)
+    dA = torch.empty((dim, N), dtype=torch.float32, device=dev)
+    dB, dC = torch.empty_like(B), torch.empty_like(C)
+    dD = torch.empty(dim, dtype=torch.float32, device=dev) if D is not None else None
+    dz = torch.empty_like(u) if z is not None else None
+    dbias = torch.empty(dim, dtype=torch.float32, device=dev) if delta_bias is not None else None
+    ws = _workspace(selective_scan_workspace_bytes(batch, dim, N, L, G), dev, workspace)
+    a = SsBwdArgs(u=_ptr(u), delta=_ptr(delta), A=_ptr(A), Bm=_ptr(B), Cm=_ptr(C), Dskip=_ptr(D), z=_ptr(z),
+                  delta_bias=_ptr(delta_bias), dout=_ptr(dout), du=_ptr(du), ddelta=_ptr(ddelta), dA=_ptr(dA),
+                  dBm=_ptr(dB), dCm=_ptr(dC), dDskip=_ptr(dD), dz=_ptr(dz), ddelta_bias=_ptr(dbias),
+                  workspace=_ptr(ws), workspace_bytes=ws.numel() * ws.element_size(),
+                  workspace_has_states=int(bool(workspace_has_states)), batch=batch, dim=dim, dstate=N,
+                  seqlen=L, ngroups=G, dtype=_dtype_code(u.dtype), delta_softplus=int(bool(delta_softplus)))
+    _check(lib().selective_scan_bwd(ctypes.byref(a), _stream(dev)), "selective_scan_bwd")
+    if squeeze:
+        dB, dC = dB[:, 0], dC[:, 0]
+    return {"du": du, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "dz": dz, "ddelta_bias": dbias}
+
+
+def ss2d_fwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=True, workspace=None,
+             out=None):
+    """Fused SS2D forward.  x, z: (batch, dim, H, W); delta: (batch, 4, dim, H*W);
+    A: (4, dim, N) fp32; B, C: (batch, 4, N, H*W); D, delta_bias: (4, dim) fp32."""
+    x, delta = _c(x), _c(delta)
+    dev = _dev(x)
+    B, C, z = _c(B), _c(C), _c(z)
+    A = _c(A, torch.float32)
+    D = _c(D, torch.float32)
+    delta_bias = _c(delta_bias, torch.float32)
+    batch, dim, H, W = x.shape
+    N = A.shape[-1]
+    if out is None:
+        out = torch.empty_like(x)
+    ws = _workspace(ss2d_workspace_bytes(batch, dim, H, W, N, x.dtype), dev, workspace)
+    a = SS2DFwdArgs(x=_ptr(x), delta=_ptr(delta), A=_ptr(A), Bm=_ptr(B), Cm=_ptr(C), Dskip=_ptr(D),
+                    delta_bias=_ptr(delta_bias), z=_ptr(z), out=_ptr(out), workspace=_ptr(ws),
+                    workspace_bytes=ws.numel() * ws.element_size(), batch=batch, dim=dim, height=H, width=W,
+                    dstate=N, dtype=_dtype_code(x.dtype), delta_softplus=int(bool(delta_softplus)))
+    _check(lib().ss2d_fwd(ctypes.byref(a), _stream(dev)), "ss2d_fwd")
+    return out
+
+
+def ss2d_bwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, dout=None, delta_softplus=True,
+             workspace=None):
+    """Backward of ss2d_fwd; returns a dict of gradients (None for absent inputs)."""
+    x, delta, dout = _c(x), _c(delta), _c(dout)
+    dev = _dev(x)
+    B, C, z = _c(B), _c(C), _c(z)
+    A = _c(A, torch.float32)
+    D = _c(D, torch.float32)
+    delta_bias = _c(delta_bias, torch.float32)
+    batch, dim, H, W = x.shape
+    N = A.shape[-1]
+    dx, ddelta = torch.empty_like(x), torch.empty_like(delta)
+    dA = torch.empty_like(A)
+    dB, dC = torch.empty_like(B), torch.empty_like(C)
+    dD = torch.empty_like(D) if D is not None else None
+    dbias = torch.empty_like(delta_bias) if delta_bias is not None else None
+    dz = torch.empty_like(z) if z is not None else None
+    ws = _workspace(ss2d_workspace_bytes(batch, dim, H, W, N, x.dtype), dev, workspace)
+    a = SS2DBwdArgs(x=_ptr(x), delta=_ptr(delta), A=_ptr(A), Bm=_ptr(B), Cm=_ptr(C), Dskip=_ptr(D),
+                    delta_bias=_ptr(delta_bias), z=_ptr(z), dout=_ptr(dout), dx=_ptr(dx), ddelta=_ptr(ddelta),
+                    dA=_ptr(dA), dBm=_ptr(dB), dCm=_ptr(dC), dDskip=_ptr(dD), ddelta_bias=_ptr(dbias), dz=_ptr(dz),
+                    workspace=_ptr(ws), workspace_bytes=ws.numel() * ws.element_size(), batch=batch, dim=dim,
+                    height=H, width=W, dstate=N, dtype=_dtype_code(x.dtype),
+                    delta_softplus=int(bool(delta_softplus)))
+    _check(lib().ss2d_bwd(ctypes.byref(a), _stream(dev)), "ss2d_bwd")
+    return {"dx": dx, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "ddelta_bias": dbias, "dz": dz}

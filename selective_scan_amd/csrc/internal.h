@@ -1,0 +1,138 @@
+// Internal launch interfaces between the C ABI layer (ss2d_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ss2d {
+
+constexpr int kTile = 32;  // time steps staged per tile
+constexpr int kCkpt = 64;  // the scan state is checkpointed before every kCkpt-th step
+
+// ---- permutations (permute_kernels.hip) ----------------------------------------------
+// Scatter one map (batch, C, H, W) into up to four route-ordered outputs.
+// out[k] (may be null) receives plane (b, c) at out[k] + b*batch_stride + c*L, in route-k order.
+struct ScanOutputs {
+  void* out[4];
+  int64_t batch_stride;  // elements
+};
+hipError_t launch_route_scatter(const void* x, const ScanOutputs& o, int64_t batch, int64_t C, int64_t H,
+                                int64_t W, int elem_bytes, hipStream_t s);
+
+// y[b, c, p] = (((r0 + r1) + r2) + r3)[p] (+ Dsum[c] * x[b, c, p]) (* silu(z[b, c, p])) with route
+// inputs in route order (fp32 when routes_f32, else dtype), grid outputs in dtype.
+// Optionally also writes the fp32 pre-gate sum to merged_f32.
+struct MergeArgs {
+  const void* routes;      // (batch, 4, C, L) fp32 or dtype
+  int routes_f32;
+  const void* x;           // grid (batch, C, H, W) dtype, optional skip input
+  const float* Dskip;      // (4, C) fp32, summed over routes (used with x)
+  const void* z;           // grid dtype, optional gate
+  void* y;                 // grid dtype
+  float* merged_f32;       // optional
+  int64_t batch, C, H, W;
+  int dtype;               // 0 f32, 1 bf16
+};
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+
+// Backward helpers of the SS2D gate: with the merged pre-gate map M (fp32),
+//   dM = dout * silu(z)            (fp32 grid, and its per-plane transpose dMT)
+//   dz = dout * M * silu'(z)       (dtype grid)
+// without z: dM = dout.
+struct GateBwdArgs {
+  const float* merged;  // (batch, C, L) fp32
+  const void* z;        // optional
+  const void* dout;
+  float* dM;            // (batch, C, L) fp32 grid order
+  float* dMT;           // (batch, C, L) fp32 column-major order
+  void* dz;             // optional
+  int64_t batch, C, H, W;
+  int dtype;
+};
+hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t s);
+
+// Writes n fp32 zeros (a kernel, so that graph capture records no memset node).
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+
+// ---- selective scan forward (scan_fwd.hip) ---------------------------------------------
+struct ScanFwdParams {
+  // generic rows: u/delta/z/out are (batch, dim, L); B/C (batch, G, N, L)
+  // ss2d rows   : row (b, k*D + d) reads u from x (k = 0, 2) or xT (k = 1, 3) plane (b, d),
+  //               reversed for k >= 2; out is fp32 in route order (batch, 4*D, L)
+  const void* u;
+  const void* uT;
+  const void* delta;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;
+  const void* z;
+  const float* delta_bias;
+  void* out;           // may be null (state-only pass)
+  float* last_state;   // may be null
+  float* ckpt;         // (batch*dim, n_ckpt, N) or null
+  float* chunk_sum;    // (batch*dim, n_chunks) or null
+  int64_t batch, dim, L, G, per_group, dblocks, chunk_len;
+  int n_chunks, n_ckpt, N;
+  int softplus;
+  int ss2d;            // rows follow the SS2D routes (G = 4, per_group = D)
+  int dtype;
+  int vec;             // 4-element vector access allowed
+  int pass;            // 0: outputs/checkpoints from the stored chunk-start state; 1: chunk-local end state
+};
+hipError_t launch_scan_fwd(const ScanFwdParams& p, hipStream_t s);
+// Turns the chunk-local end states (pass 1) into the true chunk-start states.
+hipError_t launch_chunk_combine(const ScanFwdParams& p, hipStream_t s);
+
+// ---- selective scan backward (scan_bwd.hip) ---------------------------------------------
+struct ScanBwdParams {
+  const void* u;
+  const void* uT;
+  const void* delta;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;
+  const void* z;           // generic only
+  const float* delta_bias;
+  const void* dout;        // generic: dtype (batch, dim, L); ss2d: dM (fp32 grid) and dMT
+  const void* doutT;
+  void* du;                // generic: dtype; ss2d: fp32 route order (batch, 4D, L)
+  void* ddelta;            // dtype (batch, dim, L)
+  void* dz;                // generic only, dtype
+  const float* ckpt;       // (rows, n_ckpt, N) states before every kCkpt-th step
+  float* lam_carry;        // (rows, n_chunks, N): a_{t1} * lambda_{t1} flowing into each chunk
+  float* chunk_sum;        // (rows, n_chunks)
+  float* dB_part;          // (dblocks, batch, G, N, L) fp32
+  float* dC_part;
+  float* dA_part;          // (n_chunks, rows, N)
+  float* dD_part;          // (n_chunks, rows)
+  float* dbias_part;       // (n_chunks, rows)
+  int64_t batch, dim, L, G, per_group, dblocks, chunk_len;
+  int n_chunks, n_ckpt, N;
+  int softplus;
+  int ss2d;
+  int dtype;
+  int vec;
+  int pass;                // 1: chunk-local lambda pass; 0: gradients
+};
+hipError_t launch_scan_bwd(const ScanBwdParams& p, hipStream_t s);
+hipError_t launch_lambda_combine(const ScanBwdParams& p, hipStream_t s);
+// Sums the per-block/per-chunk partials into dA, dD, ddelta_bias, dB, dC.
+struct BwdReduceArgs {
+  const float* dB_part;
+  const float* dC_part;
+  const float* dA_part;
+  const float* dD_part;
+  const float* dbias_part;
+  void* dB;
+  void* dC;
+  float* dA;
+  float* dD;
+  float* dbias;
+  int64_t batch, dim, L, G, dblocks;
+  int n_chunks, N, dtype;
+};
+hipError_t launch_bwd_reduce(const BwdReduceArgs& a, hipStream_t s);
+
+}  // namespace ss2d

@@ -1,0 +1,396 @@
+// Selective scan S6, forward kernel (included by the scan_fwd_inst_*.hip instantiations).  Semantics: `selective_scan_ref` on the "Vision Mamba structure
+// and principle" page (section 2):
+//   delta_t = softplus(delta_raw_t + bias[d]);  h_t = exp(delta_t A[d,:]) h_{t-1} + delta_t B_t u_t
+//   y_t = <C_t, h_t> + D[d] u_t ;  out_t = y_t * silu(z_t)
+//
+// Mapping on CDNA4: one wavefront = 64 consecutive channels d of one (batch, group) pair, so
+// that B_t / C_t (shared by the channels of a group) are wave-uniform: they are staged per
+// 32-step tile in LDS as fp32 and read back as broadcasts.  Each lane runs its channel's
+// recurrence sequentially with the N-entry state in VGPRs; the loads of its own row (delta, u,
+// z) are 4-element vectors, prefetched one tile ahead.
+//
+// Arithmetic is carried in base 2: with Lam = log2(1 + 2^(v log2 e)) (so delta = ln2 * Lam),
+//   exp(delta * A) = exp2(Lam * A)    and    delta * u * B = Lam * u * (ln2 * B),
+// which costs one multiply and one v_exp_f32 per (step, state) for the decay; ln2 is folded
+// into B while it is staged.
+//
+// When there are too few rows to fill the GPU, the sequence is split into chunks processed by
+// different wavefronts: pass 1 runs each chunk from a zero state and keeps its end state and
+// sum(Lam); a combine kernel chains the chunks (h_start(c+1) = exp2(A sum Lam_c) h_start(c)
+// + h_end_local(c)); pass 0 reruns every chunk from its true start state and writes outputs.
+#pragma once
+#include "device_common.h"
+#include "internal.h"
+
+namespace ss2d {
+namespace fwd_detail {
+
+// Per-lane copy of one row's tile (kTile consecutive elements), kept in the storage format.
+template <typename T>
+struct RowTile;
+template <>
+struct RowTile<float> {
+  float4 v[kTile / 4];
+  __device__ __forceinline__ float get(int i) const {
+    const float4 q = v[i / 4];
+    return (i % 4 == 0) ? q.x : (i % 4 == 1) ? q.y : (i % 4 == 2) ? q.z : q.w;
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int j = 0; j < kTile / 4; ++j) v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __device__ __forceinline__ void load_vec(const float* p, int j) { v[j] = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void set(int i, float x) {
+    float4& q = v[i / 4];
+    if (i % 4 == 0) q.x = x; else if (i % 4 == 1) q.y = x; else if (i % 4 == 2) q.z = x; else q.w = x;
+  }
+  __device__ __forceinline__ void reverse() {
+    float4 r[kTile / 4];
+#pragma unroll
+    for (int j = 0; j < kTile / 4; ++j) {
+      const float4 q = v[kTile / 4 - 1 - j];
+      r[j] = make_float4(q.w, q.z, q.y, q.x);
+    }
+#pragma unroll
+    for (int j = 0; j < kTile / 4; ++j) v[j] = r[j];
+  }
+};
+template <>
+struct RowTile<bf16> {
+  uint2 v[kTile / 4];
+  __device__ __forceinline__ float get(int i) const {
+    const uint2 q = v[i / 4];
+    const uint32_t w = ((i % 4) < 2) ? q.x : q.y;
+    return (i % 2 == 0) ? bf16lo(w) : bf16hi(w);
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int j = 0; j < kTile / 4; ++j) v[j] = make_uint2(0u, 0u);
+  }
+  __device__ __forceinline__ void load_vec(const bf16* p, int j) { v[j] = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void set(int i, uint16_t bits) {
+    uint2& q = v[i / 4];
+    uint32_t& w = ((i % 4) < 2) ? q.x : q.y;
+    w = (i % 2 == 0) ? ((w & 0xffff0000u) | bits) : ((w & 0xffffu) | (uint32_t(bits) << 16));
+  }
+  __device__ __forceinline__ void reverse() {
+    uint2 r[kTile / 4];
+#pragma unroll
+    for (int j = 0; j < kTile / 4; ++j) {
+      const uint2 q = v[kTile / 4 - 1 - j];
+      r[j] = make_uint2(__builtin_amdgcn_alignbit(q.y, q.y, 16), __builtin_amdgcn_alignbit(q.x, q.x, 16));
+    }
+#pragma unroll
+    for (int j = 0; j < kTile / 4; ++j) v[j] = r[j];
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ void set_elem(RowTile<T>& t, int i, const T* p);
+template <>
+__device__ __forceinline__ void set_elem<float>(RowTile<float>& t, int i, const float* p) { t.set(i, *p); }
+template <>
+__device__ __forceinline__ void set_elem<bf16>(RowTile<bf16>& t, int i, const bf16* p) { t.set(i, p->bits); }
+
+// Load steps [t0, t0 + kTile) of a row.  Forward rows read elements t0.., reversed rows read
+// pixels L-1-t for the same steps (then the tile is flipped so that index i is step t0 + i).
+template <typename T, bool kVec>
+__device__ __forceinline__ void load_row(RowTile<T>& tile, const T* row, int64_t t0, int64_t t_end, int64_t L,
+                                         bool rev) {
+  tile.zero();
+  if (kVec) {
+    if (!rev) {
+#pragma unroll
+      for (int j = 0; j < kTile / 4; ++j)
+        if (t0 + 4 * j < t_end) tile.load_vec(row + t0 + 4 * j, j);
+    } else {
+      const int64_t base = L - t0 - kTile;  // pixel of tile element kTile-1
+#pragma unroll
+      for (int j = 0; j < kTile / 4; ++j)
+        if (base + 4 * j >= 0 && L - 1 - (base + 4 * j + 3) < t_end) tile.load_vec(row + base + 4 * j, j);
+      tile.reverse();
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kTile; ++i) {
+      const int64_t t = t0 + i;
+      if (t < t_end) set_elem<T>(tile, i, row + (rev ? (L - 1 - t) : t));
+    }
+  }
+}
+
+// B/C staging: per lane, the raw values it copies into LDS for one tile.
+template <typename T, int NS, bool kVec>
+struct BCStage {
+  static constexpr int kVecs = (NS * kTile / 4 + kWave - 1) / kWave;  // 4-step vectors per lane
+  static constexpr int kElems = (NS * kTile + kWave - 1) / kWave;     // scalars per lane
+  float b[kVec ? 4 * kVecs : kElems];
+  float c[kVec ? 4 * kVecs : kElems];
+
+  __device__ __forceinline__ void load(const T* Bg, const T* Cg, int N, int64_t L, int64_t t0, int64_t t_end,
+                                       int lane) {
+    if (kVec) {
+#pragma unroll
+      for (int k = 0; k < kVecs; ++k) {
+        const int j = lane + k * kWave;            // vector id: n = j / (kTile/4), q = j % (kTile/4)
+        const int n = j / (kTile / 4), q = j % (kTile / 4);
+        float4 vb = make_float4(0.f, 0.f, 0.f, 0.f), vc = vb;
+        if (n < N && j < NS * kTile / 4 && t0 + 4 * q < t_end) {
+          vb = Elem<T>::load4(Bg, int64_t(n) * L + t0 + 4 * q);
+          vc = Elem<T>::load4(Cg, int64_t(n) * L + t0 + 4 * q);
+        }
+        b[4 * k + 0] = vb.x; b[4 * k + 1] = vb.y; b[4 * k + 2] = vb.z; b[4 * k + 3] = vb.w;
+        c[4 * k + 0] = vc.x; c[4 * k + 1] = vc.y; c[4 * k + 2] = vc.z; c[4 * k + 3] = vc.w;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kElems; ++k) {
+        const int e = lane + k * kWave;            // element id: n = e / kTile, i = e % kTile
+        const int n = e / kTile, i = e % kTile;
+        float vb = 0.f, vc = 0.f;
+        if (n < N && e < NS * kTile && t0 + i < t_end) {
+          vb = Elem<T>::load(Bg, int64_t(n) * L + t0 + i);
+          vc = Elem<T>::load(Cg, int64_t(n) * L + t0 + i);
+        }
+        b[k] = vb;
+        c[k] = vc;
+      }
+    }
+  }
+
+  // LDS layout: [step][state] with row stride S floats; B is pre-multiplied by ln 2.
+  template <int S>
+  __device__ __forceinline__ void store(float* sB, float* sC, int lane) const {
+    if (kVec) {
+#pragma unroll
+      for (int k = 0; k < kVecs; ++k) {
+        const int j = lane + k * kWave;
+        if (j < NS * kTile / 4) {
+          const int n = j / (kTile / 4), q = j % (kTile / 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sB[(4 * q + i) * S + n] = b[4 * k + i] * kLn2;
+            sC[(4 * q + i) * S + n] = c[4 * k + i];
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kElems; ++k) {
+        const int e = lane + k * kWave;
+        if (e < NS * kTile) {
+          const int n = e / kTile, i = e % kTile;
+          sB[i * S + n] = b[k] * kLn2;
+          sC[i * S + n] = c[k];
+        }
+      }
+    }
+  }
+};
+
+template <typename O, bool kVec>
+__device__ __forceinline__ void store_out(O* row, const float* y, int64_t t0, int64_t t_end) {
+  if (kVec) {
+#pragma unroll
+    for (int j = 0; j < kTile / 4; ++j)
+      if (t0 + 4 * j < t_end)
+        Elem<O>::store4(row, t0 + 4 * j, make_float4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]));
+  } else {
+#pragma unroll
+    for (int i = 0; i < kTile; ++i)
+      if (t0 + i < t_end) Elem<O>::store(row, t0 + i, y[i]);
+  }
+}
+
+template <int NS>
+__device__ __forceinline__ void store_state(float* dst, const float* h, int N) {
+  if (NS % 4 == 0 && (N % 4) == 0) {
+#pragma unroll
+    for (int n = 0; n < NS; n += 4)
+      if (n < N) *reinterpret_cast<float4*>(dst + n) = make_float4(h[n], h[n + 1], h[n + 2], h[n + 3]);
+  } else {
+#pragma unroll
+    for (int n = 0; n < NS; ++n)
+      if (n < N) dst[n] = h[n];
+  }
+}
+
+template <typename T, int NS, bool kSS2D, bool kVec, int kPass>
+__global__ __launch_bounds__(kWave) void scan_fwd_kernel(const ScanFwdParams p) {
+  constexpr int S = (NS < 4) ? 4 : NS + 4;  // LDS row stride (floats), keeps float4 alignment
+  __shared__ __align__(16) float sB[kTile * S];
+  __shared__ __align__(16) float sC[kTile * S];
+
+  const int lane = threadIdx.x;
+  int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t dblk = bid % p.dblocks;
+  bid /= p.dblocks;
+  const int c = int(bid % p.n_chunks);
+  bid /= p.n_chunks;
+  const int64_t g = bid % p.G;
+  const int64_t b = bid / p.G;
+  const int64_t dg = dblk * kWave + lane;
+  const bool active = dg < p.per_group;
+  const int64_t dl = active ? dg : 0;
+  const int64_t d = g * p.per_group + dl;
+  const int64_t row = b * p.dim + d;
+  const int64_t L = p.L;
+  const int N = p.N;
+
+  const T* delta_row = static_cast<const T*>(p.delta) + row * L;
+  const T* u_row;
+  bool rev = false;
+  if (kSS2D) {
+    const T* src = (g & 1) ? static_cast<const T*>(p.uT) : static_cast<const T*>(p.u);
+    u_row = src + (b * p.per_group + dl) * L;
+    rev = g >= 2;
+  } else {
+    u_row = static_cast<const T*>(p.u) + row * L;
+  }
+  const bool has_z = !kSS2D && p.z != nullptr;
+  const T* z_row = has_z ? static_cast<const T*>(p.z) + row * L : nullptr;
+  const T* Bg = static_cast<const T*>(p.Bm) + (b * p.G + g) * N * L;
+  const T* Cg = static_cast<const T*>(p.Cm) + (b * p.G + g) * N * L;
+
+  float Acoef[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) Acoef[n] = (n < N) ? p.A[d * N + n] : 0.0f;
+  const float bias = p.delta_bias ? p.delta_bias[d] : 0.0f;
+  const float Dd = (!kSS2D && p.Dskip) ? p.Dskip[d] : 0.0f;
+
+  const int64_t t_begin = int64_t(c) * p.chunk_len;
+  const int64_t t_end = (t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L;
+
+  float h[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+  if (kPass == 0 && p.n_chunks > 1 && c > 0) {
+    const float* src = p.ckpt + (row * p.n_ckpt + t_begin / kCkpt) * N;
+#pragma unroll
+    for (int n = 0; n < NS; ++n)
+      if (n < N) h[n] = src[n];
+  }
+  float lam_sum = 0.0f;
+
+  RowTile<T> nd, nu, nz;
+  BCStage<T, NS, kVec> nbc;
+  if (t_begin < t_end) {
+    load_row<T, kVec>(nd, delta_row, t_begin, t_end, L, false);
+    load_row<T, kVec>(nu, u_row, t_begin, t_end, L, rev);
+    if (has_z) load_row<T, kVec>(nz, z_row, t_begin, t_end, L, false);
+    nbc.load(Bg, Cg, N, L, t_begin, t_end, lane);
+  }
+
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTile) {
+    const RowTile<T> cd = nd, cu = nu, cz = nz;
+    __syncthreads();  // the previous tile's LDS reads are complete
+    nbc.template store<S>(sB, sC, lane);
+    __syncthreads();
+    const int64_t t1 = t0 + kTile;
+    if (t1 < t_end) {
+      load_row<T, kVec>(nd, delta_row, t1, t_end, L, false);
+      load_row<T, kVec>(nu, u_row, t1, t_end, L, rev);
+      if (has_z) load_row<T, kVec>(nz, z_row, t1, t_end, L, false);
+      nbc.load(Bg, Cg, N, L, t1, t_end, lane);
+    }
+    if (kPass == 0 && p.ckpt && (t0 % kCkpt) == 0 && active)
+      store_state<NS>(p.ckpt + (row * p.n_ckpt + t0 / kCkpt) * N, h, N);
+
+    const int nt = int((t_end - t0 < kTile) ? (t_end - t0) : kTile);
+    // per-step quantities: Lam (log2-domain step) and Lam * u
+    float lam[kTile], du[kTile];
+    if (p.softplus) {
+#pragma unroll
+      for (int i = 0; i < kTile; ++i) lam[i] = softplus_log2((cd.get(i) + bias) * kLog2e);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kTile; ++i) lam[i] = (cd.get(i) + bias) * kLog2e;
+    }
+#pragma unroll
+    for (int i = 0; i < kTile; ++i) du[i] = lam[i] * cu.get(i);
+
+    float y[kTile];
+#pragma unroll
+    for (int i = 0; i < kTile; ++i) {
+      if (i < nt) {
+        const float4* bt = reinterpret_cast<const float4*>(sB + i * S);
+        const float4* ct = reinterpret_cast<const float4*>(sC + i * S);
+        float acc = 0.0f;
+        if (NS >= 4) {
+#pragma unroll
+          for (int n4 = 0; n4 < NS / 4; ++n4) {
+            const float4 bb = bt[n4];
+            const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
+            float4 cc = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (kPass == 0) cc = ct[n4];
+            const float cv[4] = {cc.x, cc.y, cc.z, cc.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int n = 4 * n4 + k;
+              const float a = fast_exp2(lam[i] * Acoef[n]);
+              h[n] = fmaf(a, h[n], du[i] * bv[k]);
+              if (kPass == 0) acc = fmaf(cv[k], h[n], acc);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int n = 0; n < NS; ++n) {
+            const float a = fast_exp2(lam[i] * Acoef[n]);
+            h[n] = fmaf(a, h[n], du[i] * sB[i * S + n]);
+            if (kPass == 0) acc = fmaf(sC[i * S + n], h[n], acc);
+          }
+        }
+        y[i] = acc;
+        if (kPass == 1) lam_sum += lam[i];
+      } else {
+        y[i] = 0.0f;
+      }
+    }
+
+    if (kPass == 0 && p.out != nullptr && active) {
+      if (!kSS2D) {
+        if (p.Dskip) {
+#pragma unroll
+          for (int i = 0; i < kTile; ++i) y[i] = fmaf(Dd, cu.get(i), y[i]);
+        }
+        if (has_z) {
+#pragma unroll
+          for (int i = 0; i < kTile; ++i) y[i] *= silu(cz.get(i));
+        }
+        store_out<T, kVec>(static_cast<T*>(p.out) + row * L, y, t0, t_end);
+      } else {
+        store_out<float, kVec>(static_cast<float*>(p.out) + row * L, y, t0, t_end);
+      }
+    }
+  }
+
+  if (!active) return;
+  if (kPass == 1) {
+    if (t_end < L) store_state<NS>(p.ckpt + (row * p.n_ckpt + t_end / kCkpt) * N, h, N);
+    p.chunk_sum[row * p.n_chunks + c] = lam_sum;
+  } else if (p.last_state && t_end == L) {
+    store_state<NS>(p.last_state + row * N, h, N);
+  }
+}
+
+template <typename T, int NS, bool kSS2D, bool kVec>
+hipError_t launch_t(const ScanFwdParams& p, hipStream_t s) {
+  const int64_t blocks = p.batch * p.G * p.dblocks * p.n_chunks;
+  if (blocks == 0) return hipSuccess;
+  if (p.pass == 1)
+    scan_fwd_kernel<T, NS, kSS2D, kVec, 1><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
+  else
+    scan_fwd_kernel<T, NS, kSS2D, kVec, 0><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace fwd_detail
+
+template <typename T, int NS>
+hipError_t scan_fwd_launch(const ScanFwdParams& p, hipStream_t s) {
+  using namespace fwd_detail;
+  if (p.ss2d) return p.vec ? launch_t<T, NS, true, true>(p, s) : launch_t<T, NS, true, false>(p, s);
+  return p.vec ? launch_t<T, NS, false, true>(p, s) : launch_t<T, NS, false, false>(p, s);
+}
+
+}  // namespace ss2d

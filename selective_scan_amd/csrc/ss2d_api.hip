@@ -1,0 +1,330 @@
+// C ABI entry points (declared in include/ss2d.h): argument validation, workspace layout and
+// kernel dispatch.  Nothing here allocates, frees or synchronises.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/ss2d.h"
+#include "device_common.h"
+#include "internal.h"
+
+using namespace ss2d;
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+inline int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int esize(int dtype) { return dtype == SS2D_DTYPE_F32 ? 4 : 2; }
+inline bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % uintptr_t(a)) == 0; }
+
+int status_from(hipError_t e) { return e == hipSuccess ? SS2D_OK : SS2D_ERR_HIP; }
+
+bool dtype_ok(int dtype) { return dtype == SS2D_DTYPE_F32 || dtype == SS2D_DTYPE_BF16; }
+
+// Limit on grid sizes: one-dimensional grids of at most 2^31 - 1 workgroups.
+constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
+
+// ---- selective-scan workspace layout -------------------------------------------------
+struct ScanLayout {
+  int64_t rows, n_ckpt, dblocks, per_group;
+  int64_t off_ckpt, off_sum, off_lam, off_dB, off_dC, off_dA, off_dD, off_dbias, total;
+};
+
+ScanLayout scan_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int64_t ngroups) {
+  ScanLayout l{};
+  l.rows = batch * dim;
+  l.n_ckpt = cdiv(seqlen, kCkpt);
+  l.per_group = ngroups > 0 ? dim / ngroups : 0;
+  l.dblocks = cdiv(l.per_group, kWave);
+  int64_t o = 0;
+  l.off_ckpt = o;  o += align_up(l.rows * l.n_ckpt * dstate * 4);
+  l.off_sum = o;   o += align_up(l.rows * l.n_ckpt * 4);
+  l.off_lam = o;   o += align_up(l.rows * l.n_ckpt * dstate * 4);
+  l.off_dB = o;    o += align_up(l.dblocks * batch * ngroups * dstate * seqlen * 4);
+  l.off_dC = o;    o += align_up(l.dblocks * batch * ngroups * dstate * seqlen * 4);
+  l.off_dA = o;    o += align_up(l.n_ckpt * l.rows * dstate * 4);
+  l.off_dD = o;    o += align_up(l.n_ckpt * l.rows * 4);
+  l.off_dbias = o; o += align_up(l.n_ckpt * l.rows * 4);
+  l.total = o;
+  return l;
+}
+
+// Split long sequences across wavefronts only when the rows alone cannot fill the GPU
+// (1024 SIMDs on MI355X; aim for at least two wavefronts per SIMD).
+void plan_chunks(int64_t row_waves, int64_t L, bool can_chunk, int64_t* chunk_len, int* n_chunks) {
+  const int64_t n_ckpt = cdiv(L, kCkpt);
+  if (!can_chunk || row_waves >= 1024 || n_ckpt <= 1) {
+    *chunk_len = n_ckpt * kCkpt;
+    *n_chunks = 1;
+    return;
+  }
+  int64_t want = cdiv(2048, row_waves);
+  if (want > n_ckpt) want = n_ckpt;
+  const int64_t ck_per_chunk = cdiv(n_ckpt, want);
+  *chunk_len = ck_per_chunk * kCkpt;
+  *n_chunks = int(cdiv(L, *chunk_len));
+}
+
+// ---- SS2D workspace layout -----------------------------------------------------------
+struct SS2DLayout {
+  int64_t off_xT, off_ys, off_scan, off_merged, off_dM, off_dMT, total;
+  ScanLayout scan;
+};
+
+SS2DLayout ss2d_layout(int64_t batch, int64_t dim, int64_t H, int64_t W, int64_t dstate, int dtype) {
+  SS2DLayout l{};
+  const int64_t L = H * W;
+  int64_t o = 0;
+  l.off_xT = o;     o += align_up(batch * dim * L * esize(dtype));
+  l.off_ys = o;     o += align_up(batch * 4 * dim * L * 4);
+  l.scan = scan_layout(batch, 4 * dim, dstate, L, 4);
+  l.off_scan = o;   o += l.scan.total;
+  l.off_merged = o; o += align_up(batch * dim * L * 4);
+  l.off_dM = o;     o += align_up(batch * dim * L * 4);
+  l.off_dMT = o;    o += align_up(batch * dim * L * 4);
+  l.total = o;
+  return l;
+}
+
+inline char* at(void* base, int64_t off) { return static_cast<char*>(base) + off; }
+
+// Common checks of the selective-scan shapes.
+int check_scan_shapes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int64_t ngroups, int dtype) {
+  if (!dtype_ok(dtype)) return SS2D_ERR_UNSUPPORTED;
+  if (batch < 0 || dim < 0 || seqlen < 0) return SS2D_ERR_INVALID_ARGUMENT;
+  if (dstate < 1 || dstate > 64) return SS2D_ERR_UNSUPPORTED;
+  if (ngroups < 1 || (dim % ngroups) != 0) return SS2D_ERR_INVALID_ARGUMENT;
+  return SS2D_OK;
+}
+
+bool elem_aligned(int dtype, std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && !aligned(p, esize(dtype))) return false;
+  return true;
+}
+bool vec_aligned(int dtype, std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && !aligned(p, 4 * esize(dtype))) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ss2d_abi_version(void) { return SS2D_ABI_VERSION; }
+
+const char* ss2d_status_string(int status) {
+  switch (status) {
+    case SS2D_OK: return "ok";
+    case SS2D_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SS2D_ERR_UNSUPPORTED: return "unsupported dtype or state size";
+    case SS2D_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int ss2d_cross_scan(const void* x, void* xs, int64_t batch, int64_t channels, int64_t height, int64_t width,
+                    int dtype, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return SS2D_ERR_UNSUPPORTED;
+  if (batch < 0 || channels < 0 || height < 0 || width < 0) return SS2D_ERR_INVALID_ARGUMENT;
+  const int64_t L = height * width;
+  if (batch * channels * L == 0) return SS2D_OK;
+  if (!x || !xs || !elem_aligned(dtype, {x, xs})) return SS2D_ERR_INVALID_ARGUMENT;
+  if (height > (1 << 30) || width > (1 << 30) || batch * channels * cdiv(height, 32) * cdiv(width, 32) > kMaxBlocks)
+    return SS2D_ERR_INVALID_ARGUMENT;
+  const int e = esize(dtype);
+  ScanOutputs o;
+  for (int k = 0; k < 4; ++k) o.out[k] = at(xs, int64_t(k) * channels * L * e);
+  o.batch_stride = 4 * channels * L;
+  return status_from(launch_route_scatter(x, o, batch, channels, height, width, e, stream));
+}
+
+int ss2d_cross_merge(const void* ys, void* y, int64_t batch, int64_t channels, int64_t height, int64_t width,
+                     int dtype, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return SS2D_ERR_UNSUPPORTED;
+  if (batch < 0 || channels < 0 || height < 0 || width < 0) return SS2D_ERR_INVALID_ARGUMENT;
+  if (batch * channels * height * width == 0) return SS2D_OK;
+  if (!ys || !y || !elem_aligned(dtype, {ys, y})) return SS2D_ERR_INVALID_ARGUMENT;
+  if (height > (1 << 30) || width > (1 << 30) || batch * channels * cdiv(height, 32) * cdiv(width, 32) > kMaxBlocks)
+    return SS2D_ERR_INVALID_ARGUMENT;
+  MergeArgs a{};
+  a.routes = ys;
+  a.routes_f32 = dtype == SS2D_DTYPE_F32;
+  a.y = y;
+  a.batch = batch;
+  a.C = channels;
+  a.H = height;
+  a.W = width;
+  a.dtype = dtype;
+  return status_from(launch_merge(a, stream));
+}
+
+size_t selective_scan_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                      int64_t ngroups) {
+  if (batch < 0 || dim < 0 || dstate < 1 || seqlen < 0 || ngroups < 1) return 0;
+  return size_t(scan_layout(batch, dim, dstate, seqlen, ngroups).total);
+}
+
+int selective_scan_fwd(const ss_fwd_args* a, hipStream_t stream) {
+  if (!a) return SS2D_ERR_INVALID_ARGUMENT;
+  int st = check_scan_shapes(a->batch, a->dim, a->dstate, a->seqlen, a->ngroups, a->dtype);
+  if (st != SS2D_OK) return st;
+  const int64_t rows = a->batch * a->dim;
+  if (rows == 0 || a->seqlen == 0) {
+    if (rows > 0 && a->last_state)
+      return status_from(launch_fill_zero(a->last_state, rows * a->dstate, stream));
+    return SS2D_OK;
+  }
+  if (!a->u || !a->delta || !a->A || !a->Bm || !a->Cm || !a->out) return SS2D_ERR_INVALID_ARGUMENT;
+  if (!elem_aligned(a->dtype, {a->u, a->delta, a->Bm, a->Cm, a->z, a->out})) return SS2D_ERR_INVALID_ARGUMENT;
+  if (!aligned(a->A, 4) || (a->Dskip && !aligned(a->Dskip, 4)) || (a->delta_bias && !aligned(a->delta_bias, 4)) ||
+      (a->last_state && !aligned(a->last_state, 16)))
+    return SS2D_ERR_INVALID_ARGUMENT;
+  const ScanLayout lay = scan_layout(a->batch, a->dim, a->dstate, a->seqlen, a->ngroups);
+  if (a->workspace && (a->workspace_bytes < size_t(lay.total) || !aligned(a->workspace, kAlign)))
+    return SS2D_ERR_INVALID_ARGUMENT;
+
+  ScanFwdParams p{};
+  p.u = a->u;
+  p.delta = a->delta;
+  p.A = a->A;
+  p.Bm = a->Bm;
+  p.Cm = a->Cm;
+  p.Dskip = a->Dskip;
+  p.z = a->z;
+  p.delta_bias = a->delta_bias;
+  p.out = a->out;
+  p.last_state = a->last_state;
+  p.batch = a->batch;
+  p.dim = a->dim;
+  p.L = a->seqlen;
+  p.G = a->ngroups;
+  p.per_group = lay.per_group;
+  p.dblocks = lay.dblocks;
+  p.n_ckpt = int(lay.n_ckpt);
+  p.N = int(a->dstate);
+  p.softplus = a->delta_softplus ? 1 : 0;
+  p.ss2d = 0;
+  p.dtype = a->dtype;
+  p.vec = (a->seqlen % 4 == 0) && vec_aligned(a->dtype, {a->u, a->delta, a->Bm, a->Cm, a->z, a->out});
+  plan_chunks(a->batch * a->ngroups * lay.dblocks, a->seqlen, a->workspace != nullptr, &p.chunk_len, &p.n_chunks);
+  if (a->batch * a->ngroups * lay.dblocks * p.n_chunks > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
+  if (a->workspace) {
+    p.ckpt = reinterpret_cast<float*>(at(a->workspace, lay.off_ckpt));
+    p.chunk_sum = reinterpret_cast<float*>(at(a->workspace, lay.off_sum));
+  }
+  hipError_t e = hipSuccess;
+  if (p.n_chunks > 1) {
+    p.pass = 1;
+    e = launch_scan_fwd(p, stream);
+    if (e == hipSuccess) e = launch_chunk_combine(p, stream);
+  }
+  p.pass = 0;
+  if (e == hipSuccess) e = launch_scan_fwd(p, stream);
+  return status_from(e);
+}
+
+size_t ss2d_workspace_bytes(int64_t batch, int64_t dim, int64_t height, int64_t width, int64_t dstate, int dtype) {
+  if (batch < 0 || dim < 0 || height < 0 || width < 0 || dstate < 1 || !dtype_ok(dtype)) return 0;
+  return size_t(ss2d_layout(batch, dim, height, width, dstate, dtype).total);
+}
+
+// Shared by ss2d_fwd / ss2d_bwd: transpose x into the workspace and run the route scans with
+// outputs (fp32, route order) into the ys region; optionally keep every checkpoint state.
+static int ss2d_forward_scans(const ss2d_fwd_args* a, const SS2DLayout& lay, bool keep_states, hipStream_t stream) {
+  const int64_t L = a->height * a->width;
+  const int e = esize(a->dtype);
+  void* xT = at(a->workspace, lay.off_xT);
+  ScanOutputs o{};
+  o.out[1] = xT;
+  o.batch_stride = a->dim * L;
+  hipError_t err = launch_route_scatter(a->x, o, a->batch, a->dim, a->height, a->width, e, stream);
+  if (err != hipSuccess) return SS2D_ERR_HIP;
+
+  ScanFwdParams p{};
+  p.u = a->x;
+  p.uT = xT;
+  p.delta = a->delta;
+  p.A = a->A;
+  p.Bm = a->Bm;
+  p.Cm = a->Cm;
+  p.delta_bias = a->delta_bias;
+  p.out = at(a->workspace, lay.off_ys);
+  p.batch = a->batch;
+  p.dim = 4 * a->dim;
+  p.L = L;
+  p.G = 4;
+  p.per_group = a->dim;
+  p.dblocks = lay.scan.dblocks;
+  p.n_ckpt = int(lay.scan.n_ckpt);
+  p.N = int(a->dstate);
+  p.softplus = a->delta_softplus ? 1 : 0;
+  p.ss2d = 1;
+  p.dtype = a->dtype;
+  p.vec = (L % 4 == 0) && vec_aligned(a->dtype, {a->x, a->delta, a->Bm, a->Cm});
+  plan_chunks(a->batch * 4 * lay.scan.dblocks, L, true, &p.chunk_len, &p.n_chunks);
+  if (a->batch * 4 * lay.scan.dblocks * p.n_chunks > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
+  p.chunk_sum = reinterpret_cast<float*>(at(a->workspace, lay.off_scan + lay.scan.off_sum));
+  if (p.n_chunks > 1 || keep_states) p.ckpt = reinterpret_cast<float*>(at(a->workspace, lay.off_scan + lay.scan.off_ckpt));
+  if (p.n_chunks > 1) {
+    p.pass = 1;
+    err = launch_scan_fwd(p, stream);
+    if (err == hipSuccess) err = launch_chunk_combine(p, stream);
+    if (err != hipSuccess) return SS2D_ERR_HIP;
+  }
+  p.pass = 0;
+  return status_from(launch_scan_fwd(p, stream));
+}
+
+static int check_ss2d(int64_t batch, int64_t dim, int64_t height, int64_t width, int64_t dstate, int dtype) {
+  if (!dtype_ok(dtype)) return SS2D_ERR_UNSUPPORTED;
+  if (batch < 0 || dim < 0 || height < 0 || width < 0) return SS2D_ERR_INVALID_ARGUMENT;
+  if (dstate < 1 || dstate > 64) return SS2D_ERR_UNSUPPORTED;
+  if (height > (1 << 30) || width > (1 << 30)) return SS2D_ERR_INVALID_ARGUMENT;
+  return SS2D_OK;
+}
+
+int ss2d_fwd(const ss2d_fwd_args* a, hipStream_t stream) {
+  if (!a) return SS2D_ERR_INVALID_ARGUMENT;
+  int st = check_ss2d(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype);
+  if (st != SS2D_OK) return st;
+  const int64_t L = a->height * a->width;
+  if (a->batch * a->dim * L == 0) return SS2D_OK;
+  if (!a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->out || !a->workspace) return SS2D_ERR_INVALID_ARGUMENT;
+  if (!elem_aligned(a->dtype, {a->x, a->delta, a->Bm, a->Cm, a->z, a->out})) return SS2D_ERR_INVALID_ARGUMENT;
+  if (!aligned(a->A, 4) || (a->Dskip && !aligned(a->Dskip, 4)) || (a->delta_bias && !aligned(a->delta_bias, 4)))
+    return SS2D_ERR_INVALID_ARGUMENT;
+  const SS2DLayout lay = ss2d_layout(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype);
+  if (a->workspace_bytes < size_t(lay.total) || !aligned(a->workspace, kAlign)) return SS2D_ERR_INVALID_ARGUMENT;
+  if (a->batch * a->dim * cdiv(a->height, 32) * cdiv(a->width, 32) > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
+  st = ss2d_forward_scans(a, lay, false, stream);
+  if (st != SS2D_OK) return st;
+  MergeArgs m{};
+  m.routes = at(a->workspace, lay.off_ys);
+  m.routes_f32 = 1;
+  m.x = a->x;
+  m.Dskip = a->Dskip;
+  m.z = a->z;
+  m.y = a->out;
+  m.batch = a->batch;
+  m.C = a->dim;
+  m.H = a->height;
+  m.W = a->width;
+  m.dtype = a->dtype;
+  return status_from(launch_merge(m, stream));
+}
+
+int selective_scan_bwd(const ss_bwd_args* a, hipStream_t stream) {
+  (void)a;
+  (void)stream;
+  return SS2D_ERR_UNSUPPORTED;
+}
+
+int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
+  (void)a;
+  (void)stream;
+  return SS2D_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

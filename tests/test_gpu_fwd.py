@@ -1,0 +1,164 @@
+"""GPU parity of the forward path against the fp64 oracle (HIP kernels via the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_scan_amd as ss
+from gpu_util import TOL, f64, rel_err, random_bits, to_dev, to_f64
+from selective_scan_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits_equal(got_t, ref_np, dtype):
+    if dtype == "bf16":
+        got = got_t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return np.array_equal(got, ref_np)
+    got = got_t.cpu().numpy().view(np.uint32)
+    return np.array_equal(got, ref_np.view(np.uint32))
+
+
+SCAN_SHAPES = [(1, 3, 8, 8), (2, 5, 7, 9), (1, 2, 56, 56), (1, 1, 1, 1), (2, 3, 1, 13), (1, 2, 33, 65),
+               (3, 4, 14, 14)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SCAN_SHAPES)
+def test_cross_scan_bit_exact(dtype, shape):
+    x = random_bits(shape, dtype, seed=sum(shape))
+    xs = ss.ss2d_cross_scan(to_dev(x, dtype))
+    torch.cuda.synchronize()
+    assert _bits_equal(xs, oracle.cross_scan(x), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SCAN_SHAPES)
+def test_cross_merge_bit_exact(dtype, shape):
+    B, C, H, W = shape
+    rng = np.random.default_rng(sum(shape) + 1)
+    lim = 64 if dtype == "bf16" else 1 << 20  # every partial sum is exact in the storage type
+    ys = rng.integers(-lim, lim + 1, size=(B, 4, C, H * W)).astype(np.float32)
+    ys_st = synth.f32_to_bf16_bits(ys) if dtype == "bf16" else ys
+    y = ss.ss2d_cross_merge(to_dev(ys_st, dtype), H, W)
+    ref = oracle.cross_merge(ys.astype(np.float64), H, W)
+    np.testing.assert_array_equal(to_f64(y), ref)
+    # merge of scan is 4 x identity on any finite input
+    x = rng.integers(-lim // 4, lim // 4 + 1, size=shape).astype(np.float32)
+    x_st = synth.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    y2 = ss.ss2d_cross_merge(ss.ss2d_cross_scan(to_dev(x_st, dtype)), H, W)
+    np.testing.assert_array_equal(to_f64(y2), 4.0 * x)
+
+
+def _scan_case(batch, dim, N, L, G, dtype, has_z, has_D, has_bias, softplus, seed):
+    inp = synth.make_ss_inputs(batch, dim, N, L, G, dtype, has_z=has_z, seed_base=seed)
+    if not softplus:  # the raw delta is the step itself: keep it positive (|delta|, sign bit cleared)
+        inp["delta"] = (inp["delta"] & np.uint16(0x7FFF)) if dtype == "bf16" else np.abs(inp["delta"])
+    A = inp["A"] * np.float32(0.5 + np.random.default_rng(seed).random((dim, 1)))  # vary decay per channel
+    dev = dict(u=to_dev(inp["u"], dtype), delta=to_dev(inp["delta"], dtype), A=to_dev(A, "f32"),
+               B=to_dev(inp["B"], dtype), C=to_dev(inp["C"], dtype),
+               D=to_dev(inp["D"] * np.float32(0.7), "f32") if has_D else None,
+               z=to_dev(inp["z"], dtype) if has_z else None,
+               delta_bias=to_dev(inp["delta_bias"], "f32") if has_bias else None)
+    ref = dict(u=f64(inp["u"], dtype), delta=f64(inp["delta"], dtype), A=A.astype(np.float64),
+               B=f64(inp["B"], dtype), C=f64(inp["C"], dtype),
+               D=(inp["D"] * np.float32(0.7)).astype(np.float64) if has_D else None,
+               z=f64(inp["z"], dtype) if has_z else None,
+               delta_bias=inp["delta_bias"].astype(np.float64) if has_bias else None)
+    return dev, ref
+
+
+SS_CASES = [
+    # batch, dim, N, L, G, dtype, z, D, bias, softplus
+    (2, 64, 16, 256, 1, "f32", True, True, True, True),
+    (2, 96, 16, 200, 2, "bf16", True, True, True, True),     # partial wave, ragged tile
+    (1, 70, 4, 129, 1, "f32", False, True, False, True),     # L % 4 != 0: scalar path
+    (3, 32, 1, 500, 4, "bf16", False, False, True, True),
+    (1, 16, 3, 77, 1, "f32", True, False, False, False),     # N padded 3 -> 4, no softplus
+    (2, 128, 64, 96, 2, "f32", True, True, True, True),      # largest state
+    (1, 64, 8, 4096, 1, "f32", True, True, True, True),      # few rows: chunked along L
+    (1, 64, 16, 3000, 2, "bf16", True, True, True, True),    # chunked, ragged
+    (2, 8, 32, 1, 1, "f32", True, True, True, True),         # L = 1
+]
+
+
+@pytest.mark.parametrize("ci", range(len(SS_CASES)), ids=[str(c[:6]) for c in SS_CASES])
+def test_selective_scan_fwd(ci):
+    batch, dim, N, L, G, dtype, z, D, bias, sp = SS_CASES[ci]
+    dev, ref = _scan_case(batch, dim, N, L, G, dtype, z, D, bias, sp, seed=100 + ci)
+    out, last = ss.selective_scan_fwd(**dev, delta_softplus=sp, return_last_state=True)
+    r_out, r_last = oracle.ss_fwd(**ref, delta_softplus=sp, return_last_state=True)
+    assert rel_err(to_f64(out), r_out) <= TOL[dtype]
+    assert rel_err(to_f64(last), r_last) <= TOL[dtype]
+
+
+def _ss2d_dev_ref(inp, dtype, has_z=True):
+    dev = dict(x=to_dev(inp["x"], dtype), delta=to_dev(inp["delta"], dtype), A=to_dev(inp["A"], "f32"),
+               B=to_dev(inp["B"], dtype), C=to_dev(inp["C"], dtype), D=to_dev(inp["D"], "f32"),
+               delta_bias=to_dev(inp["delta_bias"], "f32"), z=to_dev(inp["z"], dtype) if has_z else None)
+    ref = dict(x=f64(inp["x"], dtype), delta=f64(inp["delta"], dtype), A=inp["A"].astype(np.float64),
+               B=f64(inp["B"], dtype), C=f64(inp["C"], dtype), D=inp["D"].astype(np.float64),
+               delta_bias=inp["delta_bias"].astype(np.float64), z=f64(inp["z"], dtype) if has_z else None)
+    return dev, ref
+
+
+SS2D_CASES = [
+    # batch, H, W, dim, N, dtype, z
+    (1, 8, 8, 16, 4, "f32", True),
+    (2, 7, 9, 20, 16, "f32", True),     # H != W, L % 4 != 0
+    (2, 14, 14, 70, 16, "bf16", True),  # L = 196, D not a multiple of 64
+    (1, 56, 56, 64, 1, "bf16", False),
+    (1, 1, 1, 8, 4, "f32", True),       # single pixel
+    (1, 3, 40, 64, 8, "bf16", True),
+    (1, 64, 64, 64, 16, "f32", True),   # few rows: chunked
+]
+
+
+@pytest.mark.parametrize("case", SS2D_CASES, ids=[str(c) for c in SS2D_CASES])
+def test_ss2d_fwd(case):
+    batch, H, W, dim, N, dtype, z = case
+    inp = synth.make_ss2d_inputs(batch, H, W, dim, N, dtype, has_z=z, seed_base=7 + H + W)
+    dev, ref = _ss2d_dev_ref(inp, dtype, z)
+    out = ss.ss2d_fwd(**dev)
+    assert rel_err(to_f64(out), oracle.ss2d_fwd(**ref)) <= TOL[dtype]
+
+
+def test_ss2d_fwd_tiny_config():
+    cfg = synth.CONFIGS[0]
+    inp = synth.make_config_inputs(cfg)
+    dev, ref = _ss2d_dev_ref(inp, cfg.dtype, cfg.has_z)
+    out = ss.ss2d_fwd(**dev)
+    assert rel_err(to_f64(out), oracle.ss2d_fwd(**ref)) <= TOL[cfg.dtype]
+
+
+def _slice_ref(ref, b, d):
+    """Inputs of the single plane (b, d): rows are independent, so this is itself a valid SS2D input."""
+    return dict(x=ref["x"][b:b + 1, d:d + 1], delta=ref["delta"][b:b + 1, :, d:d + 1], A=ref["A"][:, d:d + 1],
+                B=ref["B"][b:b + 1], C=ref["C"][b:b + 1], D=ref["D"][:, d:d + 1],
+                delta_bias=ref["delta_bias"][:, d:d + 1],
+                z=None if ref["z"] is None else ref["z"][b:b + 1, d:d + 1])
+
+
+@pytest.mark.parametrize("cfg_index", [1, 2, 3, 4])
+def test_ss2d_fwd_full_config_sampled(cfg_index):
+    """Full-size run in the benchmark's launch configuration; oracle on sampled planes."""
+    cfg = synth.CONFIGS[cfg_index]
+    inp = synth.make_config_inputs(cfg, with_dout=False)
+    dev = dict(x=to_dev(inp["x"], cfg.dtype), delta=to_dev(inp["delta"], cfg.dtype), A=to_dev(inp["A"], "f32"),
+               B=to_dev(inp["B"], cfg.dtype), C=to_dev(inp["C"], cfg.dtype), D=to_dev(inp["D"], "f32"),
+               delta_bias=to_dev(inp["delta_bias"], "f32"), z=to_dev(inp["z"], cfg.dtype) if cfg.has_z else None)
+    out = ss.ss2d_fwd(**dev)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(cfg_index)
+    planes = [(0, 0), (cfg.batch - 1, cfg.dim - 1)] + [
+        (int(rng.integers(cfg.batch)), int(rng.integers(cfg.dim))) for _ in range(4)]
+    ref_full = dict(x=inp["x"], delta=inp["delta"], A=inp["A"], B=inp["B"], C=inp["C"], D=inp["D"],
+                    delta_bias=inp["delta_bias"], z=inp["z"])
+    for b, d in planes:
+        sl = _slice_ref(ref_full, b, d)
+        sl = {k: (None if v is None else (v.astype(np.float64) if k in ("A", "D", "delta_bias")
+                                         else synth.storage_to_f64(v, cfg.dtype))) for k, v in sl.items()}
+        r = oracle.ss2d_fwd(**sl)
+        g = to_f64(out[b:b + 1, d:d + 1])
+        assert rel_err(g, r) <= TOL[cfg.dtype], (b, d)
+    assert torch.isfinite(out.float()).all()
