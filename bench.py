@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Benchmark of the SS2D hot path on one MI355X.
+
+One step = one fused SS2D forward (cross-scan addressing -> four selective scans ->
+cross-merge + skip + gate) over one batch of the stage-1 VMamba workload (batch 128,
+56x56 map, D = 192 channels, N = 16 states, bf16 I/O, fp32 state, z gate).  Inputs are
+seeded synthetic tensors already resident in HBM when the timed region starts.
+
+Prints one JSON line: elements/s (B*K*D*L per second) as the value, the whole-step
+algorithmic HBM rate, the roofline of the dominant kernel (the route-scan kernel, timed
+live with HIP events on the launch stream) and the fp64 CPU oracle timed on this host on
+a bounded sample of the same workload.  `--workload` selects one of the other shapes
+(used for profiling); `--bwd` adds the fused backward to each step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SS2D scan elements/s (B·K·D·L) + achieved HBM GB/s vs peak, 56×56 stage"
+HBM_PEAK_GBPS = 8000.0
+# fp32 vector peak without packed instructions: 256 CUs x 64 lanes x 2 flops (FMA) x 2.4 GHz
+VALU_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
+FLOPS_PER_STATE_STEP = 7  # exp(delta*A): mul + exp; delta*u*B: mul; h = a*h + b: fma; y += C*h: fma
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=1, help="index into synth.CONFIGS (default: stage-1)")
+    ap.add_argument("--bwd", action="store_true", help="time forward + backward per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time for the sample")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(cfg, bwd=False):
+    """Each tensor read once and each output written once (the fused minimum)."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    grid = cfg.batch * cfg.dim * cfg.seqlen
+    seq = cfg.batch * 4 * cfg.dim * cfg.seqlen
+    bc = 2 * cfg.batch * 4 * cfg.dstate * cfg.seqlen
+    fwd = e * (grid + seq + bc + (grid if cfg.has_z else 0) + grid)
+    if not bwd:
+        return fwd
+    # backward: reads x, delta, B, C, z, dout; writes dx, ddelta, dB, dC, dz
+    return fwd + e * (grid + grid + seq + bc + (grid if cfg.has_z else 0))
+
+
+def scan_kernel_source_hash():
+    h = hashlib.sha256()
+    for name in ("scan_fwd_kernel.h", "device_common.h"):
+        with open(os.path.join(ROOT, "selective_scan_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_name):
+    """HBM traffic of the scan kernel from the committed rocprofv3 counter summary, or None
+    when that summary was taken on a different version of the kernel source."""
+    path = os.path.join(ROOT, "profiles", "scan_fwd_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    entry = rec.get(workload_name)
+    if not entry or entry.get("kernel_source_sha") != scan_kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, target_s):
+    """The fp64 oracle (as it stands) on the first images of the same batch."""
+    import oracle
+    from selective_scan_amd import synth
+
+    def run(nb):
+        sl = lambda a: None if a is None else synth.storage_to_f64(a[:nb], cfg.dtype)
+        t0 = time.perf_counter()
+        oracle.ss2d_fwd(sl(inp["x"]), sl(inp["delta"]), inp["A"].astype(np.float64), sl(inp["B"]), sl(inp["C"]),
+                        inp["D"].astype(np.float64), inp["delta_bias"].astype(np.float64), sl(inp["z"]))
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    nb = int(max(1, min(cfg.batch, round(target_s / max(t1, 1e-3)))))
+    t = run(nb) if nb > 1 else t1
+    elems = nb * 4 * cfg.dim * cfg.seqlen
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {"value": elems / t, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {nb} of {cfg.batch} images (all {cfg.dim} channels, 4 routes, "
+                      f"L={cfg.seqlen}, N={cfg.dstate}), fp64 C oracle with OpenMP, {t:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every box here has a single "
+              f"MI355X and no multi-GPU path is part of this library.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import selective_scan_amd as ss
+    from selective_scan_amd import synth
+
+    cfg = synth.CONFIGS[args.workload]
+    inp = synth.make_config_inputs(cfg, with_dout=args.bwd)
+
+    def dev(a, dtype):
+        if a is None:
+            return None
+        if dtype == "bf16" and a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+    d = dict(x=dev(inp["x"], cfg.dtype), delta=dev(inp["delta"], cfg.dtype), A=dev(inp["A"], "f32"),
+             B=dev(inp["B"], cfg.dtype), C=dev(inp["C"], cfg.dtype), D=dev(inp["D"], "f32"),
+             delta_bias=dev(inp["delta_bias"], "f32"), z=dev(inp["z"], cfg.dtype) if cfg.has_z else None)
+    dout = dev(inp["dout"], cfg.dtype) if args.bwd else None
+    plan = ss.SS2DForwardPlan(**d)
+    stream = torch.cuda.current_stream()
+
+    def step(ev_scan=None):
+        plan.run_stage(0)
+        if ev_scan is not None:
+            ev_scan[0].record(stream)
+        plan.run_stage(1)
+        if ev_scan is not None:
+            ev_scan[1].record(stream)
+        plan.run_stage(2)
+        if args.bwd:
+            ss.ss2d_bwd(**d, dout=dout, workspace=plan.workspace)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    scan_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(scan_ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+    scan_ms = float(np.mean([a.elapsed_time(b) for a, b in scan_ev]))
+
+    elements = cfg.elements
+    step_bytes = algorithmic_bytes(cfg, args.bwd)
+    flops = elements * cfg.dstate * FLOPS_PER_STATE_STEP
+    achieved_tflops = flops / (scan_ms * 1e-3) / 1e12
+    traffic = load_traffic(cfg.name)
+    res = {
+        "metric": METRIC,
+        "value": elements / (ms * 1e-3),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) inputs, S4D-real A, inverse-softplus dt bias)",
+        "config": {"workload": ("ss2d_fwd+bwd " if args.bwd else "ss2d_fwd ") + cfg.name,
+                   "batch": cfg.batch, "height": cfg.height, "width": cfg.width, "routes": 4,
+                   "dim": cfg.dim, "dstate": cfg.dstate, "gate_z": cfg.has_z},
+        "hbm": {"algorithmic_bytes_per_step": step_bytes,
+                "achieved_GBps": step_bytes / (ms * 1e-3) / 1e9,
+                "peak_GBps": HBM_PEAK_GBPS,
+                "frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+        "roofline": {"kernel": "route scan (scan_fwd_kernel)", "bound": "alu",
+                     "achieved": achieved_tflops, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved_tflops / VALU_PEAK_TFLOPS, "traffic": traffic,
+                     "ms_per_launch": scan_ms, "flops_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

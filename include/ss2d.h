@@ -195,6 +195,17 @@ typedef struct ss2d_fwd_args {
 
 int ss2d_fwd(const ss2d_fwd_args* args, hipStream_t stream);
 
+/* One stage of ss2d_fwd, for callers that time or overlap the stages separately.
+ * ss2d_fwd(args) == stage 0, then 1, then 2 on the same workspace:
+ *   stage 0 (SS2D_STAGE_TRANSPOSE): per-plane transpose of x into the workspace (feeds the
+ *                                   column-major routes);
+ *   stage 1 (SS2D_STAGE_SCAN):      the four route scans, fp32 route outputs into the workspace;
+ *   stage 2 (SS2D_STAGE_MERGE):     cross-merge + skip term + gate into `out`.
+ * A stage reads what the earlier stages left in the workspace; any other stage value is
+ * SS2D_ERR_INVALID_ARGUMENT. */
+enum { SS2D_STAGE_TRANSPOSE = 0, SS2D_STAGE_SCAN = 1, SS2D_STAGE_MERGE = 2 };
+int ss2d_fwd_stage(const ss2d_fwd_args* args, int stage, hipStream_t stream);
+
 /* Backward of ss2d_fwd: given dout (batch, dim, height, width), writes
  *   dx, dz     : (batch, dim, height, width)  dtype  (dz iff z != NULL)
  *   ddelta     : (batch, 4, dim, L) dtype (w.r.t. the raw delta);

@@ -6,6 +6,7 @@ is the thin Python binding over that ABI; its functions carry the C entry points
 """
 from ._binding import (  # noqa: F401
     SS2DError,
+    SS2DForwardPlan,
     lib,
     selective_scan_bwd,
     selective_scan_fwd,

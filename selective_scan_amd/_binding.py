@@ -75,6 +75,8 @@ def lib():
         L.selective_scan_workspace_bytes.argtypes = [_i64] * 5
         L.ss2d_workspace_bytes.restype = _sz
         L.ss2d_workspace_bytes.argtypes = [_i64] * 5 + [_int]
+        L.ss2d_fwd_stage.restype = _int
+        L.ss2d_fwd_stage.argtypes = [ctypes.POINTER(SS2DFwdArgs), _int, _p]
         for name, st in (("selective_scan_fwd", SsFwdArgs), ("selective_scan_bwd", SsBwdArgs),
                          ("ss2d_fwd", SS2DFwdArgs), ("ss2d_bwd", SS2DBwdArgs)):
             f = getattr(L, name)
@@ -249,6 +251,39 @@ def ss2d_fwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=
                     dstate=N, dtype=_dtype_code(x.dtype), delta_softplus=int(bool(delta_softplus)))
     _check(lib().ss2d_fwd(ctypes.byref(a), _stream(dev)), "ss2d_fwd")
     return out
+
+
+class SS2DForwardPlan:
+    """A prepared ss2d_fwd call: argument block, workspace and output kept alive, so that
+    repeated launches (benchmarks, stage timing) cost one ctypes call each."""
+
+    def __init__(self, x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=True, workspace=None,
+                 out=None):
+        x, delta = _c(x), _c(delta)
+        self.device = _dev(x)
+        B, C, z = _c(B), _c(C), _c(z)
+        A = _c(A, torch.float32)
+        D = _c(D, torch.float32)
+        delta_bias = _c(delta_bias, torch.float32)
+        batch, dim, H, W = x.shape
+        N = A.shape[-1]
+        self.out = torch.empty_like(x) if out is None else out
+        self.workspace = _workspace(ss2d_workspace_bytes(batch, dim, H, W, N, x.dtype), self.device, workspace)
+        self._keep = (x, delta, A, B, C, D, delta_bias, z)
+        self.args = SS2DFwdArgs(x=_ptr(x), delta=_ptr(delta), A=_ptr(A), Bm=_ptr(B), Cm=_ptr(C), Dskip=_ptr(D),
+                                delta_bias=_ptr(delta_bias), z=_ptr(z), out=_ptr(self.out),
+                                workspace=_ptr(self.workspace),
+                                workspace_bytes=self.workspace.numel() * self.workspace.element_size(),
+                                batch=batch, dim=dim, height=H, width=W, dstate=N, dtype=_dtype_code(x.dtype),
+                                delta_softplus=int(bool(delta_softplus)))
+
+    def run(self):
+        _check(lib().ss2d_fwd(ctypes.byref(self.args), _stream(self.device)), "ss2d_fwd")
+        return self.out
+
+    def run_stage(self, stage: int):
+        _check(lib().ss2d_fwd_stage(ctypes.byref(self.args), int(stage), _stream(self.device)), "ss2d_fwd_stage")
+        return self.out
 
 
 def ss2d_bwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, dout=None, delta_softplus=True,

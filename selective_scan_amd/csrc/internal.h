@@ -7,7 +7,13 @@
 namespace ss2d {
 
 constexpr int kTile = 32;  // time steps staged per tile
-constexpr int kCkpt = 64;  // the scan state is checkpointed before every kCkpt-th step
+
+// State counts are padded to one of 1, 4, 8, 16, 32, 64 (extra states have zero B/C).
+inline int padded_states(int64_t n) { return n <= 1 ? 1 : n <= 4 ? 4 : n <= 8 ? 8 : n <= 16 ? 16 : n <= 32 ? 32 : 64; }
+// The scan state is checkpointed before every ckpt_steps(NS)-th step: NS * ckpt_steps = 128 floats
+// per lane (32 for NS = 1), the states the backward recomputes and holds in registers at a time.
+// Always a divisor of kTile.
+constexpr int ckpt_steps(int ns) { return ns >= 64 ? 2 : ns >= 32 ? 4 : ns >= 16 ? 8 : ns >= 8 ? 16 : 32; }
 
 // ---- permutations (permute_kernels.hip) ----------------------------------------------
 // Scatter one map (batch, C, H, W) into up to four route-ordered outputs.
@@ -74,6 +80,7 @@ struct ScanFwdParams {
   float* chunk_sum;    // (batch*dim, n_chunks) or null
   int64_t batch, dim, L, G, per_group, dblocks, chunk_len;
   int n_chunks, n_ckpt, N;
+  int ckpt_every;      // ckpt_steps(padded_states(N))
   int softplus;
   int ss2d;            // rows follow the SS2D routes (G = 4, per_group = D)
   int dtype;

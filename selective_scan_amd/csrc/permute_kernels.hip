@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a, int tiles_h, in
       if (a.Dskip && xg) v = fmaf(dsum, Elem<T>::load(xg, plane + p), v);
       if (a.merged_f32) a.merged_f32[plane + p] = v;
       if (zg) v *= silu(Elem<T>::load(zg, plane + p));
-      Elem<T>::store(yg, plane + p, v);
+      if (yg) Elem<T>::store(yg, plane + p, v);
     }
   }
 }

@@ -1,0 +1,106 @@
+// Selective scan backward: dispatch over (dtype, state count), the chunk combine of the adjoint,
+// and the kernel that adds the per-block / per-chunk partial sums into dA, dD, ddelta_bias, dB, dC.
+#include "device_common.h"
+#include "internal.h"
+
+namespace ss2d {
+
+template <typename T, int NS>
+hipError_t scan_bwd_launch(const ScanBwdParams& p, hipStream_t s);
+
+namespace {
+
+// One thread per (row, state): walk the chunks from the last to the first.  On entry
+// lam_carry[row][c] is chunk c's adjoint at its start computed from zero; on exit it is the
+// adjoint flowing into chunk c from all later chunks.
+__global__ __launch_bounds__(256) void lambda_combine_kernel(const ScanBwdParams p) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t rows = p.batch * p.dim;
+  if (i >= rows * p.N) return;
+  const int64_t row = i / p.N;
+  const int n = int(i % p.N);
+  const float A = p.A[(row % p.dim) * p.N + n];
+  float m = 0.0f;
+  for (int c = p.n_chunks - 1; c >= 0; --c) {
+    float* slot = p.lam_carry + (row * p.n_chunks + c) * p.N + n;
+    const float loc = *slot;
+    *slot = m;
+    m = fmaf(fast_exp2(A * p.chunk_sum[row * p.n_chunks + c]), m, loc);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void reduce_bc_kernel(const BwdReduceArgs a) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t per_block = a.batch * a.G * a.N * a.L;
+  if (i >= per_block) return;
+  float sb = 0.0f, sc = 0.0f;
+  for (int64_t k = 0; k < a.dblocks; ++k) {
+    sb += a.dB_part[k * per_block + i];
+    sc += a.dC_part[k * per_block + i];
+  }
+  Elem<T>::store(static_cast<T*>(a.dB), i, sb * kLn2);  // dB terms were formed with delta / ln 2
+  Elem<T>::store(static_cast<T*>(a.dC), i, sc);
+}
+
+__global__ __launch_bounds__(256) void reduce_params_kernel(const BwdReduceArgs a) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t rows = a.batch * a.dim;
+  if (i < a.dim * a.N) {
+    const int64_t d = i / a.N, n = i % a.N;
+    float s = 0.0f;
+    for (int c = 0; c < a.n_chunks; ++c)
+      for (int64_t b = 0; b < a.batch; ++b) s += a.dA_part[(int64_t(c) * rows + b * a.dim + d) * a.N + n];
+    a.dA[i] = s * kLn2;  // dA terms were formed with delta / ln 2
+  } else if (i < a.dim * a.N + a.dim) {
+    const int64_t d = i - a.dim * a.N;
+    float sd = 0.0f, sb = 0.0f;
+    for (int c = 0; c < a.n_chunks; ++c)
+      for (int64_t b = 0; b < a.batch; ++b) {
+        sd += a.dD_part[int64_t(c) * rows + b * a.dim + d];
+        sb += a.dbias_part[int64_t(c) * rows + b * a.dim + d];
+      }
+    if (a.dD) a.dD[d] = sd;
+    if (a.dbias) a.dbias[d] = sb;
+  }
+}
+
+template <typename T>
+hipError_t launch_dtype(const ScanBwdParams& p, hipStream_t s) {
+  if (p.N <= 1) return scan_bwd_launch<T, 1>(p, s);
+  if (p.N <= 4) return scan_bwd_launch<T, 4>(p, s);
+  if (p.N <= 8) return scan_bwd_launch<T, 8>(p, s);
+  if (p.N <= 16) return scan_bwd_launch<T, 16>(p, s);
+  if (p.N <= 32) return scan_bwd_launch<T, 32>(p, s);
+  return scan_bwd_launch<T, 64>(p, s);
+}
+
+}  // namespace
+
+hipError_t launch_scan_bwd(const ScanBwdParams& p, hipStream_t s) {
+  return p.dtype == 0 ? launch_dtype<float>(p, s) : launch_dtype<bf16>(p, s);
+}
+
+hipError_t launch_lambda_combine(const ScanBwdParams& p, hipStream_t s) {
+  const int64_t n = p.batch * p.dim * p.N;
+  if (n == 0) return hipSuccess;
+  lambda_combine_kernel<<<dim3(uint32_t((n + 255) / 256)), dim3(256), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_reduce(const BwdReduceArgs& a, hipStream_t s) {
+  const int64_t nbc = a.batch * a.G * a.N * a.L;
+  if (nbc > 0) {
+    if (a.dtype == 0)
+      reduce_bc_kernel<float><<<dim3(uint32_t((nbc + 255) / 256)), dim3(256), 0, s>>>(a);
+    else
+      reduce_bc_kernel<bf16><<<dim3(uint32_t((nbc + 255) / 256)), dim3(256), 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t np = a.dim * a.N + a.dim;
+  if (np > 0) reduce_params_kernel<<<dim3(uint32_t((np + 255) / 256)), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace ss2d

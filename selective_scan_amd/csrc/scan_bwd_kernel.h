@@ -1,0 +1,321 @@
+// Selective scan S6, backward kernel (included by the scan_bwd_inst_*.hip instantiations).
+//
+// Gradient of the forward of `selective_scan_ref` ("Vision Mamba structure and principle"
+// page, section 2), with the outputs of `SelectiveScanFn.backward` on the same page.  Per row,
+// with a_t = exp(delta_t A), dy_t = dL/dy_t (dout * silu(z_t) when gated):
+//   lambda_t = C_t dy_t + a_{t+1} lambda_{t+1}                   (adjoint of h_t, lambda_L = 0)
+//   du_t     = delta_t <lambda_t, B_t> + D dy_t
+//   ddelta_t = <lambda_t, A a_t h_{t-1} + B_t u_t>   (then * sigmoid(v_t) through the softplus)
+//   dA      += lambda_t a_t h_{t-1} delta_t,  dB_t += lambda_t delta_t u_t,  dC_t += dy_t h_t,
+//   dD      += dy_t u_t,                      dz_t  = dout_t (y_t + D u_t) silu'(z_t)
+// (dB, dC summed over the channels of a group; dA, dD, ddelta_bias over batch and time).
+//
+// Mapping: as in the forward, one wavefront = 64 channels of one (batch, group); lane = row.
+// A row is walked backwards in 32-step tiles; a tile is cut into sub-intervals of kSub steps
+// whose start states were checkpointed by the forward.  For each sub-interval the states are
+// recomputed forwards into registers (kSub x NS floats), then the adjoint recurrence runs
+// backwards over them.  The per-(step, state) terms of dB and dC are summed over the 64 lanes
+// with a transpose-reduce (halving exchanges across lanes), so every lane ends up owning a
+// slice of the (step, state) sums, which it writes once per 64-channel block; a small kernel
+// adds the blocks.  When rows are few, the sequence is split into chunks: pass 1 runs the
+// adjoint recurrence of each chunk from zero, a combine kernel chains the chunks, and pass 0
+// starts every chunk from the true carried adjoint.
+#pragma once
+#include <type_traits>
+
+#include "scan_common.h"
+
+namespace ss2d {
+namespace bwd_detail {
+using namespace scan_detail;
+
+// Sum V values per lane over the 64 lanes of the wavefront.  On return lane l holds, in
+// v[0 .. V/64), the totals of original indices l*(V/64) + r (V >= 64); for V = 32 every lane
+// holds the total of index l >> 1 in v[0].
+template <int V>
+__device__ __forceinline__ void lane_transpose_reduce(float* v, int lane) {
+  static_assert(V == 32 || V == 128 || V == 64, "unsupported reduce width");
+  int cnt = V;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    if (cnt > 1) {
+      const bool upper = (lane & m) != 0;
+      const int half = cnt / 2;
+#pragma unroll
+      for (int k = 0; k < V / 2; ++k) {
+        if (k < half) {
+          const float lo = v[k], hi = v[k + half];
+          const float send = upper ? lo : hi;
+          const float keep = upper ? hi : lo;
+          v[k] = keep + __shfl_xor(send, m, kWave);
+        }
+      }
+      cnt = half;
+    } else {
+      v[0] += __shfl_xor(v[0], m, kWave);
+    }
+  }
+}
+
+template <typename T, int NS, bool kSS2D, bool kVec, int kPass>
+__global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) {
+  using DT = typename std::conditional<kSS2D, float, T>::type;  // type of dout rows
+  constexpr int S = (NS < 4) ? 4 : NS + 4;
+  constexpr int kSub = ckpt_steps(NS);
+  constexpr int kRW = (2 * NS < 32) ? 32 : 2 * NS;  // width of the per-step dB/dC lane reduction
+  constexpr int kInner = (64 / NS < kSub) ? 64 / NS : kSub;  // steps whose states are held at once
+  __shared__ __align__(16) float sB[kTile * S];
+  __shared__ __align__(16) float sC[kTile * S];
+
+  const int lane = threadIdx.x;
+  int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t dblk = bid % p.dblocks;
+  bid /= p.dblocks;
+  const int c = int(bid % p.n_chunks);
+  bid /= p.n_chunks;
+  const int64_t g = bid % p.G;
+  const int64_t b = bid / p.G;
+  const int64_t dg = dblk * kWave + lane;
+  const bool active = dg < p.per_group;
+  const int64_t dl = active ? dg : 0;
+  const int64_t d = g * p.per_group + dl;
+  const int64_t row = b * p.dim + d;
+  const int64_t L = p.L;
+  const int N = p.N;
+
+  const T* delta_row = static_cast<const T*>(p.delta) + row * L;
+  const T* u_row;
+  const DT* dout_row;
+  bool rev = false;
+  if (kSS2D) {
+    const int64_t plane = (b * p.per_group + dl) * L;
+    u_row = ((g & 1) ? static_cast<const T*>(p.uT) : static_cast<const T*>(p.u)) + plane;
+    dout_row = ((g & 1) ? static_cast<const DT*>(p.doutT) : static_cast<const DT*>(p.dout)) + plane;
+    rev = g >= 2;
+  } else {
+    u_row = static_cast<const T*>(p.u) + row * L;
+    dout_row = static_cast<const DT*>(p.dout) + row * L;
+  }
+  const bool has_z = !kSS2D && p.z != nullptr;
+  const T* z_row = has_z ? static_cast<const T*>(p.z) + row * L : nullptr;
+  const T* Bg = static_cast<const T*>(p.Bm) + (b * p.G + g) * N * L;
+  const T* Cg = static_cast<const T*>(p.Cm) + (b * p.G + g) * N * L;
+
+  float Acoef[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) Acoef[n] = (n < N) ? p.A[d * N + n] : 0.0f;
+  const float bias = p.delta_bias ? p.delta_bias[d] : 0.0f;
+  const float Dd = p.Dskip ? p.Dskip[d] : 0.0f;
+
+  const int64_t t_begin = int64_t(c) * p.chunk_len;
+  const int64_t t_end = (t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L;
+  const int64_t n_tiles = (t_end - t_begin + kTile - 1) / kTile;
+
+  // mu = a_{t+1} lambda_{t+1}: the adjoint flowing into step t from later steps
+  float mu[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) mu[n] = 0.0f;
+  if (kPass == 0 && p.n_chunks > 1) {
+    const float* src = p.lam_carry + (row * p.n_chunks + c) * N;
+#pragma unroll
+    for (int n = 0; n < NS; ++n)
+      if (n < N) mu[n] = src[n];
+  }
+  float dA_acc[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) dA_acc[n] = 0.0f;
+  float dD_acc = 0.0f, dbias_acc = 0.0f, lam_sum = 0.0f;
+
+  for (int64_t jt = n_tiles - 1; jt >= 0; --jt) {
+    const int64_t t0 = t_begin + jt * kTile;
+    {
+      BCStage<T, NS, kVec> bc;
+      bc.load(Bg, Cg, N, L, t0, t_end, lane);
+      __syncthreads();
+      bc.template store<S>(sB, sC, lane);
+      __syncthreads();
+    }
+#pragma unroll 1
+    for (int q = kTile / kSub - 1; q >= 0; --q) {
+      const int64_t s0 = t0 + int64_t(q) * kSub;  // first step of this sub-interval
+      if (s0 >= t_end) continue;
+      const int ns = int((t_end - s0 < kSub) ? (t_end - s0) : kSub);
+      float dv[kSub], uv[kSub], gv[kSub], zv[kSub];
+      load_seg<T, kVec, kSub>(dv, delta_row, s0, t_end, L, false);
+      load_seg<T, kVec, kSub>(uv, u_row, s0, t_end, L, rev);
+      load_seg<DT, kVec, kSub>(gv, dout_row, s0, t_end, L, rev);
+      if (has_z) load_seg<T, kVec, kSub>(zv, z_row, s0, t_end, L, false);
+      // per-step quantities (steps past the range and inactive lanes contribute nothing)
+      float lam[kSub], dup[kSub], dy[kSub];
+#pragma unroll
+      for (int i = 0; i < kSub; ++i) {
+        const float v = dv[i] + bias;
+        float l = p.softplus ? softplus_log2(v * kLog2e) : v * kLog2e;
+        l = (i < ns) ? l : 0.0f;
+        lam[i] = l;
+        dup[i] = active ? l * uv[i] : 0.0f;
+        float gy = gv[i];
+        if (has_z) gy *= silu(zv[i]);
+        dy[i] = (active && i < ns) ? gy : 0.0f;
+      }
+      if (kPass == 0) {
+        // Start state of this sub-interval (its checkpoint).  The sub-interval is handled in
+        // pieces of kInner steps, last piece first; for each piece the states are recomputed
+        // forwards from the checkpoint and only the piece's own kInner x NS states are kept.
+        float h0[NS];
+        const float* ck = p.ckpt + (row * p.n_ckpt + s0 / kSub) * N;
+#pragma unroll
+        for (int n = 0; n < NS; ++n) h0[n] = (n < N) ? ck[n] : 0.0f;
+#pragma unroll
+        for (int pc = kSub / kInner - 1; pc >= 0; --pc) {
+          float hstart[NS];
+#pragma unroll
+          for (int n = 0; n < NS; ++n) hstart[n] = h0[n];
+#pragma unroll
+          for (int i = 0; i < pc * kInner; ++i) {
+            const float* bt = sB + (q * kSub + i) * S;
+#pragma unroll
+            for (int n = 0; n < NS; ++n) hstart[n] = fmaf(fast_exp2(lam[i] * Acoef[n]), hstart[n], dup[i] * bt[n]);
+          }
+          float hs[kInner][NS];
+#pragma unroll
+          for (int j = 0; j < kInner; ++j) {
+            const int i = pc * kInner + j;
+            const float* bt = sB + (q * kSub + i) * S;
+#pragma unroll
+            for (int n = 0; n < NS; ++n) {
+              const float hp = (j == 0) ? hstart[n] : hs[j - 1][n];
+              hs[j][n] = fmaf(fast_exp2(lam[i] * Acoef[n]), hp, dup[i] * bt[n]);
+            }
+          }
+          float o_du[kInner], o_dd[kInner], o_dz[kInner];
+          // adjoint recurrence backwards over the piece
+#pragma unroll
+          for (int j = kInner - 1; j >= 0; --j) {
+            const int i = pc * kInner + j;
+            const int idx = q * kSub + i;
+            const float* bt = sB + idx * S;
+            const float* ct = sC + idx * S;
+            // recompute the decays here instead of keeping the forward's values alive
+            float lr = lam[i];
+            asm volatile("" : "+v"(lr));
+            float sbl = 0.0f, ddt = 0.0f, yv = 0.0f;
+            float red[kRW];
+#pragma unroll
+            for (int e = 2 * NS; e < kRW; ++e) red[e] = 0.0f;
+#pragma unroll
+            for (int n = 0; n < NS; ++n) {
+              const float a = fast_exp2(lr * Acoef[n]);
+              const float l = fmaf(ct[n], dy[i], mu[n]);
+              const float hp = (j == 0) ? hstart[n] : hs[j - 1][n];
+              const float gg = l * a * hp;
+              dA_acc[n] = fmaf(gg, lam[i], dA_acc[n]);
+              ddt = fmaf(gg, Acoef[n], ddt);
+              sbl = fmaf(l, bt[n], sbl);
+              red[n] = l * dup[i];             // dB term (times ln 2, applied when the blocks are summed)
+              red[NS + n] = dy[i] * hs[j][n];  // dC term
+              if (has_z) yv = fmaf(ct[n], hs[j][n], yv);
+              mu[n] = a * l;
+            }
+            o_du[j] = fmaf(lam[i], sbl, Dd * dy[i]);
+            float dd = fmaf(uv[i] * kLog2e, sbl, ddt);  // ddelta (B was staged times ln 2)
+            if (p.softplus) dd *= sigmoid(dv[i] + bias);
+            dd = (i < ns && active) ? dd : 0.0f;
+            o_dd[j] = dd;
+            dbias_acc += dd;
+            dD_acc = fmaf(dy[i], uv[i], dD_acc);
+            if (has_z) {
+              const float sz = sigmoid(zv[i]);
+              o_dz[j] = gv[i] * fmaf(Dd, uv[i], yv) * sz * (1.0f + zv[i] * (1.0f - sz));
+            }
+            // dB / dC for (this step, all states): sum over the 64 channels of the block
+            lane_transpose_reduce<kRW>(red, lane);
+            if (i < ns) {
+              const int64_t t = s0 + i;
+              if (kRW >= 64) {
+#pragma unroll
+                for (int r = 0; r < kRW / 64; ++r) {
+                  const int e = lane * (kRW / 64) + r;  // e < NS: dB state e, else dC state e - NS
+                  const int n = e < NS ? e : e - NS;
+                  if (n < N) {
+                    float* dst = (e < NS) ? p.dB_part : p.dC_part;
+                    dst[(((dblk * p.batch + b) * p.G + g) * N + n) * L + t] = red[r];
+                  }
+                }
+              } else {
+                // 32-wide reduction: the total of value e lives in lanes 2e and 2e + 1
+                const int e = lane >> 1;
+                if ((lane & 1) == 0 && e < 2 * NS) {
+                  const int n = e < NS ? e : e - NS;
+                  if (n < N) {
+                    float* dst = (e < NS) ? p.dB_part : p.dC_part;
+                    dst[(((dblk * p.batch + b) * p.G + g) * N + n) * L + t] = red[0];
+                  }
+                }
+              }
+            }
+          }
+          if (active) {
+            const int64_t sp = s0 + pc * kInner;
+            store_seg<T, kVec, kInner>(static_cast<T*>(p.ddelta) + row * L, o_dd, sp, t_end);
+            if (kSS2D)
+              store_seg<float, kVec, kInner>(static_cast<float*>(p.du) + row * L, o_du, sp, t_end);
+            else
+              store_seg<T, kVec, kInner>(static_cast<T*>(p.du) + row * L, o_du, sp, t_end);
+            if (has_z) store_seg<T, kVec, kInner>(static_cast<T*>(p.dz) + row * L, o_dz, sp, t_end);
+          }
+        }
+      } else {
+        // pass 1: adjoint recurrence of the chunk from zero (no states needed)
+#pragma unroll
+        for (int i = kSub - 1; i >= 0; --i) {
+          const float* ct = sC + (q * kSub + i) * S;
+#pragma unroll
+          for (int n = 0; n < NS; ++n) {
+            const float a = fast_exp2(lam[i] * Acoef[n]);
+            mu[n] = a * fmaf(ct[n], dy[i], mu[n]);
+          }
+          lam_sum += lam[i];
+        }
+      }
+    }
+  }
+
+  if (!active) return;
+  if (kPass == 1) {
+    float* dst = p.lam_carry + (row * p.n_chunks + c) * N;  // local adjoint at the chunk start
+#pragma unroll
+    for (int n = 0; n < NS; ++n)
+      if (n < N) dst[n] = mu[n];
+    p.chunk_sum[row * p.n_chunks + c] = lam_sum;
+  } else {
+    float* dA = p.dA_part + (int64_t(c) * p.batch * p.dim + row) * N;
+#pragma unroll
+    for (int n = 0; n < NS; ++n)
+      if (n < N) dA[n] = dA_acc[n];
+    p.dD_part[int64_t(c) * p.batch * p.dim + row] = dD_acc;
+    p.dbias_part[int64_t(c) * p.batch * p.dim + row] = dbias_acc;
+  }
+}
+
+template <typename T, int NS, bool kSS2D, bool kVec>
+hipError_t launch_t(const ScanBwdParams& p, hipStream_t s) {
+  const int64_t blocks = p.batch * p.G * p.dblocks * p.n_chunks;
+  if (blocks == 0) return hipSuccess;
+  if (p.pass == 1)
+    scan_bwd_kernel<T, NS, kSS2D, kVec, 1><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
+  else
+    scan_bwd_kernel<T, NS, kSS2D, kVec, 0><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace bwd_detail
+
+template <typename T, int NS>
+hipError_t scan_bwd_launch(const ScanBwdParams& p, hipStream_t s) {
+  using namespace bwd_detail;
+  if (p.ss2d) return p.vec ? launch_t<T, NS, true, true>(p, s) : launch_t<T, NS, true, false>(p, s);
+  return p.vec ? launch_t<T, NS, false, true>(p, s) : launch_t<T, NS, false, false>(p, s);
+}
+
+}  // namespace ss2d

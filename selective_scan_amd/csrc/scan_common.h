@@ -1,0 +1,239 @@
+// Helpers shared by the selective-scan forward and backward kernels: per-lane row tiles,
+// B/C staging into LDS, output and state stores.
+#pragma once
+#include "device_common.h"
+#include "internal.h"
+
+namespace ss2d {
+namespace scan_detail {
+
+// Per-lane copy of one row's tile (kTile consecutive elements), kept in the storage format.
+template <typename T>
+struct RowTile;
+template <>
+struct RowTile<float> {
+  float4 v[kTile / 4];
+  __device__ __forceinline__ float get(int i) const {
+    const float4 q = v[i / 4];
+    return (i % 4 == 0) ? q.x : (i % 4 == 1) ? q.y : (i % 4 == 2) ? q.z : q.w;
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int j = 0; j < kTile / 4; ++j) v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __device__ __forceinline__ void load_vec(const float* p, int j) { v[j] = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void set(int i, float x) {
+    float4& q = v[i / 4];
+    if (i % 4 == 0) q.x = x; else if (i % 4 == 1) q.y = x; else if (i % 4 == 2) q.z = x; else q.w = x;
+  }
+  __device__ __forceinline__ void reverse() {
+    float4 r[kTile / 4];
+#pragma unroll
+    for (int j = 0; j < kTile / 4; ++j) {
+      const float4 q = v[kTile / 4 - 1 - j];
+      r[j] = make_float4(q.w, q.z, q.y, q.x);
+    }
+#pragma unroll
+    for (int j = 0; j < kTile / 4; ++j) v[j] = r[j];
+  }
+};
+template <>
+struct RowTile<bf16> {
+  uint2 v[kTile / 4];
+  __device__ __forceinline__ float get(int i) const {
+    const uint2 q = v[i / 4];
+    const uint32_t w = ((i % 4) < 2) ? q.x : q.y;
+    return (i % 2 == 0) ? bf16lo(w) : bf16hi(w);
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int j = 0; j < kTile / 4; ++j) v[j] = make_uint2(0u, 0u);
+  }
+  __device__ __forceinline__ void load_vec(const bf16* p, int j) { v[j] = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void set(int i, uint16_t bits) {
+    uint2& q = v[i / 4];
+    uint32_t& w = ((i % 4) < 2) ? q.x : q.y;
+    w = (i % 2 == 0) ? ((w & 0xffff0000u) | bits) : ((w & 0xffffu) | (uint32_t(bits) << 16));
+  }
+  __device__ __forceinline__ void reverse() {
+    uint2 r[kTile / 4];
+#pragma unroll
+    for (int j = 0; j < kTile / 4; ++j) {
+      const uint2 q = v[kTile / 4 - 1 - j];
+      r[j] = make_uint2(__builtin_amdgcn_alignbit(q.y, q.y, 16), __builtin_amdgcn_alignbit(q.x, q.x, 16));
+    }
+#pragma unroll
+    for (int j = 0; j < kTile / 4; ++j) v[j] = r[j];
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ void set_elem(RowTile<T>& t, int i, const T* p);
+template <>
+__device__ __forceinline__ void set_elem<float>(RowTile<float>& t, int i, const float* p) { t.set(i, *p); }
+template <>
+__device__ __forceinline__ void set_elem<bf16>(RowTile<bf16>& t, int i, const bf16* p) { t.set(i, p->bits); }
+
+// Load steps [t0, t0 + kTile) of a row.  Forward rows read elements t0.., reversed rows read
+// pixels L-1-t for the same steps (then the tile is flipped so that index i is step t0 + i).
+template <typename T, bool kVec>
+__device__ __forceinline__ void load_row(RowTile<T>& tile, const T* row, int64_t t0, int64_t t_end, int64_t L,
+                                         bool rev) {
+  tile.zero();
+  if (kVec) {
+    if (!rev) {
+#pragma unroll
+      for (int j = 0; j < kTile / 4; ++j)
+        if (t0 + 4 * j < t_end) tile.load_vec(row + t0 + 4 * j, j);
+    } else {
+      const int64_t base = L - t0 - kTile;  // pixel of tile element kTile-1
+#pragma unroll
+      for (int j = 0; j < kTile / 4; ++j)
+        if (base + 4 * j >= 0 && L - 1 - (base + 4 * j + 3) < t_end) tile.load_vec(row + base + 4 * j, j);
+      tile.reverse();
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kTile; ++i) {
+      const int64_t t = t0 + i;
+      if (t < t_end) set_elem<T>(tile, i, row + (rev ? (L - 1 - t) : t));
+    }
+  }
+}
+
+// B/C staging: per lane, the raw values it copies into LDS for one tile.
+template <typename T, int NS, bool kVec>
+struct BCStage {
+  static constexpr int kVecs = (NS * kTile / 4 + kWave - 1) / kWave;  // 4-step vectors per lane
+  static constexpr int kElems = (NS * kTile + kWave - 1) / kWave;     // scalars per lane
+  float b[kVec ? 4 * kVecs : kElems];
+  float c[kVec ? 4 * kVecs : kElems];
+
+  __device__ __forceinline__ void load(const T* Bg, const T* Cg, int N, int64_t L, int64_t t0, int64_t t_end,
+                                       int lane) {
+    if (kVec) {
+#pragma unroll
+      for (int k = 0; k < kVecs; ++k) {
+        const int j = lane + k * kWave;            // vector id: n = j / (kTile/4), q = j % (kTile/4)
+        const int n = j / (kTile / 4), q = j % (kTile / 4);
+        float4 vb = make_float4(0.f, 0.f, 0.f, 0.f), vc = vb;
+        if (n < N && j < NS * kTile / 4 && t0 + 4 * q < t_end) {
+          vb = Elem<T>::load4(Bg, int64_t(n) * L + t0 + 4 * q);
+          vc = Elem<T>::load4(Cg, int64_t(n) * L + t0 + 4 * q);
+        }
+        b[4 * k + 0] = vb.x; b[4 * k + 1] = vb.y; b[4 * k + 2] = vb.z; b[4 * k + 3] = vb.w;
+        c[4 * k + 0] = vc.x; c[4 * k + 1] = vc.y; c[4 * k + 2] = vc.z; c[4 * k + 3] = vc.w;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kElems; ++k) {
+        const int e = lane + k * kWave;            // element id: n = e / kTile, i = e % kTile
+        const int n = e / kTile, i = e % kTile;
+        float vb = 0.f, vc = 0.f;
+        if (n < N && e < NS * kTile && t0 + i < t_end) {
+          vb = Elem<T>::load(Bg, int64_t(n) * L + t0 + i);
+          vc = Elem<T>::load(Cg, int64_t(n) * L + t0 + i);
+        }
+        b[k] = vb;
+        c[k] = vc;
+      }
+    }
+  }
+
+  // LDS layout: [step][state] with row stride S floats; B is pre-multiplied by ln 2.
+  template <int S>
+  __device__ __forceinline__ void store(float* sB, float* sC, int lane) const {
+    if (kVec) {
+#pragma unroll
+      for (int k = 0; k < kVecs; ++k) {
+        const int j = lane + k * kWave;
+        if (j < NS * kTile / 4) {
+          const int n = j / (kTile / 4), q = j % (kTile / 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sB[(4 * q + i) * S + n] = b[4 * k + i] * kLn2;
+            sC[(4 * q + i) * S + n] = c[4 * k + i];
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kElems; ++k) {
+        const int e = lane + k * kWave;
+        if (e < NS * kTile) {
+          const int n = e / kTile, i = e % kTile;
+          sB[i * S + n] = b[k] * kLn2;
+          sC[i * S + n] = c[k];
+        }
+      }
+    }
+  }
+};
+
+template <typename O, bool kVec>
+__device__ __forceinline__ void store_out(O* row, const float* y, int64_t t0, int64_t t_end) {
+  if (kVec) {
+#pragma unroll
+    for (int j = 0; j < kTile / 4; ++j)
+      if (t0 + 4 * j < t_end)
+        Elem<O>::store4(row, t0 + 4 * j, make_float4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]));
+  } else {
+#pragma unroll
+    for (int i = 0; i < kTile; ++i)
+      if (t0 + i < t_end) Elem<O>::store(row, t0 + i, y[i]);
+  }
+}
+
+template <int NS>
+__device__ __forceinline__ void store_state(float* dst, const float* h, int N) {
+  if (NS % 4 == 0 && (N % 4) == 0) {
+#pragma unroll
+    for (int n = 0; n < NS; n += 4)
+      if (n < N) *reinterpret_cast<float4*>(dst + n) = make_float4(h[n], h[n + 1], h[n + 2], h[n + 3]);
+  } else {
+#pragma unroll
+    for (int n = 0; n < NS; ++n)
+      if (n < N) dst[n] = h[n];
+  }
+}
+
+// kSeg consecutive steps [t, t + kSeg) of a row as floats (reversed rows read pixel L-1-step).
+// Steps at or past t_end read as 0.  Vector loads need L % 4 == 0, t % 4 == 0 and kSeg % 4 == 0.
+template <typename T, bool kVec, int kSeg>
+__device__ __forceinline__ void load_seg(float* out, const T* row, int64_t t, int64_t t_end, int64_t L, bool rev) {
+  if (kVec && kSeg % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < kSeg / 4; ++j) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      const int64_t s = t + 4 * j;
+      if (s < t_end) v = Elem<T>::load4(row, rev ? (L - 4 - s) : s);
+      if (!rev) {
+        out[4 * j] = v.x; out[4 * j + 1] = v.y; out[4 * j + 2] = v.z; out[4 * j + 3] = v.w;
+      } else {
+        out[4 * j] = v.w; out[4 * j + 1] = v.z; out[4 * j + 2] = v.y; out[4 * j + 3] = v.x;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kSeg; ++i) {
+      const int64_t s = t + i;
+      out[i] = (s < t_end) ? Elem<T>::load(row, rev ? (L - 1 - s) : s) : 0.0f;
+    }
+  }
+}
+
+template <typename O, bool kVec, int kSeg>
+__device__ __forceinline__ void store_seg(O* row, const float* v, int64_t t, int64_t t_end) {
+  if (kVec && kSeg % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < kSeg / 4; ++j)
+      if (t + 4 * j < t_end) Elem<O>::store4(row, t + 4 * j, make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]));
+  } else {
+#pragma unroll
+    for (int i = 0; i < kSeg; ++i)
+      if (t + i < t_end) Elem<O>::store(row, t + i, v[i]);
+  }
+}
+
+}  // namespace scan_detail
+}  // namespace ss2d

@@ -25,44 +25,48 @@ bool dtype_ok(int dtype) { return dtype == SS2D_DTYPE_F32 || dtype == SS2D_DTYPE
 constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
 
 // ---- selective-scan workspace layout -------------------------------------------------
+// Split long sequences across wavefronts only when the rows alone cannot fill the GPU
+// (1024 SIMDs on MI355X; aim for at least two wavefronts per SIMD).  Chunks are whole tiles.
+void plan_chunks(int64_t row_waves, int64_t L, bool can_chunk, int64_t* chunk_len, int* n_chunks) {
+  const int64_t n_tiles = cdiv(L, kTile);
+  if (!can_chunk || row_waves >= 1024 || n_tiles <= 1) {
+    *chunk_len = (n_tiles > 0 ? n_tiles : 1) * kTile;
+    *n_chunks = 1;
+    return;
+  }
+  int64_t want = cdiv(2048, row_waves);
+  if (want > n_tiles) want = n_tiles;
+  const int64_t tiles_per_chunk = cdiv(n_tiles, want);
+  *chunk_len = tiles_per_chunk * kTile;
+  *n_chunks = int(cdiv(L, *chunk_len));
+}
+
 struct ScanLayout {
-  int64_t rows, n_ckpt, dblocks, per_group;
+  int64_t rows, n_ckpt, dblocks, per_group, chunk_len;
+  int n_chunks, ckpt_every;
   int64_t off_ckpt, off_sum, off_lam, off_dB, off_dC, off_dA, off_dD, off_dbias, total;
 };
 
 ScanLayout scan_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int64_t ngroups) {
   ScanLayout l{};
   l.rows = batch * dim;
-  l.n_ckpt = cdiv(seqlen, kCkpt);
+  l.ckpt_every = ckpt_steps(padded_states(dstate));
+  l.n_ckpt = cdiv(seqlen, l.ckpt_every);
   l.per_group = ngroups > 0 ? dim / ngroups : 0;
   l.dblocks = cdiv(l.per_group, kWave);
+  plan_chunks(batch * ngroups * l.dblocks, seqlen, true, &l.chunk_len, &l.n_chunks);
+  const int64_t nc = l.n_chunks;
   int64_t o = 0;
   l.off_ckpt = o;  o += align_up(l.rows * l.n_ckpt * dstate * 4);
-  l.off_sum = o;   o += align_up(l.rows * l.n_ckpt * 4);
-  l.off_lam = o;   o += align_up(l.rows * l.n_ckpt * dstate * 4);
+  l.off_sum = o;   o += align_up(l.rows * nc * 4);
+  l.off_lam = o;   o += align_up(l.rows * nc * dstate * 4);
   l.off_dB = o;    o += align_up(l.dblocks * batch * ngroups * dstate * seqlen * 4);
   l.off_dC = o;    o += align_up(l.dblocks * batch * ngroups * dstate * seqlen * 4);
-  l.off_dA = o;    o += align_up(l.n_ckpt * l.rows * dstate * 4);
-  l.off_dD = o;    o += align_up(l.n_ckpt * l.rows * 4);
-  l.off_dbias = o; o += align_up(l.n_ckpt * l.rows * 4);
+  l.off_dA = o;    o += align_up(nc * l.rows * dstate * 4);
+  l.off_dD = o;    o += align_up(nc * l.rows * 4);
+  l.off_dbias = o; o += align_up(nc * l.rows * 4);
   l.total = o;
   return l;
-}
-
-// Split long sequences across wavefronts only when the rows alone cannot fill the GPU
-// (1024 SIMDs on MI355X; aim for at least two wavefronts per SIMD).
-void plan_chunks(int64_t row_waves, int64_t L, bool can_chunk, int64_t* chunk_len, int* n_chunks) {
-  const int64_t n_ckpt = cdiv(L, kCkpt);
-  if (!can_chunk || row_waves >= 1024 || n_ckpt <= 1) {
-    *chunk_len = n_ckpt * kCkpt;
-    *n_chunks = 1;
-    return;
-  }
-  int64_t want = cdiv(2048, row_waves);
-  if (want > n_ckpt) want = n_ckpt;
-  const int64_t ck_per_chunk = cdiv(n_ckpt, want);
-  *chunk_len = ck_per_chunk * kCkpt;
-  *n_chunks = int(cdiv(L, *chunk_len));
 }
 
 // ---- SS2D workspace layout -----------------------------------------------------------
@@ -203,6 +207,7 @@ int selective_scan_fwd(const ss_fwd_args* a, hipStream_t stream) {
   p.per_group = lay.per_group;
   p.dblocks = lay.dblocks;
   p.n_ckpt = int(lay.n_ckpt);
+  p.ckpt_every = lay.ckpt_every;
   p.N = int(a->dstate);
   p.softplus = a->delta_softplus ? 1 : 0;
   p.ss2d = 0;
@@ -230,21 +235,21 @@ size_t ss2d_workspace_bytes(int64_t batch, int64_t dim, int64_t height, int64_t 
   return size_t(ss2d_layout(batch, dim, height, width, dstate, dtype).total);
 }
 
-// Shared by ss2d_fwd / ss2d_bwd: transpose x into the workspace and run the route scans with
-// outputs (fp32, route order) into the ys region; optionally keep every checkpoint state.
-static int ss2d_forward_scans(const ss2d_fwd_args* a, const SS2DLayout& lay, bool keep_states, hipStream_t stream) {
-  const int64_t L = a->height * a->width;
-  const int e = esize(a->dtype);
-  void* xT = at(a->workspace, lay.off_xT);
+// Stages of the SS2D forward (all on one workspace).
+static int ss2d_transpose_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, hipStream_t stream) {
   ScanOutputs o{};
-  o.out[1] = xT;
-  o.batch_stride = a->dim * L;
-  hipError_t err = launch_route_scatter(a->x, o, a->batch, a->dim, a->height, a->width, e, stream);
-  if (err != hipSuccess) return SS2D_ERR_HIP;
+  o.out[1] = at(a->workspace, lay.off_xT);
+  o.batch_stride = a->dim * a->height * a->width;
+  return status_from(launch_route_scatter(a->x, o, a->batch, a->dim, a->height, a->width, esize(a->dtype), stream));
+}
 
+// The four route scans with fp32 outputs (route order) into the ys region; when keep_states,
+// the state before every ckpt_every-th step of every row is kept for the backward.
+static int ss2d_scan_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, bool keep_states, hipStream_t stream) {
+  const int64_t L = a->height * a->width;
   ScanFwdParams p{};
   p.u = a->x;
-  p.uT = xT;
+  p.uT = at(a->workspace, lay.off_xT);
   p.delta = a->delta;
   p.A = a->A;
   p.Bm = a->Bm;
@@ -258,15 +263,18 @@ static int ss2d_forward_scans(const ss2d_fwd_args* a, const SS2DLayout& lay, boo
   p.per_group = a->dim;
   p.dblocks = lay.scan.dblocks;
   p.n_ckpt = int(lay.scan.n_ckpt);
+  p.ckpt_every = lay.scan.ckpt_every;
   p.N = int(a->dstate);
   p.softplus = a->delta_softplus ? 1 : 0;
   p.ss2d = 1;
   p.dtype = a->dtype;
   p.vec = (L % 4 == 0) && vec_aligned(a->dtype, {a->x, a->delta, a->Bm, a->Cm});
-  plan_chunks(a->batch * 4 * lay.scan.dblocks, L, true, &p.chunk_len, &p.n_chunks);
+  p.chunk_len = lay.scan.chunk_len;
+  p.n_chunks = lay.scan.n_chunks;
   if (a->batch * 4 * lay.scan.dblocks * p.n_chunks > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
   p.chunk_sum = reinterpret_cast<float*>(at(a->workspace, lay.off_scan + lay.scan.off_sum));
   if (p.n_chunks > 1 || keep_states) p.ckpt = reinterpret_cast<float*>(at(a->workspace, lay.off_scan + lay.scan.off_ckpt));
+  hipError_t err = hipSuccess;
   if (p.n_chunks > 1) {
     p.pass = 1;
     err = launch_scan_fwd(p, stream);
@@ -277,29 +285,7 @@ static int ss2d_forward_scans(const ss2d_fwd_args* a, const SS2DLayout& lay, boo
   return status_from(launch_scan_fwd(p, stream));
 }
 
-static int check_ss2d(int64_t batch, int64_t dim, int64_t height, int64_t width, int64_t dstate, int dtype) {
-  if (!dtype_ok(dtype)) return SS2D_ERR_UNSUPPORTED;
-  if (batch < 0 || dim < 0 || height < 0 || width < 0) return SS2D_ERR_INVALID_ARGUMENT;
-  if (dstate < 1 || dstate > 64) return SS2D_ERR_UNSUPPORTED;
-  if (height > (1 << 30) || width > (1 << 30)) return SS2D_ERR_INVALID_ARGUMENT;
-  return SS2D_OK;
-}
-
-int ss2d_fwd(const ss2d_fwd_args* a, hipStream_t stream) {
-  if (!a) return SS2D_ERR_INVALID_ARGUMENT;
-  int st = check_ss2d(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype);
-  if (st != SS2D_OK) return st;
-  const int64_t L = a->height * a->width;
-  if (a->batch * a->dim * L == 0) return SS2D_OK;
-  if (!a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->out || !a->workspace) return SS2D_ERR_INVALID_ARGUMENT;
-  if (!elem_aligned(a->dtype, {a->x, a->delta, a->Bm, a->Cm, a->z, a->out})) return SS2D_ERR_INVALID_ARGUMENT;
-  if (!aligned(a->A, 4) || (a->Dskip && !aligned(a->Dskip, 4)) || (a->delta_bias && !aligned(a->delta_bias, 4)))
-    return SS2D_ERR_INVALID_ARGUMENT;
-  const SS2DLayout lay = ss2d_layout(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype);
-  if (a->workspace_bytes < size_t(lay.total) || !aligned(a->workspace, kAlign)) return SS2D_ERR_INVALID_ARGUMENT;
-  if (a->batch * a->dim * cdiv(a->height, 32) * cdiv(a->width, 32) > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
-  st = ss2d_forward_scans(a, lay, false, stream);
-  if (st != SS2D_OK) return st;
+static int ss2d_merge_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, float* merged, hipStream_t stream) {
   MergeArgs m{};
   m.routes = at(a->workspace, lay.off_ys);
   m.routes_f32 = 1;
@@ -307,6 +293,7 @@ int ss2d_fwd(const ss2d_fwd_args* a, hipStream_t stream) {
   m.Dskip = a->Dskip;
   m.z = a->z;
   m.y = a->out;
+  m.merged_f32 = merged;
   m.batch = a->batch;
   m.C = a->dim;
   m.H = a->height;
@@ -315,16 +302,314 @@ int ss2d_fwd(const ss2d_fwd_args* a, hipStream_t stream) {
   return status_from(launch_merge(m, stream));
 }
 
+static int check_ss2d(int64_t batch, int64_t dim, int64_t height, int64_t width, int64_t dstate, int dtype) {
+  if (!dtype_ok(dtype)) return SS2D_ERR_UNSUPPORTED;
+  if (batch < 0 || dim < 0 || height < 0 || width < 0) return SS2D_ERR_INVALID_ARGUMENT;
+  if (dstate < 1 || dstate > 64) return SS2D_ERR_UNSUPPORTED;
+  if (height > (1 << 30) || width > (1 << 30)) return SS2D_ERR_INVALID_ARGUMENT;
+  return SS2D_OK;
+}
+
+// Validation shared by ss2d_fwd and ss2d_fwd_stage.  Returns SS2D_OK with *empty set when there
+// is nothing to compute.
+static int validate_ss2d_fwd(const ss2d_fwd_args* a, SS2DLayout* lay, bool* empty) {
+  *empty = false;
+  if (!a) return SS2D_ERR_INVALID_ARGUMENT;
+  int st = check_ss2d(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype);
+  if (st != SS2D_OK) return st;
+  if (a->batch * a->dim * a->height * a->width == 0) {
+    *empty = true;
+    return SS2D_OK;
+  }
+  if (!a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->out || !a->workspace) return SS2D_ERR_INVALID_ARGUMENT;
+  if (!elem_aligned(a->dtype, {a->x, a->delta, a->Bm, a->Cm, a->z, a->out})) return SS2D_ERR_INVALID_ARGUMENT;
+  if (!aligned(a->A, 4) || (a->Dskip && !aligned(a->Dskip, 4)) || (a->delta_bias && !aligned(a->delta_bias, 4)))
+    return SS2D_ERR_INVALID_ARGUMENT;
+  *lay = ss2d_layout(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype);
+  if (a->workspace_bytes < size_t(lay->total) || !aligned(a->workspace, kAlign)) return SS2D_ERR_INVALID_ARGUMENT;
+  if (a->batch * a->dim * cdiv(a->height, 32) * cdiv(a->width, 32) > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
+  return SS2D_OK;
+}
+
+int ss2d_fwd(const ss2d_fwd_args* a, hipStream_t stream) {
+  SS2DLayout lay;
+  bool empty;
+  int st = validate_ss2d_fwd(a, &lay, &empty);
+  if (st != SS2D_OK || empty) return st;
+  st = ss2d_transpose_stage(a, lay, stream);
+  if (st == SS2D_OK) st = ss2d_scan_stage(a, lay, false, stream);
+  if (st == SS2D_OK) st = ss2d_merge_stage(a, lay, nullptr, stream);
+  return st;
+}
+
+int ss2d_fwd_stage(const ss2d_fwd_args* a, int stage, hipStream_t stream) {
+  if (stage < SS2D_STAGE_TRANSPOSE || stage > SS2D_STAGE_MERGE) return SS2D_ERR_INVALID_ARGUMENT;
+  SS2DLayout lay;
+  bool empty;
+  int st = validate_ss2d_fwd(a, &lay, &empty);
+  if (st != SS2D_OK || empty) return st;
+  if (stage == SS2D_STAGE_TRANSPOSE) return ss2d_transpose_stage(a, lay, stream);
+  if (stage == SS2D_STAGE_SCAN) return ss2d_scan_stage(a, lay, false, stream);
+  return ss2d_merge_stage(a, lay, nullptr, stream);
+}
+
+// The forward scans with no outputs: only the checkpoint states (for a backward without them).
+static hipError_t scan_states_only(ScanFwdParams p, hipStream_t stream) {
+  p.out = nullptr;
+  p.last_state = nullptr;
+  hipError_t e = hipSuccess;
+  if (p.n_chunks > 1) {
+    p.pass = 1;
+    e = launch_scan_fwd(p, stream);
+    if (e == hipSuccess) e = launch_chunk_combine(p, stream);
+    if (e != hipSuccess) return e;
+  }
+  p.pass = 0;
+  return launch_scan_fwd(p, stream);
+}
+
+// Zero the gradients that are sums over an empty set.
+static int zero_param_grads(float* dA, float* dD, float* dbias, int64_t dim, int64_t dstate, hipStream_t stream) {
+  hipError_t e = launch_fill_zero(dA, dim * dstate, stream);
+  if (e == hipSuccess && dD) e = launch_fill_zero(dD, dim, stream);
+  if (e == hipSuccess && dbias) e = launch_fill_zero(dbias, dim, stream);
+  return status_from(e);
+}
+
+// Adjoint scans + partial-sum reduction, shared by selective_scan_bwd and ss2d_bwd.
+static int run_scan_bwd(ScanBwdParams bp, const ScanLayout& lay, void* ws, void* dB, void* dC, float* dA, float* dD,
+                        float* dbias, hipStream_t stream) {
+  bp.ckpt = reinterpret_cast<const float*>(at(ws, lay.off_ckpt));
+  bp.chunk_sum = reinterpret_cast<float*>(at(ws, lay.off_sum));
+  bp.lam_carry = reinterpret_cast<float*>(at(ws, lay.off_lam));
+  bp.dB_part = reinterpret_cast<float*>(at(ws, lay.off_dB));
+  bp.dC_part = reinterpret_cast<float*>(at(ws, lay.off_dC));
+  bp.dA_part = reinterpret_cast<float*>(at(ws, lay.off_dA));
+  bp.dD_part = reinterpret_cast<float*>(at(ws, lay.off_dD));
+  bp.dbias_part = reinterpret_cast<float*>(at(ws, lay.off_dbias));
+  bp.chunk_len = lay.chunk_len;
+  bp.n_chunks = lay.n_chunks;
+  bp.n_ckpt = int(lay.n_ckpt);
+  hipError_t e = hipSuccess;
+  if (bp.n_chunks > 1) {
+    bp.pass = 1;
+    e = launch_scan_bwd(bp, stream);
+    if (e == hipSuccess) e = launch_lambda_combine(bp, stream);
+    if (e != hipSuccess) return SS2D_ERR_HIP;
+  }
+  bp.pass = 0;
+  e = launch_scan_bwd(bp, stream);
+  if (e != hipSuccess) return SS2D_ERR_HIP;
+  BwdReduceArgs r{};
+  r.dB_part = bp.dB_part;
+  r.dC_part = bp.dC_part;
+  r.dA_part = bp.dA_part;
+  r.dD_part = bp.dD_part;
+  r.dbias_part = bp.dbias_part;
+  r.dB = dB;
+  r.dC = dC;
+  r.dA = dA;
+  r.dD = dD;
+  r.dbias = dbias;
+  r.batch = bp.batch;
+  r.dim = bp.dim;
+  r.L = bp.L;
+  r.G = bp.G;
+  r.dblocks = bp.dblocks;
+  r.n_chunks = bp.n_chunks;
+  r.N = bp.N;
+  r.dtype = bp.dtype;
+  return status_from(launch_bwd_reduce(r, stream));
+}
+
 int selective_scan_bwd(const ss_bwd_args* a, hipStream_t stream) {
-  (void)a;
-  (void)stream;
-  return SS2D_ERR_UNSUPPORTED;
+  if (!a) return SS2D_ERR_INVALID_ARGUMENT;
+  int st = check_scan_shapes(a->batch, a->dim, a->dstate, a->seqlen, a->ngroups, a->dtype);
+  if (st != SS2D_OK) return st;
+  if ((a->Dskip && !a->dDskip) || (a->delta_bias && !a->ddelta_bias) || (a->z && !a->dz))
+    return SS2D_ERR_INVALID_ARGUMENT;
+  if (a->dim == 0) return SS2D_OK;
+  if (!a->dA) return SS2D_ERR_INVALID_ARGUMENT;
+  if (a->batch == 0 || a->seqlen == 0)
+    return zero_param_grads(a->dA, a->Dskip ? a->dDskip : nullptr, a->delta_bias ? a->ddelta_bias : nullptr, a->dim,
+                            a->dstate, stream);
+  if (!a->u || !a->delta || !a->A || !a->Bm || !a->Cm || !a->dout || !a->du || !a->ddelta || !a->dBm || !a->dCm ||
+      !a->workspace)
+    return SS2D_ERR_INVALID_ARGUMENT;
+  if (!elem_aligned(a->dtype, {a->u, a->delta, a->Bm, a->Cm, a->z, a->dout, a->du, a->ddelta, a->dBm, a->dCm, a->dz}))
+    return SS2D_ERR_INVALID_ARGUMENT;
+  if (!aligned(a->A, 4) || !aligned(a->dA, 4) || (a->Dskip && !aligned(a->Dskip, 4)) ||
+      (a->delta_bias && !aligned(a->delta_bias, 4)) || (a->dDskip && !aligned(a->dDskip, 4)) ||
+      (a->ddelta_bias && !aligned(a->ddelta_bias, 4)))
+    return SS2D_ERR_INVALID_ARGUMENT;
+  const ScanLayout lay = scan_layout(a->batch, a->dim, a->dstate, a->seqlen, a->ngroups);
+  if (a->workspace_bytes < size_t(lay.total) || !aligned(a->workspace, kAlign)) return SS2D_ERR_INVALID_ARGUMENT;
+  if (a->batch * a->ngroups * lay.dblocks * lay.n_chunks > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
+  const bool vec = (a->seqlen % 4 == 0) &&
+                   vec_aligned(a->dtype, {a->u, a->delta, a->Bm, a->Cm, a->z, a->dout, a->du, a->ddelta});
+
+  if (!a->workspace_has_states) {
+    ScanFwdParams p{};
+    p.u = a->u;
+    p.delta = a->delta;
+    p.A = a->A;
+    p.Bm = a->Bm;
+    p.Cm = a->Cm;
+    p.delta_bias = a->delta_bias;
+    p.ckpt = reinterpret_cast<float*>(at(a->workspace, lay.off_ckpt));
+    p.chunk_sum = reinterpret_cast<float*>(at(a->workspace, lay.off_sum));
+    p.batch = a->batch;
+    p.dim = a->dim;
+    p.L = a->seqlen;
+    p.G = a->ngroups;
+    p.per_group = lay.per_group;
+    p.dblocks = lay.dblocks;
+    p.chunk_len = lay.chunk_len;
+    p.n_chunks = lay.n_chunks;
+    p.n_ckpt = int(lay.n_ckpt);
+    p.ckpt_every = lay.ckpt_every;
+    p.N = int(a->dstate);
+    p.softplus = a->delta_softplus ? 1 : 0;
+    p.dtype = a->dtype;
+    p.vec = vec;
+    if (scan_states_only(p, stream) != hipSuccess) return SS2D_ERR_HIP;
+  }
+  ScanBwdParams bp{};
+  bp.u = a->u;
+  bp.delta = a->delta;
+  bp.A = a->A;
+  bp.Bm = a->Bm;
+  bp.Cm = a->Cm;
+  bp.Dskip = a->Dskip;
+  bp.z = a->z;
+  bp.delta_bias = a->delta_bias;
+  bp.dout = a->dout;
+  bp.du = a->du;
+  bp.ddelta = a->ddelta;
+  bp.dz = a->dz;
+  bp.batch = a->batch;
+  bp.dim = a->dim;
+  bp.L = a->seqlen;
+  bp.G = a->ngroups;
+  bp.per_group = lay.per_group;
+  bp.dblocks = lay.dblocks;
+  bp.N = int(a->dstate);
+  bp.softplus = a->delta_softplus ? 1 : 0;
+  bp.ss2d = 0;
+  bp.dtype = a->dtype;
+  bp.vec = vec;
+  return run_scan_bwd(bp, lay, a->workspace, a->dBm, a->dCm, a->dA, a->Dskip ? a->dDskip : nullptr,
+                      a->delta_bias ? a->ddelta_bias : nullptr, stream);
 }
 
 int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
-  (void)a;
-  (void)stream;
-  return SS2D_ERR_UNSUPPORTED;
+  if (!a) return SS2D_ERR_INVALID_ARGUMENT;
+  int st = check_ss2d(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype);
+  if (st != SS2D_OK) return st;
+  if ((a->Dskip && !a->dDskip) || (a->delta_bias && !a->ddelta_bias) || (a->z && !a->dz))
+    return SS2D_ERR_INVALID_ARGUMENT;
+  if (a->dim == 0) return SS2D_OK;
+  if (!a->dA) return SS2D_ERR_INVALID_ARGUMENT;
+  if (a->batch * a->height * a->width == 0)
+    return zero_param_grads(a->dA, a->Dskip ? a->dDskip : nullptr, a->delta_bias ? a->ddelta_bias : nullptr,
+                            4 * a->dim, a->dstate, stream);
+  if (!a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->dout || !a->dx || !a->ddelta || !a->dBm || !a->dCm ||
+      !a->workspace)
+    return SS2D_ERR_INVALID_ARGUMENT;
+  if (!elem_aligned(a->dtype, {a->x, a->delta, a->Bm, a->Cm, a->z, a->dout, a->dx, a->ddelta, a->dBm, a->dCm, a->dz}))
+    return SS2D_ERR_INVALID_ARGUMENT;
+  if (!aligned(a->A, 4) || !aligned(a->dA, 4) || (a->Dskip && !aligned(a->Dskip, 4)) ||
+      (a->delta_bias && !aligned(a->delta_bias, 4)) || (a->dDskip && !aligned(a->dDskip, 4)) ||
+      (a->ddelta_bias && !aligned(a->ddelta_bias, 4)))
+    return SS2D_ERR_INVALID_ARGUMENT;
+  const SS2DLayout lay = ss2d_layout(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype);
+  if (a->workspace_bytes < size_t(lay.total) || !aligned(a->workspace, kAlign)) return SS2D_ERR_INVALID_ARGUMENT;
+  if (a->batch * a->dim * cdiv(a->height, 32) * cdiv(a->width, 32) > kMaxBlocks ||
+      a->batch * 4 * lay.scan.dblocks * lay.scan.n_chunks > kMaxBlocks)
+    return SS2D_ERR_INVALID_ARGUMENT;
+  const int64_t L = a->height * a->width;
+
+  // forward again: transposed x, route outputs and checkpoint states, merged pre-gate map
+  ss2d_fwd_args f{};
+  f.x = a->x;
+  f.delta = a->delta;
+  f.A = a->A;
+  f.Bm = a->Bm;
+  f.Cm = a->Cm;
+  f.Dskip = a->Dskip;
+  f.delta_bias = a->delta_bias;
+  f.z = nullptr;
+  f.out = nullptr;
+  f.workspace = a->workspace;
+  f.workspace_bytes = a->workspace_bytes;
+  f.batch = a->batch;
+  f.dim = a->dim;
+  f.height = a->height;
+  f.width = a->width;
+  f.dstate = a->dstate;
+  f.dtype = a->dtype;
+  f.delta_softplus = a->delta_softplus;
+  st = ss2d_transpose_stage(&f, lay, stream);
+  if (st == SS2D_OK) st = ss2d_scan_stage(&f, lay, true, stream);
+  float* merged = reinterpret_cast<float*>(at(a->workspace, lay.off_merged));
+  if (st == SS2D_OK) st = ss2d_merge_stage(&f, lay, merged, stream);
+  if (st != SS2D_OK) return st;
+
+  // gate: dM = dout * silu(z) (grid and transposed), dz = dout * M * silu'(z)
+  GateBwdArgs gb{};
+  gb.merged = merged;
+  gb.z = a->z;
+  gb.dout = a->dout;
+  gb.dM = reinterpret_cast<float*>(at(a->workspace, lay.off_dM));
+  gb.dMT = reinterpret_cast<float*>(at(a->workspace, lay.off_dMT));
+  gb.dz = a->dz;
+  gb.batch = a->batch;
+  gb.C = a->dim;
+  gb.H = a->height;
+  gb.W = a->width;
+  gb.dtype = a->dtype;
+  if (launch_gate_bwd(gb, stream) != hipSuccess) return SS2D_ERR_HIP;
+
+  // adjoint scans of the four routes; du (fp32, route order) reuses the route-output region
+  ScanBwdParams bp{};
+  bp.u = a->x;
+  bp.uT = at(a->workspace, lay.off_xT);
+  bp.delta = a->delta;
+  bp.A = a->A;
+  bp.Bm = a->Bm;
+  bp.Cm = a->Cm;
+  bp.Dskip = a->Dskip;
+  bp.delta_bias = a->delta_bias;
+  bp.dout = gb.dM;
+  bp.doutT = gb.dMT;
+  bp.du = at(a->workspace, lay.off_ys);
+  bp.ddelta = a->ddelta;
+  bp.batch = a->batch;
+  bp.dim = 4 * a->dim;
+  bp.L = L;
+  bp.G = 4;
+  bp.per_group = a->dim;
+  bp.dblocks = lay.scan.dblocks;
+  bp.N = int(a->dstate);
+  bp.softplus = a->delta_softplus ? 1 : 0;
+  bp.ss2d = 1;
+  bp.dtype = a->dtype;
+  bp.vec = (L % 4 == 0) && vec_aligned(a->dtype, {a->x, a->delta, a->Bm, a->Cm, a->ddelta});
+  st = run_scan_bwd(bp, lay.scan, at(a->workspace, lay.off_scan), a->dBm, a->dCm, a->dA,
+                    a->Dskip ? a->dDskip : nullptr, a->delta_bias ? a->ddelta_bias : nullptr, stream);
+  if (st != SS2D_OK) return st;
+
+  // dx = cross-merge of the routes' du
+  MergeArgs m{};
+  m.routes = at(a->workspace, lay.off_ys);
+  m.routes_f32 = 1;
+  m.y = a->dx;
+  m.batch = a->batch;
+  m.C = a->dim;
+  m.H = a->height;
+  m.W = a->width;
+  m.dtype = a->dtype;
+  return status_from(launch_merge(m, stream));
 }
 
 }  // extern "C"

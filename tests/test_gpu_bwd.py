@@ -1,0 +1,138 @@
+"""GPU parity of the backward paths (selective_scan_bwd, ss2d_bwd) against the fp64 oracle's
+exact gradients; gradients within 1e-3 relative (bf16 I/O: 2e-2, the storage rounding)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_scan_amd as ss
+from gpu_util import TOL, TOL_GRAD, f64, rel_err, to_dev, to_f64
+from selective_scan_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias")
+
+
+def _tol(dtype):
+    return TOL_GRAD if dtype == "f32" else TOL["bf16"]
+
+
+def _case(batch, dim, N, L, G, dtype, has_z, has_D, has_bias, softplus, seed):
+    inp = synth.make_ss_inputs(batch, dim, N, L, G, dtype, has_z=has_z, seed_base=seed, with_dout=True)
+    if not softplus:
+        inp["delta"] = (inp["delta"] & np.uint16(0x7FFF)) if dtype == "bf16" else np.abs(inp["delta"])
+    A = inp["A"] * np.float32(0.5 + np.random.default_rng(seed).random((dim, 1)))
+    Dv = inp["D"] * np.float32(0.7)
+    dev = dict(u=to_dev(inp["u"], dtype), delta=to_dev(inp["delta"], dtype), A=to_dev(A, "f32"),
+               B=to_dev(inp["B"], dtype), C=to_dev(inp["C"], dtype), D=to_dev(Dv, "f32") if has_D else None,
+               z=to_dev(inp["z"], dtype) if has_z else None,
+               delta_bias=to_dev(inp["delta_bias"], "f32") if has_bias and softplus else None)
+    ref = dict(u=f64(inp["u"], dtype), delta=f64(inp["delta"], dtype), A=A.astype(np.float64),
+               B=f64(inp["B"], dtype), C=f64(inp["C"], dtype), D=Dv.astype(np.float64) if has_D else None,
+               z=f64(inp["z"], dtype) if has_z else None,
+               delta_bias=inp["delta_bias"].astype(np.float64) if has_bias and softplus else None)
+    return dev, ref, to_dev(inp["dout"], dtype), f64(inp["dout"], dtype)
+
+
+BWD_CASES = [
+    # batch, dim, N, L, G, dtype, z, D, bias, softplus
+    (2, 64, 16, 256, 1, "f32", True, True, True, True),
+    (2, 96, 16, 200, 2, "f32", False, True, True, True),     # partial wave, ragged tile
+    (1, 70, 4, 129, 1, "f32", True, True, False, True),      # L % 4 != 0
+    (3, 32, 1, 300, 4, "f32", False, False, True, True),
+    (1, 16, 3, 77, 1, "f32", True, False, False, False),     # no softplus, N padded
+    (2, 64, 32, 96, 2, "f32", True, True, True, True),
+    (1, 64, 64, 40, 1, "f32", True, True, True, True),
+    (1, 64, 8, 2048, 1, "f32", True, True, True, True),      # few rows: chunked
+    (2, 128, 16, 256, 2, "bf16", True, True, True, True),
+    (2, 8, 16, 1, 1, "f32", True, True, True, True),         # L = 1
+]
+
+
+@pytest.mark.parametrize("ci", range(len(BWD_CASES)), ids=[str(c[:6]) for c in BWD_CASES])
+def test_selective_scan_bwd(ci):
+    batch, dim, N, L, G, dtype, z, D, bias, sp = BWD_CASES[ci]
+    dev, ref, dout, dout64 = _case(batch, dim, N, L, G, dtype, z, D, bias, sp, seed=300 + ci)
+    g = ss.selective_scan_bwd(**dev, dout=dout, delta_softplus=sp)
+    r = oracle.ss_bwd(**ref, delta_softplus=sp, dout=dout64)
+    for k in GRADS:
+        if r[k] is None:
+            assert g[k] is None
+            continue
+        e = rel_err(to_f64(g[k]), r[k])
+        assert e <= _tol(dtype), (k, e)
+
+
+def test_selective_scan_bwd_reuses_forward_states():
+    dev, ref, dout, dout64 = _case(2, 64, 16, 512, 1, "f32", True, True, True, True, seed=399)
+    batch, dim, L = dev["u"].shape
+    ws = torch.empty(ss.selective_scan_workspace_bytes(batch, dim, 16, L, 1), dtype=torch.uint8, device="cuda")
+    ss.selective_scan_fwd(**dev, delta_softplus=True, workspace=ws)
+    g = ss.selective_scan_bwd(**dev, dout=dout, delta_softplus=True, workspace=ws, workspace_has_states=True)
+    r = oracle.ss_bwd(**ref, delta_softplus=True, dout=dout64)
+    for k in GRADS:
+        assert rel_err(to_f64(g[k]), r[k]) <= TOL_GRAD, k
+
+
+def _ss2d(batch, H, W, dim, N, dtype, z, seed):
+    inp = synth.make_ss2d_inputs(batch, H, W, dim, N, dtype, has_z=z, seed_base=seed, with_dout=True)
+    dev = dict(x=to_dev(inp["x"], dtype), delta=to_dev(inp["delta"], dtype), A=to_dev(inp["A"], "f32"),
+               B=to_dev(inp["B"], dtype), C=to_dev(inp["C"], dtype), D=to_dev(inp["D"], "f32"),
+               delta_bias=to_dev(inp["delta_bias"], "f32"), z=to_dev(inp["z"], dtype) if z else None)
+    ref = dict(x=f64(inp["x"], dtype), delta=f64(inp["delta"], dtype), A=inp["A"].astype(np.float64),
+               B=f64(inp["B"], dtype), C=f64(inp["C"], dtype), D=inp["D"].astype(np.float64),
+               delta_bias=inp["delta_bias"].astype(np.float64), z=f64(inp["z"], dtype) if z else None)
+    return dev, ref, to_dev(inp["dout"], dtype), f64(inp["dout"], dtype)
+
+
+SS2D_GRADS = ("dx", "ddelta", "dA", "dB", "dC", "dD", "ddelta_bias", "dz")
+SS2D_BWD_CASES = [
+    (1, 8, 8, 16, 4, "f32", True),
+    (2, 7, 9, 20, 16, "f32", True),
+    (2, 14, 14, 70, 16, "f32", False),
+    (1, 3, 40, 64, 8, "bf16", True),
+    (1, 64, 64, 64, 16, "f32", True),   # few rows: chunked
+    (1, 1, 1, 8, 4, "f32", True),
+]
+
+
+@pytest.mark.parametrize("case", SS2D_BWD_CASES, ids=[str(c) for c in SS2D_BWD_CASES])
+def test_ss2d_bwd(case):
+    batch, H, W, dim, N, dtype, z = case
+    dev, ref, dout, dout64 = _ss2d(batch, H, W, dim, N, dtype, z, seed=50 + H * W)
+    g = ss.ss2d_bwd(**dev, dout=dout)
+    r = oracle.ss2d_bwd(**ref, dout=dout64)
+    for k in SS2D_GRADS:
+        if r[k] is None:
+            assert g[k] is None
+            continue
+        e = rel_err(to_f64(g[k]), r[k])
+        assert e <= _tol(dtype), (k, e)
+
+
+def test_ss2d_bwd_tiny_config():
+    cfg = synth.CONFIGS[0]
+    dev, ref, dout, dout64 = _ss2d(cfg.batch, cfg.height, cfg.width, cfg.dim, cfg.dstate, cfg.dtype, cfg.has_z,
+                                   seed=cfg.index)
+    g = ss.ss2d_bwd(**dev, dout=dout)
+    r = oracle.ss2d_bwd(**ref, dout=dout64)
+    for k in SS2D_GRADS:
+        assert rel_err(to_f64(g[k]), r[k]) <= TOL_GRAD, k
+
+
+def test_ss2d_bwd_highres_config_full():
+    """The high-resolution workload (128x128, B=4, D=192, N=16, fp32) at full size against the
+    oracle's full fp64 gradients, in the launch configuration the benchmark uses."""
+    cfg = synth.CONFIGS[4]
+    inp = synth.make_config_inputs(cfg, with_dout=True)
+    dev = dict(x=to_dev(inp["x"], "f32"), delta=to_dev(inp["delta"], "f32"), A=to_dev(inp["A"], "f32"),
+               B=to_dev(inp["B"], "f32"), C=to_dev(inp["C"], "f32"), D=to_dev(inp["D"], "f32"),
+               delta_bias=to_dev(inp["delta_bias"], "f32"), z=to_dev(inp["z"], "f32"))
+    g = ss.ss2d_bwd(**dev, dout=to_dev(inp["dout"], "f32"))
+    torch.cuda.synchronize()
+    ref = {k: inp[k].astype(np.float64) for k in ("x", "delta", "A", "B", "C", "D", "delta_bias", "z")}
+    r = oracle.ss2d_bwd(**ref, dout=inp["dout"].astype(np.float64))
+    for k in SS2D_GRADS:
+        e = rel_err(to_f64(g[k]), r[k])
+        assert e <= TOL_GRAD, (k, e)
