@@ -80,16 +80,20 @@ def load_traffic(workload_name):
     return entry.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, inp, target_s):
-    """The fp64 oracle (as it stands) on the first images of the same batch."""
+def cpu_baseline(cfg, inp, target_s, bwd=False):
+    """The fp64 oracle (as it stands) on the first images of the same batch (forward, or
+    forward + backward when the GPU step includes the backward)."""
     import oracle
     from selective_scan_amd import synth
 
     def run(nb):
         sl = lambda a: None if a is None else synth.storage_to_f64(a[:nb], cfg.dtype)
+        args = (sl(inp["x"]), sl(inp["delta"]), inp["A"].astype(np.float64), sl(inp["B"]), sl(inp["C"]),
+                inp["D"].astype(np.float64), inp["delta_bias"].astype(np.float64), sl(inp["z"]))
         t0 = time.perf_counter()
-        oracle.ss2d_fwd(sl(inp["x"]), sl(inp["delta"]), inp["A"].astype(np.float64), sl(inp["B"]), sl(inp["C"]),
-                        inp["D"].astype(np.float64), inp["delta_bias"].astype(np.float64), sl(inp["z"]))
+        oracle.ss2d_fwd(*args)
+        if bwd:
+            oracle.ss2d_bwd(*args, dout=sl(inp["dout"]))
         return time.perf_counter() - t0
 
     t1 = run(1)
@@ -99,7 +103,8 @@ def cpu_baseline(cfg, inp, target_s):
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     return {"value": elems / t, "unit": "elements/s", "cores": threads, "kind": "oracle",
             "sample": f"first {nb} of {cfg.batch} images (all {cfg.dim} channels, 4 routes, "
-                      f"L={cfg.seqlen}, N={cfg.dstate}), fp64 C oracle with OpenMP, {t:.2f} s wall"}
+                      f"L={cfg.seqlen}, N={cfg.dstate}), fp64 C oracle with OpenMP, "
+                      f"{'forward + backward' if bwd else 'forward'}, {t:.2f} s wall"}
 
 
 def main():
@@ -186,7 +191,7 @@ def main():
                      "ms_per_launch": scan_ms, "flops_per_launch": flops},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds, args.bwd)
     print(json.dumps(res))
 
 

@@ -25,8 +25,12 @@ namespace ss2d {
 namespace fwd_detail {
 using namespace scan_detail;
 
-template <typename T, int NS, bool kSS2D, bool kVec, int kPass>
+// kPass: 0 = outputs from the chunk-start state, 1 = chunk-local end state (chunked only),
+//        2 = as 0 and also the state before every kSub-th step (checkpoints for the backward).
+template <typename T, int NS, bool kSS2D, bool kVec, int kPassArg>
 __global__ __launch_bounds__(kWave) void scan_fwd_kernel(const ScanFwdParams p) {
+  constexpr int kPass = kPassArg == 2 ? 0 : kPassArg;
+  constexpr bool kStore = kPassArg == 2;
   constexpr int S = (NS < 4) ? 4 : NS + 4;  // LDS row stride (floats), keeps float4 alignment
   constexpr int kSub = ckpt_steps(NS);       // the state is checkpointed before every kSub-th step
   __shared__ __align__(16) float sB[kTile * S];
@@ -69,6 +73,7 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(const ScanFwdParams p) 
   const float bias = p.delta_bias ? p.delta_bias[d] : 0.0f;
   const float Dd = (!kSS2D && p.Dskip) ? p.Dskip[d] : 0.0f;
 
+  const bool softplus = p.softplus != 0;
   const int64_t t_begin = int64_t(c) * p.chunk_len;
   const int64_t t_end = (t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L;
 
@@ -106,29 +111,32 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(const ScanFwdParams p) 
     }
 
     const int nt = int((t_end - t0 < kTile) ? (t_end - t0) : kTile);
-    // per-step quantities: Lam (log2-domain step) and Lam * u
-    float lam[kTile], du[kTile];
-    if (p.softplus) {
+    // The tile is processed in groups of 4 steps: per-step quantities, recurrence, epilogue and
+    // a 4-element store per group, so that only a group's worth of temporaries is live.
 #pragma unroll
-      for (int i = 0; i < kTile; ++i) lam[i] = softplus_log2((cd.get(i) + bias) * kLog2e);
-    } else {
+    for (int g4 = 0; g4 < kTile / 4; ++g4) {
+      float lam[4], du[4], y[4];
 #pragma unroll
-      for (int i = 0; i < kTile; ++i) lam[i] = (cd.get(i) + bias) * kLog2e;
-    }
-    // Steps past the end of the range get Lam = 0: decay exp2(0) = 1 and zero input (B/C are
-    // zero-filled there), so the state passes through unchanged and no per-step branch is needed.
+      for (int k = 0; k < 4; ++k) {
+        const int i = 4 * g4 + k;
+        const float w = (cd.get(i) + bias) * kLog2e;
+        float l = softplus_log2(w);
+        l = softplus ? l : w;  // branch-free: keeps the steps in one straight-line block
+        // Steps past the end of the range get Lam = 0: decay exp2(0) = 1 and zero input (B/C
+        // are zero-filled there), so the state passes through unchanged without a branch.
+        l = (i < nt) ? l : 0.0f;
+        lam[k] = l;
+        du[k] = l * cu.get(i);
+      }
 #pragma unroll
-    for (int i = 0; i < kTile; ++i) {
-      lam[i] = (i < nt) ? lam[i] : 0.0f;
-      du[i] = lam[i] * cu.get(i);
-    }
-
-    float y[kTile];
-#pragma unroll
-    for (int i = 0; i < kTile; ++i) {
-      if (kPass == 0 && (i % kSub) == 0 && i < nt && p.ckpt != nullptr && active)
-        store_state<NS>(p.ckpt + (row * p.n_ckpt + (t0 + i) / kSub) * N, h, N);
-      {
+      for (int k = 0; k < 4; ++k) {
+        const int i = 4 * g4 + k;
+        // compiler barrier: the LDS reads of a step's B/C are not hoisted above earlier steps
+        // (that would keep several steps' values live at once and exceed the register file)
+        asm volatile("" ::: "memory");
+        if (kStore && (i % kSub) == 0) {
+          if (i < nt && active) store_state<NS>(p.ckpt + (row * p.n_ckpt + (t0 + i) / kSub) * N, h, N);
+        }
         const float4* bt = reinterpret_cast<const float4*>(sB + i * S);
         const float4* ct = reinterpret_cast<const float4*>(sC + i * S);
         float acc = 0.0f;
@@ -141,39 +149,42 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(const ScanFwdParams p) 
             if (kPass == 0) cc = ct[n4];
             const float cv[4] = {cc.x, cc.y, cc.z, cc.w};
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const int n = 4 * n4 + k;
-              const float a = fast_exp2(lam[i] * Acoef[n]);
-              h[n] = fmaf(a, h[n], du[i] * bv[k]);
-              if (kPass == 0) acc = fmaf(cv[k], h[n], acc);
+            for (int j = 0; j < 4; ++j) {
+              const int n = 4 * n4 + j;
+              const float a = fast_exp2(lam[k] * Acoef[n]);
+              h[n] = fmaf(a, h[n], du[k] * bv[j]);
+              if (kPass == 0) acc = fmaf(cv[j], h[n], acc);
             }
           }
         } else {
 #pragma unroll
           for (int n = 0; n < NS; ++n) {
-            const float a = fast_exp2(lam[i] * Acoef[n]);
-            h[n] = fmaf(a, h[n], du[i] * sB[i * S + n]);
+            const float a = fast_exp2(lam[k] * Acoef[n]);
+            h[n] = fmaf(a, h[n], du[k] * sB[i * S + n]);
             if (kPass == 0) acc = fmaf(sC[i * S + n], h[n], acc);
           }
         }
-        y[i] = acc;
-        if (kPass == 1) lam_sum += lam[i];
+        // pin the output here: otherwise the C*h sums are sunk into the (lane-conditional) store
+        // block at the end of the group, which keeps every step's states live until then
+        if (kPass == 0) asm volatile("" : "+v"(acc));
+        y[k] = acc;
+        if (kPass == 1) lam_sum += lam[k];
       }
-    }
-
-    if (kPass == 0 && p.out != nullptr && active) {
-      if (!kSS2D) {
-        if (p.Dskip) {
+      if (kPass == 0 && p.out != nullptr && active) {
+        const int64_t tg = t0 + 4 * g4;
+        if (!kSS2D) {
+          if (p.Dskip) {
 #pragma unroll
-          for (int i = 0; i < kTile; ++i) y[i] = fmaf(Dd, cu.get(i), y[i]);
-        }
-        if (has_z) {
+            for (int k = 0; k < 4; ++k) y[k] = fmaf(Dd, cu.get(4 * g4 + k), y[k]);
+          }
+          if (has_z) {
 #pragma unroll
-          for (int i = 0; i < kTile; ++i) y[i] *= silu(cz.get(i));
+            for (int k = 0; k < 4; ++k) y[k] *= silu(cz.get(4 * g4 + k));
+          }
+          store_seg<T, kVec, 4>(static_cast<T*>(p.out) + row * L, y, tg, t_end);
+        } else {
+          store_seg<float, kVec, 4>(static_cast<float*>(p.out) + row * L, y, tg, t_end);
         }
-        store_out<T, kVec>(static_cast<T*>(p.out) + row * L, y, t0, t_end);
-      } else {
-        store_out<float, kVec>(static_cast<float*>(p.out) + row * L, y, t0, t_end);
       }
     }
   }
@@ -193,6 +204,8 @@ hipError_t launch_t(const ScanFwdParams& p, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   if (p.pass == 1)
     scan_fwd_kernel<T, NS, kSS2D, kVec, 1><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
+  else if (p.ckpt != nullptr)
+    scan_fwd_kernel<T, NS, kSS2D, kVec, 2><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
   else
     scan_fwd_kernel<T, NS, kSS2D, kVec, 0><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
   return hipGetLastError();

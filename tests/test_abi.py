@@ -1,0 +1,152 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function
+include/ss2d.h declares, the binding's argument blocks match the header's struct layouts, and
+invalid arguments are rejected with the documented status before anything is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ss2d.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from selective_scan_amd import _binding
+    if not os.path.exists(_binding.LIB_PATH):
+        from selective_scan_amd import build
+        build.build()
+    return _binding.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "return")))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"ss2d_cross_scan", "ss2d_cross_merge", "selective_scan_fwd", "selective_scan_bwd", "ss2d_fwd",
+            "ss2d_bwd", "ss2d_fwd_stage", "selective_scan_workspace_bytes", "ss2d_workspace_bytes",
+            "ss2d_abi_version", "ss2d_status_string"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        getattr(lib, n)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ss2d_abi_version() == 1
+    assert lib.ss2d_status_string(0) == b"ok"
+    assert b"invalid" in lib.ss2d_status_string(1)
+    assert b"unsupported" in lib.ss2d_status_string(2)
+    assert lib.ss2d_status_string(99) == b"unknown status"
+
+
+STRUCTS = {"ss_fwd_args": "SsFwdArgs", "ss_bwd_args": "SsBwdArgs", "ss2d_fwd_args": "SS2DFwdArgs",
+           "ss2d_bwd_args": "SS2DBwdArgs"}
+
+
+def test_binding_structs_match_header(tmp_path):
+    """Compile a probe against the header with the host C compiler and compare every field offset."""
+    from selective_scan_amd import _binding
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ss2d.h"', "int main(void) {"]
+    for cname, pyname in STRUCTS.items():
+        st = getattr(_binding, pyname)
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in st._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "probe.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    subprocess.check_call(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I",
+                           "/opt/rocm/include", str(src), "-o", str(exe)])
+    out = subprocess.check_output([str(exe)], text=True).split("\n")
+    got = {}
+    for line in out:
+        if line:
+            s, f, v = line.split()
+            got[(s, f)] = int(v)
+    for cname, pyname in STRUCTS.items():
+        st = getattr(_binding, pyname)
+        assert got[(cname, "size")] == ctypes.sizeof(st), cname
+        for f, _ in st._fields_:
+            assert got[(cname, f)] == getattr(st, f).offset, (cname, f)
+
+
+def _fwd_args(**kw):
+    from selective_scan_amd._binding import SsFwdArgs
+    base = dict(u=0x1000, delta=0x2000, A=0x3000, Bm=0x4000, Cm=0x5000, out=0x6000, batch=2, dim=8, dstate=4,
+                seqlen=16, ngroups=1, dtype=0, delta_softplus=1)
+    base.update(kw)
+    return SsFwdArgs(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dstate=0), 2), (dict(dstate=65), 2), (dict(dtype=7), 2), (dict(ngroups=3), 1), (dict(ngroups=0), 1),
+    (dict(batch=-1), 1), (dict(u=0), 1), (dict(out=0), 1), (dict(A=0), 1), (dict(u=0x1001), 1),
+    (dict(workspace=0x10000, workspace_bytes=16), 1),
+])
+def test_selective_scan_fwd_rejects(lib, kw, status):
+    a = _fwd_args(**kw)
+    assert lib.selective_scan_fwd(ctypes.byref(a), None) == status
+
+
+def test_selective_scan_fwd_empty_is_noop(lib):
+    assert lib.selective_scan_fwd(ctypes.byref(_fwd_args(batch=0, u=0, delta=0, out=0)), None) == 0
+    assert lib.selective_scan_fwd(ctypes.byref(_fwd_args(seqlen=0)), None) == 0
+    assert lib.selective_scan_fwd(None, None) == 1
+
+
+def test_selective_scan_bwd_rejects(lib):
+    from selective_scan_amd._binding import SsBwdArgs
+    base = dict(u=0x1000, delta=0x2000, A=0x3000, Bm=0x4000, Cm=0x5000, dout=0x6000, du=0x7000, ddelta=0x8000,
+                dA=0x9000, dBm=0xa000, dCm=0xb000, workspace=0x10000, workspace_bytes=1, batch=2, dim=8,
+                dstate=4, seqlen=16, ngroups=1, dtype=0, delta_softplus=1)
+    assert lib.selective_scan_bwd(ctypes.byref(SsBwdArgs(**base)), None) == 1           # workspace too small
+    assert lib.selective_scan_bwd(ctypes.byref(SsBwdArgs(**{**base, "z": 0xc000})), None) == 1  # z without dz
+    assert lib.selective_scan_bwd(ctypes.byref(SsBwdArgs(**{**base, "dstate": 100})), None) == 2
+    assert lib.selective_scan_bwd(ctypes.byref(SsBwdArgs(**{**base, "dim": 0})), None) == 0
+
+
+def test_ss2d_rejects(lib):
+    from selective_scan_amd._binding import SS2DBwdArgs, SS2DFwdArgs
+    f = dict(x=0x1000, delta=0x2000, A=0x3000, Bm=0x4000, Cm=0x5000, out=0x6000, workspace=0x10000,
+             workspace_bytes=1, batch=1, dim=4, height=3, width=5, dstate=4, dtype=1, delta_softplus=1)
+    assert lib.ss2d_fwd(ctypes.byref(SS2DFwdArgs(**f)), None) == 1                       # workspace too small
+    assert lib.ss2d_fwd(ctypes.byref(SS2DFwdArgs(**{**f, "workspace": 0})), None) == 1
+    assert lib.ss2d_fwd(ctypes.byref(SS2DFwdArgs(**{**f, "dtype": 3})), None) == 2
+    assert lib.ss2d_fwd(ctypes.byref(SS2DFwdArgs(**{**f, "height": 0})), None) == 0       # empty map
+    assert lib.ss2d_fwd_stage(ctypes.byref(SS2DFwdArgs(**f)), 3, None) == 1               # bad stage
+    b = dict(x=0x1000, delta=0x2000, A=0x3000, Bm=0x4000, Cm=0x5000, dout=0x6000, dx=0x7000, ddelta=0x8000,
+             dA=0x9000, dBm=0xa000, dCm=0xb000, workspace=0x10000, workspace_bytes=1, batch=1, dim=4, height=3,
+             width=5, dstate=4, dtype=0, delta_softplus=1)
+    assert lib.ss2d_bwd(ctypes.byref(SS2DBwdArgs(**b)), None) == 1
+    assert lib.ss2d_bwd(ctypes.byref(SS2DBwdArgs(**{**b, "Dskip": 0xc000})), None) == 1  # D without dD
+
+
+def test_cross_scan_merge_reject(lib):
+    assert lib.ss2d_cross_scan(None, None, 1, 1, 2, 2, 0, None) == 1
+    assert lib.ss2d_cross_scan(0x1000, 0x2000, 1, 1, 2, 2, 5, None) == 2
+    assert lib.ss2d_cross_scan(0x1000, 0x2000, -1, 1, 2, 2, 0, None) == 1
+    assert lib.ss2d_cross_scan(None, None, 0, 1, 2, 2, 0, None) == 0   # empty: nothing to do
+    assert lib.ss2d_cross_merge(0x1001, 0x2000, 1, 1, 2, 2, 0, None) == 1  # misaligned fp32
+
+
+def test_workspace_queries(lib):
+    a = lib.selective_scan_workspace_bytes(2, 64, 16, 256, 1)
+    b = lib.selective_scan_workspace_bytes(2, 64, 16, 512, 1)
+    assert 0 < a < b
+    assert lib.selective_scan_workspace_bytes(2, 64, 0, 256, 1) == 0
+    s1 = lib.ss2d_workspace_bytes(1, 16, 8, 8, 4, 0)
+    s2 = lib.ss2d_workspace_bytes(1, 16, 8, 8, 4, 1)
+    assert 0 < s2 < s1  # the transposed copy of x is narrower in bf16
+    assert lib.ss2d_workspace_bytes(1, 16, 8, 8, 4, 9) == 0
+    assert all(v % 256 == 0 for v in (a, b, s1, s2))
