@@ -25,6 +25,10 @@ struct ScanOutputs {
 hipError_t launch_route_scatter(const void* x, const ScanOutputs& o, int64_t batch, int64_t C, int64_t H,
                                 int64_t W, int elem_bytes, hipStream_t s);
 
+// Per-plane transpose x (batch, C, H, W) -> xT (batch, C, W*H) in column-major route order.
+hipError_t launch_transpose(const void* x, void* xT, int64_t batch, int64_t C, int64_t H, int64_t W, int elem_bytes,
+                            hipStream_t s);
+
 // y[b, c, p] = (((r0 + r1) + r2) + r3)[p] (+ Dsum[c] * x[b, c, p]) (* silu(z[b, c, p])) with route
 // inputs in route order (fp32 when routes_f32, else dtype), grid outputs in dtype.
 // Optionally also writes the fp32 pre-gate sum to merged_f32.
@@ -86,6 +90,7 @@ struct ScanFwdParams {
   int dtype;
   int vec;             // 4-element vector access allowed
   int pass;            // 0: outputs/checkpoints from the stored chunk-start state; 1: chunk-local end state
+  int store_states;    // pass 0 also keeps the state before every ckpt_every-th step in ckpt
 };
 hipError_t launch_scan_fwd(const ScanFwdParams& p, hipStream_t s);
 // Turns the chunk-local end states (pass 1) into the true chunk-start states.

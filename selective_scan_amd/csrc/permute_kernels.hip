@@ -167,6 +167,117 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(GateBwdArgs a, int tiles_
   }
 }
 
+// ---- plane-resident variants: one workgroup per (b, c) plane ---------------------------------
+// Used when the plane (and, for the merge, its two column-major routes in fp32) fits in LDS.
+// Global reads and writes are 4 consecutive elements per thread, contiguous across threads.
+
+constexpr int kPlaneThreads = 256;
+
+// xT[b, c, w*H + h] = x[b, c, h*W + w]  (the column-major route order, not reversed)
+template <typename W>
+__global__ __launch_bounds__(kPlaneThreads) void transpose_plane_kernel(const W* __restrict__ x, W* __restrict__ xT,
+                                                                         int H, int Wd) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  W* tile = reinterpret_cast<W*>(smem);  // [h][w], row stride Wd + 1
+  const int64_t L = int64_t(H) * Wd;
+  const W* xp = x + int64_t(blockIdx.x) * L;
+  W* op = xT + int64_t(blockIdx.x) * L;
+  const int ld = Wd + 1;
+  // read the plane in grid order: 4 consecutive pixels per thread (Wd % 4 == 0)
+  for (int64_t q = 4 * int64_t(threadIdx.x); q < L; q += 4 * kPlaneThreads) {
+    const int h = int(q / Wd), w = int(q % Wd);
+    W v[4];
+    if (sizeof(W) == 2) {
+      const uint2 raw = *reinterpret_cast<const uint2*>(xp + q);
+      v[0] = W(raw.x & 0xffff); v[1] = W(raw.x >> 16); v[2] = W(raw.y & 0xffff); v[3] = W(raw.y >> 16);
+    } else {
+      const uint4 raw = *reinterpret_cast<const uint4*>(xp + q);
+      v[0] = W(raw.x); v[1] = W(raw.y); v[2] = W(raw.z); v[3] = W(raw.w);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tile[h * ld + w + j] = v[j];
+  }
+  __syncthreads();
+  // write in column-major order: t = w*H + h, 4 consecutive t per thread (H % 4 == 0)
+  for (int64_t t = 4 * int64_t(threadIdx.x); t < L; t += 4 * kPlaneThreads) {
+    const int w = int(t / H), h = int(t % H);
+    W v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = tile[(h + j) * ld + w];
+    if (sizeof(W) == 2) {
+      uint2 raw;
+      raw.x = uint32_t(v[0]) | (uint32_t(v[1]) << 16);
+      raw.y = uint32_t(v[2]) | (uint32_t(v[3]) << 16);
+      *reinterpret_cast<uint2*>(op + t) = raw;
+    } else {
+      *reinterpret_cast<uint4*>(op + t) = make_uint4(uint32_t(v[0]), uint32_t(v[1]), uint32_t(v[2]), uint32_t(v[3]));
+    }
+  }
+}
+
+// The SS2D merge with fp32 routes: y = (((r0 + r1) + r2) + r3) [+ Dsum * x] [* silu(z)], per plane.
+template <typename T>
+__global__ __launch_bounds__(kPlaneThreads) void merge_plane_kernel(MergeArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int H = int(a.H), Wd = int(a.W);
+  const int64_t L = int64_t(H) * Wd;
+  const int ld = H + 1;                    // [w][h] with an odd row stride: conflict-free column reads
+  float* t1 = reinterpret_cast<float*>(smem);
+  float* t3 = t1 + int64_t(Wd) * ld;
+  const int64_t plane = int64_t(blockIdx.x);  // b * C + c
+  const int64_t b = plane / a.C, c = plane % a.C;
+  const float* r0 = static_cast<const float*>(a.routes) + (b * 4 * a.C + c) * L;
+  const float* r1 = r0 + a.C * L;
+  const float* r2 = r1 + a.C * L;
+  const float* r3 = r2 + a.C * L;
+  // routes 1 and 3 are in column-major order: t1[w][h] = r1[w*H + h], t3[w][h] = r3[L-1-(w*H + h)]
+  for (int64_t t = 4 * int64_t(threadIdx.x); t < L; t += 4 * kPlaneThreads) {
+    const float4 v1 = *reinterpret_cast<const float4*>(r1 + t);
+    const float4 v3 = *reinterpret_cast<const float4*>(r3 + (L - 4 - t));  // route-3 steps L-4-t .. L-1-t
+    const float a1[4] = {v1.x, v1.y, v1.z, v1.w};
+    const float a3[4] = {v3.w, v3.z, v3.y, v3.x};  // pixel order t .. t+3
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t q = t + j;
+      const int w = int(q / H), h = int(q % H);
+      t1[w * ld + h] = a1[j];
+      t3[w * ld + h] = a3[j];
+    }
+  }
+  __syncthreads();
+  float dsum = 0.0f;
+  if (a.Dskip) dsum = ((a.Dskip[c] + a.Dskip[a.C + c]) + a.Dskip[2 * a.C + c]) + a.Dskip[3 * a.C + c];
+  const T* xg = static_cast<const T*>(a.x) + plane * L;
+  const T* zg = a.z ? static_cast<const T*>(a.z) + plane * L : nullptr;
+  T* yg = a.y ? static_cast<T*>(a.y) + plane * L : nullptr;
+  float* mg = a.merged_f32 ? a.merged_f32 + plane * L : nullptr;
+  for (int64_t p = 4 * int64_t(threadIdx.x); p < L; p += 4 * kPlaneThreads) {
+    const int h = int(p / Wd), w = int(p % Wd);  // Wd % 4 == 0: the 4 pixels share row h
+    const float4 v0 = *reinterpret_cast<const float4*>(r0 + p);
+    const float4 v2 = *reinterpret_cast<const float4*>(r2 + (L - 4 - p));
+    const float a0[4] = {v0.x, v0.y, v0.z, v0.w};
+    const float a2[4] = {v2.w, v2.z, v2.y, v2.x};
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float s = a0[j] + t1[(w + j) * ld + h];
+      s = s + a2[j];
+      v[j] = s + t3[(w + j) * ld + h];
+    }
+    if (a.Dskip && a.x) {
+      const float4 xv = Elem<T>::load4(xg, p);
+      v[0] = fmaf(dsum, xv.x, v[0]); v[1] = fmaf(dsum, xv.y, v[1]);
+      v[2] = fmaf(dsum, xv.z, v[2]); v[3] = fmaf(dsum, xv.w, v[3]);
+    }
+    if (mg) *reinterpret_cast<float4*>(mg + p) = make_float4(v[0], v[1], v[2], v[3]);
+    if (zg) {
+      const float4 zv = Elem<T>::load4(zg, p);
+      v[0] *= silu(zv.x); v[1] *= silu(zv.y); v[2] *= silu(zv.z); v[3] *= silu(zv.w);
+    }
+    if (yg) Elem<T>::store4(yg, p, make_float4(v[0], v[1], v[2], v[3]));
+  }
+}
+
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
@@ -196,7 +307,24 @@ hipError_t launch_route_scatter(const void* x, const ScanOutputs& o, int64_t bat
   return hipGetLastError();
 }
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
+  const int64_t L = a.H * a.W;
+  const size_t plane_lds = size_t(2) * size_t(a.W) * size_t(a.H + 1) * 4;
+  if (a.routes_f32 && a.W % 4 == 0 && a.H % 4 == 0 && plane_lds <= 64 * 1024 && a.batch * a.C > 0 &&
+      aligned16(a.routes) && (!a.merged_f32 || aligned16(a.merged_f32)) &&
+      (a.dtype == 0 ? (aligned16(a.y) && aligned16(a.x) && aligned16(a.z))
+                    : ((reinterpret_cast<uintptr_t>(a.y) | reinterpret_cast<uintptr_t>(a.x) |
+                        reinterpret_cast<uintptr_t>(a.z)) & 7) == 0) &&
+      L % 4 == 0) {
+    const dim3 g{uint32_t(a.batch * a.C)}, b{kPlaneThreads};
+    if (a.dtype == 0)
+      merge_plane_kernel<float><<<g, b, plane_lds, s>>>(a);
+    else
+      merge_plane_kernel<bf16><<<g, b, plane_lds, s>>>(a);
+    return hipGetLastError();
+  }
   const int th = int(cdiv(a.H, kT)), tw = int(cdiv(a.W, kT));
   const int64_t blocks = a.batch * a.C * th * tw;
   if (blocks == 0) return hipSuccess;
@@ -209,6 +337,27 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
     merge_kernel<bf16, bf16><<<g, b, 0, s>>>(a, th, tw);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_transpose(const void* x, void* xT, int64_t batch, int64_t C, int64_t H, int64_t W, int elem_bytes,
+                            hipStream_t s) {
+  const int64_t planes = batch * C;
+  if (planes == 0 || H * W == 0) return hipSuccess;
+  const size_t lds = size_t(H) * size_t(W + 1) * size_t(elem_bytes);
+  const uintptr_t al = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(xT);
+  if (W % 4 == 0 && H % 4 == 0 && lds <= 64 * 1024 && (al % (4 * elem_bytes)) == 0) {
+    if (elem_bytes == 2)
+      transpose_plane_kernel<uint16_t><<<dim3(uint32_t(planes)), dim3(kPlaneThreads), lds, s>>>(
+          static_cast<const uint16_t*>(x), static_cast<uint16_t*>(xT), int(H), int(W));
+    else
+      transpose_plane_kernel<uint32_t><<<dim3(uint32_t(planes)), dim3(kPlaneThreads), lds, s>>>(
+          static_cast<const uint32_t*>(x), static_cast<uint32_t*>(xT), int(H), int(W));
+    return hipGetLastError();
+  }
+  ScanOutputs o{};
+  o.out[1] = xT;
+  o.batch_stride = C * H * W;
+  return launch_route_scatter(x, o, batch, C, H, W, elem_bytes, s);
 }
 
 hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t s) {

@@ -184,16 +184,17 @@ __device__ __forceinline__ void store_out(O* row, const float* y, int64_t t0, in
   }
 }
 
+// Store the first `count` (<= NS) of NS state values; 16-byte stores when NS and count allow.
 template <int NS>
-__device__ __forceinline__ void store_state(float* dst, const float* h, int N) {
-  if (NS % 4 == 0 && (N % 4) == 0) {
+__device__ __forceinline__ void store_state(float* dst, const float* h, int count) {
+  if (NS % 4 == 0 && (count % 4) == 0) {
 #pragma unroll
     for (int n = 0; n < NS; n += 4)
-      if (n < N) *reinterpret_cast<float4*>(dst + n) = make_float4(h[n], h[n + 1], h[n + 2], h[n + 3]);
+      if (n < count) *reinterpret_cast<float4*>(dst + n) = make_float4(h[n], h[n + 1], h[n + 2], h[n + 3]);
   } else {
 #pragma unroll
     for (int n = 0; n < NS; ++n)
-      if (n < N) dst[n] = h[n];
+      if (n < count) dst[n] = h[n];
   }
 }
 

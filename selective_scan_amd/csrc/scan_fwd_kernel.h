@@ -3,11 +3,13 @@
 //   delta_t = softplus(delta_raw_t + bias[d]);  h_t = exp(delta_t A[d,:]) h_{t-1} + delta_t B_t u_t
 //   y_t = <C_t, h_t> + D[d] u_t ;  out_t = y_t * silu(z_t)
 //
-// Mapping on CDNA4: one wavefront = 64 consecutive channels d of one (batch, group) pair, so
-// that B_t / C_t (shared by the channels of a group) are wave-uniform: they are staged per
-// 32-step tile in LDS as fp32 and read back as broadcasts.  Each lane runs its channel's
-// recurrence sequentially with the N-entry state in VGPRs; the loads of its own row (delta, u,
-// z) are 4-element vectors, prefetched one tile ahead.
+// Mapping on CDNA4: one wavefront = consecutive channels d of one (batch, group) pair, so that
+// B_t / C_t (shared by the channels of a group) are wave-uniform: they are staged per 32-step
+// tile in LDS as fp32 and read back as broadcasts.  Each channel's recurrence runs sequentially
+// with its state in VGPRs: for N <= 8 one lane per channel (64 channels per wavefront); for
+// N >= 16 two adjacent lanes per channel, each holding half of the states (32 channels per
+// wavefront, twice the wavefronts), the two halves of y_t added with one DPP lane swap.  The
+// loads of a channel's own row (delta, u, z) are 4-element vectors, prefetched one tile ahead.
 //
 // Arithmetic is carried in base 2: with Lam = log2(1 + 2^(v log2 e)) (so delta = ln2 * Lam),
 //   exp(delta * A) = exp2(Lam * A)    and    delta * u * B = Lam * u * (ln2 * B),
@@ -27,16 +29,21 @@ using namespace scan_detail;
 
 // kPass: 0 = outputs from the chunk-start state, 1 = chunk-local end state (chunked only),
 //        2 = as 0 and also the state before every kSub-th step (checkpoints for the backward).
-template <typename T, int NS, bool kSS2D, bool kVec, int kPassArg>
+// kSplit: lanes per channel (1 or 2); NSL = NS / kSplit states per lane.
+template <typename T, int NS, int kSplit, bool kSS2D, bool kVec, int kPassArg>
 __global__ __launch_bounds__(kWave) void scan_fwd_kernel(const ScanFwdParams p) {
   constexpr int kPass = kPassArg == 2 ? 0 : kPassArg;
   constexpr bool kStore = kPassArg == 2;
+  constexpr int NSL = NS / kSplit;
+  constexpr int kRows = kWave / kSplit;      // channels per wavefront
   constexpr int S = (NS < 4) ? 4 : NS + 4;  // LDS row stride (floats), keeps float4 alignment
   constexpr int kSub = ckpt_steps(NS);       // the state is checkpointed before every kSub-th step
   __shared__ __align__(16) float sB[kTile * S];
   __shared__ __align__(16) float sC[kTile * S];
 
   const int lane = threadIdx.x;
+  const int part = lane % kSplit;            // which half of the states this lane holds
+  const int n0 = part * NSL;                 // first state of this lane
   int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t dblk = bid % p.dblocks;
   bid /= p.dblocks;
@@ -44,7 +51,7 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(const ScanFwdParams p) 
   bid /= p.n_chunks;
   const int64_t g = bid % p.G;
   const int64_t b = bid / p.G;
-  const int64_t dg = dblk * kWave + lane;
+  const int64_t dg = dblk * kRows + lane / kSplit;
   const bool active = dg < p.per_group;
   const int64_t dl = active ? dg : 0;
   const int64_t d = g * p.per_group + dl;
@@ -67,9 +74,10 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(const ScanFwdParams p) 
   const T* Bg = static_cast<const T*>(p.Bm) + (b * p.G + g) * N * L;
   const T* Cg = static_cast<const T*>(p.Cm) + (b * p.G + g) * N * L;
 
-  float Acoef[NS];
+  float Acoef[NSL];
 #pragma unroll
-  for (int n = 0; n < NS; ++n) Acoef[n] = (n < N) ? p.A[d * N + n] : 0.0f;
+  for (int n = 0; n < NSL; ++n) Acoef[n] = (n0 + n < N) ? p.A[d * N + n0 + n] : 0.0f;
+  const int nvalid = (N - n0 < 0) ? 0 : ((N - n0 > NSL) ? NSL : N - n0);  // real states of this lane
   const float bias = p.delta_bias ? p.delta_bias[d] : 0.0f;
   const float Dd = (!kSS2D && p.Dskip) ? p.Dskip[d] : 0.0f;
 
@@ -77,14 +85,14 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(const ScanFwdParams p) 
   const int64_t t_begin = int64_t(c) * p.chunk_len;
   const int64_t t_end = (t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L;
 
-  float h[NS];
+  float h[NSL];
 #pragma unroll
-  for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+  for (int n = 0; n < NSL; ++n) h[n] = 0.0f;
   if (kPass == 0 && p.n_chunks > 1 && c > 0) {
-    const float* src = p.ckpt + (row * p.n_ckpt + t_begin / kSub) * N;
+    const float* src = p.ckpt + (row * p.n_ckpt + t_begin / kSub) * N + n0;
 #pragma unroll
-    for (int n = 0; n < NS; ++n)
-      if (n < N) h[n] = src[n];
+    for (int n = 0; n < NSL; ++n)
+      if (n < nvalid) h[n] = src[n];
   }
   float lam_sum = 0.0f;
 
@@ -111,6 +119,31 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(const ScanFwdParams p) 
     }
 
     const int nt = int((t_end - t0 < kTile) ? (t_end - t0) : kTile);
+    // One step's B (times ln 2) and C from LDS; the reads for step i+1 are issued while step i
+    // computes (software pipelining of the LDS latency).
+    float nb[NSL], nc[NSL];
+    auto read_bc = [&](int i) {
+      if (NSL >= 4) {
+        const float4* bt = reinterpret_cast<const float4*>(sB + i * S + n0);
+        const float4* ct = reinterpret_cast<const float4*>(sC + i * S + n0);
+#pragma unroll
+        for (int n4 = 0; n4 < NSL / 4; ++n4) {
+          const float4 bb = bt[n4];
+          nb[4 * n4] = bb.x; nb[4 * n4 + 1] = bb.y; nb[4 * n4 + 2] = bb.z; nb[4 * n4 + 3] = bb.w;
+          if (kPass == 0) {
+            const float4 cc = ct[n4];
+            nc[4 * n4] = cc.x; nc[4 * n4 + 1] = cc.y; nc[4 * n4 + 2] = cc.z; nc[4 * n4 + 3] = cc.w;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < NSL; ++n) {
+          nb[n] = sB[i * S + n0 + n];
+          if (kPass == 0) nc[n] = sC[i * S + n0 + n];
+        }
+      }
+    };
+    read_bc(0);
     // The tile is processed in groups of 4 steps: per-step quantities, recurrence, epilogue and
     // a 4-element store per group, so that only a group's worth of temporaries is live.
 #pragma unroll
@@ -131,46 +164,38 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(const ScanFwdParams p) 
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int i = 4 * g4 + k;
-        // compiler barrier: the LDS reads of a step's B/C are not hoisted above earlier steps
-        // (that would keep several steps' values live at once and exceed the register file)
+        // compiler barrier: LDS reads are not hoisted by more than one step (that would keep
+        // several steps' values live at once and exceed the register file)
         asm volatile("" ::: "memory");
         if (kStore && (i % kSub) == 0) {
-          if (i < nt && active) store_state<NS>(p.ckpt + (row * p.n_ckpt + (t0 + i) / kSub) * N, h, N);
+          if (i < nt && active) store_state<NSL>(p.ckpt + (row * p.n_ckpt + (t0 + i) / kSub) * N + n0, h, nvalid);
         }
-        const float4* bt = reinterpret_cast<const float4*>(sB + i * S);
-        const float4* ct = reinterpret_cast<const float4*>(sC + i * S);
+        float cb[NSL], cc[NSL];
+#pragma unroll
+        for (int n = 0; n < NSL; ++n) {
+          cb[n] = nb[n];
+          cc[n] = (kPass == 0) ? nc[n] : 0.0f;
+        }
+        if (i + 1 < kTile) read_bc(i + 1);
         float acc = 0.0f;
-        if (NS >= 4) {
 #pragma unroll
-          for (int n4 = 0; n4 < NS / 4; ++n4) {
-            const float4 bb = bt[n4];
-            const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
-            float4 cc = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (kPass == 0) cc = ct[n4];
-            const float cv[4] = {cc.x, cc.y, cc.z, cc.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int n = 4 * n4 + j;
-              const float a = fast_exp2(lam[k] * Acoef[n]);
-              h[n] = fmaf(a, h[n], du[k] * bv[j]);
-              if (kPass == 0) acc = fmaf(cv[j], h[n], acc);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int n = 0; n < NS; ++n) {
-            const float a = fast_exp2(lam[k] * Acoef[n]);
-            h[n] = fmaf(a, h[n], du[k] * sB[i * S + n]);
-            if (kPass == 0) acc = fmaf(sC[i * S + n], h[n], acc);
-          }
+        for (int n = 0; n < NSL; ++n) {
+          const float a = fast_exp2(lam[k] * Acoef[n]);
+          h[n] = fmaf(a, h[n], du[k] * cb[n]);
+          if (kPass == 0) acc = fmaf(cc[n], h[n], acc);
         }
+        // the two lanes of a channel hold complementary halves of sum_n C h: add the partner's
+        // (DPP quad_perm [1,0,3,2] swaps adjacent lanes)
+        if (kPass == 0 && kSplit == 2)
+          acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc), 0xB1, 0xF,
+                                                                       0xF, false));
         // pin the output here: otherwise the C*h sums are sunk into the (lane-conditional) store
         // block at the end of the group, which keeps every step's states live until then
         if (kPass == 0) asm volatile("" : "+v"(acc));
         y[k] = acc;
         if (kPass == 1) lam_sum += lam[k];
       }
-      if (kPass == 0 && p.out != nullptr && active) {
+      if (kPass == 0 && p.out != nullptr && active && part == 0) {
         const int64_t tg = t0 + 4 * g4;
         if (!kSS2D) {
           if (p.Dskip) {
@@ -191,33 +216,38 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(const ScanFwdParams p) 
 
   if (!active) return;
   if (kPass == 1) {
-    if (t_end < L) store_state<NS>(p.ckpt + (row * p.n_ckpt + t_end / kSub) * N, h, N);
-    p.chunk_sum[row * p.n_chunks + c] = lam_sum;
+    if (t_end < L) store_state<NSL>(p.ckpt + (row * p.n_ckpt + t_end / kSub) * N + n0, h, nvalid);
+    if (part == 0) p.chunk_sum[row * p.n_chunks + c] = lam_sum;
   } else if (p.last_state && t_end == L) {
-    store_state<NS>(p.last_state + row * N, h, N);
+    store_state<NSL>(p.last_state + row * N + n0, h, nvalid);
   }
 }
 
-template <typename T, int NS, bool kSS2D, bool kVec>
-hipError_t launch_t(const ScanFwdParams& p, hipStream_t s) {
+template <typename T, int NS, int kSplit, bool kSS2D, bool kVec>
+hipError_t launch_t(ScanFwdParams p, hipStream_t s) {
+  p.dblocks = (p.per_group + kWave / kSplit - 1) / (kWave / kSplit);
   const int64_t blocks = p.batch * p.G * p.dblocks * p.n_chunks;
   if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (p.pass == 1)
-    scan_fwd_kernel<T, NS, kSS2D, kVec, 1><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
-  else if (p.ckpt != nullptr)
-    scan_fwd_kernel<T, NS, kSS2D, kVec, 2><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
+    scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 1><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
+  else if (p.store_states)
+    scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 2><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
   else
-    scan_fwd_kernel<T, NS, kSS2D, kVec, 0><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
+    scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 0><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace fwd_detail
 
+// Two lanes per channel from 16 states up (halves the per-lane state and doubles the
+// wavefronts, which balances the stage-1 workload over the 1024 SIMDs).
 template <typename T, int NS>
 hipError_t scan_fwd_launch(const ScanFwdParams& p, hipStream_t s) {
   using namespace fwd_detail;
-  if (p.ss2d) return p.vec ? launch_t<T, NS, true, true>(p, s) : launch_t<T, NS, true, false>(p, s);
-  return p.vec ? launch_t<T, NS, false, true>(p, s) : launch_t<T, NS, false, false>(p, s);
+  constexpr int kSplit = NS >= 16 ? 2 : 1;
+  if (p.ss2d) return p.vec ? launch_t<T, NS, kSplit, true, true>(p, s) : launch_t<T, NS, kSplit, true, false>(p, s);
+  return p.vec ? launch_t<T, NS, kSplit, false, true>(p, s) : launch_t<T, NS, kSplit, false, false>(p, s);
 }
 
 }  // namespace ss2d

@@ -27,14 +27,16 @@ constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
 // ---- selective-scan workspace layout -------------------------------------------------
 // Split long sequences across wavefronts only when the rows alone cannot fill the GPU
 // (1024 SIMDs on MI355X; aim for at least two wavefronts per SIMD).  Chunks are whole tiles.
-void plan_chunks(int64_t row_waves, int64_t L, bool can_chunk, int64_t* chunk_len, int* n_chunks) {
+void plan_chunks(int64_t row_waves, int64_t L, int64_t dstate, bool can_chunk, int64_t* chunk_len, int* n_chunks) {
   const int64_t n_tiles = cdiv(L, kTile);
-  if (!can_chunk || row_waves >= 1024 || n_tiles <= 1) {
+  (void)dstate;
+  const int64_t target = 2048;
+  if (!can_chunk || row_waves >= target / 2 || n_tiles <= 1) {
     *chunk_len = (n_tiles > 0 ? n_tiles : 1) * kTile;
     *n_chunks = 1;
     return;
   }
-  int64_t want = cdiv(2048, row_waves);
+  int64_t want = cdiv(target, row_waves);
   if (want > n_tiles) want = n_tiles;
   const int64_t tiles_per_chunk = cdiv(n_tiles, want);
   *chunk_len = tiles_per_chunk * kTile;
@@ -54,7 +56,7 @@ ScanLayout scan_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqle
   l.n_ckpt = cdiv(seqlen, l.ckpt_every);
   l.per_group = ngroups > 0 ? dim / ngroups : 0;
   l.dblocks = cdiv(l.per_group, kWave);
-  plan_chunks(batch * ngroups * l.dblocks, seqlen, true, &l.chunk_len, &l.n_chunks);
+  plan_chunks(batch * ngroups * l.dblocks, seqlen, dstate, true, &l.chunk_len, &l.n_chunks);
   const int64_t nc = l.n_chunks;
   int64_t o = 0;
   l.off_ckpt = o;  o += align_up(l.rows * l.n_ckpt * dstate * 4);
@@ -213,7 +215,9 @@ int selective_scan_fwd(const ss_fwd_args* a, hipStream_t stream) {
   p.ss2d = 0;
   p.dtype = a->dtype;
   p.vec = (a->seqlen % 4 == 0) && vec_aligned(a->dtype, {a->u, a->delta, a->Bm, a->Cm, a->z, a->out});
-  plan_chunks(a->batch * a->ngroups * lay.dblocks, a->seqlen, a->workspace != nullptr, &p.chunk_len, &p.n_chunks);
+  plan_chunks(a->batch * a->ngroups * lay.dblocks, a->seqlen, a->dstate, a->workspace != nullptr, &p.chunk_len,
+              &p.n_chunks);
+  p.store_states = a->workspace != nullptr;
   if (a->batch * a->ngroups * lay.dblocks * p.n_chunks > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
   if (a->workspace) {
     p.ckpt = reinterpret_cast<float*>(at(a->workspace, lay.off_ckpt));
@@ -237,10 +241,8 @@ size_t ss2d_workspace_bytes(int64_t batch, int64_t dim, int64_t height, int64_t 
 
 // Stages of the SS2D forward (all on one workspace).
 static int ss2d_transpose_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, hipStream_t stream) {
-  ScanOutputs o{};
-  o.out[1] = at(a->workspace, lay.off_xT);
-  o.batch_stride = a->dim * a->height * a->width;
-  return status_from(launch_route_scatter(a->x, o, a->batch, a->dim, a->height, a->width, esize(a->dtype), stream));
+  return status_from(launch_transpose(a->x, at(a->workspace, lay.off_xT), a->batch, a->dim, a->height, a->width,
+                                      esize(a->dtype), stream));
 }
 
 // The four route scans with fp32 outputs (route order) into the ys region; when keep_states,
@@ -274,6 +276,7 @@ static int ss2d_scan_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, bool k
   if (a->batch * 4 * lay.scan.dblocks * p.n_chunks > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
   p.chunk_sum = reinterpret_cast<float*>(at(a->workspace, lay.off_scan + lay.scan.off_sum));
   if (p.n_chunks > 1 || keep_states) p.ckpt = reinterpret_cast<float*>(at(a->workspace, lay.off_scan + lay.scan.off_ckpt));
+  p.store_states = keep_states;
   hipError_t err = hipSuccess;
   if (p.n_chunks > 1) {
     p.pass = 1;
@@ -357,6 +360,7 @@ int ss2d_fwd_stage(const ss2d_fwd_args* a, int stage, hipStream_t stream) {
 static hipError_t scan_states_only(ScanFwdParams p, hipStream_t stream) {
   p.out = nullptr;
   p.last_state = nullptr;
+  p.store_states = 1;
   hipError_t e = hipSuccess;
   if (p.n_chunks > 1) {
     p.pass = 1;
