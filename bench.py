@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--bwd", action="store_true", help="time forward + backward per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time for the sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the timed region, copy 1 GiB device-to-device 3 times (a plain copy of known size "
+                         "that calibrates the HBM byte counters of a profiler run)")
     return ap.parse_args()
 
 
@@ -60,7 +63,7 @@ def algorithmic_bytes(cfg, bwd=False):
 
 def scan_kernel_source_hash():
     h = hashlib.sha256()
-    for name in ("scan_fwd_kernel.h", "device_common.h"):
+    for name in ("scan_fwd_kernel.h", "scan_common.h", "device_common.h"):
         with open(os.path.join(ROOT, "selective_scan_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -69,7 +72,7 @@ def scan_kernel_source_hash():
 def load_traffic(workload_name):
     """HBM traffic of the scan kernel from the committed rocprofv3 counter summary, or None
     when that summary was taken on a different version of the kernel source."""
-    path = os.path.join(ROOT, "profiles", "scan_fwd_traffic.json")
+    path = os.path.join(ROOT, "profiles", "scan_fwd_traffic.txt")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -159,6 +162,13 @@ def main():
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
     scan_ms = float(np.mean([a.elapsed_time(b) for a, b in scan_ev]))
+
+    if args.copy_probe:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
     elements = cfg.elements
     step_bytes = algorithmic_bytes(cfg, args.bwd)

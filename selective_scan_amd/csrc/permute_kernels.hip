@@ -173,7 +173,8 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(GateBwdArgs a, int tiles_
 
 constexpr int kPlaneThreads = 256;
 
-// xT[b, c, w*H + h] = x[b, c, h*W + w]  (the column-major route order, not reversed)
+// xT[b, c, w*H + h] = x[b, c, h*W + w]  (the column-major route order, not reversed).
+// Four consecutive linear indices per thread (L % 4 == 0); rows may wrap inside a group of four.
 template <typename W>
 __global__ __launch_bounds__(kPlaneThreads) void transpose_plane_kernel(const W* __restrict__ x, W* __restrict__ xT,
                                                                          int H, int Wd) {
@@ -183,9 +184,8 @@ __global__ __launch_bounds__(kPlaneThreads) void transpose_plane_kernel(const W*
   const W* xp = x + int64_t(blockIdx.x) * L;
   W* op = xT + int64_t(blockIdx.x) * L;
   const int ld = Wd + 1;
-  // read the plane in grid order: 4 consecutive pixels per thread (Wd % 4 == 0)
+  // read the plane in grid order: 4 consecutive pixels per thread
   for (int64_t q = 4 * int64_t(threadIdx.x); q < L; q += 4 * kPlaneThreads) {
-    const int h = int(q / Wd), w = int(q % Wd);
     W v[4];
     if (sizeof(W) == 2) {
       const uint2 raw = *reinterpret_cast<const uint2*>(xp + q);
@@ -195,15 +195,20 @@ __global__ __launch_bounds__(kPlaneThreads) void transpose_plane_kernel(const W*
       v[0] = W(raw.x); v[1] = W(raw.y); v[2] = W(raw.z); v[3] = W(raw.w);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tile[h * ld + w + j] = v[j];
+    for (int j = 0; j < 4; ++j) {
+      const int h = int((q + j) / Wd), w = int((q + j) % Wd);
+      tile[h * ld + w] = v[j];
+    }
   }
   __syncthreads();
   // write in column-major order: t = w*H + h, 4 consecutive t per thread (H % 4 == 0)
   for (int64_t t = 4 * int64_t(threadIdx.x); t < L; t += 4 * kPlaneThreads) {
-    const int w = int(t / H), h = int(t % H);
     W v[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = tile[(h + j) * ld + w];
+    for (int j = 0; j < 4; ++j) {
+      const int w = int((t + j) / H), h = int((t + j) % H);
+      v[j] = tile[h * ld + w];
+    }
     if (sizeof(W) == 2) {
       uint2 raw;
       raw.x = uint32_t(v[0]) | (uint32_t(v[1]) << 16);
@@ -252,7 +257,6 @@ __global__ __launch_bounds__(kPlaneThreads) void merge_plane_kernel(MergeArgs a)
   T* yg = a.y ? static_cast<T*>(a.y) + plane * L : nullptr;
   float* mg = a.merged_f32 ? a.merged_f32 + plane * L : nullptr;
   for (int64_t p = 4 * int64_t(threadIdx.x); p < L; p += 4 * kPlaneThreads) {
-    const int h = int(p / Wd), w = int(p % Wd);  // Wd % 4 == 0: the 4 pixels share row h
     const float4 v0 = *reinterpret_cast<const float4*>(r0 + p);
     const float4 v2 = *reinterpret_cast<const float4*>(r2 + (L - 4 - p));
     const float a0[4] = {v0.x, v0.y, v0.z, v0.w};
@@ -260,9 +264,10 @@ __global__ __launch_bounds__(kPlaneThreads) void merge_plane_kernel(MergeArgs a)
     float v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float s = a0[j] + t1[(w + j) * ld + h];
+      const int h = int((p + j) / Wd), w = int((p + j) % Wd);
+      float s = a0[j] + t1[w * ld + h];
       s = s + a2[j];
-      v[j] = s + t3[(w + j) * ld + h];
+      v[j] = s + t3[w * ld + h];
     }
     if (a.Dskip && a.x) {
       const float4 xv = Elem<T>::load4(xg, p);
@@ -312,7 +317,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   const int64_t L = a.H * a.W;
   const size_t plane_lds = size_t(2) * size_t(a.W) * size_t(a.H + 1) * 4;
-  if (a.routes_f32 && a.W % 4 == 0 && a.H % 4 == 0 && plane_lds <= 64 * 1024 && a.batch * a.C > 0 &&
+  if (a.routes_f32 && plane_lds <= 64 * 1024 && a.batch * a.C > 0 &&
       aligned16(a.routes) && (!a.merged_f32 || aligned16(a.merged_f32)) &&
       (a.dtype == 0 ? (aligned16(a.y) && aligned16(a.x) && aligned16(a.z))
                     : ((reinterpret_cast<uintptr_t>(a.y) | reinterpret_cast<uintptr_t>(a.x) |
@@ -345,7 +350,7 @@ hipError_t launch_transpose(const void* x, void* xT, int64_t batch, int64_t C, i
   if (planes == 0 || H * W == 0) return hipSuccess;
   const size_t lds = size_t(H) * size_t(W + 1) * size_t(elem_bytes);
   const uintptr_t al = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(xT);
-  if (W % 4 == 0 && H % 4 == 0 && lds <= 64 * 1024 && (al % (4 * elem_bytes)) == 0) {
+  if ((H * W) % 4 == 0 && lds <= 64 * 1024 && (al % (4 * elem_bytes)) == 0) {
     if (elem_bytes == 2)
       transpose_plane_kernel<uint16_t><<<dim3(uint32_t(planes)), dim3(kPlaneThreads), lds, s>>>(
           static_cast<const uint16_t*>(x), static_cast<uint16_t*>(xT), int(H), int(W));
