@@ -10,7 +10,8 @@
 //   dD      += dy_t u_t,                      dz_t  = dout_t (y_t + D u_t) silu'(z_t)
 // (dB, dC summed over the channels of a group; dA, dD, ddelta_bias over batch and time).
 //
-// Mapping: as in the forward, one wavefront = 64 channels of one (batch, group); lane = row.
+// Mapping: as in the forward, one wavefront = channels of one (batch, group): one lane per channel
+// for N <= 8, two adjacent lanes per channel (half of the states each) from N = 16 up.
 // A row is walked backwards in 32-step tiles; a tile is cut into sub-intervals of kSub steps
 // whose start states were checkpointed by the forward.  For each sub-interval the states are
 // recomputed forwards into registers (kSub x NS floats), then the adjoint recurrence runs
@@ -29,15 +30,16 @@ namespace ss2d {
 namespace bwd_detail {
 using namespace scan_detail;
 
-// Sum V values per lane over the 64 lanes of the wavefront.  On return lane l holds, in
-// v[0 .. V/64), the totals of original indices l*(V/64) + r (V >= 64); for V = 32 every lane
-// holds the total of index l >> 1 in v[0].
-template <int V>
+// Sum V values per lane over the lanes that differ in the bits of the masks 32, 16, ..., kMinMask
+// (kMinMask = 1: all 64 lanes; kMinMask = 2: the 32 lanes of the same parity).  Halving exchanges
+// from the highest mask down while more than one value is left (lane bit m set: keep the upper
+// half), then plain butterflies.  On return v[0 .. V >> H) of lane l holds the totals of the
+// original indices reduce_index<V, kMinMask>(l, r).
+template <int V, int kMinMask>
 __device__ __forceinline__ void lane_transpose_reduce(float* v, int lane) {
-  static_assert(V == 32 || V == 128 || V == 64, "unsupported reduce width");
   int cnt = V;
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
+  for (int m = 32; m >= kMinMask; m >>= 1) {
     if (cnt > 1) {
       const bool upper = (lane & m) != 0;
       const int half = cnt / 2;
@@ -57,17 +59,58 @@ __device__ __forceinline__ void lane_transpose_reduce(float* v, int lane) {
   }
 }
 
-template <typename T, int NS, bool kSS2D, bool kVec, int kPass>
+// values left per lane after lane_transpose_reduce, and the original index of v[r]
+template <int V, int kMinMask>
+constexpr int reduce_left() {
+  int cnt = V;
+  for (int m = 32; m >= kMinMask; m >>= 1)
+    if (cnt > 1) cnt /= 2;
+  return cnt;
+}
+template <int V, int kMinMask>
+__device__ __forceinline__ int reduce_index(int lane, int r) {
+  int cnt = V, idx = 0;
+#pragma unroll
+  for (int m = 32; m >= kMinMask; m >>= 1) {
+    if (cnt > 1) {
+      cnt /= 2;
+      if (lane & m) idx += cnt;
+    }
+  }
+  return idx + r;
+}
+// true for the one lane (per index and parity) that writes a total: no butterfly-mask bit set
+template <int V, int kMinMask>
+__device__ __forceinline__ bool reduce_writer(int lane) {
+  int cnt = V, bits = 0;
+#pragma unroll
+  for (int m = 32; m >= kMinMask; m >>= 1) {
+    if (cnt > 1)
+      cnt /= 2;
+    else
+      bits |= m;
+  }
+  return (lane & bits) == 0;
+}
+
+// kSplit: lanes per channel (1 or 2); NSL = NS / kSplit states per lane.
+template <typename T, int NS, int kSplit, bool kSS2D, bool kVec, int kPass>
 __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) {
   using DT = typename std::conditional<kSS2D, float, T>::type;  // type of dout rows
+  constexpr int NSL = NS / kSplit;
+  constexpr int kRows = kWave / kSplit;
   constexpr int S = (NS < 4) ? 4 : NS + 4;
   constexpr int kSub = ckpt_steps(NS);
-  constexpr int kRW = (2 * NS < 32) ? 32 : 2 * NS;  // width of the per-step dB/dC lane reduction
-  constexpr int kInner = (64 / NS < kSub) ? 64 / NS : kSub;  // steps whose states are held at once
+  constexpr int kMinMask = kSplit;                                  // lanes of a channel differ in bit 0
+  constexpr int kRW = (2 * NSL < 32 / kSplit) ? 32 / kSplit : 2 * NSL;  // per-step dB/dC reduce width
+  constexpr int kLeft = reduce_left<kRW, kMinMask>();
+  constexpr int kInner = (64 / NSL < kSub) ? 64 / NSL : kSub;       // steps whose states are held at once
   __shared__ __align__(16) float sB[kTile * S];
   __shared__ __align__(16) float sC[kTile * S];
 
   const int lane = threadIdx.x;
+  const int part = lane % kSplit;
+  const int n0 = part * NSL;
   int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t dblk = bid % p.dblocks;
   bid /= p.dblocks;
@@ -75,13 +118,14 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
   bid /= p.n_chunks;
   const int64_t g = bid % p.G;
   const int64_t b = bid / p.G;
-  const int64_t dg = dblk * kWave + lane;
+  const int64_t dg = dblk * kRows + lane / kSplit;
   const bool active = dg < p.per_group;
   const int64_t dl = active ? dg : 0;
   const int64_t d = g * p.per_group + dl;
   const int64_t row = b * p.dim + d;
   const int64_t L = p.L;
   const int N = p.N;
+  const int nvalid = (N - n0 < 0) ? 0 : ((N - n0 > NSL) ? NSL : N - n0);
 
   const T* delta_row = static_cast<const T*>(p.delta) + row * L;
   const T* u_row;
@@ -101,9 +145,9 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
   const T* Bg = static_cast<const T*>(p.Bm) + (b * p.G + g) * N * L;
   const T* Cg = static_cast<const T*>(p.Cm) + (b * p.G + g) * N * L;
 
-  float Acoef[NS];
+  float Acoef[NSL];
 #pragma unroll
-  for (int n = 0; n < NS; ++n) Acoef[n] = (n < N) ? p.A[d * N + n] : 0.0f;
+  for (int n = 0; n < NSL; ++n) Acoef[n] = (n < nvalid) ? p.A[d * N + n0 + n] : 0.0f;
   const float bias = p.delta_bias ? p.delta_bias[d] : 0.0f;
   const float Dd = p.Dskip ? p.Dskip[d] : 0.0f;
 
@@ -112,19 +156,25 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
   const int64_t n_tiles = (t_end - t_begin + kTile - 1) / kTile;
 
   // mu = a_{t+1} lambda_{t+1}: the adjoint flowing into step t from later steps
-  float mu[NS];
+  float mu[NSL];
 #pragma unroll
-  for (int n = 0; n < NS; ++n) mu[n] = 0.0f;
+  for (int n = 0; n < NSL; ++n) mu[n] = 0.0f;
   if (kPass == 0 && p.n_chunks > 1) {
-    const float* src = p.lam_carry + (row * p.n_chunks + c) * N;
+    const float* src = p.lam_carry + (row * p.n_chunks + c) * N + n0;
 #pragma unroll
-    for (int n = 0; n < NS; ++n)
-      if (n < N) mu[n] = src[n];
+    for (int n = 0; n < NSL; ++n)
+      if (n < nvalid) mu[n] = src[n];
   }
-  float dA_acc[NS];
+  float dA_acc[NSL];
 #pragma unroll
-  for (int n = 0; n < NS; ++n) dA_acc[n] = 0.0f;
+  for (int n = 0; n < NSL; ++n) dA_acc[n] = 0.0f;
   float dD_acc = 0.0f, dbias_acc = 0.0f, lam_sum = 0.0f;
+
+  auto pair_sum = [&](float x) {
+    if (kSplit == 2)
+      x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+    return x;
+  };
 
   for (int64_t jt = n_tiles - 1; jt >= 0; --jt) {
     const int64_t t0 = t_begin + jt * kTile;
@@ -161,29 +211,29 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
       if (kPass == 0) {
         // Start state of this sub-interval (its checkpoint).  The sub-interval is handled in
         // pieces of kInner steps, last piece first; for each piece the states are recomputed
-        // forwards from the checkpoint and only the piece's own kInner x NS states are kept.
-        float h0[NS];
-        const float* ck = p.ckpt + (row * p.n_ckpt + s0 / kSub) * N;
+        // forwards from the checkpoint and only the piece's own kInner x NSL states are kept.
+        float h0[NSL];
+        const float* ck = p.ckpt + (row * p.n_ckpt + s0 / kSub) * N + n0;
 #pragma unroll
-        for (int n = 0; n < NS; ++n) h0[n] = (n < N) ? ck[n] : 0.0f;
+        for (int n = 0; n < NSL; ++n) h0[n] = (n < nvalid) ? ck[n] : 0.0f;
 #pragma unroll
         for (int pc = kSub / kInner - 1; pc >= 0; --pc) {
-          float hstart[NS];
+          float hstart[NSL];
 #pragma unroll
-          for (int n = 0; n < NS; ++n) hstart[n] = h0[n];
+          for (int n = 0; n < NSL; ++n) hstart[n] = h0[n];
 #pragma unroll
           for (int i = 0; i < pc * kInner; ++i) {
-            const float* bt = sB + (q * kSub + i) * S;
+            const float* bt = sB + (q * kSub + i) * S + n0;
 #pragma unroll
-            for (int n = 0; n < NS; ++n) hstart[n] = fmaf(fast_exp2(lam[i] * Acoef[n]), hstart[n], dup[i] * bt[n]);
+            for (int n = 0; n < NSL; ++n) hstart[n] = fmaf(fast_exp2(lam[i] * Acoef[n]), hstart[n], dup[i] * bt[n]);
           }
-          float hs[kInner][NS];
+          float hs[kInner][NSL];
 #pragma unroll
           for (int j = 0; j < kInner; ++j) {
             const int i = pc * kInner + j;
-            const float* bt = sB + (q * kSub + i) * S;
+            const float* bt = sB + (q * kSub + i) * S + n0;
 #pragma unroll
-            for (int n = 0; n < NS; ++n) {
+            for (int n = 0; n < NSL; ++n) {
               const float hp = (j == 0) ? hstart[n] : hs[j - 1][n];
               hs[j][n] = fmaf(fast_exp2(lam[i] * Acoef[n]), hp, dup[i] * bt[n]);
             }
@@ -194,17 +244,17 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
           for (int j = kInner - 1; j >= 0; --j) {
             const int i = pc * kInner + j;
             const int idx = q * kSub + i;
-            const float* bt = sB + idx * S;
-            const float* ct = sC + idx * S;
+            const float* bt = sB + idx * S + n0;
+            const float* ct = sC + idx * S + n0;
             // recompute the decays here instead of keeping the forward's values alive
             float lr = lam[i];
             asm volatile("" : "+v"(lr));
             float sbl = 0.0f, ddt = 0.0f, yv = 0.0f;
             float red[kRW];
 #pragma unroll
-            for (int e = 2 * NS; e < kRW; ++e) red[e] = 0.0f;
+            for (int e = 2 * NSL; e < kRW; ++e) red[e] = 0.0f;
 #pragma unroll
-            for (int n = 0; n < NS; ++n) {
+            for (int n = 0; n < NSL; ++n) {
               const float a = fast_exp2(lr * Acoef[n]);
               const float l = fmaf(ct[n], dy[i], mu[n]);
               const float hp = (j == 0) ? hstart[n] : hs[j - 1][n];
@@ -212,11 +262,15 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
               dA_acc[n] = fmaf(gg, lam[i], dA_acc[n]);
               ddt = fmaf(gg, Acoef[n], ddt);
               sbl = fmaf(l, bt[n], sbl);
-              red[n] = l * dup[i];             // dB term (times ln 2, applied when the blocks are summed)
-              red[NS + n] = dy[i] * hs[j][n];  // dC term
+              red[n] = l * dup[i];              // dB term (times ln 2, applied when the blocks are summed)
+              red[NSL + n] = dy[i] * hs[j][n];  // dC term
               if (has_z) yv = fmaf(ct[n], hs[j][n], yv);
               mu[n] = a * l;
             }
+            // the two lanes of a channel hold complementary halves of the state sums
+            sbl = pair_sum(sbl);
+            ddt = pair_sum(ddt);
+            if (has_z) yv = pair_sum(yv);
             o_du[j] = fmaf(lam[i], sbl, Dd * dy[i]);
             float dd = fmaf(uv[i] * kLog2e, sbl, ddt);  // ddelta (B was staged times ln 2)
             if (p.softplus) dd *= sigmoid(dv[i] + bias);
@@ -228,34 +282,22 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
               const float sz = sigmoid(zv[i]);
               o_dz[j] = gv[i] * fmaf(Dd, uv[i], yv) * sz * (1.0f + zv[i] * (1.0f - sz));
             }
-            // dB / dC for (this step, all states): sum over the 64 channels of the block
-            lane_transpose_reduce<kRW>(red, lane);
-            if (i < ns) {
+            // dB / dC for (this step, this lane's states): sum over the channels of the block
+            lane_transpose_reduce<kRW, kMinMask>(red, lane);
+            if (i < ns && reduce_writer<kRW, kMinMask>(lane)) {
               const int64_t t = s0 + i;
-              if (kRW >= 64) {
 #pragma unroll
-                for (int r = 0; r < kRW / 64; ++r) {
-                  const int e = lane * (kRW / 64) + r;  // e < NS: dB state e, else dC state e - NS
-                  const int n = e < NS ? e : e - NS;
-                  if (n < N) {
-                    float* dst = (e < NS) ? p.dB_part : p.dC_part;
-                    dst[(((dblk * p.batch + b) * p.G + g) * N + n) * L + t] = red[r];
-                  }
-                }
-              } else {
-                // 32-wide reduction: the total of value e lives in lanes 2e and 2e + 1
-                const int e = lane >> 1;
-                if ((lane & 1) == 0 && e < 2 * NS) {
-                  const int n = e < NS ? e : e - NS;
-                  if (n < N) {
-                    float* dst = (e < NS) ? p.dB_part : p.dC_part;
-                    dst[(((dblk * p.batch + b) * p.G + g) * N + n) * L + t] = red[0];
-                  }
+              for (int r = 0; r < kLeft; ++r) {
+                const int e = reduce_index<kRW, kMinMask>(lane, r);  // e < NSL: dB, else dC (state n0 + e % NSL)
+                const int n = e < NSL ? e : e - NSL;
+                if (e < 2 * NSL && n < nvalid) {
+                  float* dst = (e < NSL) ? p.dB_part : p.dC_part;
+                  dst[(((dblk * p.batch + b) * p.G + g) * N + n0 + n) * L + t] = red[r];
                 }
               }
             }
           }
-          if (active) {
+          if (active && part == 0) {
             const int64_t sp = s0 + pc * kInner;
             store_seg<T, kVec, kInner>(static_cast<T*>(p.ddelta) + row * L, o_dd, sp, t_end);
             if (kSS2D)
@@ -269,9 +311,9 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
         // pass 1: adjoint recurrence of the chunk from zero (no states needed)
 #pragma unroll
         for (int i = kSub - 1; i >= 0; --i) {
-          const float* ct = sC + (q * kSub + i) * S;
+          const float* ct = sC + (q * kSub + i) * S + n0;
 #pragma unroll
-          for (int n = 0; n < NS; ++n) {
+          for (int n = 0; n < NSL; ++n) {
             const float a = fast_exp2(lam[i] * Acoef[n]);
             mu[n] = a * fmaf(ct[n], dy[i], mu[n]);
           }
@@ -283,39 +325,45 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
 
   if (!active) return;
   if (kPass == 1) {
-    float* dst = p.lam_carry + (row * p.n_chunks + c) * N;  // local adjoint at the chunk start
+    float* dst = p.lam_carry + (row * p.n_chunks + c) * N + n0;  // local adjoint at the chunk start
 #pragma unroll
-    for (int n = 0; n < NS; ++n)
-      if (n < N) dst[n] = mu[n];
-    p.chunk_sum[row * p.n_chunks + c] = lam_sum;
+    for (int n = 0; n < NSL; ++n)
+      if (n < nvalid) dst[n] = mu[n];
+    if (part == 0) p.chunk_sum[row * p.n_chunks + c] = lam_sum;
   } else {
-    float* dA = p.dA_part + (int64_t(c) * p.batch * p.dim + row) * N;
+    float* dA = p.dA_part + (int64_t(c) * p.batch * p.dim + row) * N + n0;
 #pragma unroll
-    for (int n = 0; n < NS; ++n)
-      if (n < N) dA[n] = dA_acc[n];
-    p.dD_part[int64_t(c) * p.batch * p.dim + row] = dD_acc;
-    p.dbias_part[int64_t(c) * p.batch * p.dim + row] = dbias_acc;
+    for (int n = 0; n < NSL; ++n)
+      if (n < nvalid) dA[n] = dA_acc[n];
+    if (part == 0) {
+      p.dD_part[int64_t(c) * p.batch * p.dim + row] = dD_acc;
+      p.dbias_part[int64_t(c) * p.batch * p.dim + row] = dbias_acc;
+    }
   }
 }
 
-template <typename T, int NS, bool kSS2D, bool kVec>
-hipError_t launch_t(const ScanBwdParams& p, hipStream_t s) {
+template <typename T, int NS, int kSplit, bool kSS2D, bool kVec>
+hipError_t launch_t(ScanBwdParams p, hipStream_t s) {
+  p.dblocks = (p.per_group + kWave / kSplit - 1) / (kWave / kSplit);
   const int64_t blocks = p.batch * p.G * p.dblocks * p.n_chunks;
   if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (p.pass == 1)
-    scan_bwd_kernel<T, NS, kSS2D, kVec, 1><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
+    scan_bwd_kernel<T, NS, kSplit, kSS2D, kVec, 1><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
   else
-    scan_bwd_kernel<T, NS, kSS2D, kVec, 0><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
+    scan_bwd_kernel<T, NS, kSplit, kSS2D, kVec, 0><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace bwd_detail
 
+// Two lanes per channel from 16 states up (as in the forward).
 template <typename T, int NS>
 hipError_t scan_bwd_launch(const ScanBwdParams& p, hipStream_t s) {
   using namespace bwd_detail;
-  if (p.ss2d) return p.vec ? launch_t<T, NS, true, true>(p, s) : launch_t<T, NS, true, false>(p, s);
-  return p.vec ? launch_t<T, NS, false, true>(p, s) : launch_t<T, NS, false, false>(p, s);
+  constexpr int kSplit = NS >= 16 ? 2 : 1;
+  if (p.ss2d) return p.vec ? launch_t<T, NS, kSplit, true, true>(p, s) : launch_t<T, NS, kSplit, true, false>(p, s);
+  return p.vec ? launch_t<T, NS, kSplit, false, true>(p, s) : launch_t<T, NS, kSplit, false, false>(p, s);
 }
 
 }  // namespace ss2d

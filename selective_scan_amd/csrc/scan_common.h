@@ -79,6 +79,14 @@ __device__ __forceinline__ void set_elem<bf16>(RowTile<bf16>& t, int i, const bf
 template <typename T, bool kVec>
 __device__ __forceinline__ void load_row(RowTile<T>& tile, const T* row, int64_t t0, int64_t t_end, int64_t L,
                                          bool rev) {
+  if (kVec && t0 + kTile <= t_end) {
+    // whole tile in range: unconditional vector loads, nothing to zero
+    const int64_t base = rev ? (L - t0 - kTile) : t0;
+#pragma unroll
+    for (int j = 0; j < kTile / 4; ++j) tile.load_vec(row + base + 4 * j, j);
+    if (rev) tile.reverse();
+    return;
+  }
   tile.zero();
   if (kVec) {
     if (!rev) {
@@ -111,6 +119,22 @@ struct BCStage {
 
   __device__ __forceinline__ void load(const T* Bg, const T* Cg, int N, int64_t L, int64_t t0, int64_t t_end,
                                        int lane) {
+    if (kVec && t0 + kTile <= t_end && NS * kTile / 4 >= kWave * kVecs) {
+      // whole tile in range and every lane has whole vectors: states past N read as zero
+#pragma unroll
+      for (int k = 0; k < kVecs; ++k) {
+        const int j = lane + k * kWave;
+        const int n = j / (kTile / 4), q = j % (kTile / 4);
+        float4 vb = make_float4(0.f, 0.f, 0.f, 0.f), vc = vb;
+        if (n < N) {
+          vb = Elem<T>::load4(Bg, int64_t(n) * L + t0 + 4 * q);
+          vc = Elem<T>::load4(Cg, int64_t(n) * L + t0 + 4 * q);
+        }
+        b[4 * k + 0] = vb.x; b[4 * k + 1] = vb.y; b[4 * k + 2] = vb.z; b[4 * k + 3] = vb.w;
+        c[4 * k + 0] = vc.x; c[4 * k + 1] = vc.y; c[4 * k + 2] = vc.z; c[4 * k + 3] = vc.w;
+      }
+      return;
+    }
     if (kVec) {
 #pragma unroll
       for (int k = 0; k < kVecs; ++k) {

@@ -79,6 +79,7 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(const ScanFwdParams p) 
   for (int n = 0; n < NSL; ++n) Acoef[n] = (n0 + n < N) ? p.A[d * N + n0 + n] : 0.0f;
   const int nvalid = (N - n0 < 0) ? 0 : ((N - n0 > NSL) ? NSL : N - n0);  // real states of this lane
   const float bias = p.delta_bias ? p.delta_bias[d] : 0.0f;
+  const float bias_l2 = bias * kLog2e;
   const float Dd = (!kSS2D && p.Dskip) ? p.Dskip[d] : 0.0f;
 
   const bool softplus = p.softplus != 0;
@@ -119,10 +120,11 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(const ScanFwdParams p) 
     }
 
     const int nt = int((t_end - t0 < kTile) ? (t_end - t0) : kTile);
-    // One step's B (times ln 2) and C from LDS; the reads for step i+1 are issued while step i
-    // computes (software pipelining of the LDS latency).
-    float nb[NSL], nc[NSL];
-    auto read_bc = [&](int i) {
+    // One step's B (times ln 2) and C from LDS into one of two register buffers: the reads for
+    // step i+1 go to buffer (i+1)&1 while step i computes from buffer i&1 (software pipelining
+    // of the LDS latency; the buffer choice is resolved at compile time in the unrolled loop).
+    float bufb[2][NSL], bufc[2][NSL];
+    auto read_bc = [&](int i, float* nb, float* nc) {
       if (NSL >= 4) {
         const float4* bt = reinterpret_cast<const float4*>(sB + i * S + n0);
         const float4* ct = reinterpret_cast<const float4*>(sC + i * S + n0);
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(const ScanFwdParams p) 
         }
       }
     };
-    read_bc(0);
+    read_bc(0, bufb[0], bufc[0]);
     // The tile is processed in groups of 4 steps: per-step quantities, recurrence, epilogue and
     // a 4-element store per group, so that only a group's worth of temporaries is live.
 #pragma unroll
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(const ScanFwdParams p) 
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int i = 4 * g4 + k;
-        const float w = (cd.get(i) + bias) * kLog2e;
+        const float w = fmaf(cd.get(i), kLog2e, bias_l2);
         float l = softplus_log2(w);
         l = softplus ? l : w;  // branch-free: keeps the steps in one straight-line block
         // Steps past the end of the range get Lam = 0: decay exp2(0) = 1 and zero input (B/C
@@ -170,13 +172,9 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(const ScanFwdParams p) 
         if (kStore && (i % kSub) == 0) {
           if (i < nt && active) store_state<NSL>(p.ckpt + (row * p.n_ckpt + (t0 + i) / kSub) * N + n0, h, nvalid);
         }
-        float cb[NSL], cc[NSL];
-#pragma unroll
-        for (int n = 0; n < NSL; ++n) {
-          cb[n] = nb[n];
-          cc[n] = (kPass == 0) ? nc[n] : 0.0f;
-        }
-        if (i + 1 < kTile) read_bc(i + 1);
+        const float* cb = bufb[i & 1];
+        const float* cc = bufc[i & 1];
+        if (i + 1 < kTile) read_bc(i + 1, bufb[(i + 1) & 1], bufc[(i + 1) & 1]);
         float acc = 0.0f;
 #pragma unroll
         for (int n = 0; n < NSL; ++n) {

@@ -25,18 +25,30 @@ bool dtype_ok(int dtype) { return dtype == SS2D_DTYPE_F32 || dtype == SS2D_DTYPE
 constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
 
 // ---- selective-scan workspace layout -------------------------------------------------
-// Split long sequences across wavefronts only when the rows alone cannot fill the GPU
-// (1024 SIMDs on MI355X; aim for at least two wavefronts per SIMD).  Chunks are whole tiles.
-void plan_chunks(int64_t row_waves, int64_t L, int64_t dstate, bool can_chunk, int64_t* chunk_len, int* n_chunks) {
+// Split long sequences across wavefronts only when the rows alone cannot fill the GPU.  The
+// forward and the backward plan separately: each targets a whole number of "rounds" of its
+// kernel (1024 SIMDs x the wavefronts per SIMD its registers allow), so the last round is not
+// a short tail.  Chunks are whole tiles.
+constexpr int64_t kSimds = 1024;  // 256 CUs x 4 SIMDs on MI355X
+
+// channels per wavefront (two lanes per channel from 16 states up, in both directions) and
+// wavefronts per SIMD the kernels' registers allow, by padded state count
+inline int64_t rows_per_wave(int64_t dstate) { return padded_states(dstate) >= 16 ? kWave / 2 : kWave; }
+inline int64_t fwd_waves_per_simd(int64_t dstate) { return padded_states(dstate) >= 16 ? 3 : 2; }
+inline int64_t bwd_waves_per_simd(int64_t dstate) { return padded_states(dstate) >= 16 ? 2 : 2; }
+
+void plan_chunks(int64_t row_waves, int64_t L, int64_t waves_per_simd, bool can_chunk, int64_t* chunk_len,
+                 int* n_chunks) {
   const int64_t n_tiles = cdiv(L, kTile);
-  (void)dstate;
-  const int64_t target = 2048;
-  if (!can_chunk || row_waves >= target / 2 || n_tiles <= 1) {
+  const int64_t round = kSimds * waves_per_simd;
+  if (!can_chunk || row_waves * 2 >= round || n_tiles <= 1) {
     *chunk_len = (n_tiles > 0 ? n_tiles : 1) * kTile;
     *n_chunks = 1;
     return;
   }
-  int64_t want = cdiv(target, row_waves);
+  // the most chunks that still fit in one round (at least two chunks)
+  int64_t want = round / row_waves;
+  if (want < 2) want = 2;
   if (want > n_tiles) want = n_tiles;
   const int64_t tiles_per_chunk = cdiv(n_tiles, want);
   *chunk_len = tiles_per_chunk * kTile;
@@ -44,8 +56,9 @@ void plan_chunks(int64_t row_waves, int64_t L, int64_t dstate, bool can_chunk, i
 }
 
 struct ScanLayout {
-  int64_t rows, n_ckpt, dblocks, per_group, chunk_len;
-  int n_chunks, ckpt_every;
+  int64_t rows, n_ckpt, dblocks, per_group;
+  int64_t chunk_len, bwd_chunk_len;  // forward / backward chunk plans
+  int n_chunks, bwd_n_chunks, ckpt_every;
   int64_t off_ckpt, off_sum, off_lam, off_dB, off_dC, off_dA, off_dD, off_dbias, total;
 };
 
@@ -55,9 +68,11 @@ ScanLayout scan_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqle
   l.ckpt_every = ckpt_steps(padded_states(dstate));
   l.n_ckpt = cdiv(seqlen, l.ckpt_every);
   l.per_group = ngroups > 0 ? dim / ngroups : 0;
-  l.dblocks = cdiv(l.per_group, kWave);
-  plan_chunks(batch * ngroups * l.dblocks, seqlen, dstate, true, &l.chunk_len, &l.n_chunks);
-  const int64_t nc = l.n_chunks;
+  l.dblocks = cdiv(l.per_group, rows_per_wave(dstate));  // channel blocks of one wavefront (dB/dC partials)
+  const int64_t row_waves = batch * ngroups * l.dblocks;
+  plan_chunks(row_waves, seqlen, fwd_waves_per_simd(dstate), true, &l.chunk_len, &l.n_chunks);
+  plan_chunks(row_waves, seqlen, bwd_waves_per_simd(dstate), true, &l.bwd_chunk_len, &l.bwd_n_chunks);
+  const int64_t nc = l.n_chunks > l.bwd_n_chunks ? l.n_chunks : l.bwd_n_chunks;
   int64_t o = 0;
   l.off_ckpt = o;  o += align_up(l.rows * l.n_ckpt * dstate * 4);
   l.off_sum = o;   o += align_up(l.rows * nc * 4);
@@ -215,10 +230,14 @@ int selective_scan_fwd(const ss_fwd_args* a, hipStream_t stream) {
   p.ss2d = 0;
   p.dtype = a->dtype;
   p.vec = (a->seqlen % 4 == 0) && vec_aligned(a->dtype, {a->u, a->delta, a->Bm, a->Cm, a->z, a->out});
-  plan_chunks(a->batch * a->ngroups * lay.dblocks, a->seqlen, a->dstate, a->workspace != nullptr, &p.chunk_len,
-              &p.n_chunks);
+  p.chunk_len = lay.chunk_len;
+  p.n_chunks = lay.n_chunks;
+  if (!a->workspace) {  // no scratch for the chunk states: one chunk per row
+    p.chunk_len = cdiv(a->seqlen, kTile) * kTile;
+    p.n_chunks = 1;
+  }
   p.store_states = a->workspace != nullptr;
-  if (a->batch * a->ngroups * lay.dblocks * p.n_chunks > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
+  if (a->batch * a->ngroups * lay.dblocks * 2 * p.n_chunks > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
   if (a->workspace) {
     p.ckpt = reinterpret_cast<float*>(at(a->workspace, lay.off_ckpt));
     p.chunk_sum = reinterpret_cast<float*>(at(a->workspace, lay.off_sum));
@@ -273,7 +292,7 @@ static int ss2d_scan_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, bool k
   p.vec = (L % 4 == 0) && vec_aligned(a->dtype, {a->x, a->delta, a->Bm, a->Cm});
   p.chunk_len = lay.scan.chunk_len;
   p.n_chunks = lay.scan.n_chunks;
-  if (a->batch * 4 * lay.scan.dblocks * p.n_chunks > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
+  if (a->batch * 4 * lay.scan.dblocks * 2 * p.n_chunks > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
   p.chunk_sum = reinterpret_cast<float*>(at(a->workspace, lay.off_scan + lay.scan.off_sum));
   if (p.n_chunks > 1 || keep_states) p.ckpt = reinterpret_cast<float*>(at(a->workspace, lay.off_scan + lay.scan.off_ckpt));
   p.store_states = keep_states;
@@ -391,8 +410,8 @@ static int run_scan_bwd(ScanBwdParams bp, const ScanLayout& lay, void* ws, void*
   bp.dA_part = reinterpret_cast<float*>(at(ws, lay.off_dA));
   bp.dD_part = reinterpret_cast<float*>(at(ws, lay.off_dD));
   bp.dbias_part = reinterpret_cast<float*>(at(ws, lay.off_dbias));
-  bp.chunk_len = lay.chunk_len;
-  bp.n_chunks = lay.n_chunks;
+  bp.chunk_len = lay.bwd_chunk_len;
+  bp.n_chunks = lay.bwd_n_chunks;
   bp.n_ckpt = int(lay.n_ckpt);
   hipError_t e = hipSuccess;
   if (bp.n_chunks > 1) {
@@ -448,7 +467,9 @@ int selective_scan_bwd(const ss_bwd_args* a, hipStream_t stream) {
     return SS2D_ERR_INVALID_ARGUMENT;
   const ScanLayout lay = scan_layout(a->batch, a->dim, a->dstate, a->seqlen, a->ngroups);
   if (a->workspace_bytes < size_t(lay.total) || !aligned(a->workspace, kAlign)) return SS2D_ERR_INVALID_ARGUMENT;
-  if (a->batch * a->ngroups * lay.dblocks * lay.n_chunks > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
+  if (a->batch * a->ngroups * lay.dblocks * lay.bwd_n_chunks > kMaxBlocks ||
+      a->batch * a->ngroups * lay.dblocks * 2 * lay.n_chunks > kMaxBlocks)
+    return SS2D_ERR_INVALID_ARGUMENT;
   const bool vec = (a->seqlen % 4 == 0) &&
                    vec_aligned(a->dtype, {a->u, a->delta, a->Bm, a->Cm, a->z, a->dout, a->du, a->ddelta});
 
@@ -529,7 +550,8 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
   const SS2DLayout lay = ss2d_layout(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype);
   if (a->workspace_bytes < size_t(lay.total) || !aligned(a->workspace, kAlign)) return SS2D_ERR_INVALID_ARGUMENT;
   if (a->batch * a->dim * cdiv(a->height, 32) * cdiv(a->width, 32) > kMaxBlocks ||
-      a->batch * 4 * lay.scan.dblocks * lay.scan.n_chunks > kMaxBlocks)
+      a->batch * 4 * lay.scan.dblocks * 2 * lay.scan.n_chunks > kMaxBlocks ||
+      a->batch * 4 * lay.scan.dblocks * lay.scan.bwd_n_chunks > kMaxBlocks)
     return SS2D_ERR_INVALID_ARGUMENT;
   const int64_t L = a->height * a->width;
 
