@@ -14,6 +14,12 @@ inline int padded_states(int64_t n) { return n <= 1 ? 1 : n <= 4 ? 4 : n <= 8 ? 
 // per lane (32 for NS = 1), the states the backward recomputes and holds in registers at a time.
 // Always a divisor of kTile.
 constexpr int ckpt_steps(int ns) { return ns >= 64 ? 2 : ns >= 32 ? 4 : ns >= 16 ? 8 : ns >= 8 ? 16 : 32; }
+// Resident wavefronts per SIMD of the SS2D scan kernels (512 VGPRs per lane shared by the
+// resident wavefronts), by padded state count; the bf16 forward kernel is compiled to reach it.
+constexpr int fwd_waves_per_simd(int ns, bool bf16) {
+  return bf16 ? (ns <= 4 ? 4 : ns <= 16 ? 3 : ns == 32 ? 2 : 1) : (ns == 1 ? 3 : ns <= 16 ? 2 : 1);
+}
+constexpr int bwd_waves_per_simd(int ns) { return ns == 1 ? 2 : ns <= 8 ? 1 : ns <= 32 ? 2 : 1; }
 
 // ---- permutations (permute_kernels.hip) ----------------------------------------------
 // Scatter one map (batch, C, H, W) into up to four route-ordered outputs.

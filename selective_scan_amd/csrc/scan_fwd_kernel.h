@@ -31,7 +31,8 @@ using namespace scan_detail;
 //        2 = as 0 and also the state before every kSub-th step (checkpoints for the backward).
 // kSplit: lanes per channel (1 or 2); NSL = NS / kSplit states per lane.
 template <typename T, int NS, int kSplit, bool kSS2D, bool kVec, int kPassArg>
-__global__ __launch_bounds__(kWave) void scan_fwd_kernel(const ScanFwdParams p) {
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu((kSS2D && kVec && sizeof(T) == 2) ? fwd_waves_per_simd(NS, true) : 1)))
+void scan_fwd_kernel(const ScanFwdParams p) {
   constexpr int kPass = kPassArg == 2 ? 0 : kPassArg;
   constexpr bool kStore = kPassArg == 2;
   constexpr int NSL = NS / kSplit;

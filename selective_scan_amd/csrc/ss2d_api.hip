@@ -34,8 +34,6 @@ constexpr int64_t kSimds = 1024;  // 256 CUs x 4 SIMDs on MI355X
 // channels per wavefront (two lanes per channel from 16 states up, in both directions) and
 // wavefronts per SIMD the kernels' registers allow, by padded state count
 inline int64_t rows_per_wave(int64_t dstate) { return padded_states(dstate) >= 16 ? kWave / 2 : kWave; }
-inline int64_t fwd_waves_per_simd(int64_t dstate) { return padded_states(dstate) >= 16 ? 3 : 2; }
-inline int64_t bwd_waves_per_simd(int64_t dstate) { return padded_states(dstate) >= 16 ? 2 : 2; }
 
 void plan_chunks(int64_t row_waves, int64_t L, int64_t waves_per_simd, bool can_chunk, int64_t* chunk_len,
                  int* n_chunks) {
@@ -62,7 +60,13 @@ struct ScanLayout {
   int64_t off_ckpt, off_sum, off_lam, off_dB, off_dC, off_dA, off_dD, off_dbias, total;
 };
 
-ScanLayout scan_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int64_t ngroups) {
+// Wavefronts per SIMD whose whole rounds the forward chunk plan fills.  Below 16 states a
+// chunk's first pass costs nearly as much as its output pass, so the plan stops at two.
+inline int64_t fwd_plan_waves(int ns, bool bf16) { return ns >= 16 ? fwd_waves_per_simd(ns, bf16) : 2; }
+
+// The chunk plans depend on the element type (through the kernels' occupancy) but the
+// workspace size does not: the per-chunk buffers are sized for the larger plan of the two.
+ScanLayout scan_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int64_t ngroups, int dtype) {
   ScanLayout l{};
   l.rows = batch * dim;
   l.ckpt_every = ckpt_steps(padded_states(dstate));
@@ -70,9 +74,15 @@ ScanLayout scan_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqle
   l.per_group = ngroups > 0 ? dim / ngroups : 0;
   l.dblocks = cdiv(l.per_group, rows_per_wave(dstate));  // channel blocks of one wavefront (dB/dC partials)
   const int64_t row_waves = batch * ngroups * l.dblocks;
-  plan_chunks(row_waves, seqlen, fwd_waves_per_simd(dstate), true, &l.chunk_len, &l.n_chunks);
-  plan_chunks(row_waves, seqlen, bwd_waves_per_simd(dstate), true, &l.bwd_chunk_len, &l.bwd_n_chunks);
-  const int64_t nc = l.n_chunks > l.bwd_n_chunks ? l.n_chunks : l.bwd_n_chunks;
+  const int ns = padded_states(dstate);
+  const bool bf16 = dtype == SS2D_DTYPE_BF16;
+  plan_chunks(row_waves, seqlen, fwd_plan_waves(ns, bf16), true, &l.chunk_len, &l.n_chunks);
+  plan_chunks(row_waves, seqlen, bwd_waves_per_simd(ns), true, &l.bwd_chunk_len, &l.bwd_n_chunks);
+  int64_t other_len;
+  int other_n;
+  plan_chunks(row_waves, seqlen, fwd_plan_waves(ns, !bf16), true, &other_len, &other_n);
+  int64_t nc = l.n_chunks > l.bwd_n_chunks ? l.n_chunks : l.bwd_n_chunks;
+  if (other_n > nc) nc = other_n;
   int64_t o = 0;
   l.off_ckpt = o;  o += align_up(l.rows * l.n_ckpt * dstate * 4);
   l.off_sum = o;   o += align_up(l.rows * nc * 4);
@@ -98,7 +108,7 @@ SS2DLayout ss2d_layout(int64_t batch, int64_t dim, int64_t H, int64_t W, int64_t
   int64_t o = 0;
   l.off_xT = o;     o += align_up(batch * dim * L * esize(dtype));
   l.off_ys = o;     o += align_up(batch * 4 * dim * L * 4);
-  l.scan = scan_layout(batch, 4 * dim, dstate, L, 4);
+  l.scan = scan_layout(batch, 4 * dim, dstate, L, 4, dtype);
   l.off_scan = o;   o += l.scan.total;
   l.off_merged = o; o += align_up(batch * dim * L * 4);
   l.off_dM = o;     o += align_up(batch * dim * L * 4);
@@ -184,7 +194,7 @@ int ss2d_cross_merge(const void* ys, void* y, int64_t batch, int64_t channels, i
 size_t selective_scan_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                       int64_t ngroups) {
   if (batch < 0 || dim < 0 || dstate < 1 || seqlen < 0 || ngroups < 1) return 0;
-  return size_t(scan_layout(batch, dim, dstate, seqlen, ngroups).total);
+  return size_t(scan_layout(batch, dim, dstate, seqlen, ngroups, SS2D_DTYPE_BF16).total);
 }
 
 int selective_scan_fwd(const ss_fwd_args* a, hipStream_t stream) {
@@ -202,7 +212,7 @@ int selective_scan_fwd(const ss_fwd_args* a, hipStream_t stream) {
   if (!aligned(a->A, 4) || (a->Dskip && !aligned(a->Dskip, 4)) || (a->delta_bias && !aligned(a->delta_bias, 4)) ||
       (a->last_state && !aligned(a->last_state, 16)))
     return SS2D_ERR_INVALID_ARGUMENT;
-  const ScanLayout lay = scan_layout(a->batch, a->dim, a->dstate, a->seqlen, a->ngroups);
+  const ScanLayout lay = scan_layout(a->batch, a->dim, a->dstate, a->seqlen, a->ngroups, a->dtype);
   if (a->workspace && (a->workspace_bytes < size_t(lay.total) || !aligned(a->workspace, kAlign)))
     return SS2D_ERR_INVALID_ARGUMENT;
 
@@ -465,7 +475,7 @@ int selective_scan_bwd(const ss_bwd_args* a, hipStream_t stream) {
       (a->delta_bias && !aligned(a->delta_bias, 4)) || (a->dDskip && !aligned(a->dDskip, 4)) ||
       (a->ddelta_bias && !aligned(a->ddelta_bias, 4)))
     return SS2D_ERR_INVALID_ARGUMENT;
-  const ScanLayout lay = scan_layout(a->batch, a->dim, a->dstate, a->seqlen, a->ngroups);
+  const ScanLayout lay = scan_layout(a->batch, a->dim, a->dstate, a->seqlen, a->ngroups, a->dtype);
   if (a->workspace_bytes < size_t(lay.total) || !aligned(a->workspace, kAlign)) return SS2D_ERR_INVALID_ARGUMENT;
   if (a->batch * a->ngroups * lay.dblocks * lay.bwd_n_chunks > kMaxBlocks ||
       a->batch * a->ngroups * lay.dblocks * 2 * lay.n_chunks > kMaxBlocks)
