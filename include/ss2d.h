@@ -95,8 +95,9 @@ int ss2d_cross_merge(const void* ys, void* y, int64_t batch, int64_t channels, i
  *           Dskip, delta_bias: (dim)                           fp32, may be NULL
  *           last_state       : (batch, dim, dstate)            fp32, may be NULL
  * The workspace (optional for the forward) receives the scan state at every
- * checkpoint (every 64 steps) so that the backward need not recompute it, and lets the
- * forward split long sequences across wavefronts when there are few rows.
+ * checkpoint (before every 8th step up to 16 states, every 4th up to 32, else every 2nd)
+ * so that the backward need not recompute it, and lets the forward split long sequences
+ * across wavefronts when there are few rows.
  * ------------------------------------------------------------------------------- */
 size_t selective_scan_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                       int64_t ngroups);

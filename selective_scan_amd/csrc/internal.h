@@ -10,10 +10,10 @@ constexpr int kTile = 32;  // time steps staged per tile
 
 // State counts are padded to one of 1, 4, 8, 16, 32, 64 (extra states have zero B/C).
 inline int padded_states(int64_t n) { return n <= 1 ? 1 : n <= 4 ? 4 : n <= 8 ? 8 : n <= 16 ? 16 : n <= 32 ? 32 : 64; }
-// The scan state is checkpointed before every ckpt_steps(NS)-th step: NS * ckpt_steps = 128 floats
-// per lane (32 for NS = 1), the states the backward recomputes and holds in registers at a time.
-// Always a divisor of kTile.
-constexpr int ckpt_steps(int ns) { return ns >= 64 ? 2 : ns >= 32 ? 4 : ns >= 16 ? 8 : ns >= 8 ? 16 : 32; }
+// The scan state is checkpointed before every ckpt_steps(NS)-th step.  The backward recomputes
+// and holds one such sub-interval at a time (its states and per-step values in registers), so
+// it is short: 8 steps up to 16 states, then NS * ckpt_steps = 128.  Always a divisor of kTile.
+constexpr int ckpt_steps(int ns) { return ns >= 64 ? 2 : ns >= 32 ? 4 : 8; }
 // Resident wavefronts per SIMD of the SS2D scan kernels (512 VGPRs per lane shared by the
 // resident wavefronts), by padded state count; the bf16 forward kernel is compiled to reach it.
 constexpr int fwd_waves_per_simd(int ns, bool bf16) {
@@ -86,7 +86,7 @@ struct ScanFwdParams {
   const float* delta_bias;
   void* out;           // may be null (state-only pass)
   float* last_state;   // may be null
-  float* ckpt;         // (batch*dim, n_ckpt, N) or null
+  float* ckpt;         // (n_ckpt, batch*dim, N) or null: one checkpoint of all rows is contiguous
   float* chunk_sum;    // (batch*dim, n_chunks) or null
   int64_t batch, dim, L, G, per_group, dblocks, chunk_len;
   int n_chunks, n_ckpt, N;
@@ -118,7 +118,7 @@ struct ScanBwdParams {
   void* du;                // generic: dtype; ss2d: fp32 route order (batch, 4D, L)
   void* ddelta;            // dtype (batch, dim, L)
   void* dz;                // generic only, dtype
-  const float* ckpt;       // (rows, n_ckpt, N) states before every kCkpt-th step
+  const float* ckpt;       // (n_ckpt, rows, N) states before every ckpt_steps-th step
   float* lam_carry;        // (rows, n_chunks, N): a_{t1} * lambda_{t1} flowing into each chunk
   float* chunk_sum;        // (rows, n_chunks)
   float* dB_part;          // (dblocks, batch, G, N, L) fp32

@@ -30,33 +30,116 @@ namespace ss2d {
 namespace bwd_detail {
 using namespace scan_detail;
 
+// Cross-lane exchanges of the transpose-reduce below.
+//
+// v_permlane32_swap_b32 x, y exchanges lanes 32..63 of x with lanes 0..31 of y, and
+// v_permlane16_swap_b32 x, y the odd 16-lane rows of x with the even rows of y.  Either way,
+// afterwards the lane whose mask bit is clear holds (its own x, its partner's x) and the lane
+// whose bit is set (its partner's y, its own y): x + y is the pair sum of the half the lane
+// keeps, with no per-lane select.  The instructions are written as inline asm (the compiler
+// builtin returns only one of the two registers here); a VALU result read by a swap needs two
+// wait states, hence the s_nop ahead of each group of swaps.
+template <int kMask>
+__device__ __forceinline__ void swap_pairs4(float& x0, float& y0, float& x1, float& y1, float& x2, float& y2,
+                                            float& x3, float& y3) {
+  if (kMask == 32)
+    asm volatile(
+        "s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_permlane32_swap_b32 %2, %3\n\t"
+        "v_permlane32_swap_b32 %4, %5\n\tv_permlane32_swap_b32 %6, %7"
+        : "+v"(x0), "+v"(y0), "+v"(x1), "+v"(y1), "+v"(x2), "+v"(y2), "+v"(x3), "+v"(y3));
+  else
+    asm volatile(
+        "s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3\n\t"
+        "v_permlane16_swap_b32 %4, %5\n\tv_permlane16_swap_b32 %6, %7"
+        : "+v"(x0), "+v"(y0), "+v"(x1), "+v"(y1), "+v"(x2), "+v"(y2), "+v"(x3), "+v"(y3));
+}
+template <int kMask>
+__device__ __forceinline__ void swap_pair(float& x, float& y) {
+  if (kMask == 32)
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+  else
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+}
+
+// the value of lane (lane ^ m) within a 16-lane row, read by DPP; for m = 4 there is no xor
+// pattern, so lanes with bit 2 clear read row_shl:4 (lane + 4) and the others row_shr:4
+template <int kCtrl>
+__device__ __forceinline__ float dpp_read(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
+}
+template <int m, bool kUpper>
+__device__ __forceinline__ float row_partner(float x) {
+  if (m == 8) return dpp_read<0x128>(x);            // row_ror:8
+  if (m == 4) return dpp_read<kUpper ? 0x114 : 0x104>(x);  // row_shr:4 / row_shl:4
+  if (m == 2) return dpp_read<0x4E>(x);             // quad_perm [2,3,0,1]
+  return dpp_read<0xB1>(x);                         // quad_perm [1,0,3,2]
+}
+
+// One halving level at mask m over cnt values (cnt even): lane bit m set keeps the upper half.
+template <int V, int m>
+__device__ __forceinline__ void halve_level(float* v, int cnt, int lane) {
+  const int half = cnt / 2;
+  if (m >= 16) {
+    int k = 0;
+#pragma unroll
+    for (int k4 = 0; k4 < V / 8; ++k4)
+      if (4 * k4 + 3 < half) {
+        swap_pairs4<m>(v[4 * k4], v[4 * k4 + half], v[4 * k4 + 1], v[4 * k4 + 1 + half], v[4 * k4 + 2],
+                       v[4 * k4 + 2 + half], v[4 * k4 + 3], v[4 * k4 + 3 + half]);
+        k = 4 * k4 + 4;
+      }
+#pragma unroll
+    for (int j = 0; j < V / 2; ++j)
+      if (j >= k && j < half) swap_pair<m>(v[j], v[j + half]);
+#pragma unroll
+    for (int j = 0; j < V / 2; ++j)
+      if (j < half) v[j] = v[j] + v[j + half];
+  } else {
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int j = 0; j < V / 2; ++j) {
+      if (j < half) {
+        const float lo = v[j] + row_partner<m, false>(v[j]);
+        const float hi = v[j + half] + row_partner<m, true>(v[j + half]);
+        v[j] = upper ? hi : lo;
+      }
+    }
+  }
+}
+
+// Butterfly on one value at mask m: every lane gets the sum with lane (lane ^ m).
+template <int m>
+__device__ __forceinline__ void butterfly(float* v, int lane) {
+  if (m >= 16) {
+    float x = v[0], y = v[0];
+    swap_pair<m>(x, y);
+    v[0] = x + y;
+  } else if (m == 4) {
+    const float lo = row_partner<4, false>(v[0]), hi = row_partner<4, true>(v[0]);
+    v[0] += (lane & 4) ? hi : lo;
+  } else {
+    v[0] += row_partner<m, false>(v[0]);
+  }
+}
+
 // Sum V values per lane over the lanes that differ in the bits of the masks 32, 16, ..., kMinMask
 // (kMinMask = 1: all 64 lanes; kMinMask = 2: the 32 lanes of the same parity).  Halving exchanges
 // from the highest mask down while more than one value is left (lane bit m set: keep the upper
-// half), then plain butterflies.  On return v[0 .. V >> H) of lane l holds the totals of the
+// half), then butterflies.  On return v[0 .. reduce_left) of lane l holds the totals of the
 // original indices reduce_index<V, kMinMask>(l, r).
+template <int V, int kMinMask, int m = 32>
+__device__ __forceinline__ void lane_transpose_reduce_from(float* v, int lane, int cnt) {
+  if (cnt > 1) {
+    halve_level<V, m>(v, cnt, lane);
+    cnt /= 2;
+  } else {
+    butterfly<m>(v, lane);
+  }
+  if constexpr (m / 2 >= kMinMask) lane_transpose_reduce_from<V, kMinMask, m / 2>(v, lane, cnt);
+}
 template <int V, int kMinMask>
 __device__ __forceinline__ void lane_transpose_reduce(float* v, int lane) {
-  int cnt = V;
-#pragma unroll
-  for (int m = 32; m >= kMinMask; m >>= 1) {
-    if (cnt > 1) {
-      const bool upper = (lane & m) != 0;
-      const int half = cnt / 2;
-#pragma unroll
-      for (int k = 0; k < V / 2; ++k) {
-        if (k < half) {
-          const float lo = v[k], hi = v[k + half];
-          const float send = upper ? lo : hi;
-          const float keep = upper ? hi : lo;
-          v[k] = keep + __shfl_xor(send, m, kWave);
-        }
-      }
-      cnt = half;
-    } else {
-      v[0] += __shfl_xor(v[0], m, kWave);
-    }
-  }
+  lane_transpose_reduce_from<V, kMinMask, 32>(v, lane, V);
 }
 
 // values left per lane after lane_transpose_reduce, and the original index of v[r]
@@ -102,7 +185,7 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
   constexpr int S = (NS < 4) ? 4 : NS + 4;
   constexpr int kSub = ckpt_steps(NS);
   constexpr int kMinMask = kSplit;                                  // lanes of a channel differ in bit 0
-  constexpr int kRW = (2 * NSL < 32 / kSplit) ? 32 / kSplit : 2 * NSL;  // per-step dB/dC reduce width
+  constexpr int kRW = 2 * NSL;  // per-step dB/dC values of a lane (its states' dB terms, then dC terms)
   constexpr int kLeft = reduce_left<kRW, kMinMask>();
   constexpr int kInner = (64 / NSL < kSub) ? 64 / NSL : kSub;       // steps whose states are held at once
   __shared__ __align__(16) float sB[kTile * S];
@@ -153,7 +236,6 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
 
   const int64_t t_begin = int64_t(c) * p.chunk_len;
   const int64_t t_end = (t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L;
-  const int64_t n_tiles = (t_end - t_begin + kTile - 1) / kTile;
 
   // mu = a_{t+1} lambda_{t+1}: the adjoint flowing into step t from later steps
   float mu[NSL];
@@ -176,25 +258,12 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
     return x;
   };
 
-  for (int64_t jt = n_tiles - 1; jt >= 0; --jt) {
-    const int64_t t0 = t_begin + jt * kTile;
-    {
-      BCStage<T, NS, kVec> bc;
-      bc.load(Bg, Cg, N, L, t0, t_end, lane);
-      __syncthreads();
-      bc.template store<S>(sB, sC, lane);
-      __syncthreads();
-    }
-#pragma unroll 1
-    for (int q = kTile / kSub - 1; q >= 0; --q) {
-      const int64_t s0 = t0 + int64_t(q) * kSub;  // first step of this sub-interval
-      if (s0 >= t_end) continue;
+  // The range is walked backwards one sub-interval (kSub steps) at a time.  seg_body handles
+  // the sub-interval starting at s0 (index q within the tile staged in LDS): dv, uv, gv, zv are
+  // its delta, u, dout and z values and h0_of(n) the state before s0.
+  auto seg_body = [&](int64_t s0, int q, const float* dv, const float* uv, const float* gv, const float* zv,
+                      auto h0_of) {
       const int ns = int((t_end - s0 < kSub) ? (t_end - s0) : kSub);
-      float dv[kSub], uv[kSub], gv[kSub], zv[kSub];
-      load_seg<T, kVec, kSub>(dv, delta_row, s0, t_end, L, false);
-      load_seg<T, kVec, kSub>(uv, u_row, s0, t_end, L, rev);
-      load_seg<DT, kVec, kSub>(gv, dout_row, s0, t_end, L, rev);
-      if (has_z) load_seg<T, kVec, kSub>(zv, z_row, s0, t_end, L, false);
       // per-step quantities (steps past the range and inactive lanes contribute nothing)
       float lam[kSub], dup[kSub], dy[kSub];
 #pragma unroll
@@ -213,9 +282,8 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
         // pieces of kInner steps, last piece first; for each piece the states are recomputed
         // forwards from the checkpoint and only the piece's own kInner x NSL states are kept.
         float h0[NSL];
-        const float* ck = p.ckpt + (row * p.n_ckpt + s0 / kSub) * N + n0;
 #pragma unroll
-        for (int n = 0; n < NSL; ++n) h0[n] = (n < nvalid) ? ck[n] : 0.0f;
+        for (int n = 0; n < NSL; ++n) h0[n] = h0_of(n);
 #pragma unroll
         for (int pc = kSub / kInner - 1; pc >= 0; --pc) {
           float hstart[NSL];
@@ -251,8 +319,6 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
             asm volatile("" : "+v"(lr));
             float sbl = 0.0f, ddt = 0.0f, yv = 0.0f;
             float red[kRW];
-#pragma unroll
-            for (int e = 2 * NSL; e < kRW; ++e) red[e] = 0.0f;
 #pragma unroll
             for (int n = 0; n < NSL; ++n) {
               const float a = fast_exp2(lr * Acoef[n]);
@@ -290,7 +356,7 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
               for (int r = 0; r < kLeft; ++r) {
                 const int e = reduce_index<kRW, kMinMask>(lane, r);  // e < NSL: dB, else dC (state n0 + e % NSL)
                 const int n = e < NSL ? e : e - NSL;
-                if (e < 2 * NSL && n < nvalid) {
+                if (n < nvalid) {
                   float* dst = (e < NSL) ? p.dB_part : p.dC_part;
                   dst[(((dblk * p.batch + b) * p.G + g) * N + n0 + n) * L + t] = red[r];
                 }
@@ -319,6 +385,75 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
           }
           lam_sum += lam[i];
         }
+      }
+  };
+
+  auto stage_tile = [&](int64_t t0) {
+    BCStage<T, NS, kVec> bc;
+    bc.load(Bg, Cg, N, L, t0, t_end, lane);
+    __syncthreads();  // the previous tile's LDS reads are complete
+    bc.template store<S>(sB, sC, lane);
+    __syncthreads();
+  };
+  constexpr int kSegsPerTile = kTile / kSub;
+  if constexpr (kSplit == 1) {
+    // One lane per channel (used when rows are few and the kernel is latency-bound): the row
+    // segments and start state of the next sub-interval are loaded while this one computes.
+    const int64_t n_segs = (t_end - t_begin + kSub - 1) / kSub;
+    RowTile<T, kSub> nd, nu, nz;
+    RowTile<DT, kSub> ng;
+    float nh0[NSL];
+    auto prefetch_seg = [&](int64_t s0) {
+      load_row<T, kVec, kSub>(nd, delta_row, s0, t_end, L, false);
+      load_row<T, kVec, kSub>(nu, u_row, s0, t_end, L, rev);
+      load_row<DT, kVec, kSub>(ng, dout_row, s0, t_end, L, rev);
+      if (has_z) load_row<T, kVec, kSub>(nz, z_row, s0, t_end, L, false);
+      if (kPass == 0) {
+        const float* ck = p.ckpt + ((s0 / kSub) * p.batch * p.dim + row) * N + n0;
+#pragma unroll
+        for (int n = 0; n < NSL; ++n) nh0[n] = (n < nvalid) ? ck[n] : 0.0f;
+      }
+    };
+    if (n_segs > 0) prefetch_seg(t_begin + (n_segs - 1) * kSub);
+#pragma unroll 1
+    for (int64_t si = n_segs - 1; si >= 0; --si) {
+      const int64_t s0 = t_begin + si * kSub;
+      const int q = int(((s0 - t_begin) % kTile) / kSub);
+      if (si == n_segs - 1 || q == kSegsPerTile - 1) stage_tile(s0 - int64_t(q) * kSub);
+      const RowTile<T, kSub> cd = nd, cu = nu, cz = nz;
+      const RowTile<DT, kSub> cg = ng;
+      float h0[NSL];
+#pragma unroll
+      for (int n = 0; n < NSL; ++n) h0[n] = nh0[n];
+      if (si > 0) prefetch_seg(s0 - kSub);
+      float dv[kSub], uv[kSub], gv[kSub], zv[kSub];
+#pragma unroll
+      for (int i = 0; i < kSub; ++i) {
+        dv[i] = cd.get(i);
+        uv[i] = cu.get(i);
+        gv[i] = cg.get(i);
+        zv[i] = has_z ? cz.get(i) : 0.0f;
+      }
+      seg_body(s0, q, dv, uv, gv, zv, [&](int n) { return h0[n]; });
+    }
+  } else {
+    // Two lanes per channel (full occupancy): each sub-interval loads its own values; the
+    // other resident wavefronts cover the latency.
+    const int64_t n_tiles = (t_end - t_begin + kTile - 1) / kTile;
+    for (int64_t jt = n_tiles - 1; jt >= 0; --jt) {
+      const int64_t t0 = t_begin + jt * kTile;
+      stage_tile(t0);
+#pragma unroll 1
+      for (int q = kSegsPerTile - 1; q >= 0; --q) {
+        const int64_t s0 = t0 + int64_t(q) * kSub;
+        if (s0 >= t_end) continue;
+        float dv[kSub], uv[kSub], gv[kSub], zv[kSub];
+        load_seg<T, kVec, kSub>(dv, delta_row, s0, t_end, L, false);
+        load_seg<T, kVec, kSub>(uv, u_row, s0, t_end, L, rev);
+        load_seg<DT, kVec, kSub>(gv, dout_row, s0, t_end, L, rev);
+        if (has_z) load_seg<T, kVec, kSub>(zv, z_row, s0, t_end, L, false);
+        const float* ck = p.ckpt + ((s0 / kSub) * p.batch * p.dim + row) * N + n0;
+        seg_body(s0, q, dv, uv, gv, zv, [&](int n) { return (n < nvalid) ? ck[n] : 0.0f; });
       }
     }
   }

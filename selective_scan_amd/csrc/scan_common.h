@@ -7,19 +7,20 @@
 namespace ss2d {
 namespace scan_detail {
 
-// Per-lane copy of one row's tile (kTile consecutive elements), kept in the storage format.
-template <typename T>
+// Per-lane copy of kLen consecutive elements of one row (a tile by default), kept in the storage
+// format until used.
+template <typename T, int kLen = kTile>
 struct RowTile;
-template <>
-struct RowTile<float> {
-  float4 v[kTile / 4];
+template <int kLen>
+struct RowTile<float, kLen> {
+  float4 v[(kLen + 3) / 4];
   __device__ __forceinline__ float get(int i) const {
     const float4 q = v[i / 4];
     return (i % 4 == 0) ? q.x : (i % 4 == 1) ? q.y : (i % 4 == 2) ? q.z : q.w;
   }
   __device__ __forceinline__ void zero() {
 #pragma unroll
-    for (int j = 0; j < kTile / 4; ++j) v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < (kLen + 3) / 4; ++j) v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __device__ __forceinline__ void load_vec(const float* p, int j) { v[j] = *reinterpret_cast<const float4*>(p); }
   __device__ __forceinline__ void set(int i, float x) {
@@ -27,19 +28,19 @@ struct RowTile<float> {
     if (i % 4 == 0) q.x = x; else if (i % 4 == 1) q.y = x; else if (i % 4 == 2) q.z = x; else q.w = x;
   }
   __device__ __forceinline__ void reverse() {
-    float4 r[kTile / 4];
+    float4 r[(kLen + 3) / 4];
 #pragma unroll
-    for (int j = 0; j < kTile / 4; ++j) {
-      const float4 q = v[kTile / 4 - 1 - j];
+    for (int j = 0; j < kLen / 4; ++j) {
+      const float4 q = v[kLen / 4 - 1 - j];
       r[j] = make_float4(q.w, q.z, q.y, q.x);
     }
 #pragma unroll
-    for (int j = 0; j < kTile / 4; ++j) v[j] = r[j];
+    for (int j = 0; j < kLen / 4; ++j) v[j] = r[j];
   }
 };
-template <>
-struct RowTile<bf16> {
-  uint2 v[kTile / 4];
+template <int kLen>
+struct RowTile<bf16, kLen> {
+  uint2 v[(kLen + 3) / 4];
   __device__ __forceinline__ float get(int i) const {
     const uint2 q = v[i / 4];
     const uint32_t w = ((i % 4) < 2) ? q.x : q.y;
@@ -47,7 +48,7 @@ struct RowTile<bf16> {
   }
   __device__ __forceinline__ void zero() {
 #pragma unroll
-    for (int j = 0; j < kTile / 4; ++j) v[j] = make_uint2(0u, 0u);
+    for (int j = 0; j < (kLen + 3) / 4; ++j) v[j] = make_uint2(0u, 0u);
   }
   __device__ __forceinline__ void load_vec(const bf16* p, int j) { v[j] = *reinterpret_cast<const uint2*>(p); }
   __device__ __forceinline__ void set(int i, uint16_t bits) {
@@ -56,34 +57,38 @@ struct RowTile<bf16> {
     w = (i % 2 == 0) ? ((w & 0xffff0000u) | bits) : ((w & 0xffffu) | (uint32_t(bits) << 16));
   }
   __device__ __forceinline__ void reverse() {
-    uint2 r[kTile / 4];
+    uint2 r[(kLen + 3) / 4];
 #pragma unroll
-    for (int j = 0; j < kTile / 4; ++j) {
-      const uint2 q = v[kTile / 4 - 1 - j];
+    for (int j = 0; j < kLen / 4; ++j) {
+      const uint2 q = v[kLen / 4 - 1 - j];
       r[j] = make_uint2(__builtin_amdgcn_alignbit(q.y, q.y, 16), __builtin_amdgcn_alignbit(q.x, q.x, 16));
     }
 #pragma unroll
-    for (int j = 0; j < kTile / 4; ++j) v[j] = r[j];
+    for (int j = 0; j < kLen / 4; ++j) v[j] = r[j];
   }
 };
 
-template <typename T>
-__device__ __forceinline__ void set_elem(RowTile<T>& t, int i, const T* p);
-template <>
-__device__ __forceinline__ void set_elem<float>(RowTile<float>& t, int i, const float* p) { t.set(i, *p); }
-template <>
-__device__ __forceinline__ void set_elem<bf16>(RowTile<bf16>& t, int i, const bf16* p) { t.set(i, p->bits); }
+template <typename T, int kLen>
+__device__ __forceinline__ void set_elem(RowTile<T, kLen>& t, int i, const T* p) {
+  if constexpr (sizeof(T) == 4)
+    t.set(i, *p);
+  else
+    t.set(i, p->bits);
+}
 
-// Load steps [t0, t0 + kTile) of a row.  Forward rows read elements t0.., reversed rows read
+// Load steps [t0, t0 + kLen) of a row.  Forward rows read elements t0.., reversed rows read
 // pixels L-1-t for the same steps (then the tile is flipped so that index i is step t0 + i).
-template <typename T, bool kVec>
-__device__ __forceinline__ void load_row(RowTile<T>& tile, const T* row, int64_t t0, int64_t t_end, int64_t L,
+// Steps at or past t_end read as zero.  Vector loads need L % 4 == 0, t0 % 4 == 0 and
+// kLen % 4 == 0 (shorter pieces are read element by element).
+template <typename T, bool kVecArg, int kLen = kTile>
+__device__ __forceinline__ void load_row(RowTile<T, kLen>& tile, const T* row, int64_t t0, int64_t t_end, int64_t L,
                                          bool rev) {
-  if (kVec && t0 + kTile <= t_end) {
+  constexpr bool kVec = kVecArg && kLen % 4 == 0;
+  if (kVec && t0 + kLen <= t_end) {
     // whole tile in range: unconditional vector loads, nothing to zero
-    const int64_t base = rev ? (L - t0 - kTile) : t0;
+    const int64_t base = rev ? (L - t0 - kLen) : t0;
 #pragma unroll
-    for (int j = 0; j < kTile / 4; ++j) tile.load_vec(row + base + 4 * j, j);
+    for (int j = 0; j < kLen / 4; ++j) tile.load_vec(row + base + 4 * j, j);
     if (rev) tile.reverse();
     return;
   }
@@ -91,20 +96,20 @@ __device__ __forceinline__ void load_row(RowTile<T>& tile, const T* row, int64_t
   if (kVec) {
     if (!rev) {
 #pragma unroll
-      for (int j = 0; j < kTile / 4; ++j)
+      for (int j = 0; j < kLen / 4; ++j)
         if (t0 + 4 * j < t_end) tile.load_vec(row + t0 + 4 * j, j);
     } else {
-      const int64_t base = L - t0 - kTile;  // pixel of tile element kTile-1
+      const int64_t base = L - t0 - kLen;  // pixel of tile element kLen-1
 #pragma unroll
-      for (int j = 0; j < kTile / 4; ++j)
+      for (int j = 0; j < kLen / 4; ++j)
         if (base + 4 * j >= 0 && L - 1 - (base + 4 * j + 3) < t_end) tile.load_vec(row + base + 4 * j, j);
       tile.reverse();
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < kTile; ++i) {
+    for (int i = 0; i < kLen; ++i) {
       const int64_t t = t0 + i;
-      if (t < t_end) set_elem<T>(tile, i, row + (rev ? (L - 1 - t) : t));
+      if (t < t_end) set_elem<T, kLen>(tile, i, row + (rev ? (L - 1 - t) : t));
     }
   }
 }

@@ -22,7 +22,7 @@ __global__ __launch_bounds__(256) void chunk_combine_kernel(const ScanFwdParams 
   const float A = p.A[d * p.N + n];
   float h = 0.0f;
   for (int c = 0; c < p.n_chunks; ++c) {
-    float* slot = p.ckpt + (row * p.n_ckpt + (int64_t(c) * p.chunk_len) / p.ckpt_every) * p.N + n;
+    float* slot = p.ckpt + (((int64_t(c) * p.chunk_len) / p.ckpt_every) * rows + row) * p.N + n;
     if (c > 0) h = fmaf(fast_exp2(A * p.chunk_sum[row * p.n_chunks + c - 1]), h, *slot);
     *slot = h;
   }

@@ -91,7 +91,7 @@ void scan_fwd_kernel(const ScanFwdParams p) {
 #pragma unroll
   for (int n = 0; n < NSL; ++n) h[n] = 0.0f;
   if (kPass == 0 && p.n_chunks > 1 && c > 0) {
-    const float* src = p.ckpt + (row * p.n_ckpt + t_begin / kSub) * N + n0;
+    const float* src = p.ckpt + ((t_begin / kSub) * p.batch * p.dim + row) * N + n0;
 #pragma unroll
     for (int n = 0; n < NSL; ++n)
       if (n < nvalid) h[n] = src[n];
@@ -171,7 +171,7 @@ void scan_fwd_kernel(const ScanFwdParams p) {
         // several steps' values live at once and exceed the register file)
         asm volatile("" ::: "memory");
         if (kStore && (i % kSub) == 0) {
-          if (i < nt && active) store_state<NSL>(p.ckpt + (row * p.n_ckpt + (t0 + i) / kSub) * N + n0, h, nvalid);
+          if (i < nt && active) store_state<NSL>(p.ckpt + (((t0 + i) / kSub) * p.batch * p.dim + row) * N + n0, h, nvalid);
         }
         const float* cb = bufb[i & 1];
         const float* cc = bufc[i & 1];
@@ -215,7 +215,7 @@ void scan_fwd_kernel(const ScanFwdParams p) {
 
   if (!active) return;
   if (kPass == 1) {
-    if (t_end < L) store_state<NSL>(p.ckpt + (row * p.n_ckpt + t_end / kSub) * N + n0, h, nvalid);
+    if (t_end < L) store_state<NSL>(p.ckpt + ((t_end / kSub) * p.batch * p.dim + row) * N + n0, h, nvalid);
     if (part == 0) p.chunk_sum[row * p.n_chunks + c] = lam_sum;
   } else if (p.last_state && t_end == L) {
     store_state<NSL>(p.last_state + row * N + n0, h, nvalid);
