@@ -6,17 +6,23 @@ cross-merge + skip + gate) over one batch of the stage-1 VMamba workload (batch 
 56x56 map, D = 192 channels, N = 16 states, bf16 I/O, fp32 state, z gate).  Inputs are
 seeded synthetic tensors already resident in HBM when the timed region starts.
 
-Prints one JSON line: elements/s (B*K*D*L per second) as the value, the whole-step
-algorithmic HBM rate, the roofline of the dominant kernel (the route-scan kernel, timed
-live with HIP events on the launch stream) and the fp64 CPU oracle timed on this host on
-a bounded sample of the same workload.  `--workload` selects one of the other shapes
-(used for profiling); `--bwd` adds the fused backward to each step.
+Prints one JSON line: elements/s (B*K*D*L per second) as the value, per-step median /
+min / max, the whole-step algorithmic HBM rate against the 8 TB/s peak and against a
+device copy timed in the same run, the roofline of the dominant kernel (the route-scan
+kernel, timed live with HIP events on the stream it is launched on) and the fp64 CPU
+oracle timed on this host on a bounded sample of the same workload.  `--workload`
+selects one of the other shapes; `--bwd` adds the fused backward to each step.
+
+When one input/output set is smaller than the 256 MB last-level cache (MALL) several
+times over, the steps rotate over independent copies so that no step re-reads what the
+previous one left in that cache.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -28,9 +34,18 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SS2D scan elements/s (B·K·D·L) + achieved HBM GB/s vs peak, 56×56 stage"
 HBM_PEAK_GBPS = 8000.0
-# fp32 vector peak without packed instructions: 256 CUs x 64 lanes x 2 flops (FMA) x 2.4 GHz
-VALU_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
-FLOPS_PER_STATE_STEP = 7  # exp(delta*A): mul + exp; delta*u*B: mul; h = a*h + b: fma; y += C*h: fma
+CLOCK_HZ = 2.4e9
+SIMDS = 256 * 4  # 256 CUs x 4 SIMDs, 16 fp32 lanes each
+# fp32 vector peak without packed math: 1024 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz
+VALU_PEAK_TFLOPS = SIMDS * 16 * 2 * CLOCK_HZ / 1e12
+# Per (element, state) the scan issues 4 full-rate VALU ops (Lam*A, (Lam*u)*B, the FMA into
+# h, the FMA into y: 7 flops counting the exp as one) and one v_exp_f32.  A wave64 VALU op
+# occupies a 16-lane SIMD for 4 cycles, a transcendental for 8, so 64 state-steps cost
+# 4*4 + 8 = 24 SIMD cycles: the issue-limited peak for this instruction mix.
+FLOPS_PER_STATE_STEP = 7
+MIX_PEAK_TFLOPS = SIMDS * CLOCK_HZ * 64 / 24 * FLOPS_PER_STATE_STEP / 1e12
+MALL_BYTES = 256 << 20
+COPY_BYTES = 1 << 30
 
 
 def parse():
@@ -42,9 +57,6 @@ def parse():
     ap.add_argument("--bwd", action="store_true", help="time forward + backward per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time for the sample")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="after the timed region, copy 1 GiB device-to-device 3 times (a plain copy of known size "
-                         "that calibrates the HBM byte counters of a profiler run)")
     return ap.parse_args()
 
 
@@ -63,7 +75,7 @@ def algorithmic_bytes(cfg, bwd=False):
 
 def scan_kernel_source_hash():
     h = hashlib.sha256()
-    for name in ("scan_fwd_kernel.h", "scan_common.h", "device_common.h"):
+    for name in ("scan_fwd_kernel.h", "scan_common.h", "device_common.h", "internal.h"):
         with open(os.path.join(ROOT, "selective_scan_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -81,6 +93,17 @@ def load_traffic(workload_name):
     if not entry or entry.get("kernel_source_sha") != scan_kernel_source_hash():
         return None
     return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(cfg, inp, target_s, bwd=False):
@@ -106,8 +129,14 @@ def cpu_baseline(cfg, inp, target_s, bwd=False):
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     return {"value": elems / t, "unit": "elements/s", "cores": threads, "kind": "oracle",
             "sample": f"first {nb} of {cfg.batch} images (all {cfg.dim} channels, 4 routes, "
-                      f"L={cfg.seqlen}, N={cfg.dstate}), fp64 C oracle with OpenMP, "
-                      f"{'forward + backward' if bwd else 'forward'}, {t:.2f} s wall"}
+                      f"L={cfg.seqlen}, N={cfg.dstate}), fp64 C oracle with OpenMP over rows, "
+                      f"{'forward + backward' if bwd else 'forward'}, {t:.2f} s wall",
+            "cpu_model": cpu_model()}
+
+
+def stats(ms):
+    return {"median": float(np.median(ms)), "min": float(np.min(ms)), "max": float(np.max(ms)),
+            "mean": float(np.mean(ms))}
 
 
 def main():
@@ -131,50 +160,74 @@ def main():
             return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
-    d = dict(x=dev(inp["x"], cfg.dtype), delta=dev(inp["delta"], cfg.dtype), A=dev(inp["A"], "f32"),
-             B=dev(inp["B"], cfg.dtype), C=dev(inp["C"], cfg.dtype), D=dev(inp["D"], "f32"),
-             delta_bias=dev(inp["delta_bias"], "f32"), z=dev(inp["z"], cfg.dtype) if cfg.has_z else None)
-    dout = dev(inp["dout"], cfg.dtype) if args.bwd else None
-    plan = ss.SS2DForwardPlan(**d)
+    d0 = dict(x=dev(inp["x"], cfg.dtype), delta=dev(inp["delta"], cfg.dtype), A=dev(inp["A"], "f32"),
+              B=dev(inp["B"], cfg.dtype), C=dev(inp["C"], cfg.dtype), D=dev(inp["D"], "f32"),
+              delta_bias=dev(inp["delta_bias"], "f32"), z=dev(inp["z"], cfg.dtype) if cfg.has_z else None)
+    dout0 = dev(inp["dout"], cfg.dtype) if args.bwd else None
+    plan0 = ss.SS2DForwardPlan(**d0)
+    # bytes one step touches in HBM (inputs, output, workspace): rotate independent copies
+    # until one cycle over them exceeds three times the MALL
+    footprint = sum(t.numel() * t.element_size() for t in d0.values() if t is not None)
+    footprint += plan0.out.numel() * plan0.out.element_size() + plan0.workspace.numel()
+    n_sets = max(1, math.ceil(3 * MALL_BYTES / footprint))
+    sets = [(d0, dout0, plan0)]
+    for _ in range(n_sets - 1):
+        dk = {k: (None if v is None else v.clone()) for k, v in d0.items()}
+        sets.append((dk, None if dout0 is None else dout0.clone(), ss.SS2DForwardPlan(**dk)))
     stream = torch.cuda.current_stream()
 
-    def step(ev_scan=None):
+    def step(i, ev=None):
+        d, dout, plan = sets[i % n_sets]
+        if ev is not None:
+            ev[0].record(stream)
         plan.run_stage(0)
-        if ev_scan is not None:
-            ev_scan[0].record(stream)
+        if ev is not None:
+            ev[1].record(stream)
         plan.run_stage(1)
-        if ev_scan is not None:
-            ev_scan[1].record(stream)
+        if ev is not None:
+            ev[2].record(stream)
         plan.run_stage(2)
         if args.bwd:
             ss.ss2d_bwd(**d, dout=dout, workspace=plan.workspace)
+        if ev is not None:
+            ev[3].record(stream)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
-    scan_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step(scan_ev[i])
+        step(i, evs[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
-    scan_ms = float(np.mean([a.elapsed_time(b) for a, b in scan_ev]))
+    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    scan_ms = [e[1].elapsed_time(e[2]) for e in evs]
 
-    if args.copy_probe:
-        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+    # a plain device copy of known size in the same run: the practical HBM ceiling (its three
+    # dispatches also calibrate the byte counters of a profiler run of this program)
+    del sets, d0, plan0, dout0
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    copy_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
+    for a, b in copy_ev:
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * COPY_BYTES / (np.median([a.elapsed_time(b) for a, b in copy_ev]) * 1e-3) / 1e9
 
     elements = cfg.elements
     step_bytes = algorithmic_bytes(cfg, args.bwd)
     flops = elements * cfg.dstate * FLOPS_PER_STATE_STEP
-    achieved_tflops = flops / (scan_ms * 1e-3) / 1e12
+    scan_mean = float(np.mean(scan_ms))
+    achieved_tflops = flops / (scan_mean * 1e-3) / 1e12
     traffic = load_traffic(cfg.name)
+    hbm_gbps = step_bytes / (ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
         "value": elements / (ms * 1e-3),
@@ -190,15 +243,19 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs, S4D-real A, inverse-softplus dt bias)",
         "config": {"workload": ("ss2d_fwd+bwd " if args.bwd else "ss2d_fwd ") + cfg.name,
                    "batch": cfg.batch, "height": cfg.height, "width": cfg.width, "routes": 4,
-                   "dim": cfg.dim, "dstate": cfg.dstate, "gate_z": cfg.has_z},
+                   "dim": cfg.dim, "dstate": cfg.dstate, "gate_z": cfg.has_z, "io_sets_rotated": n_sets},
+        "step_ms": stats(step_ms),
         "hbm": {"algorithmic_bytes_per_step": step_bytes,
-                "achieved_GBps": step_bytes / (ms * 1e-3) / 1e9,
+                "achieved_GBps": hbm_gbps,
                 "peak_GBps": HBM_PEAK_GBPS,
-                "frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+                "frac": hbm_gbps / HBM_PEAK_GBPS,
+                "copy_ceiling_GBps": copy_gbps,
+                "frac_of_copy": hbm_gbps / copy_gbps},
         "roofline": {"kernel": "route scan (scan_fwd_kernel)", "bound": "alu",
                      "achieved": achieved_tflops, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved_tflops / VALU_PEAK_TFLOPS, "traffic": traffic,
-                     "ms_per_launch": scan_ms, "flops_per_launch": flops},
+                     "mix_peak": MIX_PEAK_TFLOPS, "frac_of_mix_peak": achieved_tflops / MIX_PEAK_TFLOPS,
+                     "ms_per_launch": scan_mean, "launch_ms": stats(scan_ms), "flops_per_launch": flops},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds, args.bwd)
