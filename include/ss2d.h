@@ -165,6 +165,8 @@ int selective_scan_bwd(const ss_bwd_args* args, hipStream_t stream);
  * Fused SS2D forward [VMamba, SS2D section]: equivalent, up to fp32 rounding order, to
  *   cross_merge(selective_scan_fwd(cross_scan(x), delta, A, B, C, D, delta_bias,
  *               softplus, ngroups = 4))  then  * silu(z)  per pixel (z optional)
+ * As in that composition, each route's output y_k is rounded to dtype before the four are
+ * summed in fp32; the gate is applied to the fp32 sum, which is rounded once to dtype.
  * Layouts:  x, z, out  : (batch, dim, height, width)      dtype   (grid)
  *           delta      : (batch, 4, dim, L)               dtype   (route k in its own order)
  *           Bm, Cm     : (batch, 4, dstate, L)            dtype   (shared by the dim channels

@@ -220,8 +220,9 @@ __global__ __launch_bounds__(kPlaneThreads) void transpose_plane_kernel(const W*
   }
 }
 
-// The SS2D merge with fp32 routes: y = (((r0 + r1) + r2) + r3) [+ Dsum * x] [* silu(z)], per plane.
-template <typename T>
+// The SS2D merge, one plane per workgroup: y = (((r0 + r1) + r2) + r3) [+ Dsum * x] [* silu(z)],
+// summed in fp32.  Routes are of type R (fp32, or the I/O type T), grid tensors of type T.
+template <typename T, typename R>
 __global__ __launch_bounds__(kPlaneThreads) void merge_plane_kernel(MergeArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int H = int(a.H), Wd = int(a.W);
@@ -231,14 +232,14 @@ __global__ __launch_bounds__(kPlaneThreads) void merge_plane_kernel(MergeArgs a)
   float* t3 = t1 + int64_t(Wd) * ld;
   const int64_t plane = int64_t(blockIdx.x);  // b * C + c
   const int64_t b = plane / a.C, c = plane % a.C;
-  const float* r0 = static_cast<const float*>(a.routes) + (b * 4 * a.C + c) * L;
-  const float* r1 = r0 + a.C * L;
-  const float* r2 = r1 + a.C * L;
-  const float* r3 = r2 + a.C * L;
+  const R* r0 = static_cast<const R*>(a.routes) + (b * 4 * a.C + c) * L;
+  const R* r1 = r0 + a.C * L;
+  const R* r2 = r1 + a.C * L;
+  const R* r3 = r2 + a.C * L;
   // routes 1 and 3 are in column-major order: t1[w][h] = r1[w*H + h], t3[w][h] = r3[L-1-(w*H + h)]
   for (int64_t t = 4 * int64_t(threadIdx.x); t < L; t += 4 * kPlaneThreads) {
-    const float4 v1 = *reinterpret_cast<const float4*>(r1 + t);
-    const float4 v3 = *reinterpret_cast<const float4*>(r3 + (L - 4 - t));  // route-3 steps L-4-t .. L-1-t
+    const float4 v1 = Elem<R>::load4(r1, t);
+    const float4 v3 = Elem<R>::load4(r3, L - 4 - t);  // route-3 steps L-4-t .. L-1-t
     const float a1[4] = {v1.x, v1.y, v1.z, v1.w};
     const float a3[4] = {v3.w, v3.z, v3.y, v3.x};  // pixel order t .. t+3
 #pragma unroll
@@ -257,8 +258,8 @@ __global__ __launch_bounds__(kPlaneThreads) void merge_plane_kernel(MergeArgs a)
   T* yg = a.y ? static_cast<T*>(a.y) + plane * L : nullptr;
   float* mg = a.merged_f32 ? a.merged_f32 + plane * L : nullptr;
   for (int64_t p = 4 * int64_t(threadIdx.x); p < L; p += 4 * kPlaneThreads) {
-    const float4 v0 = *reinterpret_cast<const float4*>(r0 + p);
-    const float4 v2 = *reinterpret_cast<const float4*>(r2 + (L - 4 - p));
+    const float4 v0 = Elem<R>::load4(r0, p);
+    const float4 v2 = Elem<R>::load4(r2, L - 4 - p);
     const float a0[4] = {v0.x, v0.y, v0.z, v0.w};
     const float a2[4] = {v2.w, v2.z, v2.y, v2.x};
     float v[4];
@@ -317,17 +318,20 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   const int64_t L = a.H * a.W;
   const size_t plane_lds = size_t(2) * size_t(a.W) * size_t(a.H + 1) * 4;
-  if (a.routes_f32 && plane_lds <= 64 * 1024 && a.batch * a.C > 0 &&
-      aligned16(a.routes) && (!a.merged_f32 || aligned16(a.merged_f32)) &&
+  const uintptr_t route_align = a.routes_f32 ? 15 : (a.dtype == 0 ? 15 : 7);
+  if (plane_lds <= 64 * 1024 && a.batch * a.C > 0 &&
+      (reinterpret_cast<uintptr_t>(a.routes) & route_align) == 0 && (!a.merged_f32 || aligned16(a.merged_f32)) &&
       (a.dtype == 0 ? (aligned16(a.y) && aligned16(a.x) && aligned16(a.z))
                     : ((reinterpret_cast<uintptr_t>(a.y) | reinterpret_cast<uintptr_t>(a.x) |
                         reinterpret_cast<uintptr_t>(a.z)) & 7) == 0) &&
       L % 4 == 0) {
     const dim3 g{uint32_t(a.batch * a.C)}, b{kPlaneThreads};
     if (a.dtype == 0)
-      merge_plane_kernel<float><<<g, b, plane_lds, s>>>(a);
+      merge_plane_kernel<float, float><<<g, b, plane_lds, s>>>(a);
+    else if (a.routes_f32)
+      merge_plane_kernel<bf16, float><<<g, b, plane_lds, s>>>(a);
     else
-      merge_plane_kernel<bf16><<<g, b, plane_lds, s>>>(a);
+      merge_plane_kernel<bf16, bf16><<<g, b, plane_lds, s>>>(a);
     return hipGetLastError();
   }
   const int th = int(cdiv(a.H, kT)), tw = int(cdiv(a.W, kT));

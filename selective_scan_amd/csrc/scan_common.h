@@ -18,6 +18,8 @@ struct RowTile<float, kLen> {
     const float4 q = v[i / 4];
     return (i % 4 == 0) ? q.x : (i % 4 == 1) ? q.y : (i % 4 == 2) ? q.z : q.w;
   }
+  // element i + sel of an even i, sel in {0, 1} chosen per lane
+  __device__ __forceinline__ float get_pair(int i, int sel) const { return sel ? get(i + 1) : get(i); }
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int j = 0; j < (kLen + 3) / 4; ++j) v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -45,6 +47,13 @@ struct RowTile<bf16, kLen> {
     const uint2 q = v[i / 4];
     const uint32_t w = ((i % 4) < 2) ? q.x : q.y;
     return (i % 2 == 0) ? bf16lo(w) : bf16hi(w);
+  }
+  // element i + sel of an even i, sel in {0, 1} chosen per lane: both halves of one dword, the
+  // wanted one moved to the top by a per-lane shift
+  __device__ __forceinline__ float get_pair(int i, int sel) const {
+    const uint2 q = v[i / 4];
+    const uint32_t w = ((i % 4) < 2) ? q.x : q.y;
+    return __uint_as_float((w << (sel ? 0 : 16)) & 0xffff0000u);
   }
   __device__ __forceinline__ void zero() {
 #pragma unroll

@@ -152,18 +152,31 @@ void scan_fwd_kernel(const ScanFwdParams p) {
 #pragma unroll
     for (int g4 = 0; g4 < kTile / 4; ++g4) {
       float lam[4], du[4], y[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = 4 * g4 + k;
-        const float w = fmaf(cd.get(i), kLog2e, bias_l2);
+      // Lam of a step.  Steps past the end of the range get Lam = 0: decay exp2(0) = 1 and zero
+      // input (B/C are zero-filled there), so the state passes through unchanged without a branch.
+      auto step_lam = [&](float d, int i) {
+        const float w = fmaf(d, kLog2e, bias_l2);
         float l = softplus_log2(w);
         l = softplus ? l : w;  // branch-free: keeps the steps in one straight-line block
-        // Steps past the end of the range get Lam = 0: decay exp2(0) = 1 and zero input (B/C
-        // are zero-filled there), so the state passes through unchanged without a branch.
-        l = (i < nt) ? l : 0.0f;
-        lam[k] = l;
-        du[k] = l * cu.get(i);
+        return (i < nt) ? l : 0.0f;
+      };
+      if (kSplit == 2) {
+        // The two lanes of a channel share the softplus work: lane part p evaluates the steps of
+        // parity p, and each result is broadcast to both lanes of the pair by DPP
+        // (quad_perm [0,0,2,2] from the even lane, [1,1,3,3] from the odd one).
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int i = 4 * g4 + 2 * j;
+          const float x = step_lam(cd.get_pair(i, part), i + part);
+          lam[2 * j] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xA0, 0xF, 0xF, false));
+          lam[2 * j + 1] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xF5, 0xF, 0xF, false));
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) lam[k] = step_lam(cd.get(4 * g4 + k), 4 * g4 + k);
       }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) du[k] = lam[k] * cu.get(4 * g4 + k);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int i = 4 * g4 + k;
@@ -207,7 +220,8 @@ void scan_fwd_kernel(const ScanFwdParams p) {
           }
           store_seg<T, kVec, 4>(static_cast<T*>(p.out) + row * L, y, tg, t_end);
         } else {
-          store_seg<float, kVec, 4>(static_cast<float*>(p.out) + row * L, y, tg, t_end);
+          // route outputs in the I/O type, as a selective scan returns them; the merge sums them in fp32
+          store_seg<T, kVec, 4>(static_cast<T*>(p.out) + row * L, y, tg, t_end);
         }
       }
     }

@@ -107,7 +107,7 @@ SS2DLayout ss2d_layout(int64_t batch, int64_t dim, int64_t H, int64_t W, int64_t
   const int64_t L = H * W;
   int64_t o = 0;
   l.off_xT = o;     o += align_up(batch * dim * L * esize(dtype));
-  l.off_ys = o;     o += align_up(batch * 4 * dim * L * 4);
+  l.off_ys = o;     o += align_up(batch * 4 * dim * L * 4);  // route outputs (I/O type); fp32 du in the backward
   l.scan = scan_layout(batch, 4 * dim, dstate, L, 4, dtype);
   l.off_scan = o;   o += l.scan.total;
   l.off_merged = o; o += align_up(batch * dim * L * 4);
@@ -274,7 +274,7 @@ static int ss2d_transpose_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, h
                                       esize(a->dtype), stream));
 }
 
-// The four route scans with fp32 outputs (route order) into the ys region; when keep_states,
+// The four route scans, outputs in the I/O type (route order) into the ys region; when keep_states,
 // the state before every ckpt_every-th step of every row is kept for the backward.
 static int ss2d_scan_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, bool keep_states, hipStream_t stream) {
   const int64_t L = a->height * a->width;
@@ -320,7 +320,7 @@ static int ss2d_scan_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, bool k
 static int ss2d_merge_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, float* merged, hipStream_t stream) {
   MergeArgs m{};
   m.routes = at(a->workspace, lay.off_ys);
-  m.routes_f32 = 1;
+  m.routes_f32 = a->dtype == SS2D_DTYPE_F32;  // the scan stage writes route outputs in the I/O type
   m.x = a->x;
   m.Dskip = a->Dskip;
   m.z = a->z;

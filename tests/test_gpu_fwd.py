@@ -50,6 +50,27 @@ def test_cross_merge_bit_exact(dtype, shape):
     np.testing.assert_array_equal(to_f64(y2), 4.0 * x)
 
 
+def test_cross_merge_bf16_rounding_ties():
+    """The merge's single rounding to bf16 is round-to-nearest-even, checked bit for bit on sums
+    that are exact ties (m + half an ulp of m) and on sums just off a tie."""
+    B, C, H, W = 2, 3, 8, 16
+    rng = np.random.default_rng(11)
+    shape = (B, C, H, W)
+    e = rng.integers(-20, 20, size=shape)
+    mant = rng.integers(128, 256, size=shape)                     # 8 significant bits: exact in bf16
+    sign = np.where(rng.random(shape) < 0.5, -1.0, 1.0)
+    m = (sign * mant * np.exp2(e - 7.0)).astype(np.float32)       # |m| in [2^e, 2^(e+1))
+    half_ulp = (sign * np.exp2(e - 8.0)).astype(np.float32)       # a tie when added to m
+    nudge = (np.where(rng.random(shape) < 0.5, 0.0, 1.0) * np.where(rng.random(shape) < 0.5, -1.0, 1.0)
+             * np.exp2(e - 16.0)).astype(np.float32)               # zero (tie) or just off the tie
+    maps = [m, half_ulp, nudge, np.zeros(shape, np.float32)]
+    ys = np.stack([oracle.cross_scan(mk)[:, k] for k, mk in enumerate(maps)], axis=1)
+    y = ss.ss2d_cross_merge(to_dev(synth.f32_to_bf16_bits(ys), "bf16"), H, W)
+    s32 = ((m + half_ulp) + nudge) + np.float32(0.0)               # exact in fp32
+    got = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, synth.f32_to_bf16_bits(s32))
+
+
 def _scan_case(batch, dim, N, L, G, dtype, has_z, has_D, has_bias, softplus, seed):
     inp = synth.make_ss_inputs(batch, dim, N, L, G, dtype, has_z=has_z, seed_base=seed)
     if not softplus:  # the raw delta is the step itself: keep it positive (|delta|, sign bit cleared)
