@@ -20,9 +20,11 @@ struct RowTile<float, kLen> {
   }
   // element i + sel of an even i, sel in {0, 1} chosen per lane
   __device__ __forceinline__ float get_pair(int i, int sel) const { return sel ? get(i + 1) : get(i); }
-  __device__ __forceinline__ void zero() {
+  // every element set to the value with bit pattern `bits`
+  __device__ __forceinline__ void fill(uint32_t bits) {
+    const float f = __uint_as_float(bits);
 #pragma unroll
-    for (int j = 0; j < (kLen + 3) / 4; ++j) v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < (kLen + 3) / 4; ++j) v[j] = make_float4(f, f, f, f);
   }
   __device__ __forceinline__ void load_vec(const float* p, int j) { v[j] = *reinterpret_cast<const float4*>(p); }
   __device__ __forceinline__ void set(int i, float x) {
@@ -55,9 +57,11 @@ struct RowTile<bf16, kLen> {
     const uint32_t w = ((i % 4) < 2) ? q.x : q.y;
     return __uint_as_float((w << (sel ? 0 : 16)) & 0xffff0000u);
   }
-  __device__ __forceinline__ void zero() {
+  // every element set to the bf16 value with bit pattern `bits` (low 16 bits)
+  __device__ __forceinline__ void fill(uint32_t bits) {
+    const uint32_t w = (bits & 0xffffu) * 0x10001u;
 #pragma unroll
-    for (int j = 0; j < (kLen + 3) / 4; ++j) v[j] = make_uint2(0u, 0u);
+    for (int j = 0; j < (kLen + 3) / 4; ++j) v[j] = make_uint2(w, w);
   }
   __device__ __forceinline__ void load_vec(const bf16* p, int j) { v[j] = *reinterpret_cast<const uint2*>(p); }
   __device__ __forceinline__ void set(int i, uint16_t bits) {
@@ -87,11 +91,12 @@ __device__ __forceinline__ void set_elem(RowTile<T, kLen>& t, int i, const T* p)
 
 // Load steps [t0, t0 + kLen) of a row.  Forward rows read elements t0.., reversed rows read
 // pixels L-1-t for the same steps (then the tile is flipped so that index i is step t0 + i).
-// Steps at or past t_end read as zero.  Vector loads need L % 4 == 0, t0 % 4 == 0 and
-// kLen % 4 == 0 (shorter pieces are read element by element).
+// Steps at or past t_end read as the value with bit pattern pad_bits (zero by default).  Vector
+// loads need L % 4 == 0, t0 % 4 == 0 and kLen % 4 == 0 (shorter pieces are read element by
+// element).
 template <typename T, bool kVecArg, int kLen = kTile>
 __device__ __forceinline__ void load_row(RowTile<T, kLen>& tile, const T* row, int64_t t0, int64_t t_end, int64_t L,
-                                         bool rev) {
+                                         bool rev, uint32_t pad_bits = 0) {
   constexpr bool kVec = kVecArg && kLen % 4 == 0;
   if (kVec && t0 + kLen <= t_end) {
     // whole tile in range: unconditional vector loads, nothing to zero
@@ -101,7 +106,7 @@ __device__ __forceinline__ void load_row(RowTile<T, kLen>& tile, const T* row, i
     if (rev) tile.reverse();
     return;
   }
-  tile.zero();
+  tile.fill(pad_bits);
   if (kVec) {
     if (!rev) {
 #pragma unroll

@@ -21,6 +21,8 @@
 // sum(Lam); a combine kernel chains the chunks (h_start(c+1) = exp2(A sum Lam_c) h_start(c)
 // + h_end_local(c)); pass 0 reruns every chunk from its true start state and writes outputs.
 #pragma once
+#include <type_traits>
+
 #include "scan_common.h"
 
 namespace ss2d {
@@ -30,7 +32,8 @@ using namespace scan_detail;
 // kPass: 0 = outputs from the chunk-start state, 1 = chunk-local end state (chunked only),
 //        2 = as 0 and also the state before every kSub-th step (checkpoints for the backward).
 // kSplit: lanes per channel (1 or 2); NSL = NS / kSplit states per lane.
-template <typename T, int NS, int kSplit, bool kSS2D, bool kVec, int kPassArg>
+// kSoftplus: delta passes through softplus (else it is used as given).
+template <typename T, int NS, int kSplit, bool kSS2D, bool kVec, int kPassArg, bool kSoftplus>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu((kSS2D && kVec && sizeof(T) == 2) ? fwd_waves_per_simd(NS, true) : 1)))
 void scan_fwd_kernel(const ScanFwdParams p) {
   constexpr int kPass = kPassArg == 2 ? 0 : kPassArg;
@@ -83,7 +86,6 @@ void scan_fwd_kernel(const ScanFwdParams p) {
   const float bias_l2 = bias * kLog2e;
   const float Dd = (!kSS2D && p.Dskip) ? p.Dskip[d] : 0.0f;
 
-  const bool softplus = p.softplus != 0;
   const int64_t t_begin = int64_t(c) * p.chunk_len;
   const int64_t t_end = (t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L;
 
@@ -98,27 +100,33 @@ void scan_fwd_kernel(const ScanFwdParams p) {
   }
   float lam_sum = 0.0f;
 
-  RowTile<T> nd, nu, nz;
+  // Steps past the end of the range must leave the state unchanged: Lam = 0 (decay exp2(0) = 1,
+  // zero input; B/C are zero-filled there).  With softplus, delta is padded with -inf there, whose
+  // softplus is exactly 0; without it Lam is masked per step.
+  const uint32_t dpad = kSoftplus ? (sizeof(T) == 2 ? 0xFF80u : 0xFF800000u) : 0u;
+  // Row tiles in two register sets: tile k computes from set k % 2 while tile k + 1 is loaded
+  // into the other (the loop body is instantiated once per set, so no copies between them).
+  RowTile<T> rd[2], ru[2], rz[2];
   BCStage<T, NS, kVec> nbc;
-  if (t_begin < t_end) {
-    load_row<T, kVec>(nd, delta_row, t_begin, t_end, L, false);
-    load_row<T, kVec>(nu, u_row, t_begin, t_end, L, rev);
-    if (has_z) load_row<T, kVec>(nz, z_row, t_begin, t_end, L, false);
-    nbc.load(Bg, Cg, N, L, t_begin, t_end, lane);
-  }
+  auto prefetch = [&](auto set, int64_t t) {
+    constexpr int k = decltype(set)::value;
+    load_row<T, kVec>(rd[k], delta_row, t, t_end, L, false, dpad);
+    load_row<T, kVec>(ru[k], u_row, t, t_end, L, rev);
+    if (has_z) load_row<T, kVec>(rz[k], z_row, t, t_end, L, false);
+    nbc.load(Bg, Cg, N, L, t, t_end, lane);
+  };
+  if (t_begin < t_end) prefetch(std::integral_constant<int, 0>{}, t_begin);
 
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTile) {
-    const RowTile<T> cd = nd, cu = nu, cz = nz;
+  auto tile = [&](auto set, int64_t t0) {
+    constexpr int k_set = decltype(set)::value;
+    const RowTile<T>& cd = rd[k_set];
+    const RowTile<T>& cu = ru[k_set];
+    const RowTile<T>& cz = rz[k_set];
     __syncthreads();  // the previous tile's LDS reads are complete
     nbc.template store<S>(sB, sC, lane);
     __syncthreads();
     const int64_t t1 = t0 + kTile;
-    if (t1 < t_end) {
-      load_row<T, kVec>(nd, delta_row, t1, t_end, L, false);
-      load_row<T, kVec>(nu, u_row, t1, t_end, L, rev);
-      if (has_z) load_row<T, kVec>(nz, z_row, t1, t_end, L, false);
-      nbc.load(Bg, Cg, N, L, t1, t_end, lane);
-    }
+    if (t1 < t_end) prefetch(std::integral_constant<int, 1 - k_set>{}, t1);
 
     const int nt = int((t_end - t0 < kTile) ? (t_end - t0) : kTile);
     // One step's B (times ln 2) and C from LDS into one of two register buffers: the reads for
@@ -152,13 +160,11 @@ void scan_fwd_kernel(const ScanFwdParams p) {
 #pragma unroll
     for (int g4 = 0; g4 < kTile / 4; ++g4) {
       float lam[4], du[4], y[4];
-      // Lam of a step.  Steps past the end of the range get Lam = 0: decay exp2(0) = 1 and zero
-      // input (B/C are zero-filled there), so the state passes through unchanged without a branch.
+      // Lam of step i (0 past the end of the range)
       auto step_lam = [&](float d, int i) {
         const float w = fmaf(d, kLog2e, bias_l2);
-        float l = softplus_log2(w);
-        l = softplus ? l : w;  // branch-free: keeps the steps in one straight-line block
-        return (i < nt) ? l : 0.0f;
+        if (kSoftplus) return softplus_log2(w);
+        return (i < nt) ? w : 0.0f;
       };
       if (kSplit == 2) {
         // The two lanes of a channel share the softplus work: lane part p evaluates the steps of
@@ -225,6 +231,14 @@ void scan_fwd_kernel(const ScanFwdParams p) {
         }
       }
     }
+    // the state is complete here: keeps the next tile's arithmetic from being interleaved with
+    // this one's (which would hold both tiles' temporaries at once)
+#pragma unroll
+    for (int n = 0; n < NSL; ++n) asm volatile("" : "+v"(h[n]));
+  };
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * kTile) {
+    tile(std::integral_constant<int, 0>{}, t0);
+    if (t0 + kTile < t_end) tile(std::integral_constant<int, 1>{}, t0 + kTile);
   }
 
   if (!active) return;
@@ -242,12 +256,22 @@ hipError_t launch_t(ScanFwdParams p, hipStream_t s) {
   const int64_t blocks = p.batch * p.G * p.dblocks * p.n_chunks;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (p.pass == 1)
-    scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 1><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
-  else if (p.store_states)
-    scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 2><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
-  else
-    scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 0><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
+  const dim3 grid{uint32_t(blocks)}, block{kWave};
+  if (p.softplus) {
+    if (p.pass == 1)
+      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 1, true><<<grid, block, 0, s>>>(p);
+    else if (p.store_states)
+      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 2, true><<<grid, block, 0, s>>>(p);
+    else
+      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 0, true><<<grid, block, 0, s>>>(p);
+  } else {
+    if (p.pass == 1)
+      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 1, false><<<grid, block, 0, s>>>(p);
+    else if (p.store_states)
+      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 2, false><<<grid, block, 0, s>>>(p);
+    else
+      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 0, false><<<grid, block, 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 
