@@ -10,6 +10,7 @@ Functions (see ``oracle/ss2d_oracle.py`` for the citations):
   cross_scan, cross_merge        exact index permutations (numpy)
   ss_fwd, ss_bwd                 the selective scan and its exact gradient (C, fp64)
   ss2d_fwd, ss2d_bwd             cross-scan -> selective scan -> cross-merge (+ gate)
+  vim_bidir_fwd, vim_bidir_bwd   Vision Mamba's two-direction scan (oracle/vim_oracle.py)
 
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against
 closed forms, invariants, a brute-force semiseparable-matrix formulation and
@@ -26,3 +27,4 @@ from .ss2d_oracle import (  # noqa: F401
     ss_bwd,
     ss_fwd,
 )
+from .vim_oracle import vim_bidir_bwd, vim_bidir_fwd  # noqa: F401

@@ -56,6 +56,33 @@ CONFIGS = [
 ]
 
 
+@dataclass(frozen=True)
+class VimConfig:
+    """A bidirectional (Vision Mamba) workload: two scan directions over one token sequence."""
+    name: str
+    batch: int
+    seqlen: int
+    dim: int
+    dstate: int
+    dtype: str
+    has_z: bool
+    index: int
+    with_bwd: bool = False
+    kind: str = "vim"
+
+    @property
+    def elements(self) -> int:
+        """B*K*D*L with K = 2 directions."""
+        return self.batch * 2 * self.dim * self.seqlen
+
+
+# Vim-Tiny at 224^2: 14 x 14 patches of 16^2 plus the class token (L = 197), embedding 192,
+# expand 2 (D = 384), d_state 16, batch 128.
+VIM_CONFIGS = [
+    VimConfig("vim_tiny_l197_b128_d384_n16_bf16", 128, 197, 384, 16, "bf16", True, 5, True),
+]
+
+
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round fp32 values to bf16 (round to nearest, ties to even); returns uint16 bit patterns."""
     bits = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
@@ -133,3 +160,34 @@ def make_ss_inputs(batch: int, dim: int, dstate: int, seqlen: int, ngroups: int,
     out["dout"] = _normal(s + T_DOUT, (batch, dim, seqlen), dtype) if with_dout else None
     out["meta"] = dict(batch=batch, dim=dim, dstate=dstate, seqlen=seqlen, ngroups=ngroups, dtype=dtype)
     return out
+
+
+def make_vim_inputs(batch: int, seqlen: int, dim: int, dstate: int, dtype: str, has_z: bool = True,
+                    seed_base: int = 0, with_dout: bool = False) -> dict:
+    """Inputs of one bidirectional scan call.  Shapes (dense, last index fastest):
+       u, delta:  (batch, 2, dim, L)      direction k in its own scan order
+       B, C:      (batch, 2, dstate, L)   direction k in its own scan order
+       z, dout:   (batch, dim, L)         forward order
+       A:         (2, dim, dstate) fp32;  D, delta_bias: (2, dim) fp32
+    Draws as for SS2D (u takes the x slot of the seed table)."""
+    s = 1000 * seed_base
+    out = {
+        "u": _normal(s + T_X, (batch, 2, dim, seqlen), dtype),
+        "z": _normal(s + T_Z, (batch, dim, seqlen), dtype) if has_z else None,
+        "delta": _normal(s + T_DELTA, (batch, 2, dim, seqlen), dtype),
+        "B": _normal(s + T_B, (batch, 2, dstate, seqlen), dtype),
+        "C": _normal(s + T_C, (batch, 2, dstate, seqlen), dtype),
+    }
+    rng = np.random.Generator(np.random.PCG64(s + T_U))
+    dt = rng.uniform(1e-3, 1e-1, size=(2, dim))
+    out["delta_bias"] = np.log(np.expm1(dt)).astype(np.float32)
+    out["A"] = np.broadcast_to(-(np.arange(dstate, dtype=np.float32) + 1.0), (2, dim, dstate)).copy()
+    out["D"] = np.ones((2, dim), dtype=np.float32)
+    out["dout"] = _normal(s + T_DOUT, (batch, dim, seqlen), dtype) if with_dout else None
+    out["meta"] = dict(batch=batch, seqlen=seqlen, dim=dim, dstate=dstate, dtype=dtype)
+    return out
+
+
+def make_vim_config_inputs(cfg: VimConfig, with_dout: bool | None = None) -> dict:
+    return make_vim_inputs(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, cfg.dtype, cfg.has_z, cfg.index,
+                           cfg.with_bwd if with_dout is None else with_dout)
