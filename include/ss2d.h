@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SS2D_ABI_VERSION 1
+#define SS2D_ABI_VERSION 2
 
 /* Status codes returned by every entry point. */
 enum {
@@ -165,8 +165,9 @@ int selective_scan_bwd(const ss_bwd_args* args, hipStream_t stream);
  * Fused SS2D forward [VMamba, SS2D section]: equivalent, up to fp32 rounding order, to
  *   cross_merge(selective_scan_fwd(cross_scan(x), delta, A, B, C, D, delta_bias,
  *               softplus, ngroups = 4))  then  * silu(z)  per pixel (z optional)
- * As in that composition, each route's output y_k is rounded to dtype before the four are
- * summed in fp32; the gate is applied to the fp32 sum, which is rounded once to dtype.
+ * The route outputs stay fp32 until they are summed; the gated sum is rounded once to dtype
+ * (the composition would also round each route's output to dtype: where routes cancel, that
+ * intermediate rounding alone can exceed one rounding of the result).
  * Layouts:  x, z, out  : (batch, dim, height, width)      dtype   (grid)
  *           delta      : (batch, 4, dim, L)               dtype   (route k in its own order)
  *           Bm, Cm     : (batch, 4, dstate, L)            dtype   (shared by the dim channels
@@ -242,6 +243,86 @@ typedef struct ss2d_bwd_args {
 } ss2d_bwd_args;
 
 int ss2d_bwd(const ss2d_bwd_args* args, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * Bidirectional scan of Vision Mamba [S6 page, section 2: `bimamba_inner_ref` and the
+ * `Mamba` module with bimamba_type "v2"; the Vim article]: two selective scans over one
+ * sequence, direction 0 in order and direction 1 over the reversed sequence, each with its own
+ * parameters, the second output flipped back and added:
+ *   y_k = selective_scan_fwd(u_k, delta_k, A_k, B_k, C_k, D_k, delta_bias_k)    (k = 0, 1)
+ *   out[b, d, l] = (y_0[b, d, l] + y_1[b, d, L-1-l]) * silu(z[b, d, l])         (z optional)
+ * The y_k stay fp32 until they are added; the gated sum is rounded once to dtype.  Gating the
+ * sum equals gating each direction with z in its own order (the page's form): silu(z) is the
+ * same factor for both terms.  The page's
+ * first variant (shared u, delta, B, C, D, delta_bias; separate A) is the case where direction
+ * 1's inputs are the flipped copies of direction 0's.
+ * Layouts:  u, delta   : (batch, 2, dim, L)    dtype  (direction k in its own scan order)
+ *           Bm, Cm     : (batch, 2, dstate, L) dtype  (direction k in its own scan order)
+ *           A          : (2, dim, dstate) fp32;  Dskip, delta_bias : (2, dim) fp32 (may be NULL)
+ *           z, out     : (batch, dim, L)       dtype  (forward order)
+ * The workspace is required (>= vim_bidir_workspace_bytes(...)); sizes as for ss2d_fwd.
+ * ------------------------------------------------------------------------------- */
+size_t vim_bidir_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int dtype);
+
+typedef struct vim_bidir_fwd_args {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;      /* may be NULL */
+  const float* delta_bias; /* may be NULL */
+  const void* z;           /* may be NULL */
+  void* out;
+  void* workspace;
+  size_t workspace_bytes;
+  int64_t batch, dim, seqlen, dstate;
+  int dtype;
+  int delta_softplus;
+} vim_bidir_fwd_args;
+
+int vim_bidir_fwd(const vim_bidir_fwd_args* args, hipStream_t stream);
+
+/* One stage of vim_bidir_fwd (the same stage codes as ss2d_fwd_stage; there is no transpose):
+ *   SS2D_STAGE_SCAN:  the two direction scans, outputs (dtype, each direction's order) into
+ *                     the workspace;
+ *   SS2D_STAGE_MERGE: flip, add and gate into `out`.
+ * SS2D_STAGE_TRANSPOSE does nothing; any other value is SS2D_ERR_INVALID_ARGUMENT. */
+int vim_bidir_fwd_stage(const vim_bidir_fwd_args* args, int stage, hipStream_t stream);
+
+/* Backward of vim_bidir_fwd: given dout (batch, dim, L), writes
+ *   du, ddelta : (batch, 2, dim, L) dtype (ddelta w.r.t. the raw delta);
+ *   dBm, dCm   : (batch, 2, dstate, L) dtype;
+ *   dA         : (2, dim, dstate) fp32;  dDskip, ddelta_bias : (2, dim) fp32 (iff given);
+ *   dz         : (batch, dim, L) dtype (iff z).
+ * Everything is overwritten.  The forward is recomputed inside; the gradient reaching each
+ * direction, dout * silu(z), is kept in fp32. */
+typedef struct vim_bidir_bwd_args {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;
+  const float* delta_bias;
+  const void* z;
+  const void* dout;
+  void* du;
+  void* ddelta;
+  float* dA;
+  void* dBm;
+  void* dCm;
+  float* dDskip;
+  float* ddelta_bias;
+  void* dz;
+  void* workspace;
+  size_t workspace_bytes;
+  int64_t batch, dim, seqlen, dstate;
+  int dtype;
+  int delta_softplus;
+} vim_bidir_bwd_args;
+
+int vim_bidir_bwd(const vim_bidir_bwd_args* args, hipStream_t stream);
 
 #ifdef __cplusplus
 }

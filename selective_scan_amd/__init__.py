@@ -1,4 +1,5 @@
-"""SS2D on AMD Instinct MI355X: cross-scan -> selective scan (S6) -> cross-merge.
+"""SS2D on AMD Instinct MI355X: cross-scan -> selective scan (S6) -> cross-merge, and the
+two-direction scan of Vision Mamba.
 
 The computation runs in hand-written HIP kernels for gfx950 behind the C ABI in
 include/ss2d.h (libss2d.so, built in-tree by __graft_entry__.build()).  This package
@@ -16,4 +17,8 @@ from ._binding import (  # noqa: F401
     ss2d_cross_scan,
     ss2d_fwd,
     ss2d_workspace_bytes,
+    VimForwardPlan,
+    vim_bidir_bwd,
+    vim_bidir_fwd,
+    vim_bidir_workspace_bytes,
 )

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libss2d.so")
 
 SS2D_OK, SS2D_ERR_INVALID_ARGUMENT, SS2D_ERR_UNSUPPORTED, SS2D_ERR_HIP = 0, 1, 2, 3
 DTYPE_F32, DTYPE_BF16 = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -53,6 +53,20 @@ class SS2DBwdArgs(ctypes.Structure):
         ("dstate", _i64), ("dtype", _int), ("delta_softplus", _int)]
 
 
+class VimFwdArgs(ctypes.Structure):
+    _fields_ = [(n, _p) for n in ("u", "delta", "A", "Bm", "Cm", "Dskip", "delta_bias", "z", "out",
+                                  "workspace")] + [
+        ("workspace_bytes", _sz), ("batch", _i64), ("dim", _i64), ("seqlen", _i64), ("dstate", _i64),
+        ("dtype", _int), ("delta_softplus", _int)]
+
+
+class VimBwdArgs(ctypes.Structure):
+    _fields_ = [(n, _p) for n in ("u", "delta", "A", "Bm", "Cm", "Dskip", "delta_bias", "z", "dout", "du",
+                                  "ddelta", "dA", "dBm", "dCm", "dDskip", "ddelta_bias", "dz", "workspace")] + [
+        ("workspace_bytes", _sz), ("batch", _i64), ("dim", _i64), ("seqlen", _i64), ("dstate", _i64),
+        ("dtype", _int), ("delta_softplus", _int)]
+
+
 _lib = None
 
 
@@ -77,8 +91,13 @@ def lib():
         L.ss2d_workspace_bytes.argtypes = [_i64] * 5 + [_int]
         L.ss2d_fwd_stage.restype = _int
         L.ss2d_fwd_stage.argtypes = [ctypes.POINTER(SS2DFwdArgs), _int, _p]
+        L.vim_bidir_workspace_bytes.restype = _sz
+        L.vim_bidir_workspace_bytes.argtypes = [_i64] * 4 + [_int]
+        L.vim_bidir_fwd_stage.restype = _int
+        L.vim_bidir_fwd_stage.argtypes = [ctypes.POINTER(VimFwdArgs), _int, _p]
         for name, st in (("selective_scan_fwd", SsFwdArgs), ("selective_scan_bwd", SsBwdArgs),
-                         ("ss2d_fwd", SS2DFwdArgs), ("ss2d_bwd", SS2DBwdArgs)):
+                         ("ss2d_fwd", SS2DFwdArgs), ("ss2d_bwd", SS2DBwdArgs),
+                         ("vim_bidir_fwd", VimFwdArgs), ("vim_bidir_bwd", VimBwdArgs)):
             f = getattr(L, name)
             f.restype = _int
             f.argtypes = [ctypes.POINTER(st), _p]
@@ -312,3 +331,78 @@ def ss2d_bwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, dout=None, delt
                     delta_softplus=int(bool(delta_softplus)))
     _check(lib().ss2d_bwd(ctypes.byref(a), _stream(dev)), "ss2d_bwd")
     return {"dx": dx, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "ddelta_bias": dbias, "dz": dz}
+
+
+def vim_bidir_workspace_bytes(batch, dim, seqlen, dstate, dtype: torch.dtype) -> int:
+    return int(lib().vim_bidir_workspace_bytes(batch, dim, seqlen, dstate, _dtype_code(dtype)))
+
+
+class VimForwardPlan:
+    """A prepared vim_bidir_fwd call (argument block, workspace and output kept alive).
+    u, delta: (batch, 2, dim, L); A: (2, dim, N); B, C: (batch, 2, N, L); D, delta_bias: (2, dim);
+    z: (batch, dim, L)."""
+
+    def __init__(self, u, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=True, workspace=None,
+                 out=None):
+        u, delta = _c(u), _c(delta)
+        self.device = _dev(u)
+        B, C, z = _c(B), _c(C), _c(z)
+        A = _c(A, torch.float32)
+        D = _c(D, torch.float32)
+        delta_bias = _c(delta_bias, torch.float32)
+        batch, K, dim, L = u.shape
+        if K != 2:
+            raise SS2DError("u must be (batch, 2, dim, L)")
+        N = A.shape[-1]
+        self.out = torch.empty((batch, dim, L), dtype=u.dtype, device=self.device) if out is None else out
+        self.workspace = _workspace(vim_bidir_workspace_bytes(batch, dim, L, N, u.dtype), self.device, workspace)
+        self._keep = (u, delta, A, B, C, D, delta_bias, z)
+        self.args = VimFwdArgs(u=_ptr(u), delta=_ptr(delta), A=_ptr(A), Bm=_ptr(B), Cm=_ptr(C), Dskip=_ptr(D),
+                               delta_bias=_ptr(delta_bias), z=_ptr(z), out=_ptr(self.out),
+                               workspace=_ptr(self.workspace),
+                               workspace_bytes=self.workspace.numel() * self.workspace.element_size(),
+                               batch=batch, dim=dim, seqlen=L, dstate=N, dtype=_dtype_code(u.dtype),
+                               delta_softplus=int(bool(delta_softplus)))
+
+    def run(self):
+        _check(lib().vim_bidir_fwd(ctypes.byref(self.args), _stream(self.device)), "vim_bidir_fwd")
+        return self.out
+
+    def run_stage(self, stage: int):
+        _check(lib().vim_bidir_fwd_stage(ctypes.byref(self.args), int(stage), _stream(self.device)),
+               "vim_bidir_fwd_stage")
+        return self.out
+
+
+def vim_bidir_fwd(u, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=True, workspace=None):
+    """Bidirectional (Vision Mamba) scan forward; returns out (batch, dim, L)."""
+    return VimForwardPlan(u, delta, A, B, C, D, delta_bias, z, delta_softplus, workspace).run()
+
+
+def vim_bidir_bwd(u, delta, A, B, C, D=None, delta_bias=None, z=None, dout=None, delta_softplus=True,
+                  workspace=None):
+    """Backward of vim_bidir_fwd; returns a dict of gradients (None for absent inputs)."""
+    u, delta, dout = _c(u), _c(delta), _c(dout)
+    dev = _dev(u)
+    B, C, z = _c(B), _c(C), _c(z)
+    A = _c(A, torch.float32)
+    D = _c(D, torch.float32)
+    delta_bias = _c(delta_bias, torch.float32)
+    batch, K, dim, L = u.shape
+    if K != 2:
+        raise SS2DError("u must be (batch, 2, dim, L)")
+    N = A.shape[-1]
+    du, ddelta = torch.empty_like(u), torch.empty_like(delta)
+    dA = torch.empty_like(A)
+    dB, dC = torch.empty_like(B), torch.empty_like(C)
+    dD = torch.empty_like(D) if D is not None else None
+    dbias = torch.empty_like(delta_bias) if delta_bias is not None else None
+    dz = torch.empty_like(z) if z is not None else None
+    ws = _workspace(vim_bidir_workspace_bytes(batch, dim, L, N, u.dtype), dev, workspace)
+    a = VimBwdArgs(u=_ptr(u), delta=_ptr(delta), A=_ptr(A), Bm=_ptr(B), Cm=_ptr(C), Dskip=_ptr(D),
+                   delta_bias=_ptr(delta_bias), z=_ptr(z), dout=_ptr(dout), du=_ptr(du), ddelta=_ptr(ddelta),
+                   dA=_ptr(dA), dBm=_ptr(dB), dCm=_ptr(dC), dDskip=_ptr(dD), ddelta_bias=_ptr(dbias), dz=_ptr(dz),
+                   workspace=_ptr(ws), workspace_bytes=ws.numel() * ws.element_size(), batch=batch, dim=dim,
+                   seqlen=L, dstate=N, dtype=_dtype_code(u.dtype), delta_softplus=int(bool(delta_softplus)))
+    _check(lib().vim_bidir_bwd(ctypes.byref(a), _stream(dev)), "vim_bidir_bwd")
+    return {"du": du, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "ddelta_bias": dbias, "dz": dz}

@@ -51,6 +51,24 @@ struct MergeArgs {
 };
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 
+// Two-direction (Vision Mamba) merge and its backward, per row r = (b, c) of length L:
+//   forward:  out[r, l] = (ys[b, 0, c, l] + ys[b, 1, c, L-1-l]) (* silu(z[r, l])), fp32, one rounding
+//   backward: M = that pre-gate sum; dM = dout * silu(z) (dout without z);
+//             dy[b, 0, c, l] = dM[r, l], dy[b, 1, c, L-1-l] = dM[r, l] (fp32, each direction's order);
+//             dz = dout * M * silu'(z)
+struct BidirArgs {
+  const float* ys;   // (batch, 2, C, L) fp32, each direction in its own order
+  const void* z;     // (batch, C, L) dtype, optional
+  void* out;         // forward output (batch, C, L) dtype
+  const void* dout;  // backward input (batch, C, L) dtype
+  float* dy;         // backward output (batch, 2, C, L) fp32
+  void* dz;          // backward output (batch, C, L) dtype, iff z
+  int64_t batch, C, L;
+  int dtype;
+};
+hipError_t launch_bidir_merge(const BidirArgs& a, hipStream_t s);
+hipError_t launch_bidir_gate_bwd(const BidirArgs& a, hipStream_t s);
+
 // Backward helpers of the SS2D gate: with the merged pre-gate map M (fp32),
 //   dM = dout * silu(z)            (fp32 grid, and its per-plane transpose dMT)
 //   dz = dout * M * silu'(z)       (dtype grid)
@@ -97,6 +115,7 @@ struct ScanFwdParams {
   int vec;             // 4-element vector access allowed
   int pass;            // 0: outputs/checkpoints from the stored chunk-start state; 1: chunk-local end state
   int store_states;    // pass 0 also keeps the state before every ckpt_every-th step in ckpt
+  int out_f32;         // generic rows: out is fp32 instead of the I/O type
 };
 hipError_t launch_scan_fwd(const ScanFwdParams& p, hipStream_t s);
 // Turns the chunk-local end states (pass 1) into the true chunk-start states.
@@ -113,7 +132,7 @@ struct ScanBwdParams {
   const float* Dskip;
   const void* z;           // generic only
   const float* delta_bias;
-  const void* dout;        // generic: dtype (batch, dim, L); ss2d: dM (fp32 grid) and dMT
+  const void* dout;        // generic: dtype (or fp32 if dout_f32) (batch, dim, L); ss2d: dM (fp32 grid) and dMT
   const void* doutT;
   void* du;                // generic: dtype; ss2d: fp32 route order (batch, 4D, L)
   void* ddelta;            // dtype (batch, dim, L)
@@ -133,6 +152,7 @@ struct ScanBwdParams {
   int dtype;
   int vec;
   int pass;                // 1: chunk-local lambda pass; 0: gradients
+  int dout_f32;            // generic rows: dout is fp32 instead of the I/O type
 };
 hipError_t launch_scan_bwd(const ScanBwdParams& p, hipStream_t s);
 hipError_t launch_lambda_combine(const ScanBwdParams& p, hipStream_t s);

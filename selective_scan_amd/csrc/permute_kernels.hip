@@ -286,6 +286,43 @@ __global__ __launch_bounds__(kPlaneThreads) void merge_plane_kernel(MergeArgs a)
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Two-direction merge: one thread per element of the (batch, C, L) output; direction 1 is read
+// at L-1-l, so consecutive threads read consecutive (descending) addresses of it.
+template <typename T>
+__global__ __launch_bounds__(256) void bidir_merge_kernel(BidirArgs a) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t n = a.batch * a.C * a.L;
+  if (i >= n) return;
+  const int64_t row = i / a.L, l = i % a.L;
+  const int64_t b = row / a.C, c = row % a.C;
+  const float* y0 = a.ys + (b * 2 * a.C + c) * a.L;
+  const float* y1 = y0 + a.C * a.L;
+  float v = y0[l] + y1[a.L - 1 - l];
+  if (a.z) v *= silu(Elem<T>::load(static_cast<const T*>(a.z), i));
+  Elem<T>::store(static_cast<T*>(a.out), i, v);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void bidir_gate_bwd_kernel(BidirArgs a) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t n = a.batch * a.C * a.L;
+  if (i >= n) return;
+  const int64_t row = i / a.L, l = i % a.L;
+  const int64_t b = row / a.C, c = row % a.C;
+  const int64_t r0 = (b * 2 * a.C + c) * a.L, r1 = r0 + a.C * a.L;
+  const float g = Elem<T>::load(static_cast<const T*>(a.dout), i);
+  float dm = g;
+  if (a.z) {
+    const float m = a.ys[r0 + l] + a.ys[r1 + a.L - 1 - l];
+    const float zv = Elem<T>::load(static_cast<const T*>(a.z), i);
+    const float sz = sigmoid(zv);
+    dm = g * zv * sz;
+    Elem<T>::store(static_cast<T*>(a.dz), i, g * m * sz * (1.0f + zv * (1.0f - sz)));
+  }
+  a.dy[r0 + l] = dm;
+  a.dy[r1 + a.L - 1 - l] = dm;
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.0f;
@@ -345,6 +382,28 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   } else {
     merge_kernel<bf16, bf16><<<g, b, 0, s>>>(a, th, tw);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_bidir_merge(const BidirArgs& a, hipStream_t s) {
+  const int64_t n = a.batch * a.C * a.L;
+  if (n == 0) return hipSuccess;
+  const dim3 g{uint32_t(cdiv(n, 256))}, b{256};
+  if (a.dtype == 0)
+    bidir_merge_kernel<float><<<g, b, 0, s>>>(a);
+  else
+    bidir_merge_kernel<bf16><<<g, b, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bidir_gate_bwd(const BidirArgs& a, hipStream_t s) {
+  const int64_t n = a.batch * a.C * a.L;
+  if (n == 0) return hipSuccess;
+  const dim3 g{uint32_t(cdiv(n, 256))}, b{256};
+  if (a.dtype == 0)
+    bidir_gate_bwd_kernel<float><<<g, b, 0, s>>>(a);
+  else
+    bidir_gate_bwd_kernel<bf16><<<g, b, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -177,9 +177,12 @@ __device__ __forceinline__ bool reduce_writer(int lane) {
 }
 
 // kSplit: lanes per channel (1 or 2); NSL = NS / kSplit states per lane.
-template <typename T, int NS, int kSplit, bool kSS2D, bool kVec, int kPass>
+// kMode: 0 = generic rows, dout in the I/O type; 1 = SS2D routes (u from the map and its
+// transpose, fp32 dout planes); 2 = generic rows with an fp32 dout.
+template <typename T, int NS, int kSplit, int kMode, bool kVec, int kPass>
 __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) {
-  using DT = typename std::conditional<kSS2D, float, T>::type;  // type of dout rows
+  constexpr bool kSS2D = kMode == 1;
+  using DT = typename std::conditional<kMode == 0, T, float>::type;  // type of dout rows
   constexpr int NSL = NS / kSplit;
   constexpr int kRows = kWave / kSplit;
   constexpr int S = (NS < 4) ? 4 : NS + 4;
@@ -477,16 +480,16 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
   }
 }
 
-template <typename T, int NS, int kSplit, bool kSS2D, bool kVec>
+template <typename T, int NS, int kSplit, int kMode, bool kVec>
 hipError_t launch_t(ScanBwdParams p, hipStream_t s) {
   p.dblocks = (p.per_group + kWave / kSplit - 1) / (kWave / kSplit);
   const int64_t blocks = p.batch * p.G * p.dblocks * p.n_chunks;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (p.pass == 1)
-    scan_bwd_kernel<T, NS, kSplit, kSS2D, kVec, 1><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
+    scan_bwd_kernel<T, NS, kSplit, kMode, kVec, 1><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
   else
-    scan_bwd_kernel<T, NS, kSplit, kSS2D, kVec, 0><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
+    scan_bwd_kernel<T, NS, kSplit, kMode, kVec, 0><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -497,8 +500,12 @@ template <typename T, int NS>
 hipError_t scan_bwd_launch(const ScanBwdParams& p, hipStream_t s) {
   using namespace bwd_detail;
   constexpr int kSplit = NS >= 16 ? 2 : 1;
-  if (p.ss2d) return p.vec ? launch_t<T, NS, kSplit, true, true>(p, s) : launch_t<T, NS, kSplit, true, false>(p, s);
-  return p.vec ? launch_t<T, NS, kSplit, false, true>(p, s) : launch_t<T, NS, kSplit, false, false>(p, s);
+  if (p.ss2d) return p.vec ? launch_t<T, NS, kSplit, 1, true>(p, s) : launch_t<T, NS, kSplit, 1, false>(p, s);
+  if constexpr (sizeof(T) != 4) {  // for fp32 I/O an fp32 dout is the ordinary case
+    if (p.dout_f32)
+      return p.vec ? launch_t<T, NS, kSplit, 2, true>(p, s) : launch_t<T, NS, kSplit, 2, false>(p, s);
+  }
+  return p.vec ? launch_t<T, NS, kSplit, 0, true>(p, s) : launch_t<T, NS, kSplit, 0, false>(p, s);
 }
 
 }  // namespace ss2d

@@ -224,10 +224,13 @@ void scan_fwd_kernel(const ScanFwdParams p) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) y[k] *= silu(cz.get(4 * g4 + k));
           }
-          store_seg<T, kVec, 4>(static_cast<T*>(p.out) + row * L, y, tg, t_end);
+          if (p.out_f32)
+            store_seg<float, kVec, 4>(static_cast<float*>(p.out) + row * L, y, tg, t_end);
+          else
+            store_seg<T, kVec, 4>(static_cast<T*>(p.out) + row * L, y, tg, t_end);
         } else {
-          // route outputs in the I/O type, as a selective scan returns them; the merge sums them in fp32
-          store_seg<T, kVec, 4>(static_cast<T*>(p.out) + row * L, y, tg, t_end);
+          // route outputs stay fp32 until the merge has added them: the result is rounded once
+          store_seg<float, kVec, 4>(static_cast<float*>(p.out) + row * L, y, tg, t_end);
         }
       }
     }

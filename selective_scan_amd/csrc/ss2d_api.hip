@@ -107,7 +107,7 @@ SS2DLayout ss2d_layout(int64_t batch, int64_t dim, int64_t H, int64_t W, int64_t
   const int64_t L = H * W;
   int64_t o = 0;
   l.off_xT = o;     o += align_up(batch * dim * L * esize(dtype));
-  l.off_ys = o;     o += align_up(batch * 4 * dim * L * 4);  // route outputs (I/O type); fp32 du in the backward
+  l.off_ys = o;     o += align_up(batch * 4 * dim * L * 4);  // fp32 route outputs; fp32 du in the backward
   l.scan = scan_layout(batch, 4 * dim, dstate, L, 4, dtype);
   l.off_scan = o;   o += l.scan.total;
   l.off_merged = o; o += align_up(batch * dim * L * 4);
@@ -197,7 +197,9 @@ size_t selective_scan_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate
   return size_t(scan_layout(batch, dim, dstate, seqlen, ngroups, SS2D_DTYPE_BF16).total);
 }
 
-int selective_scan_fwd(const ss_fwd_args* a, hipStream_t stream) {
+// The generic forward; with a workspace the sequence may be chunked, and with keep_states the
+// state before every ckpt_every-th step is kept there for the backward.
+static int scan_fwd_impl(const ss_fwd_args* a, bool keep_states, hipStream_t stream, bool out_f32 = false) {
   if (!a) return SS2D_ERR_INVALID_ARGUMENT;
   int st = check_scan_shapes(a->batch, a->dim, a->dstate, a->seqlen, a->ngroups, a->dtype);
   if (st != SS2D_OK) return st;
@@ -246,7 +248,8 @@ int selective_scan_fwd(const ss_fwd_args* a, hipStream_t stream) {
     p.chunk_len = cdiv(a->seqlen, kTile) * kTile;
     p.n_chunks = 1;
   }
-  p.store_states = a->workspace != nullptr;
+  p.store_states = keep_states && a->workspace != nullptr;
+  p.out_f32 = out_f32 ? 1 : 0;
   if (a->batch * a->ngroups * lay.dblocks * 2 * p.n_chunks > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
   if (a->workspace) {
     p.ckpt = reinterpret_cast<float*>(at(a->workspace, lay.off_ckpt));
@@ -263,6 +266,10 @@ int selective_scan_fwd(const ss_fwd_args* a, hipStream_t stream) {
   return status_from(e);
 }
 
+int selective_scan_fwd(const ss_fwd_args* a, hipStream_t stream) {
+  return scan_fwd_impl(a, a && a->workspace != nullptr, stream);
+}
+
 size_t ss2d_workspace_bytes(int64_t batch, int64_t dim, int64_t height, int64_t width, int64_t dstate, int dtype) {
   if (batch < 0 || dim < 0 || height < 0 || width < 0 || dstate < 1 || !dtype_ok(dtype)) return 0;
   return size_t(ss2d_layout(batch, dim, height, width, dstate, dtype).total);
@@ -274,7 +281,7 @@ static int ss2d_transpose_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, h
                                       esize(a->dtype), stream));
 }
 
-// The four route scans, outputs in the I/O type (route order) into the ys region; when keep_states,
+// The four route scans with fp32 outputs (route order) into the ys region; when keep_states,
 // the state before every ckpt_every-th step of every row is kept for the backward.
 static int ss2d_scan_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, bool keep_states, hipStream_t stream) {
   const int64_t L = a->height * a->width;
@@ -320,7 +327,7 @@ static int ss2d_scan_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, bool k
 static int ss2d_merge_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, float* merged, hipStream_t stream) {
   MergeArgs m{};
   m.routes = at(a->workspace, lay.off_ys);
-  m.routes_f32 = a->dtype == SS2D_DTYPE_F32;  // the scan stage writes route outputs in the I/O type
+  m.routes_f32 = 1;  // the scan stage writes fp32 route outputs
   m.x = a->x;
   m.Dskip = a->Dskip;
   m.z = a->z;
@@ -646,6 +653,193 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
   m.W = a->width;
   m.dtype = a->dtype;
   return status_from(launch_merge(m, stream));
+}
+
+// ---- Bidirectional (Vision Mamba) scan --------------------------------------------------
+// The two directions are the two groups of one generic scan over rows (b, k*D + d): the
+// direction-major layouts of u, delta, B, C, A, D and delta_bias are exactly that scan's
+// (batch, 2D, L), (batch, 2, N, L), (2D, N) and (2D) layouts.
+struct VimLayout {
+  ScanLayout scan;
+  int64_t off_scan, off_ys, off_dy, total;
+};
+
+static VimLayout vim_layout(int64_t batch, int64_t dim, int64_t L, int64_t dstate, int dtype) {
+  VimLayout l{};
+  l.scan = scan_layout(batch, 2 * dim, dstate, L, 2, dtype);
+  int64_t o = 0;
+  l.off_scan = o; o += align_up(l.scan.total);
+  l.off_ys = o;   o += align_up(batch * 2 * dim * L * 4);              // fp32 direction outputs, own order
+  l.off_dy = o;   o += align_up(batch * 2 * dim * L * 4);              // fp32 gradient reaching them
+  l.total = o;
+  return l;
+}
+
+static int check_vim(int64_t batch, int64_t dim, int64_t L, int64_t dstate, int dtype) {
+  if (!dtype_ok(dtype)) return SS2D_ERR_UNSUPPORTED;
+  if (batch < 0 || dim < 0 || L < 0) return SS2D_ERR_INVALID_ARGUMENT;
+  if (dstate < 1 || dstate > 64) return SS2D_ERR_UNSUPPORTED;
+  if (cdiv(batch * dim * L, 256) > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
+  return SS2D_OK;
+}
+
+size_t vim_bidir_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int dtype) {
+  if (check_vim(batch, dim, seqlen, dstate, dtype) != SS2D_OK) return 0;
+  return size_t(vim_layout(batch, dim, seqlen, dstate, dtype).total);
+}
+
+static int validate_vim_fwd(const vim_bidir_fwd_args* a, VimLayout* lay, bool* empty) {
+  *empty = false;
+  if (!a) return SS2D_ERR_INVALID_ARGUMENT;
+  int st = check_vim(a->batch, a->dim, a->seqlen, a->dstate, a->dtype);
+  if (st != SS2D_OK) return st;
+  if (a->batch * a->dim * a->seqlen == 0) {
+    *empty = true;
+    return SS2D_OK;
+  }
+  if (!a->u || !a->delta || !a->A || !a->Bm || !a->Cm || !a->out || !a->workspace) return SS2D_ERR_INVALID_ARGUMENT;
+  if (!elem_aligned(a->dtype, {a->u, a->delta, a->Bm, a->Cm, a->z, a->out})) return SS2D_ERR_INVALID_ARGUMENT;
+  if (!aligned(a->A, 4) || (a->Dskip && !aligned(a->Dskip, 4)) || (a->delta_bias && !aligned(a->delta_bias, 4)))
+    return SS2D_ERR_INVALID_ARGUMENT;
+  *lay = vim_layout(a->batch, a->dim, a->seqlen, a->dstate, a->dtype);
+  if (a->workspace_bytes < size_t(lay->total) || !aligned(a->workspace, kAlign)) return SS2D_ERR_INVALID_ARGUMENT;
+  return SS2D_OK;
+}
+
+// the two direction scans as one generic scan, outputs into the workspace
+static ss_fwd_args vim_scan_args(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
+                                 const float* Dskip, const float* delta_bias, void* ws, const VimLayout& lay,
+                                 int64_t batch, int64_t dim, int64_t L, int64_t dstate, int dtype, int softplus) {
+  ss_fwd_args f{};
+  f.u = u;
+  f.delta = delta;
+  f.A = A;
+  f.Bm = Bm;
+  f.Cm = Cm;
+  f.Dskip = Dskip;
+  f.z = nullptr;
+  f.delta_bias = delta_bias;
+  f.out = at(ws, lay.off_ys);
+  f.workspace = at(ws, lay.off_scan);
+  f.workspace_bytes = size_t(lay.scan.total);
+  f.batch = batch;
+  f.dim = 2 * dim;
+  f.dstate = dstate;
+  f.seqlen = L;
+  f.ngroups = 2;
+  f.dtype = dtype;
+  f.delta_softplus = softplus;
+  return f;
+}
+
+static int vim_merge_stage(const vim_bidir_fwd_args* a, const VimLayout& lay, hipStream_t stream) {
+  BidirArgs m{};
+  m.ys = reinterpret_cast<const float*>(at(a->workspace, lay.off_ys));
+  m.z = a->z;
+  m.out = a->out;
+  m.batch = a->batch;
+  m.C = a->dim;
+  m.L = a->seqlen;
+  m.dtype = a->dtype;
+  return status_from(launch_bidir_merge(m, stream));
+}
+
+static int vim_scan_stage(const vim_bidir_fwd_args* a, const VimLayout& lay, hipStream_t stream) {
+  const ss_fwd_args f = vim_scan_args(a->u, a->delta, a->A, a->Bm, a->Cm, a->Dskip, a->delta_bias, a->workspace, lay,
+                                      a->batch, a->dim, a->seqlen, a->dstate, a->dtype, a->delta_softplus);
+  return scan_fwd_impl(&f, false, stream, true);
+}
+
+int vim_bidir_fwd(const vim_bidir_fwd_args* a, hipStream_t stream) {
+  VimLayout lay;
+  bool empty;
+  int st = validate_vim_fwd(a, &lay, &empty);
+  if (st != SS2D_OK || empty) return st;
+  st = vim_scan_stage(a, lay, stream);
+  if (st == SS2D_OK) st = vim_merge_stage(a, lay, stream);
+  return st;
+}
+
+int vim_bidir_fwd_stage(const vim_bidir_fwd_args* a, int stage, hipStream_t stream) {
+  if (stage != SS2D_STAGE_TRANSPOSE && stage != SS2D_STAGE_SCAN && stage != SS2D_STAGE_MERGE)
+    return SS2D_ERR_INVALID_ARGUMENT;
+  VimLayout lay;
+  bool empty;
+  int st = validate_vim_fwd(a, &lay, &empty);
+  if (st != SS2D_OK || empty || stage == SS2D_STAGE_TRANSPOSE) return st;
+  return stage == SS2D_STAGE_SCAN ? vim_scan_stage(a, lay, stream) : vim_merge_stage(a, lay, stream);
+}
+
+int vim_bidir_bwd(const vim_bidir_bwd_args* a, hipStream_t stream) {
+  if (!a) return SS2D_ERR_INVALID_ARGUMENT;
+  int st = check_vim(a->batch, a->dim, a->seqlen, a->dstate, a->dtype);
+  if (st != SS2D_OK) return st;
+  if ((a->Dskip && !a->dDskip) || (a->delta_bias && !a->ddelta_bias) || (a->z && !a->dz))
+    return SS2D_ERR_INVALID_ARGUMENT;
+  if (a->dim == 0) return SS2D_OK;
+  if (!a->dA) return SS2D_ERR_INVALID_ARGUMENT;
+  if (a->batch == 0 || a->seqlen == 0)
+    return zero_param_grads(a->dA, a->Dskip ? a->dDskip : nullptr, a->delta_bias ? a->ddelta_bias : nullptr,
+                            2 * a->dim, a->dstate, stream);
+  if (!a->u || !a->delta || !a->A || !a->Bm || !a->Cm || !a->dout || !a->du || !a->ddelta || !a->dBm || !a->dCm ||
+      !a->workspace)
+    return SS2D_ERR_INVALID_ARGUMENT;
+  if (!elem_aligned(a->dtype, {a->u, a->delta, a->Bm, a->Cm, a->z, a->dout, a->du, a->ddelta, a->dBm, a->dCm, a->dz}))
+    return SS2D_ERR_INVALID_ARGUMENT;
+  if (!aligned(a->A, 4) || !aligned(a->dA, 4) || (a->Dskip && !aligned(a->Dskip, 4)) ||
+      (a->delta_bias && !aligned(a->delta_bias, 4)) || (a->dDskip && !aligned(a->dDskip, 4)) ||
+      (a->ddelta_bias && !aligned(a->ddelta_bias, 4)))
+    return SS2D_ERR_INVALID_ARGUMENT;
+  const VimLayout lay = vim_layout(a->batch, a->dim, a->seqlen, a->dstate, a->dtype);
+  if (a->workspace_bytes < size_t(lay.total) || !aligned(a->workspace, kAlign)) return SS2D_ERR_INVALID_ARGUMENT;
+  if (a->batch * 2 * lay.scan.dblocks * lay.scan.bwd_n_chunks > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
+  const int64_t L = a->seqlen;
+
+  // forward again: direction outputs and checkpoint states
+  const ss_fwd_args f = vim_scan_args(a->u, a->delta, a->A, a->Bm, a->Cm, a->Dskip, a->delta_bias, a->workspace, lay,
+                                      a->batch, a->dim, L, a->dstate, a->dtype, a->delta_softplus);
+  st = scan_fwd_impl(&f, true, stream, true);
+  if (st != SS2D_OK) return st;
+
+  // gate: dz, and the fp32 gradient reaching each direction in its own order
+  BidirArgs g{};
+  g.ys = reinterpret_cast<const float*>(at(a->workspace, lay.off_ys));
+  g.z = a->z;
+  g.dout = a->dout;
+  g.dy = reinterpret_cast<float*>(at(a->workspace, lay.off_dy));
+  g.dz = a->dz;
+  g.batch = a->batch;
+  g.C = a->dim;
+  g.L = L;
+  g.dtype = a->dtype;
+  if (launch_bidir_gate_bwd(g, stream) != hipSuccess) return SS2D_ERR_HIP;
+
+  // adjoint scans of the two directions
+  ScanBwdParams bp{};
+  bp.u = a->u;
+  bp.delta = a->delta;
+  bp.A = a->A;
+  bp.Bm = a->Bm;
+  bp.Cm = a->Cm;
+  bp.Dskip = a->Dskip;
+  bp.delta_bias = a->delta_bias;
+  bp.dout = g.dy;
+  bp.dout_f32 = 1;
+  bp.du = a->du;
+  bp.ddelta = a->ddelta;
+  bp.batch = a->batch;
+  bp.dim = 2 * a->dim;
+  bp.L = L;
+  bp.G = 2;
+  bp.per_group = lay.scan.per_group;
+  bp.dblocks = lay.scan.dblocks;
+  bp.N = int(a->dstate);
+  bp.softplus = a->delta_softplus ? 1 : 0;
+  bp.ss2d = 0;
+  bp.dtype = a->dtype;
+  bp.vec = (L % 4 == 0) && vec_aligned(a->dtype, {a->u, a->delta, a->Bm, a->Cm, a->du, a->ddelta});
+  return run_scan_bwd(bp, lay.scan, at(a->workspace, lay.off_scan), a->dBm, a->dCm, a->dA,
+                      a->Dskip ? a->dDskip : nullptr, a->delta_bias ? a->ddelta_bias : nullptr, stream);
 }
 
 }  // extern "C"

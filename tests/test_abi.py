@@ -32,7 +32,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"ss2d_cross_scan", "ss2d_cross_merge", "selective_scan_fwd", "selective_scan_bwd", "ss2d_fwd",
             "ss2d_bwd", "ss2d_fwd_stage", "selective_scan_workspace_bytes", "ss2d_workspace_bytes",
-            "ss2d_abi_version", "ss2d_status_string"} <= set(names)
+            "ss2d_abi_version", "ss2d_status_string", "vim_bidir_workspace_bytes", "vim_bidir_fwd",
+            "vim_bidir_fwd_stage", "vim_bidir_bwd"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
     missing = [n for n in names if n not in exported]
@@ -42,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ss2d_abi_version() == 1
+    assert lib.ss2d_abi_version() == 2
     assert lib.ss2d_status_string(0) == b"ok"
     assert b"invalid" in lib.ss2d_status_string(1)
     assert b"unsupported" in lib.ss2d_status_string(2)
@@ -50,7 +51,7 @@ def test_version_and_status_strings(lib):
 
 
 STRUCTS = {"ss_fwd_args": "SsFwdArgs", "ss_bwd_args": "SsBwdArgs", "ss2d_fwd_args": "SS2DFwdArgs",
-           "ss2d_bwd_args": "SS2DBwdArgs"}
+           "ss2d_bwd_args": "SS2DBwdArgs", "vim_bidir_fwd_args": "VimFwdArgs", "vim_bidir_bwd_args": "VimBwdArgs"}
 
 
 def test_binding_structs_match_header(tmp_path):
@@ -132,6 +133,28 @@ def test_ss2d_rejects(lib):
     assert lib.ss2d_bwd(ctypes.byref(SS2DBwdArgs(**{**b, "Dskip": 0xc000})), None) == 1  # D without dD
 
 
+def test_vim_bidir_rejects(lib):
+    from selective_scan_amd._binding import VimBwdArgs, VimFwdArgs
+    f = dict(u=0x1000, delta=0x2000, A=0x3000, Bm=0x4000, Cm=0x5000, out=0x6000, workspace=0x10000,
+             workspace_bytes=1, batch=1, dim=4, seqlen=7, dstate=4, dtype=1, delta_softplus=1)
+    assert lib.vim_bidir_fwd(ctypes.byref(VimFwdArgs(**f)), None) == 1                    # workspace too small
+    assert lib.vim_bidir_fwd(ctypes.byref(VimFwdArgs(**{**f, "workspace": 0})), None) == 1
+    assert lib.vim_bidir_fwd(ctypes.byref(VimFwdArgs(**{**f, "dtype": 3})), None) == 2
+    assert lib.vim_bidir_fwd(ctypes.byref(VimFwdArgs(**{**f, "dstate": 65})), None) == 2
+    assert lib.vim_bidir_fwd(ctypes.byref(VimFwdArgs(**{**f, "seqlen": -1})), None) == 1
+    assert lib.vim_bidir_fwd(ctypes.byref(VimFwdArgs(**{**f, "u": 0x1001})), None) == 1    # misaligned bf16
+    assert lib.vim_bidir_fwd(ctypes.byref(VimFwdArgs(**{**f, "seqlen": 0})), None) == 0    # empty
+    assert lib.vim_bidir_fwd(None, None) == 1
+    assert lib.vim_bidir_fwd_stage(ctypes.byref(VimFwdArgs(**f)), 5, None) == 1           # bad stage
+    assert lib.vim_bidir_fwd_stage(ctypes.byref(VimFwdArgs(**{**f, "seqlen": 0})), 0, None) == 0
+    b = dict(u=0x1000, delta=0x2000, A=0x3000, Bm=0x4000, Cm=0x5000, dout=0x6000, du=0x7000, ddelta=0x8000,
+             dA=0x9000, dBm=0xa000, dCm=0xb000, workspace=0x10000, workspace_bytes=1, batch=1, dim=4, seqlen=7,
+             dstate=4, dtype=0, delta_softplus=1)
+    assert lib.vim_bidir_bwd(ctypes.byref(VimBwdArgs(**b)), None) == 1                    # workspace too small
+    assert lib.vim_bidir_bwd(ctypes.byref(VimBwdArgs(**{**b, "z": 0xc000})), None) == 1   # z without dz
+    assert lib.vim_bidir_bwd(ctypes.byref(VimBwdArgs(**{**b, "dim": 0})), None) == 0
+
+
 def test_cross_scan_merge_reject(lib):
     assert lib.ss2d_cross_scan(None, None, 1, 1, 2, 2, 0, None) == 1
     assert lib.ss2d_cross_scan(0x1000, 0x2000, 1, 1, 2, 2, 5, None) == 2
@@ -149,4 +172,9 @@ def test_workspace_queries(lib):
     s2 = lib.ss2d_workspace_bytes(1, 16, 8, 8, 4, 1)
     assert 0 < s2 < s1  # the transposed copy of x is narrower in bf16
     assert lib.ss2d_workspace_bytes(1, 16, 8, 8, 4, 9) == 0
-    assert all(v % 256 == 0 for v in (a, b, s1, s2))
+    v1 = lib.vim_bidir_workspace_bytes(2, 8, 197, 16, 1)
+    v2 = lib.vim_bidir_workspace_bytes(2, 8, 197, 16, 0)
+    assert 0 < v1 < v2  # the direction outputs are narrower in bf16
+    assert lib.vim_bidir_workspace_bytes(2, 8, 197, 0, 1) == 0
+    assert lib.vim_bidir_workspace_bytes(2, 8, 197, 16, 4) == 0
+    assert all(v % 256 == 0 for v in (a, b, s1, s2, v1, v2))
