@@ -174,7 +174,7 @@ def test_workspace_queries(lib):
     assert lib.ss2d_workspace_bytes(1, 16, 8, 8, 4, 9) == 0
     v1 = lib.vim_bidir_workspace_bytes(2, 8, 197, 16, 1)
     v2 = lib.vim_bidir_workspace_bytes(2, 8, 197, 16, 0)
-    assert 0 < v1 < v2  # the direction outputs are narrower in bf16
+    assert 0 < v1 == v2  # fp32 direction outputs and gradients: the same size for either I/O type
     assert lib.vim_bidir_workspace_bytes(2, 8, 197, 0, 1) == 0
     assert lib.vim_bidir_workspace_bytes(2, 8, 197, 16, 4) == 0
     assert all(v % 256 == 0 for v in (a, b, s1, s2, v1, v2))
