@@ -11,7 +11,8 @@ min / max, the whole-step algorithmic HBM rate against the 8 TB/s peak and again
 device copy timed in the same run, the roofline of the dominant kernel (the route-scan
 kernel, timed live with HIP events on the stream it is launched on) and the fp64 CPU
 oracle timed on this host on a bounded sample of the same workload.  `--workload`
-selects one of the other shapes; `--bwd` adds the fused backward to each step.
+selects one of the other shapes (0-4 SS2D, 5 the Vision Mamba bidirectional scan at
+Vim-Tiny size); `--bwd` adds the fused backward to each step.
 
 When one input/output set is smaller than the 256 MB last-level cache (MALL) several
 times over, the steps rotate over independent copies so that no step re-reads what the
@@ -53,7 +54,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=1, help="index into synth.CONFIGS (default: stage-1)")
+    ap.add_argument("--workload", type=int, default=1,
+                    help="index into synth.CONFIGS + synth.VIM_CONFIGS (default 1: SS2D stage-1; 5: Vim-Tiny)")
     ap.add_argument("--bwd", action="store_true", help="time forward + backward per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time for the sample")
@@ -63,6 +65,14 @@ def parse():
 def algorithmic_bytes(cfg, bwd=False):
     """Each tensor read once and each output written once (the fused minimum)."""
     e = 2 if cfg.dtype == "bf16" else 4
+    if getattr(cfg, "kind", "ss2d") == "vim":
+        seq = cfg.batch * cfg.dim * cfg.seqlen  # one direction, or the gate / output sequence
+        bc = 2 * cfg.batch * 2 * cfg.dstate * cfg.seqlen
+        fwd = e * (2 * seq + 2 * seq + bc + (seq if cfg.has_z else 0) + seq)  # u, delta, B/C, z in; out
+        if not bwd:
+            return fwd
+        # backward: reads u, delta, B, C, z, dout; writes du, ddelta, dB, dC, dz
+        return fwd + e * (seq + 2 * seq + 2 * seq + bc + (seq if cfg.has_z else 0))
     grid = cfg.batch * cfg.dim * cfg.seqlen
     seq = cfg.batch * 4 * cfg.dim * cfg.seqlen
     bc = 2 * cfg.batch * 4 * cfg.dstate * cfg.seqlen
@@ -112,7 +122,21 @@ def cpu_baseline(cfg, inp, target_s, bwd=False):
     import oracle
     from selective_scan_amd import synth
 
+    vim = getattr(cfg, "kind", "ss2d") == "vim"
+
+    def run_vim(nb):
+        sl = lambda a: None if a is None else synth.storage_to_f64(a[:nb], cfg.dtype)
+        args = (sl(inp["u"]), sl(inp["delta"]), inp["A"].astype(np.float64), sl(inp["B"]), sl(inp["C"]),
+                inp["D"].astype(np.float64), inp["delta_bias"].astype(np.float64), sl(inp["z"]))
+        t0 = time.perf_counter()
+        oracle.vim_bidir_fwd(*args)
+        if bwd:
+            oracle.vim_bidir_bwd(*args, dout=sl(inp["dout"]))
+        return time.perf_counter() - t0
+
     def run(nb):
+        if vim:
+            return run_vim(nb)
         sl = lambda a: None if a is None else synth.storage_to_f64(a[:nb], cfg.dtype)
         args = (sl(inp["x"]), sl(inp["delta"]), inp["A"].astype(np.float64), sl(inp["B"]), sl(inp["C"]),
                 inp["D"].astype(np.float64), inp["delta_bias"].astype(np.float64), sl(inp["z"]))
@@ -125,13 +149,24 @@ def cpu_baseline(cfg, inp, target_s, bwd=False):
     t1 = run(1)
     nb = int(max(1, min(cfg.batch, round(target_s / max(t1, 1e-3)))))
     t = run(nb) if nb > 1 else t1
-    elems = nb * 4 * cfg.dim * cfg.seqlen
+    routes = 2 if vim else 4
+    elems = nb * routes * cfg.dim * cfg.seqlen
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     return {"value": elems / t, "unit": "elements/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {nb} of {cfg.batch} images (all {cfg.dim} channels, 4 routes, "
-                      f"L={cfg.seqlen}, N={cfg.dstate}), fp64 C oracle with OpenMP over rows, "
-                      f"{'forward + backward' if bwd else 'forward'}, {t:.2f} s wall",
+            "sample": f"first {nb} of {cfg.batch} {'sequences' if vim else 'images'} (all {cfg.dim} channels, "
+                      f"{routes} {'directions' if vim else 'routes'}, L={cfg.seqlen}, N={cfg.dstate}), fp64 C "
+                      f"oracle with OpenMP over rows, {'forward + backward' if bwd else 'forward'}, {t:.2f} s wall",
             "cpu_model": cpu_model()}
+
+
+def config_record(cfg, vim, bwd, n_sets):
+    if vim:
+        return {"workload": ("vim_bidir_fwd+bwd " if bwd else "vim_bidir_fwd ") + cfg.name, "batch": cfg.batch,
+                "seqlen": cfg.seqlen, "directions": 2, "dim": cfg.dim, "dstate": cfg.dstate, "gate_z": cfg.has_z,
+                "io_sets_rotated": n_sets}
+    return {"workload": ("ss2d_fwd+bwd " if bwd else "ss2d_fwd ") + cfg.name, "batch": cfg.batch,
+            "height": cfg.height, "width": cfg.width, "routes": 4, "dim": cfg.dim, "dstate": cfg.dstate,
+            "gate_z": cfg.has_z, "io_sets_rotated": n_sets}
 
 
 def stats(ms):
@@ -150,8 +185,10 @@ def main():
     import selective_scan_amd as ss
     from selective_scan_amd import synth
 
-    cfg = synth.CONFIGS[args.workload]
-    inp = synth.make_config_inputs(cfg, with_dout=args.bwd)
+    workloads = list(synth.CONFIGS) + list(synth.VIM_CONFIGS)
+    cfg = workloads[args.workload]
+    vim = getattr(cfg, "kind", "ss2d") == "vim"
+    inp = (synth.make_vim_config_inputs if vim else synth.make_config_inputs)(cfg, with_dout=args.bwd)
 
     def dev(a, dtype):
         if a is None:
@@ -160,11 +197,14 @@ def main():
             return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
-    d0 = dict(x=dev(inp["x"], cfg.dtype), delta=dev(inp["delta"], cfg.dtype), A=dev(inp["A"], "f32"),
-              B=dev(inp["B"], cfg.dtype), C=dev(inp["C"], cfg.dtype), D=dev(inp["D"], "f32"),
-              delta_bias=dev(inp["delta_bias"], "f32"), z=dev(inp["z"], cfg.dtype) if cfg.has_z else None)
+    first = "u" if vim else "x"
+    d0 = {first: dev(inp[first], cfg.dtype), "delta": dev(inp["delta"], cfg.dtype), "A": dev(inp["A"], "f32"),
+          "B": dev(inp["B"], cfg.dtype), "C": dev(inp["C"], cfg.dtype), "D": dev(inp["D"], "f32"),
+          "delta_bias": dev(inp["delta_bias"], "f32"), "z": dev(inp["z"], cfg.dtype) if cfg.has_z else None}
     dout0 = dev(inp["dout"], cfg.dtype) if args.bwd else None
-    plan0 = ss.SS2DForwardPlan(**d0)
+    Plan = ss.VimForwardPlan if vim else ss.SS2DForwardPlan
+    backward = ss.vim_bidir_bwd if vim else ss.ss2d_bwd
+    plan0 = Plan(**d0)
     # bytes one step touches in HBM (inputs, output, workspace): rotate independent copies
     # until one cycle over them exceeds three times the MALL
     footprint = sum(t.numel() * t.element_size() for t in d0.values() if t is not None)
@@ -173,7 +213,7 @@ def main():
     sets = [(d0, dout0, plan0)]
     for _ in range(n_sets - 1):
         dk = {k: (None if v is None else v.clone()) for k, v in d0.items()}
-        sets.append((dk, None if dout0 is None else dout0.clone(), ss.SS2DForwardPlan(**dk)))
+        sets.append((dk, None if dout0 is None else dout0.clone(), Plan(**dk)))
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
@@ -188,7 +228,7 @@ def main():
             ev[2].record(stream)
         plan.run_stage(2)
         if args.bwd:
-            ss.ss2d_bwd(**d, dout=dout, workspace=plan.workspace)
+            backward(**d, dout=dout, workspace=plan.workspace)
         if ev is not None:
             ev[3].record(stream)
 
@@ -241,9 +281,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) inputs, S4D-real A, inverse-softplus dt bias)",
-        "config": {"workload": ("ss2d_fwd+bwd " if args.bwd else "ss2d_fwd ") + cfg.name,
-                   "batch": cfg.batch, "height": cfg.height, "width": cfg.width, "routes": 4,
-                   "dim": cfg.dim, "dstate": cfg.dstate, "gate_z": cfg.has_z, "io_sets_rotated": n_sets},
+        "config": config_record(cfg, vim, args.bwd, n_sets),
         "step_ms": stats(step_ms),
         "hbm": {"algorithmic_bytes_per_step": step_bytes,
                 "achieved_GBps": hbm_gbps,
@@ -251,7 +289,7 @@ def main():
                 "frac": hbm_gbps / HBM_PEAK_GBPS,
                 "copy_ceiling_GBps": copy_gbps,
                 "frac_of_copy": hbm_gbps / copy_gbps},
-        "roofline": {"kernel": "route scan (scan_fwd_kernel)", "bound": "alu",
+        "roofline": {"kernel": ("direction" if vim else "route") + " scan (scan_fwd_kernel)", "bound": "alu",
                      "achieved": achieved_tflops, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved_tflops / VALU_PEAK_TFLOPS, "traffic": traffic,
                      "mix_peak": MIX_PEAK_TFLOPS, "frac_of_mix_peak": achieved_tflops / MIX_PEAK_TFLOPS,
