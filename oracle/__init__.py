@@ -11,6 +11,7 @@ Functions (see ``oracle/ss2d_oracle.py`` for the citations):
   ss_fwd, ss_bwd                 the selective scan and its exact gradient (C, fp64)
   ss2d_fwd, ss2d_bwd             cross-scan -> selective scan -> cross-merge (+ gate)
   vim_bidir_fwd, vim_bidir_bwd   Vision Mamba's two-direction scan (oracle/vim_oracle.py)
+  ss_step                        one recurrent step from a carried state (oracle/step_oracle.py)
 
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against
 closed forms, invariants, a brute-force semiseparable-matrix formulation and
@@ -27,4 +28,5 @@ from .ss2d_oracle import (  # noqa: F401
     ss_bwd,
     ss_fwd,
 )
+from .step_oracle import ss_step  # noqa: F401
 from .vim_oracle import vim_bidir_bwd, vim_bidir_fwd  # noqa: F401
