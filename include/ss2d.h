@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SS2D_ABI_VERSION 2
+#define SS2D_ABI_VERSION 3
 
 /* Status codes returned by every entry point. */
 enum {
@@ -160,6 +160,39 @@ typedef struct ss_bwd_args {
 } ss_bwd_args;
 
 int selective_scan_bwd(const ss_bwd_args* args, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * One recurrent step from a carried state, for token-by-token inference [S6 page, section 2:
+ * the `Mamba` module keeps `ssm_state` -- the last_state of selective_scan_fwd -- and advances
+ * it one token at a time in place; the step is one iteration of `selective_scan_ref`'s loop]:
+ *   delta = softplus(delta_raw + delta_bias)          (bias/softplus optional)
+ *   state[b, d, n] <- exp(delta*A[d, n]) * state[b, d, n] + delta * B[b, g, n] * x[b, d]
+ *   out[b, d] = (sum_n C[b, g, n] * state[b, d, n] + D[d] * x[b, d]) * silu(z[b, d])  (z optional)
+ * with channel d reading group g = d / (dim / ngroups).
+ * Layouts:  state          : (batch, dim, dstate) fp32, read and overwritten (caller-owned)
+ *           x, delta, z, out: (batch, dim)          dtype
+ *           A              : (dim, dstate) fp32;  Bm, Cm : (batch, ngroups, dstate) dtype
+ *           Dskip, delta_bias : (dim) fp32, may be NULL
+ * No workspace.  Chaining steps from a zero state gives selective_scan_fwd's outputs and
+ * last_state, up to rounding.
+ * ------------------------------------------------------------------------------- */
+typedef struct ss_step_args {
+  float* state;
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;      /* may be NULL */
+  const void* z;           /* may be NULL */
+  const float* delta_bias; /* may be NULL */
+  void* out;
+  int64_t batch, dim, dstate, ngroups;
+  int dtype;
+  int delta_softplus;
+} ss_step_args;
+
+int selective_scan_step(const ss_step_args* args, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
  * Fused SS2D forward [VMamba, SS2D section]: equivalent, up to fp32 rounding order, to

@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     lib,
     selective_scan_bwd,
     selective_scan_fwd,
+    selective_scan_step,
     selective_scan_workspace_bytes,
     ss2d_bwd,
     ss2d_cross_merge,

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libss2d.so")
 
 SS2D_OK, SS2D_ERR_INVALID_ARGUMENT, SS2D_ERR_UNSUPPORTED, SS2D_ERR_HIP = 0, 1, 2, 3
 DTYPE_F32, DTYPE_BF16 = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -51,6 +51,12 @@ class SS2DBwdArgs(ctypes.Structure):
                                   "ddelta", "dA", "dBm", "dCm", "dDskip", "ddelta_bias", "dz", "workspace")] + [
         ("workspace_bytes", _sz), ("batch", _i64), ("dim", _i64), ("height", _i64), ("width", _i64),
         ("dstate", _i64), ("dtype", _int), ("delta_softplus", _int)]
+
+
+class SsStepArgs(ctypes.Structure):
+    _fields_ = [(n, _p) for n in ("state", "x", "delta", "A", "Bm", "Cm", "Dskip", "z", "delta_bias", "out")] + [
+        ("batch", _i64), ("dim", _i64), ("dstate", _i64), ("ngroups", _i64), ("dtype", _int),
+        ("delta_softplus", _int)]
 
 
 class VimFwdArgs(ctypes.Structure):
@@ -97,7 +103,8 @@ def lib():
         L.vim_bidir_fwd_stage.argtypes = [ctypes.POINTER(VimFwdArgs), _int, _p]
         for name, st in (("selective_scan_fwd", SsFwdArgs), ("selective_scan_bwd", SsBwdArgs),
                          ("ss2d_fwd", SS2DFwdArgs), ("ss2d_bwd", SS2DBwdArgs),
-                         ("vim_bidir_fwd", VimFwdArgs), ("vim_bidir_bwd", VimBwdArgs)):
+                         ("vim_bidir_fwd", VimFwdArgs), ("vim_bidir_bwd", VimBwdArgs),
+                         ("selective_scan_step", SsStepArgs)):
             f = getattr(L, name)
             f.restype = _int
             f.argtypes = [ctypes.POINTER(st), _p]
@@ -406,3 +413,27 @@ def vim_bidir_bwd(u, delta, A, B, C, D=None, delta_bias=None, z=None, dout=None,
                    seqlen=L, dstate=N, dtype=_dtype_code(u.dtype), delta_softplus=int(bool(delta_softplus)))
     _check(lib().vim_bidir_bwd(ctypes.byref(a), _stream(dev)), "vim_bidir_bwd")
     return {"du": du, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "ddelta_bias": dbias, "dz": dz}
+
+
+def selective_scan_step(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False):
+    """One recurrent step from a carried state: `state` (batch, dim, N), a contiguous fp32 device
+    tensor, is updated in place; x, delta, z are (batch, dim); B, C are (batch, G, N) or
+    (batch, N).  Returns out (batch, dim)."""
+    if state.dtype != torch.float32 or not state.is_contiguous():
+        raise SS2DError("state must be a contiguous fp32 tensor (it is updated in place)")
+    x, delta = _c(x), _c(delta)
+    dev = _dev(x)
+    if B.dim() == 2:
+        B, C = B.unsqueeze(1), C.unsqueeze(1)
+    B, C, z = _c(B), _c(C), _c(z)
+    A = _c(A, torch.float32)
+    D = _c(D, torch.float32)
+    delta_bias = _c(delta_bias, torch.float32)
+    batch, dim = x.shape
+    N = A.shape[1]
+    out = torch.empty_like(x)
+    a = SsStepArgs(state=_ptr(state), x=_ptr(x), delta=_ptr(delta), A=_ptr(A), Bm=_ptr(B), Cm=_ptr(C), Dskip=_ptr(D),
+                   z=_ptr(z), delta_bias=_ptr(delta_bias), out=_ptr(out), batch=batch, dim=dim, dstate=N,
+                   ngroups=B.shape[1], dtype=_dtype_code(x.dtype), delta_softplus=int(bool(delta_softplus)))
+    _check(lib().selective_scan_step(ctypes.byref(a), _stream(dev)), "selective_scan_step")
+    return out

@@ -121,6 +121,25 @@ hipError_t launch_scan_fwd(const ScanFwdParams& p, hipStream_t s);
 // Turns the chunk-local end states (pass 1) into the true chunk-start states.
 hipError_t launch_chunk_combine(const ScanFwdParams& p, hipStream_t s);
 
+// ---- one recurrent step (scan_step.hip) ---------------------------------------------------
+struct StepParams {
+  float* state;             // (batch, dim, N) fp32, updated in place
+  const void* x;            // (batch, dim) dtype
+  const void* delta;        // (batch, dim) dtype
+  const float* A;           // (dim, N)
+  const void* Bm;           // (batch, G, N) dtype
+  const void* Cm;           // (batch, G, N) dtype
+  const float* Dskip;       // (dim) or null
+  const void* z;            // (batch, dim) dtype or null
+  const float* delta_bias;  // (dim) or null
+  void* out;                // (batch, dim) dtype
+  int64_t batch, dim, G;
+  int N;
+  int softplus;
+  int dtype;
+};
+hipError_t launch_scan_step(const StepParams& p, hipStream_t s);
+
 // ---- selective scan backward (scan_bwd.hip) ---------------------------------------------
 struct ScanBwdParams {
   const void* u;

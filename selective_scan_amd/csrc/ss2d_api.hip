@@ -270,6 +270,39 @@ int selective_scan_fwd(const ss_fwd_args* a, hipStream_t stream) {
   return scan_fwd_impl(a, a && a->workspace != nullptr, stream);
 }
 
+int selective_scan_step(const ss_step_args* a, hipStream_t stream) {
+  if (!a) return SS2D_ERR_INVALID_ARGUMENT;
+  if (!dtype_ok(a->dtype)) return SS2D_ERR_UNSUPPORTED;
+  if (a->dstate < 1 || a->dstate > 64) return SS2D_ERR_UNSUPPORTED;
+  if (a->batch < 0 || a->dim < 0 || a->ngroups < 1 || a->dim % a->ngroups != 0) return SS2D_ERR_INVALID_ARGUMENT;
+  const int64_t rows = a->batch * a->dim;
+  if (rows == 0) return SS2D_OK;
+  if (cdiv(rows * padded_states(a->dstate), 256) > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
+  if (!a->state || !a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->out) return SS2D_ERR_INVALID_ARGUMENT;
+  if (!elem_aligned(a->dtype, {a->x, a->delta, a->Bm, a->Cm, a->z, a->out})) return SS2D_ERR_INVALID_ARGUMENT;
+  if (!aligned(a->state, 4) || !aligned(a->A, 4) || (a->Dskip && !aligned(a->Dskip, 4)) ||
+      (a->delta_bias && !aligned(a->delta_bias, 4)))
+    return SS2D_ERR_INVALID_ARGUMENT;
+  StepParams p{};
+  p.state = a->state;
+  p.x = a->x;
+  p.delta = a->delta;
+  p.A = a->A;
+  p.Bm = a->Bm;
+  p.Cm = a->Cm;
+  p.Dskip = a->Dskip;
+  p.z = a->z;
+  p.delta_bias = a->delta_bias;
+  p.out = a->out;
+  p.batch = a->batch;
+  p.dim = a->dim;
+  p.G = a->ngroups;
+  p.N = int(a->dstate);
+  p.softplus = a->delta_softplus ? 1 : 0;
+  p.dtype = a->dtype;
+  return status_from(launch_scan_step(p, stream));
+}
+
 size_t ss2d_workspace_bytes(int64_t batch, int64_t dim, int64_t height, int64_t width, int64_t dstate, int dtype) {
   if (batch < 0 || dim < 0 || height < 0 || width < 0 || dstate < 1 || !dtype_ok(dtype)) return 0;
   return size_t(ss2d_layout(batch, dim, height, width, dstate, dtype).total);

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert {"ss2d_cross_scan", "ss2d_cross_merge", "selective_scan_fwd", "selective_scan_bwd", "ss2d_fwd",
             "ss2d_bwd", "ss2d_fwd_stage", "selective_scan_workspace_bytes", "ss2d_workspace_bytes",
             "ss2d_abi_version", "ss2d_status_string", "vim_bidir_workspace_bytes", "vim_bidir_fwd",
-            "vim_bidir_fwd_stage", "vim_bidir_bwd"} <= set(names)
+            "vim_bidir_fwd_stage", "vim_bidir_bwd", "selective_scan_step"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
     missing = [n for n in names if n not in exported]
@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ss2d_abi_version() == 2
+    assert lib.ss2d_abi_version() == 3
     assert lib.ss2d_status_string(0) == b"ok"
     assert b"invalid" in lib.ss2d_status_string(1)
     assert b"unsupported" in lib.ss2d_status_string(2)
@@ -51,7 +51,8 @@ def test_version_and_status_strings(lib):
 
 
 STRUCTS = {"ss_fwd_args": "SsFwdArgs", "ss_bwd_args": "SsBwdArgs", "ss2d_fwd_args": "SS2DFwdArgs",
-           "ss2d_bwd_args": "SS2DBwdArgs", "vim_bidir_fwd_args": "VimFwdArgs", "vim_bidir_bwd_args": "VimBwdArgs"}
+           "ss2d_bwd_args": "SS2DBwdArgs", "vim_bidir_fwd_args": "VimFwdArgs", "vim_bidir_bwd_args": "VimBwdArgs",
+           "ss_step_args": "SsStepArgs"}
 
 
 def test_binding_structs_match_header(tmp_path):
@@ -153,6 +154,20 @@ def test_vim_bidir_rejects(lib):
     assert lib.vim_bidir_bwd(ctypes.byref(VimBwdArgs(**b)), None) == 1                    # workspace too small
     assert lib.vim_bidir_bwd(ctypes.byref(VimBwdArgs(**{**b, "z": 0xc000})), None) == 1   # z without dz
     assert lib.vim_bidir_bwd(ctypes.byref(VimBwdArgs(**{**b, "dim": 0})), None) == 0
+
+
+def test_selective_scan_step_rejects(lib):
+    from selective_scan_amd._binding import SsStepArgs
+    a = dict(state=0x1000, x=0x2000, delta=0x3000, A=0x4000, Bm=0x5000, Cm=0x6000, out=0x7000, batch=2, dim=8,
+             dstate=16, ngroups=2, dtype=1, delta_softplus=1)
+    assert lib.selective_scan_step(ctypes.byref(SsStepArgs(**{**a, "state": 0})), None) == 1
+    assert lib.selective_scan_step(ctypes.byref(SsStepArgs(**{**a, "ngroups": 3})), None) == 1
+    assert lib.selective_scan_step(ctypes.byref(SsStepArgs(**{**a, "dstate": 0})), None) == 2
+    assert lib.selective_scan_step(ctypes.byref(SsStepArgs(**{**a, "dtype": 2})), None) == 2
+    assert lib.selective_scan_step(ctypes.byref(SsStepArgs(**{**a, "x": 0x2001})), None) == 1   # misaligned bf16
+    assert lib.selective_scan_step(ctypes.byref(SsStepArgs(**{**a, "state": 0x1002})), None) == 1
+    assert lib.selective_scan_step(ctypes.byref(SsStepArgs(**{**a, "batch": 0})), None) == 0    # empty
+    assert lib.selective_scan_step(None, None) == 1
 
 
 def test_cross_scan_merge_reject(lib):
