@@ -76,6 +76,17 @@ __device__ __forceinline__ float softplus_log2(float w) {
   return m + fast_log2(s) + corr * kLog2e;
 }
 
+// softplus_log2(w) and, from the same e = 2^-|w| and s = 1 + e, the sigmoid of the softplus
+// argument v = w ln 2 (its derivative): 1 / (1 + e^-v) = (w >= 0 ? 1 : e) / s.
+__device__ __forceinline__ void softplus_sigmoid_log2(float w, float& lam, float& sg) {
+  const float m = fmaxf(w, 0.0f);
+  const float e = fast_exp2(-fabsf(w));
+  const float s = 1.0f + e;
+  const float corr = e - (s - 1.0f);
+  lam = m + fast_log2(s) + corr * kLog2e;
+  sg = (w >= 0.0f ? 1.0f : e) * fast_rcp(s);
+}
+
 // silu(z) = z / (1 + e^-z)
 __device__ __forceinline__ float silu(float z) { return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e)); }
 __device__ __forceinline__ float sigmoid(float z) { return fast_rcp(1.0f + fast_exp2(-z * kLog2e)); }

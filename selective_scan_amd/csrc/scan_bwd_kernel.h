@@ -267,13 +267,36 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
   auto seg_body = [&](int64_t s0, int q, const float* dv, const float* uv, const float* gv, const float* zv,
                       auto h0_of) {
       const int ns = int((t_end - s0 < kSub) ? (t_end - s0) : kSub);
-      // per-step quantities (steps past the range and inactive lanes contribute nothing)
-      float lam[kSub], dup[kSub], dy[kSub];
+      // per-step quantities (steps past the range and inactive lanes contribute nothing):
+      // Lam = delta / ln 2 and sg = d delta / d raw (the sigmoid through the softplus, else 1)
+      float lam[kSub], sg[kSub], dup[kSub], dy[kSub];
+      auto lam_sg = [&](float v, float& l, float& g) {
+        if (p.softplus) {
+          softplus_sigmoid_log2(v * kLog2e, l, g);
+        } else {
+          l = v * kLog2e;
+          g = 1.0f;
+        }
+      };
+      if (kSplit == 2) {
+        // the two lanes of a channel evaluate alternate steps and share the results by DPP
+        // (quad_perm [0,0,2,2] from the even lane, [1,1,3,3] from the odd one)
+#pragma unroll
+        for (int i = 0; i < kSub; i += 2) {
+          float l, g;
+          lam_sg((part ? dv[i + 1] : dv[i]) + bias, l, g);
+          lam[i] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, l), 0xA0, 0xF, 0xF, false));
+          lam[i + 1] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, l), 0xF5, 0xF, 0xF, false));
+          sg[i] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, g), 0xA0, 0xF, 0xF, false));
+          sg[i + 1] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, g), 0xF5, 0xF, 0xF, false));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kSub; ++i) lam_sg(dv[i] + bias, lam[i], sg[i]);
+      }
 #pragma unroll
       for (int i = 0; i < kSub; ++i) {
-        const float v = dv[i] + bias;
-        float l = p.softplus ? softplus_log2(v * kLog2e) : v * kLog2e;
-        l = (i < ns) ? l : 0.0f;
+        const float l = (i < ns) ? lam[i] : 0.0f;
         lam[i] = l;
         dup[i] = active ? l * uv[i] : 0.0f;
         float gy = gv[i];
@@ -342,7 +365,7 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
             if (has_z) yv = pair_sum(yv);
             o_du[j] = fmaf(lam[i], sbl, Dd * dy[i]);
             float dd = fmaf(uv[i] * kLog2e, sbl, ddt);  // ddelta (B was staged times ln 2)
-            if (p.softplus) dd *= sigmoid(dv[i] + bias);
+            dd *= sg[i];
             dd = (i < ns && active) ? dd : 0.0f;
             o_dd[j] = dd;
             dbias_acc += dd;
