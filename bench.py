@@ -202,8 +202,13 @@ def main():
           "B": dev(inp["B"], cfg.dtype), "C": dev(inp["C"], cfg.dtype), "D": dev(inp["D"], "f32"),
           "delta_bias": dev(inp["delta_bias"], "f32"), "z": dev(inp["z"], cfg.dtype) if cfg.has_z else None}
     dout0 = dev(inp["dout"], cfg.dtype) if args.bwd else None
-    Plan = ss.VimForwardPlan if vim else ss.SS2DForwardPlan
-    backward = ss.vim_bidir_bwd if vim else ss.ss2d_bwd
+    # with --bwd a step is a training step: for SS2D the forward keeps its checkpoint states and
+    # the backward runs on them (the Vim backward recomputes its forward)
+    if vim:
+        Plan, backward = ss.VimForwardPlan, ss.vim_bidir_bwd
+    else:
+        Plan = (lambda **kw: ss.SS2DForwardPlan(**kw, keep_states=True)) if args.bwd else ss.SS2DForwardPlan
+        backward = (lambda **kw: ss.ss2d_bwd(**kw, workspace_has_states=True))
     plan0 = Plan(**d0)
     # bytes one step touches in HBM (inputs, output, workspace): rotate independent copies
     # until one cycle over them exceeds three times the MALL

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SS2D_ABI_VERSION 3
+#define SS2D_ABI_VERSION 4
 
 /* Status codes returned by every entry point. */
 enum {
@@ -228,6 +228,8 @@ typedef struct ss2d_fwd_args {
   int64_t batch, dim, height, width, dstate;
   int dtype;
   int delta_softplus;
+  int keep_states;         /* nonzero: the workspace also keeps the checkpoint states, so that
+                              ss2d_bwd can run with workspace_has_states (a training forward) */
 } ss2d_fwd_args;
 
 int ss2d_fwd(const ss2d_fwd_args* args, hipStream_t stream);
@@ -248,8 +250,10 @@ int ss2d_fwd_stage(const ss2d_fwd_args* args, int stage, hipStream_t stream);
  *   ddelta     : (batch, 4, dim, L) dtype (w.r.t. the raw delta);
  *   dBm, dCm   : (batch, 4, dstate, L) dtype;
  *   dA         : (4, dim, dstate) fp32;  dDskip, ddelta_bias : (4, dim) fp32 (iff given)
- * Everything is overwritten.  The forward states are recomputed inside (the workspace,
- * >= ss2d_workspace_bytes(...), holds them). */
+ * Everything is overwritten.  The workspace (>= ss2d_workspace_bytes(...)) is required.  With
+ * workspace_has_states == 0 the forward is recomputed inside it; otherwise it must hold what
+ * ss2d_fwd with keep_states wrote for the same inputs (the transposed x, the route outputs and
+ * the checkpoint states), untouched since, and the forward is not run again. */
 typedef struct ss2d_bwd_args {
   const void* x;
   const void* delta;
@@ -273,6 +277,7 @@ typedef struct ss2d_bwd_args {
   int64_t batch, dim, height, width, dstate;
   int dtype;
   int delta_softplus;
+  int workspace_has_states;
 } ss2d_bwd_args;
 
 int ss2d_bwd(const ss2d_bwd_args* args, hipStream_t stream);

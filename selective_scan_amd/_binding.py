@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libss2d.so")
 
 SS2D_OK, SS2D_ERR_INVALID_ARGUMENT, SS2D_ERR_UNSUPPORTED, SS2D_ERR_HIP = 0, 1, 2, 3
 DTYPE_F32, DTYPE_BF16 = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -43,14 +43,14 @@ class SS2DFwdArgs(ctypes.Structure):
     _fields_ = [(n, _p) for n in ("x", "delta", "A", "Bm", "Cm", "Dskip", "delta_bias", "z", "out",
                                   "workspace")] + [
         ("workspace_bytes", _sz), ("batch", _i64), ("dim", _i64), ("height", _i64), ("width", _i64),
-        ("dstate", _i64), ("dtype", _int), ("delta_softplus", _int)]
+        ("dstate", _i64), ("dtype", _int), ("delta_softplus", _int), ("keep_states", _int)]
 
 
 class SS2DBwdArgs(ctypes.Structure):
     _fields_ = [(n, _p) for n in ("x", "delta", "A", "Bm", "Cm", "Dskip", "delta_bias", "z", "dout", "dx",
                                   "ddelta", "dA", "dBm", "dCm", "dDskip", "ddelta_bias", "dz", "workspace")] + [
         ("workspace_bytes", _sz), ("batch", _i64), ("dim", _i64), ("height", _i64), ("width", _i64),
-        ("dstate", _i64), ("dtype", _int), ("delta_softplus", _int)]
+        ("dstate", _i64), ("dtype", _int), ("delta_softplus", _int), ("workspace_has_states", _int)]
 
 
 class SsStepArgs(ctypes.Structure):
@@ -257,9 +257,10 @@ def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dout=
 
 
 def ss2d_fwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=True, workspace=None,
-             out=None):
+             out=None, keep_states=False):
     """Fused SS2D forward.  x, z: (batch, dim, H, W); delta: (batch, 4, dim, H*W);
-    A: (4, dim, N) fp32; B, C: (batch, 4, N, H*W); D, delta_bias: (4, dim) fp32."""
+    A: (4, dim, N) fp32; B, C: (batch, 4, N, H*W); D, delta_bias: (4, dim) fp32.  With
+    keep_states the given workspace keeps what ss2d_bwd(..., workspace_has_states=True) needs."""
     x, delta = _c(x), _c(delta)
     dev = _dev(x)
     B, C, z = _c(B), _c(C), _c(z)
@@ -274,7 +275,8 @@ def ss2d_fwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=
     a = SS2DFwdArgs(x=_ptr(x), delta=_ptr(delta), A=_ptr(A), Bm=_ptr(B), Cm=_ptr(C), Dskip=_ptr(D),
                     delta_bias=_ptr(delta_bias), z=_ptr(z), out=_ptr(out), workspace=_ptr(ws),
                     workspace_bytes=ws.numel() * ws.element_size(), batch=batch, dim=dim, height=H, width=W,
-                    dstate=N, dtype=_dtype_code(x.dtype), delta_softplus=int(bool(delta_softplus)))
+                    dstate=N, dtype=_dtype_code(x.dtype), delta_softplus=int(bool(delta_softplus)),
+                    keep_states=int(bool(keep_states)))
     _check(lib().ss2d_fwd(ctypes.byref(a), _stream(dev)), "ss2d_fwd")
     return out
 
@@ -284,7 +286,7 @@ class SS2DForwardPlan:
     repeated launches (benchmarks, stage timing) cost one ctypes call each."""
 
     def __init__(self, x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=True, workspace=None,
-                 out=None):
+                 out=None, keep_states=False):
         x, delta = _c(x), _c(delta)
         self.device = _dev(x)
         B, C, z = _c(B), _c(C), _c(z)
@@ -301,7 +303,7 @@ class SS2DForwardPlan:
                                 workspace=_ptr(self.workspace),
                                 workspace_bytes=self.workspace.numel() * self.workspace.element_size(),
                                 batch=batch, dim=dim, height=H, width=W, dstate=N, dtype=_dtype_code(x.dtype),
-                                delta_softplus=int(bool(delta_softplus)))
+                                delta_softplus=int(bool(delta_softplus)), keep_states=int(bool(keep_states)))
 
     def run(self):
         _check(lib().ss2d_fwd(ctypes.byref(self.args), _stream(self.device)), "ss2d_fwd")
@@ -313,8 +315,10 @@ class SS2DForwardPlan:
 
 
 def ss2d_bwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, dout=None, delta_softplus=True,
-             workspace=None):
-    """Backward of ss2d_fwd; returns a dict of gradients (None for absent inputs)."""
+             workspace=None, workspace_has_states=False):
+    """Backward of ss2d_fwd; returns a dict of gradients (None for absent inputs).  With
+    workspace_has_states, `workspace` must be the one a forward with keep_states=True used for
+    the same inputs (the forward is then not recomputed)."""
     x, delta, dout = _c(x), _c(delta), _c(dout)
     dev = _dev(x)
     B, C, z = _c(B), _c(C), _c(z)
@@ -335,7 +339,7 @@ def ss2d_bwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, dout=None, delt
                     dA=_ptr(dA), dBm=_ptr(dB), dCm=_ptr(dC), dDskip=_ptr(dD), ddelta_bias=_ptr(dbias), dz=_ptr(dz),
                     workspace=_ptr(ws), workspace_bytes=ws.numel() * ws.element_size(), batch=batch, dim=dim,
                     height=H, width=W, dstate=N, dtype=_dtype_code(x.dtype),
-                    delta_softplus=int(bool(delta_softplus)))
+                    delta_softplus=int(bool(delta_softplus)), workspace_has_states=int(bool(workspace_has_states)))
     _check(lib().ss2d_bwd(ctypes.byref(a), _stream(dev)), "ss2d_bwd")
     return {"dx": dx, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "ddelta_bias": dbias, "dz": dz}
 

@@ -85,6 +85,26 @@ struct GateBwdArgs {
 };
 hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t s);
 
+// The SS2D gate backward fused with the merge that it needs (z present): per pixel
+//   M  = (((r0 + r1) + r2) + r3) + Dsum * x    (the fp32 pre-gate merge, as in the forward)
+//   dz = dout * M * silu'(z),  dM = dout * silu(z)  (fp32 grid, and its per-plane transpose dMT)
+// One workgroup per plane when the plane's two column-major routes and dM fit in LDS; else the
+// merge writes M to `merged` (fp32 scratch) and the gate kernel reads it.
+struct MergeGateArgs {
+  const float* routes;  // (batch, 4, C, L) fp32, route order
+  const void* x;        // grid dtype (skip input, with Dskip)
+  const float* Dskip;   // (4, C) or null
+  const void* z;        // grid dtype
+  const void* dout;     // grid dtype
+  void* dz;             // grid dtype
+  float* dM;            // (batch, C, L) fp32 grid order
+  float* dMT;           // (batch, C, L) fp32 column-major order
+  float* merged;        // (batch, C, L) fp32 scratch for the two-kernel fallback
+  int64_t batch, C, H, W;
+  int dtype;
+};
+hipError_t launch_merge_gate_bwd(const MergeGateArgs& a, hipStream_t s);
+
 // Writes n fp32 zeros (a kernel, so that graph capture records no memset node).
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 

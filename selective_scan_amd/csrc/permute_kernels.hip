@@ -284,6 +284,80 @@ __global__ __launch_bounds__(kPlaneThreads) void merge_plane_kernel(MergeArgs a)
   }
 }
 
+// The gate backward fused with its merge (see MergeGateArgs), one plane per workgroup.  LDS:
+// routes 1 and 3 transposed to [w][h] (as in the merge), and dM as [h][w] for the dMT write.
+template <typename T>
+__global__ __launch_bounds__(kPlaneThreads) void merge_gate_bwd_plane_kernel(MergeGateArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int H = int(a.H), Wd = int(a.W);
+  const int64_t L = int64_t(H) * Wd;
+  const int ldc = H + 1, ldr = Wd + 1;
+  float* t1 = reinterpret_cast<float*>(smem);
+  float* t3 = t1 + int64_t(Wd) * ldc;
+  float* tm = t3 + int64_t(Wd) * ldc;  // [h][w]
+  const int64_t plane = int64_t(blockIdx.x);
+  const int64_t b = plane / a.C, c = plane % a.C;
+  const float* r0 = a.routes + (b * 4 * a.C + c) * L;
+  const float* r1 = r0 + a.C * L;
+  const float* r2 = r1 + a.C * L;
+  const float* r3 = r2 + a.C * L;
+  for (int64_t t = 4 * int64_t(threadIdx.x); t < L; t += 4 * kPlaneThreads) {
+    const float4 v1 = *reinterpret_cast<const float4*>(r1 + t);
+    const float4 v3 = *reinterpret_cast<const float4*>(r3 + (L - 4 - t));
+    const float a1[4] = {v1.x, v1.y, v1.z, v1.w};
+    const float a3[4] = {v3.w, v3.z, v3.y, v3.x};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t q = t + j;
+      const int w = int(q / H), h = int(q % H);
+      t1[w * ldc + h] = a1[j];
+      t3[w * ldc + h] = a3[j];
+    }
+  }
+  __syncthreads();
+  float dsum = 0.0f;
+  if (a.Dskip) dsum = ((a.Dskip[c] + a.Dskip[a.C + c]) + a.Dskip[2 * a.C + c]) + a.Dskip[3 * a.C + c];
+  const T* xg = static_cast<const T*>(a.x) + plane * L;
+  const T* zg = static_cast<const T*>(a.z) + plane * L;
+  const T* gg = static_cast<const T*>(a.dout) + plane * L;
+  T* dzg = static_cast<T*>(a.dz) + plane * L;
+  float* dmg = a.dM + plane * L;
+  for (int64_t p = 4 * int64_t(threadIdx.x); p < L; p += 4 * kPlaneThreads) {
+    const float4 v0 = *reinterpret_cast<const float4*>(r0 + p);
+    const float4 v2 = *reinterpret_cast<const float4*>(r2 + (L - 4 - p));
+    const float a0[4] = {v0.x, v0.y, v0.z, v0.w};
+    const float a2[4] = {v2.w, v2.z, v2.y, v2.x};
+    const float4 xv = Elem<T>::load4(xg, p), zv = Elem<T>::load4(zg, p), gv = Elem<T>::load4(gg, p);
+    const float xs[4] = {xv.x, xv.y, xv.z, xv.w}, zs[4] = {zv.x, zv.y, zv.z, zv.w}, gs[4] = {gv.x, gv.y, gv.z, gv.w};
+    float dz[4], dm[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = int((p + j) / Wd), w = int((p + j) % Wd);
+      float m = a0[j] + t1[w * ldc + h];
+      m = m + a2[j];
+      m = m + t3[w * ldc + h];
+      if (a.Dskip && a.x) m = fmaf(dsum, xs[j], m);
+      const float sz = sigmoid(zs[j]);
+      dm[j] = gs[j] * zs[j] * sz;
+      dz[j] = gs[j] * m * sz * (1.0f + zs[j] * (1.0f - sz));
+      tm[h * ldr + w] = dm[j];
+    }
+    *reinterpret_cast<float4*>(dmg + p) = make_float4(dm[0], dm[1], dm[2], dm[3]);
+    Elem<T>::store4(dzg, p, make_float4(dz[0], dz[1], dz[2], dz[3]));
+  }
+  __syncthreads();
+  float* dmt = a.dMT + plane * L;
+  for (int64_t t = 4 * int64_t(threadIdx.x); t < L; t += 4 * kPlaneThreads) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int w = int((t + j) / H), h = int((t + j) % H);
+      v[j] = tm[h * ldr + w];
+    }
+    *reinterpret_cast<float4*>(dmt + t) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Two-direction merge: one thread per element of the (batch, C, L) output; direction 1 is read
@@ -426,6 +500,51 @@ hipError_t launch_transpose(const void* x, void* xT, int64_t batch, int64_t C, i
   o.out[1] = xT;
   o.batch_stride = C * H * W;
   return launch_route_scatter(x, o, batch, C, H, W, elem_bytes, s);
+}
+
+hipError_t launch_merge_gate_bwd(const MergeGateArgs& a, hipStream_t s) {
+  const int64_t L = a.H * a.W;
+  const size_t lds = (size_t(2) * size_t(a.W) * size_t(a.H + 1) + size_t(a.H) * size_t(a.W + 1)) * 4;
+  const uintptr_t io = reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.z) |
+                       reinterpret_cast<uintptr_t>(a.dout) | reinterpret_cast<uintptr_t>(a.dz);
+  if (a.z && lds <= 64 * 1024 && L % 4 == 0 && a.batch * a.C > 0 && aligned16(a.routes) && aligned16(a.dM) &&
+      aligned16(a.dMT) && (io & (a.dtype == 0 ? 15 : 7)) == 0) {
+    const dim3 g{uint32_t(a.batch * a.C)}, b{kPlaneThreads};
+    if (a.dtype == 0)
+      merge_gate_bwd_plane_kernel<float><<<g, b, lds, s>>>(a);
+    else
+      merge_gate_bwd_plane_kernel<bf16><<<g, b, lds, s>>>(a);
+    return hipGetLastError();
+  }
+  // two kernels: the pre-gate merge into `merged` (only needed with a gate), then the gate
+  if (a.z) {
+    MergeArgs m{};
+    m.routes = a.routes;
+    m.routes_f32 = 1;
+    m.x = a.x;
+    m.Dskip = a.Dskip;
+    m.merged_f32 = a.merged;
+    m.batch = a.batch;
+    m.C = a.C;
+    m.H = a.H;
+    m.W = a.W;
+    m.dtype = a.dtype;
+    const hipError_t e = launch_merge(m, s);
+    if (e != hipSuccess) return e;
+  }
+  GateBwdArgs g{};
+  g.merged = a.merged;
+  g.z = a.z;
+  g.dout = a.dout;
+  g.dM = a.dM;
+  g.dMT = a.dMT;
+  g.dz = a.dz;
+  g.batch = a.batch;
+  g.C = a.C;
+  g.H = a.H;
+  g.W = a.W;
+  g.dtype = a.dtype;
+  return launch_gate_bwd(g, s);
 }
 
 hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t s) {

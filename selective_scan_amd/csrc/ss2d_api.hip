@@ -409,7 +409,7 @@ int ss2d_fwd(const ss2d_fwd_args* a, hipStream_t stream) {
   int st = validate_ss2d_fwd(a, &lay, &empty);
   if (st != SS2D_OK || empty) return st;
   st = ss2d_transpose_stage(a, lay, stream);
-  if (st == SS2D_OK) st = ss2d_scan_stage(a, lay, false, stream);
+  if (st == SS2D_OK) st = ss2d_scan_stage(a, lay, a->keep_states != 0, stream);
   if (st == SS2D_OK) st = ss2d_merge_stage(a, lay, nullptr, stream);
   return st;
 }
@@ -421,7 +421,7 @@ int ss2d_fwd_stage(const ss2d_fwd_args* a, int stage, hipStream_t stream) {
   int st = validate_ss2d_fwd(a, &lay, &empty);
   if (st != SS2D_OK || empty) return st;
   if (stage == SS2D_STAGE_TRANSPOSE) return ss2d_transpose_stage(a, lay, stream);
-  if (stage == SS2D_STAGE_SCAN) return ss2d_scan_stage(a, lay, false, stream);
+  if (stage == SS2D_STAGE_SCAN) return ss2d_scan_stage(a, lay, a->keep_states != 0, stream);
   return ss2d_merge_stage(a, lay, nullptr, stream);
 }
 
@@ -605,46 +605,48 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
     return SS2D_ERR_INVALID_ARGUMENT;
   const int64_t L = a->height * a->width;
 
-  // forward again: transposed x, route outputs and checkpoint states, merged pre-gate map
-  ss2d_fwd_args f{};
-  f.x = a->x;
-  f.delta = a->delta;
-  f.A = a->A;
-  f.Bm = a->Bm;
-  f.Cm = a->Cm;
-  f.Dskip = a->Dskip;
-  f.delta_bias = a->delta_bias;
-  f.z = nullptr;
-  f.out = nullptr;
-  f.workspace = a->workspace;
-  f.workspace_bytes = a->workspace_bytes;
-  f.batch = a->batch;
-  f.dim = a->dim;
-  f.height = a->height;
-  f.width = a->width;
-  f.dstate = a->dstate;
-  f.dtype = a->dtype;
-  f.delta_softplus = a->delta_softplus;
-  st = ss2d_transpose_stage(&f, lay, stream);
-  if (st == SS2D_OK) st = ss2d_scan_stage(&f, lay, true, stream);
-  float* merged = reinterpret_cast<float*>(at(a->workspace, lay.off_merged));
-  if (st == SS2D_OK) st = ss2d_merge_stage(&f, lay, merged, stream);
-  if (st != SS2D_OK) return st;
+  // forward again (unless the workspace holds it): transposed x, route outputs, checkpoint states
+  if (!a->workspace_has_states) {
+    ss2d_fwd_args f{};
+    f.x = a->x;
+    f.delta = a->delta;
+    f.A = a->A;
+    f.Bm = a->Bm;
+    f.Cm = a->Cm;
+    f.Dskip = a->Dskip;
+    f.delta_bias = a->delta_bias;
+    f.workspace = a->workspace;
+    f.workspace_bytes = a->workspace_bytes;
+    f.batch = a->batch;
+    f.dim = a->dim;
+    f.height = a->height;
+    f.width = a->width;
+    f.dstate = a->dstate;
+    f.dtype = a->dtype;
+    f.delta_softplus = a->delta_softplus;
+    st = ss2d_transpose_stage(&f, lay, stream);
+    if (st == SS2D_OK) st = ss2d_scan_stage(&f, lay, true, stream);
+    if (st != SS2D_OK) return st;
+  }
 
-  // gate: dM = dout * silu(z) (grid and transposed), dz = dout * M * silu'(z)
-  GateBwdArgs gb{};
-  gb.merged = merged;
+  // gate (with the pre-gate merge it needs): dz, and dM = dout * silu(z) in grid and
+  // transposed order
+  MergeGateArgs gb{};
+  gb.routes = reinterpret_cast<const float*>(at(a->workspace, lay.off_ys));
+  gb.x = a->x;
+  gb.Dskip = a->Dskip;
   gb.z = a->z;
   gb.dout = a->dout;
+  gb.dz = a->dz;
   gb.dM = reinterpret_cast<float*>(at(a->workspace, lay.off_dM));
   gb.dMT = reinterpret_cast<float*>(at(a->workspace, lay.off_dMT));
-  gb.dz = a->dz;
+  gb.merged = reinterpret_cast<float*>(at(a->workspace, lay.off_merged));
   gb.batch = a->batch;
   gb.C = a->dim;
   gb.H = a->height;
   gb.W = a->width;
   gb.dtype = a->dtype;
-  if (launch_gate_bwd(gb, stream) != hipSuccess) return SS2D_ERR_HIP;
+  if (launch_merge_gate_bwd(gb, stream) != hipSuccess) return SS2D_ERR_HIP;
 
   // adjoint scans of the four routes; du (fp32, route order) reuses the route-output region
   ScanBwdParams bp{};

@@ -111,6 +111,29 @@ def test_ss2d_bwd(case):
         assert e <= _tol(dtype), (k, e)
 
 
+@pytest.mark.parametrize("case", [(1, 8, 8, 16, 4, "f32", True), (2, 7, 9, 20, 16, "f32", True),
+                                  (1, 3, 40, 64, 8, "bf16", True), (1, 64, 64, 64, 16, "f32", True),
+                                  (2, 14, 14, 70, 16, "f32", False)], ids=str)
+def test_ss2d_bwd_reuses_forward_states(case):
+    """A training forward (keep_states) then the backward on its workspace: the oracle's gradients,
+    and bit for bit what the backward that recomputes the forward gives."""
+    batch, H, W, dim, N, dtype, z = case
+    dev, ref, dout, dout64 = _ss2d(batch, H, W, dim, N, dtype, z, seed=70 + H * W)
+    ws = torch.empty(ss.ss2d_workspace_bytes(batch, dim, H, W, N, dev["x"].dtype), dtype=torch.uint8, device="cuda")
+    out = ss.ss2d_fwd(**dev, workspace=ws, keep_states=True)
+    g = ss.ss2d_bwd(**dev, dout=dout, workspace=ws, workspace_has_states=True)
+    g2 = ss.ss2d_bwd(**dev, dout=dout)
+    assert torch.equal(out, ss.ss2d_fwd(**dev))
+    r = oracle.ss2d_bwd(**ref, dout=dout64)
+    for k in SS2D_GRADS:
+        if r[k] is None:
+            assert g[k] is None
+            continue
+        assert torch.equal(g[k], g2[k]), k
+        e = rel_err(to_f64(g[k]), r[k])
+        assert e <= _tol(dtype), (k, e)
+
+
 def test_ss2d_bwd_tiny_config():
     cfg = synth.CONFIGS[0]
     dev, ref, dout, dout64 = _ss2d(cfg.batch, cfg.height, cfg.width, cfg.dim, cfg.dstate, cfg.dtype, cfg.has_z,
