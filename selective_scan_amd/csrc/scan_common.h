@@ -106,6 +106,28 @@ __device__ __forceinline__ void load_row(RowTile<T, kLen>& tile, const T* row, i
     if (rev) tile.reverse();
     return;
   }
+  if constexpr (!kVec && sizeof(T) == 2 && kLen % 4 == 0) {
+    if (!rev && t0 + kLen <= t_end) {
+      // a whole bf16 tile at any 2-byte offset: the dwords from the 4-byte boundary at or below
+      // its first element, each output word shifted into place (v_alignbit by 0 or 16 bits);
+      // when the tile starts mid-dword its last element is fetched on its own, so that no load
+      // reaches past the tile
+      const uintptr_t addr = reinterpret_cast<uintptr_t>(row + t0);
+      const uint32_t odd = uint32_t(addr >> 1) & 1u;
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(addr - 2 * odd);
+      uint32_t d[kLen / 2 + 1];
+#pragma unroll
+      for (int j = 0; j < kLen / 2; ++j) d[j] = w[j];
+      d[kLen / 2] = odd ? uint32_t(row[t0 + kLen - 1].bits) : 0u;
+#pragma unroll
+      for (int j = 0; j < kLen / 4; ++j) {
+        const uint32_t lo = __builtin_amdgcn_alignbit(d[2 * j + 1], d[2 * j], 16u * odd);
+        const uint32_t hi = __builtin_amdgcn_alignbit(d[2 * j + 2], d[2 * j + 1], 16u * odd);
+        tile.v[j] = make_uint2(lo, hi);
+      }
+      return;
+    }
+  }
   tile.fill(pad_bits);
   if (kVec) {
     if (!rev) {
@@ -245,6 +267,15 @@ __device__ __forceinline__ void store_state(float* dst, const float* h, int coun
 // Steps at or past t_end read as 0.  Vector loads need L % 4 == 0, t % 4 == 0 and kSeg % 4 == 0.
 template <typename T, bool kVec, int kSeg>
 __device__ __forceinline__ void load_seg(float* out, const T* row, int64_t t, int64_t t_end, int64_t L, bool rev) {
+  if constexpr (!kVec && sizeof(T) == 2 && kSeg % 4 == 0) {
+    if (!rev && t + kSeg <= t_end) {  // whole bf16 segment at any 2-byte offset (as in load_row)
+      RowTile<T, kSeg> tile;
+      load_row<T, false, kSeg>(tile, row, t, t_end, L, false);
+#pragma unroll
+      for (int i = 0; i < kSeg; ++i) out[i] = tile.get(i);
+      return;
+    }
+  }
   if (kVec && kSeg % 4 == 0) {
 #pragma unroll
     for (int j = 0; j < kSeg / 4; ++j) {
