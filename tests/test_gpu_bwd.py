@@ -159,3 +159,48 @@ def test_ss2d_bwd_highres_config_full():
     for k in SS2D_GRADS:
         e = rel_err(to_f64(g[k]), r[k])
         assert e <= TOL_GRAD, (k, e)
+
+
+def test_ss2d_bwd_stage1_full_size_training_path():
+    """Stage-1 (B=128, 56x56, D=192, N=16, bf16) at full size in the benchmark's training launch
+    configuration (forward with keep_states, backward on its states).  Checked on what the oracle
+    can compute from slices: per-element gradients (dx, ddelta, dz) on sampled (image, channel)
+    planes; dA, dD, ddelta_bias of sampled channels from all images; dB, dC of a sampled image
+    from all its channels."""
+    cfg = synth.CONFIGS[1]
+    inp = synth.make_config_inputs(cfg, with_dout=True)
+    dt = cfg.dtype
+    dev = dict(x=to_dev(inp["x"], dt), delta=to_dev(inp["delta"], dt), A=to_dev(inp["A"], "f32"),
+               B=to_dev(inp["B"], dt), C=to_dev(inp["C"], dt), D=to_dev(inp["D"], "f32"),
+               delta_bias=to_dev(inp["delta_bias"], "f32"), z=to_dev(inp["z"], dt))
+    ws = torch.empty(ss.ss2d_workspace_bytes(cfg.batch, cfg.dim, cfg.height, cfg.width, cfg.dstate, dev["x"].dtype),
+                     dtype=torch.uint8, device="cuda")
+    ss.ss2d_fwd(**dev, workspace=ws, keep_states=True)
+    g = ss.ss2d_bwd(**dev, dout=to_dev(inp["dout"], dt), workspace=ws, workspace_has_states=True)
+    torch.cuda.synchronize()
+    f = lambda a: synth.storage_to_f64(a, dt)
+
+    def ref(bs, ds):
+        return oracle.ss2d_bwd(x=f(inp["x"][bs][:, ds]), delta=f(inp["delta"][bs][:, :, ds]),
+                               A=inp["A"][:, ds].astype(np.float64), B=f(inp["B"][bs]), C=f(inp["C"][bs]),
+                               D=inp["D"][:, ds].astype(np.float64), delta_bias=inp["delta_bias"][:, ds].astype(np.float64),
+                               z=f(inp["z"][bs][:, ds]), dout=f(inp["dout"][bs][:, ds]))
+
+    rng = np.random.default_rng(21)
+    tol = TOL["bf16"]
+    for b, d in [(0, 0), (cfg.batch - 1, cfg.dim - 1), (int(rng.integers(cfg.batch)), int(rng.integers(cfg.dim)))]:
+        r = ref(slice(b, b + 1), slice(d, d + 1))
+        for k, gk in (("dx", g["dx"][b:b + 1, d:d + 1]), ("ddelta", g["ddelta"][b:b + 1, :, d:d + 1]),
+                      ("dz", g["dz"][b:b + 1, d:d + 1])):
+            e = rel_err(to_f64(gk), r[k])
+            assert e <= tol, (k, b, d, e)
+    d = int(rng.integers(cfg.dim))
+    r = ref(slice(0, cfg.batch), slice(d, d + 1))
+    for k, gk in (("dA", g["dA"][:, d:d + 1]), ("dD", g["dD"][:, d:d + 1]), ("ddelta_bias", g["ddelta_bias"][:, d:d + 1])):
+        e = rel_err(to_f64(gk), r[k])
+        assert e <= tol, (k, d, e)
+    b = int(rng.integers(cfg.batch))
+    r = ref(slice(b, b + 1), slice(0, cfg.dim))
+    for k in ("dB", "dC"):
+        e = rel_err(to_f64(g[k][b:b + 1]), r[k])
+        assert e <= tol, (k, b, e)
