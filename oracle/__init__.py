@@ -12,6 +12,7 @@ Functions (see ``oracle/ss2d_oracle.py`` for the citations):
   ss2d_fwd, ss2d_bwd             cross-scan -> selective scan -> cross-merge (+ gate)
   vim_bidir_fwd, vim_bidir_bwd   Vision Mamba's two-direction scan (oracle/vim_oracle.py)
   ss_step                        one recurrent step from a carried state (oracle/step_oracle.py)
+  dwconv, ss2d_front_fwd/_bwd    SS2D after a depthwise conv + SiLU front (oracle/front_oracle.py)
 
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against
 closed forms, invariants, a brute-force semiseparable-matrix formulation and
@@ -28,5 +29,6 @@ from .ss2d_oracle import (  # noqa: F401
     ss_bwd,
     ss_fwd,
 )
+from .front_oracle import dwconv, ss2d_front_bwd, ss2d_front_fwd  # noqa: F401
 from .step_oracle import ss_step  # noqa: F401
 from .vim_oracle import vim_bidir_bwd, vim_bidir_fwd  # noqa: F401
