@@ -12,7 +12,8 @@ device copy timed in the same run, the roofline of the dominant kernel (the rout
 kernel, timed live with HIP events on the stream it is launched on) and the fp64 CPU
 oracle timed on this host on a bounded sample of the same workload.  `--workload`
 selects one of the other shapes (0-4 SS2D, 5 the Vision Mamba bidirectional scan at
-Vim-Tiny size); `--bwd` adds the fused backward to each step.
+Vim-Tiny size); `--bwd` adds the fused backward to each step; `--front K` puts the
+input front (depthwise K x K convolution + SiLU) ahead of the SS2D routes.
 
 When one input/output set is smaller than the 256 MB last-level cache (MALL) several
 times over, the steps rotate over independent copies so that no step re-reads what the
@@ -57,9 +58,20 @@ def parse():
     ap.add_argument("--workload", type=int, default=1,
                     help="index into synth.CONFIGS + synth.VIM_CONFIGS (default 1: SS2D stage-1; 5: Vim-Tiny)")
     ap.add_argument("--bwd", action="store_true", help="time forward + backward per step")
+    ap.add_argument("--front", type=int, default=0,
+                    help="SS2D only: K > 0 adds the input front (depthwise K x K convolution + SiLU)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time for the sample")
     return ap.parse_args()
+
+
+def front_bytes(cfg, bwd=False):
+    """The input front's own minimum: the forward reads x and writes the front output in grid
+    and column-major order; the backward reads x and the fp32 gradient of the front output and
+    writes dx (the filter partial sums are a few bytes per 32 x 32 tile)."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    grid = cfg.batch * cfg.dim * cfg.seqlen
+    return e * 3 * grid + ((2 * e + 4) * grid if bwd else 0)
 
 
 def algorithmic_bytes(cfg, bwd=False):
@@ -116,7 +128,7 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(cfg, inp, target_s, bwd=False):
+def cpu_baseline(cfg, inp, target_s, bwd=False, front=None):
     """The fp64 oracle (as it stands) on the first images of the same batch (forward, or
     forward + backward when the GPU step includes the backward)."""
     import oracle
@@ -141,9 +153,15 @@ def cpu_baseline(cfg, inp, target_s, bwd=False):
         args = (sl(inp["x"]), sl(inp["delta"]), inp["A"].astype(np.float64), sl(inp["B"]), sl(inp["C"]),
                 inp["D"].astype(np.float64), inp["delta_bias"].astype(np.float64), sl(inp["z"]))
         t0 = time.perf_counter()
-        oracle.ss2d_fwd(*args)
-        if bwd:
-            oracle.ss2d_bwd(*args, dout=sl(inp["dout"]))
+        if front is not None:
+            fa = (args[0], front["conv_w"].astype(np.float64), front["conv_b"].astype(np.float64)) + args[1:]
+            oracle.ss2d_front_fwd(*fa)
+            if bwd:
+                oracle.ss2d_front_bwd(*fa, dout=sl(inp["dout"]))
+        else:
+            oracle.ss2d_fwd(*args)
+            if bwd:
+                oracle.ss2d_bwd(*args, dout=sl(inp["dout"]))
         return time.perf_counter() - t0
 
     t1 = run(1)
@@ -155,18 +173,23 @@ def cpu_baseline(cfg, inp, target_s, bwd=False):
     return {"value": elems / t, "unit": "elements/s", "cores": threads, "kind": "oracle",
             "sample": f"first {nb} of {cfg.batch} {'sequences' if vim else 'images'} (all {cfg.dim} channels, "
                       f"{routes} {'directions' if vim else 'routes'}, L={cfg.seqlen}, N={cfg.dstate}), fp64 C "
-                      f"oracle with OpenMP over rows, {'forward + backward' if bwd else 'forward'}, {t:.2f} s wall",
+                      f"oracle with OpenMP over rows{', with the input front' if front is not None else ''}, "
+                      f"{'forward + backward' if bwd else 'forward'}, {t:.2f} s wall",
             "cpu_model": cpu_model()}
 
 
-def config_record(cfg, vim, bwd, n_sets):
+def config_record(cfg, vim, bwd, n_sets, front_k=0):
     if vim:
         return {"workload": ("vim_bidir_fwd+bwd " if bwd else "vim_bidir_fwd ") + cfg.name, "batch": cfg.batch,
                 "seqlen": cfg.seqlen, "directions": 2, "dim": cfg.dim, "dstate": cfg.dstate, "gate_z": cfg.has_z,
                 "io_sets_rotated": n_sets}
-    return {"workload": ("ss2d_fwd+bwd " if bwd else "ss2d_fwd ") + cfg.name, "batch": cfg.batch,
-            "height": cfg.height, "width": cfg.width, "routes": 4, "dim": cfg.dim, "dstate": cfg.dstate,
-            "gate_z": cfg.has_z, "io_sets_rotated": n_sets}
+    rec = {"workload": ("ss2d_fwd+bwd " if bwd else "ss2d_fwd ") + cfg.name, "batch": cfg.batch,
+           "height": cfg.height, "width": cfg.width, "routes": 4, "dim": cfg.dim, "dstate": cfg.dstate,
+           "gate_z": cfg.has_z, "io_sets_rotated": n_sets}
+    if front_k:
+        rec["workload"] = rec["workload"].replace("ss2d_fwd", f"ss2d_fwd(front dwconv{front_k}x{front_k}+silu)", 1)
+        rec["front_conv_k"] = front_k
+    return rec
 
 
 def stats(ms):
@@ -188,7 +211,11 @@ def main():
     workloads = list(synth.CONFIGS) + list(synth.VIM_CONFIGS)
     cfg = workloads[args.workload]
     vim = getattr(cfg, "kind", "ss2d") == "vim"
+    if args.front and vim:
+        print("--front applies to the SS2D workloads only", file=sys.stderr)
+        sys.exit(2)
     inp = (synth.make_vim_config_inputs if vim else synth.make_config_inputs)(cfg, with_dout=args.bwd)
+    front = synth.make_front_params(cfg.dim, args.front, seed_base=cfg.index) if args.front else None
 
     def dev(a, dtype):
         if a is None:
@@ -201,6 +228,8 @@ def main():
     d0 = {first: dev(inp[first], cfg.dtype), "delta": dev(inp["delta"], cfg.dtype), "A": dev(inp["A"], "f32"),
           "B": dev(inp["B"], cfg.dtype), "C": dev(inp["C"], cfg.dtype), "D": dev(inp["D"], "f32"),
           "delta_bias": dev(inp["delta_bias"], "f32"), "z": dev(inp["z"], cfg.dtype) if cfg.has_z else None}
+    if front is not None:
+        d0.update(conv_w=dev(front["conv_w"], "f32"), conv_b=dev(front["conv_b"], "f32"))
     dout0 = dev(inp["dout"], cfg.dtype) if args.bwd else None
     # with --bwd a step is a training step: for SS2D the forward keeps its checkpoint states and
     # the backward runs on them (the Vim backward recomputes its forward)
@@ -251,6 +280,7 @@ def main():
     ms = t_start.elapsed_time(t_end) / args.steps
     step_ms = [e[0].elapsed_time(e[3]) for e in evs]
     scan_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    stage0_ms = [e[0].elapsed_time(e[1]) for e in evs]
 
     # a plain device copy of known size in the same run: the practical HBM ceiling (its three
     # dispatches also calibrate the byte counters of a profiler run of this program)
@@ -267,7 +297,7 @@ def main():
     copy_gbps = 2 * COPY_BYTES / (np.median([a.elapsed_time(b) for a, b in copy_ev]) * 1e-3) / 1e9
 
     elements = cfg.elements
-    step_bytes = algorithmic_bytes(cfg, args.bwd)
+    step_bytes = algorithmic_bytes(cfg, args.bwd) + (front_bytes(cfg, args.bwd) if front is not None else 0)
     flops = elements * cfg.dstate * FLOPS_PER_STATE_STEP
     scan_mean = float(np.mean(scan_ms))
     achieved_tflops = flops / (scan_mean * 1e-3) / 1e12
@@ -286,7 +316,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) inputs, S4D-real A, inverse-softplus dt bias)",
-        "config": config_record(cfg, vim, args.bwd, n_sets),
+        "config": config_record(cfg, vim, args.bwd, n_sets, args.front),
         "step_ms": stats(step_ms),
         "hbm": {"algorithmic_bytes_per_step": step_bytes,
                 "achieved_GBps": hbm_gbps,
@@ -300,8 +330,15 @@ def main():
                      "mix_peak": MIX_PEAK_TFLOPS, "frac_of_mix_peak": achieved_tflops / MIX_PEAK_TFLOPS,
                      "ms_per_launch": scan_mean, "launch_ms": stats(scan_ms), "flops_per_launch": flops},
     }
+    if front is not None:
+        fb = front_bytes(cfg, False)
+        f_ms = float(np.mean(stage0_ms))
+        res["front"] = {"kernel": "front_fwd_kernel (stage 0)", "bound": "hbm", "ms_per_launch": f_ms,
+                        "launch_ms": stats(stage0_ms), "algorithmic_bytes": fb,
+                        "achieved_GBps": fb / (f_ms * 1e-3) / 1e9, "peak_GBps": HBM_PEAK_GBPS,
+                        "frac": fb / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds, args.bwd)
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds, args.bwd, front)
     print(json.dumps(res))
 
 

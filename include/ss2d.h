@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SS2D_ABI_VERSION 4
+#define SS2D_ABI_VERSION 5
 
 /* Status codes returned by every entry point. */
 enum {
@@ -230,6 +230,14 @@ typedef struct ss2d_fwd_args {
   int delta_softplus;
   int keep_states;         /* nonzero: the workspace also keeps the checkpoint states, so that
                               ss2d_bwd can run with workspace_has_states (a training forward) */
+  /* Optional input front [S6 page, section 1: in the VSS block the SS2D input passes through a
+   * depthwise convolution and SiLU]: with conv_w != NULL the four routes scan
+   *   u = silu(pre),  pre[b,c,h,w] = conv_b[c] + sum_{i,j} conv_w[c,i,j] x[b,c,h+i-r,w+j-r]
+   * (r = conv_k / 2, zero outside the map; conv_k odd, 1..7), computed once per pixel and kept
+   * in dtype; the skip term then uses u as well. */
+  const float* conv_w;     /* (dim, conv_k, conv_k) fp32, or NULL: no front (u = x) */
+  const float* conv_b;     /* (dim) fp32, may be NULL */
+  int conv_k;
 } ss2d_fwd_args;
 
 int ss2d_fwd(const ss2d_fwd_args* args, hipStream_t stream);
@@ -278,6 +286,14 @@ typedef struct ss2d_bwd_args {
   int dtype;
   int delta_softplus;
   int workspace_has_states;
+  /* the input front, as in ss2d_fwd_args; with conv_w != NULL dx is the gradient w.r.t. the
+   * input of the convolution, and dconv_w (dim, conv_k, conv_k) and dconv_b (dim, iff conv_b)
+   * receive the filter's gradients (fp32, summed over images and pixels, overwritten) */
+  const float* conv_w;
+  const float* conv_b;
+  int conv_k;
+  float* dconv_w;
+  float* dconv_b;
 } ss2d_bwd_args;
 
 int ss2d_bwd(const ss2d_bwd_args* args, hipStream_t stream);

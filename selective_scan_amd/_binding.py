@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libss2d.so")
 
 SS2D_OK, SS2D_ERR_INVALID_ARGUMENT, SS2D_ERR_UNSUPPORTED, SS2D_ERR_HIP = 0, 1, 2, 3
 DTYPE_F32, DTYPE_BF16 = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -43,14 +43,16 @@ class SS2DFwdArgs(ctypes.Structure):
     _fields_ = [(n, _p) for n in ("x", "delta", "A", "Bm", "Cm", "Dskip", "delta_bias", "z", "out",
                                   "workspace")] + [
         ("workspace_bytes", _sz), ("batch", _i64), ("dim", _i64), ("height", _i64), ("width", _i64),
-        ("dstate", _i64), ("dtype", _int), ("delta_softplus", _int), ("keep_states", _int)]
+        ("dstate", _i64), ("dtype", _int), ("delta_softplus", _int), ("keep_states", _int),
+        ("conv_w", _p), ("conv_b", _p), ("conv_k", _int)]
 
 
 class SS2DBwdArgs(ctypes.Structure):
     _fields_ = [(n, _p) for n in ("x", "delta", "A", "Bm", "Cm", "Dskip", "delta_bias", "z", "dout", "dx",
                                   "ddelta", "dA", "dBm", "dCm", "dDskip", "ddelta_bias", "dz", "workspace")] + [
         ("workspace_bytes", _sz), ("batch", _i64), ("dim", _i64), ("height", _i64), ("width", _i64),
-        ("dstate", _i64), ("dtype", _int), ("delta_softplus", _int), ("workspace_has_states", _int)]
+        ("dstate", _i64), ("dtype", _int), ("delta_softplus", _int), ("workspace_has_states", _int),
+        ("conv_w", _p), ("conv_b", _p), ("conv_k", _int), ("dconv_w", _p), ("dconv_b", _p)]
 
 
 class SsStepArgs(ctypes.Structure):
@@ -256,17 +258,30 @@ def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dout=
     return {"du": du, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "dz": dz, "ddelta_bias": dbias}
 
 
+def _conv_k(conv_w, dim):
+    """Filter size of a depthwise filter given as (dim, k, k) or (dim, 1, k, k)."""
+    if conv_w is None:
+        return 0
+    k = int(conv_w.shape[-1])
+    if conv_w.dim() < 2 or conv_w.shape[-2] != k or conv_w.numel() != dim * k * k:
+        raise ValueError(f"conv_w must be (dim, k, k) for dim={dim}, got {tuple(conv_w.shape)}")
+    return k
+
+
 def ss2d_fwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=True, workspace=None,
-             out=None, keep_states=False):
+             out=None, keep_states=False, conv_w=None, conv_b=None):
     """Fused SS2D forward.  x, z: (batch, dim, H, W); delta: (batch, 4, dim, H*W);
     A: (4, dim, N) fp32; B, C: (batch, 4, N, H*W); D, delta_bias: (4, dim) fp32.  With
-    keep_states the given workspace keeps what ss2d_bwd(..., workspace_has_states=True) needs."""
+    keep_states the given workspace keeps what ss2d_bwd(..., workspace_has_states=True) needs.
+    conv_w (dim, k, k) and conv_b (dim,), fp32, add the input front: the routes scan
+    silu(depthwise_conv(x) + conv_b) instead of x."""
     x, delta = _c(x), _c(delta)
     dev = _dev(x)
     B, C, z = _c(B), _c(C), _c(z)
     A = _c(A, torch.float32)
     D = _c(D, torch.float32)
     delta_bias = _c(delta_bias, torch.float32)
+    conv_w, conv_b = _c(conv_w, torch.float32), _c(conv_b, torch.float32)
     batch, dim, H, W = x.shape
     N = A.shape[-1]
     if out is None:
@@ -276,7 +291,8 @@ def ss2d_fwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=
                     delta_bias=_ptr(delta_bias), z=_ptr(z), out=_ptr(out), workspace=_ptr(ws),
                     workspace_bytes=ws.numel() * ws.element_size(), batch=batch, dim=dim, height=H, width=W,
                     dstate=N, dtype=_dtype_code(x.dtype), delta_softplus=int(bool(delta_softplus)),
-                    keep_states=int(bool(keep_states)))
+                    keep_states=int(bool(keep_states)), conv_w=_ptr(conv_w), conv_b=_ptr(conv_b),
+                    conv_k=_conv_k(conv_w, dim))
     _check(lib().ss2d_fwd(ctypes.byref(a), _stream(dev)), "ss2d_fwd")
     return out
 
@@ -286,24 +302,26 @@ class SS2DForwardPlan:
     repeated launches (benchmarks, stage timing) cost one ctypes call each."""
 
     def __init__(self, x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=True, workspace=None,
-                 out=None, keep_states=False):
+                 out=None, keep_states=False, conv_w=None, conv_b=None):
         x, delta = _c(x), _c(delta)
         self.device = _dev(x)
         B, C, z = _c(B), _c(C), _c(z)
         A = _c(A, torch.float32)
         D = _c(D, torch.float32)
         delta_bias = _c(delta_bias, torch.float32)
+        conv_w, conv_b = _c(conv_w, torch.float32), _c(conv_b, torch.float32)
         batch, dim, H, W = x.shape
         N = A.shape[-1]
         self.out = torch.empty_like(x) if out is None else out
         self.workspace = _workspace(ss2d_workspace_bytes(batch, dim, H, W, N, x.dtype), self.device, workspace)
-        self._keep = (x, delta, A, B, C, D, delta_bias, z)
+        self._keep = (x, delta, A, B, C, D, delta_bias, z, conv_w, conv_b)
         self.args = SS2DFwdArgs(x=_ptr(x), delta=_ptr(delta), A=_ptr(A), Bm=_ptr(B), Cm=_ptr(C), Dskip=_ptr(D),
                                 delta_bias=_ptr(delta_bias), z=_ptr(z), out=_ptr(self.out),
                                 workspace=_ptr(self.workspace),
                                 workspace_bytes=self.workspace.numel() * self.workspace.element_size(),
                                 batch=batch, dim=dim, height=H, width=W, dstate=N, dtype=_dtype_code(x.dtype),
-                                delta_softplus=int(bool(delta_softplus)), keep_states=int(bool(keep_states)))
+                                delta_softplus=int(bool(delta_softplus)), keep_states=int(bool(keep_states)),
+                                conv_w=_ptr(conv_w), conv_b=_ptr(conv_b), conv_k=_conv_k(conv_w, dim))
 
     def run(self):
         _check(lib().ss2d_fwd(ctypes.byref(self.args), _stream(self.device)), "ss2d_fwd")
@@ -315,16 +333,21 @@ class SS2DForwardPlan:
 
 
 def ss2d_bwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, dout=None, delta_softplus=True,
-             workspace=None, workspace_has_states=False):
+             workspace=None, workspace_has_states=False, conv_w=None, conv_b=None):
     """Backward of ss2d_fwd; returns a dict of gradients (None for absent inputs).  With
     workspace_has_states, `workspace` must be the one a forward with keep_states=True used for
-    the same inputs (the forward is then not recomputed)."""
+    the same inputs (the forward is then not recomputed).  With the input front (conv_w,
+    conv_b) dx is the gradient w.r.t. the convolution's input and the dict also holds
+    dconv_w and dconv_b."""
     x, delta, dout = _c(x), _c(delta), _c(dout)
     dev = _dev(x)
     B, C, z = _c(B), _c(C), _c(z)
     A = _c(A, torch.float32)
     D = _c(D, torch.float32)
     delta_bias = _c(delta_bias, torch.float32)
+    conv_w, conv_b = _c(conv_w, torch.float32), _c(conv_b, torch.float32)
+    dconv_w = torch.empty_like(conv_w) if conv_w is not None else None
+    dconv_b = torch.empty_like(conv_b) if conv_b is not None else None
     batch, dim, H, W = x.shape
     N = A.shape[-1]
     dx, ddelta = torch.empty_like(x), torch.empty_like(delta)
@@ -339,9 +362,14 @@ def ss2d_bwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, dout=None, delt
                     dA=_ptr(dA), dBm=_ptr(dB), dCm=_ptr(dC), dDskip=_ptr(dD), ddelta_bias=_ptr(dbias), dz=_ptr(dz),
                     workspace=_ptr(ws), workspace_bytes=ws.numel() * ws.element_size(), batch=batch, dim=dim,
                     height=H, width=W, dstate=N, dtype=_dtype_code(x.dtype),
-                    delta_softplus=int(bool(delta_softplus)), workspace_has_states=int(bool(workspace_has_states)))
+                    delta_softplus=int(bool(delta_softplus)), workspace_has_states=int(bool(workspace_has_states)),
+                    conv_w=_ptr(conv_w), conv_b=_ptr(conv_b), conv_k=_conv_k(conv_w, dim), dconv_w=_ptr(dconv_w),
+                    dconv_b=_ptr(dconv_b))
     _check(lib().ss2d_bwd(ctypes.byref(a), _stream(dev)), "ss2d_bwd")
-    return {"dx": dx, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "ddelta_bias": dbias, "dz": dz}
+    g = {"dx": dx, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "ddelta_bias": dbias, "dz": dz}
+    if conv_w is not None:
+        g.update(dconv_w=dconv_w, dconv_b=dconv_b)
+    return g
 
 
 def vim_bidir_workspace_bytes(batch, dim, seqlen, dstate, dtype: torch.dtype) -> int:

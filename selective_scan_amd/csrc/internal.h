@@ -105,6 +105,33 @@ struct MergeGateArgs {
 };
 hipError_t launch_merge_gate_bwd(const MergeGateArgs& a, hipStream_t s);
 
+// The SS2D input front: a depthwise k x k convolution ('same' zero padding, bias) and SiLU,
+//   xc = silu(pre),  pre[b,c,h,w] = bias[c] + sum_{i,j} w[c,i,j] x[b,c,h+i-r,w+j-r],  r = k/2
+// written both in grid order (xc) and per-plane transposed (xcT), from the same rounded value.
+// Backward: dpre = dxc * silu'(pre) (pre recomputed), dx = the transposed convolution of dpre,
+// and per-tile partial sums of dw[c,i,j] = sum dpre * x (shifted) and dbias[c] = sum dpre,
+// which launch_front_reduce adds in a fixed order.
+constexpr int kFrontMaxK = 7;
+struct FrontArgs {
+  const void* x;        // (batch, C, H, W) dtype
+  const float* w;       // (C, k, k)
+  const float* bias;    // (C) or null
+  void* xc;             // forward: (batch, C, H, W) dtype
+  void* xcT;            // forward: (batch, C, W*H) dtype, column-major per plane
+  const float* dxc;     // backward: (batch, C, H, W) fp32
+  void* dx;             // backward: (batch, C, H, W) dtype
+  float* part;          // backward: (batch, C, tiles, 7*7 + 1) fp32 partial sums (tap (i,j) at i*7+j)
+  float* dw;            // reduce: (C, k, k)
+  float* dbias;         // reduce: (C) or null
+  int64_t batch, C, H, W;
+  int k;
+  int dtype;
+};
+hipError_t launch_front_fwd(const FrontArgs& a, hipStream_t s);
+hipError_t launch_front_bwd(const FrontArgs& a, hipStream_t s);
+hipError_t launch_front_reduce(const FrontArgs& a, hipStream_t s);
+__host__ __device__ inline int64_t front_tiles(int64_t H, int64_t W) { return ((H + 31) / 32) * ((W + 31) / 32); }
+
 // Writes n fp32 zeros (a kernel, so that graph capture records no memset node).
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 

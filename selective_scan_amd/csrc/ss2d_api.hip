@@ -98,7 +98,7 @@ ScanLayout scan_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqle
 
 // ---- SS2D workspace layout -----------------------------------------------------------
 struct SS2DLayout {
-  int64_t off_xT, off_ys, off_scan, off_merged, off_dM, off_dMT, total;
+  int64_t off_xT, off_ys, off_scan, off_merged, off_dM, off_dMT, off_xc, off_cpart, total;
   ScanLayout scan;
 };
 
@@ -113,6 +113,8 @@ SS2DLayout ss2d_layout(int64_t batch, int64_t dim, int64_t H, int64_t W, int64_t
   l.off_merged = o; o += align_up(batch * dim * L * 4);
   l.off_dM = o;     o += align_up(batch * dim * L * 4);
   l.off_dMT = o;    o += align_up(batch * dim * L * 4);
+  l.off_xc = o;     o += align_up(batch * dim * L * esize(dtype));                 // input front output
+  l.off_cpart = o;  o += align_up(batch * dim * front_tiles(H, W) * (kFrontMaxK * kFrontMaxK + 1) * 4);
   l.total = o;
   return l;
 }
@@ -309,7 +311,28 @@ size_t ss2d_workspace_bytes(int64_t batch, int64_t dim, int64_t height, int64_t 
 }
 
 // Stages of the SS2D forward (all on one workspace).
+// The map the four routes scan: x, or the input front's output (in the workspace).
+static const void* scan_input(const void* x, const float* conv_w, void* ws, const SS2DLayout& lay) {
+  return conv_w ? static_cast<const void*>(at(ws, lay.off_xc)) : x;
+}
+
+// Stage 0: the column-major copy of the scanned map (and, with the input front, the map itself).
 static int ss2d_transpose_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, hipStream_t stream) {
+  if (a->conv_w) {
+    FrontArgs f{};
+    f.x = a->x;
+    f.w = a->conv_w;
+    f.bias = a->conv_b;
+    f.xc = at(a->workspace, lay.off_xc);
+    f.xcT = at(a->workspace, lay.off_xT);
+    f.batch = a->batch;
+    f.C = a->dim;
+    f.H = a->height;
+    f.W = a->width;
+    f.k = a->conv_k;
+    f.dtype = a->dtype;
+    return status_from(launch_front_fwd(f, stream));
+  }
   return status_from(launch_transpose(a->x, at(a->workspace, lay.off_xT), a->batch, a->dim, a->height, a->width,
                                       esize(a->dtype), stream));
 }
@@ -319,7 +342,7 @@ static int ss2d_transpose_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, h
 static int ss2d_scan_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, bool keep_states, hipStream_t stream) {
   const int64_t L = a->height * a->width;
   ScanFwdParams p{};
-  p.u = a->x;
+  p.u = scan_input(a->x, a->conv_w, a->workspace, lay);
   p.uT = at(a->workspace, lay.off_xT);
   p.delta = a->delta;
   p.A = a->A;
@@ -339,7 +362,7 @@ static int ss2d_scan_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, bool k
   p.softplus = a->delta_softplus ? 1 : 0;
   p.ss2d = 1;
   p.dtype = a->dtype;
-  p.vec = (L % 4 == 0) && vec_aligned(a->dtype, {a->x, a->delta, a->Bm, a->Cm});
+  p.vec = (L % 4 == 0) && vec_aligned(a->dtype, {p.u, a->delta, a->Bm, a->Cm});
   p.chunk_len = lay.scan.chunk_len;
   p.n_chunks = lay.scan.n_chunks;
   if (a->batch * 4 * lay.scan.dblocks * 2 * p.n_chunks > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
@@ -361,7 +384,7 @@ static int ss2d_merge_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, float
   MergeArgs m{};
   m.routes = at(a->workspace, lay.off_ys);
   m.routes_f32 = 1;  // the scan stage writes fp32 route outputs
-  m.x = a->x;
+  m.x = scan_input(a->x, a->conv_w, a->workspace, lay);
   m.Dskip = a->Dskip;
   m.z = a->z;
   m.y = a->out;
@@ -382,12 +405,21 @@ static int check_ss2d(int64_t batch, int64_t dim, int64_t height, int64_t width,
   return SS2D_OK;
 }
 
+// The input front's filter: odd size 1..7, fp32 pointers 4-byte aligned.
+static int check_front(const float* w, const float* b, int k) {
+  if (!w) return b ? SS2D_ERR_INVALID_ARGUMENT : SS2D_OK;
+  if (k < 1 || k > kFrontMaxK || k % 2 == 0) return SS2D_ERR_UNSUPPORTED;
+  if (!aligned(w, 4) || (b && !aligned(b, 4))) return SS2D_ERR_INVALID_ARGUMENT;
+  return SS2D_OK;
+}
+
 // Validation shared by ss2d_fwd and ss2d_fwd_stage.  Returns SS2D_OK with *empty set when there
 // is nothing to compute.
 static int validate_ss2d_fwd(const ss2d_fwd_args* a, SS2DLayout* lay, bool* empty) {
   *empty = false;
   if (!a) return SS2D_ERR_INVALID_ARGUMENT;
   int st = check_ss2d(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype);
+  if (st == SS2D_OK) st = check_front(a->conv_w, a->conv_b, a->conv_k);
   if (st != SS2D_OK) return st;
   if (a->batch * a->dim * a->height * a->width == 0) {
     *empty = true;
@@ -580,14 +612,23 @@ int selective_scan_bwd(const ss_bwd_args* a, hipStream_t stream) {
 int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
   if (!a) return SS2D_ERR_INVALID_ARGUMENT;
   int st = check_ss2d(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype);
+  if (st == SS2D_OK) st = check_front(a->conv_w, a->conv_b, a->conv_k);
   if (st != SS2D_OK) return st;
-  if ((a->Dskip && !a->dDskip) || (a->delta_bias && !a->ddelta_bias) || (a->z && !a->dz))
+  if ((a->Dskip && !a->dDskip) || (a->delta_bias && !a->ddelta_bias) || (a->z && !a->dz) ||
+      (a->conv_w && !a->dconv_w) || (a->conv_b && !a->dconv_b))
+    return SS2D_ERR_INVALID_ARGUMENT;
+  if ((a->dconv_w && !aligned(a->dconv_w, 4)) || (a->dconv_b && !aligned(a->dconv_b, 4)))
     return SS2D_ERR_INVALID_ARGUMENT;
   if (a->dim == 0) return SS2D_OK;
   if (!a->dA) return SS2D_ERR_INVALID_ARGUMENT;
-  if (a->batch * a->height * a->width == 0)
-    return zero_param_grads(a->dA, a->Dskip ? a->dDskip : nullptr, a->delta_bias ? a->ddelta_bias : nullptr,
-                            4 * a->dim, a->dstate, stream);
+  if (a->batch * a->height * a->width == 0) {
+    st = zero_param_grads(a->dA, a->Dskip ? a->dDskip : nullptr, a->delta_bias ? a->ddelta_bias : nullptr,
+                          4 * a->dim, a->dstate, stream);
+    if (st == SS2D_OK && a->conv_w)
+      st = zero_param_grads(a->dconv_w, a->conv_b ? a->dconv_b : nullptr, nullptr, a->dim,
+                            int64_t(a->conv_k) * a->conv_k, stream);
+    return st;
+  }
   if (!a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->dout || !a->dx || !a->ddelta || !a->dBm || !a->dCm ||
       !a->workspace)
     return SS2D_ERR_INVALID_ARGUMENT;
@@ -624,6 +665,9 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
     f.dstate = a->dstate;
     f.dtype = a->dtype;
     f.delta_softplus = a->delta_softplus;
+    f.conv_w = a->conv_w;
+    f.conv_b = a->conv_b;
+    f.conv_k = a->conv_k;
     st = ss2d_transpose_stage(&f, lay, stream);
     if (st == SS2D_OK) st = ss2d_scan_stage(&f, lay, true, stream);
     if (st != SS2D_OK) return st;
@@ -632,8 +676,9 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
   // gate (with the pre-gate merge it needs): dz, and dM = dout * silu(z) in grid and
   // transposed order
   MergeGateArgs gb{};
+  const void* u = scan_input(a->x, a->conv_w, a->workspace, lay);
   gb.routes = reinterpret_cast<const float*>(at(a->workspace, lay.off_ys));
-  gb.x = a->x;
+  gb.x = u;
   gb.Dskip = a->Dskip;
   gb.z = a->z;
   gb.dout = a->dout;
@@ -650,7 +695,7 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
 
   // adjoint scans of the four routes; du (fp32, route order) reuses the route-output region
   ScanBwdParams bp{};
-  bp.u = a->x;
+  bp.u = u;
   bp.uT = at(a->workspace, lay.off_xT);
   bp.delta = a->delta;
   bp.A = a->A;
@@ -672,22 +717,45 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
   bp.softplus = a->delta_softplus ? 1 : 0;
   bp.ss2d = 1;
   bp.dtype = a->dtype;
-  bp.vec = (L % 4 == 0) && vec_aligned(a->dtype, {a->x, a->delta, a->Bm, a->Cm, a->ddelta});
+  bp.vec = (L % 4 == 0) && vec_aligned(a->dtype, {u, a->delta, a->Bm, a->Cm, a->ddelta});
   st = run_scan_bwd(bp, lay.scan, at(a->workspace, lay.off_scan), a->dBm, a->dCm, a->dA,
                     a->Dskip ? a->dDskip : nullptr, a->delta_bias ? a->ddelta_bias : nullptr, stream);
   if (st != SS2D_OK) return st;
 
-  // dx = cross-merge of the routes' du
+  // dx = cross-merge of the routes' du (with the input front: the gradient w.r.t. its output,
+  // in fp32, which the front's backward turns into dx and the filter gradients)
   MergeArgs m{};
   m.routes = at(a->workspace, lay.off_ys);
   m.routes_f32 = 1;
-  m.y = a->dx;
   m.batch = a->batch;
   m.C = a->dim;
   m.H = a->height;
   m.W = a->width;
   m.dtype = a->dtype;
-  return status_from(launch_merge(m, stream));
+  if (!a->conv_w) {
+    m.y = a->dx;
+    return status_from(launch_merge(m, stream));
+  }
+  float* dxc = reinterpret_cast<float*>(at(a->workspace, lay.off_merged));
+  m.merged_f32 = dxc;
+  if (launch_merge(m, stream) != hipSuccess) return SS2D_ERR_HIP;
+  FrontArgs fr{};
+  fr.x = a->x;
+  fr.w = a->conv_w;
+  fr.bias = a->conv_b;
+  fr.dxc = dxc;
+  fr.dx = a->dx;
+  fr.part = reinterpret_cast<float*>(at(a->workspace, lay.off_cpart));
+  fr.dw = a->dconv_w;
+  fr.dbias = a->conv_b ? a->dconv_b : nullptr;
+  fr.batch = a->batch;
+  fr.C = a->dim;
+  fr.H = a->height;
+  fr.W = a->width;
+  fr.k = a->conv_k;
+  fr.dtype = a->dtype;
+  if (launch_front_bwd(fr, stream) != hipSuccess) return SS2D_ERR_HIP;
+  return status_from(launch_front_reduce(fr, stream));
 }
 
 // ---- Bidirectional (Vision Mamba) scan --------------------------------------------------

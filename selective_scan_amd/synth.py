@@ -18,7 +18,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-T_X, T_Z, T_DELTA, T_B, T_C, T_U, T_DOUT = range(7)
+T_X, T_Z, T_DELTA, T_B, T_C, T_U, T_DOUT, T_CONV = range(8)
 
 
 @dataclass(frozen=True)
@@ -132,6 +132,15 @@ def make_ss2d_inputs(batch: int, height: int, width: int, dim: int, dstate: int,
     out["dout"] = _normal(s + T_DOUT, (batch, dim, height, width), dtype) if with_dout else None
     out["meta"] = dict(batch=batch, height=height, width=width, dim=dim, dstate=dstate, dtype=dtype)
     return out
+
+
+def make_front_params(dim: int, k: int, seed_base: int = 0, with_bias: bool = True) -> dict:
+    """Parameters of the SS2D input front: conv_w (dim, k, k) fp32 drawn N(0, 1/k^2) (unit
+    gain for a unit-variance input), conv_b (dim,) fp32 drawn N(0, 0.1^2), or None."""
+    rng = np.random.Generator(np.random.PCG64(1000 * seed_base + T_CONV))
+    w = (rng.standard_normal(size=(dim, k, k), dtype=np.float32) / np.float32(k)).astype(np.float32)
+    b = (np.float32(0.1) * rng.standard_normal(size=(dim,), dtype=np.float32)) if with_bias else None
+    return {"conv_w": w, "conv_b": b}
 
 
 def make_config_inputs(cfg: SS2DConfig, with_dout: bool | None = None) -> dict:

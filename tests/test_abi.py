@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ss2d_abi_version() == 4
+    assert lib.ss2d_abi_version() == 5
     assert lib.ss2d_status_string(0) == b"ok"
     assert b"invalid" in lib.ss2d_status_string(1)
     assert b"unsupported" in lib.ss2d_status_string(2)
@@ -132,6 +132,15 @@ def test_ss2d_rejects(lib):
              width=5, dstate=4, dtype=0, delta_softplus=1)
     assert lib.ss2d_bwd(ctypes.byref(SS2DBwdArgs(**b)), None) == 1
     assert lib.ss2d_bwd(ctypes.byref(SS2DBwdArgs(**{**b, "Dskip": 0xc000})), None) == 1  # D without dD
+    # the input front: odd filter sizes 1..7 only, a bias needs a filter, gradients need outputs
+    for k, st in ((2, 2), (9, 2), (0, 2), (-3, 2)):
+        assert lib.ss2d_fwd(ctypes.byref(SS2DFwdArgs(**{**f, "conv_w": 0xd000, "conv_k": k})), None) == st, k
+    assert lib.ss2d_fwd(ctypes.byref(SS2DFwdArgs(**{**f, "conv_b": 0xe000, "conv_k": 3})), None) == 1
+    assert lib.ss2d_fwd(ctypes.byref(SS2DFwdArgs(**{**f, "conv_w": 0xd002, "conv_k": 3})), None) == 1
+    big = dict(workspace_bytes=1 << 40, dz=0, conv_w=0xd000, conv_k=3)
+    assert lib.ss2d_bwd(ctypes.byref(SS2DBwdArgs(**{**b, **big})), None) == 1                 # no dconv_w
+    assert lib.ss2d_bwd(ctypes.byref(SS2DBwdArgs(**{**b, **big, "dconv_w": 0xf000, "conv_b": 0xe000})),
+                        None) == 1                                                            # no dconv_b
 
 
 def test_vim_bidir_rejects(lib):
