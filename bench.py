@@ -66,12 +66,12 @@ def parse():
 
 
 def front_bytes(cfg, bwd=False):
-    """The input front's own minimum: the forward reads x and writes the front output in grid
-    and column-major order; the backward reads x and the fp32 gradient of the front output and
-    writes dx (the filter partial sums are a few bytes per 32 x 32 tile)."""
+    """The input front's own minimum: the forward reads x and writes the fp32 front output in
+    grid and column-major order; the backward reads x and the fp32 gradient of the front output
+    and writes dx (the filter partial sums are 200 bytes per plane)."""
     e = 2 if cfg.dtype == "bf16" else 4
     grid = cfg.batch * cfg.dim * cfg.seqlen
-    return e * 3 * grid + ((2 * e + 4) * grid if bwd else 0)
+    return (e + 8) * grid + ((2 * e + 4) * grid if bwd else 0)
 
 
 def algorithmic_bytes(cfg, bwd=False):

@@ -208,7 +208,8 @@ int selective_scan_step(const ss_step_args* args, hipStream_t stream);
  *           A          : (4, dim, dstate) fp32;  Dskip, delta_bias : (4, dim) fp32 (may be NULL)
  * The gate is applied once per pixel after the merge, which equals gating every route
  * with the cross-scanned z and merging (silu(z) is the same factor on all four).
- * The workspace is required (>= ss2d_workspace_bytes(...)).
+ * The workspace is required (>= ss2d_workspace_bytes(...)); the same size serves calls with
+ * and without the input front.
  * ------------------------------------------------------------------------------- */
 size_t ss2d_workspace_bytes(int64_t batch, int64_t dim, int64_t height, int64_t width,
                             int64_t dstate, int dtype);
@@ -234,7 +235,8 @@ typedef struct ss2d_fwd_args {
    * depthwise convolution and SiLU]: with conv_w != NULL the four routes scan
    *   u = silu(pre),  pre[b,c,h,w] = conv_b[c] + sum_{i,j} conv_w[c,i,j] x[b,c,h+i-r,w+j-r]
    * (r = conv_k / 2, zero outside the map; conv_k odd, 1..7), computed once per pixel and kept
-   * in dtype; the skip term then uses u as well. */
+   * in fp32 in the workspace (the routes and the skip term read it without a rounding to the
+   * I/O type); the skip term then uses u as well. */
   const float* conv_w;     /* (dim, conv_k, conv_k) fp32, or NULL: no front (u = x) */
   const float* conv_b;     /* (dim) fp32, may be NULL */
   int conv_k;

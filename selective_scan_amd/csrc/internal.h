@@ -41,7 +41,8 @@ hipError_t launch_transpose(const void* x, void* xT, int64_t batch, int64_t C, i
 struct MergeArgs {
   const void* routes;      // (batch, 4, C, L) fp32 or dtype
   int routes_f32;
-  const void* x;           // grid (batch, C, H, W) dtype, optional skip input
+  const void* x;           // grid (batch, C, H, W) dtype (fp32 if x_f32), optional skip input
+  int x_f32;
   const float* Dskip;      // (4, C) fp32, summed over routes (used with x)
   const void* z;           // grid dtype, optional gate
   void* y;                 // grid dtype
@@ -92,7 +93,8 @@ hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t s);
 // merge writes M to `merged` (fp32 scratch) and the gate kernel reads it.
 struct MergeGateArgs {
   const float* routes;  // (batch, 4, C, L) fp32, route order
-  const void* x;        // grid dtype (skip input, with Dskip)
+  const void* x;        // grid dtype (fp32 if x_f32) (skip input, with Dskip)
+  int x_f32;
   const float* Dskip;   // (4, C) or null
   const void* z;        // grid dtype
   const void* dout;     // grid dtype
@@ -107,20 +109,22 @@ hipError_t launch_merge_gate_bwd(const MergeGateArgs& a, hipStream_t s);
 
 // The SS2D input front: a depthwise k x k convolution ('same' zero padding, bias) and SiLU,
 //   xc = silu(pre),  pre[b,c,h,w] = bias[c] + sum_{i,j} w[c,i,j] x[b,c,h+i-r,w+j-r],  r = k/2
-// written both in grid order (xc) and per-plane transposed (xcT), from the same rounded value.
+// written in fp32 both in grid order (xc) and per-plane transposed (xcT): the routes scan it,
+// and the merge adds its skip term, without an intermediate rounding to the I/O type.
 // Backward: dpre = dxc * silu'(pre) (pre recomputed), dx = the transposed convolution of dpre,
-// and per-tile partial sums of dw[c,i,j] = sum dpre * x (shifted) and dbias[c] = sum dpre,
-// which launch_front_reduce adds in a fixed order.
+// and per-plane (or per-tile) partial sums of dw[c,i,j] = sum dpre * x (shifted) and
+// dbias[c] = sum dpre, which launch_front_reduce adds in a fixed order.  Planes whose halo'd
+// copies fit 64 KB of LDS take one workgroup each; larger maps go by 32 x 32 tiles.
 constexpr int kFrontMaxK = 7;
 struct FrontArgs {
   const void* x;        // (batch, C, H, W) dtype
   const float* w;       // (C, k, k)
   const float* bias;    // (C) or null
-  void* xc;             // forward: (batch, C, H, W) dtype
-  void* xcT;            // forward: (batch, C, W*H) dtype, column-major per plane
+  float* xc;            // forward: (batch, C, H, W) fp32
+  float* xcT;           // forward: (batch, C, W*H) fp32, column-major per plane
   const float* dxc;     // backward: (batch, C, H, W) fp32
   void* dx;             // backward: (batch, C, H, W) dtype
-  float* part;          // backward: (batch, C, tiles, 7*7 + 1) fp32 partial sums (tap (i,j) at i*7+j)
+  float* part;          // backward: (batch, C, front_part_rows, 7*7 + 1) fp32 partial sums (tap (i,j) at i*7+j)
   float* dw;            // reduce: (C, k, k)
   float* dbias;         // reduce: (C) or null
   int64_t batch, C, H, W;
@@ -131,6 +135,15 @@ hipError_t launch_front_fwd(const FrontArgs& a, hipStream_t s);
 hipError_t launch_front_bwd(const FrontArgs& a, hipStream_t s);
 hipError_t launch_front_reduce(const FrontArgs& a, hipStream_t s);
 __host__ __device__ inline int64_t front_tiles(int64_t H, int64_t W) { return ((H + 31) / 32) * ((W + 31) / 32); }
+// LDS of the whole-plane kernels: the forward holds x with an r halo and the output transposed,
+// the backward x and dpre, each with an r halo.
+inline int64_t front_plane_lds(int64_t H, int64_t W, int k) {
+  const int64_t r = k / 2, halo = (H + 2 * r) * (W + 2 * r);
+  const int64_t fwd = (halo + W * (H + 1)) * 4, bwd = 2 * halo * 4;
+  return fwd > bwd ? fwd : bwd;
+}
+inline bool front_plane_path(int64_t H, int64_t W, int k) { return front_plane_lds(H, W, k) <= 64 * 1024; }
+inline int64_t front_part_rows(int64_t H, int64_t W, int k) { return front_plane_path(H, W, k) ? 1 : front_tiles(H, W); }
 
 // Writes n fp32 zeros (a kernel, so that graph capture records no memset node).
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
@@ -163,6 +176,7 @@ struct ScanFwdParams {
   int pass;            // 0: outputs/checkpoints from the stored chunk-start state; 1: chunk-local end state
   int store_states;    // pass 0 also keeps the state before every ckpt_every-th step in ckpt
   int out_f32;         // generic rows: out is fp32 instead of the I/O type
+  int u_f32;           // ss2d rows, bf16 I/O: u and uT are fp32 (the input front's output)
 };
 hipError_t launch_scan_fwd(const ScanFwdParams& p, hipStream_t s);
 // Turns the chunk-local end states (pass 1) into the true chunk-start states.
@@ -219,6 +233,7 @@ struct ScanBwdParams {
   int vec;
   int pass;                // 1: chunk-local lambda pass; 0: gradients
   int dout_f32;            // generic rows: dout is fp32 instead of the I/O type
+  int u_f32;               // ss2d rows, bf16 I/O: u and uT are fp32 (the input front's output)
 };
 hipError_t launch_scan_bwd(const ScanBwdParams& p, hipStream_t s);
 hipError_t launch_lambda_combine(const ScanBwdParams& p, hipStream_t s);

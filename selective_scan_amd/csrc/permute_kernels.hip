@@ -121,7 +121,8 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a, int tiles_h, in
       float v = ld_route(r0, p) + t1[tx][ty + kTy * r];
       v = v + ld_route(r2, L - 1 - p);
       v = v + t3[tx][ty + kTy * r];
-      if (a.Dskip && xg) v = fmaf(dsum, Elem<T>::load(xg, plane + p), v);
+      if (a.Dskip && xg)
+        v = fmaf(dsum, a.x_f32 ? static_cast<const float*>(a.x)[plane + p] : Elem<T>::load(xg, plane + p), v);
       if (a.merged_f32) a.merged_f32[plane + p] = v;
       if (zg) v *= silu(Elem<T>::load(zg, plane + p));
       if (yg) Elem<T>::store(yg, plane + p, v);
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(kPlaneThreads) void merge_plane_kernel(MergeArgs a)
       v[j] = s + t3[w * ld + h];
     }
     if (a.Dskip && a.x) {
-      const float4 xv = Elem<T>::load4(xg, p);
+      const float4 xv = a.x_f32 ? Elem<float>::load4(static_cast<const float*>(a.x) + plane * L, p) : Elem<T>::load4(xg, p);
       v[0] = fmaf(dsum, xv.x, v[0]); v[1] = fmaf(dsum, xv.y, v[1]);
       v[2] = fmaf(dsum, xv.z, v[2]); v[3] = fmaf(dsum, xv.w, v[3]);
     }
@@ -327,7 +328,8 @@ __global__ __launch_bounds__(kPlaneThreads) void merge_gate_bwd_plane_kernel(Mer
     const float4 v2 = *reinterpret_cast<const float4*>(r2 + (L - 4 - p));
     const float a0[4] = {v0.x, v0.y, v0.z, v0.w};
     const float a2[4] = {v2.w, v2.z, v2.y, v2.x};
-    const float4 xv = Elem<T>::load4(xg, p), zv = Elem<T>::load4(zg, p), gv = Elem<T>::load4(gg, p);
+    const float4 xv = a.x_f32 ? Elem<float>::load4(static_cast<const float*>(a.x) + plane * L, p) : Elem<T>::load4(xg, p);
+    const float4 zv = Elem<T>::load4(zg, p), gv = Elem<T>::load4(gg, p);
     const float xs[4] = {xv.x, xv.y, xv.z, xv.w}, zs[4] = {zv.x, zv.y, zv.z, zv.w}, gs[4] = {gv.x, gv.y, gv.z, gv.w};
     float dz[4], dm[4];
 #pragma unroll
@@ -435,7 +437,7 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
       (a.dtype == 0 ? (aligned16(a.y) && aligned16(a.x) && aligned16(a.z))
                     : ((reinterpret_cast<uintptr_t>(a.y) | reinterpret_cast<uintptr_t>(a.x) |
                         reinterpret_cast<uintptr_t>(a.z)) & 7) == 0) &&
-      L % 4 == 0) {
+      (!a.x_f32 || aligned16(a.x)) && L % 4 == 0) {
     const dim3 g{uint32_t(a.batch * a.C)}, b{kPlaneThreads};
     if (a.dtype == 0)
       merge_plane_kernel<float, float><<<g, b, plane_lds, s>>>(a);
@@ -508,7 +510,7 @@ hipError_t launch_merge_gate_bwd(const MergeGateArgs& a, hipStream_t s) {
   const uintptr_t io = reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.z) |
                        reinterpret_cast<uintptr_t>(a.dout) | reinterpret_cast<uintptr_t>(a.dz);
   if (a.z && lds <= 64 * 1024 && L % 4 == 0 && a.batch * a.C > 0 && aligned16(a.routes) && aligned16(a.dM) &&
-      aligned16(a.dMT) && (io & (a.dtype == 0 ? 15 : 7)) == 0) {
+      aligned16(a.dMT) && (io & (a.dtype == 0 ? 15 : 7)) == 0 && (!a.x_f32 || aligned16(a.x))) {
     const dim3 g{uint32_t(a.batch * a.C)}, b{kPlaneThreads};
     if (a.dtype == 0)
       merge_gate_bwd_plane_kernel<float><<<g, b, lds, s>>>(a);
@@ -522,6 +524,7 @@ hipError_t launch_merge_gate_bwd(const MergeGateArgs& a, hipStream_t s) {
     m.routes = a.routes;
     m.routes_f32 = 1;
     m.x = a.x;
+    m.x_f32 = a.x_f32;
     m.Dskip = a.Dskip;
     m.merged_f32 = a.merged;
     m.batch = a.batch;

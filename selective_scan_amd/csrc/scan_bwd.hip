@@ -5,7 +5,7 @@
 
 namespace ss2d {
 
-template <typename T, int NS>
+template <typename T, int NS, typename TU>
 hipError_t scan_bwd_launch(const ScanBwdParams& p, hipStream_t s);
 
 namespace {
@@ -65,20 +65,21 @@ __global__ __launch_bounds__(256) void reduce_params_kernel(const BwdReduceArgs 
   }
 }
 
-template <typename T>
+template <typename T, typename TU>
 hipError_t launch_dtype(const ScanBwdParams& p, hipStream_t s) {
-  if (p.N <= 1) return scan_bwd_launch<T, 1>(p, s);
-  if (p.N <= 4) return scan_bwd_launch<T, 4>(p, s);
-  if (p.N <= 8) return scan_bwd_launch<T, 8>(p, s);
-  if (p.N <= 16) return scan_bwd_launch<T, 16>(p, s);
-  if (p.N <= 32) return scan_bwd_launch<T, 32>(p, s);
-  return scan_bwd_launch<T, 64>(p, s);
+  if (p.N <= 1) return scan_bwd_launch<T, 1, TU>(p, s);
+  if (p.N <= 4) return scan_bwd_launch<T, 4, TU>(p, s);
+  if (p.N <= 8) return scan_bwd_launch<T, 8, TU>(p, s);
+  if (p.N <= 16) return scan_bwd_launch<T, 16, TU>(p, s);
+  if (p.N <= 32) return scan_bwd_launch<T, 32, TU>(p, s);
+  return scan_bwd_launch<T, 64, TU>(p, s);
 }
 
 }  // namespace
 
 hipError_t launch_scan_bwd(const ScanBwdParams& p, hipStream_t s) {
-  return p.dtype == 0 ? launch_dtype<float>(p, s) : launch_dtype<bf16>(p, s);
+  if (p.dtype == 0) return launch_dtype<float, float>(p, s);
+  return p.u_f32 ? launch_dtype<bf16, float>(p, s) : launch_dtype<bf16, bf16>(p, s);
 }
 
 hipError_t launch_lambda_combine(const ScanBwdParams& p, hipStream_t s) {

@@ -2,5 +2,5 @@
 #include "scan_bwd_kernel.h"
 
 namespace ss2d {
-template hipError_t scan_bwd_launch<bf16, 8>(const ScanBwdParams&, hipStream_t);
+template hipError_t scan_bwd_launch<bf16, 8, bf16>(const ScanBwdParams&, hipStream_t);
 }  // namespace ss2d

@@ -179,7 +179,8 @@ __device__ __forceinline__ bool reduce_writer(int lane) {
 // kSplit: lanes per channel (1 or 2); NSL = NS / kSplit states per lane.
 // kMode: 0 = generic rows, dout in the I/O type; 1 = SS2D routes (u from the map and its
 // transpose, fp32 dout planes); 2 = generic rows with an fp32 dout.
-template <typename T, int NS, int kSplit, int kMode, bool kVec, int kPass>
+// TU: element type of u (T, or fp32 for an SS2D input computed in fp32 by the input front).
+template <typename T, int NS, int kSplit, int kMode, bool kVec, int kPass, typename TU>
 __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) {
   constexpr bool kSS2D = kMode == 1;
   using DT = typename std::conditional<kMode == 0, T, float>::type;  // type of dout rows
@@ -214,16 +215,16 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
   const int nvalid = (N - n0 < 0) ? 0 : ((N - n0 > NSL) ? NSL : N - n0);
 
   const T* delta_row = static_cast<const T*>(p.delta) + row * L;
-  const T* u_row;
+  const TU* u_row;
   const DT* dout_row;
   bool rev = false;
   if (kSS2D) {
     const int64_t plane = (b * p.per_group + dl) * L;
-    u_row = ((g & 1) ? static_cast<const T*>(p.uT) : static_cast<const T*>(p.u)) + plane;
+    u_row = ((g & 1) ? static_cast<const TU*>(p.uT) : static_cast<const TU*>(p.u)) + plane;
     dout_row = ((g & 1) ? static_cast<const DT*>(p.doutT) : static_cast<const DT*>(p.dout)) + plane;
     rev = g >= 2;
   } else {
-    u_row = static_cast<const T*>(p.u) + row * L;
+    u_row = static_cast<const TU*>(p.u) + row * L;
     dout_row = static_cast<const DT*>(p.dout) + row * L;
   }
   const bool has_z = !kSS2D && p.z != nullptr;
@@ -426,12 +427,13 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
     // One lane per channel (used when rows are few and the kernel is latency-bound): the row
     // segments and start state of the next sub-interval are loaded while this one computes.
     const int64_t n_segs = (t_end - t_begin + kSub - 1) / kSub;
-    RowTile<T, kSub> nd, nu, nz;
+    RowTile<T, kSub> nd, nz;
+    RowTile<TU, kSub> nu;
     RowTile<DT, kSub> ng;
     float nh0[NSL];
     auto prefetch_seg = [&](int64_t s0) {
       load_row<T, kVec, kSub>(nd, delta_row, s0, t_end, L, false);
-      load_row<T, kVec, kSub>(nu, u_row, s0, t_end, L, rev);
+      load_row<TU, kVec, kSub>(nu, u_row, s0, t_end, L, rev);
       load_row<DT, kVec, kSub>(ng, dout_row, s0, t_end, L, rev);
       if (has_z) load_row<T, kVec, kSub>(nz, z_row, s0, t_end, L, false);
       if (kPass == 0) {
@@ -446,7 +448,8 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
       const int64_t s0 = t_begin + si * kSub;
       const int q = int(((s0 - t_begin) % kTile) / kSub);
       if (si == n_segs - 1 || q == kSegsPerTile - 1) stage_tile(s0 - int64_t(q) * kSub);
-      const RowTile<T, kSub> cd = nd, cu = nu, cz = nz;
+      const RowTile<T, kSub> cd = nd, cz = nz;
+      const RowTile<TU, kSub> cu = nu;
       const RowTile<DT, kSub> cg = ng;
       float h0[NSL];
 #pragma unroll
@@ -475,7 +478,7 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
         if (s0 >= t_end) continue;
         float dv[kSub], uv[kSub], gv[kSub], zv[kSub];
         load_seg<T, kVec, kSub>(dv, delta_row, s0, t_end, L, false);
-        load_seg<T, kVec, kSub>(uv, u_row, s0, t_end, L, rev);
+        load_seg<TU, kVec, kSub>(uv, u_row, s0, t_end, L, rev);
         load_seg<DT, kVec, kSub>(gv, dout_row, s0, t_end, L, rev);
         if (has_z) load_seg<T, kVec, kSub>(zv, z_row, s0, t_end, L, false);
         const float* ck = p.ckpt + ((s0 / kSub) * p.batch * p.dim + row) * N + n0;
@@ -503,32 +506,37 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
   }
 }
 
-template <typename T, int NS, int kSplit, int kMode, bool kVec>
+template <typename T, int NS, int kSplit, int kMode, bool kVec, typename TU>
 hipError_t launch_t(ScanBwdParams p, hipStream_t s) {
   p.dblocks = (p.per_group + kWave / kSplit - 1) / (kWave / kSplit);
   const int64_t blocks = p.batch * p.G * p.dblocks * p.n_chunks;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (p.pass == 1)
-    scan_bwd_kernel<T, NS, kSplit, kMode, kVec, 1><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
+    scan_bwd_kernel<T, NS, kSplit, kMode, kVec, 1, TU><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
   else
-    scan_bwd_kernel<T, NS, kSplit, kMode, kVec, 0><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
+    scan_bwd_kernel<T, NS, kSplit, kMode, kVec, 0, TU><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace bwd_detail
 
-// Two lanes per channel from 16 states up (as in the forward).
-template <typename T, int NS>
+// Two lanes per channel from 16 states up (as in the forward).  TU != T (fp32 u with bf16 I/O)
+// exists for the SS2D routes only.
+template <typename T, int NS, typename TU>
 hipError_t scan_bwd_launch(const ScanBwdParams& p, hipStream_t s) {
   using namespace bwd_detail;
   constexpr int kSplit = NS >= 16 ? 2 : 1;
-  if (p.ss2d) return p.vec ? launch_t<T, NS, kSplit, 1, true>(p, s) : launch_t<T, NS, kSplit, 1, false>(p, s);
-  if constexpr (sizeof(T) != 4) {  // for fp32 I/O an fp32 dout is the ordinary case
-    if (p.dout_f32)
-      return p.vec ? launch_t<T, NS, kSplit, 2, true>(p, s) : launch_t<T, NS, kSplit, 2, false>(p, s);
+  if (p.ss2d) return p.vec ? launch_t<T, NS, kSplit, 1, true, TU>(p, s) : launch_t<T, NS, kSplit, 1, false, TU>(p, s);
+  if constexpr (!std::is_same_v<T, TU>) {
+    return hipErrorInvalidValue;
+  } else {
+    if constexpr (sizeof(T) != 4) {  // for fp32 I/O an fp32 dout is the ordinary case
+      if (p.dout_f32)
+        return p.vec ? launch_t<T, NS, kSplit, 2, true, TU>(p, s) : launch_t<T, NS, kSplit, 2, false, TU>(p, s);
+    }
+    return p.vec ? launch_t<T, NS, kSplit, 0, true, TU>(p, s) : launch_t<T, NS, kSplit, 0, false, TU>(p, s);
   }
-  return p.vec ? launch_t<T, NS, kSplit, 0, true>(p, s) : launch_t<T, NS, kSplit, 0, false>(p, s);
 }
 
 }  // namespace ss2d

@@ -2,5 +2,5 @@
 #include "scan_fwd_kernel.h"
 
 namespace ss2d {
-template hipError_t scan_fwd_launch<bf16, 32>(const ScanFwdParams&, hipStream_t);
+template hipError_t scan_fwd_launch<bf16, 32, bf16>(const ScanFwdParams&, hipStream_t);
 }  // namespace ss2d

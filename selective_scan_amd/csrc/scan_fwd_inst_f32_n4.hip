@@ -2,5 +2,5 @@
 #include "scan_fwd_kernel.h"
 
 namespace ss2d {
-template hipError_t scan_fwd_launch<float, 4>(const ScanFwdParams&, hipStream_t);
+template hipError_t scan_fwd_launch<float, 4, float>(const ScanFwdParams&, hipStream_t);
 }  // namespace ss2d

@@ -2,5 +2,5 @@
 #include "scan_fwd_kernel.h"
 
 namespace ss2d {
-template hipError_t scan_fwd_launch<float, 64>(const ScanFwdParams&, hipStream_t);
+template hipError_t scan_fwd_launch<float, 64, float>(const ScanFwdParams&, hipStream_t);
 }  // namespace ss2d

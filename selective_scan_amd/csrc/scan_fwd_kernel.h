@@ -33,8 +33,10 @@ using namespace scan_detail;
 //        2 = as 0 and also the state before every kSub-th step (checkpoints for the backward).
 // kSplit: lanes per channel (1 or 2); NSL = NS / kSplit states per lane.
 // kSoftplus: delta passes through softplus (else it is used as given).
-template <typename T, int NS, int kSplit, bool kSS2D, bool kVec, int kPassArg, bool kSoftplus>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu((kSS2D && kVec && sizeof(T) == 2) ? fwd_waves_per_simd(NS, true) : 1)))
+// TU: element type of u (T, or fp32 for an SS2D input computed in fp32 by the input front).
+template <typename T, int NS, int kSplit, bool kSS2D, bool kVec, int kPassArg, bool kSoftplus, typename TU>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(
+    (kSS2D && kVec && sizeof(T) == 2 && sizeof(TU) == 2) ? fwd_waves_per_simd(NS, true) : 1)))
 void scan_fwd_kernel(const ScanFwdParams p) {
   constexpr int kPass = kPassArg == 2 ? 0 : kPassArg;
   constexpr bool kStore = kPassArg == 2;
@@ -64,14 +66,14 @@ void scan_fwd_kernel(const ScanFwdParams p) {
   const int N = p.N;
 
   const T* delta_row = static_cast<const T*>(p.delta) + row * L;
-  const T* u_row;
+  const TU* u_row;
   bool rev = false;
   if (kSS2D) {
-    const T* src = (g & 1) ? static_cast<const T*>(p.uT) : static_cast<const T*>(p.u);
+    const TU* src = (g & 1) ? static_cast<const TU*>(p.uT) : static_cast<const TU*>(p.u);
     u_row = src + (b * p.per_group + dl) * L;
     rev = g >= 2;
   } else {
-    u_row = static_cast<const T*>(p.u) + row * L;
+    u_row = static_cast<const TU*>(p.u) + row * L;
   }
   const bool has_z = !kSS2D && p.z != nullptr;
   const T* z_row = has_z ? static_cast<const T*>(p.z) + row * L : nullptr;
@@ -106,12 +108,13 @@ void scan_fwd_kernel(const ScanFwdParams p) {
   const uint32_t dpad = kSoftplus ? (sizeof(T) == 2 ? 0xFF80u : 0xFF800000u) : 0u;
   // Row tiles in two register sets: tile k computes from set k % 2 while tile k + 1 is loaded
   // into the other (the loop body is instantiated once per set, so no copies between them).
-  RowTile<T> rd[2], ru[2], rz[2];
+  RowTile<T> rd[2], rz[2];
+  RowTile<TU> ru[2];
   BCStage<T, NS, kVec> nbc;
   auto prefetch = [&](auto set, int64_t t) {
     constexpr int k = decltype(set)::value;
     load_row<T, kVec>(rd[k], delta_row, t, t_end, L, false, dpad);
-    load_row<T, kVec>(ru[k], u_row, t, t_end, L, rev);
+    load_row<TU, kVec>(ru[k], u_row, t, t_end, L, rev);
     if (has_z) load_row<T, kVec>(rz[k], z_row, t, t_end, L, false);
     nbc.load(Bg, Cg, N, L, t, t_end, lane);
   };
@@ -120,7 +123,7 @@ void scan_fwd_kernel(const ScanFwdParams p) {
   auto tile = [&](auto set, int64_t t0) {
     constexpr int k_set = decltype(set)::value;
     const RowTile<T>& cd = rd[k_set];
-    const RowTile<T>& cu = ru[k_set];
+    const RowTile<TU>& cu = ru[k_set];
     const RowTile<T>& cz = rz[k_set];
     __syncthreads();  // the previous tile's LDS reads are complete
     nbc.template store<S>(sB, sC, lane);
@@ -253,7 +256,7 @@ void scan_fwd_kernel(const ScanFwdParams p) {
   }
 }
 
-template <typename T, int NS, int kSplit, bool kSS2D, bool kVec>
+template <typename T, int NS, int kSplit, bool kSS2D, bool kVec, typename TU>
 hipError_t launch_t(ScanFwdParams p, hipStream_t s) {
   p.dblocks = (p.per_group + kWave / kSplit - 1) / (kWave / kSplit);
   const int64_t blocks = p.batch * p.G * p.dblocks * p.n_chunks;
@@ -262,18 +265,18 @@ hipError_t launch_t(ScanFwdParams p, hipStream_t s) {
   const dim3 grid{uint32_t(blocks)}, block{kWave};
   if (p.softplus) {
     if (p.pass == 1)
-      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 1, true><<<grid, block, 0, s>>>(p);
+      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 1, true, TU><<<grid, block, 0, s>>>(p);
     else if (p.store_states)
-      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 2, true><<<grid, block, 0, s>>>(p);
+      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 2, true, TU><<<grid, block, 0, s>>>(p);
     else
-      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 0, true><<<grid, block, 0, s>>>(p);
+      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 0, true, TU><<<grid, block, 0, s>>>(p);
   } else {
     if (p.pass == 1)
-      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 1, false><<<grid, block, 0, s>>>(p);
+      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 1, false, TU><<<grid, block, 0, s>>>(p);
     else if (p.store_states)
-      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 2, false><<<grid, block, 0, s>>>(p);
+      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 2, false, TU><<<grid, block, 0, s>>>(p);
     else
-      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 0, false><<<grid, block, 0, s>>>(p);
+      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 0, false, TU><<<grid, block, 0, s>>>(p);
   }
   return hipGetLastError();
 }
@@ -282,12 +285,17 @@ hipError_t launch_t(ScanFwdParams p, hipStream_t s) {
 
 // Two lanes per channel from 16 states up (halves the per-lane state and doubles the
 // wavefronts, which balances the stage-1 workload over the 1024 SIMDs).
-template <typename T, int NS>
+// TU != T (fp32 u with bf16 I/O) exists for the SS2D routes only.
+template <typename T, int NS, typename TU>
 hipError_t scan_fwd_launch(const ScanFwdParams& p, hipStream_t s) {
   using namespace fwd_detail;
   constexpr int kSplit = NS >= 16 ? 2 : 1;
-  if (p.ss2d) return p.vec ? launch_t<T, NS, kSplit, true, true>(p, s) : launch_t<T, NS, kSplit, true, false>(p, s);
-  return p.vec ? launch_t<T, NS, kSplit, false, true>(p, s) : launch_t<T, NS, kSplit, false, false>(p, s);
+  if (p.ss2d) return p.vec ? launch_t<T, NS, kSplit, true, true, TU>(p, s) : launch_t<T, NS, kSplit, true, false, TU>(p, s);
+  if constexpr (!std::is_same_v<T, TU>) {
+    return hipErrorInvalidValue;
+  } else {
+    return p.vec ? launch_t<T, NS, kSplit, false, true, TU>(p, s) : launch_t<T, NS, kSplit, false, false, TU>(p, s);
+  }
 }
 
 }  // namespace ss2d

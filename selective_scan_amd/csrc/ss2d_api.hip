@@ -106,14 +106,14 @@ SS2DLayout ss2d_layout(int64_t batch, int64_t dim, int64_t H, int64_t W, int64_t
   SS2DLayout l{};
   const int64_t L = H * W;
   int64_t o = 0;
-  l.off_xT = o;     o += align_up(batch * dim * L * esize(dtype));
+  l.off_xT = o;     o += align_up(batch * dim * L * 4);  // the map's transpose (dtype, or fp32 from the front)
   l.off_ys = o;     o += align_up(batch * 4 * dim * L * 4);  // fp32 route outputs; fp32 du in the backward
   l.scan = scan_layout(batch, 4 * dim, dstate, L, 4, dtype);
   l.off_scan = o;   o += l.scan.total;
   l.off_merged = o; o += align_up(batch * dim * L * 4);
   l.off_dM = o;     o += align_up(batch * dim * L * 4);
   l.off_dMT = o;    o += align_up(batch * dim * L * 4);
-  l.off_xc = o;     o += align_up(batch * dim * L * esize(dtype));                 // input front output
+  l.off_xc = o;     o += align_up(batch * dim * L * 4);                            // input front output (fp32)
   l.off_cpart = o;  o += align_up(batch * dim * front_tiles(H, W) * (kFrontMaxK * kFrontMaxK + 1) * 4);
   l.total = o;
   return l;
@@ -323,8 +323,8 @@ static int ss2d_transpose_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, h
     f.x = a->x;
     f.w = a->conv_w;
     f.bias = a->conv_b;
-    f.xc = at(a->workspace, lay.off_xc);
-    f.xcT = at(a->workspace, lay.off_xT);
+    f.xc = reinterpret_cast<float*>(at(a->workspace, lay.off_xc));
+    f.xcT = reinterpret_cast<float*>(at(a->workspace, lay.off_xT));
     f.batch = a->batch;
     f.C = a->dim;
     f.H = a->height;
@@ -344,6 +344,7 @@ static int ss2d_scan_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, bool k
   ScanFwdParams p{};
   p.u = scan_input(a->x, a->conv_w, a->workspace, lay);
   p.uT = at(a->workspace, lay.off_xT);
+  p.u_f32 = a->conv_w != nullptr && a->dtype != 0;
   p.delta = a->delta;
   p.A = a->A;
   p.Bm = a->Bm;
@@ -385,6 +386,7 @@ static int ss2d_merge_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, float
   m.routes = at(a->workspace, lay.off_ys);
   m.routes_f32 = 1;  // the scan stage writes fp32 route outputs
   m.x = scan_input(a->x, a->conv_w, a->workspace, lay);
+  m.x_f32 = a->conv_w != nullptr;
   m.Dskip = a->Dskip;
   m.z = a->z;
   m.y = a->out;
@@ -679,6 +681,7 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
   const void* u = scan_input(a->x, a->conv_w, a->workspace, lay);
   gb.routes = reinterpret_cast<const float*>(at(a->workspace, lay.off_ys));
   gb.x = u;
+  gb.x_f32 = a->conv_w != nullptr;
   gb.Dskip = a->Dskip;
   gb.z = a->z;
   gb.dout = a->dout;
@@ -697,6 +700,7 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
   ScanBwdParams bp{};
   bp.u = u;
   bp.uT = at(a->workspace, lay.off_xT);
+  bp.u_f32 = a->conv_w != nullptr && a->dtype != 0;
   bp.delta = a->delta;
   bp.A = a->A;
   bp.Bm = a->Bm;

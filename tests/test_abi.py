@@ -194,7 +194,7 @@ def test_workspace_queries(lib):
     assert lib.selective_scan_workspace_bytes(2, 64, 0, 256, 1) == 0
     s1 = lib.ss2d_workspace_bytes(1, 16, 8, 8, 4, 0)
     s2 = lib.ss2d_workspace_bytes(1, 16, 8, 8, 4, 1)
-    assert 0 < s2 < s1  # the transposed copy of x is narrower in bf16
+    assert 0 < s2 <= s1  # fp32 intermediates: the I/O type changes no workspace region
     assert lib.ss2d_workspace_bytes(1, 16, 8, 8, 4, 9) == 0
     v1 = lib.vim_bidir_workspace_bytes(2, 8, 197, 16, 1)
     v2 = lib.vim_bidir_workspace_bytes(2, 8, 197, 16, 0)

@@ -35,10 +35,13 @@ CASES = [
     (1, 8, 8, 16, 4, "f32", True, 3, True),
     (2, 7, 9, 20, 16, "f32", True, 5, True),     # ragged, filter wider than the map's short side
     (1, 3, 40, 64, 8, "bf16", True, 3, False),
-    (2, 33, 35, 24, 16, "f32", False, 7, True),  # several 32 x 32 tiles with ragged tails
+    (2, 33, 35, 24, 16, "f32", False, 7, True),  # 7 x 7 filter (halo 3), odd sizes
     (1, 1, 1, 8, 4, "f32", True, 3, True),       # one pixel: only the filter's centre tap sees data
     (2, 14, 14, 70, 16, "bf16", True, 1, True),  # 1 x 1 filter: a per-channel scale and shift
     (1, 64, 64, 64, 16, "f32", True, 3, True),   # few rows: chunked route scans
+    # maps whose halo'd planes exceed 64 KB of LDS: the 32 x 32 tile kernels
+    (1, 100, 90, 8, 4, "f32", True, 5, True),
+    (1, 130, 72, 8, 4, "bf16", True, 3, False),
 ]
 
 
