@@ -13,7 +13,8 @@ kernel, timed live with HIP events on the stream it is launched on) and the fp64
 oracle timed on this host on a bounded sample of the same workload.  `--workload`
 selects one of the other shapes (0-4 SS2D, 5 the Vision Mamba bidirectional scan at
 Vim-Tiny size); `--bwd` adds the fused backward to each step; `--front K` puts the
-input front (depthwise K x K convolution + SiLU) ahead of the SS2D routes.
+input front (depthwise K x K convolution + SiLU) ahead of the SS2D routes; `--ln` adds the
+back half (LayerNorm over the channels of the merged map before the gate).
 
 When one input/output set is smaller than the 256 MB last-level cache (MALL) several
 times over, the steps rotate over independent copies so that no step re-reads what the
@@ -60,6 +61,8 @@ def parse():
     ap.add_argument("--bwd", action="store_true", help="time forward + backward per step")
     ap.add_argument("--front", type=int, default=0,
                     help="SS2D only: K > 0 adds the input front (depthwise K x K convolution + SiLU)")
+    ap.add_argument("--ln", action="store_true",
+                    help="SS2D only: LayerNorm over the channels of the merged map before the gate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time for the sample")
     return ap.parse_args()
@@ -128,7 +131,7 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(cfg, inp, target_s, bwd=False, front=None):
+def cpu_baseline(cfg, inp, target_s, bwd=False, front=None, ln=None):
     """The fp64 oracle (as it stands) on the first images of the same batch (forward, or
     forward + backward when the GPU step includes the backward)."""
     import oracle
@@ -153,7 +156,14 @@ def cpu_baseline(cfg, inp, target_s, bwd=False, front=None):
         args = (sl(inp["x"]), sl(inp["delta"]), inp["A"].astype(np.float64), sl(inp["B"]), sl(inp["C"]),
                 inp["D"].astype(np.float64), inp["delta_bias"].astype(np.float64), sl(inp["z"]))
         t0 = time.perf_counter()
-        if front is not None:
+        if ln is not None:
+            kw = dict(ln_w=ln["ln_w"].astype(np.float64), ln_b=ln["ln_b"].astype(np.float64))
+            if front is not None:
+                kw.update(conv_w=front["conv_w"].astype(np.float64), conv_b=front["conv_b"].astype(np.float64))
+            oracle.ss2d_ln_fwd(*args, **kw)
+            if bwd:
+                oracle.ss2d_ln_bwd(*args, **kw, dout=sl(inp["dout"]))
+        elif front is not None:
             fa = (args[0], front["conv_w"].astype(np.float64), front["conv_b"].astype(np.float64)) + args[1:]
             oracle.ss2d_front_fwd(*fa)
             if bwd:
@@ -173,12 +183,13 @@ def cpu_baseline(cfg, inp, target_s, bwd=False, front=None):
     return {"value": elems / t, "unit": "elements/s", "cores": threads, "kind": "oracle",
             "sample": f"first {nb} of {cfg.batch} {'sequences' if vim else 'images'} (all {cfg.dim} channels, "
                       f"{routes} {'directions' if vim else 'routes'}, L={cfg.seqlen}, N={cfg.dstate}), fp64 C "
-                      f"oracle with OpenMP over rows{', with the input front' if front is not None else ''}, "
+                      f"oracle with OpenMP over rows{', with the input front' if front is not None else ''}"
+                      f"{', with the LayerNorm' if ln is not None else ''}, "
                       f"{'forward + backward' if bwd else 'forward'}, {t:.2f} s wall",
             "cpu_model": cpu_model()}
 
 
-def config_record(cfg, vim, bwd, n_sets, front_k=0):
+def config_record(cfg, vim, bwd, n_sets, front_k=0, ln=False):
     if vim:
         return {"workload": ("vim_bidir_fwd+bwd " if bwd else "vim_bidir_fwd ") + cfg.name, "batch": cfg.batch,
                 "seqlen": cfg.seqlen, "directions": 2, "dim": cfg.dim, "dstate": cfg.dstate, "gate_z": cfg.has_z,
@@ -189,6 +200,9 @@ def config_record(cfg, vim, bwd, n_sets, front_k=0):
     if front_k:
         rec["workload"] = rec["workload"].replace("ss2d_fwd", f"ss2d_fwd(front dwconv{front_k}x{front_k}+silu)", 1)
         rec["front_conv_k"] = front_k
+    if ln:
+        rec["workload"] = rec["workload"].replace(" " + cfg.name, "(+layernorm) " + cfg.name, 1)
+        rec["layer_norm"] = True
     return rec
 
 
@@ -211,11 +225,12 @@ def main():
     workloads = list(synth.CONFIGS) + list(synth.VIM_CONFIGS)
     cfg = workloads[args.workload]
     vim = getattr(cfg, "kind", "ss2d") == "vim"
-    if args.front and vim:
-        print("--front applies to the SS2D workloads only", file=sys.stderr)
+    if (args.front or args.ln) and vim:
+        print("--front and --ln apply to the SS2D workloads only", file=sys.stderr)
         sys.exit(2)
     inp = (synth.make_vim_config_inputs if vim else synth.make_config_inputs)(cfg, with_dout=args.bwd)
     front = synth.make_front_params(cfg.dim, args.front, seed_base=cfg.index) if args.front else None
+    ln = synth.make_ln_params(cfg.dim, seed_base=cfg.index) if args.ln else None
 
     def dev(a, dtype):
         if a is None:
@@ -230,6 +245,8 @@ def main():
           "delta_bias": dev(inp["delta_bias"], "f32"), "z": dev(inp["z"], cfg.dtype) if cfg.has_z else None}
     if front is not None:
         d0.update(conv_w=dev(front["conv_w"], "f32"), conv_b=dev(front["conv_b"], "f32"))
+    if ln is not None:
+        d0.update(ln_w=dev(ln["ln_w"], "f32"), ln_b=dev(ln["ln_b"], "f32"))
     dout0 = dev(inp["dout"], cfg.dtype) if args.bwd else None
     # with --bwd a step is a training step: for SS2D the forward keeps its checkpoint states and
     # the backward runs on them (the Vim backward recomputes its forward)
@@ -316,7 +333,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) inputs, S4D-real A, inverse-softplus dt bias)",
-        "config": config_record(cfg, vim, args.bwd, n_sets, args.front),
+        "config": config_record(cfg, vim, args.bwd, n_sets, args.front, args.ln),
         "step_ms": stats(step_ms),
         "hbm": {"algorithmic_bytes_per_step": step_bytes,
                 "achieved_GBps": hbm_gbps,
@@ -338,7 +355,7 @@ def main():
                         "achieved_GBps": fb / (f_ms * 1e-3) / 1e9, "peak_GBps": HBM_PEAK_GBPS,
                         "frac": fb / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds, args.bwd, front)
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds, args.bwd, front, ln)
     print(json.dumps(res))
 
 

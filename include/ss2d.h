@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SS2D_ABI_VERSION 5
+#define SS2D_ABI_VERSION 6
 
 /* Status codes returned by every entry point. */
 enum {
@@ -240,6 +240,15 @@ typedef struct ss2d_fwd_args {
   const float* conv_w;     /* (dim, conv_k, conv_k) fp32, or NULL: no front (u = x) */
   const float* conv_b;     /* (dim) fp32, may be NULL */
   int conv_k;
+  /* Optional back half [S6 page, section 1: in the VSS block the SS2D features are
+   * layer-normalised, then multiplied by the gate branch]: with layer_norm != 0,
+   *   out = LN(M) * silu(z)  (LN(M) without z),  LN(M)[c] = (M[c] - mu) / sqrt(var + ln_eps) * ln_w[c] + ln_b[c]
+   * with mu, var (biased) over the dim channels of each pixel of the merged map M (the four
+   * routes' sum with its skip term), all in fp32, one rounding at the end. */
+  int layer_norm;
+  const float* ln_w;       /* (dim) fp32, or NULL: 1 */
+  const float* ln_b;       /* (dim) fp32, or NULL: 0 */
+  float ln_eps;            /* >= 0 (1e-5 is the usual LayerNorm default) */
 } ss2d_fwd_args;
 
 int ss2d_fwd(const ss2d_fwd_args* args, hipStream_t stream);
@@ -296,6 +305,14 @@ typedef struct ss2d_bwd_args {
   int conv_k;
   float* dconv_w;
   float* dconv_b;
+  /* the back half, as in ss2d_fwd_args; dln_w, dln_b (dim, fp32, overwritten) receive the
+   * LayerNorm parameters' gradients (required iff ln_w, ln_b are given) */
+  int layer_norm;
+  const float* ln_w;
+  const float* ln_b;
+  float ln_eps;
+  float* dln_w;
+  float* dln_b;
 } ss2d_bwd_args;
 
 int ss2d_bwd(const ss2d_bwd_args* args, hipStream_t stream);

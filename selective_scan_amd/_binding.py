@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libss2d.so")
 
 SS2D_OK, SS2D_ERR_INVALID_ARGUMENT, SS2D_ERR_UNSUPPORTED, SS2D_ERR_HIP = 0, 1, 2, 3
 DTYPE_F32, DTYPE_BF16 = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -44,7 +44,8 @@ class SS2DFwdArgs(ctypes.Structure):
                                   "workspace")] + [
         ("workspace_bytes", _sz), ("batch", _i64), ("dim", _i64), ("height", _i64), ("width", _i64),
         ("dstate", _i64), ("dtype", _int), ("delta_softplus", _int), ("keep_states", _int),
-        ("conv_w", _p), ("conv_b", _p), ("conv_k", _int)]
+        ("conv_w", _p), ("conv_b", _p), ("conv_k", _int),
+        ("layer_norm", _int), ("ln_w", _p), ("ln_b", _p), ("ln_eps", ctypes.c_float)]
 
 
 class SS2DBwdArgs(ctypes.Structure):
@@ -52,7 +53,8 @@ class SS2DBwdArgs(ctypes.Structure):
                                   "ddelta", "dA", "dBm", "dCm", "dDskip", "ddelta_bias", "dz", "workspace")] + [
         ("workspace_bytes", _sz), ("batch", _i64), ("dim", _i64), ("height", _i64), ("width", _i64),
         ("dstate", _i64), ("dtype", _int), ("delta_softplus", _int), ("workspace_has_states", _int),
-        ("conv_w", _p), ("conv_b", _p), ("conv_k", _int), ("dconv_w", _p), ("dconv_b", _p)]
+        ("conv_w", _p), ("conv_b", _p), ("conv_k", _int), ("dconv_w", _p), ("dconv_b", _p),
+        ("layer_norm", _int), ("ln_w", _p), ("ln_b", _p), ("ln_eps", ctypes.c_float), ("dln_w", _p), ("dln_b", _p)]
 
 
 class SsStepArgs(ctypes.Structure):
@@ -268,13 +270,19 @@ def _conv_k(conv_w, dim):
     return k
 
 
+def _ln_on(layer_norm, ln_w, ln_b):
+    return int(bool(layer_norm) or ln_w is not None or ln_b is not None)
+
+
 def ss2d_fwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=True, workspace=None,
-             out=None, keep_states=False, conv_w=None, conv_b=None):
+             out=None, keep_states=False, conv_w=None, conv_b=None, layer_norm=False, ln_w=None, ln_b=None,
+             ln_eps=1e-5):
     """Fused SS2D forward.  x, z: (batch, dim, H, W); delta: (batch, 4, dim, H*W);
     A: (4, dim, N) fp32; B, C: (batch, 4, N, H*W); D, delta_bias: (4, dim) fp32.  With
     keep_states the given workspace keeps what ss2d_bwd(..., workspace_has_states=True) needs.
     conv_w (dim, k, k) and conv_b (dim,), fp32, add the input front: the routes scan
-    silu(depthwise_conv(x) + conv_b) instead of x."""
+    silu(depthwise_conv(x) + conv_b) instead of x.  layer_norm (implied by ln_w or ln_b, fp32
+    (dim,)) adds the back half: out = LayerNorm_channels(merged) * silu(z)."""
     x, delta = _c(x), _c(delta)
     dev = _dev(x)
     B, C, z = _c(B), _c(C), _c(z)
@@ -282,6 +290,7 @@ def ss2d_fwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=
     D = _c(D, torch.float32)
     delta_bias = _c(delta_bias, torch.float32)
     conv_w, conv_b = _c(conv_w, torch.float32), _c(conv_b, torch.float32)
+    ln_w, ln_b = _c(ln_w, torch.float32), _c(ln_b, torch.float32)
     batch, dim, H, W = x.shape
     N = A.shape[-1]
     if out is None:
@@ -292,7 +301,8 @@ def ss2d_fwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=
                     workspace_bytes=ws.numel() * ws.element_size(), batch=batch, dim=dim, height=H, width=W,
                     dstate=N, dtype=_dtype_code(x.dtype), delta_softplus=int(bool(delta_softplus)),
                     keep_states=int(bool(keep_states)), conv_w=_ptr(conv_w), conv_b=_ptr(conv_b),
-                    conv_k=_conv_k(conv_w, dim))
+                    conv_k=_conv_k(conv_w, dim), layer_norm=_ln_on(layer_norm, ln_w, ln_b), ln_w=_ptr(ln_w),
+                    ln_b=_ptr(ln_b), ln_eps=float(ln_eps))
     _check(lib().ss2d_fwd(ctypes.byref(a), _stream(dev)), "ss2d_fwd")
     return out
 
@@ -302,7 +312,8 @@ class SS2DForwardPlan:
     repeated launches (benchmarks, stage timing) cost one ctypes call each."""
 
     def __init__(self, x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=True, workspace=None,
-                 out=None, keep_states=False, conv_w=None, conv_b=None):
+                 out=None, keep_states=False, conv_w=None, conv_b=None, layer_norm=False, ln_w=None, ln_b=None,
+                 ln_eps=1e-5):
         x, delta = _c(x), _c(delta)
         self.device = _dev(x)
         B, C, z = _c(B), _c(C), _c(z)
@@ -310,18 +321,21 @@ class SS2DForwardPlan:
         D = _c(D, torch.float32)
         delta_bias = _c(delta_bias, torch.float32)
         conv_w, conv_b = _c(conv_w, torch.float32), _c(conv_b, torch.float32)
+        ln_w, ln_b = _c(ln_w, torch.float32), _c(ln_b, torch.float32)
         batch, dim, H, W = x.shape
         N = A.shape[-1]
         self.out = torch.empty_like(x) if out is None else out
         self.workspace = _workspace(ss2d_workspace_bytes(batch, dim, H, W, N, x.dtype), self.device, workspace)
-        self._keep = (x, delta, A, B, C, D, delta_bias, z, conv_w, conv_b)
+        self._keep = (x, delta, A, B, C, D, delta_bias, z, conv_w, conv_b, ln_w, ln_b)
         self.args = SS2DFwdArgs(x=_ptr(x), delta=_ptr(delta), A=_ptr(A), Bm=_ptr(B), Cm=_ptr(C), Dskip=_ptr(D),
                                 delta_bias=_ptr(delta_bias), z=_ptr(z), out=_ptr(self.out),
                                 workspace=_ptr(self.workspace),
                                 workspace_bytes=self.workspace.numel() * self.workspace.element_size(),
                                 batch=batch, dim=dim, height=H, width=W, dstate=N, dtype=_dtype_code(x.dtype),
                                 delta_softplus=int(bool(delta_softplus)), keep_states=int(bool(keep_states)),
-                                conv_w=_ptr(conv_w), conv_b=_ptr(conv_b), conv_k=_conv_k(conv_w, dim))
+                                conv_w=_ptr(conv_w), conv_b=_ptr(conv_b), conv_k=_conv_k(conv_w, dim),
+                                layer_norm=_ln_on(layer_norm, ln_w, ln_b), ln_w=_ptr(ln_w), ln_b=_ptr(ln_b),
+                                ln_eps=float(ln_eps))
 
     def run(self):
         _check(lib().ss2d_fwd(ctypes.byref(self.args), _stream(self.device)), "ss2d_fwd")
@@ -333,12 +347,13 @@ class SS2DForwardPlan:
 
 
 def ss2d_bwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, dout=None, delta_softplus=True,
-             workspace=None, workspace_has_states=False, conv_w=None, conv_b=None):
+             workspace=None, workspace_has_states=False, conv_w=None, conv_b=None, layer_norm=False, ln_w=None,
+             ln_b=None, ln_eps=1e-5):
     """Backward of ss2d_fwd; returns a dict of gradients (None for absent inputs).  With
     workspace_has_states, `workspace` must be the one a forward with keep_states=True used for
     the same inputs (the forward is then not recomputed).  With the input front (conv_w,
     conv_b) dx is the gradient w.r.t. the convolution's input and the dict also holds
-    dconv_w and dconv_b."""
+    dconv_w and dconv_b; with the LayerNorm it holds dln_w and dln_b."""
     x, delta, dout = _c(x), _c(delta), _c(dout)
     dev = _dev(x)
     B, C, z = _c(B), _c(C), _c(z)
@@ -348,6 +363,10 @@ def ss2d_bwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, dout=None, delt
     conv_w, conv_b = _c(conv_w, torch.float32), _c(conv_b, torch.float32)
     dconv_w = torch.empty_like(conv_w) if conv_w is not None else None
     dconv_b = torch.empty_like(conv_b) if conv_b is not None else None
+    ln_w, ln_b = _c(ln_w, torch.float32), _c(ln_b, torch.float32)
+    ln = _ln_on(layer_norm, ln_w, ln_b)
+    dln_w = torch.empty_like(ln_w) if ln_w is not None else None
+    dln_b = torch.empty_like(ln_b) if ln_b is not None else None
     batch, dim, H, W = x.shape
     N = A.shape[-1]
     dx, ddelta = torch.empty_like(x), torch.empty_like(delta)
@@ -364,11 +383,14 @@ def ss2d_bwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, dout=None, delt
                     height=H, width=W, dstate=N, dtype=_dtype_code(x.dtype),
                     delta_softplus=int(bool(delta_softplus)), workspace_has_states=int(bool(workspace_has_states)),
                     conv_w=_ptr(conv_w), conv_b=_ptr(conv_b), conv_k=_conv_k(conv_w, dim), dconv_w=_ptr(dconv_w),
-                    dconv_b=_ptr(dconv_b))
+                    dconv_b=_ptr(dconv_b), layer_norm=ln, ln_w=_ptr(ln_w), ln_b=_ptr(ln_b), ln_eps=float(ln_eps),
+                    dln_w=_ptr(dln_w), dln_b=_ptr(dln_b))
     _check(lib().ss2d_bwd(ctypes.byref(a), _stream(dev)), "ss2d_bwd")
     g = {"dx": dx, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "ddelta_bias": dbias, "dz": dz}
     if conv_w is not None:
         g.update(dconv_w=dconv_w, dconv_b=dconv_b)
+    if ln:
+        g.update(dln_w=dln_w, dln_b=dln_b)
     return g
 
 

@@ -145,6 +145,35 @@ inline int64_t front_plane_lds(int64_t H, int64_t W, int k) {
 inline bool front_plane_path(int64_t H, int64_t W, int k) { return front_plane_lds(H, W, k) <= 64 * 1024; }
 inline int64_t front_part_rows(int64_t H, int64_t W, int k) { return front_plane_path(H, W, k) ? 1 : front_tiles(H, W); }
 
+// LayerNorm over the channels of each pixel of an fp32 map M (batch, C, L), then the gate:
+//   out = ((M - mu) * rstd * w[c] + b[c]) * silu(z),  mu, var over c (biased), rstd = 1/sqrt(var + eps)
+// (w, b default to 1, 0; no factor without z).  One workgroup = 64 consecutive pixels of one
+// image (one per lane) x four wavefronts splitting the channels.  Backward: dz, and
+// dM = rstd (g - mean_c g - xhat mean_c(g xhat)) with g = dy w, dy = dout silu(z), in fp32;
+// per-workgroup partial sums of dw = sum dy xhat and db = sum dy, which launch_ln_reduce adds
+// per channel in a fixed order.
+constexpr int kLnPixels = 64;
+struct LnArgs {
+  const float* M;   // (batch, C, L) fp32
+  const float* w;   // (C) or null
+  const float* b;   // (C) or null
+  const void* z;    // (batch, C, L) dtype or null
+  void* out;        // forward: (batch, C, L) dtype
+  const void* dout; // backward: (batch, C, L) dtype
+  float* dM;        // backward: (batch, C, L) fp32
+  void* dz;         // backward: dtype (iff z)
+  float* part;      // backward: (batch * ceil(L / 64), 2, C) fp32
+  float* dw;        // reduce: (C) or null
+  float* db;        // reduce: (C) or null
+  int64_t batch, C, L;
+  float eps;
+  int dtype;
+};
+hipError_t launch_ln_gate_fwd(const LnArgs& a, hipStream_t s);
+hipError_t launch_ln_gate_bwd(const LnArgs& a, hipStream_t s);
+hipError_t launch_ln_reduce(const LnArgs& a, hipStream_t s);
+inline int64_t ln_part_rows(int64_t batch, int64_t L) { return batch * ((L + kLnPixels - 1) / kLnPixels); }
+
 // Writes n fp32 zeros (a kernel, so that graph capture records no memset node).
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 

@@ -98,7 +98,7 @@ ScanLayout scan_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqle
 
 // ---- SS2D workspace layout -----------------------------------------------------------
 struct SS2DLayout {
-  int64_t off_xT, off_ys, off_scan, off_merged, off_dM, off_dMT, off_xc, off_cpart, total;
+  int64_t off_xT, off_ys, off_scan, off_merged, off_dM, off_dMT, off_xc, off_cpart, off_lnpart, total;
   ScanLayout scan;
 };
 
@@ -115,6 +115,7 @@ SS2DLayout ss2d_layout(int64_t batch, int64_t dim, int64_t H, int64_t W, int64_t
   l.off_dMT = o;    o += align_up(batch * dim * L * 4);
   l.off_xc = o;     o += align_up(batch * dim * L * 4);                            // input front output (fp32)
   l.off_cpart = o;  o += align_up(batch * dim * front_tiles(H, W) * (kFrontMaxK * kFrontMaxK + 1) * 4);
+  l.off_lnpart = o; o += align_up(ln_part_rows(batch, L) * 2 * dim * 4);  // LayerNorm parameter partials
   l.total = o;
   return l;
 }
@@ -381,22 +382,39 @@ static int ss2d_scan_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, bool k
   return status_from(launch_scan_fwd(p, stream));
 }
 
-static int ss2d_merge_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, float* merged, hipStream_t stream) {
+static int ss2d_merge_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, hipStream_t stream) {
   MergeArgs m{};
   m.routes = at(a->workspace, lay.off_ys);
   m.routes_f32 = 1;  // the scan stage writes fp32 route outputs
   m.x = scan_input(a->x, a->conv_w, a->workspace, lay);
   m.x_f32 = a->conv_w != nullptr;
   m.Dskip = a->Dskip;
-  m.z = a->z;
-  m.y = a->out;
-  m.merged_f32 = merged;
   m.batch = a->batch;
   m.C = a->dim;
   m.H = a->height;
   m.W = a->width;
   m.dtype = a->dtype;
-  return status_from(launch_merge(m, stream));
+  if (!a->layer_norm) {
+    m.z = a->z;
+    m.y = a->out;
+    return status_from(launch_merge(m, stream));
+  }
+  // with the LayerNorm: the fp32 merged map, then the normalisation and the gate per pixel
+  float* merged = reinterpret_cast<float*>(at(a->workspace, lay.off_merged));
+  m.merged_f32 = merged;
+  if (launch_merge(m, stream) != hipSuccess) return SS2D_ERR_HIP;
+  LnArgs l{};
+  l.M = merged;
+  l.w = a->ln_w;
+  l.b = a->ln_b;
+  l.z = a->z;
+  l.out = a->out;
+  l.batch = a->batch;
+  l.C = a->dim;
+  l.L = a->height * a->width;
+  l.eps = a->ln_eps;
+  l.dtype = a->dtype;
+  return status_from(launch_ln_gate_fwd(l, stream));
 }
 
 static int check_ss2d(int64_t batch, int64_t dim, int64_t height, int64_t width, int64_t dstate, int dtype) {
@@ -404,6 +422,14 @@ static int check_ss2d(int64_t batch, int64_t dim, int64_t height, int64_t width,
   if (batch < 0 || dim < 0 || height < 0 || width < 0) return SS2D_ERR_INVALID_ARGUMENT;
   if (dstate < 1 || dstate > 64) return SS2D_ERR_UNSUPPORTED;
   if (height > (1 << 30) || width > (1 << 30)) return SS2D_ERR_INVALID_ARGUMENT;
+  return SS2D_OK;
+}
+
+// The LayerNorm parameters: fp32, 4-byte aligned; eps finite and >= 0.
+static int check_ln(int on, const float* w, const float* b, float eps) {
+  if (!on) return SS2D_OK;
+  if ((w && !aligned(w, 4)) || (b && !aligned(b, 4))) return SS2D_ERR_INVALID_ARGUMENT;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return SS2D_ERR_INVALID_ARGUMENT;
   return SS2D_OK;
 }
 
@@ -422,6 +448,7 @@ static int validate_ss2d_fwd(const ss2d_fwd_args* a, SS2DLayout* lay, bool* empt
   if (!a) return SS2D_ERR_INVALID_ARGUMENT;
   int st = check_ss2d(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype);
   if (st == SS2D_OK) st = check_front(a->conv_w, a->conv_b, a->conv_k);
+  if (st == SS2D_OK) st = check_ln(a->layer_norm, a->ln_w, a->ln_b, a->ln_eps);
   if (st != SS2D_OK) return st;
   if (a->batch * a->dim * a->height * a->width == 0) {
     *empty = true;
@@ -444,7 +471,7 @@ int ss2d_fwd(const ss2d_fwd_args* a, hipStream_t stream) {
   if (st != SS2D_OK || empty) return st;
   st = ss2d_transpose_stage(a, lay, stream);
   if (st == SS2D_OK) st = ss2d_scan_stage(a, lay, a->keep_states != 0, stream);
-  if (st == SS2D_OK) st = ss2d_merge_stage(a, lay, nullptr, stream);
+  if (st == SS2D_OK) st = ss2d_merge_stage(a, lay, stream);
   return st;
 }
 
@@ -456,7 +483,7 @@ int ss2d_fwd_stage(const ss2d_fwd_args* a, int stage, hipStream_t stream) {
   if (st != SS2D_OK || empty) return st;
   if (stage == SS2D_STAGE_TRANSPOSE) return ss2d_transpose_stage(a, lay, stream);
   if (stage == SS2D_STAGE_SCAN) return ss2d_scan_stage(a, lay, a->keep_states != 0, stream);
-  return ss2d_merge_stage(a, lay, nullptr, stream);
+  return ss2d_merge_stage(a, lay, stream);
 }
 
 // The forward scans with no outputs: only the checkpoint states (for a backward without them).
@@ -615,11 +642,14 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
   if (!a) return SS2D_ERR_INVALID_ARGUMENT;
   int st = check_ss2d(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype);
   if (st == SS2D_OK) st = check_front(a->conv_w, a->conv_b, a->conv_k);
+  if (st == SS2D_OK) st = check_ln(a->layer_norm, a->ln_w, a->ln_b, a->ln_eps);
   if (st != SS2D_OK) return st;
+  const bool lnw = a->layer_norm && a->ln_w, lnb = a->layer_norm && a->ln_b;
   if ((a->Dskip && !a->dDskip) || (a->delta_bias && !a->ddelta_bias) || (a->z && !a->dz) ||
-      (a->conv_w && !a->dconv_w) || (a->conv_b && !a->dconv_b))
+      (a->conv_w && !a->dconv_w) || (a->conv_b && !a->dconv_b) || (lnw && !a->dln_w) || (lnb && !a->dln_b))
     return SS2D_ERR_INVALID_ARGUMENT;
-  if ((a->dconv_w && !aligned(a->dconv_w, 4)) || (a->dconv_b && !aligned(a->dconv_b, 4)))
+  if ((a->dconv_w && !aligned(a->dconv_w, 4)) || (a->dconv_b && !aligned(a->dconv_b, 4)) ||
+      (a->dln_w && !aligned(a->dln_w, 4)) || (a->dln_b && !aligned(a->dln_b, 4)))
     return SS2D_ERR_INVALID_ARGUMENT;
   if (a->dim == 0) return SS2D_OK;
   if (!a->dA) return SS2D_ERR_INVALID_ARGUMENT;
@@ -629,6 +659,8 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
     if (st == SS2D_OK && a->conv_w)
       st = zero_param_grads(a->dconv_w, a->conv_b ? a->dconv_b : nullptr, nullptr, a->dim,
                             int64_t(a->conv_k) * a->conv_k, stream);
+    if (st == SS2D_OK && lnw) st = status_from(launch_fill_zero(a->dln_w, a->dim, stream));
+    if (st == SS2D_OK && lnb) st = status_from(launch_fill_zero(a->dln_b, a->dim, stream));
     return st;
   }
   if (!a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->dout || !a->dx || !a->ddelta || !a->dBm || !a->dCm ||
@@ -675,26 +707,66 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
     if (st != SS2D_OK) return st;
   }
 
-  // gate (with the pre-gate merge it needs): dz, and dM = dout * silu(z) in grid and
-  // transposed order
-  MergeGateArgs gb{};
   const void* u = scan_input(a->x, a->conv_w, a->workspace, lay);
-  gb.routes = reinterpret_cast<const float*>(at(a->workspace, lay.off_ys));
-  gb.x = u;
-  gb.x_f32 = a->conv_w != nullptr;
-  gb.Dskip = a->Dskip;
-  gb.z = a->z;
-  gb.dout = a->dout;
-  gb.dz = a->dz;
-  gb.dM = reinterpret_cast<float*>(at(a->workspace, lay.off_dM));
-  gb.dMT = reinterpret_cast<float*>(at(a->workspace, lay.off_dMT));
-  gb.merged = reinterpret_cast<float*>(at(a->workspace, lay.off_merged));
-  gb.batch = a->batch;
-  gb.C = a->dim;
-  gb.H = a->height;
-  gb.W = a->width;
-  gb.dtype = a->dtype;
-  if (launch_merge_gate_bwd(gb, stream) != hipSuccess) return SS2D_ERR_HIP;
+  if (a->layer_norm) {
+    // the LayerNorm's and the gate's backward need the whole pixel: the fp32 merged map first,
+    // then dz, dM (grid order) and the parameter partials per pixel block, then dM transposed
+    float* merged = reinterpret_cast<float*>(at(a->workspace, lay.off_merged));
+    float* dM = reinterpret_cast<float*>(at(a->workspace, lay.off_dM));
+    MergeArgs m{};
+    m.routes = at(a->workspace, lay.off_ys);
+    m.routes_f32 = 1;
+    m.x = u;
+    m.x_f32 = a->conv_w != nullptr;
+    m.Dskip = a->Dskip;
+    m.merged_f32 = merged;
+    m.batch = a->batch;
+    m.C = a->dim;
+    m.H = a->height;
+    m.W = a->width;
+    m.dtype = a->dtype;
+    if (launch_merge(m, stream) != hipSuccess) return SS2D_ERR_HIP;
+    LnArgs l{};
+    l.M = merged;
+    l.w = a->ln_w;
+    l.b = a->ln_b;
+    l.z = a->z;
+    l.dout = a->dout;
+    l.dM = dM;
+    l.dz = a->dz;
+    l.part = reinterpret_cast<float*>(at(a->workspace, lay.off_lnpart));
+    l.dw = a->ln_w ? a->dln_w : nullptr;
+    l.db = a->ln_b ? a->dln_b : nullptr;
+    l.batch = a->batch;
+    l.C = a->dim;
+    l.L = L;
+    l.eps = a->ln_eps;
+    l.dtype = a->dtype;
+    if (launch_ln_gate_bwd(l, stream) != hipSuccess || launch_ln_reduce(l, stream) != hipSuccess) return SS2D_ERR_HIP;
+    if (launch_transpose(dM, at(a->workspace, lay.off_dMT), a->batch, a->dim, a->height, a->width, 4, stream) !=
+        hipSuccess)
+      return SS2D_ERR_HIP;
+  } else {
+    // gate (with the pre-gate merge it needs): dz, and dM = dout * silu(z) in grid and
+    // transposed order
+    MergeGateArgs gb{};
+    gb.routes = reinterpret_cast<const float*>(at(a->workspace, lay.off_ys));
+    gb.x = u;
+    gb.x_f32 = a->conv_w != nullptr;
+    gb.Dskip = a->Dskip;
+    gb.z = a->z;
+    gb.dout = a->dout;
+    gb.dz = a->dz;
+    gb.dM = reinterpret_cast<float*>(at(a->workspace, lay.off_dM));
+    gb.dMT = reinterpret_cast<float*>(at(a->workspace, lay.off_dMT));
+    gb.merged = reinterpret_cast<float*>(at(a->workspace, lay.off_merged));
+    gb.batch = a->batch;
+    gb.C = a->dim;
+    gb.H = a->height;
+    gb.W = a->width;
+    gb.dtype = a->dtype;
+    if (launch_merge_gate_bwd(gb, stream) != hipSuccess) return SS2D_ERR_HIP;
+  }
 
   // adjoint scans of the four routes; du (fp32, route order) reuses the route-output region
   ScanBwdParams bp{};
@@ -707,8 +779,8 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
   bp.Cm = a->Cm;
   bp.Dskip = a->Dskip;
   bp.delta_bias = a->delta_bias;
-  bp.dout = gb.dM;
-  bp.doutT = gb.dMT;
+  bp.dout = at(a->workspace, lay.off_dM);
+  bp.doutT = at(a->workspace, lay.off_dMT);
   bp.du = at(a->workspace, lay.off_ys);
   bp.ddelta = a->ddelta;
   bp.batch = a->batch;

@@ -18,7 +18,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-T_X, T_Z, T_DELTA, T_B, T_C, T_U, T_DOUT, T_CONV = range(8)
+T_X, T_Z, T_DELTA, T_B, T_C, T_U, T_DOUT, T_CONV, T_LN = range(9)
 
 
 @dataclass(frozen=True)
@@ -141,6 +141,15 @@ def make_front_params(dim: int, k: int, seed_base: int = 0, with_bias: bool = Tr
     w = (rng.standard_normal(size=(dim, k, k), dtype=np.float32) / np.float32(k)).astype(np.float32)
     b = (np.float32(0.1) * rng.standard_normal(size=(dim,), dtype=np.float32)) if with_bias else None
     return {"conv_w": w, "conv_b": b}
+
+
+def make_ln_params(dim: int, seed_base: int = 0) -> dict:
+    """LayerNorm parameters of the VSS block's back half: ln_w = 1 + N(0, 0.3^2), ln_b = N(0, 0.2^2),
+    fp32 (dim,)."""
+    rng = np.random.Generator(np.random.PCG64(1000 * seed_base + T_LN))
+    w = (1.0 + 0.3 * rng.standard_normal(size=(dim,), dtype=np.float32)).astype(np.float32)
+    b = (np.float32(0.2) * rng.standard_normal(size=(dim,), dtype=np.float32)).astype(np.float32)
+    return {"ln_w": w, "ln_b": b}
 
 
 def make_config_inputs(cfg: SS2DConfig, with_dout: bool | None = None) -> dict:

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ss2d_abi_version() == 5
+    assert lib.ss2d_abi_version() == 6
     assert lib.ss2d_status_string(0) == b"ok"
     assert b"invalid" in lib.ss2d_status_string(1)
     assert b"unsupported" in lib.ss2d_status_string(2)
@@ -141,6 +141,13 @@ def test_ss2d_rejects(lib):
     assert lib.ss2d_bwd(ctypes.byref(SS2DBwdArgs(**{**b, **big})), None) == 1                 # no dconv_w
     assert lib.ss2d_bwd(ctypes.byref(SS2DBwdArgs(**{**b, **big, "dconv_w": 0xf000, "conv_b": 0xe000})),
                         None) == 1                                                            # no dconv_b
+    # the LayerNorm: eps finite and >= 0, aligned parameters, gradients need outputs
+    for eps in (-1.0, float("nan"), float("inf")):
+        assert lib.ss2d_fwd(ctypes.byref(SS2DFwdArgs(**{**f, "layer_norm": 1, "ln_eps": eps})), None) == 1, eps
+    assert lib.ss2d_fwd(ctypes.byref(SS2DFwdArgs(**{**f, "layer_norm": 1, "ln_w": 0xd001})), None) == 1
+    ln = dict(workspace_bytes=1 << 40, dz=0, layer_norm=1, ln_eps=1e-5)
+    assert lib.ss2d_bwd(ctypes.byref(SS2DBwdArgs(**{**b, **ln, "ln_w": 0xd000})), None) == 1        # no dln_w
+    assert lib.ss2d_bwd(ctypes.byref(SS2DBwdArgs(**{**b, **ln, "ln_b": 0xd000})), None) == 1        # no dln_b
 
 
 def test_vim_bidir_rejects(lib):
