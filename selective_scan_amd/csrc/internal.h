@@ -148,7 +148,7 @@ inline int64_t front_part_rows(int64_t H, int64_t W, int k) { return front_plane
 // LayerNorm over the channels of each pixel of an fp32 map M (batch, C, L), then the gate:
 //   out = ((M - mu) * rstd * w[c] + b[c]) * silu(z),  mu, var over c (biased), rstd = 1/sqrt(var + eps)
 // (w, b default to 1, 0; no factor without z).  One workgroup = 64 consecutive pixels of one
-// image (one per lane) x four wavefronts splitting the channels.  Backward: dz, and
+// image (one per lane) x eight wavefronts splitting the channels.  Backward: dz, and
 // dM = rstd (g - mean_c g - xhat mean_c(g xhat)) with g = dy w, dy = dout silu(z), in fp32;
 // per-workgroup partial sums of dw = sum dy xhat and db = sum dy, which launch_ln_reduce adds
 // per channel in a fixed order.

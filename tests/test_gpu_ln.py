@@ -48,6 +48,8 @@ CASES = [
     (2, 9, 11, 24, 16, "bf16", True, True, 3),     # with the input front
     (1, 64, 64, 64, 16, "f32", True, True, 0),     # few rows: chunked route scans
     (1, 130, 72, 8, 4, "bf16", True, True, 5),     # the front's tile path
+    (1, 4, 6, 300, 4, "f32", True, True, 0),       # more than 256 channels: the map is read twice
+    (2, 5, 7, 260, 4, "bf16", True, False, 0),
 ]
 
 
