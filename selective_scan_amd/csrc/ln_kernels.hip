@@ -48,6 +48,23 @@ __device__ __forceinline__ float pixel_sum(float (*red)[kLnPixels], float v) {
   return s;
 }
 
+// LayerNorm scale and shift of the (at most 8 kPer) channels in LDS, so that the per-channel
+// reads in the output pass are LDS reads rather than global loads (whose waits would also wait
+// for the pass's own stores).  Ordered before use by the barriers of the statistics.
+template <int kPer>
+struct LnParams {
+  float w[kPer > 0 ? kWaves * kPer : 1], b[kPer > 0 ? kWaves * kPer : 1];
+};
+template <int kPer>
+__device__ __forceinline__ void stage_params(const LnArgs& a, LnParams<kPer>& p) {
+  if constexpr (kPer > 0) {
+    for (int c = threadIdx.x; c < a.C; c += kThreads) {
+      p.w[c] = a.w ? a.w[c] : 1.0f;
+      p.b[c] = a.b ? a.b[c] : 0.0f;
+    }
+  }
+}
+
 // Shifted sums of the pixel's channels over the wavefronts (each value less the pixel's
 // first channel, so that a large mean does not cancel the variance's digits): the mean and
 // 1/std.  s1 = sum (m - shift), s2 = sum (m - shift)^2 of this lane's channels.
@@ -64,115 +81,149 @@ __device__ __forceinline__ void finish_stats(const LnArgs& a, float (*r1)[kLnPix
 
 // kPer > 0: the C <= 8 kPer channels of a lane are held in registers between the passes (the
 // map is read once); kPer = 0: the map is read again for each pass (wide channel counts).
-template <typename T, int kPer>
+// Loads are unconditional (channel index clamped, inactive pixels read pixel 0) so that they are
+// all in flight together; out-of-range values are masked by selects.
+template <typename T, int kPer, bool kZ>
 __global__ __launch_bounds__(kThreads) void ln_gate_fwd_kernel(LnArgs a) {
   __shared__ float r1[kWaves][kLnPixels], r2[kWaves][kLnPixels];
+  __shared__ LnParams<kPer> prm;
   const PixelBlock pb = pixel_block(a);
-  const int wv = threadIdx.x / kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
   const float* m = a.M + pb.base;
-  const float shift = pb.active ? m[0] : 0.0f;
+  const T* zg = kZ ? static_cast<const T*>(a.z) + pb.base : nullptr;
+  const float shift = m[0];
   float s1 = 0.0f, s2 = 0.0f;
-  float mv[kPer > 0 ? kPer : 1];
-  if (pb.active) {
-    if constexpr (kPer > 0) {
+  constexpr int kArr = kPer > 0 ? kPer : 1;
+  float mv[kArr], zv[kArr] = {};
+  if constexpr (kPer > 0) {
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int64_t c = wv + int64_t(kWaves) * i;
-        mv[i] = c < a.C ? m[c * a.L] : 0.0f;
-      }
+    for (int i = 0; i < kPer; ++i) {
+      const int64_t c = wv + int64_t(kWaves) * i, cc = c < a.C ? c : a.C - 1;
+      mv[i] = m[cc * a.L];
+      if constexpr (kZ) zv[i] = Elem<T>::load(zg, cc * a.L);  // the gate's loads overlap the statistics
+    }
+    stage_params<kPer>(a, prm);  // while the loads are in flight
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        if (wv + int64_t(kWaves) * i < a.C) {
-          const float v = mv[i] - shift;
-          s1 += v;
-          s2 = fmaf(v, v, s2);
-        }
-      }
-    } else {
+    for (int i = 0; i < kPer; ++i) {
+      const float v = (wv + int64_t(kWaves) * i < a.C) ? mv[i] - shift : 0.0f;
+      s1 += v;
+      s2 = fmaf(v, v, s2);
+    }
+  } else {
 #pragma unroll 4
-      for (int64_t c = wv; c < a.C; c += kWaves) {
-        const float v = m[c * a.L] - shift;
-        s1 += v;
-        s2 = fmaf(v, v, s2);
-      }
+    for (int64_t c = wv; c < a.C; c += kWaves) {
+      const float v = m[c * a.L] - shift;
+      s1 += v;
+      s2 = fmaf(v, v, s2);
     }
   }
   float mu, rstd;
   finish_stats(a, r1, r2, shift, s1, s2, mu, rstd);
   if (!pb.active) return;
-  const T* zg = a.z ? static_cast<const T*>(a.z) + pb.base : nullptr;
   T* og = static_cast<T*>(a.out) + pb.base;
-  auto emit = [&](int64_t c, float mval) {
-    const int64_t o = c * a.L;
+  auto emit = [&](int64_t c, float mval, float zval) {
     float y = (mval - mu) * rstd;
-    y = fmaf(y, a.w ? a.w[c] : 1.0f, a.b ? a.b[c] : 0.0f);
-    if (zg) y *= silu(Elem<T>::load(zg, o));
-    Elem<T>::store(og, o, y);
+    if constexpr (kPer > 0)
+      y = fmaf(y, prm.w[c], prm.b[c]);
+    else
+      y = fmaf(y, a.w ? a.w[c] : 1.0f, a.b ? a.b[c] : 0.0f);
+    if constexpr (kZ) y *= silu(zval);
+    Elem<T>::store(og, c * a.L, y);
   };
   if constexpr (kPer > 0) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int64_t c = wv + int64_t(kWaves) * i;
-      if (c < a.C) emit(c, mv[i]);
+      if (c < a.C) emit(c, mv[i], zv[i]);
     }
   } else {
 #pragma unroll 4
-    for (int64_t c = wv; c < a.C; c += kWaves) emit(c, m[c * a.L]);
+    for (int64_t c = wv; c < a.C; c += kWaves) emit(c, m[c * a.L], kZ ? Elem<T>::load(zg, c * a.L) : 0.0f);
   }
 }
 
-// Sum over the 64 lanes (pixels) of a wavefront; every lane receives it.
+// Sum over the 64 lanes (pixels) of a wavefront, returned wave-uniform: within each row of 16
+// lanes by DPP shifts (row_shr 1, 2, 4, 8 with zero fill; lane 15 of the row ends with the row's
+// sum), then the four rows' last lanes added in a fixed order.
+__device__ __forceinline__ float dpp_shr_add(float v, int ctrl_shift) {
+  int src = __builtin_bit_cast(int, v), sh;
+  switch (ctrl_shift) {
+    case 1: sh = __builtin_amdgcn_update_dpp(0, src, 0x111, 0xF, 0xF, true); break;
+    case 2: sh = __builtin_amdgcn_update_dpp(0, src, 0x112, 0xF, 0xF, true); break;
+    case 4: sh = __builtin_amdgcn_update_dpp(0, src, 0x114, 0xF, 0xF, true); break;
+    default: sh = __builtin_amdgcn_update_dpp(0, src, 0x118, 0xF, 0xF, true); break;
+  }
+  return v + __builtin_bit_cast(float, sh);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = kWave / 2; m >= 1; m /= 2) v += __shfl_xor(v, m, kWave);
-  return v;
+  v = dpp_shr_add(v, 1);
+  v = dpp_shr_add(v, 2);
+  v = dpp_shr_add(v, 4);
+  v = dpp_shr_add(v, 8);
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 15));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 31));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 47));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 63));
+  return ((r0 + r1) + r2) + r3;
 }
 
 // One pass gathers everything the pixel needs: with dy = dout silu(z) (dout without a gate),
 // g = dy w, and m' = m - shift, the sums of m', m'^2, g and g m' give the mean, 1/std and the
 // two means of the gradient formula (sum g xhat = rstd (sum g m' - (mu - shift) sum g)).
 // The second pass writes dM, dz and the per-channel partials of dw and db.
-template <typename T, int kPer>
+template <typename T, int kPer, bool kZ>
 __global__ __launch_bounds__(kThreads) void ln_gate_bwd_kernel(LnArgs a) {
   __shared__ float r1[kWaves][kLnPixels], r2[kWaves][kLnPixels];
+  __shared__ LnParams<kPer> prm;
   const PixelBlock pb = pixel_block(a);
-  const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave), lane = threadIdx.x % kWave;
   const float* m = a.M + pb.base;
-  const T* zg = a.z ? static_cast<const T*>(a.z) + pb.base : nullptr;
+  const T* zg = kZ ? static_cast<const T*>(a.z) + pb.base : nullptr;
   const T* gg = static_cast<const T*>(a.dout) + pb.base;
-  const float shift = pb.active ? m[0] : 0.0f;
+  auto wt = [&](int64_t c) {
+    if constexpr (kPer > 0) return prm.w[c];
+    else return a.w ? a.w[c] : 1.0f;
+  };
+  auto bs = [&](int64_t c) {
+    if constexpr (kPer > 0) return prm.b[c];
+    else return a.b ? a.b[c] : 0.0f;
+  };
+  const float shift = m[0];
   float s1 = 0.0f, s2 = 0.0f, sg = 0.0f, sgm = 0.0f;
   constexpr int kArr = kPer > 0 ? kPer : 1;
-  float mv[kArr], gv[kArr], zv[kArr];
+  float mv[kArr], gv[kArr], zv[kArr] = {};
   auto gather = [&](int64_t c, float mval, float gout, float zval) {
-    const float dy = zg ? gout * silu(zval) : gout;
-    const float g = dy * (a.w ? a.w[c] : 1.0f);
+    const float dy = kZ ? gout * silu(zval) : gout;
+    const float g = dy * wt(c);
     const float v = mval - shift;
     s1 += v;
     s2 = fmaf(v, v, s2);
     sg += g;
     sgm = fmaf(g, v, sgm);
   };
-  if (pb.active) {
-    if constexpr (kPer > 0) {
+  if constexpr (kPer > 0) {
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int64_t c = wv + int64_t(kWaves) * i;
-        const bool in = c < a.C;
-        mv[i] = in ? m[c * a.L] : 0.0f;
-        gv[i] = in ? Elem<T>::load(gg, c * a.L) : 0.0f;
-        zv[i] = (in && zg) ? Elem<T>::load(zg, c * a.L) : 0.0f;
-      }
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int64_t c = wv + int64_t(kWaves) * i;
-        if (c < a.C) gather(c, mv[i], gv[i], zv[i]);
-      }
-    } else {
-#pragma unroll 4
-      for (int64_t c = wv; c < a.C; c += kWaves)
-        gather(c, m[c * a.L], Elem<T>::load(gg, c * a.L), zg ? Elem<T>::load(zg, c * a.L) : 0.0f);
+    for (int i = 0; i < kPer; ++i) {
+      const int64_t c = wv + int64_t(kWaves) * i, cc = c < a.C ? c : a.C - 1;
+      mv[i] = m[cc * a.L];
+      gv[i] = Elem<T>::load(gg, cc * a.L);
+      if constexpr (kZ) zv[i] = Elem<T>::load(zg, cc * a.L);
     }
+  }
+  stage_params<kPer>(a, prm);  // while the loads are in flight
+  __syncthreads();
+  if constexpr (kPer > 0) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int64_t c = wv + int64_t(kWaves) * i;
+      if (c < a.C) gather(c, mv[i], gv[i], zv[i]);
+    }
+  } else {
+#pragma unroll 4
+    for (int64_t c = wv; c < a.C; c += kWaves)
+      gather(c, m[c * a.L], Elem<T>::load(gg, c * a.L), kZ ? Elem<T>::load(zg, c * a.L) : 0.0f);
   }
   float mu, rstd;
   finish_stats(a, r1, r2, shift, s1, s2, mu, rstd);
@@ -181,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void ln_gate_bwd_kernel(LnArgs a) {
   const float mg = tg * inv;
   const float mgx = rstd * (tgm - (mu - shift) * tg) * inv;
   float* dmg = a.dM + pb.base;
-  T* dzg = a.z ? static_cast<T*>(a.dz) + pb.base : nullptr;
+  T* dzg = kZ ? static_cast<T*>(a.dz) + pb.base : nullptr;
   float* part = a.part + int64_t(blockIdx.x) * 2 * a.C;
   auto emit = [&](int64_t c, float mval, float gout, float zval) {
     const int64_t o = c * a.L;
@@ -189,13 +240,13 @@ __global__ __launch_bounds__(kThreads) void ln_gate_bwd_kernel(LnArgs a) {
     if (pb.active) {
       const float xh = (mval - mu) * rstd;
       float dy = gout;
-      if (zg) {
+      if constexpr (kZ) {
         const float sz = sigmoid(zval);
         dy *= zval * sz;
-        const float y = fmaf(xh, a.w ? a.w[c] : 1.0f, a.b ? a.b[c] : 0.0f);
+        const float y = fmaf(xh, wt(c), bs(c));
         Elem<T>::store(dzg, o, gout * y * sz * (1.0f + zval * (1.0f - sz)));
       }
-      const float g = dy * (a.w ? a.w[c] : 1.0f);
+      const float g = dy * wt(c);
       dmg[o] = rstd * (g - mg - xh * mgx);
       pw = dy * xh;
       pbias = dy;
@@ -217,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void ln_gate_bwd_kernel(LnArgs a) {
     for (int64_t c = wv; c < a.C; c += kWaves) {
       const bool act = pb.active;
       emit(c, act ? m[c * a.L] : 0.0f, act ? Elem<T>::load(gg, c * a.L) : 0.0f,
-           (act && zg) ? Elem<T>::load(zg, c * a.L) : 0.0f);
+           (kZ && act) ? Elem<T>::load(zg, c * a.L) : 0.0f);
     }
   }
 }
@@ -255,27 +306,30 @@ __global__ __launch_bounds__(kThreads) void ln_reduce_kernel(LnArgs a, int64_t r
 // channels per lane held in registers: up to 32 (C <= 256), else the map is re-read
 constexpr int kRegPer = 32;
 
-template <template <typename, int> class K>
+template <template <typename, int, bool> class K>
 hipError_t launch_ln(const LnArgs& a, hipStream_t s) {
   const int64_t blocks = ln_part_rows(a.batch, a.L);
   if (blocks == 0 || a.C == 0) return hipSuccess;
   if (blocks > int64_t(UINT32_MAX)) return hipErrorInvalidValue;
   const dim3 g{uint32_t(blocks)}, b{kThreads};
-  const bool regs = a.C <= int64_t(kWaves) * kRegPer;
-  if (a.dtype == 0)
-    regs ? K<float, kRegPer>::run(a, g, b, s) : K<float, 0>::run(a, g, b, s);
-  else
-    regs ? K<bf16, kRegPer>::run(a, g, b, s) : K<bf16, 0>::run(a, g, b, s);
+  const bool regs = a.C <= int64_t(kWaves) * kRegPer, z = a.z != nullptr;
+  if (a.dtype == 0) {
+    if (regs) z ? K<float, kRegPer, true>::run(a, g, b, s) : K<float, kRegPer, false>::run(a, g, b, s);
+    else z ? K<float, 0, true>::run(a, g, b, s) : K<float, 0, false>::run(a, g, b, s);
+  } else {
+    if (regs) z ? K<bf16, kRegPer, true>::run(a, g, b, s) : K<bf16, kRegPer, false>::run(a, g, b, s);
+    else z ? K<bf16, 0, true>::run(a, g, b, s) : K<bf16, 0, false>::run(a, g, b, s);
+  }
   return hipGetLastError();
 }
 
-template <typename T, int kPer>
+template <typename T, int kPer, bool kZ>
 struct FwdK {
-  static void run(const LnArgs& a, dim3 g, dim3 b, hipStream_t s) { ln_gate_fwd_kernel<T, kPer><<<g, b, 0, s>>>(a); }
+  static void run(const LnArgs& a, dim3 g, dim3 b, hipStream_t s) { ln_gate_fwd_kernel<T, kPer, kZ><<<g, b, 0, s>>>(a); }
 };
-template <typename T, int kPer>
+template <typename T, int kPer, bool kZ>
 struct BwdK {
-  static void run(const LnArgs& a, dim3 g, dim3 b, hipStream_t s) { ln_gate_bwd_kernel<T, kPer><<<g, b, 0, s>>>(a); }
+  static void run(const LnArgs& a, dim3 g, dim3 b, hipStream_t s) { ln_gate_bwd_kernel<T, kPer, kZ><<<g, b, 0, s>>>(a); }
 };
 
 }  // namespace
