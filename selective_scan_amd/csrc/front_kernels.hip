@@ -69,21 +69,36 @@ __device__ __forceinline__ void zero_halo(float* s, int H, int W) {
 }
 
 // Copies an H x W plane into the interior of a halo'd LDS array (pixel (h, w) at
-// (h + R) * ld + w + R); vec: H*W % 4 == 0 and the plane 4-element aligned.
+// (h + R) * ld + w + R); vec: H*W % 4 == 0 and the plane 4-element aligned.  The vector path
+// issues kBatch loads per thread before writing any of them: loads past the plane read a valid
+// address instead and their values go to the spare LDS word `trash`, so that neither the loads
+// nor the writes sit behind a branch (a load moved into a conditional block would be waited for
+// on its own, one round trip per load).
+constexpr int kBatch = 4;
 template <int R, typename T>
-__device__ __forceinline__ void stage_plane(float* s, const T* g, int H, int W, bool vec) {
+__device__ __forceinline__ void stage_plane(float* s, float* trash, const T* g, int H, int W, bool vec) {
   const int ld = W + 2 * R, L = H * W;
   if (vec) {
-    for (int p = 4 * int(threadIdx.x); p < L; p += 4 * kThreads) {
-      const float4 v = Elem<T>::load4(g, p);
-      const float vv[4] = {v.x, v.y, v.z, v.w};
-      int h = p / W, w = p - h * W;
+    for (int p0 = 4 * int(threadIdx.x); p0 < L; p0 += 4 * kThreads * kBatch) {
+      float4 v[kBatch];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        s[(h + R) * ld + w + R] = vv[j];
-        if (++w == W) {
-          w = 0;
-          ++h;
+      for (int u = 0; u < kBatch; ++u) {
+        const int p = p0 + 4 * kThreads * u;
+        v[u] = Elem<T>::load4(g, p < L ? p : p0);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int p = p0 + 4 * kThreads * u;
+        const bool in = p < L;
+        const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        int h = in ? p / W : 0, w = in ? p - h * W : 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          *(in ? s + (h + R) * ld + w + R : trash) = vv[j];
+          if (++w == W) {
+            w = 0;
+            ++h;
+          }
         }
       }
     }
@@ -142,9 +157,10 @@ __global__ __launch_bounds__(kThreads) void front_fwd_plane_kernel(FrontArgs a, 
   const int H = int(a.H), W = int(a.W), L = H * W, ld = W + 2 * R, ldt = H + 1;
   float* xin = smem;                      // x with the zero halo
   float* tout = smem + (H + 2 * R) * ld;  // the output, pixel (h, w) at w * ldt + h
+  float* trash = tout + W * ldt;          // one spare word
   const int64_t plane = blockIdx.x, c = plane % a.C;
   zero_halo<R>(xin, H, W);
-  stage_plane<R>(xin, static_cast<const T*>(a.x) + plane * L, H, W, vec != 0);
+  stage_plane<R>(xin, trash, static_cast<const T*>(a.x) + plane * L, H, W, vec != 0);
   float wk[K * K], bias;
   load_taps<K>(a, c, wk, bias);
   __syncthreads();
@@ -185,20 +201,22 @@ __global__ __launch_bounds__(kThreads) void front_bwd_plane_kernel(FrontArgs a, 
   const int H = int(a.H), W = int(a.W), L = H * W, ld = W + 2 * R;
   float* xin = smem;                    // x with the zero halo
   float* dp = smem + (H + 2 * R) * ld;  // dpre with the zero halo
+  float* trash = dp + (H + 2 * R) * ld; // one spare word
   const int64_t plane = blockIdx.x, c = plane % a.C;
   zero_halo<R>(xin, H, W);
   zero_halo<R>(dp, H, W);
-  stage_plane<R>(xin, static_cast<const T*>(a.x) + plane * L, H, W, vec != 0);
+  stage_plane<R>(xin, trash, static_cast<const T*>(a.x) + plane * L, H, W, vec != 0);
+  stage_plane<R>(dp, trash, a.dxc + plane * L, H, W, vec != 0);  // dxc first; dpre replaces it in place
   float wk[KK], bias;
   load_taps<K>(a, c, wk, bias);
   __syncthreads();
-  const float* dxc = a.dxc + plane * L;
   {
     Walk pw(W);
     for (int p = threadIdx.x; p < L; p += kThreads, pw.next()) {
       const float pre = window<K>(xin + pw.row * ld + pw.col, ld, wk, bias);
       const float sg = sigmoid(pre);
-      dp[(pw.row + R) * ld + pw.col + R] = dxc[p] * sg * (1.0f + pre * (1.0f - sg));
+      float& d = dp[(pw.row + R) * ld + pw.col + R];
+      d = d * sg * (1.0f + pre * (1.0f - sg));
     }
   }
   __syncthreads();
@@ -370,11 +388,13 @@ __global__ __launch_bounds__(kThreads) void front_reduce_kernel(FrontArgs a, int
 }
 
 // 4-element vector access: whole planes of a multiple of 4 pixels, x aligned for its type,
-// the fp32 outputs to 16 bytes
-bool vec_plane(const FrontArgs& a, bool outputs) {
+// the fp32 arrays (the forward's outputs, the backward's dxc) to 16 bytes
+bool vec_plane(const FrontArgs& a, bool forward) {
   if ((a.H * a.W) % 4 != 0) return false;
   if (reinterpret_cast<uintptr_t>(a.x) & (a.dtype == 0 ? 15 : 7)) return false;
-  return !outputs || ((reinterpret_cast<uintptr_t>(a.xc) | reinterpret_cast<uintptr_t>(a.xcT)) & 15) == 0;
+  const uintptr_t f32 = forward ? (reinterpret_cast<uintptr_t>(a.xc) | reinterpret_cast<uintptr_t>(a.xcT))
+                                : reinterpret_cast<uintptr_t>(a.dxc);
+  return (f32 & 15) == 0;
 }
 
 template <int K, typename T>
@@ -382,7 +402,7 @@ hipError_t fwd_k(const FrontArgs& a, hipStream_t s) {
   if (front_plane_path(a.H, a.W, K)) {
     const int64_t blocks = a.batch * a.C;
     if (blocks > int64_t(UINT32_MAX)) return hipErrorInvalidValue;
-    const size_t lds = size_t(((a.H + K - 1) * (a.W + K - 1) + a.W * (a.H + 1)) * 4);
+    const size_t lds = size_t(((a.H + K - 1) * (a.W + K - 1) + a.W * (a.H + 1) + 1) * 4);
     front_fwd_plane_kernel<K, T><<<dim3(uint32_t(blocks)), dim3(kThreads), lds, s>>>(
         a, vec_plane(a, true) ? 1 : 0);
   } else {
@@ -398,7 +418,7 @@ hipError_t bwd_k(const FrontArgs& a, hipStream_t s) {
   if (front_plane_path(a.H, a.W, K)) {
     const int64_t blocks = a.batch * a.C;
     if (blocks > int64_t(UINT32_MAX)) return hipErrorInvalidValue;
-    const size_t lds = size_t(2 * (a.H + K - 1) * (a.W + K - 1) * 4);
+    const size_t lds = size_t((2 * (a.H + K - 1) * (a.W + K - 1) + 1) * 4);
     front_bwd_plane_kernel<K, T><<<dim3(uint32_t(blocks)), dim3(kThreads), lds, s>>>(a, vec_plane(a, false) ? 1 : 0);
   } else {
     const int64_t blocks = a.batch * a.C * front_tiles(a.H, a.W);

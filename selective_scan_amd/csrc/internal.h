@@ -139,7 +139,7 @@ __host__ __device__ inline int64_t front_tiles(int64_t H, int64_t W) { return ((
 // the backward x and dpre, each with an r halo.
 inline int64_t front_plane_lds(int64_t H, int64_t W, int k) {
   const int64_t r = k / 2, halo = (H + 2 * r) * (W + 2 * r);
-  const int64_t fwd = (halo + W * (H + 1)) * 4, bwd = 2 * halo * 4;
+  const int64_t fwd = (halo + W * (H + 1) + 1) * 4, bwd = (2 * halo + 1) * 4;  // + one spare word
   return fwd > bwd ? fwd : bwd;
 }
 inline bool front_plane_path(int64_t H, int64_t W, int k) { return front_plane_lds(H, W, k) <= 64 * 1024; }
