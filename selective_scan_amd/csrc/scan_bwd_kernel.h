@@ -181,7 +181,8 @@ __device__ __forceinline__ bool reduce_writer(int lane) {
 // transpose, fp32 dout planes); 2 = generic rows with an fp32 dout.
 // TU: element type of u (T, or fp32 for an SS2D input computed in fp32 by the input front).
 template <typename T, int NS, int kSplit, int kMode, bool kVec, int kPass, typename TU>
-__global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) {
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kPass == 0 && NS >= 16 ? 2 : 1)))
+void scan_bwd_kernel(const ScanBwdParams p) {
   constexpr bool kSS2D = kMode == 1;
   using DT = typename std::conditional<kMode == 0, T, float>::type;  // type of dout rows
   constexpr int NSL = NS / kSplit;
@@ -433,13 +434,18 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
     float nh0[NSL];
     auto prefetch_seg = [&](int64_t s0) {
       load_row<T, kVec, kSub>(nd, delta_row, s0, t_end, L, false);
-      load_row<TU, kVec, kSub>(nu, u_row, s0, t_end, L, rev);
-      load_row<DT, kVec, kSub>(ng, dout_row, s0, t_end, L, rev);
+      // reversed rows stay in memory order here (reversed when used), and no load sits behind a
+      // branch: either would make this prefetch wait for its own loads
+      load_row<TU, kVec, kSub, true>(nu, u_row, s0, t_end, L, rev);
+      load_row<DT, kVec, kSub, true>(ng, dout_row, s0, t_end, L, rev);
       if (has_z) load_row<T, kVec, kSub>(nz, z_row, s0, t_end, L, false);
       if (kPass == 0) {
         const float* ck = p.ckpt + ((s0 / kSub) * p.batch * p.dim + row) * N + n0;
 #pragma unroll
-        for (int n = 0; n < NSL; ++n) nh0[n] = (n < nvalid) ? ck[n] : 0.0f;
+        for (int n = 0; n < NSL; ++n) {
+          const float v = ck[n < nvalid ? n : 0];
+          nh0[n] = (n < nvalid) ? v : 0.0f;
+        }
       }
     };
     if (n_segs > 0) prefetch_seg(t_begin + (n_segs - 1) * kSub);
@@ -449,8 +455,12 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
       const int q = int(((s0 - t_begin) % kTile) / kSub);
       if (si == n_segs - 1 || q == kSegsPerTile - 1) stage_tile(s0 - int64_t(q) * kSub);
       const RowTile<T, kSub> cd = nd, cz = nz;
-      const RowTile<TU, kSub> cu = nu;
-      const RowTile<DT, kSub> cg = ng;
+      RowTile<TU, kSub> cu = nu;
+      RowTile<DT, kSub> cg = ng;
+      if (kVec && rev) {  // vector loads leave a reversed row in memory order
+        cu.reverse();
+        cg.reverse();
+      }
       float h0[NSL];
 #pragma unroll
       for (int n = 0; n < NSL; ++n) h0[n] = nh0[n];
@@ -482,7 +492,11 @@ __global__ __launch_bounds__(kWave) void scan_bwd_kernel(const ScanBwdParams p) 
         load_seg<DT, kVec, kSub>(gv, dout_row, s0, t_end, L, rev);
         if (has_z) load_seg<T, kVec, kSub>(zv, z_row, s0, t_end, L, false);
         const float* ck = p.ckpt + ((s0 / kSub) * p.batch * p.dim + row) * N + n0;
-        seg_body(s0, q, dv, uv, gv, zv, [&](int n) { return (n < nvalid) ? ck[n] : 0.0f; });
+        // unconditional load (a state past N re-reads state n0, zeroed by a select)
+        seg_body(s0, q, dv, uv, gv, zv, [&](int n) {
+          const float v = ck[n < nvalid ? n : 0];
+          return (n < nvalid) ? v : 0.0f;
+        });
       }
     }
   }

@@ -94,7 +94,10 @@ __device__ __forceinline__ void set_elem(RowTile<T, kLen>& t, int i, const T* p)
 // Steps at or past t_end read as the value with bit pattern pad_bits (zero by default).  Vector
 // loads need L % 4 == 0, t0 % 4 == 0 and kLen % 4 == 0 (shorter pieces are read element by
 // element).
-template <typename T, bool kVecArg, int kLen = kTile>
+// kDeferRev: with vector loads a reversed row is left in memory order and the caller reverses the
+// tile just before using it -- reversing here would make the prefetch wait for its own loads.
+// (The element-by-element path places reversed rows in step order either way.)
+template <typename T, bool kVecArg, int kLen = kTile, bool kDeferRev = false>
 __device__ __forceinline__ void load_row(RowTile<T, kLen>& tile, const T* row, int64_t t0, int64_t t_end, int64_t L,
                                          bool rev, uint32_t pad_bits = 0) {
   constexpr bool kVec = kVecArg && kLen % 4 == 0;
@@ -103,7 +106,7 @@ __device__ __forceinline__ void load_row(RowTile<T, kLen>& tile, const T* row, i
     const int64_t base = rev ? (L - t0 - kLen) : t0;
 #pragma unroll
     for (int j = 0; j < kLen / 4; ++j) tile.load_vec(row + base + 4 * j, j);
-    if (rev) tile.reverse();
+    if (!kDeferRev && rev) tile.reverse();
     return;
   }
   if constexpr (!kVec && sizeof(T) == 2 && kLen % 4 == 0) {
@@ -139,7 +142,7 @@ __device__ __forceinline__ void load_row(RowTile<T, kLen>& tile, const T* row, i
 #pragma unroll
       for (int j = 0; j < kLen / 4; ++j)
         if (base + 4 * j >= 0 && L - 1 - (base + 4 * j + 3) < t_end) tile.load_vec(row + base + 4 * j, j);
-      tile.reverse();
+      if (!kDeferRev) tile.reverse();
     }
   } else {
 #pragma unroll
@@ -164,13 +167,13 @@ struct BCStage {
       // whole tile in range and every lane has whole vectors: states past N read as zero
 #pragma unroll
       for (int k = 0; k < kVecs; ++k) {
+        // no branch around the loads (a load in a conditional block is waited for at the join):
+        // states past N read state N-1 and are zeroed by a select
         const int j = lane + k * kWave;
         const int n = j / (kTile / 4), q = j % (kTile / 4);
-        float4 vb = make_float4(0.f, 0.f, 0.f, 0.f), vc = vb;
-        if (n < N) {
-          vb = Elem<T>::load4(Bg, int64_t(n) * L + t0 + 4 * q);
-          vc = Elem<T>::load4(Cg, int64_t(n) * L + t0 + 4 * q);
-        }
+        const int64_t off = int64_t(n < N ? n : N - 1) * L + t0 + 4 * q;
+        float4 vb = Elem<T>::load4(Bg, off), vc = Elem<T>::load4(Cg, off);
+        if (n >= N) vb = vc = make_float4(0.f, 0.f, 0.f, 0.f);
         b[4 * k + 0] = vb.x; b[4 * k + 1] = vb.y; b[4 * k + 2] = vb.z; b[4 * k + 3] = vb.w;
         c[4 * k + 0] = vc.x; c[4 * k + 1] = vc.y; c[4 * k + 2] = vc.z; c[4 * k + 3] = vc.w;
       }
@@ -276,12 +279,16 @@ __device__ __forceinline__ void load_seg(float* out, const T* row, int64_t t, in
       return;
     }
   }
+  // Loads are unconditional (steps past t_end re-read step t, which is in range, and are zeroed
+  // by a select): a load behind a branch is waited for at the join, one round trip per load.
   if (kVec && kSeg % 4 == 0) {
 #pragma unroll
     for (int j = 0; j < kSeg / 4; ++j) {
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       const int64_t s = t + 4 * j;
-      if (s < t_end) v = Elem<T>::load4(row, rev ? (L - 4 - s) : s);
+      const bool in = s < t_end;
+      const int64_t sc = in ? s : t;
+      float4 v = Elem<T>::load4(row, rev ? (L - 4 - sc) : sc);
+      if (!in) v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (!rev) {
         out[4 * j] = v.x; out[4 * j + 1] = v.y; out[4 * j + 2] = v.z; out[4 * j + 3] = v.w;
       } else {
@@ -292,7 +299,10 @@ __device__ __forceinline__ void load_seg(float* out, const T* row, int64_t t, in
 #pragma unroll
     for (int i = 0; i < kSeg; ++i) {
       const int64_t s = t + i;
-      out[i] = (s < t_end) ? Elem<T>::load(row, rev ? (L - 1 - s) : s) : 0.0f;
+      const bool in = s < t_end;
+      const int64_t sc = in ? s : t;
+      const float v = Elem<T>::load(row, rev ? (L - 1 - sc) : sc);
+      out[i] = in ? v : 0.0f;
     }
   }
 }

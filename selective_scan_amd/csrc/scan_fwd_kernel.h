@@ -114,7 +114,7 @@ void scan_fwd_kernel(const ScanFwdParams p) {
   auto prefetch = [&](auto set, int64_t t) {
     constexpr int k = decltype(set)::value;
     load_row<T, kVec>(rd[k], delta_row, t, t_end, L, false, dpad);
-    load_row<TU, kVec>(ru[k], u_row, t, t_end, L, rev);
+    load_row<TU, kVec, kTile, true>(ru[k], u_row, t, t_end, L, rev);  // reversed when used
     if (has_z) load_row<T, kVec>(rz[k], z_row, t, t_end, L, false);
     nbc.load(Bg, Cg, N, L, t, t_end, lane);
   };
@@ -123,13 +123,16 @@ void scan_fwd_kernel(const ScanFwdParams p) {
   auto tile = [&](auto set, int64_t t0) {
     constexpr int k_set = decltype(set)::value;
     const RowTile<T>& cd = rd[k_set];
-    const RowTile<TU>& cu = ru[k_set];
+    RowTile<TU>& cu = ru[k_set];
     const RowTile<T>& cz = rz[k_set];
     __syncthreads();  // the previous tile's LDS reads are complete
     nbc.template store<S>(sB, sC, lane);
     __syncthreads();
     const int64_t t1 = t0 + kTile;
     if (t1 < t_end) prefetch(std::integral_constant<int, 1 - k_set>{}, t1);
+    // vector loads leave a reversed row in memory order (the scalar path indexes steps directly);
+    // flipped here, after the next tile's loads are issued, so the wait covers only this tile's
+    if (kVec && rev) cu.reverse();
 
     const int nt = int((t_end - t0 < kTile) ? (t_end - t0) : kTile);
     // One step's B (times ln 2) and C from LDS into one of two register buffers: the reads for
