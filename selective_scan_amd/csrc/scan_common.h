@@ -1,6 +1,8 @@
 // Helpers shared by the selective-scan forward and backward kernels: per-lane row tiles,
 // B/C staging into LDS, output and state stores.
 #pragma once
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -153,29 +155,45 @@ __device__ __forceinline__ void load_row(RowTile<T, kLen>& tile, const T* row, i
   }
 }
 
-// B/C staging: per lane, the raw values it copies into LDS for one tile.
+// B/C staging: per lane, the raw values it copies into LDS for one tile.  The vector path keeps
+// the loaded words as they are (bf16 pairs, or fp32) and converts them only in store(), at the
+// next tile: converting at load time would make the prefetch wait for its own loads.
 template <typename T, int NS, bool kVec>
 struct BCStage {
+  using Raw = typename std::conditional<sizeof(T) == 2, uint2, float4>::type;  // 4 steps of one state
   static constexpr int kVecs = (NS * kTile / 4 + kWave - 1) / kWave;  // 4-step vectors per lane
   static constexpr int kElems = (NS * kTile + kWave - 1) / kWave;     // scalars per lane
-  float b[kVec ? 4 * kVecs : kElems];
-  float c[kVec ? 4 * kVecs : kElems];
+  Raw rb[kVec ? kVecs : 1], rc[kVec ? kVecs : 1];
+  float b[kVec ? 1 : kElems], c[kVec ? 1 : kElems];
+
+  __device__ __forceinline__ static Raw raw_zero() {
+    if constexpr (sizeof(T) == 2)
+      return make_uint2(0u, 0u);
+    else
+      return make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __device__ __forceinline__ static float4 to_f32(const Raw& r) {
+    if constexpr (sizeof(T) == 2)
+      return make_float4(bf16lo(r.x), bf16hi(r.x), bf16lo(r.y), bf16hi(r.y));
+    else
+      return r;
+  }
 
   __device__ __forceinline__ void load(const T* Bg, const T* Cg, int N, int64_t L, int64_t t0, int64_t t_end,
                                        int lane) {
     if (kVec && t0 + kTile <= t_end && NS * kTile / 4 >= kWave * kVecs) {
-      // whole tile in range and every lane has whole vectors: states past N read as zero
+      // whole tile in range and every lane has whole vectors: no branch around the loads (a load
+      // in a conditional block is waited for at the join); states past N read state N-1 and are
+      // zeroed by a select
 #pragma unroll
       for (int k = 0; k < kVecs; ++k) {
-        // no branch around the loads (a load in a conditional block is waited for at the join):
-        // states past N read state N-1 and are zeroed by a select
         const int j = lane + k * kWave;
         const int n = j / (kTile / 4), q = j % (kTile / 4);
         const int64_t off = int64_t(n < N ? n : N - 1) * L + t0 + 4 * q;
-        float4 vb = Elem<T>::load4(Bg, off), vc = Elem<T>::load4(Cg, off);
-        if (n >= N) vb = vc = make_float4(0.f, 0.f, 0.f, 0.f);
-        b[4 * k + 0] = vb.x; b[4 * k + 1] = vb.y; b[4 * k + 2] = vb.z; b[4 * k + 3] = vb.w;
-        c[4 * k + 0] = vc.x; c[4 * k + 1] = vc.y; c[4 * k + 2] = vc.z; c[4 * k + 3] = vc.w;
+        Raw vb = *reinterpret_cast<const Raw*>(Bg + off), vc = *reinterpret_cast<const Raw*>(Cg + off);
+        if (n >= N) vb = vc = raw_zero();
+        rb[k] = vb;
+        rc[k] = vc;
       }
       return;
     }
@@ -184,13 +202,13 @@ struct BCStage {
       for (int k = 0; k < kVecs; ++k) {
         const int j = lane + k * kWave;            // vector id: n = j / (kTile/4), q = j % (kTile/4)
         const int n = j / (kTile / 4), q = j % (kTile / 4);
-        float4 vb = make_float4(0.f, 0.f, 0.f, 0.f), vc = vb;
+        Raw vb = raw_zero(), vc = raw_zero();
         if (n < N && j < NS * kTile / 4 && t0 + 4 * q < t_end) {
-          vb = Elem<T>::load4(Bg, int64_t(n) * L + t0 + 4 * q);
-          vc = Elem<T>::load4(Cg, int64_t(n) * L + t0 + 4 * q);
+          vb = *reinterpret_cast<const Raw*>(Bg + int64_t(n) * L + t0 + 4 * q);
+          vc = *reinterpret_cast<const Raw*>(Cg + int64_t(n) * L + t0 + 4 * q);
         }
-        b[4 * k + 0] = vb.x; b[4 * k + 1] = vb.y; b[4 * k + 2] = vb.z; b[4 * k + 3] = vb.w;
-        c[4 * k + 0] = vc.x; c[4 * k + 1] = vc.y; c[4 * k + 2] = vc.z; c[4 * k + 3] = vc.w;
+        rb[k] = vb;
+        rc[k] = vc;
       }
     } else {
 #pragma unroll
@@ -217,10 +235,12 @@ struct BCStage {
         const int j = lane + k * kWave;
         if (j < NS * kTile / 4) {
           const int n = j / (kTile / 4), q = j % (kTile / 4);
+          const float4 vb = to_f32(rb[k]), vc = to_f32(rc[k]);
+          const float bb[4] = {vb.x, vb.y, vb.z, vb.w}, cc[4] = {vc.x, vc.y, vc.z, vc.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            sB[(4 * q + i) * S + n] = b[4 * k + i] * kLn2;
-            sC[(4 * q + i) * S + n] = c[4 * k + i];
+            sB[(4 * q + i) * S + n] = bb[i] * kLn2;
+            sC[(4 * q + i) * S + n] = cc[i];
           }
         }
       }
