@@ -15,6 +15,8 @@ Functions (see ``oracle/ss2d_oracle.py`` for the citations):
   dwconv, ss2d_front_fwd/_bwd    SS2D after a depthwise conv + SiLU front (oracle/front_oracle.py)
   channel_layer_norm(_bwd),      SS2D followed by LayerNorm over channels and the gate
   ss2d_ln_fwd/_bwd                 (oracle/vss_oracle.py)
+  route_projections,             SS2D with its delta/B/C produced by per-route x_proj and
+  ss2d_proj_fwd/_bwd               dt_proj of the scanned sequence (oracle/proj_oracle.py)
 
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against
 closed forms, invariants, a brute-force semiseparable-matrix formulation and
@@ -31,7 +33,8 @@ from .ss2d_oracle import (  # noqa: F401
     ss_bwd,
     ss_fwd,
 )
-from .front_oracle import dwconv, ss2d_front_bwd, ss2d_front_fwd  # noqa: F401
+from .front_oracle import dwconv, front_bwd, front_fwd, ss2d_front_bwd, ss2d_front_fwd  # noqa: F401
+from .proj_oracle import route_projections, ss2d_proj_bwd, ss2d_proj_fwd  # noqa: F401
 from .step_oracle import ss_step  # noqa: F401
 from .vim_oracle import vim_bidir_bwd, vim_bidir_fwd  # noqa: F401
 from .vss_oracle import channel_layer_norm, channel_layer_norm_bwd, ss2d_ln_bwd, ss2d_ln_fwd  # noqa: F401

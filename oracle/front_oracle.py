@@ -49,11 +49,27 @@ def ss2d_front_bwd(x, conv_w, conv_b, delta, A, B, C, D=None, delta_bias=None, z
                    delta_softplus=True):
     """Exact gradient of ss2d_front_fwd: the SS2D gradient w.r.t. its input u = silu(pre),
     pre = dwconv(x), times silu'(pre), then the depthwise convolution's own gradients."""
+    g = ss2d_bwd(front_fwd(x, conv_w, conv_b), delta, A, B, C, D, delta_bias, z, dout, delta_softplus)
+    dx, dw, db = front_bwd(x, conv_w, conv_b, g["dx"])
+    out = dict(g)
+    out["dx"] = dx
+    out["dconv_w"] = dw
+    out["dconv_b"] = db
+    return out
+
+
+def front_fwd(x, conv_w, conv_b):
+    """The front alone: u = silu(dwconv(x, conv_w, conv_b))."""
+    return _silu(dwconv(x, conv_w, conv_b))
+
+
+def front_bwd(x, conv_w, conv_b, du):
+    """Gradient of front_fwd given dL/du: dpre = du * silu'(pre); dx = the transposed
+    convolution of dpre; dw[c,i,j] = sum dpre * x shifted by (i - r, j - r); db = sum dpre."""
     x, w = _f64(x), _f64(conv_w)
     pre = dwconv(x, w, conv_b)
     s = 1.0 / (1.0 + np.exp(-pre))
-    g = ss2d_bwd(pre * s, delta, A, B, C, D, delta_bias, z, dout, delta_softplus)
-    dpre = g["dx"] * s * (1.0 + pre * (1.0 - s))
+    dpre = _f64(du) * s * (1.0 + pre * (1.0 - s))
     Bt, Cc, H, W = x.shape
     k = w.shape[-1]
     r = (k - 1) // 2
@@ -65,8 +81,4 @@ def ss2d_front_bwd(x, conv_w, conv_b, delta, A, B, C, D=None, delta_bias=None, z
         for j in range(k):
             dw[:, i, j] = np.sum(dpre * xp[:, :, i:i + H, j:j + W], axis=(0, 2, 3))
             dxp[:, :, i:i + H, j:j + W] += w[None, :, i, j, None, None] * dpre
-    out = dict(g)
-    out["dx"] = dxp[:, :, r:r + H, r:r + W]
-    out["dconv_w"] = dw
-    out["dconv_b"] = np.sum(dpre, axis=(0, 2, 3)) if conv_b is not None else None
-    return out
+    return dxp[:, :, r:r + H, r:r + W], dw, (np.sum(dpre, axis=(0, 2, 3)) if conv_b is not None else None)
