@@ -14,7 +14,9 @@ oracle timed on this host on a bounded sample of the same workload.  `--workload
 selects one of the other shapes (0-4 SS2D, 5 the Vision Mamba bidirectional scan at
 Vim-Tiny size); `--bwd` adds the fused backward to each step; `--front K` puts the
 input front (depthwise K x K convolution + SiLU) ahead of the SS2D routes; `--ln` adds the
-back half (LayerNorm over the channels of the merged map before the gate).
+back half (LayerNorm over the channels of the merged map before the gate); `--proj R` makes
+Δ, B and C come from the per-route projections of the scanned sequence (dt_rank R, on the
+matrix cores) instead of being inputs.
 
 When one input/output set is smaller than the 256 MB last-level cache (MALL) several
 times over, the steps rotate over independent copies so that no step re-reads what the
@@ -47,6 +49,7 @@ VALU_PEAK_TFLOPS = SIMDS * 16 * 2 * CLOCK_HZ / 1e12
 # 4*4 + 8 = 24 SIMD cycles: the issue-limited peak for this instruction mix.
 FLOPS_PER_STATE_STEP = 7
 MIX_PEAK_TFLOPS = SIMDS * CLOCK_HZ * 64 / 24 * FLOPS_PER_STATE_STEP / 1e12
+FP32_MFMA_PEAK_TFLOPS = 157.3  # dense fp32 matrix-core peak of the MI355X
 MALL_BYTES = 256 << 20
 COPY_BYTES = 1 << 30
 
@@ -63,6 +66,8 @@ def parse():
                     help="SS2D only: K > 0 adds the input front (depthwise K x K convolution + SiLU)")
     ap.add_argument("--ln", action="store_true",
                     help="SS2D only: LayerNorm over the channels of the merged map before the gate")
+    ap.add_argument("--proj", type=int, default=0,
+                    help="SS2D only: R > 0 produces delta/B/C from per-route x_proj/dt_proj (dt_rank R)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time for the sample")
     return ap.parse_args()
@@ -77,9 +82,22 @@ def front_bytes(cfg, bwd=False):
     return (e + 8) * grid + ((2 * e + 4) * grid if bwd else 0)
 
 
-def algorithmic_bytes(cfg, bwd=False):
-    """Each tensor read once and each output written once (the fused minimum)."""
+def proj_flops(cfg, R):
+    """Multiply-adds x 2 of the Δ/B/C producer per forward: x_proj (R + 2N rows) and dt_proj per
+    route and pixel."""
+    tokens = 4 * cfg.batch * cfg.seqlen
+    return 2 * tokens * ((R + 2 * cfg.dstate) * cfg.dim + cfg.dim * R)
+
+
+def algorithmic_bytes(cfg, bwd=False, proj=False):
+    """Each tensor read once and each output written once (the fused minimum).  With the Δ/B/C
+    producer, delta, B and C are not inputs (nor their gradients outputs)."""
     e = 2 if cfg.dtype == "bf16" else 4
+    if proj and getattr(cfg, "kind", "ss2d") != "vim":
+        grid = cfg.batch * cfg.dim * cfg.seqlen
+        z = grid if cfg.has_z else 0
+        fwd = e * (grid + z + grid)
+        return fwd + (e * (grid + grid + z + grid + z) if bwd else 0)
     if getattr(cfg, "kind", "ss2d") == "vim":
         seq = cfg.batch * cfg.dim * cfg.seqlen  # one direction, or the gate / output sequence
         bc = 2 * cfg.batch * 2 * cfg.dstate * cfg.seqlen
@@ -131,7 +149,7 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(cfg, inp, target_s, bwd=False, front=None, ln=None):
+def cpu_baseline(cfg, inp, target_s, bwd=False, front=None, ln=None, proj=None):
     """The fp64 oracle (as it stands) on the first images of the same batch (forward, or
     forward + backward when the GPU step includes the backward)."""
     import oracle
@@ -156,7 +174,17 @@ def cpu_baseline(cfg, inp, target_s, bwd=False, front=None, ln=None):
         args = (sl(inp["x"]), sl(inp["delta"]), inp["A"].astype(np.float64), sl(inp["B"]), sl(inp["C"]),
                 inp["D"].astype(np.float64), inp["delta_bias"].astype(np.float64), sl(inp["z"]))
         t0 = time.perf_counter()
-        if ln is not None:
+        if proj is not None:
+            kw = dict(x_proj_w=proj["x_proj_w"].astype(np.float64), dt_proj_w=proj["dt_proj_w"].astype(np.float64),
+                      A=args[2], D=args[5], delta_bias=args[6], z=args[7])
+            if front is not None:
+                kw.update(conv_w=front["conv_w"].astype(np.float64), conv_b=front["conv_b"].astype(np.float64))
+            if ln is not None:
+                kw.update(layer_norm=True, ln_w=ln["ln_w"].astype(np.float64), ln_b=ln["ln_b"].astype(np.float64))
+            oracle.ss2d_proj_fwd(args[0], **kw)
+            if bwd:
+                oracle.ss2d_proj_bwd(args[0], **kw, dout=sl(inp["dout"]))
+        elif ln is not None:
             kw = dict(ln_w=ln["ln_w"].astype(np.float64), ln_b=ln["ln_b"].astype(np.float64))
             if front is not None:
                 kw.update(conv_w=front["conv_w"].astype(np.float64), conv_b=front["conv_b"].astype(np.float64))
@@ -184,12 +212,13 @@ def cpu_baseline(cfg, inp, target_s, bwd=False, front=None, ln=None):
             "sample": f"first {nb} of {cfg.batch} {'sequences' if vim else 'images'} (all {cfg.dim} channels, "
                       f"{routes} {'directions' if vim else 'routes'}, L={cfg.seqlen}, N={cfg.dstate}), fp64 C "
                       f"oracle with OpenMP over rows{', with the input front' if front is not None else ''}"
-                      f"{', with the LayerNorm' if ln is not None else ''}, "
+                      f"{', with the LayerNorm' if ln is not None else ''}"
+                      f"{', with the delta/B/C producer' if proj is not None else ''}, "
                       f"{'forward + backward' if bwd else 'forward'}, {t:.2f} s wall",
             "cpu_model": cpu_model()}
 
 
-def config_record(cfg, vim, bwd, n_sets, front_k=0, ln=False):
+def config_record(cfg, vim, bwd, n_sets, front_k=0, ln=False, proj_r=0):
     if vim:
         return {"workload": ("vim_bidir_fwd+bwd " if bwd else "vim_bidir_fwd ") + cfg.name, "batch": cfg.batch,
                 "seqlen": cfg.seqlen, "directions": 2, "dim": cfg.dim, "dstate": cfg.dstate, "gate_z": cfg.has_z,
@@ -203,6 +232,9 @@ def config_record(cfg, vim, bwd, n_sets, front_k=0, ln=False):
     if ln:
         rec["workload"] = rec["workload"].replace(" " + cfg.name, "(+layernorm) " + cfg.name, 1)
         rec["layer_norm"] = True
+    if proj_r:
+        rec["workload"] = rec["workload"].replace(" " + cfg.name, f"(+x_proj/dt_proj R={proj_r}) " + cfg.name, 1)
+        rec["dt_rank"] = proj_r
     return rec
 
 
@@ -225,12 +257,13 @@ def main():
     workloads = list(synth.CONFIGS) + list(synth.VIM_CONFIGS)
     cfg = workloads[args.workload]
     vim = getattr(cfg, "kind", "ss2d") == "vim"
-    if (args.front or args.ln) and vim:
-        print("--front and --ln apply to the SS2D workloads only", file=sys.stderr)
+    if (args.front or args.ln or args.proj) and vim:
+        print("--front, --ln and --proj apply to the SS2D workloads only", file=sys.stderr)
         sys.exit(2)
     inp = (synth.make_vim_config_inputs if vim else synth.make_config_inputs)(cfg, with_dout=args.bwd)
     front = synth.make_front_params(cfg.dim, args.front, seed_base=cfg.index) if args.front else None
     ln = synth.make_ln_params(cfg.dim, seed_base=cfg.index) if args.ln else None
+    proj = synth.make_proj_params(cfg.dim, cfg.dstate, args.proj, seed_base=cfg.index) if args.proj else None
 
     def dev(a, dtype):
         if a is None:
@@ -247,6 +280,9 @@ def main():
         d0.update(conv_w=dev(front["conv_w"], "f32"), conv_b=dev(front["conv_b"], "f32"))
     if ln is not None:
         d0.update(ln_w=dev(ln["ln_w"], "f32"), ln_b=dev(ln["ln_b"], "f32"))
+    if proj is not None:
+        d0.update(delta=None, B=None, C=None, x_proj_w=dev(proj["x_proj_w"], "f32"),
+                  dt_proj_w=dev(proj["dt_proj_w"], "f32"))
     dout0 = dev(inp["dout"], cfg.dtype) if args.bwd else None
     # with --bwd a step is a training step: for SS2D the forward keeps its checkpoint states and
     # the backward runs on them (the Vim backward recomputes its forward)
@@ -314,7 +350,7 @@ def main():
     copy_gbps = 2 * COPY_BYTES / (np.median([a.elapsed_time(b) for a, b in copy_ev]) * 1e-3) / 1e9
 
     elements = cfg.elements
-    step_bytes = algorithmic_bytes(cfg, args.bwd) + (front_bytes(cfg, args.bwd) if front is not None else 0)
+    step_bytes = algorithmic_bytes(cfg, args.bwd, proj is not None) + (front_bytes(cfg, args.bwd) if front is not None else 0)
     flops = elements * cfg.dstate * FLOPS_PER_STATE_STEP
     scan_mean = float(np.mean(scan_ms))
     achieved_tflops = flops / (scan_mean * 1e-3) / 1e12
@@ -333,7 +369,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) inputs, S4D-real A, inverse-softplus dt bias)",
-        "config": config_record(cfg, vim, args.bwd, n_sets, args.front, args.ln),
+        "config": config_record(cfg, vim, args.bwd, n_sets, args.front, args.ln, args.proj),
         "step_ms": stats(step_ms),
         "hbm": {"algorithmic_bytes_per_step": step_bytes,
                 "achieved_GBps": hbm_gbps,
@@ -354,8 +390,15 @@ def main():
                         "launch_ms": stats(stage0_ms), "algorithmic_bytes": fb,
                         "achieved_GBps": fb / (f_ms * 1e-3) / 1e9, "peak_GBps": HBM_PEAK_GBPS,
                         "frac": fb / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    if proj is not None:
+        pf = proj_flops(cfg, args.proj)
+        s_ms = float(np.mean(stage0_ms))
+        res["producer"] = {"kernel": "gemm_kernel (v_mfma_f32_32x32x2f32), stage 0 with the fp32 copies",
+                           "bound": "mfma", "flops_per_step": pf, "stage0_ms": s_ms, "launch_ms": stats(stage0_ms),
+                           "achieved_TFLOPs": pf / (s_ms * 1e-3) / 1e12, "peak_TFLOPs": FP32_MFMA_PEAK_TFLOPS,
+                           "frac": pf / (s_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds, args.bwd, front, ln)
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds, args.bwd, front, ln, proj)
     print(json.dumps(res))
 
 

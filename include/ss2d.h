@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SS2D_ABI_VERSION 6
+#define SS2D_ABI_VERSION 7
 
 /* Status codes returned by every entry point. */
 enum {
@@ -211,6 +211,10 @@ int selective_scan_step(const ss_step_args* args, hipStream_t stream);
  * The workspace is required (>= ss2d_workspace_bytes(...)); the same size serves calls with
  * and without the input front.
  * ------------------------------------------------------------------------------- */
+/* Workspace of ss2d_fwd / ss2d_bwd with the Δ/B/C producer (dt_rank >= 1): the plain size plus
+ * the fp32 projected inputs, their gradients and the weight-gradient partials.  0 if invalid. */
+size_t ss2d_proj_workspace_bytes(int64_t batch, int64_t dim, int64_t height, int64_t width, int64_t dstate,
+                                 int64_t dt_rank, int dtype);
 size_t ss2d_workspace_bytes(int64_t batch, int64_t dim, int64_t height, int64_t width,
                             int64_t dstate, int dtype);
 
@@ -249,6 +253,16 @@ typedef struct ss2d_fwd_args {
   const float* ln_w;       /* (dim) fp32, or NULL: 1 */
   const float* ln_b;       /* (dim) fp32, or NULL: 0 */
   float ln_eps;            /* >= 0 (1e-5 is the usual LayerNorm default) */
+  /* Optional Δ/B/C producer [S6 page, section 2: the Mamba module's x_proj and dt_proj, one
+   * S6 block per route]: with x_proj_w != NULL, delta, Bm and Cm are not read (pass NULL), and
+   * route k's inputs come from its own scanned sequence xs_k (of u: the front's output, or x):
+   *   x_dbl = x_proj_w[k] @ xs_k   ((dt_rank + 2 dstate) x L), dt = rows [0, R), B = rows
+   *   [R, R + N), C = rows [R + N, R + 2N), delta_raw = dt_proj_w[k] @ dt   (R = dt_rank)
+   * in fp32 on the matrix cores; the route scans then run in fp32 (delta_bias is dt_proj's
+   * bias).  The workspace must hold ss2d_proj_workspace_bytes(...). */
+  const float* x_proj_w;   /* (4, dt_rank + 2 dstate, dim) fp32 */
+  const float* dt_proj_w;  /* (4, dim, dt_rank) fp32 */
+  int dt_rank;             /* 1..dim */
 } ss2d_fwd_args;
 
 int ss2d_fwd(const ss2d_fwd_args* args, hipStream_t stream);
@@ -313,6 +327,15 @@ typedef struct ss2d_bwd_args {
   float ln_eps;
   float* dln_w;
   float* dln_b;
+  /* the Δ/B/C producer, as in ss2d_fwd_args: then delta, Bm, Cm are not read and ddelta,
+   * dBm, dCm not written (may be NULL); dx includes the projections' path, and dx_proj_w
+   * (4, dt_rank + 2 dstate, dim) and ddt_proj_w (4, dim, dt_rank) receive the weights'
+   * gradients (fp32, summed over images, overwritten) */
+  const float* x_proj_w;
+  const float* dt_proj_w;
+  int dt_rank;
+  float* dx_proj_w;
+  float* ddt_proj_w;
 } ss2d_bwd_args;
 
 int ss2d_bwd(const ss2d_bwd_args* args, hipStream_t stream);

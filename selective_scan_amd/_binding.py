@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libss2d.so")
 
 SS2D_OK, SS2D_ERR_INVALID_ARGUMENT, SS2D_ERR_UNSUPPORTED, SS2D_ERR_HIP = 0, 1, 2, 3
 DTYPE_F32, DTYPE_BF16 = 0, 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -45,7 +45,8 @@ class SS2DFwdArgs(ctypes.Structure):
         ("workspace_bytes", _sz), ("batch", _i64), ("dim", _i64), ("height", _i64), ("width", _i64),
         ("dstate", _i64), ("dtype", _int), ("delta_softplus", _int), ("keep_states", _int),
         ("conv_w", _p), ("conv_b", _p), ("conv_k", _int),
-        ("layer_norm", _int), ("ln_w", _p), ("ln_b", _p), ("ln_eps", ctypes.c_float)]
+        ("layer_norm", _int), ("ln_w", _p), ("ln_b", _p), ("ln_eps", ctypes.c_float),
+        ("x_proj_w", _p), ("dt_proj_w", _p), ("dt_rank", _int)]
 
 
 class SS2DBwdArgs(ctypes.Structure):
@@ -54,7 +55,8 @@ class SS2DBwdArgs(ctypes.Structure):
         ("workspace_bytes", _sz), ("batch", _i64), ("dim", _i64), ("height", _i64), ("width", _i64),
         ("dstate", _i64), ("dtype", _int), ("delta_softplus", _int), ("workspace_has_states", _int),
         ("conv_w", _p), ("conv_b", _p), ("conv_k", _int), ("dconv_w", _p), ("dconv_b", _p),
-        ("layer_norm", _int), ("ln_w", _p), ("ln_b", _p), ("ln_eps", ctypes.c_float), ("dln_w", _p), ("dln_b", _p)]
+        ("layer_norm", _int), ("ln_w", _p), ("ln_b", _p), ("ln_eps", ctypes.c_float), ("dln_w", _p), ("dln_b", _p),
+        ("x_proj_w", _p), ("dt_proj_w", _p), ("dt_rank", _int), ("dx_proj_w", _p), ("ddt_proj_w", _p)]
 
 
 class SsStepArgs(ctypes.Structure):
@@ -99,6 +101,8 @@ def lib():
         L.selective_scan_workspace_bytes.argtypes = [_i64] * 5
         L.ss2d_workspace_bytes.restype = _sz
         L.ss2d_workspace_bytes.argtypes = [_i64] * 5 + [_int]
+        L.ss2d_proj_workspace_bytes.restype = _sz
+        L.ss2d_proj_workspace_bytes.argtypes = [_i64] * 6 + [_int]
         L.ss2d_fwd_stage.restype = _int
         L.ss2d_fwd_stage.argtypes = [ctypes.POINTER(SS2DFwdArgs), _int, _p]
         L.vim_bidir_workspace_bytes.restype = _sz
@@ -191,8 +195,26 @@ def selective_scan_workspace_bytes(batch, dim, dstate, seqlen, ngroups) -> int:
     return int(lib().selective_scan_workspace_bytes(batch, dim, dstate, seqlen, ngroups))
 
 
-def ss2d_workspace_bytes(batch, dim, height, width, dstate, dtype: torch.dtype) -> int:
+def ss2d_workspace_bytes(batch, dim, height, width, dstate, dtype: torch.dtype, dt_rank: int = 0) -> int:
+    """Workspace of ss2d_fwd / ss2d_bwd; with dt_rank > 0, of the path with the Δ/B/C producer."""
+    if dt_rank:
+        return int(lib().ss2d_proj_workspace_bytes(batch, dim, height, width, dstate, dt_rank, _dtype_code(dtype)))
     return int(lib().ss2d_workspace_bytes(batch, dim, height, width, dstate, _dtype_code(dtype)))
+
+
+def _proj(x_proj_w, dt_proj_w, dim):
+    """(x_proj_w, dt_proj_w, dt_rank, dstate from x_proj_w) of the Δ/B/C producer, or Nones."""
+    if x_proj_w is None and dt_proj_w is None:
+        return None, None, 0
+    if x_proj_w is None or dt_proj_w is None:
+        raise ValueError("x_proj_w and dt_proj_w go together")
+    x_proj_w, dt_proj_w = _c(x_proj_w, torch.float32), _c(dt_proj_w, torch.float32)
+    R = int(dt_proj_w.shape[-1])
+    if tuple(dt_proj_w.shape) != (4, dim, R) or x_proj_w.dim() != 3 or x_proj_w.shape[0] != 4 or \
+            x_proj_w.shape[2] != dim or (x_proj_w.shape[1] - R) % 2:
+        raise ValueError(f"x_proj_w (4, R + 2N, dim) and dt_proj_w (4, dim, R) expected, got "
+                         f"{tuple(x_proj_w.shape)}, {tuple(dt_proj_w.shape)}")
+    return x_proj_w, dt_proj_w, R
 
 
 def _bc4(Bm):
@@ -276,13 +298,15 @@ def _ln_on(layer_norm, ln_w, ln_b):
 
 def ss2d_fwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=True, workspace=None,
              out=None, keep_states=False, conv_w=None, conv_b=None, layer_norm=False, ln_w=None, ln_b=None,
-             ln_eps=1e-5):
+             ln_eps=1e-5, x_proj_w=None, dt_proj_w=None):
     """Fused SS2D forward.  x, z: (batch, dim, H, W); delta: (batch, 4, dim, H*W);
     A: (4, dim, N) fp32; B, C: (batch, 4, N, H*W); D, delta_bias: (4, dim) fp32.  With
     keep_states the given workspace keeps what ss2d_bwd(..., workspace_has_states=True) needs.
     conv_w (dim, k, k) and conv_b (dim,), fp32, add the input front: the routes scan
     silu(depthwise_conv(x) + conv_b) instead of x.  layer_norm (implied by ln_w or ln_b, fp32
-    (dim,)) adds the back half: out = LayerNorm_channels(merged) * silu(z)."""
+    (dim,)) adds the back half: out = LayerNorm_channels(merged) * silu(z).  x_proj_w
+    (4, R + 2N, dim) and dt_proj_w (4, dim, R), fp32, add the Δ/B/C producer: delta, B and C
+    (pass None) come from each route's projections of its scanned sequence."""
     x, delta = _c(x), _c(delta)
     dev = _dev(x)
     B, C, z = _c(B), _c(C), _c(z)
@@ -293,16 +317,20 @@ def ss2d_fwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=
     ln_w, ln_b = _c(ln_w, torch.float32), _c(ln_b, torch.float32)
     batch, dim, H, W = x.shape
     N = A.shape[-1]
+    x_proj_w, dt_proj_w, R = _proj(x_proj_w, dt_proj_w, dim)
+    if R and x_proj_w.shape[1] != R + 2 * N:
+        raise ValueError(f"x_proj_w has {x_proj_w.shape[1]} rows, expected dt_rank + 2 dstate = {R + 2 * N}")
     if out is None:
         out = torch.empty_like(x)
-    ws = _workspace(ss2d_workspace_bytes(batch, dim, H, W, N, x.dtype), dev, workspace)
+    ws = _workspace(ss2d_workspace_bytes(batch, dim, H, W, N, x.dtype, R), dev, workspace)
     a = SS2DFwdArgs(x=_ptr(x), delta=_ptr(delta), A=_ptr(A), Bm=_ptr(B), Cm=_ptr(C), Dskip=_ptr(D),
                     delta_bias=_ptr(delta_bias), z=_ptr(z), out=_ptr(out), workspace=_ptr(ws),
                     workspace_bytes=ws.numel() * ws.element_size(), batch=batch, dim=dim, height=H, width=W,
                     dstate=N, dtype=_dtype_code(x.dtype), delta_softplus=int(bool(delta_softplus)),
                     keep_states=int(bool(keep_states)), conv_w=_ptr(conv_w), conv_b=_ptr(conv_b),
                     conv_k=_conv_k(conv_w, dim), layer_norm=_ln_on(layer_norm, ln_w, ln_b), ln_w=_ptr(ln_w),
-                    ln_b=_ptr(ln_b), ln_eps=float(ln_eps))
+                    ln_b=_ptr(ln_b), ln_eps=float(ln_eps), x_proj_w=_ptr(x_proj_w), dt_proj_w=_ptr(dt_proj_w),
+                    dt_rank=R)
     _check(lib().ss2d_fwd(ctypes.byref(a), _stream(dev)), "ss2d_fwd")
     return out
 
@@ -313,7 +341,7 @@ class SS2DForwardPlan:
 
     def __init__(self, x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=True, workspace=None,
                  out=None, keep_states=False, conv_w=None, conv_b=None, layer_norm=False, ln_w=None, ln_b=None,
-                 ln_eps=1e-5):
+                 ln_eps=1e-5, x_proj_w=None, dt_proj_w=None):
         x, delta = _c(x), _c(delta)
         self.device = _dev(x)
         B, C, z = _c(B), _c(C), _c(z)
@@ -324,9 +352,10 @@ class SS2DForwardPlan:
         ln_w, ln_b = _c(ln_w, torch.float32), _c(ln_b, torch.float32)
         batch, dim, H, W = x.shape
         N = A.shape[-1]
+        x_proj_w, dt_proj_w, R = _proj(x_proj_w, dt_proj_w, dim)
         self.out = torch.empty_like(x) if out is None else out
-        self.workspace = _workspace(ss2d_workspace_bytes(batch, dim, H, W, N, x.dtype), self.device, workspace)
-        self._keep = (x, delta, A, B, C, D, delta_bias, z, conv_w, conv_b, ln_w, ln_b)
+        self.workspace = _workspace(ss2d_workspace_bytes(batch, dim, H, W, N, x.dtype, R), self.device, workspace)
+        self._keep = (x, delta, A, B, C, D, delta_bias, z, conv_w, conv_b, ln_w, ln_b, x_proj_w, dt_proj_w)
         self.args = SS2DFwdArgs(x=_ptr(x), delta=_ptr(delta), A=_ptr(A), Bm=_ptr(B), Cm=_ptr(C), Dskip=_ptr(D),
                                 delta_bias=_ptr(delta_bias), z=_ptr(z), out=_ptr(self.out),
                                 workspace=_ptr(self.workspace),
@@ -335,7 +364,8 @@ class SS2DForwardPlan:
                                 delta_softplus=int(bool(delta_softplus)), keep_states=int(bool(keep_states)),
                                 conv_w=_ptr(conv_w), conv_b=_ptr(conv_b), conv_k=_conv_k(conv_w, dim),
                                 layer_norm=_ln_on(layer_norm, ln_w, ln_b), ln_w=_ptr(ln_w), ln_b=_ptr(ln_b),
-                                ln_eps=float(ln_eps))
+                                ln_eps=float(ln_eps), x_proj_w=_ptr(x_proj_w), dt_proj_w=_ptr(dt_proj_w),
+                                dt_rank=R)
 
     def run(self):
         _check(lib().ss2d_fwd(ctypes.byref(self.args), _stream(self.device)), "ss2d_fwd")
@@ -348,12 +378,13 @@ class SS2DForwardPlan:
 
 def ss2d_bwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, dout=None, delta_softplus=True,
              workspace=None, workspace_has_states=False, conv_w=None, conv_b=None, layer_norm=False, ln_w=None,
-             ln_b=None, ln_eps=1e-5):
+             ln_b=None, ln_eps=1e-5, x_proj_w=None, dt_proj_w=None):
     """Backward of ss2d_fwd; returns a dict of gradients (None for absent inputs).  With
     workspace_has_states, `workspace` must be the one a forward with keep_states=True used for
     the same inputs (the forward is then not recomputed).  With the input front (conv_w,
     conv_b) dx is the gradient w.r.t. the convolution's input and the dict also holds
-    dconv_w and dconv_b; with the LayerNorm it holds dln_w and dln_b."""
+    dconv_w and dconv_b; with the LayerNorm it holds dln_w and dln_b; with the Δ/B/C producer it
+    holds dx_proj_w and ddt_proj_w (and ddelta, dB, dC are None: delta, B, C are internal)."""
     x, delta, dout = _c(x), _c(delta), _c(dout)
     dev = _dev(x)
     B, C, z = _c(B), _c(C), _c(z)
@@ -369,13 +400,19 @@ def ss2d_bwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, dout=None, delt
     dln_b = torch.empty_like(ln_b) if ln_b is not None else None
     batch, dim, H, W = x.shape
     N = A.shape[-1]
-    dx, ddelta = torch.empty_like(x), torch.empty_like(delta)
+    x_proj_w, dt_proj_w, R = _proj(x_proj_w, dt_proj_w, dim)
+    if R and x_proj_w.shape[1] != R + 2 * N:
+        raise ValueError(f"x_proj_w has {x_proj_w.shape[1]} rows, expected dt_rank + 2 dstate = {R + 2 * N}")
+    dx = torch.empty_like(x)
+    ddelta = torch.empty_like(delta) if not R else None
     dA = torch.empty_like(A)
-    dB, dC = torch.empty_like(B), torch.empty_like(C)
+    dB, dC = (torch.empty_like(B), torch.empty_like(C)) if not R else (None, None)
     dD = torch.empty_like(D) if D is not None else None
     dbias = torch.empty_like(delta_bias) if delta_bias is not None else None
     dz = torch.empty_like(z) if z is not None else None
-    ws = _workspace(ss2d_workspace_bytes(batch, dim, H, W, N, x.dtype), dev, workspace)
+    dxp = torch.empty_like(x_proj_w) if R else None
+    ddtp = torch.empty_like(dt_proj_w) if R else None
+    ws = _workspace(ss2d_workspace_bytes(batch, dim, H, W, N, x.dtype, R), dev, workspace)
     a = SS2DBwdArgs(x=_ptr(x), delta=_ptr(delta), A=_ptr(A), Bm=_ptr(B), Cm=_ptr(C), Dskip=_ptr(D),
                     delta_bias=_ptr(delta_bias), z=_ptr(z), dout=_ptr(dout), dx=_ptr(dx), ddelta=_ptr(ddelta),
                     dA=_ptr(dA), dBm=_ptr(dB), dCm=_ptr(dC), dDskip=_ptr(dD), ddelta_bias=_ptr(dbias), dz=_ptr(dz),
@@ -384,13 +421,16 @@ def ss2d_bwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, dout=None, delt
                     delta_softplus=int(bool(delta_softplus)), workspace_has_states=int(bool(workspace_has_states)),
                     conv_w=_ptr(conv_w), conv_b=_ptr(conv_b), conv_k=_conv_k(conv_w, dim), dconv_w=_ptr(dconv_w),
                     dconv_b=_ptr(dconv_b), layer_norm=ln, ln_w=_ptr(ln_w), ln_b=_ptr(ln_b), ln_eps=float(ln_eps),
-                    dln_w=_ptr(dln_w), dln_b=_ptr(dln_b))
+                    dln_w=_ptr(dln_w), dln_b=_ptr(dln_b), x_proj_w=_ptr(x_proj_w), dt_proj_w=_ptr(dt_proj_w),
+                    dt_rank=R, dx_proj_w=_ptr(dxp), ddt_proj_w=_ptr(ddtp))
     _check(lib().ss2d_bwd(ctypes.byref(a), _stream(dev)), "ss2d_bwd")
     g = {"dx": dx, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "ddelta_bias": dbias, "dz": dz}
     if conv_w is not None:
         g.update(dconv_w=dconv_w, dconv_b=dconv_b)
     if ln:
         g.update(dln_w=dln_w, dln_b=dln_b)
+    if R:
+        g.update(dx_proj_w=dxp, ddt_proj_w=ddtp)
     return g
 
 

@@ -174,6 +174,37 @@ hipError_t launch_ln_gate_bwd(const LnArgs& a, hipStream_t s);
 hipError_t launch_ln_reduce(const LnArgs& a, hipStream_t s);
 inline int64_t ln_part_rows(int64_t batch, int64_t L) { return batch * ((L + kLnPixels - 1) / kLnPixels); }
 
+// Small dense fp32 products of the Δ/B/C producer on MFMA (v_mfma_f32_32x32x2f32):
+//   C(i, j) (+)= sum_kk A(i, kk) B(kk, j)   for every batch (b0, b1)
+// Each operand is a strided view: element (r, c) of batch (b0, b1) of segment s is at
+//   p[s] + b0 * s_b0[s] + b1 * s_b1[s] + (r - first row of s) * s_r[s] + c' * s_c,
+// c' = (rev_c ? ncols - 1 - c : c); rows split into up to three segments at split1 <= split2
+// (one buffer each, e.g. the dt, B and C rows of the projected sequence).  With sum_b0 the
+// products of all b0 in [b0_begin, b0_end) of a block's slice are added into one output (no b0
+// offset on C): the weight gradients, summed over images.
+struct GemmOpnd {
+  const float* p[3];
+  int64_t s_r[3], s_b0[3], s_b1[3];
+  int64_t s_c;
+  int64_t split1, split2;  // rows [0, split1) -> segment 0, [split1, split2) -> 1, the rest -> 2
+  int rev_c;
+};
+struct GemmArgs {
+  GemmOpnd a, b, c;     // A (M x K), B (K x N), C (M x N); C's p are written
+  int64_t M, N, K;
+  int64_t nb0, nb1;     // batch extents
+  int sum_b0;           // reduce over b0: blockIdx.z splits b0 into b0_splits slices, each a partial C
+  int64_t b0_splits;    // with sum_b0: slice s writes C + s * c_split (partials summed by the caller)
+  int64_t c_split;
+  int accumulate;       // C += product (else C = product)
+};
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
+// out[i] = sum_{s < n_parts} part[s * n + i] in that order (partials of sum_b0 products)
+hipError_t launch_sum_parts(const float* part, float* out, int64_t n, int64_t n_parts, hipStream_t s);
+// fp32 copies of an SS2D input map: grid order (xf) and per-plane transposed (xfT)
+hipError_t launch_cast_transpose(const void* x, float* xf, float* xfT, int64_t batch, int64_t C, int64_t H,
+                                 int64_t W, int dtype, hipStream_t s);
+
 // Writes n fp32 zeros (a kernel, so that graph capture records no memset node).
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 

@@ -99,10 +99,18 @@ ScanLayout scan_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqle
 // ---- SS2D workspace layout -----------------------------------------------------------
 struct SS2DLayout {
   int64_t off_xT, off_ys, off_scan, off_merged, off_dM, off_dMT, off_xc, off_cpart, off_lnpart, total;
-  ScanLayout scan;
+  // the Δ/B/C producer (dt_rank > 0): fp32 projected inputs, their gradients, weight partials
+  int64_t off_pdt, off_pB, off_pC, off_pdelta, off_pddelta, off_pddt, off_pdB, off_pdC, off_pwx, off_pwdt;
+  int64_t proj_splits;
+  ScanLayout scan;    // chunk plan for the I/O type
+  ScanLayout scan32;  // chunk plan of the fp32 scans of the projected path (same offsets)
 };
 
-SS2DLayout ss2d_layout(int64_t batch, int64_t dim, int64_t H, int64_t W, int64_t dstate, int dtype) {
+// image slices of the weight-gradient products (each a partial summed afterwards)
+inline int64_t proj_splits(int64_t batch) { return batch < 128 ? batch : 128; }
+
+SS2DLayout ss2d_layout(int64_t batch, int64_t dim, int64_t H, int64_t W, int64_t dstate, int dtype,
+                       int64_t dt_rank = 0) {
   SS2DLayout l{};
   const int64_t L = H * W;
   int64_t o = 0;
@@ -116,6 +124,21 @@ SS2DLayout ss2d_layout(int64_t batch, int64_t dim, int64_t H, int64_t W, int64_t
   l.off_xc = o;     o += align_up(batch * dim * L * 4);                            // input front output (fp32)
   l.off_cpart = o;  o += align_up(batch * dim * front_tiles(H, W) * (kFrontMaxK * kFrontMaxK + 1) * 4);
   l.off_lnpart = o; o += align_up(ln_part_rows(batch, L) * 2 * dim * 4);  // LayerNorm parameter partials
+  l.scan32 = scan_layout(batch, 4 * dim, dstate, L, 4, SS2D_DTYPE_F32);
+  if (dt_rank > 0) {
+    const int64_t R = dt_rank, N = dstate, Cp = R + 2 * N, S = proj_splits(batch);
+    l.proj_splits = S;
+    l.off_pdt = o;     o += align_up(batch * 4 * R * L * 4);
+    l.off_pB = o;      o += align_up(batch * 4 * N * L * 4);
+    l.off_pC = o;      o += align_up(batch * 4 * N * L * 4);
+    l.off_pdelta = o;  o += align_up(batch * 4 * dim * L * 4);
+    l.off_pddelta = o; o += align_up(batch * 4 * dim * L * 4);
+    l.off_pddt = o;    o += align_up(batch * 4 * R * L * 4);
+    l.off_pdB = o;     o += align_up(batch * 4 * N * L * 4);
+    l.off_pdC = o;     o += align_up(batch * 4 * N * L * 4);
+    l.off_pwx = o;     o += align_up(S * 4 * Cp * dim * 4);
+    l.off_pwdt = o;    o += align_up(S * 4 * dim * R * 4);
+  }
   l.total = o;
   return l;
 }
@@ -311,10 +334,89 @@ size_t ss2d_workspace_bytes(int64_t batch, int64_t dim, int64_t height, int64_t 
   return size_t(ss2d_layout(batch, dim, height, width, dstate, dtype).total);
 }
 
+size_t ss2d_proj_workspace_bytes(int64_t batch, int64_t dim, int64_t height, int64_t width, int64_t dstate,
+                                 int64_t dt_rank, int dtype) {
+  if (batch < 0 || dim < 0 || height < 0 || width < 0 || dstate < 1 || dstate > 64 || !dtype_ok(dtype) ||
+      dt_rank < 1 || dt_rank > (dim > 0 ? dim : 1))
+    return 0;
+  return size_t(ss2d_layout(batch, dim, height, width, dstate, dtype, dt_rank).total);
+}
+
 // Stages of the SS2D forward (all on one workspace).
-// The map the four routes scan: x, or the input front's output (in the workspace).
-static const void* scan_input(const void* x, const float* conv_w, void* ws, const SS2DLayout& lay) {
-  return conv_w ? static_cast<const void*>(at(ws, lay.off_xc)) : x;
+// The map the four routes scan: x, or its fp32 copy in the workspace (the input front's output,
+// or the cast copy the projected path scans).
+static const void* scan_input(const void* x, bool in_ws, void* ws, const SS2DLayout& lay) {
+  return in_ws ? static_cast<const void*>(at(ws, lay.off_xc)) : x;
+}
+
+static float* wsf(void* ws, int64_t off) { return reinterpret_cast<float*>(at(ws, off)); }
+
+// The Δ/B/C producer: for each route k, x_dbl = x_proj_w[k] @ xs_k split into dt, B, C rows, then
+// delta = dt_proj_w[k] @ dt, all fp32 in route order in the workspace.  xs_k is the fp32 map
+// (routes 0, 2) or its transpose (routes 1, 3), read backwards for the reversed routes.
+static int ss2d_project(const ss2d_fwd_args* a, const SS2DLayout& lay, hipStream_t stream) {
+  const int64_t L = a->height * a->width, D = a->dim, N = a->dstate, R = a->dt_rank, Cp = R + 2 * N;
+  void* ws = a->workspace;
+  for (int k = 0; k < 4; ++k) {
+    GemmArgs g{};
+    g.a.p[0] = g.a.p[1] = g.a.p[2] = a->x_proj_w + k * Cp * D;
+    for (int q = 0; q < 3; ++q) g.a.s_r[q] = D;
+    g.a.s_c = 1;
+    g.a.split1 = g.a.split2 = Cp;
+    g.b.p[0] = g.b.p[1] = g.b.p[2] = wsf(ws, (k & 1) ? lay.off_xT : lay.off_xc);
+    for (int q = 0; q < 3; ++q) {
+      g.b.s_r[q] = L;
+      g.b.s_b0[q] = D * L;
+    }
+    g.b.s_c = 1;
+    g.b.split1 = g.b.split2 = D;
+    g.b.rev_c = k >= 2;
+    g.c.p[0] = wsf(ws, lay.off_pdt) + k * R * L;
+    g.c.p[1] = wsf(ws, lay.off_pB) + k * N * L;
+    g.c.p[2] = wsf(ws, lay.off_pC) + k * N * L;
+    for (int q = 0; q < 3; ++q) g.c.s_r[q] = L;
+    g.c.s_b0[0] = 4 * R * L;
+    g.c.s_b0[1] = g.c.s_b0[2] = 4 * N * L;
+    g.c.s_c = 1;
+    g.c.split1 = R;
+    g.c.split2 = R + N;
+    g.M = Cp;
+    g.N = L;
+    g.K = D;
+    g.nb0 = a->batch;
+    g.nb1 = 1;
+    if (launch_gemm(g, stream) != hipSuccess) return SS2D_ERR_HIP;
+  }
+  GemmArgs g{};
+  g.a.p[0] = g.a.p[1] = g.a.p[2] = a->dt_proj_w;
+  for (int q = 0; q < 3; ++q) {
+    g.a.s_r[q] = R;
+    g.a.s_b1[q] = D * R;
+  }
+  g.a.s_c = 1;
+  g.a.split1 = g.a.split2 = D;
+  g.b.p[0] = g.b.p[1] = g.b.p[2] = wsf(ws, lay.off_pdt);
+  for (int q = 0; q < 3; ++q) {
+    g.b.s_r[q] = L;
+    g.b.s_b0[q] = 4 * R * L;
+    g.b.s_b1[q] = R * L;
+  }
+  g.b.s_c = 1;
+  g.b.split1 = g.b.split2 = R;
+  g.c.p[0] = g.c.p[1] = g.c.p[2] = wsf(ws, lay.off_pdelta);
+  for (int q = 0; q < 3; ++q) {
+    g.c.s_r[q] = L;
+    g.c.s_b0[q] = 4 * D * L;
+    g.c.s_b1[q] = D * L;
+  }
+  g.c.s_c = 1;
+  g.c.split1 = g.c.split2 = D;
+  g.M = D;
+  g.N = L;
+  g.K = R;
+  g.nb0 = a->batch;
+  g.nb1 = 4;
+  return status_from(launch_gemm(g, stream));
 }
 
 // Stage 0: the column-major copy of the scanned map (and, with the input front, the map itself).
@@ -332,7 +434,14 @@ static int ss2d_transpose_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, h
     f.W = a->width;
     f.k = a->conv_k;
     f.dtype = a->dtype;
-    return status_from(launch_front_fwd(f, stream));
+    if (launch_front_fwd(f, stream) != hipSuccess) return SS2D_ERR_HIP;
+    return a->x_proj_w ? ss2d_project(a, lay, stream) : SS2D_OK;
+  }
+  if (a->x_proj_w) {
+    if (launch_cast_transpose(a->x, wsf(a->workspace, lay.off_xc), wsf(a->workspace, lay.off_xT), a->batch, a->dim,
+                              a->height, a->width, a->dtype, stream) != hipSuccess)
+      return SS2D_ERR_HIP;
+    return ss2d_project(a, lay, stream);
   }
   return status_from(launch_transpose(a->x, at(a->workspace, lay.off_xT), a->batch, a->dim, a->height, a->width,
                                       esize(a->dtype), stream));
@@ -343,13 +452,15 @@ static int ss2d_transpose_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, h
 static int ss2d_scan_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, bool keep_states, hipStream_t stream) {
   const int64_t L = a->height * a->width;
   ScanFwdParams p{};
-  p.u = scan_input(a->x, a->conv_w, a->workspace, lay);
+  const bool proj = a->x_proj_w != nullptr;  // fp32 scans of the projected inputs
+  const ScanLayout& sl = proj ? lay.scan32 : lay.scan;
+  p.u = scan_input(a->x, (a->conv_w != nullptr || a->x_proj_w != nullptr), a->workspace, lay);
   p.uT = at(a->workspace, lay.off_xT);
-  p.u_f32 = a->conv_w != nullptr && a->dtype != 0;
-  p.delta = a->delta;
+  p.u_f32 = a->conv_w != nullptr && a->dtype != 0 && !proj;
+  p.delta = proj ? wsf(a->workspace, lay.off_pdelta) : a->delta;
   p.A = a->A;
-  p.Bm = a->Bm;
-  p.Cm = a->Cm;
+  p.Bm = proj ? wsf(a->workspace, lay.off_pB) : a->Bm;
+  p.Cm = proj ? wsf(a->workspace, lay.off_pC) : a->Cm;
   p.delta_bias = a->delta_bias;
   p.out = at(a->workspace, lay.off_ys);
   p.batch = a->batch;
@@ -357,17 +468,17 @@ static int ss2d_scan_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, bool k
   p.L = L;
   p.G = 4;
   p.per_group = a->dim;
-  p.dblocks = lay.scan.dblocks;
-  p.n_ckpt = int(lay.scan.n_ckpt);
-  p.ckpt_every = lay.scan.ckpt_every;
+  p.dblocks = sl.dblocks;
+  p.n_ckpt = int(sl.n_ckpt);
+  p.ckpt_every = sl.ckpt_every;
   p.N = int(a->dstate);
   p.softplus = a->delta_softplus ? 1 : 0;
   p.ss2d = 1;
-  p.dtype = a->dtype;
-  p.vec = (L % 4 == 0) && vec_aligned(a->dtype, {p.u, a->delta, a->Bm, a->Cm});
-  p.chunk_len = lay.scan.chunk_len;
-  p.n_chunks = lay.scan.n_chunks;
-  if (a->batch * 4 * lay.scan.dblocks * 2 * p.n_chunks > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
+  p.dtype = proj ? SS2D_DTYPE_F32 : a->dtype;
+  p.vec = (L % 4 == 0) && vec_aligned(p.dtype, {p.u, p.delta, p.Bm, p.Cm});
+  p.chunk_len = sl.chunk_len;
+  p.n_chunks = sl.n_chunks;
+  if (a->batch * 4 * sl.dblocks * 2 * p.n_chunks > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
   p.chunk_sum = reinterpret_cast<float*>(at(a->workspace, lay.off_scan + lay.scan.off_sum));
   if (p.n_chunks > 1 || keep_states) p.ckpt = reinterpret_cast<float*>(at(a->workspace, lay.off_scan + lay.scan.off_ckpt));
   p.store_states = keep_states;
@@ -386,8 +497,8 @@ static int ss2d_merge_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, hipSt
   MergeArgs m{};
   m.routes = at(a->workspace, lay.off_ys);
   m.routes_f32 = 1;  // the scan stage writes fp32 route outputs
-  m.x = scan_input(a->x, a->conv_w, a->workspace, lay);
-  m.x_f32 = a->conv_w != nullptr;
+  m.x = scan_input(a->x, (a->conv_w != nullptr || a->x_proj_w != nullptr), a->workspace, lay);
+  m.x_f32 = (a->conv_w != nullptr || a->x_proj_w != nullptr);
   m.Dskip = a->Dskip;
   m.batch = a->batch;
   m.C = a->dim;
@@ -433,6 +544,13 @@ static int check_ln(int on, const float* w, const float* b, float eps) {
   return SS2D_OK;
 }
 
+// The Δ/B/C producer's weights: both or neither, dt_rank in [1, dim], fp32 4-byte aligned.
+static int check_proj(const float* wx, const float* wdt, int rank, int64_t dim) {
+  if (!wx) return wdt ? SS2D_ERR_INVALID_ARGUMENT : SS2D_OK;
+  if (!wdt || rank < 1 || rank > dim || !aligned(wx, 4) || !aligned(wdt, 4)) return SS2D_ERR_INVALID_ARGUMENT;
+  return SS2D_OK;
+}
+
 // The input front's filter: odd size 1..7, fp32 pointers 4-byte aligned.
 static int check_front(const float* w, const float* b, int k) {
   if (!w) return b ? SS2D_ERR_INVALID_ARGUMENT : SS2D_OK;
@@ -449,16 +567,21 @@ static int validate_ss2d_fwd(const ss2d_fwd_args* a, SS2DLayout* lay, bool* empt
   int st = check_ss2d(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype);
   if (st == SS2D_OK) st = check_front(a->conv_w, a->conv_b, a->conv_k);
   if (st == SS2D_OK) st = check_ln(a->layer_norm, a->ln_w, a->ln_b, a->ln_eps);
+  if (st == SS2D_OK && a->dim > 0) st = check_proj(a->x_proj_w, a->dt_proj_w, a->dt_rank, a->dim);
   if (st != SS2D_OK) return st;
   if (a->batch * a->dim * a->height * a->width == 0) {
     *empty = true;
     return SS2D_OK;
   }
-  if (!a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->out || !a->workspace) return SS2D_ERR_INVALID_ARGUMENT;
-  if (!elem_aligned(a->dtype, {a->x, a->delta, a->Bm, a->Cm, a->z, a->out})) return SS2D_ERR_INVALID_ARGUMENT;
+  const bool proj = a->x_proj_w != nullptr;  // delta, Bm, Cm come from the producer
+  if (!a->x || (!proj && (!a->delta || !a->Bm || !a->Cm)) || !a->A || !a->out || !a->workspace)
+    return SS2D_ERR_INVALID_ARGUMENT;
+  if (!elem_aligned(a->dtype, {a->x, proj ? nullptr : a->delta, proj ? nullptr : a->Bm, proj ? nullptr : a->Cm, a->z,
+                               a->out}))
+    return SS2D_ERR_INVALID_ARGUMENT;
   if (!aligned(a->A, 4) || (a->Dskip && !aligned(a->Dskip, 4)) || (a->delta_bias && !aligned(a->delta_bias, 4)))
     return SS2D_ERR_INVALID_ARGUMENT;
-  *lay = ss2d_layout(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype);
+  *lay = ss2d_layout(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype, proj ? a->dt_rank : 0);
   if (a->workspace_bytes < size_t(lay->total) || !aligned(a->workspace, kAlign)) return SS2D_ERR_INVALID_ARGUMENT;
   if (a->batch * a->dim * cdiv(a->height, 32) * cdiv(a->width, 32) > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
   return SS2D_OK;
@@ -638,18 +761,116 @@ int selective_scan_bwd(const ss_bwd_args* a, hipStream_t stream) {
                       a->delta_bias ? a->ddelta_bias : nullptr, stream);
 }
 
+// The Δ/B/C producer's gradient, given the scans' fp32 gradients of delta, B and C (route order):
+//   d dt = dt_proj_w[k]^T ddelta;  du_k += x_proj_w[k]^T (d dt; dB; dC)  (added to the routes' du
+//   before the merge);  dx_proj_w[k] = sum_b (d dt; dB; dC) xs_k^T;  ddt_proj_w[k] = sum_b ddelta dt^T
+// (the two weight products summed over images in proj_splits slices, then over the slices).
+static int ss2d_project_bwd(const ss2d_bwd_args* a, const SS2DLayout& lay, hipStream_t stream) {
+  const int64_t L = a->height * a->width, D = a->dim, N = a->dstate, R = a->dt_rank, Cp = R + 2 * N;
+  const int64_t S = lay.proj_splits;
+  void* ws = a->workspace;
+  auto uniform = [](GemmOpnd& o, const float* p, int64_t s_r, int64_t s_c, int64_t s_b0, int64_t s_b1, int64_t rows) {
+    o.p[0] = o.p[1] = o.p[2] = p;
+    for (int q = 0; q < 3; ++q) {
+      o.s_r[q] = s_r;
+      o.s_b0[q] = s_b0;
+      o.s_b1[q] = s_b1;
+    }
+    o.s_c = s_c;
+    o.split1 = o.split2 = rows;
+  };
+  // the rows (d dt; dB; dC) of route k's projected-sequence gradient, columns = steps
+  auto dxdbl = [&](GemmOpnd& o, int64_t k_off_rows, bool with_b1) {
+    o.p[0] = wsf(ws, lay.off_pddt) + k_off_rows * R * L;
+    o.p[1] = wsf(ws, lay.off_pdB) + k_off_rows * N * L;
+    o.p[2] = wsf(ws, lay.off_pdC) + k_off_rows * N * L;
+    for (int q = 0; q < 3; ++q) o.s_r[q] = L;
+    o.s_b0[0] = 4 * R * L;
+    o.s_b0[1] = o.s_b0[2] = 4 * N * L;
+    o.s_b1[0] = with_b1 ? R * L : 0;
+    o.s_b1[1] = o.s_b1[2] = with_b1 ? N * L : 0;
+    o.s_c = 1;
+    o.split1 = R;
+    o.split2 = R + N;
+  };
+  {  // d dt (R x L) = dt_proj_w[k]^T (R x D) ddelta (D x L), every (b, k)
+    GemmArgs g{};
+    uniform(g.a, a->dt_proj_w, 1, R, 0, D * R, R);
+    uniform(g.b, wsf(ws, lay.off_pddelta), L, 1, 4 * D * L, D * L, D);
+    uniform(g.c, wsf(ws, lay.off_pddt), L, 1, 4 * R * L, R * L, R);
+    g.M = R;
+    g.N = L;
+    g.K = D;
+    g.nb0 = a->batch;
+    g.nb1 = 4;
+    if (launch_gemm(g, stream) != hipSuccess) return SS2D_ERR_HIP;
+  }
+  {  // du_k (D x L) += x_proj_w[k]^T (D x Cp) (d dt; dB; dC) (Cp x L), into the routes' du
+    GemmArgs g{};
+    uniform(g.a, a->x_proj_w, 1, D, 0, Cp * D, D);
+    dxdbl(g.b, 0, true);
+    uniform(g.c, wsf(ws, lay.off_ys), L, 1, 4 * D * L, D * L, D);
+    g.M = D;
+    g.N = L;
+    g.K = Cp;
+    g.nb0 = a->batch;
+    g.nb1 = 4;
+    g.accumulate = 1;
+    if (launch_gemm(g, stream) != hipSuccess) return SS2D_ERR_HIP;
+  }
+  for (int k = 0; k < 4; ++k) {  // dx_proj_w[k] (Cp x D) = sum_{b, l} dx_dbl[c, l] xs_k[d, l]
+    GemmArgs g{};
+    dxdbl(g.a, k, false);
+    g.a.rev_c = k >= 2;  // reversed routes: step l of xs_k is pixel L-1-l of the source map
+    uniform(g.b, wsf(ws, (k & 1) ? lay.off_xT : lay.off_xc), 1, L, D * L, 0, L);
+    uniform(g.c, wsf(ws, lay.off_pwx) + k * Cp * D, D, 1, 0, 0, Cp);
+    g.M = Cp;
+    g.N = D;
+    g.K = L;
+    g.nb0 = a->batch;
+    g.nb1 = 1;
+    g.sum_b0 = 1;
+    g.b0_splits = S;
+    g.c_split = 4 * Cp * D;
+    if (launch_gemm(g, stream) != hipSuccess) return SS2D_ERR_HIP;
+  }
+  {  // ddt_proj_w[k] (D x R) = sum_{b, l} ddelta[d, l] dt[r, l]
+    GemmArgs g{};
+    uniform(g.a, wsf(ws, lay.off_pddelta), L, 1, 4 * D * L, D * L, D);
+    uniform(g.b, wsf(ws, lay.off_pdt), 1, L, 4 * R * L, R * L, L);
+    uniform(g.c, wsf(ws, lay.off_pwdt), R, 1, 0, D * R, D);
+    g.M = D;
+    g.N = R;
+    g.K = L;
+    g.nb0 = a->batch;
+    g.nb1 = 4;
+    g.sum_b0 = 1;
+    g.b0_splits = S;
+    g.c_split = 4 * D * R;
+    if (launch_gemm(g, stream) != hipSuccess) return SS2D_ERR_HIP;
+  }
+  if (launch_sum_parts(wsf(ws, lay.off_pwx), a->dx_proj_w, 4 * Cp * D, S, stream) != hipSuccess ||
+      launch_sum_parts(wsf(ws, lay.off_pwdt), a->ddt_proj_w, 4 * D * R, S, stream) != hipSuccess)
+    return SS2D_ERR_HIP;
+  return SS2D_OK;
+}
+
 int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
   if (!a) return SS2D_ERR_INVALID_ARGUMENT;
   int st = check_ss2d(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype);
   if (st == SS2D_OK) st = check_front(a->conv_w, a->conv_b, a->conv_k);
   if (st == SS2D_OK) st = check_ln(a->layer_norm, a->ln_w, a->ln_b, a->ln_eps);
+  if (st == SS2D_OK && a->dim > 0) st = check_proj(a->x_proj_w, a->dt_proj_w, a->dt_rank, a->dim);
   if (st != SS2D_OK) return st;
   const bool lnw = a->layer_norm && a->ln_w, lnb = a->layer_norm && a->ln_b;
+  const bool proj = a->x_proj_w != nullptr;
   if ((a->Dskip && !a->dDskip) || (a->delta_bias && !a->ddelta_bias) || (a->z && !a->dz) ||
-      (a->conv_w && !a->dconv_w) || (a->conv_b && !a->dconv_b) || (lnw && !a->dln_w) || (lnb && !a->dln_b))
+      (a->conv_w && !a->dconv_w) || (a->conv_b && !a->dconv_b) || (lnw && !a->dln_w) || (lnb && !a->dln_b) ||
+      (proj && (!a->dx_proj_w || !a->ddt_proj_w)))
     return SS2D_ERR_INVALID_ARGUMENT;
   if ((a->dconv_w && !aligned(a->dconv_w, 4)) || (a->dconv_b && !aligned(a->dconv_b, 4)) ||
-      (a->dln_w && !aligned(a->dln_w, 4)) || (a->dln_b && !aligned(a->dln_b, 4)))
+      (a->dln_w && !aligned(a->dln_w, 4)) || (a->dln_b && !aligned(a->dln_b, 4)) ||
+      (proj && (!aligned(a->dx_proj_w, 4) || !aligned(a->ddt_proj_w, 4))))
     return SS2D_ERR_INVALID_ARGUMENT;
   if (a->dim == 0) return SS2D_OK;
   if (!a->dA) return SS2D_ERR_INVALID_ARGUMENT;
@@ -661,21 +882,28 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
                             int64_t(a->conv_k) * a->conv_k, stream);
     if (st == SS2D_OK && lnw) st = status_from(launch_fill_zero(a->dln_w, a->dim, stream));
     if (st == SS2D_OK && lnb) st = status_from(launch_fill_zero(a->dln_b, a->dim, stream));
+    if (st == SS2D_OK && proj) {
+      const int64_t Cp = a->dt_rank + 2 * a->dstate;
+      st = status_from(launch_fill_zero(a->dx_proj_w, 4 * Cp * a->dim, stream));
+      if (st == SS2D_OK) st = status_from(launch_fill_zero(a->ddt_proj_w, 4 * a->dim * a->dt_rank, stream));
+    }
     return st;
   }
-  if (!a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->dout || !a->dx || !a->ddelta || !a->dBm || !a->dCm ||
-      !a->workspace)
+  if (!a->x || !a->A || !a->dout || !a->dx || !a->workspace ||
+      (!proj && (!a->delta || !a->Bm || !a->Cm || !a->ddelta || !a->dBm || !a->dCm)))
     return SS2D_ERR_INVALID_ARGUMENT;
-  if (!elem_aligned(a->dtype, {a->x, a->delta, a->Bm, a->Cm, a->z, a->dout, a->dx, a->ddelta, a->dBm, a->dCm, a->dz}))
+  if (!elem_aligned(a->dtype, {a->x, a->z, a->dout, a->dx, a->dz}) ||
+      (!proj && !elem_aligned(a->dtype, {a->delta, a->Bm, a->Cm, a->ddelta, a->dBm, a->dCm})))
     return SS2D_ERR_INVALID_ARGUMENT;
   if (!aligned(a->A, 4) || !aligned(a->dA, 4) || (a->Dskip && !aligned(a->Dskip, 4)) ||
       (a->delta_bias && !aligned(a->delta_bias, 4)) || (a->dDskip && !aligned(a->dDskip, 4)) ||
       (a->ddelta_bias && !aligned(a->ddelta_bias, 4)))
     return SS2D_ERR_INVALID_ARGUMENT;
-  const SS2DLayout lay = ss2d_layout(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype);
+  const SS2DLayout lay =
+      ss2d_layout(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype, proj ? a->dt_rank : 0);
   if (a->workspace_bytes < size_t(lay.total) || !aligned(a->workspace, kAlign)) return SS2D_ERR_INVALID_ARGUMENT;
   if (a->batch * a->dim * cdiv(a->height, 32) * cdiv(a->width, 32) > kMaxBlocks ||
-      a->batch * 4 * lay.scan.dblocks * 2 * lay.scan.n_chunks > kMaxBlocks ||
+      a->batch * 4 * lay.scan.dblocks * 2 * (proj ? lay.scan32.n_chunks : lay.scan.n_chunks) > kMaxBlocks ||
       a->batch * 4 * lay.scan.dblocks * lay.scan.bwd_n_chunks > kMaxBlocks)
     return SS2D_ERR_INVALID_ARGUMENT;
   const int64_t L = a->height * a->width;
@@ -702,12 +930,15 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
     f.conv_w = a->conv_w;
     f.conv_b = a->conv_b;
     f.conv_k = a->conv_k;
+    f.x_proj_w = a->x_proj_w;
+    f.dt_proj_w = a->dt_proj_w;
+    f.dt_rank = a->dt_rank;
     st = ss2d_transpose_stage(&f, lay, stream);
     if (st == SS2D_OK) st = ss2d_scan_stage(&f, lay, true, stream);
     if (st != SS2D_OK) return st;
   }
 
-  const void* u = scan_input(a->x, a->conv_w, a->workspace, lay);
+  const void* u = scan_input(a->x, (a->conv_w != nullptr || a->x_proj_w != nullptr), a->workspace, lay);
   if (a->layer_norm) {
     // the LayerNorm's and the gate's backward need the whole pixel: the fp32 merged map first,
     // then dz, dM (grid order) and the parameter partials per pixel block, then dM transposed
@@ -717,7 +948,7 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
     m.routes = at(a->workspace, lay.off_ys);
     m.routes_f32 = 1;
     m.x = u;
-    m.x_f32 = a->conv_w != nullptr;
+    m.x_f32 = (a->conv_w != nullptr || a->x_proj_w != nullptr);
     m.Dskip = a->Dskip;
     m.merged_f32 = merged;
     m.batch = a->batch;
@@ -752,7 +983,7 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
     MergeGateArgs gb{};
     gb.routes = reinterpret_cast<const float*>(at(a->workspace, lay.off_ys));
     gb.x = u;
-    gb.x_f32 = a->conv_w != nullptr;
+    gb.x_f32 = (a->conv_w != nullptr || a->x_proj_w != nullptr);
     gb.Dskip = a->Dskip;
     gb.z = a->z;
     gb.dout = a->dout;
@@ -770,19 +1001,20 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
 
   // adjoint scans of the four routes; du (fp32, route order) reuses the route-output region
   ScanBwdParams bp{};
+  void* ws = a->workspace;
   bp.u = u;
-  bp.uT = at(a->workspace, lay.off_xT);
-  bp.u_f32 = a->conv_w != nullptr && a->dtype != 0;
-  bp.delta = a->delta;
+  bp.uT = at(ws, lay.off_xT);
+  bp.u_f32 = a->conv_w != nullptr && a->dtype != 0 && !proj;
+  bp.delta = proj ? wsf(ws, lay.off_pdelta) : a->delta;
   bp.A = a->A;
-  bp.Bm = a->Bm;
-  bp.Cm = a->Cm;
+  bp.Bm = proj ? wsf(ws, lay.off_pB) : a->Bm;
+  bp.Cm = proj ? wsf(ws, lay.off_pC) : a->Cm;
   bp.Dskip = a->Dskip;
   bp.delta_bias = a->delta_bias;
   bp.dout = at(a->workspace, lay.off_dM);
   bp.doutT = at(a->workspace, lay.off_dMT);
   bp.du = at(a->workspace, lay.off_ys);
-  bp.ddelta = a->ddelta;
+  bp.ddelta = proj ? wsf(ws, lay.off_pddelta) : a->ddelta;
   bp.batch = a->batch;
   bp.dim = 4 * a->dim;
   bp.L = L;
@@ -792,11 +1024,16 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
   bp.N = int(a->dstate);
   bp.softplus = a->delta_softplus ? 1 : 0;
   bp.ss2d = 1;
-  bp.dtype = a->dtype;
-  bp.vec = (L % 4 == 0) && vec_aligned(a->dtype, {u, a->delta, a->Bm, a->Cm, a->ddelta});
-  st = run_scan_bwd(bp, lay.scan, at(a->workspace, lay.off_scan), a->dBm, a->dCm, a->dA,
-                    a->Dskip ? a->dDskip : nullptr, a->delta_bias ? a->ddelta_bias : nullptr, stream);
+  bp.dtype = proj ? SS2D_DTYPE_F32 : a->dtype;
+  bp.vec = (L % 4 == 0) && vec_aligned(bp.dtype, {u, bp.delta, bp.Bm, bp.Cm, bp.ddelta});
+  st = run_scan_bwd(bp, lay.scan, at(ws, lay.off_scan), proj ? wsf(ws, lay.off_pdB) : a->dBm,
+                    proj ? wsf(ws, lay.off_pdC) : a->dCm, a->dA, a->Dskip ? a->dDskip : nullptr,
+                    a->delta_bias ? a->ddelta_bias : nullptr, stream);
   if (st != SS2D_OK) return st;
+  if (proj) {
+    st = ss2d_project_bwd(a, lay, stream);
+    if (st != SS2D_OK) return st;
+  }
 
   // dx = cross-merge of the routes' du (with the input front: the gradient w.r.t. its output,
   // in fp32, which the front's backward turns into dx and the filter gradients)

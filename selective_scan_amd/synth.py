@@ -18,7 +18,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-T_X, T_Z, T_DELTA, T_B, T_C, T_U, T_DOUT, T_CONV, T_LN = range(9)
+T_X, T_Z, T_DELTA, T_B, T_C, T_U, T_DOUT, T_CONV, T_LN, T_PROJ = range(10)
 
 
 @dataclass(frozen=True)
@@ -150,6 +150,17 @@ def make_ln_params(dim: int, seed_base: int = 0) -> dict:
     w = (1.0 + 0.3 * rng.standard_normal(size=(dim,), dtype=np.float32)).astype(np.float32)
     b = (np.float32(0.2) * rng.standard_normal(size=(dim,), dtype=np.float32)).astype(np.float32)
     return {"ln_w": w, "ln_b": b}
+
+
+def make_proj_params(dim: int, dstate: int, dt_rank: int, seed_base: int = 0) -> dict:
+    """Weights of the Δ/B/C producer, fp32: x_proj_w (4, R + 2N, dim) ~ N(0, 1/dim) (unit-variance
+    projections of a unit-variance input), dt_proj_w (4, dim, R) ~ U(-R^-1/2, R^-1/2) (the `Mamba`
+    module's "random" dt initialisation with dt_scale 1)."""
+    rng = np.random.Generator(np.random.PCG64(1000 * seed_base + T_PROJ))
+    wx = (rng.standard_normal(size=(4, dt_rank + 2 * dstate, dim), dtype=np.float32) / np.float32(np.sqrt(dim)))
+    std = np.float32(dt_rank ** -0.5)
+    wdt = rng.uniform(-std, std, size=(4, dim, dt_rank)).astype(np.float32)
+    return {"x_proj_w": wx.astype(np.float32), "dt_proj_w": wdt}
 
 
 def make_config_inputs(cfg: SS2DConfig, with_dout: bool | None = None) -> dict:

@@ -33,6 +33,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert {"ss2d_cross_scan", "ss2d_cross_merge", "selective_scan_fwd", "selective_scan_bwd", "ss2d_fwd",
             "ss2d_bwd", "ss2d_fwd_stage", "selective_scan_workspace_bytes", "ss2d_workspace_bytes",
             "ss2d_abi_version", "ss2d_status_string", "vim_bidir_workspace_bytes", "vim_bidir_fwd",
+            "ss2d_proj_workspace_bytes",
             "vim_bidir_fwd_stage", "vim_bidir_bwd", "selective_scan_step"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
@@ -43,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ss2d_abi_version() == 6
+    assert lib.ss2d_abi_version() == 7
     assert lib.ss2d_status_string(0) == b"ok"
     assert b"invalid" in lib.ss2d_status_string(1)
     assert b"unsupported" in lib.ss2d_status_string(2)
@@ -148,6 +149,17 @@ def test_ss2d_rejects(lib):
     ln = dict(workspace_bytes=1 << 40, dz=0, layer_norm=1, ln_eps=1e-5)
     assert lib.ss2d_bwd(ctypes.byref(SS2DBwdArgs(**{**b, **ln, "ln_w": 0xd000})), None) == 1        # no dln_w
     assert lib.ss2d_bwd(ctypes.byref(SS2DBwdArgs(**{**b, **ln, "ln_b": 0xd000})), None) == 1        # no dln_b
+    # the Δ/B/C producer: both weights, dt_rank in [1, dim], weight gradients required
+    pf = {**f, "delta": 0, "Bm": 0, "Cm": 0, "workspace_bytes": 1 << 40}
+    assert lib.ss2d_fwd(ctypes.byref(SS2DFwdArgs(**{**pf, "x_proj_w": 0xd000, "dt_rank": 2})), None) == 1  # no dt_proj_w
+    assert lib.ss2d_fwd(ctypes.byref(SS2DFwdArgs(**{**pf, "dt_proj_w": 0xd000, "dt_rank": 2})), None) == 1  # no x_proj_w
+    for r in (0, 5):
+        assert lib.ss2d_fwd(ctypes.byref(SS2DFwdArgs(**{**pf, "x_proj_w": 0xd000, "dt_proj_w": 0xe000, "dt_rank": r})),
+                            None) == 1, r
+    assert lib.ss2d_fwd(ctypes.byref(SS2DFwdArgs(**{**f, "delta": 0})), None) == 1    # no delta, no producer
+    pb = {**b, "delta": 0, "Bm": 0, "Cm": 0, "ddelta": 0, "dBm": 0, "dCm": 0, "workspace_bytes": 1 << 40,
+          "x_proj_w": 0xd000, "dt_proj_w": 0xe000, "dt_rank": 2}
+    assert lib.ss2d_bwd(ctypes.byref(SS2DBwdArgs(**pb)), None) == 1                   # no weight gradients
 
 
 def test_vim_bidir_rejects(lib):
@@ -203,6 +215,10 @@ def test_workspace_queries(lib):
     s2 = lib.ss2d_workspace_bytes(1, 16, 8, 8, 4, 1)
     assert 0 < s2 <= s1  # fp32 intermediates: the I/O type changes no workspace region
     assert lib.ss2d_workspace_bytes(1, 16, 8, 8, 4, 9) == 0
+    p1 = lib.ss2d_proj_workspace_bytes(1, 16, 8, 8, 4, 2, 1)
+    assert p1 > s2 and p1 % 256 == 0  # the plain regions plus the producer's
+    assert lib.ss2d_proj_workspace_bytes(1, 16, 8, 8, 4, 0, 1) == 0
+    assert lib.ss2d_proj_workspace_bytes(1, 16, 8, 8, 4, 17, 1) == 0
     v1 = lib.vim_bidir_workspace_bytes(2, 8, 197, 16, 1)
     v2 = lib.vim_bidir_workspace_bytes(2, 8, 197, 16, 0)
     assert 0 < v1 == v2  # fp32 direction outputs and gradients: the same size for either I/O type
