@@ -174,32 +174,57 @@ hipError_t launch_ln_gate_bwd(const LnArgs& a, hipStream_t s);
 hipError_t launch_ln_reduce(const LnArgs& a, hipStream_t s);
 inline int64_t ln_part_rows(int64_t batch, int64_t L) { return batch * ((L + kLnPixels - 1) / kLnPixels); }
 
-// Small dense fp32 products of the Δ/B/C producer on MFMA (v_mfma_f32_32x32x2f32):
-//   C(i, j) (+)= sum_kk A(i, kk) B(kk, j)   for every batch (b0, b1)
-// Each operand is a strided view: element (r, c) of batch (b0, b1) of segment s is at
-//   p[s] + b0 * s_b0[s] + b1 * s_b1[s] + (r - first row of s) * s_r[s] + c' * s_c,
-// c' = (rev_c ? ncols - 1 - c : c); rows split into up to three segments at split1 <= split2
-// (one buffer each, e.g. the dt, B and C rows of the projected sequence).  With sum_b0 the
-// products of all b0 in [b0_begin, b0_end) of a block's slice are added into one output (no b0
-// offset on C): the weight gradients, summed over images.
-struct GemmOpnd {
-  const float* p[3];
-  int64_t s_r[3], s_b0[3], s_b1[3];
-  int64_t s_c;
-  int64_t split1, split2;  // rows [0, split1) -> segment 0, [split1, split2) -> 1, the rest -> 2
-  int rev_c;
+// Dense fp32 products of the Δ/B/C producer on MFMA (v_mfma_f32_32x32x2f32).  Every product runs
+// over the (image b, route k) pairs of a launch, z = b * nk + k.
+//
+// Weight times sequence (x_proj and dt_proj of a route's sequence, and the transposed products of
+// the gradient):  C_z(i, j) (+)= sum_kk W_k(i, kk) X_z(kk, j),  i < M, kk < K, j < L, with
+//   W_k(i, kk) = w[k * w_k + i * w_i + kk * w_kk]                       (any strides: W or W^T)
+//   X_z(kk, j) = xk[b * x_b + k * x_k + kk * x_r + j'],  xk = (k odd ? x1 : x0),
+//                j' = L - 1 - j for routes k >= 2 when rev_routes, else j
+//   C_z(i, j)  = c[b * c_b + k * c_k + i * c_r + j]
+struct ProjArgs {
+  const float* w;
+  int64_t w_k, w_i, w_kk;
+  const float* x0;
+  const float* x1;
+  int64_t x_b, x_k, x_r;
+  float* c;
+  int64_t c_b, c_k, c_r;
+  int64_t M, K, L, batch;
+  int nk;
+  int rev_routes;
+  int accumulate;  // C += product, else C = product
+  int64_t m_tiles; // set by launch_proj
 };
-struct GemmArgs {
-  GemmOpnd a, b, c;     // A (M x K), B (K x N), C (M x N); C's p are written
-  int64_t M, N, K;
-  int64_t nb0, nb1;     // batch extents
-  int sum_b0;           // reduce over b0: blockIdx.z splits b0 into b0_splits slices, each a partial C
-  int64_t b0_splits;    // with sum_b0: slice s writes C + s * c_split (partials summed by the caller)
-  int64_t c_split;
-  int accumulate;       // C += product (else C = product)
+hipError_t launch_proj(const ProjArgs& g, hipStream_t s);
+
+// Weight gradient: per route k, C_k(i, j) = sum over the images and steps of a slice of
+//   A_z(i, l) B_z(j, l),  i < M, j < N, l < K (the sequence length), with
+//   A_z(i, l) = a[b * a_b + k * a_k + i * a_r + l'],  l' = K - 1 - l for routes k >= 2 when
+//               rev_routes, else l
+//   B_z(j, l) = bk[b * b_b + k * b_k + j * b_r + l],  bk = (k odd ? b1 : b0)
+// The (image, 64-step unit) pairs are cut into `splits` contiguous slices; slice s writes its
+// partial to c[(s * nk + k) * M * N + i * N + j] (summed afterwards by launch_sum_parts).
+struct WgradArgs {
+  const float* a;
+  int64_t a_b, a_k, a_r;
+  const float* b0;
+  const float* b1;
+  int64_t b_b, b_k, b_r;
+  float* c;
+  int64_t M, N, K, batch;
+  int nk, splits;
+  int rev_routes;
 };
-hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
-// out[i] = sum_{s < n_parts} part[s * n + i] in that order (partials of sum_b0 products)
+hipError_t launch_wgrad(const WgradArgs& g, hipStream_t s);
+// steps per work unit of launch_wgrad (one 16-step piece per wavefront)
+constexpr int kWgradUnit = 64;
+inline int64_t wgrad_splits(int64_t batch, int64_t L) {
+  const int64_t units = batch * ((L + kWgradUnit - 1) / kWgradUnit);
+  return units < 256 ? units : 256;
+}
+// out[i] = sum_{s < n_parts} part[s * n + i] in that order (the weight-gradient partials)
 hipError_t launch_sum_parts(const float* part, float* out, int64_t n, int64_t n_parts, hipStream_t s);
 // fp32 copies of an SS2D input map: grid order (xf) and per-plane transposed (xfT)
 hipError_t launch_cast_transpose(const void* x, float* xf, float* xfT, int64_t batch, int64_t C, int64_t H,
@@ -237,6 +262,7 @@ struct ScanFwdParams {
   int store_states;    // pass 0 also keeps the state before every ckpt_every-th step in ckpt
   int out_f32;         // generic rows: out is fp32 instead of the I/O type
   int u_f32;           // ss2d rows, bf16 I/O: u and uT are fp32 (the input front's output)
+  int64_t bc_stride;   // elements between the (b, g) blocks of B and C (0: N * L, dense)
 };
 hipError_t launch_scan_fwd(const ScanFwdParams& p, hipStream_t s);
 // Turns the chunk-local end states (pass 1) into the true chunk-start states.
@@ -294,6 +320,7 @@ struct ScanBwdParams {
   int pass;                // 1: chunk-local lambda pass; 0: gradients
   int dout_f32;            // generic rows: dout is fp32 instead of the I/O type
   int u_f32;               // ss2d rows, bf16 I/O: u and uT are fp32 (the input front's output)
+  int64_t bc_stride;       // elements between the (b, g) blocks of B and C (0: N * L, dense)
 };
 hipError_t launch_scan_bwd(const ScanBwdParams& p, hipStream_t s);
 hipError_t launch_lambda_combine(const ScanBwdParams& p, hipStream_t s);
@@ -311,6 +338,7 @@ struct BwdReduceArgs {
   float* dbias;
   int64_t batch, dim, L, G, dblocks;
   int n_chunks, N, dtype;
+  int64_t bc_out_stride;  // elements between the (b, g) blocks of dB / dC (0: N * L, dense)
 };
 hipError_t launch_bwd_reduce(const BwdReduceArgs& a, hipStream_t s);
 

@@ -1,15 +1,30 @@
 // Dense fp32 products of the Δ/B/C producer (the per-route x_proj and dt_proj of the scanned
 // sequence, the `Mamba` module's projections on "Vision Mamba structure and principle", section
 // 2) and of its gradient, on the matrix cores: v_mfma_f32_32x32x2f32, fp32 operands and
-// accumulation (no rounding of any operand).
+// accumulation (no rounding of any operand).  Lane layout of the instruction (checked on the
+// device): lane l supplies A[l % 32][l / 32] and B[l / 32][l % 32]; accumulator v of lane l is
+// C[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].  The two k-slots of an instruction may stand for any
+// two elements of the contraction as long as A and B agree: here step s of a chunk of 2H
+// elements takes slot 0 from element s and slot 1 from element H + s, so that each lane reads H
+// consecutive elements of its row.
 //
-// One workgroup computes a 64 x 64 tile of C with four wavefronts (2 x 2 blocks of 32 x 32, 16
-// accumulators per lane).  K advances in chunks of 32: each thread loads 8 elements of the A tile
-// and 8 of the B tile (strided views, addresses clamped and out-of-range values zeroed by a
-// select, so the loads carry no branch), the tiles go through LDS k-major, and each wavefront
-// issues 16 MFMAs per chunk.  Lane layout of the instruction (checked on the device): lane l
-// supplies A[l % 32][l / 32] and B[l / 32][l % 32]; accumulator v of lane l is
-// C[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
+// Two kernels, both with every load branch-free (clamped addresses) and the next chunk's loads
+// issued before the current chunk's MFMAs.  Values past the end of the contraction are zeroed
+// on one operand by a product with a 0/1 mask (exact for the finite values read through a
+// clamped address), not by a select: the compiler turns a select of a loaded word into a branch
+// around the load and so moves the load behind the MFMAs.  The other operand is then finite
+// (a valid element), so the padded terms are exact zeros.
+//   proj_kernel   C (M x L) (+)= W (M x K) X (K x L): a small weight times a long sequence (x_proj,
+//                 dt_proj, and the transposed products of the gradient).  A tile is 32 MB rows x
+//                 128 columns (MB <= 4); wavefront w owns columns [32 w, 32 w + 32) and all MB
+//                 row blocks.
+//                 The sequence chunk goes through LDS (double buffered); the weight values come
+//                 straight from memory (a few KB per route, cache resident).
+//   wgrad_kernel  C (M x N) = sum_l A (M x l) B (N x l): the weight gradients, a contraction over
+//                 images and steps.  Each wavefront takes 16 steps of every 64-step unit of its
+//                 slice and keeps the whole tile; the four wavefronts are summed through LDS.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -18,88 +33,274 @@ namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int kTM = 64, kTN = 64, kTK = 32, kThreads = 256, kPad = 4;
+constexpr int kThreads = 256;
+constexpr int kPN = 128;  // columns per tile of proj_kernel
 
-// Address of element (r, c) of an operand view, batch (b0, b1); ncols = the column extent (for
-// reversed columns).  Segment pointers are picked by selects (no dynamic indexing of the
-// argument block).
-__device__ __forceinline__ const float* opnd_addr(const GemmOpnd& o, int64_t r, int64_t c, int64_t ncols, int64_t b0,
-                                                  int64_t b1) {
-  const bool s1 = r >= o.split1, s2 = r >= o.split2;
-  const float* p = s2 ? o.p[2] : (s1 ? o.p[1] : o.p[0]);
-  const int64_t sr = s2 ? o.s_r[2] : (s1 ? o.s_r[1] : o.s_r[0]);
-  const int64_t sb0 = s2 ? o.s_b0[2] : (s1 ? o.s_b0[1] : o.s_b0[0]);
-  const int64_t sb1 = s2 ? o.s_b1[2] : (s1 ? o.s_b1[1] : o.s_b1[0]);
-  const int64_t r0 = s2 ? o.split2 : (s1 ? o.split1 : 0);
-  const int64_t cc = o.rev_c ? ncols - 1 - c : c;
-  return p + b0 * sb0 + b1 * sb1 + (r - r0) * sr + cc * o.s_c;
+__device__ __forceinline__ float4 rev4(float4 v) { return make_float4(v.w, v.z, v.y, v.x); }
+
+template <int MB, int TK, bool kVec>
+__global__ __launch_bounds__(kThreads) void proj_kernel(const ProjArgs g) {
+  constexpr int kHalf = TK / 2;
+  constexpr int kXPer = kVec ? TK * kPN / 4 / kThreads : TK * kPN / kThreads;
+  typedef typename std::conditional<kVec, float4, float>::type XReg;
+  __shared__ float xs[2][TK][kPN + 4];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, jl = lane & 31, h = lane >> 5;
+  const int64_t z = blockIdx.y, b = z / g.nk;
+  const int k = int(z - b * g.nk);
+  // x = column tile * row tiles + row tile: the row tiles of one column tile run together and
+  // share the sequence chunk in the caches
+  const int64_t ct = blockIdx.x / g.m_tiles;
+  const int64_t n0 = ct * kPN, m0 = (int64_t(blockIdx.x) - ct * g.m_tiles) * (32 * MB);
+  const bool rev = g.rev_routes && k >= 2;
+  const float* xb = ((k & 1) ? g.x1 : g.x0) + b * g.x_b + k * g.x_k;
+  const float* wrow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int64_t i = m0 + 32 * mb + jl;
+    wrow[mb] = g.w + k * g.w_k + (i < g.M ? i : g.M - 1) * g.w_i;  // rows past M feed no output
+  }
+  // this thread's column of the sequence chunk and its first row
+  const int xr0 = kVec ? (t >> 5) : (t >> 7), xstep = kVec ? 8 : 2;
+  const int xcol = kVec ? 4 * (t & 31) : (t & 127);
+  const int64_t cg = n0 + xcol;
+  const bool colok = cg < g.L;  // vector path: L % 4 == 0, so a granule is all in or all out
+  const int64_t gcol = colok ? (rev ? g.L - (kVec ? 4 : 1) - cg : cg) : 0;
+  const float* xcolp = xb + gcol;
+  const int64_t nch = (g.K + TK - 1) / TK;
+
+  // Loads keep the raw words; the column reversal and the zeroing of rows past K happen when the
+  // chunk is written to LDS, after the MFMAs (a select right after a load would make the compiler
+  // wait for it there).  Weight values past K need no zeroing: they meet zero sequence rows.
+  XReg xr[kXPer];
+  bool xok[kXPer];
+  float acur[MB][kHalf], anxt[MB][kHalf];
+  auto load = [&](int64_t k0, float (&a)[MB][kHalf]) {
+#pragma unroll
+    for (int q = 0; q < kXPer; ++q) {
+      const int64_t kk = k0 + xr0 + xstep * q;
+      xok[q] = colok && kk < g.K;
+      const float* p = xcolp + (kk < g.K ? kk : g.K - 1) * g.x_r;
+      if constexpr (kVec)
+        xr[q] = *reinterpret_cast<const float4*>(p);
+      else
+        xr[q] = *p;
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int s = 0; s < kHalf; ++s) {
+        const int64_t kk = k0 + h * kHalf + s;
+        a[mb][s] = wrow[mb][(kk < g.K ? kk : g.K - 1) * g.w_kk];
+      }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < kXPer; ++q) {
+      const float m = xok[q] ? 1.0f : 0.0f;
+      if constexpr (kVec) {
+        const float4 v = rev ? rev4(xr[q]) : xr[q];
+        *reinterpret_cast<float4*>(&xs[buf][xr0 + xstep * q][xcol]) = make_float4(v.x * m, v.y * m, v.z * m, v.w * m);
+      } else {
+        xs[buf][xr0 + xstep * q][xcol] = xr[q] * m;
+      }
+    }
+  };
+
+  floatx16 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx16{};
+  load(0, acur);
+  store(0);
+  __syncthreads();
+  for (int64_t c = 0; c < nch; ++c) {
+    load((c + 1 < nch ? c + 1 : c) * TK, anxt);  // the last chunk reloads itself (unused)
+    __builtin_amdgcn_sched_barrier(0);            // issue the loads before the MFMAs
+    const int buf = int(c & 1);
+#pragma unroll
+    for (int s = 0; s < kHalf; ++s) {
+      const float bv = xs[buf][h * kHalf + s][32 * wave + jl];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(acur[mb][s], bv, acc[mb], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // use the new words only after the MFMAs
+    store(buf ^ 1);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int s = 0; s < kHalf; ++s) acur[mb][s] = anxt[mb][s];
+    __syncthreads();
+  }
+
+  // accumulator v of row block mb is row m0 + 32 mb + 4 h + 8 (v / 4) + v % 4, column jc
+  const int64_t jc = n0 + 32 * wave + jl;
+  const bool jok = jc < g.L;
+  float* cb = g.c + b * g.c_b + k * g.c_k + (jok ? jc : 0);
+  // two row blocks at a time: the previous values (when accumulating) are all loaded first
+#pragma unroll
+  for (int m2 = 0; m2 < MB; m2 += 2) {
+    constexpr int kPair = MB > 1 ? 2 : 1;
+    if (g.accumulate) {
+      float old[kPair][16];
+#pragma unroll
+      for (int e = 0; e < kPair; ++e)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t i = m0 + 32 * (m2 + e) + 4 * h + 8 * (v / 4) + v % 4;
+          old[e][v] = (m2 + e < MB) ? cb[(jok && i < g.M ? i : 0) * g.c_r] : 0.0f;
+        }
+#pragma unroll
+      for (int e = 0; e < kPair; ++e)
+        if (m2 + e < MB)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[m2 + e][v] += old[e][v];
+    }
+#pragma unroll
+    for (int e = 0; e < kPair; ++e)
+      if (m2 + e < MB)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t i = m0 + 32 * (m2 + e) + 4 * h + 8 * (v / 4) + v % 4;
+          if (jok && i < g.M) cb[i * g.c_r] = acc[m2 + e][v];
+        }
+  }
 }
 
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
-  __shared__ float As[kTK][kTM + kPad];  // k-major: As[kk][i]
-  __shared__ float Bs[kTK][kTN + kPad];  // Bs[kk][j]
-  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
-  const int wm = wave / 2, wn = wave % 2;
-  const int64_t m0 = int64_t(blockIdx.y) * kTM, n0 = int64_t(blockIdx.x) * kTN;
-  int64_t b1, b0_begin, b0_end, split = 0;
-  if (g.sum_b0) {
-    split = blockIdx.z % g.b0_splits;
-    b1 = blockIdx.z / g.b0_splits;
-    const int64_t per = (g.nb0 + g.b0_splits - 1) / g.b0_splits;
-    b0_begin = split * per;
-    b0_end = b0_begin + per < g.nb0 ? b0_begin + per : g.nb0;
-  } else {
-    b0_begin = blockIdx.z % g.nb0;
-    b0_end = b0_begin + 1;
-    b1 = blockIdx.z / g.nb0;
+template <int MBW, int NBW, bool kVec>
+__global__ __launch_bounds__(kThreads) void wgrad_kernel(const WgradArgs g) {
+  constexpr int kBlk = MBW * NBW;
+  __shared__ float red[kBlk * 16][64];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, jl = lane & 31, h = lane >> 5;
+  const int64_t tiles_n = (g.N + 32 * NBW - 1) / (32 * NBW);
+  const int64_t mt = blockIdx.x / tiles_n, nt = blockIdx.x - mt * tiles_n;
+  const int64_t m0 = mt * (32 * MBW), n0 = nt * (32 * NBW);
+  const int64_t sl = blockIdx.y / g.nk;
+  const int k = int(blockIdx.y - sl * g.nk);
+  const bool rev = g.rev_routes && k >= 2;
+  const int64_t upi = (g.K + kWgradUnit - 1) / kWgradUnit, units = g.batch * upi;
+  const int64_t per = (units + g.splits - 1) / g.splits;
+  const int64_t u0 = sl * per, u1 = u0 + per < units ? u0 + per : units;
+  // rows of this lane (clamped: an out-of-range row only feeds an output that is not written)
+  const float* arow[MBW];
+  const float* brow[NBW];
+#pragma unroll
+  for (int mb = 0; mb < MBW; ++mb) {
+    const int64_t i = m0 + 32 * mb + jl;
+    arow[mb] = g.a + k * g.a_k + (i < g.M ? i : g.M - 1) * g.a_r;
   }
-  // each thread's 8 elements of a tile: unit-stride index fastest across threads
-  const bool a_kfast = g.a.s_c == 1, b_nfast = g.b.s_c == 1;
-  floatx16 acc = {};
-  for (int64_t b0 = b0_begin; b0 < b0_end; ++b0) {
-    for (int64_t k0 = 0; k0 < g.K; k0 += kTK) {
-      float va[8], vb[8];
+  const float* bk = (k & 1) ? g.b1 : g.b0;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int e = t + kThreads * q;
-        const int ia = a_kfast ? e / kTK : e % kTM, ka = a_kfast ? e % kTK : e / kTM;
-        const int64_t ri = m0 + ia, ck = k0 + ka;
-        const bool ina = ri < g.M && ck < g.K;
-        const float x = *opnd_addr(g.a, ina ? ri : 0, ina ? ck : 0, g.K, b0, b1);
-        va[q] = ina ? x : 0.0f;
-        const int kb = b_nfast ? e / kTN : e % kTK, jb = b_nfast ? e % kTN : e / kTK;
-        const int64_t rk = k0 + kb, cj = n0 + jb;
-        const bool inb = rk < g.K && cj < g.N;
-        const float y = *opnd_addr(g.b, inb ? rk : 0, inb ? cj : 0, g.N, b0, b1);
-        vb[q] = inb ? y : 0.0f;
-      }
-      __syncthreads();  // the previous chunk's MFMAs have read the tiles
+  for (int nb = 0; nb < NBW; ++nb) {
+    const int64_t j = n0 + 32 * nb + jl;
+    brow[nb] = bk + k * g.b_k + (j < g.N ? j : g.N - 1) * g.b_r;
+  }
+  // lane's 8 steps of unit q: [l0, l0 + 8), l0 = 64 (q mod upi) + 16 wave + 8 h.  Loads keep the
+  // raw words in memory order; the reversal and the zeroing of steps past K are applied when the
+  // next unit's values become the current ones, after the MFMAs.
+  typedef typename std::conditional<kVec, float4, float>::type Raw;
+  constexpr int kR = kVec ? 2 : 8;
+  Raw ra[MBW][kR], rb[NBW][kR];
+  bool rok[kR];
+  float acur[MBW][8], bcur[NBW][8];
+  auto load = [&](int64_t bi, int64_t ui) {  // unit ui of image bi
+    const int64_t l0 = ui * kWgradUnit + 16 * wave + 8 * h;
+    const int64_t aoff = bi * g.a_b, boff = bi * g.b_b;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int e = t + kThreads * q;
-        const int ia = a_kfast ? e / kTK : e % kTM, ka = a_kfast ? e % kTK : e / kTM;
-        const int kb = b_nfast ? e / kTN : e % kTK, jb = b_nfast ? e % kTN : e / kTK;
-        As[ka][ia] = va[q];
-        Bs[kb][jb] = vb[q];
-      }
-      __syncthreads();
+    for (int e = 0; e < kR; ++e) {
+      const int64_t l = l0 + (kVec ? 4 : 1) * e;
+      rok[e] = l < g.K;  // vector path: K % 4 == 0, so a granule is all in or all out
+      const int64_t lc = l < g.K ? l : 0;
+      const int64_t la = rev ? g.K - (kVec ? 4 : 1) - lc : lc;
 #pragma unroll
-      for (int s = 0; s < kTK / 2; ++s) {
-        const float a = As[2 * s + lane / 32][wm * 32 + lane % 32];
-        const float b = Bs[2 * s + lane / 32][wn * 32 + lane % 32];
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+      for (int mb = 0; mb < MBW; ++mb) ra[mb][e] = *reinterpret_cast<const Raw*>(arow[mb] + aoff + la);
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) rb[nb][e] = *reinterpret_cast<const Raw*>(brow[nb] + boff + lc);
+    }
+  };
+  auto take = [&]() {
+#pragma unroll
+    for (int e = 0; e < kR; ++e) {
+      const float m = rok[e] ? 1.0f : 0.0f;  // zeroing of B alone suffices: A is finite
+      if constexpr (kVec) {
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb) {
+          const float4 v = rev ? rev4(ra[mb][e]) : ra[mb][e];
+          acur[mb][4 * e] = v.x;
+          acur[mb][4 * e + 1] = v.y;
+          acur[mb][4 * e + 2] = v.z;
+          acur[mb][4 * e + 3] = v.w;
+        }
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+          const float4 v = rb[nb][e];
+          bcur[nb][4 * e] = v.x * m;
+          bcur[nb][4 * e + 1] = v.y * m;
+          bcur[nb][4 * e + 2] = v.z * m;
+          bcur[nb][4 * e + 3] = v.w * m;
+        }
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb) acur[mb][e] = ra[mb][e];
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) bcur[nb][e] = rb[nb][e] * m;
       }
     }
-  }
-  const int64_t cb0 = g.sum_b0 ? 0 : b0_begin;
+  };
+
+  floatx16 acc[MBW][NBW];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int64_t i = m0 + wm * 32 + (v / 4) * 8 + (lane / 32) * 4 + v % 4;
-    const int64_t j = n0 + wn * 32 + lane % 32;
-    if (i < g.M && j < g.N) {
-      float* c = const_cast<float*>(opnd_addr(g.c, i, j, g.N, cb0, b1)) + split * g.c_split;
-      *c = g.accumulate ? *c + acc[v] : acc[v];
+  for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = floatx16{};
+  const int64_t uf = u0 < units ? u0 : units - 1;
+  int64_t bi = uf / upi, ui = uf - bi * upi;  // image and unit of the next load
+  load(bi, ui);
+  take();
+  for (int64_t q = u0; q < u1; ++q) {
+    if (q + 1 < u1 && ++ui == upi) {  // the last unit reloads itself (unused)
+      ui = 0;
+      ++bi;
     }
+    load(bi, ui);
+    __builtin_amdgcn_sched_barrier(0);  // issue the loads before the MFMAs
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(acur[mb][s], bcur[nb][s], acc[mb][nb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);  // use the new words only after the MFMAs
+    take();
+  }
+
+  // the four wavefronts' tiles summed through LDS (wave 3 first, wave 0 writes the result)
+#pragma unroll
+  for (int r = 3; r >= 1; --r) {
+    if (wave == r) {
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            float& e = red[(mb * NBW + nb) * 16 + v][lane];
+            e = r == 3 ? acc[mb][nb][v] : e + acc[mb][nb][v];
+          }
+    }
+    __syncthreads();
+  }
+  if (wave == 0) {
+    float* c = g.c + (sl * g.nk + k) * g.M * g.N;
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t i = m0 + 32 * mb + 8 * (v / 4) + 4 * h + v % 4, j = n0 + 32 * nb + jl;
+          const float val = acc[mb][nb][v] + red[(mb * NBW + nb) * 16 + v][lane];
+          if (i < g.M && j < g.N) c[i * g.N + j] = val;
+        }
   }
 }
 
@@ -142,14 +343,79 @@ __global__ __launch_bounds__(256) void cast_transpose_kernel(const T* x, float* 
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
-  if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  const int64_t tm = (g.M + kTM - 1) / kTM, tn = (g.N + kTN - 1) / kTN;
-  const int64_t z = g.sum_b0 ? g.b0_splits * g.nb1 : g.nb0 * g.nb1;
-  if (tm > 65535 || z > 65535 || tn > int64_t(INT32_MAX) || z <= 0) return hipErrorInvalidValue;
-  if (g.sum_b0 && (g.b0_splits <= 0 || g.b0_splits > g.nb0)) return hipErrorInvalidValue;
-  gemm_kernel<<<dim3(uint32_t(tn), uint32_t(tm), uint32_t(z)), dim3(kThreads), 0, s>>>(g);
+namespace {
+inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+template <int MB, int TK>
+hipError_t run_proj(const ProjArgs& g, dim3 grid, bool vec, hipStream_t s) {
+  if (vec)
+    proj_kernel<MB, TK, true><<<grid, dim3(kThreads), 0, s>>>(g);
+  else
+    proj_kernel<MB, TK, false><<<grid, dim3(kThreads), 0, s>>>(g);
   return hipGetLastError();
+}
+template <int MB>
+hipError_t run_proj_tk(const ProjArgs& g, dim3 grid, bool vec, int tk, hipStream_t s) {
+  return tk == 8 ? run_proj<MB, 8>(g, grid, vec, s) : run_proj<MB, 16>(g, grid, vec, s);
+}
+template <int MBW, int NBW>
+hipError_t run_wgrad(const WgradArgs& g, dim3 grid, bool vec, hipStream_t s) {
+  if (vec)
+    wgrad_kernel<MBW, NBW, true><<<grid, dim3(kThreads), 0, s>>>(g);
+  else
+    wgrad_kernel<MBW, NBW, false><<<grid, dim3(kThreads), 0, s>>>(g);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_proj(const ProjArgs& g, hipStream_t s) {
+  if (g.M <= 0 || g.L <= 0 || g.batch <= 0) return hipSuccess;
+  if (g.K <= 0 || g.nk <= 0) return hipErrorInvalidValue;
+  // row blocks of 32 spread evenly over tiles of at most 4 blocks
+  const int64_t blocks = (g.M + 31) / 32, tiles = (blocks + 3) / 4;
+  const int mb = int((blocks + tiles - 1) / tiles);
+  // chunk of 8 when it pads the contraction less than a chunk of 16
+  const int tk = (g.K <= 8 || (g.K + 7) / 8 * 8 < (g.K + 15) / 16 * 16) ? 8 : 16;
+  ProjArgs a = g;
+  a.m_tiles = (g.M + 32 * mb - 1) / (32 * mb);
+  const int64_t gx = (g.L + kPN - 1) / kPN * a.m_tiles, gy = g.batch * g.nk;
+  if (gx > int64_t(INT32_MAX) || gy > 65535) return hipErrorInvalidValue;
+  const bool vec = g.L % 4 == 0 && g.x_b % 4 == 0 && g.x_k % 4 == 0 && g.x_r % 4 == 0 && al16(g.x0) && al16(g.x1);
+  const dim3 grid{uint32_t(gx), uint32_t(gy), 1u};
+  switch (mb) {
+    case 1: return run_proj_tk<1>(a, grid, vec, tk, s);
+    case 2: return run_proj_tk<2>(a, grid, vec, tk, s);
+    case 3: return run_proj_tk<3>(a, grid, vec, tk, s);
+    default: return run_proj_tk<4>(a, grid, vec, tk, s);
+  }
+}
+
+hipError_t launch_wgrad(const WgradArgs& g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (g.K <= 0 || g.batch <= 0 || g.nk <= 0 || g.splits <= 0) return hipErrorInvalidValue;
+  const int64_t mbn = (g.M + 31) / 32, nbn = (g.N + 31) / 32;
+  const int mbw = mbn < 3 ? int(mbn) : 3;
+  const int nmax = 6 / mbw;
+  const int nbw = nbn < nmax ? int(nbn) : nmax;
+  const int64_t tiles = ((g.M + 32 * mbw - 1) / (32 * mbw)) * ((g.N + 32 * nbw - 1) / (32 * nbw));
+  const int64_t gy = g.splits * g.nk;
+  if (tiles > int64_t(INT32_MAX) || gy > 65535) return hipErrorInvalidValue;
+  const bool vec = g.K % 4 == 0 && g.a_b % 4 == 0 && g.a_k % 4 == 0 && g.a_r % 4 == 0 && g.b_b % 4 == 0 &&
+                   g.b_k % 4 == 0 && g.b_r % 4 == 0 && al16(g.a) && al16(g.b0) && al16(g.b1);
+  const dim3 grid{uint32_t(tiles), uint32_t(gy), 1u};
+  switch (mbw * 8 + nbw) {
+    case 8 + 1: return run_wgrad<1, 1>(g, grid, vec, s);
+    case 8 + 2: return run_wgrad<1, 2>(g, grid, vec, s);
+    case 8 + 3: return run_wgrad<1, 3>(g, grid, vec, s);
+    case 8 + 4: return run_wgrad<1, 4>(g, grid, vec, s);
+    case 8 + 5: return run_wgrad<1, 5>(g, grid, vec, s);
+    case 8 + 6: return run_wgrad<1, 6>(g, grid, vec, s);
+    case 16 + 1: return run_wgrad<2, 1>(g, grid, vec, s);
+    case 16 + 2: return run_wgrad<2, 2>(g, grid, vec, s);
+    case 16 + 3: return run_wgrad<2, 3>(g, grid, vec, s);
+    case 24 + 1: return run_wgrad<3, 1>(g, grid, vec, s);
+    default: return run_wgrad<3, 2>(g, grid, vec, s);
+  }
 }
 
 hipError_t launch_sum_parts(const float* part, float* out, int64_t n, int64_t n_parts, hipStream_t s) {

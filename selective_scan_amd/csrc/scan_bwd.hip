@@ -39,8 +39,10 @@ __global__ __launch_bounds__(256) void reduce_bc_kernel(const BwdReduceArgs a) {
     sb += a.dB_part[k * per_block + i];
     sc += a.dC_part[k * per_block + i];
   }
-  Elem<T>::store(static_cast<T*>(a.dB), i, sb * kLn2);  // dB terms were formed with delta / ln 2
-  Elem<T>::store(static_cast<T*>(a.dC), i, sc);
+  const int64_t nl = int64_t(a.N) * a.L;
+  const int64_t o = a.bc_out_stride ? (i / nl) * a.bc_out_stride + i % nl : i;
+  Elem<T>::store(static_cast<T*>(a.dB), o, sb * kLn2);  // dB terms were formed with delta / ln 2
+  Elem<T>::store(static_cast<T*>(a.dC), o, sc);
 }
 
 __global__ __launch_bounds__(256) void reduce_params_kernel(const BwdReduceArgs a) {

@@ -77,8 +77,9 @@ void scan_fwd_kernel(const ScanFwdParams p) {
   }
   const bool has_z = !kSS2D && p.z != nullptr;
   const T* z_row = has_z ? static_cast<const T*>(p.z) + row * L : nullptr;
-  const T* Bg = static_cast<const T*>(p.Bm) + (b * p.G + g) * N * L;
-  const T* Cg = static_cast<const T*>(p.Cm) + (b * p.G + g) * N * L;
+  const int64_t bcs = p.bc_stride ? p.bc_stride : N * L;
+  const T* Bg = static_cast<const T*>(p.Bm) + (b * p.G + g) * bcs;
+  const T* Cg = static_cast<const T*>(p.Cm) + (b * p.G + g) * bcs;
 
   float Acoef[NSL];
 #pragma unroll

@@ -100,14 +100,12 @@ ScanLayout scan_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqle
 struct SS2DLayout {
   int64_t off_xT, off_ys, off_scan, off_merged, off_dM, off_dMT, off_xc, off_cpart, off_lnpart, total;
   // the Δ/B/C producer (dt_rank > 0): fp32 projected inputs, their gradients, weight partials
-  int64_t off_pdt, off_pB, off_pC, off_pdelta, off_pddelta, off_pddt, off_pdB, off_pdC, off_pwx, off_pwdt;
-  int64_t proj_splits;
+  // x_dbl and its gradient are (batch, 4, R + 2N, L): rows [0, R) dt, [R, R + N) B, [R + N, R + 2N) C
+  int64_t off_pxdbl, off_pdelta, off_pddelta, off_pdxdbl, off_pwx, off_pwdt;
+  int64_t proj_splits;  // slices of the weight-gradient products (partials summed afterwards)
   ScanLayout scan;    // chunk plan for the I/O type
   ScanLayout scan32;  // chunk plan of the fp32 scans of the projected path (same offsets)
 };
-
-// image slices of the weight-gradient products (each a partial summed afterwards)
-inline int64_t proj_splits(int64_t batch) { return batch < 128 ? batch : 128; }
 
 SS2DLayout ss2d_layout(int64_t batch, int64_t dim, int64_t H, int64_t W, int64_t dstate, int dtype,
                        int64_t dt_rank = 0) {
@@ -126,16 +124,12 @@ SS2DLayout ss2d_layout(int64_t batch, int64_t dim, int64_t H, int64_t W, int64_t
   l.off_lnpart = o; o += align_up(ln_part_rows(batch, L) * 2 * dim * 4);  // LayerNorm parameter partials
   l.scan32 = scan_layout(batch, 4 * dim, dstate, L, 4, SS2D_DTYPE_F32);
   if (dt_rank > 0) {
-    const int64_t R = dt_rank, N = dstate, Cp = R + 2 * N, S = proj_splits(batch);
+    const int64_t R = dt_rank, N = dstate, Cp = R + 2 * N, S = wgrad_splits(batch, L);
     l.proj_splits = S;
-    l.off_pdt = o;     o += align_up(batch * 4 * R * L * 4);
-    l.off_pB = o;      o += align_up(batch * 4 * N * L * 4);
-    l.off_pC = o;      o += align_up(batch * 4 * N * L * 4);
+    l.off_pxdbl = o;   o += align_up(batch * 4 * Cp * L * 4);
     l.off_pdelta = o;  o += align_up(batch * 4 * dim * L * 4);
     l.off_pddelta = o; o += align_up(batch * 4 * dim * L * 4);
-    l.off_pddt = o;    o += align_up(batch * 4 * R * L * 4);
-    l.off_pdB = o;     o += align_up(batch * 4 * N * L * 4);
-    l.off_pdC = o;     o += align_up(batch * 4 * N * L * 4);
+    l.off_pdxdbl = o;  o += align_up(batch * 4 * Cp * L * 4);
     l.off_pwx = o;     o += align_up(S * 4 * Cp * dim * 4);
     l.off_pwdt = o;    o += align_up(S * 4 * dim * R * 4);
   }
@@ -351,72 +345,51 @@ static const void* scan_input(const void* x, bool in_ws, void* ws, const SS2DLay
 
 static float* wsf(void* ws, int64_t off) { return reinterpret_cast<float*>(at(ws, off)); }
 
-// The Δ/B/C producer: for each route k, x_dbl = x_proj_w[k] @ xs_k split into dt, B, C rows, then
+// The Δ/B/C producer: for each route k, x_dbl = x_proj_w[k] @ xs_k (rows dt, B, C), then
 // delta = dt_proj_w[k] @ dt, all fp32 in route order in the workspace.  xs_k is the fp32 map
 // (routes 0, 2) or its transpose (routes 1, 3), read backwards for the reversed routes.
 static int ss2d_project(const ss2d_fwd_args* a, const SS2DLayout& lay, hipStream_t stream) {
   const int64_t L = a->height * a->width, D = a->dim, N = a->dstate, R = a->dt_rank, Cp = R + 2 * N;
   void* ws = a->workspace;
-  for (int k = 0; k < 4; ++k) {
-    GemmArgs g{};
-    g.a.p[0] = g.a.p[1] = g.a.p[2] = a->x_proj_w + k * Cp * D;
-    for (int q = 0; q < 3; ++q) g.a.s_r[q] = D;
-    g.a.s_c = 1;
-    g.a.split1 = g.a.split2 = Cp;
-    g.b.p[0] = g.b.p[1] = g.b.p[2] = wsf(ws, (k & 1) ? lay.off_xT : lay.off_xc);
-    for (int q = 0; q < 3; ++q) {
-      g.b.s_r[q] = L;
-      g.b.s_b0[q] = D * L;
-    }
-    g.b.s_c = 1;
-    g.b.split1 = g.b.split2 = D;
-    g.b.rev_c = k >= 2;
-    g.c.p[0] = wsf(ws, lay.off_pdt) + k * R * L;
-    g.c.p[1] = wsf(ws, lay.off_pB) + k * N * L;
-    g.c.p[2] = wsf(ws, lay.off_pC) + k * N * L;
-    for (int q = 0; q < 3; ++q) g.c.s_r[q] = L;
-    g.c.s_b0[0] = 4 * R * L;
-    g.c.s_b0[1] = g.c.s_b0[2] = 4 * N * L;
-    g.c.s_c = 1;
-    g.c.split1 = R;
-    g.c.split2 = R + N;
-    g.M = Cp;
-    g.N = L;
-    g.K = D;
-    g.nb0 = a->batch;
-    g.nb1 = 1;
-    if (launch_gemm(g, stream) != hipSuccess) return SS2D_ERR_HIP;
-  }
-  GemmArgs g{};
-  g.a.p[0] = g.a.p[1] = g.a.p[2] = a->dt_proj_w;
-  for (int q = 0; q < 3; ++q) {
-    g.a.s_r[q] = R;
-    g.a.s_b1[q] = D * R;
-  }
-  g.a.s_c = 1;
-  g.a.split1 = g.a.split2 = D;
-  g.b.p[0] = g.b.p[1] = g.b.p[2] = wsf(ws, lay.off_pdt);
-  for (int q = 0; q < 3; ++q) {
-    g.b.s_r[q] = L;
-    g.b.s_b0[q] = 4 * R * L;
-    g.b.s_b1[q] = R * L;
-  }
-  g.b.s_c = 1;
-  g.b.split1 = g.b.split2 = R;
-  g.c.p[0] = g.c.p[1] = g.c.p[2] = wsf(ws, lay.off_pdelta);
-  for (int q = 0; q < 3; ++q) {
-    g.c.s_r[q] = L;
-    g.c.s_b0[q] = 4 * D * L;
-    g.c.s_b1[q] = D * L;
-  }
-  g.c.s_c = 1;
-  g.c.split1 = g.c.split2 = D;
+  ProjArgs f{};  // x_dbl (Cp x L) = x_proj_w[k] (Cp x D) xs_k (D x L)
+  f.w = a->x_proj_w;
+  f.w_k = Cp * D;
+  f.w_i = D;
+  f.w_kk = 1;
+  f.x0 = wsf(ws, lay.off_xc);
+  f.x1 = wsf(ws, lay.off_xT);
+  f.x_b = D * L;
+  f.x_r = L;
+  f.c = wsf(ws, lay.off_pxdbl);
+  f.c_b = 4 * Cp * L;
+  f.c_k = Cp * L;
+  f.c_r = L;
+  f.M = Cp;
+  f.K = D;
+  f.L = L;
+  f.batch = a->batch;
+  f.nk = 4;
+  f.rev_routes = 1;
+  if (launch_proj(f, stream) != hipSuccess) return SS2D_ERR_HIP;
+  ProjArgs g{};  // delta (D x L) = dt_proj_w[k] (D x R) dt (R x L)
+  g.w = a->dt_proj_w;
+  g.w_k = D * R;
+  g.w_i = R;
+  g.w_kk = 1;
+  g.x0 = g.x1 = wsf(ws, lay.off_pxdbl);
+  g.x_b = 4 * Cp * L;
+  g.x_k = Cp * L;
+  g.x_r = L;
+  g.c = wsf(ws, lay.off_pdelta);
+  g.c_b = 4 * D * L;
+  g.c_k = D * L;
+  g.c_r = L;
   g.M = D;
-  g.N = L;
   g.K = R;
-  g.nb0 = a->batch;
-  g.nb1 = 4;
-  return status_from(launch_gemm(g, stream));
+  g.L = L;
+  g.batch = a->batch;
+  g.nk = 4;
+  return status_from(launch_proj(g, stream));
 }
 
 // Stage 0: the column-major copy of the scanned map (and, with the input front, the map itself).
@@ -459,8 +432,9 @@ static int ss2d_scan_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, bool k
   p.u_f32 = a->conv_w != nullptr && a->dtype != 0 && !proj;
   p.delta = proj ? wsf(a->workspace, lay.off_pdelta) : a->delta;
   p.A = a->A;
-  p.Bm = proj ? wsf(a->workspace, lay.off_pB) : a->Bm;
-  p.Cm = proj ? wsf(a->workspace, lay.off_pC) : a->Cm;
+  p.Bm = proj ? wsf(a->workspace, lay.off_pxdbl) + a->dt_rank * L : a->Bm;
+  p.Cm = proj ? wsf(a->workspace, lay.off_pxdbl) + (a->dt_rank + a->dstate) * L : a->Cm;
+  p.bc_stride = proj ? (a->dt_rank + 2 * a->dstate) * L : 0;
   p.delta_bias = a->delta_bias;
   p.out = at(a->workspace, lay.off_ys);
   p.batch = a->batch;
@@ -676,6 +650,7 @@ static int run_scan_bwd(ScanBwdParams bp, const ScanLayout& lay, void* ws, void*
   r.n_chunks = bp.n_chunks;
   r.N = bp.N;
   r.dtype = bp.dtype;
+  r.bc_out_stride = bp.bc_stride;
   return status_from(launch_bwd_reduce(r, stream));
 }
 
@@ -761,93 +736,98 @@ int selective_scan_bwd(const ss_bwd_args* a, hipStream_t stream) {
                       a->delta_bias ? a->ddelta_bias : nullptr, stream);
 }
 
-// The Δ/B/C producer's gradient, given the scans' fp32 gradients of delta, B and C (route order):
-//   d dt = dt_proj_w[k]^T ddelta;  du_k += x_proj_w[k]^T (d dt; dB; dC)  (added to the routes' du
-//   before the merge);  dx_proj_w[k] = sum_b (d dt; dB; dC) xs_k^T;  ddt_proj_w[k] = sum_b ddelta dt^T
-// (the two weight products summed over images in proj_splits slices, then over the slices).
+// The Δ/B/C producer's gradient, given the scans' fp32 gradients of delta, B and C (route order,
+// dB and dC already in rows [R, R + 2N) of the x_dbl gradient):
+//   d dt = dt_proj_w[k]^T ddelta (rows [0, R));  du_k += x_proj_w[k]^T (d dt; dB; dC) (added to the
+//   routes' du before the merge);  dx_proj_w[k] = sum_b (d dt; dB; dC) xs_k^T;
+//   ddt_proj_w[k] = sum_b ddelta dt^T  (the weight products as partials of proj_splits slices,
+//   then summed over the slices).
 static int ss2d_project_bwd(const ss2d_bwd_args* a, const SS2DLayout& lay, hipStream_t stream) {
   const int64_t L = a->height * a->width, D = a->dim, N = a->dstate, R = a->dt_rank, Cp = R + 2 * N;
   const int64_t S = lay.proj_splits;
   void* ws = a->workspace;
-  auto uniform = [](GemmOpnd& o, const float* p, int64_t s_r, int64_t s_c, int64_t s_b0, int64_t s_b1, int64_t rows) {
-    o.p[0] = o.p[1] = o.p[2] = p;
-    for (int q = 0; q < 3; ++q) {
-      o.s_r[q] = s_r;
-      o.s_b0[q] = s_b0;
-      o.s_b1[q] = s_b1;
-    }
-    o.s_c = s_c;
-    o.split1 = o.split2 = rows;
-  };
-  // the rows (d dt; dB; dC) of route k's projected-sequence gradient, columns = steps
-  auto dxdbl = [&](GemmOpnd& o, int64_t k_off_rows, bool with_b1) {
-    o.p[0] = wsf(ws, lay.off_pddt) + k_off_rows * R * L;
-    o.p[1] = wsf(ws, lay.off_pdB) + k_off_rows * N * L;
-    o.p[2] = wsf(ws, lay.off_pdC) + k_off_rows * N * L;
-    for (int q = 0; q < 3; ++q) o.s_r[q] = L;
-    o.s_b0[0] = 4 * R * L;
-    o.s_b0[1] = o.s_b0[2] = 4 * N * L;
-    o.s_b1[0] = with_b1 ? R * L : 0;
-    o.s_b1[1] = o.s_b1[2] = with_b1 ? N * L : 0;
-    o.s_c = 1;
-    o.split1 = R;
-    o.split2 = R + N;
-  };
-  {  // d dt (R x L) = dt_proj_w[k]^T (R x D) ddelta (D x L), every (b, k)
-    GemmArgs g{};
-    uniform(g.a, a->dt_proj_w, 1, R, 0, D * R, R);
-    uniform(g.b, wsf(ws, lay.off_pddelta), L, 1, 4 * D * L, D * L, D);
-    uniform(g.c, wsf(ws, lay.off_pddt), L, 1, 4 * R * L, R * L, R);
+  {  // d dt (R x L) = dt_proj_w[k]^T (R x D) ddelta (D x L)
+    ProjArgs g{};
+    g.w = a->dt_proj_w;
+    g.w_k = D * R;
+    g.w_i = 1;
+    g.w_kk = R;
+    g.x0 = g.x1 = wsf(ws, lay.off_pddelta);
+    g.x_b = 4 * D * L;
+    g.x_k = D * L;
+    g.x_r = L;
+    g.c = wsf(ws, lay.off_pdxdbl);
+    g.c_b = 4 * Cp * L;
+    g.c_k = Cp * L;
+    g.c_r = L;
     g.M = R;
-    g.N = L;
     g.K = D;
-    g.nb0 = a->batch;
-    g.nb1 = 4;
-    if (launch_gemm(g, stream) != hipSuccess) return SS2D_ERR_HIP;
+    g.L = L;
+    g.batch = a->batch;
+    g.nk = 4;
+    if (launch_proj(g, stream) != hipSuccess) return SS2D_ERR_HIP;
   }
-  {  // du_k (D x L) += x_proj_w[k]^T (D x Cp) (d dt; dB; dC) (Cp x L), into the routes' du
-    GemmArgs g{};
-    uniform(g.a, a->x_proj_w, 1, D, 0, Cp * D, D);
-    dxdbl(g.b, 0, true);
-    uniform(g.c, wsf(ws, lay.off_ys), L, 1, 4 * D * L, D * L, D);
+  {  // du_k (D x L) += x_proj_w[k]^T (D x Cp) dx_dbl (Cp x L), into the routes' du
+    ProjArgs g{};
+    g.w = a->x_proj_w;
+    g.w_k = Cp * D;
+    g.w_i = 1;
+    g.w_kk = D;
+    g.x0 = g.x1 = wsf(ws, lay.off_pdxdbl);
+    g.x_b = 4 * Cp * L;
+    g.x_k = Cp * L;
+    g.x_r = L;
+    g.c = wsf(ws, lay.off_ys);
+    g.c_b = 4 * D * L;
+    g.c_k = D * L;
+    g.c_r = L;
     g.M = D;
-    g.N = L;
     g.K = Cp;
-    g.nb0 = a->batch;
-    g.nb1 = 4;
+    g.L = L;
+    g.batch = a->batch;
+    g.nk = 4;
     g.accumulate = 1;
-    if (launch_gemm(g, stream) != hipSuccess) return SS2D_ERR_HIP;
+    if (launch_proj(g, stream) != hipSuccess) return SS2D_ERR_HIP;
   }
-  for (int k = 0; k < 4; ++k) {  // dx_proj_w[k] (Cp x D) = sum_{b, l} dx_dbl[c, l] xs_k[d, l]
-    GemmArgs g{};
-    dxdbl(g.a, k, false);
-    g.a.rev_c = k >= 2;  // reversed routes: step l of xs_k is pixel L-1-l of the source map
-    uniform(g.b, wsf(ws, (k & 1) ? lay.off_xT : lay.off_xc), 1, L, D * L, 0, L);
-    uniform(g.c, wsf(ws, lay.off_pwx) + k * Cp * D, D, 1, 0, 0, Cp);
+  {  // dx_proj_w[k] (Cp x D) = sum_{b, l} dx_dbl[c, l] xs_k[d, l]; the reversed routes pair step l
+     // of dx_dbl with pixel L-1-l of the source map
+    WgradArgs g{};
+    g.a = wsf(ws, lay.off_pdxdbl);
+    g.a_b = 4 * Cp * L;
+    g.a_k = Cp * L;
+    g.a_r = L;
+    g.b0 = wsf(ws, lay.off_xc);
+    g.b1 = wsf(ws, lay.off_xT);
+    g.b_b = D * L;
+    g.b_r = L;
+    g.c = wsf(ws, lay.off_pwx);
     g.M = Cp;
     g.N = D;
     g.K = L;
-    g.nb0 = a->batch;
-    g.nb1 = 1;
-    g.sum_b0 = 1;
-    g.b0_splits = S;
-    g.c_split = 4 * Cp * D;
-    if (launch_gemm(g, stream) != hipSuccess) return SS2D_ERR_HIP;
+    g.batch = a->batch;
+    g.nk = 4;
+    g.splits = int(S);
+    g.rev_routes = 1;
+    if (launch_wgrad(g, stream) != hipSuccess) return SS2D_ERR_HIP;
   }
   {  // ddt_proj_w[k] (D x R) = sum_{b, l} ddelta[d, l] dt[r, l]
-    GemmArgs g{};
-    uniform(g.a, wsf(ws, lay.off_pddelta), L, 1, 4 * D * L, D * L, D);
-    uniform(g.b, wsf(ws, lay.off_pdt), 1, L, 4 * R * L, R * L, L);
-    uniform(g.c, wsf(ws, lay.off_pwdt), R, 1, 0, D * R, D);
+    WgradArgs g{};
+    g.a = wsf(ws, lay.off_pddelta);
+    g.a_b = 4 * D * L;
+    g.a_k = D * L;
+    g.a_r = L;
+    g.b0 = g.b1 = wsf(ws, lay.off_pxdbl);
+    g.b_b = 4 * Cp * L;
+    g.b_k = Cp * L;
+    g.b_r = L;
+    g.c = wsf(ws, lay.off_pwdt);
     g.M = D;
     g.N = R;
     g.K = L;
-    g.nb0 = a->batch;
-    g.nb1 = 4;
-    g.sum_b0 = 1;
-    g.b0_splits = S;
-    g.c_split = 4 * D * R;
-    if (launch_gemm(g, stream) != hipSuccess) return SS2D_ERR_HIP;
+    g.batch = a->batch;
+    g.nk = 4;
+    g.splits = int(S);
+    if (launch_wgrad(g, stream) != hipSuccess) return SS2D_ERR_HIP;
   }
   if (launch_sum_parts(wsf(ws, lay.off_pwx), a->dx_proj_w, 4 * Cp * D, S, stream) != hipSuccess ||
       launch_sum_parts(wsf(ws, lay.off_pwdt), a->ddt_proj_w, 4 * D * R, S, stream) != hipSuccess)
@@ -1007,8 +987,9 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
   bp.u_f32 = a->conv_w != nullptr && a->dtype != 0 && !proj;
   bp.delta = proj ? wsf(ws, lay.off_pdelta) : a->delta;
   bp.A = a->A;
-  bp.Bm = proj ? wsf(ws, lay.off_pB) : a->Bm;
-  bp.Cm = proj ? wsf(ws, lay.off_pC) : a->Cm;
+  bp.Bm = proj ? wsf(ws, lay.off_pxdbl) + a->dt_rank * L : a->Bm;
+  bp.Cm = proj ? wsf(ws, lay.off_pxdbl) + (a->dt_rank + a->dstate) * L : a->Cm;
+  bp.bc_stride = proj ? (a->dt_rank + 2 * a->dstate) * L : 0;
   bp.Dskip = a->Dskip;
   bp.delta_bias = a->delta_bias;
   bp.dout = at(a->workspace, lay.off_dM);
@@ -1026,8 +1007,8 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
   bp.ss2d = 1;
   bp.dtype = proj ? SS2D_DTYPE_F32 : a->dtype;
   bp.vec = (L % 4 == 0) && vec_aligned(bp.dtype, {u, bp.delta, bp.Bm, bp.Cm, bp.ddelta});
-  st = run_scan_bwd(bp, lay.scan, at(ws, lay.off_scan), proj ? wsf(ws, lay.off_pdB) : a->dBm,
-                    proj ? wsf(ws, lay.off_pdC) : a->dCm, a->dA, a->Dskip ? a->dDskip : nullptr,
+  st = run_scan_bwd(bp, lay.scan, at(ws, lay.off_scan), proj ? wsf(ws, lay.off_pdxdbl) + a->dt_rank * L : a->dBm,
+                    proj ? wsf(ws, lay.off_pdxdbl) + (a->dt_rank + a->dstate) * L : a->dCm, a->dA, a->Dskip ? a->dDskip : nullptr,
                     a->delta_bias ? a->ddelta_bias : nullptr, stream);
   if (st != SS2D_OK) return st;
   if (proj) {
