@@ -263,6 +263,12 @@ struct ScanFwdParams {
   int out_f32;         // generic rows: out is fp32 instead of the I/O type
   int u_f32;           // ss2d rows, bf16 I/O: u and uT are fp32 (the input front's output)
   int64_t bc_stride;   // elements between the (b, g) blocks of B and C (0: N * L, dense)
+  // ss2d rows, fp32 I/O: raw delta formed in the kernel as dt_w[g, d, :] . dt[b, g, :, t] instead
+  // of being read (dt: (b, g) blocks bc_stride apart, rows L apart; dt_w: (G, per_group, dt_rank);
+  // 1 <= dt_rank <= 16); delta is then unused
+  const float* dt;
+  const float* dt_w;
+  int dt_rank;
 };
 hipError_t launch_scan_fwd(const ScanFwdParams& p, hipStream_t s);
 // Turns the chunk-local end states (pass 1) into the true chunk-start states.
@@ -321,6 +327,9 @@ struct ScanBwdParams {
   int dout_f32;            // generic rows: dout is fp32 instead of the I/O type
   int u_f32;               // ss2d rows, bf16 I/O: u and uT are fp32 (the input front's output)
   int64_t bc_stride;       // elements between the (b, g) blocks of B and C (0: N * L, dense)
+  const float* dt;         // as in ScanFwdParams: raw delta from dt_w . dt (delta unused)
+  const float* dt_w;
+  int dt_rank;
 };
 hipError_t launch_scan_bwd(const ScanBwdParams& p, hipStream_t s);
 hipError_t launch_lambda_combine(const ScanBwdParams& p, hipStream_t s);

@@ -180,7 +180,9 @@ __device__ __forceinline__ bool reduce_writer(int lane) {
 // kMode: 0 = generic rows, dout in the I/O type; 1 = SS2D routes (u from the map and its
 // transpose, fp32 dout planes); 2 = generic rows with an fp32 dout.
 // TU: element type of u (T, or fp32 for an SS2D input computed in fp32 by the input front).
-template <typename T, int NS, int kSplit, int kMode, bool kVec, int kPass, typename TU>
+// kDtR: 0, or the padded rank (8, 16) of the dt_proj product that forms the raw delta in the
+//       kernel (fp32 SS2D rows; dt rows staged per tile in LDS beside B and C).
+template <typename T, int NS, int kSplit, int kMode, bool kVec, int kPass, typename TU, int kDtR = 0>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kPass == 0 && NS >= 16 ? 2 : 1)))
 void scan_bwd_kernel(const ScanBwdParams p) {
   constexpr bool kSS2D = kMode == 1;
@@ -195,6 +197,7 @@ void scan_bwd_kernel(const ScanBwdParams p) {
   constexpr int kInner = (64 / NSL < kSub) ? 64 / NSL : kSub;       // steps whose states are held at once
   __shared__ __align__(16) float sB[kTile * S];
   __shared__ __align__(16) float sC[kTile * S];
+  __shared__ __align__(16) float sDt[kDtR > 0 ? kTile * kDtR : 4];
 
   const int lane = threadIdx.x;
   const int part = lane % kSplit;
@@ -215,7 +218,7 @@ void scan_bwd_kernel(const ScanBwdParams p) {
   const int N = p.N;
   const int nvalid = (N - n0 < 0) ? 0 : ((N - n0 > NSL) ? NSL : N - n0);
 
-  const T* delta_row = static_cast<const T*>(p.delta) + row * L;
+  const T* delta_row = kDtR > 0 ? nullptr : static_cast<const T*>(p.delta) + row * L;
   const TU* u_row;
   const DT* dout_row;
   bool rev = false;
@@ -233,6 +236,9 @@ void scan_bwd_kernel(const ScanBwdParams p) {
   const int64_t bcs = p.bc_stride ? p.bc_stride : N * L;
   const T* Bg = static_cast<const T*>(p.Bm) + (b * p.G + g) * bcs;
   const T* Cg = static_cast<const T*>(p.Cm) + (b * p.G + g) * bcs;
+  const float* dtg = kDtR > 0 ? p.dt + (b * p.G + g) * bcs : nullptr;
+  float wdt[kDtR > 0 ? kDtR : 1];
+  if constexpr (kDtR > 0) load_dt_w<kDtR>(wdt, p.dt_w + d * p.dt_rank, p.dt_rank);
 
   float Acoef[NSL];
 #pragma unroll
@@ -420,9 +426,26 @@ void scan_bwd_kernel(const ScanBwdParams p) {
   auto stage_tile = [&](int64_t t0) {
     BCStage<T, NS, kVec> bc;
     bc.load(Bg, Cg, N, L, t0, t_end, lane);
+    DtStage<(kDtR > 0 ? kDtR : 8), kVec> dts;
+    if constexpr (kDtR > 0) dts.load(dtg, p.dt_rank, L, t0, t_end, lane);
     __syncthreads();  // the previous tile's LDS reads are complete
     bc.template store<S>(sB, sC, lane);
+    if constexpr (kDtR > 0) dts.store(sDt, lane);
     __syncthreads();
+  };
+  // raw delta of the kSub steps of sub-interval q of the staged tile, formed from the dt rows;
+  // with two lanes per channel a lane needs only the steps of its parity (both slots of a pair
+  // get that value)
+  auto fused_delta = [&](float* dv, int q) {
+    if constexpr (kDtR > 0) {
+      if (kSplit == 2) {
+#pragma unroll
+        for (int i = 0; i < kSub; i += 2) dv[i] = dv[i + 1] = dt_dot<kDtR>(sDt, wdt, q * kSub + i + part);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kSub; ++i) dv[i] = dt_dot<kDtR>(sDt, wdt, q * kSub + i);
+      }
+    }
   };
   constexpr int kSegsPerTile = kTile / kSub;
   if constexpr (kSplit == 1) {
@@ -434,7 +457,7 @@ void scan_bwd_kernel(const ScanBwdParams p) {
     RowTile<DT, kSub> ng;
     float nh0[NSL];
     auto prefetch_seg = [&](int64_t s0) {
-      load_row<T, kVec, kSub>(nd, delta_row, s0, t_end, L, false);
+      if constexpr (kDtR == 0) load_row<T, kVec, kSub>(nd, delta_row, s0, t_end, L, false);
       // reversed rows stay in memory order here (reversed when used), and no load sits behind a
       // branch: either would make this prefetch wait for its own loads
       load_row<TU, kVec, kSub, true>(nu, u_row, s0, t_end, L, rev);
@@ -469,11 +492,12 @@ void scan_bwd_kernel(const ScanBwdParams p) {
       float dv[kSub], uv[kSub], gv[kSub], zv[kSub];
 #pragma unroll
       for (int i = 0; i < kSub; ++i) {
-        dv[i] = cd.get(i);
+        dv[i] = kDtR > 0 ? 0.0f : cd.get(i);
         uv[i] = cu.get(i);
         gv[i] = cg.get(i);
         zv[i] = has_z ? cz.get(i) : 0.0f;
       }
+      fused_delta(dv, q);
       seg_body(s0, q, dv, uv, gv, zv, [&](int n) { return h0[n]; });
     }
   } else {
@@ -488,7 +512,10 @@ void scan_bwd_kernel(const ScanBwdParams p) {
         const int64_t s0 = t0 + int64_t(q) * kSub;
         if (s0 >= t_end) continue;
         float dv[kSub], uv[kSub], gv[kSub], zv[kSub];
-        load_seg<T, kVec, kSub>(dv, delta_row, s0, t_end, L, false);
+        if constexpr (kDtR > 0)
+          fused_delta(dv, q);
+        else
+          load_seg<T, kVec, kSub>(dv, delta_row, s0, t_end, L, false);
         load_seg<TU, kVec, kSub>(uv, u_row, s0, t_end, L, rev);
         load_seg<DT, kVec, kSub>(gv, dout_row, s0, t_end, L, rev);
         if (has_z) load_seg<T, kVec, kSub>(zv, z_row, s0, t_end, L, false);
@@ -521,12 +548,32 @@ void scan_bwd_kernel(const ScanBwdParams p) {
   }
 }
 
+template <typename T, int NS, int kSplit, int kMode, bool kVec, typename TU, int kDtR>
+void launch_dt(const ScanBwdParams& p, dim3 grid, hipStream_t s) {
+  if (p.pass == 1)
+    scan_bwd_kernel<T, NS, kSplit, kMode, kVec, 1, TU, kDtR><<<grid, dim3(kWave), 0, s>>>(p);
+  else
+    scan_bwd_kernel<T, NS, kSplit, kMode, kVec, 0, TU, kDtR><<<grid, dim3(kWave), 0, s>>>(p);
+}
+
 template <typename T, int NS, int kSplit, int kMode, bool kVec, typename TU>
 hipError_t launch_t(ScanBwdParams p, hipStream_t s) {
   p.dblocks = (p.per_group + kWave / kSplit - 1) / (kWave / kSplit);
   const int64_t blocks = p.batch * p.G * p.dblocks * p.n_chunks;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if constexpr (kMode == 1 && std::is_same_v<T, float> && std::is_same_v<TU, float>) {
+    if (p.dt_w) {
+      if (p.dt_rank < 1 || p.dt_rank > 16 || p.dt == nullptr) return hipErrorInvalidValue;
+      const dim3 grid{uint32_t(blocks)};
+      if (p.dt_rank <= 8)
+        launch_dt<T, NS, kSplit, kMode, kVec, TU, 8>(p, grid, s);
+      else
+        launch_dt<T, NS, kSplit, kMode, kVec, TU, 16>(p, grid, s);
+      return hipGetLastError();
+    }
+  }
+  if (p.dt_w) return hipErrorInvalidValue;
   if (p.pass == 1)
     scan_bwd_kernel<T, NS, kSplit, kMode, kVec, 1, TU><<<dim3(uint32_t(blocks)), dim3(kWave), 0, s>>>(p);
   else

@@ -258,6 +258,87 @@ struct BCStage {
   }
 };
 
+// The low-rank projection rows dt (R <= kR rows, fp32, shared by the channels of a group) of one
+// 32-step tile, staged in LDS as [step][kR] (rows past R are zero) so that a channel forms its
+// raw delta for a step as the dot product of its kR dt_proj weights with the step's kR values.
+// As in BCStage, the loads are unconditional (clamped addresses) and keep the raw words; values
+// outside the rows or the range are zeroed when stored (a product with a 0/1 mask: a select of
+// a loaded word would be turned into a branch around the load).
+template <int kR, bool kVec>
+struct DtStage {
+  static constexpr int kVecs = kR * kTile / 4 / kWave;  // 4-step vectors per lane (kR = 8 or 16)
+  static constexpr int kElems = kR * kTile / kWave;     // scalars per lane
+  float4 rv[kVec ? kVecs : 1];
+  float re[kVec ? 1 : kElems];
+  bool ok[kVec ? kVecs : kElems];
+
+  // dt: the group's rows, row r at dt + r * L; steps [t0, t0 + kTile) clipped at t_end
+  __device__ __forceinline__ void load(const float* dt, int R, int64_t L, int64_t t0, int64_t t_end, int lane) {
+    if (kVec) {  // L % 4 == 0 and t0, t_end are multiples of 4
+#pragma unroll
+      for (int k = 0; k < kVecs; ++k) {
+        const int j = lane + k * kWave, r = j / (kTile / 4), q = j % (kTile / 4);
+        const int64_t t = t0 + 4 * q;
+        ok[k] = r < R && t < t_end;
+        rv[k] = *reinterpret_cast<const float4*>(dt + int64_t(r < R ? r : R - 1) * L + (t < t_end ? t : t0));
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kElems; ++k) {
+        const int e = lane + k * kWave, r = e / kTile, i = e % kTile;
+        const int64_t t = t0 + i;
+        ok[k] = r < R && t < t_end;
+        re[k] = dt[int64_t(r < R ? r : R - 1) * L + (t < t_end ? t : t0)];
+      }
+    }
+  }
+  __device__ __forceinline__ void store(float* sDt, int lane) const {
+    if (kVec) {
+#pragma unroll
+      for (int k = 0; k < kVecs; ++k) {
+        const int j = lane + k * kWave, r = j / (kTile / 4), q = j % (kTile / 4);
+        const float m = ok[k] ? 1.0f : 0.0f;
+        sDt[(4 * q) * kR + r] = rv[k].x * m;
+        sDt[(4 * q + 1) * kR + r] = rv[k].y * m;
+        sDt[(4 * q + 2) * kR + r] = rv[k].z * m;
+        sDt[(4 * q + 3) * kR + r] = rv[k].w * m;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kElems; ++k) {
+        const int e = lane + k * kWave, r = e / kTile, i = e % kTile;
+        sDt[i * kR + r] = re[k] * (ok[k] ? 1.0f : 0.0f);
+      }
+    }
+  }
+};
+
+// raw delta of one step: <w, dt(step)> over the kR staged rows (w past R is zero)
+template <int kR>
+__device__ __forceinline__ float dt_dot(const float* sDt, const float* w, int step) {
+  const float4* v = reinterpret_cast<const float4*>(sDt + step * kR);
+  float acc = 0.0f;
+#pragma unroll
+  for (int m = 0; m < kR / 4; ++m) {
+    const float4 x = v[m];
+    acc = fmaf(w[4 * m], x.x, acc);
+    acc = fmaf(w[4 * m + 1], x.y, acc);
+    acc = fmaf(w[4 * m + 2], x.z, acc);
+    acc = fmaf(w[4 * m + 3], x.w, acc);
+  }
+  return acc;
+}
+
+// a channel's dt_proj row (kR weights, zero past R)
+template <int kR>
+__device__ __forceinline__ void load_dt_w(float* w, const float* row, int R) {
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const float v = row[r < R ? r : 0];
+    w[r] = r < R ? v : 0.0f;
+  }
+}
+
 template <typename O, bool kVec>
 __device__ __forceinline__ void store_out(O* row, const float* y, int64_t t0, int64_t t_end) {
   if (kVec) {

@@ -34,7 +34,10 @@ using namespace scan_detail;
 // kSplit: lanes per channel (1 or 2); NSL = NS / kSplit states per lane.
 // kSoftplus: delta passes through softplus (else it is used as given).
 // TU: element type of u (T, or fp32 for an SS2D input computed in fp32 by the input front).
-template <typename T, int NS, int kSplit, bool kSS2D, bool kVec, int kPassArg, bool kSoftplus, typename TU>
+// kDtR: 0, or the padded rank (8, 16) of the dt_proj product that forms the raw delta in the
+//       kernel (fp32 SS2D rows): the group's dt rows are staged per tile in LDS beside B and C.
+template <typename T, int NS, int kSplit, bool kSS2D, bool kVec, int kPassArg, bool kSoftplus, typename TU,
+          int kDtR = 0>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(
     (kSS2D && kVec && sizeof(T) == 2 && sizeof(TU) == 2) ? fwd_waves_per_simd(NS, true) : 1)))
 void scan_fwd_kernel(const ScanFwdParams p) {
@@ -46,6 +49,7 @@ void scan_fwd_kernel(const ScanFwdParams p) {
   constexpr int kSub = ckpt_steps(NS);       // the state is checkpointed before every kSub-th step
   __shared__ __align__(16) float sB[kTile * S];
   __shared__ __align__(16) float sC[kTile * S];
+  __shared__ __align__(16) float sDt[kDtR > 0 ? kTile * kDtR : 4];
 
   const int lane = threadIdx.x;
   const int part = lane % kSplit;            // which half of the states this lane holds
@@ -65,7 +69,7 @@ void scan_fwd_kernel(const ScanFwdParams p) {
   const int64_t L = p.L;
   const int N = p.N;
 
-  const T* delta_row = static_cast<const T*>(p.delta) + row * L;
+  const T* delta_row = kDtR > 0 ? nullptr : static_cast<const T*>(p.delta) + row * L;
   const TU* u_row;
   bool rev = false;
   if (kSS2D) {
@@ -80,6 +84,9 @@ void scan_fwd_kernel(const ScanFwdParams p) {
   const int64_t bcs = p.bc_stride ? p.bc_stride : N * L;
   const T* Bg = static_cast<const T*>(p.Bm) + (b * p.G + g) * bcs;
   const T* Cg = static_cast<const T*>(p.Cm) + (b * p.G + g) * bcs;
+  const float* dtg = kDtR > 0 ? p.dt + (b * p.G + g) * bcs : nullptr;
+  float wdt[kDtR > 0 ? kDtR : 1];
+  if constexpr (kDtR > 0) load_dt_w<kDtR>(wdt, p.dt_w + d * p.dt_rank, p.dt_rank);
 
   float Acoef[NSL];
 #pragma unroll
@@ -112,9 +119,13 @@ void scan_fwd_kernel(const ScanFwdParams p) {
   RowTile<T> rd[2], rz[2];
   RowTile<TU> ru[2];
   BCStage<T, NS, kVec> nbc;
+  DtStage<(kDtR > 0 ? kDtR : 8), kVec> ndt;
   auto prefetch = [&](auto set, int64_t t) {
     constexpr int k = decltype(set)::value;
-    load_row<T, kVec>(rd[k], delta_row, t, t_end, L, false, dpad);
+    if constexpr (kDtR > 0)
+      ndt.load(dtg, p.dt_rank, L, t, t_end, lane);
+    else
+      load_row<T, kVec>(rd[k], delta_row, t, t_end, L, false, dpad);
     load_row<TU, kVec, kTile, true>(ru[k], u_row, t, t_end, L, rev);  // reversed when used
     if (has_z) load_row<T, kVec>(rz[k], z_row, t, t_end, L, false);
     nbc.load(Bg, Cg, N, L, t, t_end, lane);
@@ -128,6 +139,7 @@ void scan_fwd_kernel(const ScanFwdParams p) {
     const RowTile<T>& cz = rz[k_set];
     __syncthreads();  // the previous tile's LDS reads are complete
     nbc.template store<S>(sB, sC, lane);
+    if constexpr (kDtR > 0) ndt.store(sDt, lane);
     __syncthreads();
     const int64_t t1 = t0 + kTile;
     if (t1 < t_end) prefetch(std::integral_constant<int, 1 - k_set>{}, t1);
@@ -167,6 +179,16 @@ void scan_fwd_kernel(const ScanFwdParams p) {
 #pragma unroll
     for (int g4 = 0; g4 < kTile / 4; ++g4) {
       float lam[4], du[4], y[4];
+      // raw delta of step i of the tile: loaded, or formed from the staged dt rows (-inf past
+      // the end of the range, as the padded loads give)
+      auto raw_delta = [&](const RowTile<T>& rt, int i, int lane_part) {
+        if constexpr (kDtR > 0) {
+          const int st = i + lane_part;
+          return st < nt ? dt_dot<kDtR>(sDt, wdt, st) : -__builtin_huge_valf();
+        } else {
+          return kSplit == 2 ? rt.get_pair(i, lane_part) : rt.get(i);
+        }
+      };
       // Lam of step i (0 past the end of the range)
       auto step_lam = [&](float d, int i) {
         const float w = fmaf(d, kLog2e, bias_l2);
@@ -180,13 +202,13 @@ void scan_fwd_kernel(const ScanFwdParams p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int i = 4 * g4 + 2 * j;
-          const float x = step_lam(cd.get_pair(i, part), i + part);
+          const float x = step_lam(raw_delta(cd, i, part), i + part);
           lam[2 * j] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xA0, 0xF, 0xF, false));
           lam[2 * j + 1] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xF5, 0xF, 0xF, false));
         }
       } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) lam[k] = step_lam(cd.get(4 * g4 + k), 4 * g4 + k);
+        for (int k = 0; k < 4; ++k) lam[k] = step_lam(raw_delta(cd, 4 * g4 + k, 0), 4 * g4 + k);
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) du[k] = lam[k] * cu.get(4 * g4 + k);
@@ -260,6 +282,25 @@ void scan_fwd_kernel(const ScanFwdParams p) {
   }
 }
 
+template <typename T, int NS, int kSplit, bool kSS2D, bool kVec, typename TU, int kDtR>
+void launch_dt(const ScanFwdParams& p, dim3 grid, dim3 block, hipStream_t s) {
+  if (p.softplus) {
+    if (p.pass == 1)
+      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 1, true, TU, kDtR><<<grid, block, 0, s>>>(p);
+    else if (p.store_states)
+      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 2, true, TU, kDtR><<<grid, block, 0, s>>>(p);
+    else
+      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 0, true, TU, kDtR><<<grid, block, 0, s>>>(p);
+  } else {
+    if (p.pass == 1)
+      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 1, false, TU, kDtR><<<grid, block, 0, s>>>(p);
+    else if (p.store_states)
+      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 2, false, TU, kDtR><<<grid, block, 0, s>>>(p);
+    else
+      scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 0, false, TU, kDtR><<<grid, block, 0, s>>>(p);
+  }
+}
+
 template <typename T, int NS, int kSplit, bool kSS2D, bool kVec, typename TU>
 hipError_t launch_t(ScanFwdParams p, hipStream_t s) {
   p.dblocks = (p.per_group + kWave / kSplit - 1) / (kWave / kSplit);
@@ -267,6 +308,17 @@ hipError_t launch_t(ScanFwdParams p, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid{uint32_t(blocks)}, block{kWave};
+  if constexpr (kSS2D && std::is_same_v<T, float> && std::is_same_v<TU, float>) {
+    if (p.dt_w) {
+      if (p.dt_rank < 1 || p.dt_rank > 16 || p.dt == nullptr) return hipErrorInvalidValue;
+      if (p.dt_rank <= 8)
+        launch_dt<T, NS, kSplit, kSS2D, kVec, TU, 8>(p, grid, block, s);
+      else
+        launch_dt<T, NS, kSplit, kSS2D, kVec, TU, 16>(p, grid, block, s);
+      return hipGetLastError();
+    }
+  }
+  if (p.dt_w) return hipErrorInvalidValue;
   if (p.softplus) {
     if (p.pass == 1)
       scan_fwd_kernel<T, NS, kSplit, kSS2D, kVec, 1, true, TU><<<grid, block, 0, s>>>(p);

@@ -96,6 +96,10 @@ ScanLayout scan_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqle
   return l;
 }
 
+// Up to rank 16 the dt_proj product is formed inside the route scans (the raw delta never goes
+// through memory); larger ranks materialise delta with a separate product.
+static bool fused_dt(int64_t dt_rank) { return dt_rank >= 1 && dt_rank <= 16; }
+
 // ---- SS2D workspace layout -----------------------------------------------------------
 struct SS2DLayout {
   int64_t off_xT, off_ys, off_scan, off_merged, off_dM, off_dMT, off_xc, off_cpart, off_lnpart, total;
@@ -127,7 +131,7 @@ SS2DLayout ss2d_layout(int64_t batch, int64_t dim, int64_t H, int64_t W, int64_t
     const int64_t R = dt_rank, N = dstate, Cp = R + 2 * N, S = wgrad_splits(batch, L);
     l.proj_splits = S;
     l.off_pxdbl = o;   o += align_up(batch * 4 * Cp * L * 4);
-    l.off_pdelta = o;  o += align_up(batch * 4 * dim * L * 4);
+    l.off_pdelta = o;  o += fused_dt(R) ? 0 : align_up(batch * 4 * dim * L * 4);
     l.off_pddelta = o; o += align_up(batch * 4 * dim * L * 4);
     l.off_pdxdbl = o;  o += align_up(batch * 4 * Cp * L * 4);
     l.off_pwx = o;     o += align_up(S * 4 * Cp * dim * 4);
@@ -345,6 +349,7 @@ static const void* scan_input(const void* x, bool in_ws, void* ws, const SS2DLay
 
 static float* wsf(void* ws, int64_t off) { return reinterpret_cast<float*>(at(ws, off)); }
 
+
 // The Δ/B/C producer: for each route k, x_dbl = x_proj_w[k] @ xs_k (rows dt, B, C), then
 // delta = dt_proj_w[k] @ dt, all fp32 in route order in the workspace.  xs_k is the fp32 map
 // (routes 0, 2) or its transpose (routes 1, 3), read backwards for the reversed routes.
@@ -371,6 +376,7 @@ static int ss2d_project(const ss2d_fwd_args* a, const SS2DLayout& lay, hipStream
   f.nk = 4;
   f.rev_routes = 1;
   if (launch_proj(f, stream) != hipSuccess) return SS2D_ERR_HIP;
+  if (fused_dt(R)) return SS2D_OK;
   ProjArgs g{};  // delta (D x L) = dt_proj_w[k] (D x R) dt (R x L)
   g.w = a->dt_proj_w;
   g.w_k = D * R;
@@ -430,7 +436,12 @@ static int ss2d_scan_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, bool k
   p.u = scan_input(a->x, (a->conv_w != nullptr || a->x_proj_w != nullptr), a->workspace, lay);
   p.uT = at(a->workspace, lay.off_xT);
   p.u_f32 = a->conv_w != nullptr && a->dtype != 0 && !proj;
-  p.delta = proj ? wsf(a->workspace, lay.off_pdelta) : a->delta;
+  p.delta = proj ? (fused_dt(a->dt_rank) ? nullptr : wsf(a->workspace, lay.off_pdelta)) : a->delta;
+  if (proj && fused_dt(a->dt_rank)) {
+    p.dt = wsf(a->workspace, lay.off_pxdbl);
+    p.dt_w = a->dt_proj_w;
+    p.dt_rank = int(a->dt_rank);
+  }
   p.A = a->A;
   p.Bm = proj ? wsf(a->workspace, lay.off_pxdbl) + a->dt_rank * L : a->Bm;
   p.Cm = proj ? wsf(a->workspace, lay.off_pxdbl) + (a->dt_rank + a->dstate) * L : a->Cm;
@@ -985,7 +996,12 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
   bp.u = u;
   bp.uT = at(ws, lay.off_xT);
   bp.u_f32 = a->conv_w != nullptr && a->dtype != 0 && !proj;
-  bp.delta = proj ? wsf(ws, lay.off_pdelta) : a->delta;
+  bp.delta = proj ? (fused_dt(a->dt_rank) ? nullptr : wsf(ws, lay.off_pdelta)) : a->delta;
+  if (proj && fused_dt(a->dt_rank)) {
+    bp.dt = wsf(ws, lay.off_pxdbl);
+    bp.dt_w = a->dt_proj_w;
+    bp.dt_rank = int(a->dt_rank);
+  }
   bp.A = a->A;
   bp.Bm = proj ? wsf(ws, lay.off_pxdbl) + a->dt_rank * L : a->Bm;
   bp.Cm = proj ? wsf(ws, lay.off_pxdbl) + (a->dt_rank + a->dstate) * L : a->Cm;

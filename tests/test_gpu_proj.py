@@ -48,6 +48,9 @@ CASES = [
     (1, 64, 64, 64, 16, 4, "f32", True, 0, False),    # few rows: chunked route scans
     (2, 9, 11, 96, 16, 6, "bf16", True, 3, True),     # dim over one 64-row tile
     (3, 5, 6, 24, 1, 2, "f32", True, 0, False),       # one state
+    (1, 10, 12, 48, 8, 12, "f32", True, 0, False),    # rank 9..16: the wider in-scan dt_proj
+    (1, 5, 7, 32, 16, 9, "bf16", True, 0, False),     # same, L % 4 != 0 (scalar loads)
+    (2, 6, 8, 40, 4, 20, "bf16", True, 3, False),     # rank > 16: delta through its own product
 ]
 
 
