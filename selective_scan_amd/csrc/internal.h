@@ -195,6 +195,11 @@ struct ProjArgs {
   int nk;
   int rev_routes;
   int accumulate;  // C += product, else C = product
+  // routes k and k + 2 (k < 2, nk = 2) in one product: rows [0, M/2) belong to route k, rows
+  // [M/2, M) to route k + 2 (weights w_{k+2}, written at column L - 1 - j); X (x_k = 0, shared
+  // by the two routes) is read forwards.  Requires weights contiguous along the contraction
+  // (w_kk = 1, K % 4 == 0, aligned).
+  int pair_routes;
   int64_t m_tiles; // set by launch_proj
 };
 hipError_t launch_proj(const ProjArgs& g, hipStream_t s);
@@ -216,6 +221,10 @@ struct WgradArgs {
   int64_t M, N, K, batch;
   int nk, splits;
   int rev_routes;
+  // routes k and k + 2 (k < 2, nk = 2) in one product: A rows [0, M/2) of route k, rows [M/2, M)
+  // of route k + 2, both against B of route k (b_k = 0); partials laid out for 4 routes of M/2
+  // rows
+  int pair_routes;
 };
 hipError_t launch_wgrad(const WgradArgs& g, hipStream_t s);
 // steps per work unit of launch_wgrad (one 16-step piece per wavefront)

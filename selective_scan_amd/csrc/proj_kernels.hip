@@ -38,7 +38,11 @@ constexpr int kPN = 128;  // columns per tile of proj_kernel
 
 __device__ __forceinline__ float4 rev4(float4 v) { return make_float4(v.w, v.z, v.y, v.x); }
 
-template <int MB, int TK, bool kVec>
+// kVec: 4-element sequence loads (L % 4 == 0, aligned views).  kAVec: the weight rows are
+// contiguous along the contraction (K % 4 == 0, aligned): 4-element weight loads.  kPair: routes
+// k and k + 2 in one tile (rows [0, M/2) route k, rows [M/2, M) route k + 2, written at column
+// L - 1 - j, since route k + 2 is route k read backwards): one read of the sequence serves both.
+template <int MB, int TK, bool kVec, bool kAVec, bool kPair>
 __global__ __launch_bounds__(kThreads) void proj_kernel(const ProjArgs g) {
   constexpr int kHalf = TK / 2;
   constexpr int kXPer = kVec ? TK * kPN / 4 / kThreads : TK * kPN / kThreads;
@@ -51,13 +55,17 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(const ProjArgs g) {
   // share the sequence chunk in the caches
   const int64_t ct = blockIdx.x / g.m_tiles;
   const int64_t n0 = ct * kPN, m0 = (int64_t(blockIdx.x) - ct * g.m_tiles) * (32 * MB);
-  const bool rev = g.rev_routes && k >= 2;
+  const bool rev = !kPair && g.rev_routes && k >= 2;
   const float* xb = ((k & 1) ? g.x1 : g.x0) + b * g.x_b + k * g.x_k;
+  const int64_t mh = g.M / 2;  // rows per route when paired
   const float* wrow[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    const int64_t i = m0 + 32 * mb + jl;
-    wrow[mb] = g.w + k * g.w_k + (i < g.M ? i : g.M - 1) * g.w_i;  // rows past M feed no output
+    const int64_t i = m0 + 32 * mb + jl, ic = i < g.M ? i : g.M - 1;  // rows past M feed no output
+    if (kPair)
+      wrow[mb] = g.w + (ic < mh ? k : k + 2) * g.w_k + (ic < mh ? ic : ic - mh) * g.w_i;
+    else
+      wrow[mb] = g.w + k * g.w_k + ic * g.w_i;
   }
   // this thread's column of the sequence chunk and its first row
   const int xr0 = kVec ? (t >> 5) : (t >> 7), xstep = kVec ? 8 : 2;
@@ -86,12 +94,25 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(const ProjArgs g) {
         xr[q] = *p;
     }
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb) {
+      if constexpr (kAVec) {  // K % 4 == 0: a granule is all in or all out
 #pragma unroll
-      for (int s = 0; s < kHalf; ++s) {
-        const int64_t kk = k0 + h * kHalf + s;
-        a[mb][s] = wrow[mb][(kk < g.K ? kk : g.K - 1) * g.w_kk];
+        for (int q = 0; q < kHalf / 4; ++q) {
+          const int64_t kk = k0 + h * kHalf + 4 * q;
+          const float4 v = *reinterpret_cast<const float4*>(wrow[mb] + (kk < g.K ? kk : g.K - 4));
+          a[mb][4 * q] = v.x;
+          a[mb][4 * q + 1] = v.y;
+          a[mb][4 * q + 2] = v.z;
+          a[mb][4 * q + 3] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < kHalf; ++s) {
+          const int64_t kk = k0 + h * kHalf + s;
+          a[mb][s] = wrow[mb][(kk < g.K ? kk : g.K - 1) * g.w_kk];
+        }
       }
+    }
   };
   auto store = [&](int buf) {
 #pragma unroll
@@ -135,37 +156,44 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(const ProjArgs g) {
   const int64_t jc = n0 + 32 * wave + jl;
   const bool jok = jc < g.L;
   float* cb = g.c + b * g.c_b + k * g.c_k + (jok ? jc : 0);
+  float* cb2 = kPair ? g.c + b * g.c_b + (k + 2) * g.c_k + (jok ? g.L - 1 - jc : 0) : cb;  // route k + 2
+  auto cptr = [&](int64_t i) {  // i < M
+    if (kPair) return i < mh ? cb + i * g.c_r : cb2 + (i - mh) * g.c_r;
+    return cb + i * g.c_r;
+  };
   // two row blocks at a time: the previous values (when accumulating) are all loaded first
 #pragma unroll
   for (int m2 = 0; m2 < MB; m2 += 2) {
-    constexpr int kPair = MB > 1 ? 2 : 1;
+    constexpr int kPairRows = MB > 1 ? 2 : 1;
     if (g.accumulate) {
-      float old[kPair][16];
+      float old[kPairRows][16];
 #pragma unroll
-      for (int e = 0; e < kPair; ++e)
+      for (int e = 0; e < kPairRows; ++e)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int64_t i = m0 + 32 * (m2 + e) + 4 * h + 8 * (v / 4) + v % 4;
-          old[e][v] = (m2 + e < MB) ? cb[(jok && i < g.M ? i : 0) * g.c_r] : 0.0f;
+          old[e][v] = (m2 + e < MB) ? *cptr(jok && i < g.M ? i : 0) : 0.0f;
         }
 #pragma unroll
-      for (int e = 0; e < kPair; ++e)
+      for (int e = 0; e < kPairRows; ++e)
         if (m2 + e < MB)
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[m2 + e][v] += old[e][v];
     }
 #pragma unroll
-    for (int e = 0; e < kPair; ++e)
+    for (int e = 0; e < kPairRows; ++e)
       if (m2 + e < MB)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int64_t i = m0 + 32 * (m2 + e) + 4 * h + 8 * (v / 4) + v % 4;
-          if (jok && i < g.M) cb[i * g.c_r] = acc[m2 + e][v];
+          if (jok && i < g.M) *cptr(i) = acc[m2 + e][v];
         }
   }
 }
 
-template <int MBW, int NBW, bool kVec>
+// kPair: routes k and k + 2 in one tile (A rows [0, M/2) of route k, rows [M/2, M) of route
+// k + 2, which pairs its step l with step K - 1 - l of the same B): one read of B serves both.
+template <int MBW, int NBW, bool kVec, bool kPair>
 __global__ __launch_bounds__(kThreads) void wgrad_kernel(const WgradArgs g) {
   constexpr int kBlk = MBW * NBW;
   __shared__ float red[kBlk * 16][64];
@@ -175,17 +203,20 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(const WgradArgs g) {
   const int64_t m0 = mt * (32 * MBW), n0 = nt * (32 * NBW);
   const int64_t sl = blockIdx.y / g.nk;
   const int k = int(blockIdx.y - sl * g.nk);
-  const bool rev = g.rev_routes && k >= 2;
+  const int64_t mh = g.M / 2;  // rows per route when paired
   const int64_t upi = (g.K + kWgradUnit - 1) / kWgradUnit, units = g.batch * upi;
   const int64_t per = (units + g.splits - 1) / g.splits;
   const int64_t u0 = sl * per, u1 = u0 + per < units ? u0 + per : units;
   // rows of this lane (clamped: an out-of-range row only feeds an output that is not written)
   const float* arow[MBW];
   const float* brow[NBW];
+  bool arev[MBW];  // A row read backwards (per lane when paired)
 #pragma unroll
   for (int mb = 0; mb < MBW; ++mb) {
-    const int64_t i = m0 + 32 * mb + jl;
-    arow[mb] = g.a + k * g.a_k + (i < g.M ? i : g.M - 1) * g.a_r;
+    const int64_t i = m0 + 32 * mb + jl, ic = i < g.M ? i : g.M - 1;
+    const int ka = kPair ? (ic < mh ? k : k + 2) : k;
+    arow[mb] = g.a + ka * g.a_k + (kPair && ic >= mh ? ic - mh : ic) * g.a_r;
+    arev[mb] = g.rev_routes && ka >= 2;
   }
   const float* bk = (k & 1) ? g.b1 : g.b0;
 #pragma unroll
@@ -209,9 +240,10 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(const WgradArgs g) {
       const int64_t l = l0 + (kVec ? 4 : 1) * e;
       rok[e] = l < g.K;  // vector path: K % 4 == 0, so a granule is all in or all out
       const int64_t lc = l < g.K ? l : 0;
-      const int64_t la = rev ? g.K - (kVec ? 4 : 1) - lc : lc;
+      const int64_t lr = g.K - (kVec ? 4 : 1) - lc;
 #pragma unroll
-      for (int mb = 0; mb < MBW; ++mb) ra[mb][e] = *reinterpret_cast<const Raw*>(arow[mb] + aoff + la);
+      for (int mb = 0; mb < MBW; ++mb)
+        ra[mb][e] = *reinterpret_cast<const Raw*>(arow[mb] + aoff + (arev[mb] ? lr : lc));
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) rb[nb][e] = *reinterpret_cast<const Raw*>(brow[nb] + boff + lc);
     }
@@ -223,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(const WgradArgs g) {
       if constexpr (kVec) {
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb) {
-          const float4 v = rev ? rev4(ra[mb][e]) : ra[mb][e];
+          const float4 v = arev[mb] ? rev4(ra[mb][e]) : ra[mb][e];
           acur[mb][4 * e] = v.x;
           acur[mb][4 * e + 1] = v.y;
           acur[mb][4 * e + 2] = v.z;
@@ -290,7 +322,8 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(const WgradArgs g) {
     __syncthreads();
   }
   if (wave == 0) {
-    float* c = g.c + (sl * g.nk + k) * g.M * g.N;
+    // partial of route r: c + ((sl * routes + r) * rows + i) * N, routes = 2 nk when paired
+    const int64_t rows = kPair ? mh : g.M, routes = kPair ? 2 * g.nk : g.nk;
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
@@ -299,7 +332,8 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(const WgradArgs g) {
         for (int v = 0; v < 16; ++v) {
           const int64_t i = m0 + 32 * mb + 8 * (v / 4) + 4 * h + v % 4, j = n0 + 32 * nb + jl;
           const float val = acc[mb][nb][v] + red[(mb * NBW + nb) * 16 + v][lane];
-          if (i < g.M && j < g.N) c[i * g.N + j] = val;
+          const int64_t r = kPair && i >= mh ? k + 2 : k, ir = kPair && i >= mh ? i - mh : i;
+          if (i < g.M && j < g.N) g.c[((sl * routes + r) * rows + ir) * g.N + j] = val;
         }
   }
 }
@@ -346,24 +380,31 @@ __global__ __launch_bounds__(256) void cast_transpose_kernel(const T* x, float* 
 namespace {
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-template <int MB, int TK>
-hipError_t run_proj(const ProjArgs& g, dim3 grid, bool vec, hipStream_t s) {
-  if (vec)
-    proj_kernel<MB, TK, true><<<grid, dim3(kThreads), 0, s>>>(g);
+template <int MB, int TK, bool kVec>
+void run_proj_v(const ProjArgs& g, dim3 grid, bool avec, hipStream_t s) {
+  if (g.pair_routes)  // the launcher pairs only weights with 4-element loads
+    proj_kernel<MB, TK, kVec, true, true><<<grid, dim3(kThreads), 0, s>>>(g);
+  else if (avec)
+    proj_kernel<MB, TK, kVec, true, false><<<grid, dim3(kThreads), 0, s>>>(g);
   else
-    proj_kernel<MB, TK, false><<<grid, dim3(kThreads), 0, s>>>(g);
-  return hipGetLastError();
+    proj_kernel<MB, TK, kVec, false, false><<<grid, dim3(kThreads), 0, s>>>(g);
 }
 template <int MB>
-hipError_t run_proj_tk(const ProjArgs& g, dim3 grid, bool vec, int tk, hipStream_t s) {
-  return tk == 8 ? run_proj<MB, 8>(g, grid, vec, s) : run_proj<MB, 16>(g, grid, vec, s);
+hipError_t run_proj(const ProjArgs& g, dim3 grid, bool vec, bool avec, int tk, hipStream_t s) {
+  if (tk == 8)
+    vec ? run_proj_v<MB, 8, true>(g, grid, avec, s) : run_proj_v<MB, 8, false>(g, grid, avec, s);
+  else
+    vec ? run_proj_v<MB, 16, true>(g, grid, avec, s) : run_proj_v<MB, 16, false>(g, grid, avec, s);
+  return hipGetLastError();
 }
 template <int MBW, int NBW>
 hipError_t run_wgrad(const WgradArgs& g, dim3 grid, bool vec, hipStream_t s) {
-  if (vec)
-    wgrad_kernel<MBW, NBW, true><<<grid, dim3(kThreads), 0, s>>>(g);
+  if (g.pair_routes)
+    vec ? wgrad_kernel<MBW, NBW, true, true><<<grid, dim3(kThreads), 0, s>>>(g)
+        : wgrad_kernel<MBW, NBW, false, true><<<grid, dim3(kThreads), 0, s>>>(g);
   else
-    wgrad_kernel<MBW, NBW, false><<<grid, dim3(kThreads), 0, s>>>(g);
+    vec ? wgrad_kernel<MBW, NBW, true, false><<<grid, dim3(kThreads), 0, s>>>(g)
+        : wgrad_kernel<MBW, NBW, false, false><<<grid, dim3(kThreads), 0, s>>>(g);
   return hipGetLastError();
 }
 }  // namespace
@@ -381,18 +422,21 @@ hipError_t launch_proj(const ProjArgs& g, hipStream_t s) {
   const int64_t gx = (g.L + kPN - 1) / kPN * a.m_tiles, gy = g.batch * g.nk;
   if (gx > int64_t(INT32_MAX) || gy > 65535) return hipErrorInvalidValue;
   const bool vec = g.L % 4 == 0 && g.x_b % 4 == 0 && g.x_k % 4 == 0 && g.x_r % 4 == 0 && al16(g.x0) && al16(g.x1);
+  const bool avec = g.w_kk == 1 && g.K % 4 == 0 && g.w_i % 4 == 0 && g.w_k % 4 == 0 && al16(g.w);
+  if (g.pair_routes && (!avec || g.nk != 2 || g.M % 2 != 0 || g.x_k != 0)) return hipErrorInvalidValue;
   const dim3 grid{uint32_t(gx), uint32_t(gy), 1u};
   switch (mb) {
-    case 1: return run_proj_tk<1>(a, grid, vec, tk, s);
-    case 2: return run_proj_tk<2>(a, grid, vec, tk, s);
-    case 3: return run_proj_tk<3>(a, grid, vec, tk, s);
-    default: return run_proj_tk<4>(a, grid, vec, tk, s);
+    case 1: return run_proj<1>(a, grid, vec, avec, tk, s);
+    case 2: return run_proj<2>(a, grid, vec, avec, tk, s);
+    case 3: return run_proj<3>(a, grid, vec, avec, tk, s);
+    default: return run_proj<4>(a, grid, vec, avec, tk, s);
   }
 }
 
 hipError_t launch_wgrad(const WgradArgs& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (g.K <= 0 || g.batch <= 0 || g.nk <= 0 || g.splits <= 0) return hipErrorInvalidValue;
+  if (g.pair_routes && (g.nk != 2 || g.M % 2 != 0 || g.b_k != 0)) return hipErrorInvalidValue;
   const int64_t mbn = (g.M + 31) / 32, nbn = (g.N + 31) / 32;
   const int mbw = mbn < 3 ? int(mbn) : 3;
   const int nmax = 6 / mbw;

@@ -375,6 +375,12 @@ static int ss2d_project(const ss2d_fwd_args* a, const SS2DLayout& lay, hipStream
   f.batch = a->batch;
   f.nk = 4;
   f.rev_routes = 1;
+  if (D % 4 == 0 && (reinterpret_cast<uintptr_t>(a->x_proj_w) & 15) == 0) {  // routes k and k + 2 from one read of their map
+    f.M = 2 * Cp;
+    f.nk = 2;
+    f.rev_routes = 0;
+    f.pair_routes = 1;
+  }
   if (launch_proj(f, stream) != hipSuccess) return SS2D_ERR_HIP;
   if (fused_dt(R)) return SS2D_OK;
   ProjArgs g{};  // delta (D x L) = dt_proj_w[k] (D x R) dt (R x L)
@@ -812,13 +818,14 @@ static int ss2d_project_bwd(const ss2d_bwd_args* a, const SS2DLayout& lay, hipSt
     g.b_b = D * L;
     g.b_r = L;
     g.c = wsf(ws, lay.off_pwx);
-    g.M = Cp;
+    g.M = 2 * Cp;  // routes k and k + 2 from one read of their map
     g.N = D;
     g.K = L;
     g.batch = a->batch;
-    g.nk = 4;
+    g.nk = 2;
     g.splits = int(S);
     g.rev_routes = 1;
+    g.pair_routes = 1;
     if (launch_wgrad(g, stream) != hipSuccess) return SS2D_ERR_HIP;
   }
   {  // ddt_proj_w[k] (D x R) = sum_{b, l} ddelta[d, l] dt[r, l]
