@@ -83,10 +83,11 @@ def front_bytes(cfg, bwd=False):
 
 
 def proj_flops(cfg, R):
-    """Multiply-adds x 2 of the Δ/B/C producer per forward: x_proj (R + 2N rows) and dt_proj per
-    route and pixel."""
+    """Multiply-adds x 2 of the Δ/B/C producer's matrix-core products per forward: x_proj (R + 2N
+    rows) per route and pixel, and dt_proj when its rank exceeds 16 (up to 16 the route scans form
+    the raw delta themselves, on the vector units)."""
     tokens = 4 * cfg.batch * cfg.seqlen
-    return 2 * tokens * ((R + 2 * cfg.dstate) * cfg.dim + cfg.dim * R)
+    return 2 * tokens * ((R + 2 * cfg.dstate) * cfg.dim + (cfg.dim * R if R > 16 else 0))
 
 
 def algorithmic_bytes(cfg, bwd=False, proj=False):
@@ -393,7 +394,8 @@ def main():
     if proj is not None:
         pf = proj_flops(cfg, args.proj)
         s_ms = float(np.mean(stage0_ms))
-        res["producer"] = {"kernel": "gemm_kernel (v_mfma_f32_32x32x2f32), stage 0 with the fp32 copies",
+        res["producer"] = {"kernel": "proj_kernel (v_mfma_f32_32x32x2f32, routes k and k+2 per tile); "
+                                     "stage 0 also writes the fp32 copies of the map",
                            "bound": "mfma", "flops_per_step": pf, "stage0_ms": s_ms, "launch_ms": stats(stage0_ms),
                            "achieved_TFLOPs": pf / (s_ms * 1e-3) / 1e12, "peak_TFLOPs": FP32_MFMA_PEAK_TFLOPS,
                            "frac": pf / (s_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS}
