@@ -209,7 +209,17 @@ def cpu_baseline(cfg, inp, target_s, bwd=False, front=None, ln=None, proj=None):
     routes = 2 if vim else 4
     elems = nb * routes * cfg.dim * cfg.seqlen
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    return {"value": elems / t, "unit": "elements/s", "cores": threads, "kind": "oracle",
+    single = None
+    if not vim and cfg.index in (0, 2) and proj is None and front is None and ln is None:
+        # the tiny and stage-3 workloads also on one core (one image)
+        prev = oracle.set_num_threads(1)
+        try:
+            ts = run(1)
+        finally:
+            oracle.set_num_threads(prev)
+        single = {"value": routes * cfg.dim * cfg.seqlen / ts, "unit": "elements/s", "cores": 1,
+                  "sample": f"first image, {'forward + backward' if bwd else 'forward'}, {ts * 1e3:.2f} ms wall"}
+    return {"value": elems / t, "unit": "elements/s", "cores": threads, "kind": "oracle", "single_thread": single,
             "sample": f"first {nb} of {cfg.batch} {'sequences' if vim else 'images'} (all {cfg.dim} channels, "
                       f"{routes} {'directions' if vim else 'routes'}, L={cfg.seqlen}, N={cfg.dstate}), fp64 C "
                       f"oracle with OpenMP over rows{', with the input front' if front is not None else ''}"

@@ -27,6 +27,7 @@ from .ss2d_oracle import (  # noqa: F401
     cross_merge,
     cross_scan,
     perm_indices,
+    set_num_threads,
     softplus,
     ss2d_bwd,
     ss2d_fwd,

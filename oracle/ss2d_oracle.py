@@ -51,6 +51,16 @@ def _get_lib():
     return _lib
 
 
+def set_num_threads(n: int) -> int:
+    """Threads of the C part's OpenMP loops from now on (for timing); returns the previous count.
+    Threading only: each row is computed by one thread in the same order whatever the count."""
+    lib = _get_lib()
+    lib.omp_get_max_threads.restype = ctypes.c_int
+    prev = int(lib.omp_get_max_threads())
+    lib.omp_set_num_threads(ctypes.c_int(int(n)))
+    return prev
+
+
 def _f64(a):
     return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
 
