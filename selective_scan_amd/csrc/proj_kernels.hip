@@ -419,18 +419,29 @@ hipError_t launch_proj(const ProjArgs& g, hipStream_t s) {
   const int tk = (g.K <= 8 || (g.K + 7) / 8 * 8 < (g.K + 15) / 16 * 16) ? 8 : 16;
   ProjArgs a = g;
   a.m_tiles = (g.M + 32 * mb - 1) / (32 * mb);
-  const int64_t gx = (g.L + kPN - 1) / kPN * a.m_tiles, gy = g.batch * g.nk;
-  if (gx > int64_t(INT32_MAX) || gy > 65535) return hipErrorInvalidValue;
+  const int64_t gx = (g.L + kPN - 1) / kPN * a.m_tiles;
+  if (gx > int64_t(INT32_MAX)) return hipErrorInvalidValue;
   const bool vec = g.L % 4 == 0 && g.x_b % 4 == 0 && g.x_k % 4 == 0 && g.x_r % 4 == 0 && al16(g.x0) && al16(g.x1);
   const bool avec = g.w_kk == 1 && g.K % 4 == 0 && g.w_i % 4 == 0 && g.w_k % 4 == 0 && al16(g.w);
   if (g.pair_routes && (!avec || g.nk != 2 || g.M % 2 != 0 || g.x_k != 0)) return hipErrorInvalidValue;
-  const dim3 grid{uint32_t(gx), uint32_t(gy), 1u};
-  switch (mb) {
-    case 1: return run_proj<1>(a, grid, vec, avec, tk, s);
-    case 2: return run_proj<2>(a, grid, vec, avec, tk, s);
-    case 3: return run_proj<3>(a, grid, vec, avec, tk, s);
-    default: return run_proj<4>(a, grid, vec, avec, tk, s);
+  // grid y = (image, route) pairs, at most 65535 per launch: images in slices
+  const int64_t per = 65535 / g.nk;
+  for (int64_t b0 = 0; b0 < g.batch; b0 += per) {
+    a.batch = g.batch - b0 < per ? g.batch - b0 : per;
+    a.x0 = g.x0 + b0 * g.x_b;
+    a.x1 = g.x1 + b0 * g.x_b;
+    a.c = g.c + b0 * g.c_b;
+    const dim3 grid{uint32_t(gx), uint32_t(a.batch * g.nk), 1u};
+    hipError_t e;
+    switch (mb) {
+      case 1: e = run_proj<1>(a, grid, vec, avec, tk, s); break;
+      case 2: e = run_proj<2>(a, grid, vec, avec, tk, s); break;
+      case 3: e = run_proj<3>(a, grid, vec, avec, tk, s); break;
+      default: e = run_proj<4>(a, grid, vec, avec, tk, s); break;
+    }
+    if (e != hipSuccess) return e;
   }
+  return hipSuccess;
 }
 
 hipError_t launch_wgrad(const WgradArgs& g, hipStream_t s) {
