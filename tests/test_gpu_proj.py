@@ -135,3 +135,49 @@ def test_ss2d_proj_stage1_full_size_image_slices():
             e = rel_err(to_f64(g[key][s]), r[key])
             assert e <= tol, (key, b, e)
     assert all(torch.isfinite(g[k]).all() for k in ("dx_proj_w", "ddt_proj_w", "dA", "dconv_w", "dln_w"))
+
+
+def test_ss2d_proj_stage3_full_size_rank24():
+    """Stage-3 (B=128, 14x14, D=768, N=16, bf16) with the producer at dt_rank 24 (delta through
+    its own product), training launch configuration: the output, dx and dz of sampled images
+    against the oracle; the weight gradients, sums over all images, equal the sums of those of
+    the two half batches (whose slices group the images' steps differently), to fp32 rounding."""
+    cfg = synth.CONFIGS[2]
+    inp = synth.make_config_inputs(cfg, with_dout=True)
+    R = 24
+    pw = synth.make_proj_params(cfg.dim, cfg.dstate, R, seed_base=cfg.index)
+    dt = cfg.dtype
+
+    def run(sl):
+        dev = dict(x=to_dev(inp["x"][sl], dt), delta=None, A=to_dev(inp["A"], "f32"), B=None, C=None,
+                   D=to_dev(inp["D"], "f32"), delta_bias=to_dev(inp["delta_bias"], "f32"),
+                   z=to_dev(inp["z"][sl], dt), x_proj_w=to_dev(pw["x_proj_w"], "f32"),
+                   dt_proj_w=to_dev(pw["dt_proj_w"], "f32"))
+        nb = dev["x"].shape[0]
+        ws = torch.empty(ss.ss2d_workspace_bytes(nb, cfg.dim, cfg.height, cfg.width, cfg.dstate, dev["x"].dtype, R),
+                         dtype=torch.uint8, device="cuda")
+        out = ss.ss2d_fwd(**dev, workspace=ws, keep_states=True)
+        g = ss.ss2d_bwd(**dev, dout=to_dev(inp["dout"][sl], dt), workspace=ws, workspace_has_states=True)
+        torch.cuda.synchronize()
+        return out, g
+
+    out, g = run(slice(0, cfg.batch))
+    f = lambda a: synth.storage_to_f64(a, dt)
+    tol = TOL["bf16"]
+    rng = np.random.default_rng(53)
+    for b in (cfg.batch - 1, int(rng.integers(cfg.batch))):
+        s = slice(b, b + 1)
+        a = dict(x=f(inp["x"][s]), x_proj_w=pw["x_proj_w"].astype(np.float64),
+                 dt_proj_w=pw["dt_proj_w"].astype(np.float64), A=inp["A"].astype(np.float64),
+                 D=inp["D"].astype(np.float64), delta_bias=inp["delta_bias"].astype(np.float64), z=f(inp["z"][s]))
+        assert rel_err(to_f64(out[s]), oracle.ss2d_proj_fwd(**a)) <= tol, ("out", b)
+        r = oracle.ss2d_proj_bwd(**a, dout=f(inp["dout"][s]))
+        for key in ("dx", "dz"):
+            e = rel_err(to_f64(g[key][s]), r[key])
+            assert e <= tol, (key, b, e)
+    h = cfg.batch // 2
+    _, g1 = run(slice(0, h))
+    _, g2 = run(slice(h, cfg.batch))
+    for key in ("dx_proj_w", "ddt_proj_w", "dA", "dD", "ddelta_bias"):
+        e = rel_err(to_f64(g[key]), to_f64(g1[key]) + to_f64(g2[key]))
+        assert e <= 1e-4, (key, e)
