@@ -175,9 +175,11 @@ void scan_fwd_kernel(const ScanFwdParams p) {
     };
     read_bc(0, bufb[0], bufc[0]);
     // The tile is processed in groups of 4 steps: per-step quantities, recurrence, epilogue and
-    // a 4-element store per group, so that only a group's worth of temporaries is live.
+    // a 4-element store per group, so that only a group's worth of temporaries is live.  Groups
+    // wholly past the end of the range are skipped (a padded step leaves the state as it is).
 #pragma unroll
     for (int g4 = 0; g4 < kTile / 4; ++g4) {
+      if (4 * g4 >= nt) break;
       float lam[4], du[4], y[4];
       // raw delta of step i of the tile: loaded, or formed from the staged dt rows (-inf past
       // the end of the range, as the padded loads give)
