@@ -6,6 +6,8 @@
 // Each workgroup owns a 32 x 32 pixel tile of one (b, c) plane.  Row-major routes are read and
 // written along w; column-major routes along h, through a padded LDS tile so that both the
 // global reads and the global writes stay contiguous.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -185,29 +187,43 @@ __global__ __launch_bounds__(kPlaneThreads) void transpose_plane_kernel(const W*
   const W* xp = x + int64_t(blockIdx.x) * L;
   W* op = xT + int64_t(blockIdx.x) * L;
   const int ld = Wd + 1;
-  // read the plane in grid order: 4 consecutive pixels per thread
-  for (int64_t q = 4 * int64_t(threadIdx.x); q < L; q += 4 * kPlaneThreads) {
-    W v[4];
-    if (sizeof(W) == 2) {
-      const uint2 raw = *reinterpret_cast<const uint2*>(xp + q);
-      v[0] = W(raw.x & 0xffff); v[1] = W(raw.x >> 16); v[2] = W(raw.y & 0xffff); v[3] = W(raw.y >> 16);
-    } else {
-      const uint4 raw = *reinterpret_cast<const uint4*>(xp + q);
-      v[0] = W(raw.x); v[1] = W(raw.y); v[2] = W(raw.z); v[3] = W(raw.w);
+  const int Li = int(L);  // the plane fits the LDS, so 32-bit indices suffice
+  // read the plane in grid order: 4 consecutive pixels per thread, four loads issued before any
+  // LDS write (a load used right away costs one round trip each); quads past the plane re-read
+  // quad 0 and are not stored
+  using Raw = typename std::conditional<sizeof(W) == 2, uint2, uint4>::type;
+  constexpr int kBatch = 4;
+  for (int q0 = 4 * int(threadIdx.x); q0 < Li; q0 += 4 * kPlaneThreads * kBatch) {
+    Raw raw[kBatch];
+#pragma unroll
+    for (int e = 0; e < kBatch; ++e) {
+      const int q = q0 + 4 * kPlaneThreads * e;
+      raw[e] = *reinterpret_cast<const Raw*>(xp + (q < Li ? q : 0));
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int h = int((q + j) / Wd), w = int((q + j) % Wd);
-      tile[h * ld + w] = v[j];
+    for (int e = 0; e < kBatch; ++e) {
+      const int q = q0 + 4 * kPlaneThreads * e;
+      if (q >= Li) break;
+      W v[4];
+      if constexpr (sizeof(W) == 2) {
+        v[0] = W(raw[e].x & 0xffff); v[1] = W(raw[e].x >> 16); v[2] = W(raw[e].y & 0xffff); v[3] = W(raw[e].y >> 16);
+      } else {
+        v[0] = W(raw[e].x); v[1] = W(raw[e].y); v[2] = W(raw[e].z); v[3] = W(raw[e].w);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int h = (q + j) / Wd, w = (q + j) - h * Wd;
+        tile[h * ld + w] = v[j];
+      }
     }
   }
   __syncthreads();
-  // write in column-major order: t = w*H + h, 4 consecutive t per thread (H % 4 == 0)
-  for (int64_t t = 4 * int64_t(threadIdx.x); t < L; t += 4 * kPlaneThreads) {
+  // write in column-major order: t = w*H + h, 4 consecutive t per thread (L % 4 == 0)
+  for (int t = 4 * int(threadIdx.x); t < Li; t += 4 * kPlaneThreads) {
     W v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int w = int((t + j) / H), h = int((t + j) % H);
+      const int w = (t + j) / H, h = (t + j) - w * H;
       v[j] = tile[h * ld + w];
     }
     if (sizeof(W) == 2) {
