@@ -238,66 +238,91 @@ __global__ __launch_bounds__(kPlaneThreads) void transpose_plane_kernel(const W*
 }
 
 // The SS2D merge, one plane per workgroup: y = (((r0 + r1) + r2) + r3) [+ Dsum * x] [* silu(z)],
-// summed in fp32.  Routes are of type R (fp32, or the I/O type T), grid tensors of type T.
-template <typename T, typename R>
+// summed in fp32.  Routes are of type R (fp32, or the I/O type T), grid tensors of type T.  The
+// skip term (kSkip), the gate (kZ) and an fp32 x (kXF32) are template parameters, and each loop
+// issues up to kMergeBatch iterations' loads before using any of them: a load behind a branch,
+// or used right away, costs a round trip of its own.
+constexpr int kMergeBatch = 4;
+template <typename T, typename R, bool kSkip, bool kZ, bool kXF32>
 __global__ __launch_bounds__(kPlaneThreads) void merge_plane_kernel(MergeArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int H = int(a.H), Wd = int(a.W);
-  const int64_t L = int64_t(H) * Wd;
+  const int L = H * Wd;                    // the plane fits the LDS: 32-bit indices
   const int ld = H + 1;                    // [w][h] with an odd row stride: conflict-free column reads
   float* t1 = reinterpret_cast<float*>(smem);
-  float* t3 = t1 + int64_t(Wd) * ld;
+  float* t3 = t1 + Wd * ld;
   const int64_t plane = int64_t(blockIdx.x);  // b * C + c
   const int64_t b = plane / a.C, c = plane % a.C;
   const R* r0 = static_cast<const R*>(a.routes) + (b * 4 * a.C + c) * L;
   const R* r1 = r0 + a.C * L;
   const R* r2 = r1 + a.C * L;
   const R* r3 = r2 + a.C * L;
+  constexpr int kStep = 4 * kPlaneThreads;
   // routes 1 and 3 are in column-major order: t1[w][h] = r1[w*H + h], t3[w][h] = r3[L-1-(w*H + h)]
-  for (int64_t t = 4 * int64_t(threadIdx.x); t < L; t += 4 * kPlaneThreads) {
-    const float4 v1 = Elem<R>::load4(r1, t);
-    const float4 v3 = Elem<R>::load4(r3, L - 4 - t);  // route-3 steps L-4-t .. L-1-t
-    const float a1[4] = {v1.x, v1.y, v1.z, v1.w};
-    const float a3[4] = {v3.w, v3.z, v3.y, v3.x};  // pixel order t .. t+3
+  for (int t0 = 4 * int(threadIdx.x); t0 < L; t0 += kStep * kMergeBatch) {
+    float4 v1[kMergeBatch], v3[kMergeBatch];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t q = t + j;
-      const int w = int(q / H), h = int(q % H);
-      t1[w * ld + h] = a1[j];
-      t3[w * ld + h] = a3[j];
+    for (int e = 0; e < kMergeBatch; ++e) {  // past the plane: re-read quad 0, not stored
+      const int t = t0 + kStep * e, tc = t < L ? t : 0;
+      v1[e] = Elem<R>::load4(r1, tc);
+      v3[e] = Elem<R>::load4(r3, L - 4 - tc);  // route-3 steps L-4-t .. L-1-t
+    }
+#pragma unroll
+    for (int e = 0; e < kMergeBatch; ++e) {
+      const int t = t0 + kStep * e;
+      if (t >= L) break;
+      const float a1[4] = {v1[e].x, v1[e].y, v1[e].z, v1[e].w};
+      const float a3[4] = {v3[e].w, v3[e].z, v3[e].y, v3[e].x};  // pixel order t .. t+3
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int w = (t + j) / H, h = (t + j) - w * H;
+        t1[w * ld + h] = a1[j];
+        t3[w * ld + h] = a3[j];
+      }
     }
   }
   __syncthreads();
   float dsum = 0.0f;
-  if (a.Dskip) dsum = ((a.Dskip[c] + a.Dskip[a.C + c]) + a.Dskip[2 * a.C + c]) + a.Dskip[3 * a.C + c];
+  if (kSkip) dsum = ((a.Dskip[c] + a.Dskip[a.C + c]) + a.Dskip[2 * a.C + c]) + a.Dskip[3 * a.C + c];
   const T* xg = static_cast<const T*>(a.x) + plane * L;
-  const T* zg = a.z ? static_cast<const T*>(a.z) + plane * L : nullptr;
+  const float* xf = static_cast<const float*>(a.x) + plane * L;
+  const T* zg = kZ ? static_cast<const T*>(a.z) + plane * L : nullptr;
   T* yg = a.y ? static_cast<T*>(a.y) + plane * L : nullptr;
   float* mg = a.merged_f32 ? a.merged_f32 + plane * L : nullptr;
-  for (int64_t p = 4 * int64_t(threadIdx.x); p < L; p += 4 * kPlaneThreads) {
-    const float4 v0 = Elem<R>::load4(r0, p);
-    const float4 v2 = Elem<R>::load4(r2, L - 4 - p);
-    const float a0[4] = {v0.x, v0.y, v0.z, v0.w};
-    const float a2[4] = {v2.w, v2.z, v2.y, v2.x};
-    float v[4];
+  for (int p0 = 4 * int(threadIdx.x); p0 < L; p0 += kStep * kMergeBatch) {
+    float4 v0[kMergeBatch], v2[kMergeBatch], xv[kMergeBatch], zv[kMergeBatch];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int h = int((p + j) / Wd), w = int((p + j) % Wd);
-      float s = a0[j] + t1[w * ld + h];
-      s = s + a2[j];
-      v[j] = s + t3[w * ld + h];
+    for (int e = 0; e < kMergeBatch; ++e) {
+      const int p = p0 + kStep * e, pc = p < L ? p : 0;
+      v0[e] = Elem<R>::load4(r0, pc);
+      v2[e] = Elem<R>::load4(r2, L - 4 - pc);
+      if constexpr (kSkip) xv[e] = kXF32 ? Elem<float>::load4(xf, pc) : Elem<T>::load4(xg, pc);
+      if constexpr (kZ) zv[e] = Elem<T>::load4(zg, pc);
     }
-    if (a.Dskip && a.x) {
-      const float4 xv = a.x_f32 ? Elem<float>::load4(static_cast<const float*>(a.x) + plane * L, p) : Elem<T>::load4(xg, p);
-      v[0] = fmaf(dsum, xv.x, v[0]); v[1] = fmaf(dsum, xv.y, v[1]);
-      v[2] = fmaf(dsum, xv.z, v[2]); v[3] = fmaf(dsum, xv.w, v[3]);
+#pragma unroll
+    for (int e = 0; e < kMergeBatch; ++e) {
+      const int p = p0 + kStep * e;
+      if (p >= L) break;
+      const float a0[4] = {v0[e].x, v0[e].y, v0[e].z, v0[e].w};
+      const float a2[4] = {v2[e].w, v2[e].z, v2[e].y, v2[e].x};
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int h = (p + j) / Wd, w = (p + j) - h * Wd;
+        float sum = a0[j] + t1[w * ld + h];
+        sum = sum + a2[j];
+        v[j] = sum + t3[w * ld + h];
+      }
+      if constexpr (kSkip) {
+        v[0] = fmaf(dsum, xv[e].x, v[0]); v[1] = fmaf(dsum, xv[e].y, v[1]);
+        v[2] = fmaf(dsum, xv[e].z, v[2]); v[3] = fmaf(dsum, xv[e].w, v[3]);
+      }
+      if (mg) *reinterpret_cast<float4*>(mg + p) = make_float4(v[0], v[1], v[2], v[3]);
+      if constexpr (kZ) {
+        v[0] *= silu(zv[e].x); v[1] *= silu(zv[e].y); v[2] *= silu(zv[e].z); v[3] *= silu(zv[e].w);
+      }
+      if (yg) Elem<T>::store4(yg, p, make_float4(v[0], v[1], v[2], v[3]));
     }
-    if (mg) *reinterpret_cast<float4*>(mg + p) = make_float4(v[0], v[1], v[2], v[3]);
-    if (zg) {
-      const float4 zv = Elem<T>::load4(zg, p);
-      v[0] *= silu(zv.x); v[1] *= silu(zv.y); v[2] *= silu(zv.z); v[3] *= silu(zv.w);
-    }
-    if (yg) Elem<T>::store4(yg, p, make_float4(v[0], v[1], v[2], v[3]));
   }
 }
 
@@ -444,6 +469,24 @@ hipError_t launch_route_scatter(const void* x, const ScanOutputs& o, int64_t bat
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+namespace {
+template <typename T, typename R, bool kSkip, bool kZ>
+void launch_merge_plane_x(const MergeArgs& a, dim3 g, dim3 b, size_t lds, hipStream_t s) {
+  if (kSkip && a.x_f32)
+    merge_plane_kernel<T, R, kSkip, kZ, true><<<g, b, lds, s>>>(a);
+  else
+    merge_plane_kernel<T, R, kSkip, kZ, false><<<g, b, lds, s>>>(a);
+}
+template <typename T, typename R>
+void launch_merge_plane(const MergeArgs& a, dim3 g, dim3 b, size_t lds, hipStream_t s) {
+  const bool skip = a.Dskip != nullptr && a.x != nullptr, z = a.z != nullptr;
+  if (skip)
+    z ? launch_merge_plane_x<T, R, true, true>(a, g, b, lds, s) : launch_merge_plane_x<T, R, true, false>(a, g, b, lds, s);
+  else
+    z ? launch_merge_plane_x<T, R, false, true>(a, g, b, lds, s) : launch_merge_plane_x<T, R, false, false>(a, g, b, lds, s);
+}
+}  // namespace
+
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   const int64_t L = a.H * a.W;
   const size_t plane_lds = size_t(2) * size_t(a.W) * size_t(a.H + 1) * 4;
@@ -456,11 +499,11 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
       (!a.x_f32 || aligned16(a.x)) && L % 4 == 0) {
     const dim3 g{uint32_t(a.batch * a.C)}, b{kPlaneThreads};
     if (a.dtype == 0)
-      merge_plane_kernel<float, float><<<g, b, plane_lds, s>>>(a);
+      launch_merge_plane<float, float>(a, g, b, plane_lds, s);
     else if (a.routes_f32)
-      merge_plane_kernel<bf16, float><<<g, b, plane_lds, s>>>(a);
+      launch_merge_plane<bf16, float>(a, g, b, plane_lds, s);
     else
-      merge_plane_kernel<bf16, bf16><<<g, b, plane_lds, s>>>(a);
+      launch_merge_plane<bf16, bf16>(a, g, b, plane_lds, s);
     return hipGetLastError();
   }
   const int th = int(cdiv(a.H, kT)), tw = int(cdiv(a.W, kT));
