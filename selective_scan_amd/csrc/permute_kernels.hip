@@ -327,74 +327,99 @@ __global__ __launch_bounds__(kPlaneThreads) void merge_plane_kernel(MergeArgs a)
 }
 
 // The gate backward fused with its merge (see MergeGateArgs), one plane per workgroup.  LDS:
-// routes 1 and 3 transposed to [w][h] (as in the merge), and dM as [h][w] for the dMT write.
-template <typename T>
+// routes 1 and 3 transposed to [w][h] (as in the merge), and dM as [h][w] for the dMT write.  As
+// in the merge, the skip term and an fp32 x are template parameters and the loads of up to
+// kMergeBatch iterations are issued before any is used.
+template <typename T, bool kSkip, bool kXF32>
 __global__ __launch_bounds__(kPlaneThreads) void merge_gate_bwd_plane_kernel(MergeGateArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int H = int(a.H), Wd = int(a.W);
-  const int64_t L = int64_t(H) * Wd;
+  const int L = H * Wd;  // the plane fits the LDS: 32-bit indices
   const int ldc = H + 1, ldr = Wd + 1;
   float* t1 = reinterpret_cast<float*>(smem);
-  float* t3 = t1 + int64_t(Wd) * ldc;
-  float* tm = t3 + int64_t(Wd) * ldc;  // [h][w]
+  float* t3 = t1 + Wd * ldc;
+  float* tm = t3 + Wd * ldc;  // [h][w]
   const int64_t plane = int64_t(blockIdx.x);
   const int64_t b = plane / a.C, c = plane % a.C;
   const float* r0 = a.routes + (b * 4 * a.C + c) * L;
   const float* r1 = r0 + a.C * L;
   const float* r2 = r1 + a.C * L;
   const float* r3 = r2 + a.C * L;
-  for (int64_t t = 4 * int64_t(threadIdx.x); t < L; t += 4 * kPlaneThreads) {
-    const float4 v1 = *reinterpret_cast<const float4*>(r1 + t);
-    const float4 v3 = *reinterpret_cast<const float4*>(r3 + (L - 4 - t));
-    const float a1[4] = {v1.x, v1.y, v1.z, v1.w};
-    const float a3[4] = {v3.w, v3.z, v3.y, v3.x};
+  constexpr int kStep = 4 * kPlaneThreads;
+  for (int t0 = 4 * int(threadIdx.x); t0 < L; t0 += kStep * kMergeBatch) {
+    float4 v1[kMergeBatch], v3[kMergeBatch];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t q = t + j;
-      const int w = int(q / H), h = int(q % H);
-      t1[w * ldc + h] = a1[j];
-      t3[w * ldc + h] = a3[j];
+    for (int e = 0; e < kMergeBatch; ++e) {  // past the plane: re-read quad 0, not stored
+      const int t = t0 + kStep * e, tc = t < L ? t : 0;
+      v1[e] = *reinterpret_cast<const float4*>(r1 + tc);
+      v3[e] = *reinterpret_cast<const float4*>(r3 + (L - 4 - tc));
+    }
+#pragma unroll
+    for (int e = 0; e < kMergeBatch; ++e) {
+      const int t = t0 + kStep * e;
+      if (t >= L) break;
+      const float a1[4] = {v1[e].x, v1[e].y, v1[e].z, v1[e].w};
+      const float a3[4] = {v3[e].w, v3[e].z, v3[e].y, v3[e].x};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int w = (t + j) / H, h = (t + j) - w * H;
+        t1[w * ldc + h] = a1[j];
+        t3[w * ldc + h] = a3[j];
+      }
     }
   }
   __syncthreads();
   float dsum = 0.0f;
-  if (a.Dskip) dsum = ((a.Dskip[c] + a.Dskip[a.C + c]) + a.Dskip[2 * a.C + c]) + a.Dskip[3 * a.C + c];
+  if (kSkip) dsum = ((a.Dskip[c] + a.Dskip[a.C + c]) + a.Dskip[2 * a.C + c]) + a.Dskip[3 * a.C + c];
   const T* xg = static_cast<const T*>(a.x) + plane * L;
+  const float* xf = static_cast<const float*>(a.x) + plane * L;
   const T* zg = static_cast<const T*>(a.z) + plane * L;
   const T* gg = static_cast<const T*>(a.dout) + plane * L;
   T* dzg = static_cast<T*>(a.dz) + plane * L;
   float* dmg = a.dM + plane * L;
-  for (int64_t p = 4 * int64_t(threadIdx.x); p < L; p += 4 * kPlaneThreads) {
-    const float4 v0 = *reinterpret_cast<const float4*>(r0 + p);
-    const float4 v2 = *reinterpret_cast<const float4*>(r2 + (L - 4 - p));
-    const float a0[4] = {v0.x, v0.y, v0.z, v0.w};
-    const float a2[4] = {v2.w, v2.z, v2.y, v2.x};
-    const float4 xv = a.x_f32 ? Elem<float>::load4(static_cast<const float*>(a.x) + plane * L, p) : Elem<T>::load4(xg, p);
-    const float4 zv = Elem<T>::load4(zg, p), gv = Elem<T>::load4(gg, p);
-    const float xs[4] = {xv.x, xv.y, xv.z, xv.w}, zs[4] = {zv.x, zv.y, zv.z, zv.w}, gs[4] = {gv.x, gv.y, gv.z, gv.w};
-    float dz[4], dm[4];
+  for (int p0 = 4 * int(threadIdx.x); p0 < L; p0 += kStep * kMergeBatch) {
+    float4 v0[kMergeBatch], v2[kMergeBatch], xv[kMergeBatch], zv[kMergeBatch], gv[kMergeBatch];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int h = int((p + j) / Wd), w = int((p + j) % Wd);
-      float m = a0[j] + t1[w * ldc + h];
-      m = m + a2[j];
-      m = m + t3[w * ldc + h];
-      if (a.Dskip && a.x) m = fmaf(dsum, xs[j], m);
-      const float sz = sigmoid(zs[j]);
-      dm[j] = gs[j] * zs[j] * sz;
-      dz[j] = gs[j] * m * sz * (1.0f + zs[j] * (1.0f - sz));
-      tm[h * ldr + w] = dm[j];
+    for (int e = 0; e < kMergeBatch; ++e) {
+      const int p = p0 + kStep * e, pc = p < L ? p : 0;
+      v0[e] = *reinterpret_cast<const float4*>(r0 + pc);
+      v2[e] = *reinterpret_cast<const float4*>(r2 + (L - 4 - pc));
+      if constexpr (kSkip) xv[e] = kXF32 ? Elem<float>::load4(xf, pc) : Elem<T>::load4(xg, pc);
+      zv[e] = Elem<T>::load4(zg, pc);
+      gv[e] = Elem<T>::load4(gg, pc);
     }
-    *reinterpret_cast<float4*>(dmg + p) = make_float4(dm[0], dm[1], dm[2], dm[3]);
-    Elem<T>::store4(dzg, p, make_float4(dz[0], dz[1], dz[2], dz[3]));
+#pragma unroll
+    for (int e = 0; e < kMergeBatch; ++e) {
+      const int p = p0 + kStep * e;
+      if (p >= L) break;
+      const float a0[4] = {v0[e].x, v0[e].y, v0[e].z, v0[e].w};
+      const float a2[4] = {v2[e].w, v2[e].z, v2[e].y, v2[e].x};
+      const float xs[4] = {xv[e].x, xv[e].y, xv[e].z, xv[e].w};
+      const float zs[4] = {zv[e].x, zv[e].y, zv[e].z, zv[e].w}, gs[4] = {gv[e].x, gv[e].y, gv[e].z, gv[e].w};
+      float dz[4], dm[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int h = (p + j) / Wd, w = (p + j) - h * Wd;
+        float m = a0[j] + t1[w * ldc + h];
+        m = m + a2[j];
+        m = m + t3[w * ldc + h];
+        if (kSkip) m = fmaf(dsum, xs[j], m);
+        const float sz = sigmoid(zs[j]);
+        dm[j] = gs[j] * zs[j] * sz;
+        dz[j] = gs[j] * m * sz * (1.0f + zs[j] * (1.0f - sz));
+        tm[h * ldr + w] = dm[j];
+      }
+      *reinterpret_cast<float4*>(dmg + p) = make_float4(dm[0], dm[1], dm[2], dm[3]);
+      Elem<T>::store4(dzg, p, make_float4(dz[0], dz[1], dz[2], dz[3]));
+    }
   }
   __syncthreads();
   float* dmt = a.dMT + plane * L;
-  for (int64_t t = 4 * int64_t(threadIdx.x); t < L; t += 4 * kPlaneThreads) {
+  for (int t = 4 * int(threadIdx.x); t < L; t += kStep) {
     float v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int w = int((t + j) / H), h = int((t + j) % H);
+      const int w = (t + j) / H, h = (t + j) - w * H;
       v[j] = tm[h * ldr + w];
     }
     *reinterpret_cast<float4*>(dmt + t) = make_float4(v[0], v[1], v[2], v[3]);
@@ -571,10 +596,20 @@ hipError_t launch_merge_gate_bwd(const MergeGateArgs& a, hipStream_t s) {
   if (a.z && lds <= 64 * 1024 && L % 4 == 0 && a.batch * a.C > 0 && aligned16(a.routes) && aligned16(a.dM) &&
       aligned16(a.dMT) && (io & (a.dtype == 0 ? 15 : 7)) == 0 && (!a.x_f32 || aligned16(a.x))) {
     const dim3 g{uint32_t(a.batch * a.C)}, b{kPlaneThreads};
-    if (a.dtype == 0)
-      merge_gate_bwd_plane_kernel<float><<<g, b, lds, s>>>(a);
-    else
-      merge_gate_bwd_plane_kernel<bf16><<<g, b, lds, s>>>(a);
+    const bool skip = a.Dskip != nullptr && a.x != nullptr;
+    if (a.dtype == 0) {
+      if (skip)
+        merge_gate_bwd_plane_kernel<float, true, true><<<g, b, lds, s>>>(a);
+      else
+        merge_gate_bwd_plane_kernel<float, false, false><<<g, b, lds, s>>>(a);
+    } else {
+      if (skip && a.x_f32)
+        merge_gate_bwd_plane_kernel<bf16, true, true><<<g, b, lds, s>>>(a);
+      else if (skip)
+        merge_gate_bwd_plane_kernel<bf16, true, false><<<g, b, lds, s>>>(a);
+      else
+        merge_gate_bwd_plane_kernel<bf16, false, false><<<g, b, lds, s>>>(a);
+    }
     return hipGetLastError();
   }
   // two kernels: the pre-gate merge into `merged` (only needed with a gate), then the gate
