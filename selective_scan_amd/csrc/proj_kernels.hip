@@ -358,20 +358,71 @@ __global__ __launch_bounds__(256) void cast_transpose_kernel(const T* x, float* 
   const int h0 = (t / tw) * 32, w0 = (t % tw) * 32;
   const int64_t base = plane * int64_t(H) * W;
   const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;
+  // the four loads are issued unconditionally (clamped to the tile's first pixel) before any is
+  // used: a load behind a branch is waited for at the branch's end
+  float v[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = h0 + ty + 8 * r, w = w0 + tx;
-    if (h < H && w < W) {
-      const float v = Elem<T>::load(x, base + int64_t(h) * W + w);
-      xf[base + int64_t(h) * W + w] = v;
-      tile[ty + 8 * r][tx] = v;
-    }
+    const bool in = h < H && w < W;
+    v[r] = Elem<T>::load(x, base + (in ? int64_t(h) * W + w : int64_t(h0) * W + w0));
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = h0 + ty + 8 * r, w = w0 + tx;
+    tile[ty + 8 * r][tx] = v[r];
+    if (h < H && w < W) xf[base + int64_t(h) * W + w] = v[r];
   }
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int w = w0 + ty + 8 * r, h = h0 + tx;
     if (h < H && w < W) xfT[base + int64_t(w) * H + h] = tile[tx][ty + 8 * r];
+  }
+}
+
+// One plane per workgroup (when the fp32 plane fits the LDS): 4 consecutive pixels per thread,
+// four loads issued before any is used, the grid-order copy written as it is read, the
+// column-major copy from the LDS tile.
+template <typename T>
+__global__ __launch_bounds__(256) void cast_transpose_plane_kernel(const T* x, float* xf, float* xfT, int H, int W) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* tile = reinterpret_cast<float*>(smem);  // [h][w], row stride W + 1
+  const int L = H * W, ld = W + 1;
+  const int64_t base = int64_t(blockIdx.x) * L;
+  const T* xp = x + base;
+  float* fp = xf + base;
+  float* tp = xfT + base;
+  constexpr int kStep = 4 * 256, kBatch = 4;
+  for (int q0 = 4 * int(threadIdx.x); q0 < L; q0 += kStep * kBatch) {
+    float4 v[kBatch];
+#pragma unroll
+    for (int e = 0; e < kBatch; ++e) {  // past the plane: re-read quad 0, not stored
+      const int q = q0 + kStep * e;
+      v[e] = Elem<T>::load4(xp, q < L ? q : 0);
+    }
+#pragma unroll
+    for (int e = 0; e < kBatch; ++e) {
+      const int q = q0 + kStep * e;
+      if (q >= L) break;
+      *reinterpret_cast<float4*>(fp + q) = v[e];
+      const float a4[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int h = (q + j) / W, w = (q + j) - h * W;
+        tile[h * ld + w] = a4[j];
+      }
+    }
+  }
+  __syncthreads();
+  for (int t = 4 * int(threadIdx.x); t < L; t += kStep) {  // t = w * H + h
+    float a4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int w = (t + j) / H, h = (t + j) - w * H;
+      a4[j] = tile[h * ld + w];
+    }
+    *reinterpret_cast<float4*>(tp + t) = make_float4(a4[0], a4[1], a4[2], a4[3]);
   }
 }
 
@@ -481,6 +532,19 @@ hipError_t launch_sum_parts(const float* part, float* out, int64_t n, int64_t n_
 
 hipError_t launch_cast_transpose(const void* x, float* xf, float* xfT, int64_t batch, int64_t C, int64_t H,
                                  int64_t W, int dtype, hipStream_t s) {
+  const size_t lds = size_t(H) * size_t(W + 1) * 4;
+  const int64_t planes = batch * C;
+  const uintptr_t xa = reinterpret_cast<uintptr_t>(x);
+  if (planes > 0 && (H * W) % 4 == 0 && lds <= 64 * 1024 && planes <= int64_t(UINT32_MAX) && al16(xf) && al16(xfT) &&
+      (xa & (dtype == 0 ? 15 : 7)) == 0) {
+    if (dtype == 0)
+      cast_transpose_plane_kernel<float><<<dim3(uint32_t(planes)), dim3(256), lds, s>>>(
+          static_cast<const float*>(x), xf, xfT, int(H), int(W));
+    else
+      cast_transpose_plane_kernel<bf16><<<dim3(uint32_t(planes)), dim3(256), lds, s>>>(
+          static_cast<const bf16*>(x), xf, xfT, int(H), int(W));
+    return hipGetLastError();
+  }
   const int64_t blocks = batch * C * ((H + 31) / 32) * ((W + 31) / 32);
   if (blocks == 0) return hipSuccess;
   if (blocks > int64_t(UINT32_MAX)) return hipErrorInvalidValue;
