@@ -233,7 +233,7 @@ inline int64_t wgrad_splits(int64_t batch, int64_t L) {
   const int64_t units = batch * ((L + kWgradUnit - 1) / kWgradUnit);
   return units < 256 ? units : 256;
 }
-// out[i] = sum_{s < n_parts} part[s * n + i] in that order (the weight-gradient partials)
+// out[i] = sum_{s < n_parts} part[s * n + i] (the weight-gradient partials), in a fixed order
 hipError_t launch_sum_parts(const float* part, float* out, int64_t n, int64_t n_parts, hipStream_t s);
 // fp32 copies of an SS2D input map: grid order (xf) and per-plane transposed (xfT)
 hipError_t launch_cast_transpose(const void* x, float* xf, float* xfT, int64_t batch, int64_t C, int64_t H,

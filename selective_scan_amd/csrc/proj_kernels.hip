@@ -338,12 +338,29 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(const WgradArgs g) {
   }
 }
 
+// out[i] = sum over the partials, in a fixed order: a workgroup takes 64 outputs; its four
+// wavefronts sum the partials s = g, g + 4, g + 8, ... (g = wavefront) with eight loads in flight,
+// and the four sums are added in the order g = 0, 1, 2, 3.  Partials past the end re-read a valid
+// one and are weighted 0 (they are finite).
 __global__ __launch_bounds__(256) void sum_parts_kernel(const float* part, float* out, int64_t n, int64_t n_parts) {
-  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  float s = 0.0f;
-  for (int64_t k = 0; k < n_parts; ++k) s += part[k * n + i];
-  out[i] = s;
+  __shared__ float red[4][64];
+  const int c = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int64_t i = int64_t(blockIdx.x) * 64 + c, ic = i < n ? i : n - 1;
+  constexpr int kInFlight = 8;
+  float acc = 0.0f;
+  for (int64_t s0 = g; s0 < n_parts; s0 += 4 * kInFlight) {
+    float v[kInFlight];
+#pragma unroll
+    for (int e = 0; e < kInFlight; ++e) {
+      const int64_t sp = s0 + 4 * e;
+      v[e] = part[(sp < n_parts ? sp : g) * n + ic];
+    }
+#pragma unroll
+    for (int e = 0; e < kInFlight; ++e) acc += v[e] * (s0 + 4 * e < n_parts ? 1.0f : 0.0f);
+  }
+  red[g][c] = acc;
+  __syncthreads();
+  if (g == 0 && i < n) out[i] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
 }
 
 // 32 x 32 tile of one plane: fp32 copy in grid order and, through LDS, transposed
@@ -526,7 +543,8 @@ hipError_t launch_wgrad(const WgradArgs& g, hipStream_t s) {
 
 hipError_t launch_sum_parts(const float* part, float* out, int64_t n, int64_t n_parts, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  sum_parts_kernel<<<dim3(uint32_t((n + 255) / 256)), dim3(256), 0, s>>>(part, out, n, n_parts);
+  if (n_parts <= 0 || (n + 63) / 64 > int64_t(UINT32_MAX)) return hipErrorInvalidValue;
+  sum_parts_kernel<<<dim3(uint32_t((n + 63) / 64)), dim3(256), 0, s>>>(part, out, n, n_parts);
   return hipGetLastError();
 }
 
