@@ -23,3 +23,4 @@ from ._binding import (  # noqa: F401
     vim_bidir_fwd,
     vim_bidir_workspace_bytes,
 )
+from .autograd import SelectiveScanFn, SS2DFn, selective_scan_fn, ss2d  # noqa: F401,E402
