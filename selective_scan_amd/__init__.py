@@ -23,4 +23,4 @@ from ._binding import (  # noqa: F401
     vim_bidir_fwd,
     vim_bidir_workspace_bytes,
 )
-from .autograd import SelectiveScanFn, SS2DFn, selective_scan_fn, ss2d  # noqa: F401,E402
+from .autograd import SelectiveScanFn, SS2DFn, VimBidirFn, selective_scan_fn, ss2d, vim_bidir  # noqa: F401,E402

@@ -5,8 +5,10 @@ and principle", section 2: `SelectiveScanFn`): u, delta, A, B, C, D=None, z=None
 delta_bias=None, delta_softplus=False, return_last_state=False; B and C may be 3-D (one group);
 the gradient of last_state is not propagated; gradients of absent optionals are None.  `ss2d`
 is the fused SS2D op (ss2d_fwd / ss2d_bwd) with its optional input front, LayerNorm and Δ/B/C
-producer.  Each forward keeps its checkpoint states in a workspace that its backward reuses, so
-the backward does not recompute the forward.  Every step runs in the library's kernels.
+producer; `vim_bidir` is Vision Mamba's two-direction scan (vim_bidir_fwd / vim_bidir_bwd).  The
+selective_scan_fn and ss2d forwards keep their checkpoint states in a workspace that the backward
+reuses, so their backward does not recompute the forward; vim_bidir's backward recomputes it.
+Every step runs in the library's kernels.
 """
 from __future__ import annotations
 
@@ -75,3 +77,28 @@ def ss2d(x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=True
     """Fused SS2D with autograd (arguments as ss2d_fwd); returns out."""
     opts = dict(delta_softplus=bool(delta_softplus), layer_norm=bool(layer_norm), ln_eps=float(ln_eps))
     return SS2DFn.apply(opts, x, delta, A, B, C, D, delta_bias, z, conv_w, conv_b, ln_w, ln_b, x_proj_w, dt_proj_w)
+
+
+_VIM_KEYS = ("u", "delta", "A", "B", "C", "D", "delta_bias", "z")
+_VIM_GRADS = ("du", "ddelta", "dA", "dB", "dC", "dD", "ddelta_bias", "dz")
+
+
+class VimBidirFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, delta_softplus, *tensors):
+        kw = dict(zip(_VIM_KEYS, tensors))
+        out = _bind.vim_bidir_fwd(**kw, delta_softplus=delta_softplus)
+        ctx.save_for_backward(*tensors)
+        ctx.delta_softplus = delta_softplus
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        kw = dict(zip(_VIM_KEYS, ctx.saved_tensors))
+        g = _bind.vim_bidir_bwd(**kw, dout=dout, delta_softplus=ctx.delta_softplus)
+        return (None,) + tuple(g[k] for k in _VIM_GRADS)
+
+
+def vim_bidir(u, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=True):
+    """Vision Mamba's two-direction scan with autograd (arguments as vim_bidir_fwd); returns out."""
+    return VimBidirFn.apply(bool(delta_softplus), u, delta, A, B, C, D, delta_bias, z)

@@ -1,4 +1,4 @@
-"""The autograd wrappers (selective_scan_fn, ss2d): the gradients autograd produces equal those of
+"""The autograd wrappers (selective_scan_fn, ss2d, vim_bidir): the gradients autograd produces equal those of
 the direct backward calls (which recompute the forward instead of reusing its kept states), the
 outputs equal the direct forward's, absent optionals get no gradient, and one case is checked
 against the fp64 oracle."""
@@ -103,3 +103,19 @@ def test_ss2d_autograd_against_oracle():
     g = oracle.ss2d_bwd(**ref, dout=inp["dout"].astype(np.float64))
     for key in ("x", "delta", "A", "B", "C", "D", "delta_bias", "z"):
         assert rel_err(to_f64(leaves[key].grad), g[GRAD_OF[key]]) <= TOL_GRAD, key
+
+
+def test_vim_bidir_autograd_matches_direct_backward():
+    inp = synth.make_vim_inputs(2, 29, 12, 8, "f32", True, 960, True)
+    t = dict(u=to_dev(inp["u"], "f32"), delta=to_dev(inp["delta"], "f32"), A=to_dev(inp["A"], "f32"),
+             B=to_dev(inp["B"], "f32"), C=to_dev(inp["C"], "f32"), D=to_dev(inp["D"], "f32"),
+             delta_bias=to_dev(inp["delta_bias"], "f32"), z=to_dev(inp["z"], "f32"))
+    dout = to_dev(inp["dout"], "f32")
+    leaves = {k: _leaf(v) for k, v in t.items()}
+    out = ss.vim_bidir(**leaves)
+    out.backward(dout)
+    _close(out, ss.vim_bidir_fwd(**t), "out")
+    r = ss.vim_bidir_bwd(**t, dout=dout)
+    for key, grad in (("u", "du"), ("delta", "ddelta"), ("A", "dA"), ("B", "dB"), ("C", "dC"), ("D", "dD"),
+                      ("delta_bias", "ddelta_bias"), ("z", "dz")):
+        _close(leaves[key].grad, r[grad], key)
