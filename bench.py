@@ -9,7 +9,8 @@ seeded synthetic tensors already resident in HBM when the timed region starts.
 Prints one JSON line: elements/s (B*K*D*L per second) as the value, per-step median /
 min / max, the whole-step algorithmic HBM rate against the 8 TB/s peak and against a
 device copy timed in the same run, the roofline of the dominant kernel (the route-scan
-kernel, timed live with HIP events on the stream it is launched on) and the fp64 CPU
+kernel, timed live with HIP events on the stream it is launched on; for state sizes 1, 2
+and 4 the whole forward is one HBM-bound kernel per plane, and that one) and the fp64 CPU
 oracle timed on this host on a bounded sample of the same workload.  `--workload`
 selects one of the other shapes (0-4 SS2D, 5 the Vision Mamba bidirectional scan at
 Vim-Tiny size); `--bwd` adds the fused backward to each step; `--front K` puts the
@@ -125,16 +126,24 @@ def scan_kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload_name):
-    """HBM traffic of the scan kernel from the committed rocprofv3 counter summary, or None
+def plane_kernel_source_hash():
+    h = hashlib.sha256()
+    for name in ("plane_fwd.hip", "plane_fwd.h", "device_common.h"):
+        with open(os.path.join(ROOT, "selective_scan_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(key, sha):
+    """HBM traffic of the dominant kernel from the committed rocprofv3 counter summary, or None
     when that summary was taken on a different version of the kernel source."""
     path = os.path.join(ROOT, "profiles", "scan_fwd_traffic.txt")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    entry = rec.get(workload_name)
-    if not entry or entry.get("kernel_source_sha") != scan_kernel_source_hash():
+    entry = rec.get(key)
+    if not entry or entry.get("kernel_source_sha") != sha:
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -303,6 +312,7 @@ def main():
         Plan = (lambda **kw: ss.SS2DForwardPlan(**kw, keep_states=True)) if args.bwd else ss.SS2DForwardPlan
         backward = (lambda **kw: ss.ss2d_bwd(**kw, workspace_has_states=True))
     plan0 = Plan(**d0)
+    single = plan0.single_kernel  # the forward runs as one kernel per plane (small state sizes)
     # bytes one step touches in HBM (inputs, output, workspace): rotate independent copies
     # until one cycle over them exceeds three times the MALL
     footprint = sum(t.numel() * t.element_size() for t in d0.values() if t is not None)
@@ -316,6 +326,15 @@ def main():
 
     def step(i, ev=None):
         d, dout, plan = sets[i % n_sets]
+        if single:
+            if ev is not None:
+                ev[0].record(stream)
+                ev[1].record(stream)
+            plan.run()
+            if ev is not None:
+                ev[2].record(stream)
+                ev[3].record(stream)
+            return
         if ev is not None:
             ev[0].record(stream)
         plan.run_stage(0)
@@ -365,7 +384,7 @@ def main():
     flops = elements * cfg.dstate * FLOPS_PER_STATE_STEP
     scan_mean = float(np.mean(scan_ms))
     achieved_tflops = flops / (scan_mean * 1e-3) / 1e12
-    traffic = load_traffic(cfg.name)
+    traffic = load_traffic(cfg.name, scan_kernel_source_hash())
     hbm_gbps = step_bytes / (ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
@@ -394,6 +413,15 @@ def main():
                      "mix_peak": MIX_PEAK_TFLOPS, "frac_of_mix_peak": achieved_tflops / MIX_PEAK_TFLOPS,
                      "ms_per_launch": scan_mean, "launch_ms": stats(scan_ms), "flops_per_launch": flops},
     }
+    if single:
+        # one kernel moves exactly the fused minimum: x, delta, B, C (and z) in, out written
+        gbps = step_bytes / (scan_mean * 1e-3) / 1e9
+        res["roofline"] = {"kernel": "plane_fwd_kernel (cross-scan, the four route scans and the cross-merge; "
+                                     "one workgroup per plane)", "bound": "hbm",
+                           "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                           "traffic": load_traffic(cfg.name + ":plane", plane_kernel_source_hash()),
+                           "frac_of_copy": gbps / copy_gbps, "ms_per_launch": scan_mean,
+                           "launch_ms": stats(scan_ms), "bytes_per_launch": step_bytes}
     if front is not None:
         fb = front_bytes(cfg, False)
         f_ms = float(np.mean(stage0_ms))

@@ -267,8 +267,20 @@ typedef struct ss2d_fwd_args {
 
 int ss2d_fwd(const ss2d_fwd_args* args, hipStream_t stream);
 
+/* Whether ss2d_fwd(args) runs as one kernel per (image, channel) plane instead of the three
+ * stages below: 1 for dstate 1, 2 or 4 without the input front, the LayerNorm, the producer
+ * and keep_states, when height * width is a multiple of 8, the plane's LDS arrays
+ * (16 L' bytes, L' = L rounded up to 16) fit 63 KB and every I/O
+ * tensor is 16-byte aligned; 0 otherwise (also for invalid or empty arguments).  The single
+ * kernel reads x, delta, B, C and z once and writes only out (the workspace is unused); its
+ * result equals the staged one up to the order of the scan's roundings (the single kernel
+ * scans each route in parallel segments, the stages step by step).  Enqueues nothing. */
+int ss2d_fwd_single_kernel(const ss2d_fwd_args* args);
+
 /* One stage of ss2d_fwd, for callers that time or overlap the stages separately.
- * ss2d_fwd(args) == stage 0, then 1, then 2 on the same workspace:
+ * ss2d_fwd(args) == stage 0, then 1, then 2 on the same workspace (where
+ * ss2d_fwd_single_kernel(args) is 1, ss2d_fwd runs its one kernel instead, and the stages give
+ * its result up to rounding):
  *   stage 0 (SS2D_STAGE_TRANSPOSE): per-plane transpose of x into the workspace (feeds the
  *                                   column-major routes);
  *   stage 1 (SS2D_STAGE_SCAN):      the four route scans, fp32 route outputs into the workspace;

@@ -105,6 +105,8 @@ def lib():
         L.ss2d_proj_workspace_bytes.argtypes = [_i64] * 6 + [_int]
         L.ss2d_fwd_stage.restype = _int
         L.ss2d_fwd_stage.argtypes = [ctypes.POINTER(SS2DFwdArgs), _int, _p]
+        L.ss2d_fwd_single_kernel.restype = _int
+        L.ss2d_fwd_single_kernel.argtypes = [ctypes.POINTER(SS2DFwdArgs)]
         L.vim_bidir_workspace_bytes.restype = _sz
         L.vim_bidir_workspace_bytes.argtypes = [_i64] * 4 + [_int]
         L.vim_bidir_fwd_stage.restype = _int
@@ -366,6 +368,12 @@ class SS2DForwardPlan:
                                 layer_norm=_ln_on(layer_norm, ln_w, ln_b), ln_w=_ptr(ln_w), ln_b=_ptr(ln_b),
                                 ln_eps=float(ln_eps), x_proj_w=_ptr(x_proj_w), dt_proj_w=_ptr(dt_proj_w),
                                 dt_rank=R)
+
+    @property
+    def single_kernel(self) -> bool:
+        """Whether run() launches one kernel per plane (ss2d_fwd_single_kernel) instead of the
+        three stages of run_stage."""
+        return bool(lib().ss2d_fwd_single_kernel(ctypes.byref(self.args)))
 
     def run(self):
         _check(lib().ss2d_fwd(ctypes.byref(self.args), _stream(self.device)), "ss2d_fwd")

@@ -6,6 +6,7 @@
 #include "../../include/ss2d.h"
 #include "device_common.h"
 #include "internal.h"
+#include "plane_fwd.h"
 
 using namespace ss2d;
 
@@ -578,11 +579,44 @@ static int validate_ss2d_fwd(const ss2d_fwd_args* a, SS2DLayout* lay, bool* empt
   return SS2D_OK;
 }
 
+// The single-kernel path (small state sizes, plain SS2D: no front, LayerNorm, producer or
+// kept states), when its shape and alignment conditions hold.
+static bool plane_path(const ss2d_fwd_args* a, PlaneFwdArgs* p) {
+  if (a->conv_w || a->x_proj_w || a->layer_norm || a->keep_states) return false;
+  p->x = a->x;
+  p->delta = a->delta;
+  p->Bm = a->Bm;
+  p->Cm = a->Cm;
+  p->A = a->A;
+  p->Dskip = a->Dskip;
+  p->delta_bias = a->delta_bias;
+  p->z = a->z;
+  p->out = a->out;
+  p->batch = a->batch;
+  p->dim = a->dim;
+  p->H = a->height;
+  p->W = a->width;
+  p->N = int(a->dstate);
+  p->dtype = a->dtype;
+  p->softplus = a->delta_softplus ? 1 : 0;
+  return plane_fwd_supported(*p);
+}
+
+int ss2d_fwd_single_kernel(const ss2d_fwd_args* a) {
+  SS2DLayout lay;
+  bool empty;
+  if (validate_ss2d_fwd(a, &lay, &empty) != SS2D_OK || empty) return 0;
+  PlaneFwdArgs p{};
+  return plane_path(a, &p) ? 1 : 0;
+}
+
 int ss2d_fwd(const ss2d_fwd_args* a, hipStream_t stream) {
   SS2DLayout lay;
   bool empty;
   int st = validate_ss2d_fwd(a, &lay, &empty);
   if (st != SS2D_OK || empty) return st;
+  PlaneFwdArgs pa{};
+  if (plane_path(a, &pa)) return status_from(launch_plane_fwd(pa, stream));
   st = ss2d_transpose_stage(a, lay, stream);
   if (st == SS2D_OK) st = ss2d_scan_stage(a, lay, a->keep_states != 0, stream);
   if (st == SS2D_OK) st = ss2d_merge_stage(a, lay, stream);

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
             "ss2d_bwd", "ss2d_fwd_stage", "selective_scan_workspace_bytes", "ss2d_workspace_bytes",
             "ss2d_abi_version", "ss2d_status_string", "vim_bidir_workspace_bytes", "vim_bidir_fwd",
             "ss2d_proj_workspace_bytes",
-            "vim_bidir_fwd_stage", "vim_bidir_bwd", "selective_scan_step"} <= set(names)
+            "vim_bidir_fwd_stage", "vim_bidir_bwd", "selective_scan_step", "ss2d_fwd_single_kernel"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
     missing = [n for n in names if n not in exported]
@@ -160,6 +160,32 @@ def test_ss2d_rejects(lib):
     pb = {**b, "delta": 0, "Bm": 0, "Cm": 0, "ddelta": 0, "dBm": 0, "dCm": 0, "workspace_bytes": 1 << 40,
           "x_proj_w": 0xd000, "dt_proj_w": 0xe000, "dt_rank": 2}
     assert lib.ss2d_bwd(ctypes.byref(SS2DBwdArgs(**pb)), None) == 1                   # no weight gradients
+
+
+def test_ss2d_single_kernel_query(lib):
+    """Which ss2d_fwd calls run as one kernel per plane (host logic only, nothing enqueued)."""
+    from selective_scan_amd._binding import SS2DFwdArgs
+    f = dict(x=0x1000, delta=0x2000, A=0x3000, Bm=0x4000, Cm=0x5000, out=0x6000, workspace=0x10000,
+             workspace_bytes=1 << 40, batch=2, dim=4, height=8, width=8, dstate=1, dtype=1, delta_softplus=1)
+
+    def q(**kw):
+        return lib.ss2d_fwd_single_kernel(ctypes.byref(SS2DFwdArgs(**{**f, **kw})))
+
+    for n, want in ((1, 1), (2, 1), (4, 1), (3, 0), (8, 0), (16, 0)):
+        assert q(dstate=n) == want, n
+    assert q(dtype=0, z=0x7000, Dskip=0x8000, delta_bias=0x9000, delta_softplus=0) == 1
+    assert q(height=56, width=56) == 1
+    assert q(height=3, width=5) == 0          # L not a multiple of 8
+    assert q(height=64, width=64) == 0        # the plane's LDS arrays exceed 63 KB
+    assert q(x=0x1008) == 0                   # an I/O tensor not 16-byte aligned
+    assert q(z=0x7008) == 0
+    assert q(keep_states=1) == 0
+    assert q(layer_norm=1, ln_eps=1e-5) == 0
+    assert q(conv_w=0xd000, conv_k=3) == 0
+    assert q(delta=0, Bm=0, Cm=0, x_proj_w=0xd000, dt_proj_w=0xe000, dt_rank=2) == 0
+    assert q(workspace_bytes=1) == 0          # invalid arguments
+    assert q(height=0) == 0                   # empty map
+    assert q(dtype=3) == 0
 
 
 def test_vim_bidir_rejects(lib):

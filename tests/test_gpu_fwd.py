@@ -144,6 +144,41 @@ def test_ss2d_fwd(case):
     assert rel_err(to_f64(out), oracle.ss2d_fwd(**ref)) <= TOL[dtype]
 
 
+PLANE_CASES = [
+    # batch, H, W, dim, N, dtype, z, softplus, skip term
+    (2, 8, 8, 16, 1, "f32", True, True, True),
+    (1, 6, 12, 24, 2, "bf16", True, True, True),     # H != W
+    (2, 40, 40, 8, 4, "f32", True, True, True),      # N = 4: two segments of 1024 steps
+    (1, 56, 56, 6, 4, "bf16", True, True, True),     # four segments, the last one partial
+    (1, 56, 56, 6, 2, "f32", False, True, False),    # two segments of 2048, no gate, no skip term
+    (2, 12, 10, 20, 1, "bf16", True, False, True),   # delta used as given (no softplus)
+    (1, 24, 100, 4, 1, "f32", True, True, True),     # W > H
+]
+
+
+@pytest.mark.parametrize("case", PLANE_CASES, ids=[str(c) for c in PLANE_CASES])
+def test_ss2d_fwd_single_kernel(case):
+    """The one-kernel forward (state sizes 1, 2, 4): against the oracle, and against the three
+    staged kernels on the same inputs (they differ only in the order of the scan's roundings)."""
+    batch, H, W, dim, N, dtype, z, sp, skip = case
+    inp = synth.make_ss2d_inputs(batch, H, W, dim, N, dtype, has_z=z, seed_base=31 + H + W + N)
+    if not sp:  # without softplus, |delta_raw| and no bias keep every step a decay
+        inp["delta"] = inp["delta"] & np.uint16(0x7FFF) if dtype == "bf16" else np.abs(inp["delta"])
+    dev, ref = _ss2d_dev_ref(inp, dtype, z)
+    if not sp:
+        dev["delta_bias"] = ref["delta_bias"] = None
+    if not skip:
+        dev["D"] = ref["D"] = None
+    plan = ss.SS2DForwardPlan(**dev, delta_softplus=sp)
+    assert plan.single_kernel
+    out = plan.run().clone()
+    assert rel_err(to_f64(out), oracle.ss2d_fwd(**ref, delta_softplus=sp)) <= TOL[dtype]
+    for stage in (0, 1, 2):
+        plan.run_stage(stage)
+    # fp32: a few ulps of the scan; bf16: at most one rounding step of the output
+    assert rel_err(to_f64(out), to_f64(plan.out)) <= (1e-5 if dtype == "f32" else 8e-3)
+
+
 def test_ss2d_fwd_tiny_config():
     cfg = synth.CONFIGS[0]
     inp = synth.make_config_inputs(cfg)
