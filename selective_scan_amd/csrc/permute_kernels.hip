@@ -178,16 +178,20 @@ constexpr int kPlaneThreads = 256;
 
 // xT[b, c, w*H + h] = x[b, c, h*W + w]  (the column-major route order, not reversed).
 // Four consecutive linear indices per thread (L % 4 == 0); rows may wrap inside a group of four.
-template <typename W>
+// kMulti: `pp` consecutive planes per workgroup (small planes: one plane would leave most of the
+// workgroup idle); the planes are contiguous, and a quad never straddles two of them.
+template <typename W, bool kMulti>
 __global__ __launch_bounds__(kPlaneThreads) void transpose_plane_kernel(const W* __restrict__ x, W* __restrict__ xT,
-                                                                         int H, int Wd) {
+                                                                         int H, int Wd, int64_t planes, int pp) {
   extern __shared__ __align__(16) unsigned char smem[];
-  W* tile = reinterpret_cast<W*>(smem);  // [h][w], row stride Wd + 1
-  const int64_t L = int64_t(H) * Wd;
-  const W* xp = x + int64_t(blockIdx.x) * L;
-  W* op = xT + int64_t(blockIdx.x) * L;
-  const int ld = Wd + 1;
-  const int Li = int(L);  // the plane fits the LDS, so 32-bit indices suffice
+  W* tile = reinterpret_cast<W*>(smem);  // [plane][h][w], row stride Wd + 1
+  const int L = H * Wd;
+  const int64_t p0 = kMulti ? int64_t(blockIdx.x) * pp : int64_t(blockIdx.x);
+  const W* xp = x + p0 * L;
+  W* op = xT + p0 * L;
+  const int ld = Wd + 1, pls = H * ld;
+  // elements of this workgroup (they fit the LDS, so 32-bit indices suffice)
+  const int Li = kMulti ? int((planes - p0 < pp ? planes - p0 : pp) * L) : L;
   // read the plane in grid order: 4 consecutive pixels per thread, four loads issued before any
   // LDS write (a load used right away costs one round trip each); quads past the plane re-read
   // quad 0 and are not stored
@@ -210,10 +214,13 @@ __global__ __launch_bounds__(kPlaneThreads) void transpose_plane_kernel(const W*
       } else {
         v[0] = W(raw[e].x); v[1] = W(raw[e].y); v[2] = W(raw[e].z); v[3] = W(raw[e].w);
       }
+      // one division per index: the quad's pixels follow in row order (wrapping rows)
+      const int pl = kMulti ? q / L : 0, r = q - pl * L;
+      int h = r / Wd, w = r - h * Wd;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int h = (q + j) / Wd, w = (q + j) - h * Wd;
-        tile[h * ld + w] = v[j];
+        tile[pl * pls + h * ld + w] = v[j];
+        if (++w == Wd) { w = 0; ++h; }
       }
     }
   }
@@ -221,10 +228,12 @@ __global__ __launch_bounds__(kPlaneThreads) void transpose_plane_kernel(const W*
   // write in column-major order: t = w*H + h, 4 consecutive t per thread (L % 4 == 0)
   for (int t = 4 * int(threadIdx.x); t < Li; t += 4 * kPlaneThreads) {
     W v[4];
+    const int pl = kMulti ? t / L : 0, r = t - pl * L;
+    int w = r / H, h = r - w * H;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int w = (t + j) / H, h = (t + j) - w * H;
-      v[j] = tile[h * ld + w];
+      v[j] = tile[pl * pls + h * ld + w];
+      if (++h == H) { h = 0; ++w; }
     }
     if (sizeof(W) == 2) {
       uint2 raw;
@@ -273,11 +282,12 @@ __global__ __launch_bounds__(kPlaneThreads) void merge_plane_kernel(MergeArgs a)
       if (t >= L) break;
       const float a1[4] = {v1[e].x, v1[e].y, v1[e].z, v1[e].w};
       const float a3[4] = {v3[e].w, v3[e].z, v3[e].y, v3[e].x};  // pixel order t .. t+3
+      int w = t / H, h = t - w * H;  // one division; the quad's steps follow down the column
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int w = (t + j) / H, h = (t + j) - w * H;
         t1[w * ld + h] = a1[j];
         t3[w * ld + h] = a3[j];
+        if (++h == H) { h = 0; ++w; }
       }
     }
   }
@@ -306,12 +316,13 @@ __global__ __launch_bounds__(kPlaneThreads) void merge_plane_kernel(MergeArgs a)
       const float a0[4] = {v0[e].x, v0[e].y, v0[e].z, v0[e].w};
       const float a2[4] = {v2[e].w, v2[e].z, v2[e].y, v2[e].x};
       float v[4];
+      int h = p / Wd, w = p - h * Wd;  // one division; the quad's pixels follow along the row
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int h = (p + j) / Wd, w = (p + j) - h * Wd;
         float sum = a0[j] + t1[w * ld + h];
         sum = sum + a2[j];
         v[j] = sum + t3[w * ld + h];
+        if (++w == Wd) { w = 0; ++h; }
       }
       if constexpr (kSkip) {
         v[0] = fmaf(dsum, xv[e].x, v[0]); v[1] = fmaf(dsum, xv[e].y, v[1]);
@@ -360,11 +371,12 @@ __global__ __launch_bounds__(kPlaneThreads) void merge_gate_bwd_plane_kernel(Mer
       if (t >= L) break;
       const float a1[4] = {v1[e].x, v1[e].y, v1[e].z, v1[e].w};
       const float a3[4] = {v3[e].w, v3[e].z, v3[e].y, v3[e].x};
+      int w = t / H, h = t - w * H;  // one division; the quad's steps follow down the column
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int w = (t + j) / H, h = (t + j) - w * H;
         t1[w * ldc + h] = a1[j];
         t3[w * ldc + h] = a3[j];
+        if (++h == H) { h = 0; ++w; }
       }
     }
   }
@@ -397,9 +409,9 @@ __global__ __launch_bounds__(kPlaneThreads) void merge_gate_bwd_plane_kernel(Mer
       const float xs[4] = {xv[e].x, xv[e].y, xv[e].z, xv[e].w};
       const float zs[4] = {zv[e].x, zv[e].y, zv[e].z, zv[e].w}, gs[4] = {gv[e].x, gv[e].y, gv[e].z, gv[e].w};
       float dz[4], dm[4];
+      int h = p / Wd, w = p - h * Wd;  // one division; the quad's pixels follow along the row
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int h = (p + j) / Wd, w = (p + j) - h * Wd;
         float m = a0[j] + t1[w * ldc + h];
         m = m + a2[j];
         m = m + t3[w * ldc + h];
@@ -408,6 +420,7 @@ __global__ __launch_bounds__(kPlaneThreads) void merge_gate_bwd_plane_kernel(Mer
         dm[j] = gs[j] * zs[j] * sz;
         dz[j] = gs[j] * m * sz * (1.0f + zs[j] * (1.0f - sz));
         tm[h * ldr + w] = dm[j];
+        if (++w == Wd) { w = 0; ++h; }
       }
       *reinterpret_cast<float4*>(dmg + p) = make_float4(dm[0], dm[1], dm[2], dm[3]);
       Elem<T>::store4(dzg, p, make_float4(dz[0], dz[1], dz[2], dz[3]));
@@ -417,10 +430,11 @@ __global__ __launch_bounds__(kPlaneThreads) void merge_gate_bwd_plane_kernel(Mer
   float* dmt = a.dMT + plane * L;
   for (int t = 4 * int(threadIdx.x); t < L; t += kStep) {
     float v[4];
+    int w = t / H, h = t - w * H;  // one division; the quad's steps follow down the column
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int w = (t + j) / H, h = (t + j) - w * H;
       v[j] = tm[h * ldr + w];
+      if (++h == H) { h = 0; ++w; }
     }
     *reinterpret_cast<float4*>(dmt + t) = make_float4(v[0], v[1], v[2], v[3]);
   }
@@ -574,12 +588,28 @@ hipError_t launch_transpose(const void* x, void* xT, int64_t batch, int64_t C, i
   const size_t lds = size_t(H) * size_t(W + 1) * size_t(elem_bytes);
   const uintptr_t al = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(xT);
   if ((H * W) % 4 == 0 && lds <= 64 * 1024 && (al % (4 * elem_bytes)) == 0) {
-    if (elem_bytes == 2)
-      transpose_plane_kernel<uint16_t><<<dim3(uint32_t(planes)), dim3(kPlaneThreads), lds, s>>>(
-          static_cast<const uint16_t*>(x), static_cast<uint16_t*>(xT), int(H), int(W));
-    else
-      transpose_plane_kernel<uint32_t><<<dim3(uint32_t(planes)), dim3(kPlaneThreads), lds, s>>>(
-          static_cast<const uint32_t*>(x), static_cast<uint32_t*>(xT), int(H), int(W));
+    // planes of under 512 pixels: several per workgroup, about 2048 pixels in all
+    int pp = H * W < 512 ? int(2048 / (H * W)) : 1;
+    if (pp > 16) pp = 16;
+    while (pp > 1 && size_t(pp) * lds > 64 * 1024) --pp;
+    const int64_t blocks = (planes + pp - 1) / pp;
+    const dim3 g{uint32_t(blocks)}, b{kPlaneThreads};
+    const size_t l = size_t(pp) * lds;
+    if (elem_bytes == 2) {
+      const auto* xi = static_cast<const uint16_t*>(x);
+      auto* xo = static_cast<uint16_t*>(xT);
+      if (pp > 1)
+        transpose_plane_kernel<uint16_t, true><<<g, b, l, s>>>(xi, xo, int(H), int(W), planes, pp);
+      else
+        transpose_plane_kernel<uint16_t, false><<<g, b, l, s>>>(xi, xo, int(H), int(W), planes, 1);
+    } else {
+      const auto* xi = static_cast<const uint32_t*>(x);
+      auto* xo = static_cast<uint32_t*>(xT);
+      if (pp > 1)
+        transpose_plane_kernel<uint32_t, true><<<g, b, l, s>>>(xi, xo, int(H), int(W), planes, pp);
+      else
+        transpose_plane_kernel<uint32_t, false><<<g, b, l, s>>>(xi, xo, int(H), int(W), planes, 1);
+    }
     return hipGetLastError();
   }
   ScanOutputs o{};

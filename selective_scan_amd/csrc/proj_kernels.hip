@@ -424,20 +424,22 @@ __global__ __launch_bounds__(256) void cast_transpose_plane_kernel(const T* x, f
       if (q >= L) break;
       *reinterpret_cast<float4*>(fp + q) = v[e];
       const float a4[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
+      int h = q / W, w = q - h * W;  // one division; the quad's pixels follow along the row
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int h = (q + j) / W, w = (q + j) - h * W;
         tile[h * ld + w] = a4[j];
+        if (++w == W) { w = 0; ++h; }
       }
     }
   }
   __syncthreads();
   for (int t = 4 * int(threadIdx.x); t < L; t += kStep) {  // t = w * H + h
     float a4[4];
+    int w = t / H, h = t - w * H;  // one division; the quad's steps follow down the column
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int w = (t + j) / H, h = (t + j) - w * H;
       a4[j] = tile[h * ld + w];
+      if (++h == H) { h = 0; ++w; }
     }
     *reinterpret_cast<float4*>(tp + t) = make_float4(a4[0], a4[1], a4[2], a4[3]);
   }

@@ -1,7 +1,7 @@
 """The autograd wrappers (selective_scan_fn, ss2d, vim_bidir): the gradients autograd produces equal those of
 the direct backward calls (which recompute the forward instead of reusing its kept states), the
-outputs equal the direct forward's, absent optionals get no gradient, and one case is checked
-against the fp64 oracle."""
+outputs equal the direct forward's (up to the order of the scan's roundings), absent optionals get
+no gradient, and one case is checked against the fp64 oracle."""
 import numpy as np
 import pytest
 import torch
@@ -14,9 +14,9 @@ from selective_scan_amd import synth
 pytestmark = pytest.mark.gpu
 
 
-def _close(a, b, what):
+def _close(a, b, what, tol=1e-6):
     e = rel_err(to_f64(a), to_f64(b))
-    assert e <= 1e-6, (what, e)
+    assert e <= tol, (what, e)
 
 
 def _leaf(t):
@@ -83,7 +83,9 @@ def test_ss2d_autograd_matches_direct_backward(k, ln, proj):
     leaves = {key: _leaf(v) if isinstance(v, torch.Tensor) else v for key, v in t.items()}
     out = ss.ss2d(**leaves)
     out.backward(dout)
-    _close(out, ss.ss2d_fwd(**t), "out")
+    # (the direct forward of the plain case runs as one kernel per plane, whose route scans round
+    # in another order than the kept-states forward's)
+    _close(out, ss.ss2d_fwd(**t), "out", tol=1e-5)
     r = ss.ss2d_bwd(**t, dout=dout)
     for key, v in leaves.items():
         if not isinstance(v, torch.Tensor):

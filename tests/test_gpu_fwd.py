@@ -132,6 +132,8 @@ SS2D_CASES = [
     (1, 1, 1, 8, 4, "f32", True),       # single pixel
     (1, 3, 40, 64, 8, "bf16", True),
     (1, 64, 64, 64, 16, "f32", True),   # few rows: chunked
+    (1, 12, 12, 13, 16, "bf16", True),  # small planes, several per transpose workgroup (a partial one)
+    (2, 6, 10, 9, 16, "f32", True),     # the same in fp32: 16 planes per workgroup, then 2
 ]
 
 
