@@ -312,7 +312,7 @@ def main():
         Plan = (lambda **kw: ss.SS2DForwardPlan(**kw, keep_states=True)) if args.bwd else ss.SS2DForwardPlan
         backward = (lambda **kw: ss.ss2d_bwd(**kw, workspace_has_states=True))
     plan0 = Plan(**d0)
-    single = plan0.single_kernel  # the forward runs as one kernel per plane (small state sizes)
+    single = (not vim) and plan0.single_kernel  # the forward runs as one kernel per plane (small state sizes)
     # bytes one step touches in HBM (inputs, output, workspace): rotate independent copies
     # until one cycle over them exceeds three times the MALL
     footprint = sum(t.numel() * t.element_size() for t in d0.values() if t is not None)

@@ -251,9 +251,11 @@ __global__ __launch_bounds__(kPlaneThreads) void transpose_plane_kernel(const W*
 // skip term (kSkip), the gate (kZ) and an fp32 x (kXF32) are template parameters, and each loop
 // issues up to kMergeBatch iterations' loads before using any of them: a load behind a branch,
 // or used right away, costs a round trip of its own.
+// kThreads: 256, or 64 (one wavefront) for planes of up to 1024 pixels, which would leave most
+// of 256 threads idle.
 constexpr int kMergeBatch = 4;
-template <typename T, typename R, bool kSkip, bool kZ, bool kXF32>
-__global__ __launch_bounds__(kPlaneThreads) void merge_plane_kernel(MergeArgs a) {
+template <typename T, typename R, bool kSkip, bool kZ, bool kXF32, int kThreads>
+__global__ __launch_bounds__(kThreads) void merge_plane_kernel(MergeArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int H = int(a.H), Wd = int(a.W);
   const int L = H * Wd;                    // the plane fits the LDS: 32-bit indices
@@ -266,7 +268,7 @@ __global__ __launch_bounds__(kPlaneThreads) void merge_plane_kernel(MergeArgs a)
   const R* r1 = r0 + a.C * L;
   const R* r2 = r1 + a.C * L;
   const R* r3 = r2 + a.C * L;
-  constexpr int kStep = 4 * kPlaneThreads;
+  constexpr int kStep = 4 * kThreads;
   // routes 1 and 3 are in column-major order: t1[w][h] = r1[w*H + h], t3[w][h] = r3[L-1-(w*H + h)]
   for (int t0 = 4 * int(threadIdx.x); t0 < L; t0 += kStep * kMergeBatch) {
     float4 v1[kMergeBatch], v3[kMergeBatch];
@@ -509,12 +511,20 @@ hipError_t launch_route_scatter(const void* x, const ScanOutputs& o, int64_t bat
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 namespace {
+template <typename T, typename R, bool kSkip, bool kZ, int kThreads>
+void launch_merge_plane_t(const MergeArgs& a, dim3 g, size_t lds, hipStream_t s) {
+  const dim3 b{kThreads};
+  if (kSkip && a.x_f32)
+    merge_plane_kernel<T, R, kSkip, kZ, true, kThreads><<<g, b, lds, s>>>(a);
+  else
+    merge_plane_kernel<T, R, kSkip, kZ, false, kThreads><<<g, b, lds, s>>>(a);
+}
 template <typename T, typename R, bool kSkip, bool kZ>
 void launch_merge_plane_x(const MergeArgs& a, dim3 g, dim3 b, size_t lds, hipStream_t s) {
-  if (kSkip && a.x_f32)
-    merge_plane_kernel<T, R, kSkip, kZ, true><<<g, b, lds, s>>>(a);
+  if (b.x == 64)
+    launch_merge_plane_t<T, R, kSkip, kZ, 64>(a, g, lds, s);
   else
-    merge_plane_kernel<T, R, kSkip, kZ, false><<<g, b, lds, s>>>(a);
+    launch_merge_plane_t<T, R, kSkip, kZ, kPlaneThreads>(a, g, lds, s);
 }
 template <typename T, typename R>
 void launch_merge_plane(const MergeArgs& a, dim3 g, dim3 b, size_t lds, hipStream_t s) {
@@ -536,7 +546,7 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
                     : ((reinterpret_cast<uintptr_t>(a.y) | reinterpret_cast<uintptr_t>(a.x) |
                         reinterpret_cast<uintptr_t>(a.z)) & 7) == 0) &&
       (!a.x_f32 || aligned16(a.x)) && L % 4 == 0) {
-    const dim3 g{uint32_t(a.batch * a.C)}, b{kPlaneThreads};
+    const dim3 g{uint32_t(a.batch * a.C)}, b{L <= 1024 ? 64u : uint32_t(kPlaneThreads)};
     if (a.dtype == 0)
       launch_merge_plane<float, float>(a, g, b, plane_lds, s);
     else if (a.routes_f32)
