@@ -304,10 +304,11 @@ def main():
         d0.update(delta=None, B=None, C=None, x_proj_w=dev(proj["x_proj_w"], "f32"),
                   dt_proj_w=dev(proj["dt_proj_w"], "f32"))
     dout0 = dev(inp["dout"], cfg.dtype) if args.bwd else None
-    # with --bwd a step is a training step: for SS2D the forward keeps its checkpoint states and
-    # the backward runs on them (the Vim backward recomputes its forward)
+    # with --bwd a step is a training step: the forward keeps its checkpoint states and the
+    # backward runs on them
     if vim:
-        Plan, backward = ss.VimForwardPlan, ss.vim_bidir_bwd
+        Plan = (lambda **kw: ss.VimForwardPlan(**kw, keep_states=True)) if args.bwd else ss.VimForwardPlan
+        backward = (lambda **kw: ss.vim_bidir_bwd(**kw, workspace_has_states=True))
     else:
         Plan = (lambda **kw: ss.SS2DForwardPlan(**kw, keep_states=True)) if args.bwd else ss.SS2DForwardPlan
         backward = (lambda **kw: ss.ss2d_bwd(**kw, workspace_has_states=True))

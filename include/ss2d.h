@@ -387,6 +387,9 @@ typedef struct vim_bidir_fwd_args {
   int64_t batch, dim, seqlen, dstate;
   int dtype;
   int delta_softplus;
+  int keep_states;         /* nonzero: the workspace also keeps the direction outputs' checkpoint
+                              states, so that vim_bidir_bwd can run with workspace_has_states
+                              (a training forward) */
 } vim_bidir_fwd_args;
 
 int vim_bidir_fwd(const vim_bidir_fwd_args* args, hipStream_t stream);
@@ -403,8 +406,10 @@ int vim_bidir_fwd_stage(const vim_bidir_fwd_args* args, int stage, hipStream_t s
  *   dBm, dCm   : (batch, 2, dstate, L) dtype;
  *   dA         : (2, dim, dstate) fp32;  dDskip, ddelta_bias : (2, dim) fp32 (iff given);
  *   dz         : (batch, dim, L) dtype (iff z).
- * Everything is overwritten.  The forward is recomputed inside; the gradient reaching each
- * direction, dout * silu(z), is kept in fp32. */
+ * Everything is overwritten.  The forward is recomputed inside unless workspace_has_states is
+ * nonzero: then `workspace` must be the one a vim_bidir_fwd with keep_states used on the same
+ * inputs (its direction outputs and states are read, and the gradients are bit for bit those of
+ * the recomputing call).  The gradient reaching each direction, dout * silu(z), is kept in fp32. */
 typedef struct vim_bidir_bwd_args {
   const void* u;
   const void* delta;
@@ -428,6 +433,7 @@ typedef struct vim_bidir_bwd_args {
   int64_t batch, dim, seqlen, dstate;
   int dtype;
   int delta_softplus;
+  int workspace_has_states;
 } vim_bidir_bwd_args;
 
 int vim_bidir_bwd(const vim_bidir_bwd_args* args, hipStream_t stream);

@@ -69,14 +69,14 @@ class VimFwdArgs(ctypes.Structure):
     _fields_ = [(n, _p) for n in ("u", "delta", "A", "Bm", "Cm", "Dskip", "delta_bias", "z", "out",
                                   "workspace")] + [
         ("workspace_bytes", _sz), ("batch", _i64), ("dim", _i64), ("seqlen", _i64), ("dstate", _i64),
-        ("dtype", _int), ("delta_softplus", _int)]
+        ("dtype", _int), ("delta_softplus", _int), ("keep_states", _int)]
 
 
 class VimBwdArgs(ctypes.Structure):
     _fields_ = [(n, _p) for n in ("u", "delta", "A", "Bm", "Cm", "Dskip", "delta_bias", "z", "dout", "du",
                                   "ddelta", "dA", "dBm", "dCm", "dDskip", "ddelta_bias", "dz", "workspace")] + [
         ("workspace_bytes", _sz), ("batch", _i64), ("dim", _i64), ("seqlen", _i64), ("dstate", _i64),
-        ("dtype", _int), ("delta_softplus", _int)]
+        ("dtype", _int), ("delta_softplus", _int), ("workspace_has_states", _int)]
 
 
 _lib = None
@@ -449,10 +449,11 @@ def vim_bidir_workspace_bytes(batch, dim, seqlen, dstate, dtype: torch.dtype) ->
 class VimForwardPlan:
     """A prepared vim_bidir_fwd call (argument block, workspace and output kept alive).
     u, delta: (batch, 2, dim, L); A: (2, dim, N); B, C: (batch, 2, N, L); D, delta_bias: (2, dim);
-    z: (batch, dim, L)."""
+    z: (batch, dim, L).  With keep_states the workspace also keeps what
+    vim_bidir_bwd(..., workspace_has_states=True) needs."""
 
     def __init__(self, u, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=True, workspace=None,
-                 out=None):
+                 out=None, keep_states=False):
         u, delta = _c(u), _c(delta)
         self.device = _dev(u)
         B, C, z = _c(B), _c(C), _c(z)
@@ -471,7 +472,7 @@ class VimForwardPlan:
                                workspace=_ptr(self.workspace),
                                workspace_bytes=self.workspace.numel() * self.workspace.element_size(),
                                batch=batch, dim=dim, seqlen=L, dstate=N, dtype=_dtype_code(u.dtype),
-                               delta_softplus=int(bool(delta_softplus)))
+                               delta_softplus=int(bool(delta_softplus)), keep_states=int(bool(keep_states)))
 
     def run(self):
         _check(lib().vim_bidir_fwd(ctypes.byref(self.args), _stream(self.device)), "vim_bidir_fwd")
@@ -483,14 +484,19 @@ class VimForwardPlan:
         return self.out
 
 
-def vim_bidir_fwd(u, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=True, workspace=None):
-    """Bidirectional (Vision Mamba) scan forward; returns out (batch, dim, L)."""
-    return VimForwardPlan(u, delta, A, B, C, D, delta_bias, z, delta_softplus, workspace).run()
+def vim_bidir_fwd(u, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=True, workspace=None,
+                  keep_states=False):
+    """Bidirectional (Vision Mamba) scan forward; returns out (batch, dim, L).  With keep_states the
+    given workspace keeps what vim_bidir_bwd(..., workspace_has_states=True) needs."""
+    return VimForwardPlan(u, delta, A, B, C, D, delta_bias, z, delta_softplus, workspace,
+                          keep_states=keep_states).run()
 
 
 def vim_bidir_bwd(u, delta, A, B, C, D=None, delta_bias=None, z=None, dout=None, delta_softplus=True,
-                  workspace=None):
-    """Backward of vim_bidir_fwd; returns a dict of gradients (None for absent inputs)."""
+                  workspace=None, workspace_has_states=False):
+    """Backward of vim_bidir_fwd; returns a dict of gradients (None for absent inputs).  With
+    workspace_has_states, `workspace` must be the one a forward with keep_states=True used for the
+    same inputs (the forward is then not recomputed)."""
     u, delta, dout = _c(u), _c(delta), _c(dout)
     dev = _dev(u)
     B, C, z = _c(B), _c(C), _c(z)
@@ -512,7 +518,10 @@ def vim_bidir_bwd(u, delta, A, B, C, D=None, delta_bias=None, z=None, dout=None,
                    delta_bias=_ptr(delta_bias), z=_ptr(z), dout=_ptr(dout), du=_ptr(du), ddelta=_ptr(ddelta),
                    dA=_ptr(dA), dBm=_ptr(dB), dCm=_ptr(dC), dDskip=_ptr(dD), ddelta_bias=_ptr(dbias), dz=_ptr(dz),
                    workspace=_ptr(ws), workspace_bytes=ws.numel() * ws.element_size(), batch=batch, dim=dim,
-                   seqlen=L, dstate=N, dtype=_dtype_code(u.dtype), delta_softplus=int(bool(delta_softplus)))
+                   seqlen=L, dstate=N, dtype=_dtype_code(u.dtype), delta_softplus=int(bool(delta_softplus)),
+                   workspace_has_states=int(bool(workspace_has_states)))
+    if workspace_has_states and workspace is None:
+        raise SS2DError("workspace_has_states needs the forward's workspace")
     _check(lib().vim_bidir_bwd(ctypes.byref(a), _stream(dev)), "vim_bidir_bwd")
     return {"du": du, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "ddelta_bias": dbias, "dz": dz}
 

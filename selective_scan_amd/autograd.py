@@ -5,10 +5,9 @@ and principle", section 2: `SelectiveScanFn`): u, delta, A, B, C, D=None, z=None
 delta_bias=None, delta_softplus=False, return_last_state=False; B and C may be 3-D (one group);
 the gradient of last_state is not propagated; gradients of absent optionals are None.  `ss2d`
 is the fused SS2D op (ss2d_fwd / ss2d_bwd) with its optional input front, LayerNorm and Δ/B/C
-producer; `vim_bidir` is Vision Mamba's two-direction scan (vim_bidir_fwd / vim_bidir_bwd).  The
-selective_scan_fn and ss2d forwards keep their checkpoint states in a workspace that the backward
-reuses, so their backward does not recompute the forward; vim_bidir's backward recomputes it.
-Every step runs in the library's kernels.
+producer; `vim_bidir` is Vision Mamba's two-direction scan (vim_bidir_fwd / vim_bidir_bwd).  Each
+forward keeps its checkpoint states in a workspace that its backward reuses, so the backward does
+not recompute the forward.  Every step runs in the library's kernels.
 """
 from __future__ import annotations
 
@@ -87,15 +86,21 @@ class VimBidirFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, delta_softplus, *tensors):
         kw = dict(zip(_VIM_KEYS, tensors))
-        out = _bind.vim_bidir_fwd(**kw, delta_softplus=delta_softplus)
-        ctx.save_for_backward(*tensors)
+        u, A = kw["u"], kw["A"]
+        batch, _, dim, L = u.shape
+        ws = torch.empty(_bind.vim_bidir_workspace_bytes(batch, dim, L, A.shape[-1], u.dtype), dtype=torch.uint8,
+                         device=u.device)
+        out = _bind.vim_bidir_fwd(**kw, delta_softplus=delta_softplus, workspace=ws, keep_states=True)
+        ctx.save_for_backward(*tensors, ws)
         ctx.delta_softplus = delta_softplus
         return out
 
     @staticmethod
     def backward(ctx, dout):
-        kw = dict(zip(_VIM_KEYS, ctx.saved_tensors))
-        g = _bind.vim_bidir_bwd(**kw, dout=dout, delta_softplus=ctx.delta_softplus)
+        *tensors, ws = ctx.saved_tensors
+        kw = dict(zip(_VIM_KEYS, tensors))
+        g = _bind.vim_bidir_bwd(**kw, dout=dout, delta_softplus=ctx.delta_softplus, workspace=ws,
+                                workspace_has_states=True)
         return (None,) + tuple(g[k] for k in _VIM_GRADS)
 
 

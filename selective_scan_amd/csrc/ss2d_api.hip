@@ -1201,7 +1201,7 @@ static int vim_merge_stage(const vim_bidir_fwd_args* a, const VimLayout& lay, hi
 static int vim_scan_stage(const vim_bidir_fwd_args* a, const VimLayout& lay, hipStream_t stream) {
   const ss_fwd_args f = vim_scan_args(a->u, a->delta, a->A, a->Bm, a->Cm, a->Dskip, a->delta_bias, a->workspace, lay,
                                       a->batch, a->dim, a->seqlen, a->dstate, a->dtype, a->delta_softplus);
-  return scan_fwd_impl(&f, false, stream, true);
+  return scan_fwd_impl(&f, a->keep_states != 0, stream, true);
 }
 
 int vim_bidir_fwd(const vim_bidir_fwd_args* a, hipStream_t stream) {
@@ -1249,11 +1249,13 @@ int vim_bidir_bwd(const vim_bidir_bwd_args* a, hipStream_t stream) {
   if (a->batch * 2 * lay.scan.dblocks * lay.scan.bwd_n_chunks > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
   const int64_t L = a->seqlen;
 
-  // forward again: direction outputs and checkpoint states
-  const ss_fwd_args f = vim_scan_args(a->u, a->delta, a->A, a->Bm, a->Cm, a->Dskip, a->delta_bias, a->workspace, lay,
-                                      a->batch, a->dim, L, a->dstate, a->dtype, a->delta_softplus);
-  st = scan_fwd_impl(&f, true, stream, true);
-  if (st != SS2D_OK) return st;
+  // forward again, unless a training forward left them: direction outputs and checkpoint states
+  if (!a->workspace_has_states) {
+    const ss_fwd_args f = vim_scan_args(a->u, a->delta, a->A, a->Bm, a->Cm, a->Dskip, a->delta_bias, a->workspace,
+                                        lay, a->batch, a->dim, L, a->dstate, a->dtype, a->delta_softplus);
+    st = scan_fwd_impl(&f, true, stream, true);
+    if (st != SS2D_OK) return st;
+  }
 
   // gate: dz, and the fp32 gradient reaching each direction in its own order
   BidirArgs g{};

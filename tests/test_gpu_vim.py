@@ -114,6 +114,26 @@ def test_vim_bidir_bwd(case):
         assert e <= tol, (k, e)
 
 
+@pytest.mark.parametrize("case", [(2, 197, 40, 16, "bf16", True, True, True), (1, 1024, 32, 16, "f32", True, True, True),
+                                  (2, 33, 24, 4, "f32", False, False, True)], ids=str)
+def test_vim_bidir_bwd_reuses_forward_states(case):
+    """A training forward (keep_states) then the backward on its workspace: the output of the plain
+    forward and, bit for bit, the gradients of the backward that recomputes the forward (the
+    chunked case included)."""
+    batch, L, dim, N, dtype, z, D, bias = case
+    dev, _, dout, _ = _vim(batch, L, dim, N, dtype, z, seed=140 + L, with_D=D, with_bias=bias, dout=True)
+    ws = torch.empty(ss.vim_bidir_workspace_bytes(batch, dim, L, N, dev["u"].dtype), dtype=torch.uint8, device="cuda")
+    out = ss.vim_bidir_fwd(**dev, workspace=ws, keep_states=True)
+    assert torch.equal(out, ss.vim_bidir_fwd(**dev))
+    g = ss.vim_bidir_bwd(**dev, dout=dout, workspace=ws, workspace_has_states=True)
+    g2 = ss.vim_bidir_bwd(**dev, dout=dout)
+    for k in GRADS:
+        if g2[k] is None:
+            assert g[k] is None, k
+            continue
+        assert torch.equal(g[k], g2[k]), k
+
+
 def test_vim_bidir_bwd_full_config_sliced():
     """Vim-Tiny (B=128, L=197, D=384, N=16, bf16) forward+backward at full size, checked on oracle
     slices: per-element gradients of sampled (batch, channel) rows; dA, dD, ddelta_bias of a
