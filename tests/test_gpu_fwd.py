@@ -155,6 +155,9 @@ PLANE_CASES = [
     (1, 56, 56, 6, 2, "f32", False, True, False),    # two segments of 2048, no gate, no skip term
     (2, 12, 10, 20, 1, "bf16", True, False, True),   # delta used as given (no softplus)
     (1, 24, 100, 4, 1, "f32", True, True, True),     # W > H
+    (2, 1, 16, 8, 2, "bf16", True, True, True),      # one row: the column routes equal the row routes
+    (1, 8, 1, 8, 1, "f32", True, True, True),        # one column
+    (3, 8, 8, 5, 4, "f32", False, True, True),       # 15 planes (not a multiple of the 8 XCDs), L = 64
 ]
 
 
