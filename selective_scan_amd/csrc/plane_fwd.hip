@@ -47,6 +47,8 @@ __device__ __forceinline__ int swz(int i) {
   const int q = i >> 2;
   return ((q ^ ((q >> 4) & 3)) << 2) | (i & 3);
 }
+// the layout permutes within groups of 64 words, so a step of 256 words maps to itself:
+// swz(i + 256) == swz(i) + 256
 
 // n (4 or 8) consecutive elements from a 16-byte aligned (8-byte for 4 bf16) position
 template <typename T>
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(kPT) void plane_fwd_kernel(const PlaneFwdArgs a) {
   __syncthreads();
   {  // column-major index t is pixel (h, w) = (t % H, t / H)
     DivWalk dw(tid, kPT, H);
-    for (int t = tid; t < L; t += kPT, dw.next()) sxT[swz(t)] = sxR[swz(dw.r * Wd + dw.q)];
+    for (int t = tid, st = swz(tid); t < L; t += kPT, st += kPT, dw.next()) sxT[st] = sxR[swz(dw.r * Wd + dw.q)];
   }
   // (route 0's segment barrier orders these writes before route 1 reads them)
 
@@ -276,7 +278,7 @@ __global__ __launch_bounds__(kPT) void plane_fwd_kernel(const PlaneFwdArgs a) {
     if constexpr (kCol) {  // fold into the sum, pixel p = (h, w) <- column-major index w H + h
       __syncthreads();
       DivWalk dw(tid, kPT, Wd);
-      for (int p = tid; p < L; p += kPT, dw.next()) sacc[swz(p)] += syb[swz(dw.r * H + dw.q)];
+      for (int p = tid, sp = swz(tid); p < L; p += kPT, sp += kPT, dw.next()) sacc[sp] += syb[swz(dw.r * H + dw.q)];
       // (the next route's segment barrier orders this fold before the sum or syb is rewritten)
     }
   };
