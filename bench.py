@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=1,
-                    help="index into synth.CONFIGS + synth.VIM_CONFIGS (default 1: SS2D stage-1; 5: Vim-Tiny)")
+                    help="workload: 0 tiny, 1 SS2D stage-1 (default), 2 stage-3, 3 low-state, 4 high-res, 5 Vim-Tiny")
     ap.add_argument("--bwd", action="store_true", help="time forward + backward per step")
     ap.add_argument("--front", type=int, default=0,
                     help="SS2D only: K > 0 adds the input front (depthwise K x K convolution + SiLU)")
@@ -274,7 +274,7 @@ def main():
     import selective_scan_amd as ss
     from selective_scan_amd import synth
 
-    workloads = list(synth.CONFIGS) + list(synth.VIM_CONFIGS)
+    workloads = list(synth.WORKLOADS) + list(synth.VIM_WORKLOADS)
     cfg = workloads[args.workload]
     vim = getattr(cfg, "kind", "ss2d") == "vim"
     if (args.front or args.ln or args.proj) and vim:

@@ -47,13 +47,14 @@ class SS2DConfig:
 # The five workloads: VMamba stage grids at 224^2 input (56^2 stage 1, 14^2 stage 3),
 # channels D = 2 x embedding dim (96/192/384/768), d_state 16, and the stage-1 grid of
 # a 512^2 segmentation input (128^2).
-CONFIGS = [
+WORKLOADS = [
     SS2DConfig("tiny_8x8_d16_n4_f32", 1, 8, 8, 16, 4, "f32", True, 0),
     SS2DConfig("stage1_56x56_b128_d192_n16_bf16", 128, 56, 56, 192, 16, "bf16", True, 1),
     SS2DConfig("stage3_14x14_b128_d768_n16_bf16", 128, 14, 14, 768, 16, "bf16", True, 2),
     SS2DConfig("lowstate_56x56_b128_d96_n1_bf16_noz", 128, 56, 56, 96, 1, "bf16", False, 3),
     SS2DConfig("highres_128x128_b4_d192_n16_f32", 4, 128, 128, 192, 16, "f32", True, 4, True),
 ]
+TINY, STAGE1, STAGE3, LOWSTATE, HIGHRES = WORKLOADS
 
 
 @dataclass(frozen=True)
@@ -78,9 +79,10 @@ class VimConfig:
 
 # Vim-Tiny at 224^2: 14 x 14 patches of 16^2 plus the class token (L = 197), embedding 192,
 # expand 2 (D = 384), d_state 16, batch 128.
-VIM_CONFIGS = [
+VIM_WORKLOADS = [
     VimConfig("vim_tiny_l197_b128_d384_n16_bf16", 128, 197, 384, 16, "bf16", True, 5, True),
 ]
+(VIM_TINY,) = VIM_WORKLOADS
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:

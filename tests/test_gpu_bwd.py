@@ -138,7 +138,7 @@ def test_ss2d_bwd_reuses_forward_states(case):
 
 
 def test_ss2d_bwd_tiny_config():
-    cfg = synth.CONFIGS[0]
+    cfg = synth.TINY
     dev, ref, dout, dout64 = _ss2d(cfg.batch, cfg.height, cfg.width, cfg.dim, cfg.dstate, cfg.dtype, cfg.has_z,
                                    seed=cfg.index)
     g = ss.ss2d_bwd(**dev, dout=dout)
@@ -150,7 +150,7 @@ def test_ss2d_bwd_tiny_config():
 def test_ss2d_bwd_highres_config_full():
     """The high-resolution workload (128x128, B=4, D=192, N=16, fp32) at full size against the
     oracle's full fp64 gradients, in the launch configuration the benchmark uses."""
-    cfg = synth.CONFIGS[4]
+    cfg = synth.HIGHRES
     inp = synth.make_config_inputs(cfg, with_dout=True)
     dev = dict(x=to_dev(inp["x"], "f32"), delta=to_dev(inp["delta"], "f32"), A=to_dev(inp["A"], "f32"),
                B=to_dev(inp["B"], "f32"), C=to_dev(inp["C"], "f32"), D=to_dev(inp["D"], "f32"),
@@ -170,7 +170,7 @@ def test_ss2d_bwd_stage1_full_size_training_path():
     can compute from slices: per-element gradients (dx, ddelta, dz) on sampled (image, channel)
     planes; dA, dD, ddelta_bias of sampled channels from all images; dB, dC of a sampled image
     from all its channels."""
-    cfg = synth.CONFIGS[1]
+    cfg = synth.STAGE1
     inp = synth.make_config_inputs(cfg, with_dout=True)
     dt = cfg.dtype
     dev = dict(x=to_dev(inp["x"], dt), delta=to_dev(inp["delta"], dt), A=to_dev(inp["A"], "f32"),

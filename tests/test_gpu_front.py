@@ -102,7 +102,7 @@ def test_ss2d_front_stage1_full_size_sampled():
     """Stage-1 (B=128, 56x56, D=192, N=16, bf16) with a 3 x 3 front at full size, training launch
     configuration.  The front is per channel, so the oracle checks (image, channel) planes of the
     output and of dx, ddelta, dz, and one channel's filter gradients over all images."""
-    cfg = synth.CONFIGS[1]
+    cfg = synth.STAGE1
     inp = synth.make_config_inputs(cfg, with_dout=True)
     fp = synth.make_front_params(cfg.dim, 3, seed_base=cfg.index)
     dt = cfg.dtype

@@ -185,7 +185,7 @@ def test_ss2d_fwd_single_kernel(case):
 
 
 def test_ss2d_fwd_tiny_config():
-    cfg = synth.CONFIGS[0]
+    cfg = synth.TINY
     inp = synth.make_config_inputs(cfg)
     dev, ref = _ss2d_dev_ref(inp, cfg.dtype, cfg.has_z)
     out = ss.ss2d_fwd(**dev)
@@ -200,17 +200,16 @@ def _slice_ref(ref, b, d):
                 z=None if ref["z"] is None else ref["z"][b:b + 1, d:d + 1])
 
 
-@pytest.mark.parametrize("cfg_index", [1, 2, 3, 4])
-def test_ss2d_fwd_full_config_sampled(cfg_index):
+@pytest.mark.parametrize("cfg", [synth.STAGE1, synth.STAGE3, synth.LOWSTATE, synth.HIGHRES], ids=lambda c: c.name)
+def test_ss2d_fwd_full_config_sampled(cfg):
     """Full-size run in the benchmark's launch configuration; oracle on sampled planes."""
-    cfg = synth.CONFIGS[cfg_index]
     inp = synth.make_config_inputs(cfg, with_dout=False)
     dev = dict(x=to_dev(inp["x"], cfg.dtype), delta=to_dev(inp["delta"], cfg.dtype), A=to_dev(inp["A"], "f32"),
                B=to_dev(inp["B"], cfg.dtype), C=to_dev(inp["C"], cfg.dtype), D=to_dev(inp["D"], "f32"),
                delta_bias=to_dev(inp["delta_bias"], "f32"), z=to_dev(inp["z"], cfg.dtype) if cfg.has_z else None)
     out = ss.ss2d_fwd(**dev)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(cfg_index)
+    rng = np.random.default_rng(cfg.index)
     planes = [(0, 0), (cfg.batch - 1, cfg.dim - 1)] + [
         (int(rng.integers(cfg.batch)), int(rng.integers(cfg.dim))) for _ in range(4)]
     ref_full = dict(x=inp["x"], delta=inp["delta"], A=inp["A"], B=inp["B"], C=inp["C"], D=inp["D"],

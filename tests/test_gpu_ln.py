@@ -114,7 +114,7 @@ def test_ss2d_ln_stage1_full_size_image_slices():
     """Stage-1 (B=128, 56x56, D=192, N=16, bf16) with the LayerNorm and the gate at full size,
     training launch configuration.  The normalisation couples the channels of a pixel, so the
     oracle checks whole images: the output and dx, ddelta, dz, dB, dC of sampled images."""
-    cfg = synth.CONFIGS[1]
+    cfg = synth.STAGE1
     inp = synth.make_config_inputs(cfg, with_dout=True)
     dt = cfg.dtype
     rng = np.random.default_rng(41)

@@ -102,7 +102,7 @@ def test_ss2d_proj_stage1_full_size_image_slices():
     """Stage-1 (B=128, 56x56, D=192, N=16, dt_rank 6, bf16) with the producer, the 3x3 front and the
     LayerNorm at full size, training launch configuration.  The projections mix a pixel's channels,
     so the oracle checks whole images: the output, dx and dz of sampled images."""
-    cfg = synth.CONFIGS[1]
+    cfg = synth.STAGE1
     inp = synth.make_config_inputs(cfg, with_dout=True)
     R = 6
     pw = synth.make_proj_params(cfg.dim, cfg.dstate, R, seed_base=cfg.index)
@@ -142,7 +142,7 @@ def test_ss2d_proj_stage3_full_size_rank24():
     its own product), training launch configuration: the output, dx and dz of sampled images
     against the oracle; the weight gradients, sums over all images, equal the sums of those of
     the two half batches (whose slices group the images' steps differently), to fp32 rounding."""
-    cfg = synth.CONFIGS[2]
+    cfg = synth.STAGE3
     inp = synth.make_config_inputs(cfg, with_dout=True)
     R = 24
     pw = synth.make_proj_params(cfg.dim, cfg.dstate, R, seed_base=cfg.index)

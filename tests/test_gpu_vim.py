@@ -67,7 +67,7 @@ def test_vim_bidir_stages_equal_fused():
 def test_vim_bidir_fwd_full_config_sampled():
     """Full Vim-Tiny size in the benchmark's launch configuration; oracle on sampled (batch, channel)
     rows (each takes both directions of its channel)."""
-    cfg = synth.VIM_CONFIGS[0]
+    cfg = synth.VIM_TINY
     inp = synth.make_vim_config_inputs(cfg, with_dout=False)
     dev = dict(u=to_dev(inp["u"], cfg.dtype), delta=to_dev(inp["delta"], cfg.dtype), A=to_dev(inp["A"], "f32"),
                B=to_dev(inp["B"], cfg.dtype), C=to_dev(inp["C"], cfg.dtype), D=to_dev(inp["D"], "f32"),
@@ -138,7 +138,7 @@ def test_vim_bidir_bwd_full_config_sliced():
     """Vim-Tiny (B=128, L=197, D=384, N=16, bf16) forward+backward at full size, checked on oracle
     slices: per-element gradients of sampled (batch, channel) rows; dA, dD, ddelta_bias of a
     sampled channel from all sequences; dB, dC of a sampled sequence from all its channels."""
-    cfg = synth.VIM_CONFIGS[0]
+    cfg = synth.VIM_TINY
     inp = synth.make_vim_config_inputs(cfg, with_dout=True)
     dt = cfg.dtype
     dev = dict(u=to_dev(inp["u"], dt), delta=to_dev(inp["delta"], dt), A=to_dev(inp["A"], "f32"),
