@@ -175,6 +175,7 @@ def test_ss2d_single_kernel_query(lib):
         assert q(dstate=n) == want, n
     assert q(dtype=0, z=0x7000, Dskip=0x8000, delta_bias=0x9000, delta_softplus=0) == 1
     assert q(height=56, width=56) == 1
+    assert q(height=63, width=64) == 1        # L = 4032: the largest plane within 63 KB
     assert q(height=3, width=5) == 0          # L not a multiple of 8
     assert q(height=64, width=64) == 0        # the plane's LDS arrays exceed 63 KB
     assert q(x=0x1008) == 0                   # an I/O tensor not 16-byte aligned

@@ -158,6 +158,8 @@ PLANE_CASES = [
     (2, 1, 16, 8, 2, "bf16", True, True, True),      # one row: the column routes equal the row routes
     (1, 8, 1, 8, 1, "f32", True, True, True),        # one column
     (3, 8, 8, 5, 4, "f32", False, True, True),       # 15 planes (not a multiple of the 8 XCDs), L = 64
+    (1, 63, 64, 3, 1, "bf16", True, True, True),     # the largest plane the LDS holds (L = 4032): 252 threads
+    (1, 64, 63, 2, 4, "f32", True, True, True),      # the same at N = 4: four segments, the last one partial
 ]
 
 
