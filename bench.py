@@ -44,6 +44,9 @@ CLOCK_HZ = 2.4e9
 SIMDS = 256 * 4  # 256 CUs x 4 SIMDs, 16 fp32 lanes each
 # fp32 vector peak without packed math: 1024 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz
 VALU_PEAK_TFLOPS = SIMDS * 16 * 2 * CLOCK_HZ / 1e12
+# the published fp32 vector peak counts packed-FP32 instructions (two lanes' FMAs in one), which
+# this library does not issue; reported beside the peak above for reference
+PUBLISHED_FP32_VECTOR_TFLOPS = 157.3
 # Per (element, state) the scan issues 4 full-rate VALU ops (Lam*A, (Lam*u)*B, the FMA into
 # h, the FMA into y: 7 flops counting the exp as one) and one v_exp_f32.  A wave64 VALU op
 # occupies a 16-lane SIMD for 4 cycles, a transcendental for 8, so 64 state-steps cost
@@ -412,6 +415,8 @@ def main():
                      "achieved": achieved_tflops, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved_tflops / VALU_PEAK_TFLOPS, "traffic": traffic,
                      "mix_peak": MIX_PEAK_TFLOPS, "frac_of_mix_peak": achieved_tflops / MIX_PEAK_TFLOPS,
+                     "published_fp32_vector_peak": PUBLISHED_FP32_VECTOR_TFLOPS,
+                     "frac_of_published_peak": achieved_tflops / PUBLISHED_FP32_VECTOR_TFLOPS,
                      "ms_per_launch": scan_mean, "launch_ms": stats(scan_ms), "flops_per_launch": flops},
     }
     if single:
