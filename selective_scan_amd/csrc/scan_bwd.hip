@@ -45,25 +45,42 @@ __global__ __launch_bounds__(256) void reduce_bc_kernel(const BwdReduceArgs a) {
   Elem<T>::store(static_cast<T*>(a.dC), o, sc);
 }
 
+// 64 outputs per workgroup (dA entries, then (dD, dbias) pairs); its four wavefronts take every
+// fourth image, and their sums are added in a fixed order, so the result is deterministic.
 __global__ __launch_bounds__(256) void reduce_params_kernel(const BwdReduceArgs a) {
-  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t rows = a.batch * a.dim;
-  if (i < a.dim * a.N) {
+  __shared__ float red[4][kWave][2];
+  const int lane = int(threadIdx.x) % kWave, w = int(threadIdx.x) / kWave;
+  const int64_t i = int64_t(blockIdx.x) * kWave + lane;
+  const int64_t rows = a.batch * a.dim, nA = a.dim * a.N;
+  float s0 = 0.0f, s1 = 0.0f;
+  if (i < nA) {
     const int64_t d = i / a.N, n = i % a.N;
-    float s = 0.0f;
-    for (int c = 0; c < a.n_chunks; ++c)
-      for (int64_t b = 0; b < a.batch; ++b) s += a.dA_part[(int64_t(c) * rows + b * a.dim + d) * a.N + n];
-    a.dA[i] = s * kLn2;  // dA terms were formed with delta / ln 2
-  } else if (i < a.dim * a.N + a.dim) {
-    const int64_t d = i - a.dim * a.N;
-    float sd = 0.0f, sb = 0.0f;
-    for (int c = 0; c < a.n_chunks; ++c)
-      for (int64_t b = 0; b < a.batch; ++b) {
-        sd += a.dD_part[int64_t(c) * rows + b * a.dim + d];
-        sb += a.dbias_part[int64_t(c) * rows + b * a.dim + d];
+    for (int c = 0; c < a.n_chunks; ++c) {
+#pragma unroll 4
+      for (int64_t b = w; b < a.batch; b += 4) s0 += a.dA_part[(int64_t(c) * rows + b * a.dim + d) * a.N + n];
+    }
+  } else if (i < nA + a.dim) {
+    const int64_t d = i - nA;
+    for (int c = 0; c < a.n_chunks; ++c) {
+#pragma unroll 4
+      for (int64_t b = w; b < a.batch; b += 4) {
+        s0 += a.dD_part[int64_t(c) * rows + b * a.dim + d];
+        s1 += a.dbias_part[int64_t(c) * rows + b * a.dim + d];
       }
-    if (a.dD) a.dD[d] = sd;
-    if (a.dbias) a.dbias[d] = sb;
+    }
+  }
+  red[w][lane][0] = s0;
+  red[w][lane][1] = s1;
+  __syncthreads();
+  if (w != 0) return;
+  const float t0 = (red[0][lane][0] + red[1][lane][0]) + (red[2][lane][0] + red[3][lane][0]);
+  const float t1 = (red[0][lane][1] + red[1][lane][1]) + (red[2][lane][1] + red[3][lane][1]);
+  if (i < nA) {
+    a.dA[i] = t0 * kLn2;  // dA terms were formed with delta / ln 2
+  } else if (i < nA + a.dim) {
+    const int64_t d = i - nA;
+    if (a.dD) a.dD[d] = t0;
+    if (a.dbias) a.dbias[d] = t1;
   }
 }
 
@@ -102,7 +119,7 @@ hipError_t launch_bwd_reduce(const BwdReduceArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int64_t np = a.dim * a.N + a.dim;
-  if (np > 0) reduce_params_kernel<<<dim3(uint32_t((np + 255) / 256)), dim3(256), 0, s>>>(a);
+  if (np > 0) reduce_params_kernel<<<dim3(uint32_t((np + kWave - 1) / kWave)), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 
