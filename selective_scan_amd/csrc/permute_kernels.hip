@@ -446,13 +446,26 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Two-direction merge: one thread per element of the (batch, C, L) output; direction 1 is read
 // at L-1-l, so consecutive threads read consecutive (descending) addresses of it.
+// element i of (batch, C, L) -> row = b C + c and position l: 32-bit divisions when every index
+// fits (a 64-bit division costs several times as many instructions)
+__device__ __forceinline__ void row_of(const BidirArgs& a, int64_t i, int64_t& row, int64_t& l, int64_t& b,
+                                       int64_t& c) {
+  if (a.batch * a.C * a.L <= 0xffffffffLL) {
+    const uint32_t ii = uint32_t(i), L = uint32_t(a.L), C = uint32_t(a.C);
+    const uint32_t r = ii / L, bb = r / C;
+    row = r; l = ii - r * L; b = bb; c = r - bb * C;
+  } else {
+    row = i / a.L; l = i - row * a.L; b = row / a.C; c = row - b * a.C;
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void bidir_merge_kernel(BidirArgs a) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t n = a.batch * a.C * a.L;
   if (i >= n) return;
-  const int64_t row = i / a.L, l = i % a.L;
-  const int64_t b = row / a.C, c = row % a.C;
+  int64_t row, l, b, c;
+  row_of(a, i, row, l, b, c);
   const float* y0 = a.ys + (b * 2 * a.C + c) * a.L;
   const float* y1 = y0 + a.C * a.L;
   float v = y0[l] + y1[a.L - 1 - l];
@@ -465,8 +478,8 @@ __global__ __launch_bounds__(256) void bidir_gate_bwd_kernel(BidirArgs a) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t n = a.batch * a.C * a.L;
   if (i >= n) return;
-  const int64_t row = i / a.L, l = i % a.L;
-  const int64_t b = row / a.C, c = row % a.C;
+  int64_t row, l, b, c;
+  row_of(a, i, row, l, b, c);
   const int64_t r0 = (b * 2 * a.C + c) * a.L, r1 = r0 + a.C * a.L;
   const float g = Elem<T>::load(static_cast<const T*>(a.dout), i);
   float dm = g;
