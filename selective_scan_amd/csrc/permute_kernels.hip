@@ -343,8 +343,9 @@ __global__ __launch_bounds__(kThreads) void merge_plane_kernel(MergeArgs a) {
 // routes 1 and 3 transposed to [w][h] (as in the merge), and dM as [h][w] for the dMT write.  As
 // in the merge, the skip term and an fp32 x are template parameters and the loads of up to
 // kMergeBatch iterations are issued before any is used.
-template <typename T, bool kSkip, bool kXF32>
-__global__ __launch_bounds__(kPlaneThreads) void merge_gate_bwd_plane_kernel(MergeGateArgs a) {
+// kThreads: as in the merge (one wavefront for planes of up to 1024 pixels).
+template <typename T, bool kSkip, bool kXF32, int kThreads>
+__global__ __launch_bounds__(kThreads) void merge_gate_bwd_plane_kernel(MergeGateArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int H = int(a.H), Wd = int(a.W);
   const int L = H * Wd;  // the plane fits the LDS: 32-bit indices
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(kPlaneThreads) void merge_gate_bwd_plane_kernel(Mer
   const float* r1 = r0 + a.C * L;
   const float* r2 = r1 + a.C * L;
   const float* r3 = r2 + a.C * L;
-  constexpr int kStep = 4 * kPlaneThreads;
+  constexpr int kStep = 4 * kThreads;
   for (int t0 = 4 * int(threadIdx.x); t0 < L; t0 += kStep * kMergeBatch) {
     float4 v1[kMergeBatch], v3[kMergeBatch];
 #pragma unroll
@@ -641,6 +642,25 @@ hipError_t launch_transpose(const void* x, void* xT, int64_t batch, int64_t C, i
   return launch_route_scatter(x, o, batch, C, H, W, elem_bytes, s);
 }
 
+template <int kThreads>
+static void launch_merge_gate_bwd_t(const MergeGateArgs& a, dim3 g, size_t lds, hipStream_t s) {
+  const dim3 b{kThreads};
+  const bool skip = a.Dskip != nullptr && a.x != nullptr;
+  if (a.dtype == 0) {
+    if (skip)
+      merge_gate_bwd_plane_kernel<float, true, true, kThreads><<<g, b, lds, s>>>(a);
+    else
+      merge_gate_bwd_plane_kernel<float, false, false, kThreads><<<g, b, lds, s>>>(a);
+  } else {
+    if (skip && a.x_f32)
+      merge_gate_bwd_plane_kernel<bf16, true, true, kThreads><<<g, b, lds, s>>>(a);
+    else if (skip)
+      merge_gate_bwd_plane_kernel<bf16, true, false, kThreads><<<g, b, lds, s>>>(a);
+    else
+      merge_gate_bwd_plane_kernel<bf16, false, false, kThreads><<<g, b, lds, s>>>(a);
+  }
+}
+
 hipError_t launch_merge_gate_bwd(const MergeGateArgs& a, hipStream_t s) {
   const int64_t L = a.H * a.W;
   const size_t lds = (size_t(2) * size_t(a.W) * size_t(a.H + 1) + size_t(a.H) * size_t(a.W + 1)) * 4;
@@ -648,21 +668,11 @@ hipError_t launch_merge_gate_bwd(const MergeGateArgs& a, hipStream_t s) {
                        reinterpret_cast<uintptr_t>(a.dout) | reinterpret_cast<uintptr_t>(a.dz);
   if (a.z && lds <= 64 * 1024 && L % 4 == 0 && a.batch * a.C > 0 && aligned16(a.routes) && aligned16(a.dM) &&
       aligned16(a.dMT) && (io & (a.dtype == 0 ? 15 : 7)) == 0 && (!a.x_f32 || aligned16(a.x))) {
-    const dim3 g{uint32_t(a.batch * a.C)}, b{kPlaneThreads};
-    const bool skip = a.Dskip != nullptr && a.x != nullptr;
-    if (a.dtype == 0) {
-      if (skip)
-        merge_gate_bwd_plane_kernel<float, true, true><<<g, b, lds, s>>>(a);
-      else
-        merge_gate_bwd_plane_kernel<float, false, false><<<g, b, lds, s>>>(a);
-    } else {
-      if (skip && a.x_f32)
-        merge_gate_bwd_plane_kernel<bf16, true, true><<<g, b, lds, s>>>(a);
-      else if (skip)
-        merge_gate_bwd_plane_kernel<bf16, true, false><<<g, b, lds, s>>>(a);
-      else
-        merge_gate_bwd_plane_kernel<bf16, false, false><<<g, b, lds, s>>>(a);
-    }
+    const dim3 g{uint32_t(a.batch * a.C)};
+    if (L <= 1024)
+      launch_merge_gate_bwd_t<64>(a, g, lds, s);
+    else
+      launch_merge_gate_bwd_t<kPlaneThreads>(a, g, lds, s);
     return hipGetLastError();
   }
   // two kernels: the pre-gate merge into `merged` (only needed with a gate), then the gate
