@@ -427,7 +427,11 @@ def main():
                            "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
                            "traffic": load_traffic(cfg.name + ":plane", plane_kernel_source_hash()),
                            "frac_of_copy": gbps / copy_gbps, "ms_per_launch": scan_mean,
-                           "launch_ms": stats(scan_ms), "bytes_per_launch": step_bytes}
+                           "launch_ms": stats(scan_ms), "bytes_per_launch": step_bytes,
+                           # what the counters show limiting it (profiles/plane_fwd_lowstate_56x56_counters.txt):
+                           # VALU issue (softplus, decay and the two scan passes, ~27 instructions per
+                           # route step), not HBM
+                           "limiter": "valu"}
     if front is not None:
         fb = front_bytes(cfg, False)
         f_ms = float(np.mean(stage0_ms))
