@@ -298,7 +298,9 @@ int ss2d_fwd_stage(const ss2d_fwd_args* args, int stage, hipStream_t stream);
  * Everything is overwritten.  The workspace (>= ss2d_workspace_bytes(...)) is required.  With
  * workspace_has_states == 0 the forward is recomputed inside it; otherwise it must hold what
  * ss2d_fwd with keep_states wrote for the same inputs (the transposed x, the route outputs and
- * the checkpoint states), untouched since, and the forward is not run again. */
+ * the checkpoint states), untouched since, and the forward is not run again.  ss2d_bwd itself
+ * overwrites the route outputs there (with the routes' input gradients), so a second backward on
+ * the same workspace must pass workspace_has_states == 0. */
 typedef struct ss2d_bwd_args {
   const void* x;
   const void* delta;

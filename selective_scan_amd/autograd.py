@@ -61,13 +61,18 @@ class SS2DFn(torch.autograd.Function):
         out = _bind.ss2d_fwd(**kw, **opts, workspace=ws, keep_states=True)
         ctx.save_for_backward(*tensors, ws)
         ctx.opts = opts
+        ctx.states_valid = True
         return out
 
     @staticmethod
     def backward(ctx, dout):
         *tensors, ws = ctx.saved_tensors
         kw = dict(zip(_SS2D_KEYS, tensors))
-        g = _bind.ss2d_bwd(**kw, **ctx.opts, dout=dout, workspace=ws, workspace_has_states=True)
+        # ss2d_bwd reuses the workspace's route-output region for its own gradients, so only the
+        # first backward finds the forward's states there; a repeated backward (retain_graph)
+        # lets the library recompute the forward in the same workspace.
+        g = _bind.ss2d_bwd(**kw, **ctx.opts, dout=dout, workspace=ws, workspace_has_states=ctx.states_valid)
+        ctx.states_valid = False
         return (None,) + tuple(g.get(k) for k in _SS2D_GRADS)
 
 

@@ -11,6 +11,14 @@ Seeds: numpy PCG64 with seed = 1000 * config_index + tensor_index, tensor index 
 the order x, z, delta_raw, B, C, U, dout.  Values are drawn in fp32; bf16 storage
 is the round-to-nearest-even bf16 of that fp32 value, so the GPU and the oracle see
 identical numbers.
+
+The workloads use the initialisation above (params="s4d").  Parity tests draw the
+parameters with no structure instead (params="general", the default of the make_*_inputs
+functions): A is learned (A_log is a trained parameter of the `Mamba` module), so a kernel
+must read A[k, d, n] and D[k, d] of every route, channel and state.  Then
+  * A[..., n] = -exp(U[log 1/16, log 16])  per (route, channel, state), independent draws
+  * D[...]    = N(1, 0.3^2)               per (route, channel)
+from their own seed (tensor index T_GEN).
 """
 from __future__ import annotations
 
@@ -18,7 +26,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-T_X, T_Z, T_DELTA, T_B, T_C, T_U, T_DOUT, T_CONV, T_LN, T_PROJ = range(10)
+T_X, T_Z, T_DELTA, T_B, T_C, T_U, T_DOUT, T_CONV, T_LN, T_PROJ, T_GEN = range(11)
+PARAMS = ("s4d", "general")
 
 
 @dataclass(frozen=True)
@@ -109,8 +118,23 @@ def _normal(seed: int, shape, dtype: str) -> np.ndarray:
     return f32_to_bf16_bits(v) if dtype == "bf16" else v
 
 
+def _a_d(seed_base: int, lead: tuple, dstate: int, params: str):
+    """(A, D) of shapes lead + (dstate,) and lead, fp32: the S4D-real initialisation or, with
+    params="general", independent draws per (route, channel[, state])."""
+    if params == "s4d":
+        A = np.broadcast_to(-(np.arange(dstate, dtype=np.float32) + 1.0), lead + (dstate,)).copy()
+        return A, np.ones(lead, dtype=np.float32)
+    if params != "general":
+        raise ValueError(f"params must be one of {PARAMS}")
+    rng = np.random.Generator(np.random.PCG64(1000 * seed_base + T_GEN))
+    A = -np.exp(rng.uniform(np.log(1.0 / 16.0), np.log(16.0), size=lead + (dstate,))).astype(np.float32)
+    D = (1.0 + 0.3 * rng.standard_normal(size=lead)).astype(np.float32)
+    return A, D
+
+
 def make_ss2d_inputs(batch: int, height: int, width: int, dim: int, dstate: int, dtype: str,
-                     has_z: bool = True, seed_base: int = 0, with_dout: bool = False) -> dict:
+                     has_z: bool = True, seed_base: int = 0, with_dout: bool = False,
+                     params: str = "general") -> dict:
     """Inputs of one SS2D call.  Shapes (all dense, last index fastest):
        x, z, dout: (batch, dim, H, W)      grid layout
        delta:      (batch, 4, dim, L)      per-route sequence order
@@ -129,8 +153,7 @@ def make_ss2d_inputs(batch: int, height: int, width: int, dim: int, dstate: int,
     rng = np.random.Generator(np.random.PCG64(s + T_U))
     dt = rng.uniform(1e-3, 1e-1, size=(4, dim))
     out["delta_bias"] = np.log(np.expm1(dt)).astype(np.float32)  # inverse softplus of dt
-    out["A"] = np.broadcast_to(-(np.arange(dstate, dtype=np.float32) + 1.0), (4, dim, dstate)).copy()
-    out["D"] = np.ones((4, dim), dtype=np.float32)
+    out["A"], out["D"] = _a_d(seed_base, (4, dim), dstate, params)
     out["dout"] = _normal(s + T_DOUT, (batch, dim, height, width), dtype) if with_dout else None
     out["meta"] = dict(batch=batch, height=height, width=width, dim=dim, dstate=dstate, dtype=dtype)
     return out
@@ -165,13 +188,16 @@ def make_proj_params(dim: int, dstate: int, dt_rank: int, seed_base: int = 0) ->
     return {"x_proj_w": wx.astype(np.float32), "dt_proj_w": wdt}
 
 
-def make_config_inputs(cfg: SS2DConfig, with_dout: bool | None = None) -> dict:
+def make_config_inputs(cfg: SS2DConfig, with_dout: bool | None = None, params: str = "s4d") -> dict:
+    """Inputs of a workload: its parameters as the workload states them (params="s4d") unless
+    a test asks for general ones."""
     return make_ss2d_inputs(cfg.batch, cfg.height, cfg.width, cfg.dim, cfg.dstate, cfg.dtype,
-                            cfg.has_z, cfg.index, cfg.with_bwd if with_dout is None else with_dout)
+                            cfg.has_z, cfg.index, cfg.with_bwd if with_dout is None else with_dout, params)
 
 
 def make_ss_inputs(batch: int, dim: int, dstate: int, seqlen: int, ngroups: int, dtype: str,
-                   has_z: bool = True, seed_base: int = 0, with_dout: bool = False) -> dict:
+                   has_z: bool = True, seed_base: int = 0, with_dout: bool = False,
+                   params: str = "general") -> dict:
     """Inputs of one generic selective-scan call (the `selective_scan_fn` shapes):
        u, delta, z, dout: (batch, dim, L); B, C: (batch, G, N, L); A: (dim, N) fp32;
        D, delta_bias: (dim,) fp32."""
@@ -186,15 +212,14 @@ def make_ss_inputs(batch: int, dim: int, dstate: int, seqlen: int, ngroups: int,
     rng = np.random.Generator(np.random.PCG64(s + T_U))
     dt = rng.uniform(1e-3, 1e-1, size=(dim,))
     out["delta_bias"] = np.log(np.expm1(dt)).astype(np.float32)
-    out["A"] = np.broadcast_to(-(np.arange(dstate, dtype=np.float32) + 1.0), (dim, dstate)).copy()
-    out["D"] = np.ones((dim,), dtype=np.float32)
+    out["A"], out["D"] = _a_d(seed_base, (dim,), dstate, params)
     out["dout"] = _normal(s + T_DOUT, (batch, dim, seqlen), dtype) if with_dout else None
     out["meta"] = dict(batch=batch, dim=dim, dstate=dstate, seqlen=seqlen, ngroups=ngroups, dtype=dtype)
     return out
 
 
 def make_vim_inputs(batch: int, seqlen: int, dim: int, dstate: int, dtype: str, has_z: bool = True,
-                    seed_base: int = 0, with_dout: bool = False) -> dict:
+                    seed_base: int = 0, with_dout: bool = False, params: str = "general") -> dict:
     """Inputs of one bidirectional scan call.  Shapes (dense, last index fastest):
        u, delta:  (batch, 2, dim, L)      direction k in its own scan order
        B, C:      (batch, 2, dstate, L)   direction k in its own scan order
@@ -212,13 +237,12 @@ def make_vim_inputs(batch: int, seqlen: int, dim: int, dstate: int, dtype: str, 
     rng = np.random.Generator(np.random.PCG64(s + T_U))
     dt = rng.uniform(1e-3, 1e-1, size=(2, dim))
     out["delta_bias"] = np.log(np.expm1(dt)).astype(np.float32)
-    out["A"] = np.broadcast_to(-(np.arange(dstate, dtype=np.float32) + 1.0), (2, dim, dstate)).copy()
-    out["D"] = np.ones((2, dim), dtype=np.float32)
+    out["A"], out["D"] = _a_d(seed_base, (2, dim), dstate, params)
     out["dout"] = _normal(s + T_DOUT, (batch, dim, seqlen), dtype) if with_dout else None
     out["meta"] = dict(batch=batch, seqlen=seqlen, dim=dim, dstate=dstate, dtype=dtype)
     return out
 
 
-def make_vim_config_inputs(cfg: VimConfig, with_dout: bool | None = None) -> dict:
+def make_vim_config_inputs(cfg: VimConfig, with_dout: bool | None = None, params: str = "s4d") -> dict:
     return make_vim_inputs(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, cfg.dtype, cfg.has_z, cfg.index,
-                           cfg.with_bwd if with_dout is None else with_dout)
+                           cfg.with_bwd if with_dout is None else with_dout, params)

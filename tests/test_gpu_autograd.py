@@ -121,3 +121,49 @@ def test_vim_bidir_autograd_matches_direct_backward():
     for key, grad in (("u", "du"), ("delta", "ddelta"), ("A", "dA"), ("B", "dB"), ("C", "dC"), ("D", "dD"),
                       ("delta_bias", "ddelta_bias"), ("z", "dz")):
         _close(leaves[key].grad, r[grad], key)
+
+
+@pytest.mark.parametrize("k,ln,proj", [(0, False, False), (3, True, True)], ids=["plain", "producer+front+ln"])
+def test_ss2d_autograd_repeated_backward(k, ln, proj):
+    """Two backwards through one graph (retain_graph=True) give the same gradients: the first
+    reuses the forward's kept states, whose workspace the backward then overwrites; the second
+    recomputes them."""
+    t, _, dout = _ss2d_case(k, ln, proj, seed=970 + k)
+    leaves = {key: _leaf(v) if isinstance(v, torch.Tensor) else v for key, v in t.items()}
+    out = ss.ss2d(**leaves)
+    out.backward(dout, retain_graph=True)
+    first = {key: v.grad.clone() for key, v in leaves.items() if isinstance(v, torch.Tensor)}
+    for v in leaves.values():
+        if isinstance(v, torch.Tensor):
+            v.grad = None
+    out.backward(dout)
+    for key, g1 in first.items():
+        assert torch.equal(leaves[key].grad, g1), key
+
+
+def test_selective_scan_fn_and_vim_repeated_backward():
+    """The same for the generic scan and the bidirectional scan."""
+    g = torch.Generator().manual_seed(5)
+    rnd = lambda *s: torch.randn(*s, generator=g).cuda()
+    u, delta, A = rnd(2, 16, 45), 0.5 * rnd(2, 16, 45), -(torch.rand(16, 8, generator=g) + 0.2).cuda()
+    Bm, Cm, D, z, bias, dout = rnd(2, 1, 8, 45), rnd(2, 1, 8, 45), rnd(16), rnd(2, 16, 45), 0.1 * rnd(16), rnd(2, 16, 45)
+    leaves = [_leaf(x) for x in (u, delta, A, Bm, Cm, D, z, bias)]
+    out = ss.selective_scan_fn(*leaves, delta_softplus=True)
+    out.backward(dout, retain_graph=True)
+    first = [x.grad.clone() for x in leaves]
+    for x in leaves:
+        x.grad = None
+    out.backward(dout)
+    for x, g1 in zip(leaves, first):
+        assert torch.equal(x.grad, g1)
+    inp = synth.make_vim_inputs(2, 29, 12, 8, "f32", True, 961, True)
+    vl = {k: _leaf(to_dev(inp[k], "f32")) for k in ("u", "delta", "A", "B", "C", "D", "delta_bias", "z")}
+    out = ss.vim_bidir(**vl)
+    dout = to_dev(inp["dout"], "f32")
+    out.backward(dout, retain_graph=True)
+    first = {k: v.grad.clone() for k, v in vl.items()}
+    for v in vl.values():
+        v.grad = None
+    out.backward(dout)
+    for k, g1 in first.items():
+        assert torch.equal(vl[k].grad, g1), k

@@ -1,21 +1,20 @@
 """GPU parity of the backward paths (selective_scan_bwd, ss2d_bwd) against the fp64 oracle's
-exact gradients; gradients within 1e-3 relative (bf16 I/O: 2e-2, the storage rounding)."""
+exact gradients: within 1e-3 relative, except the gradients stored in bf16 in a bf16 run (du,
+ddelta, dB, dC, dz, dx), whose one rounding to bf16 alone is up to 2^-9: 2e-2, as for bf16 outputs.
+The fp32-stored gradients (dA, dD, ddelta_bias) are held to 1e-3 in every run."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import selective_scan_amd as ss
-from gpu_util import TOL, TOL_GRAD, f64, rel_err, to_dev, to_f64
+from gpu_util import TOL_GRAD, f64, grad_tol, rel_err, to_dev, to_f64
 from selective_scan_amd import synth
 
 pytestmark = pytest.mark.gpu
 
 GRADS = ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias")
-
-
-def _tol(dtype):
-    return TOL_GRAD if dtype == "f32" else TOL["bf16"]
+_tol = grad_tol
 
 
 def _case(batch, dim, N, L, G, dtype, has_z, has_D, has_bias, softplus, seed):
@@ -61,7 +60,7 @@ def test_selective_scan_bwd(ci):
             assert g[k] is None
             continue
         e = rel_err(to_f64(g[k]), r[k])
-        assert e <= _tol(dtype), (k, e)
+        assert e <= _tol(dtype, k), (k, e)
 
 
 def test_selective_scan_bwd_reuses_forward_states():
@@ -108,7 +107,7 @@ def test_ss2d_bwd(case):
             assert g[k] is None
             continue
         e = rel_err(to_f64(g[k]), r[k])
-        assert e <= _tol(dtype), (k, e)
+        assert e <= _tol(dtype, k), (k, e)
 
 
 @pytest.mark.parametrize("case", [(1, 8, 8, 16, 4, "f32", True), (2, 7, 9, 20, 16, "f32", True),
@@ -134,44 +133,61 @@ def test_ss2d_bwd_reuses_forward_states(case):
             continue
         assert torch.equal(g[k], g2[k]), k
         e = rel_err(to_f64(g[k]), r[k])
-        assert e <= _tol(dtype), (k, e)
+        assert e <= _tol(dtype, k), (k, e)
 
 
-def test_ss2d_bwd_tiny_config():
+@pytest.mark.parametrize("params", synth.PARAMS)
+def test_ss2d_bwd_tiny_config(params):
     cfg = synth.TINY
-    dev, ref, dout, dout64 = _ss2d(cfg.batch, cfg.height, cfg.width, cfg.dim, cfg.dstate, cfg.dtype, cfg.has_z,
-                                   seed=cfg.index)
-    g = ss.ss2d_bwd(**dev, dout=dout)
-    r = oracle.ss2d_bwd(**ref, dout=dout64)
+    inp = synth.make_config_inputs(cfg, with_dout=True, params=params)
+    dev, ref = _dev_ref(inp, cfg.dtype, cfg.has_z)
+    g = ss.ss2d_bwd(**dev, dout=to_dev(inp["dout"], cfg.dtype))
+    r = oracle.ss2d_bwd(**ref, dout=f64(inp["dout"], cfg.dtype))
     for k in SS2D_GRADS:
         assert rel_err(to_f64(g[k]), r[k]) <= TOL_GRAD, k
 
 
-def test_ss2d_bwd_highres_config_full():
-    """The high-resolution workload (128x128, B=4, D=192, N=16, fp32) at full size against the
-    oracle's full fp64 gradients, in the launch configuration the benchmark uses."""
-    cfg = synth.HIGHRES
-    inp = synth.make_config_inputs(cfg, with_dout=True)
-    dev = dict(x=to_dev(inp["x"], "f32"), delta=to_dev(inp["delta"], "f32"), A=to_dev(inp["A"], "f32"),
-               B=to_dev(inp["B"], "f32"), C=to_dev(inp["C"], "f32"), D=to_dev(inp["D"], "f32"),
-               delta_bias=to_dev(inp["delta_bias"], "f32"), z=to_dev(inp["z"], "f32"))
-    g = ss.ss2d_bwd(**dev, dout=to_dev(inp["dout"], "f32"))
-    torch.cuda.synchronize()
-    ref = {k: inp[k].astype(np.float64) for k in ("x", "delta", "A", "B", "C", "D", "delta_bias", "z")}
-    r = oracle.ss2d_bwd(**ref, dout=inp["dout"].astype(np.float64))
+def _dev_ref(inp, dt, has_z=True):
+    dev = dict(x=to_dev(inp["x"], dt), delta=to_dev(inp["delta"], dt), A=to_dev(inp["A"], "f32"),
+               B=to_dev(inp["B"], dt), C=to_dev(inp["C"], dt), D=to_dev(inp["D"], "f32"),
+               delta_bias=to_dev(inp["delta_bias"], "f32"), z=to_dev(inp["z"], dt) if has_z else None)
+    ref = dict(x=f64(inp["x"], dt), delta=f64(inp["delta"], dt), A=inp["A"].astype(np.float64),
+               B=f64(inp["B"], dt), C=f64(inp["C"], dt), D=inp["D"].astype(np.float64),
+               delta_bias=inp["delta_bias"].astype(np.float64), z=f64(inp["z"], dt) if has_z else None)
+    return dev, ref
+
+
+@pytest.mark.parametrize("cfg", [synth.HIGHRES, synth.STAGE3], ids=lambda c: c.name)
+def test_ss2d_bwd_config_full(cfg):
+    """The high-resolution (128x128, B=4, D=192, N=16, fp32) and stage-3 (14x14, B=128, D=768,
+    N=16, bf16) workloads at full size, in the benchmark's training launch configuration (forward
+    with keep_states, backward on its states), against the oracle's full fp64 gradients.  A and D
+    are drawn per route, channel and state."""
+    inp = synth.make_config_inputs(cfg, with_dout=True, params="general")
+    dev, ref = _dev_ref(inp, cfg.dtype, cfg.has_z)
+    print(f"full-config backward {cfg.name}", flush=True)
+    ws = torch.empty(ss.ss2d_workspace_bytes(cfg.batch, cfg.dim, cfg.height, cfg.width, cfg.dstate, dev["x"].dtype),
+                     dtype=torch.uint8, device="cuda")
+    ss.ss2d_fwd(**dev, workspace=ws, keep_states=True)
+    g = ss.ss2d_bwd(**dev, dout=to_dev(inp["dout"], cfg.dtype), workspace=ws, workspace_has_states=True)
+    got = {k: to_f64(g[k]) for k in SS2D_GRADS}
+    del g, ws, dev
+    torch.cuda.empty_cache()
+    r = oracle.ss2d_bwd(**ref, dout=f64(inp["dout"], cfg.dtype))
     for k in SS2D_GRADS:
-        e = rel_err(to_f64(g[k]), r[k])
-        assert e <= TOL_GRAD, (k, e)
+        e = rel_err(got[k], r[k])
+        assert e <= _tol(cfg.dtype, k), (k, e)
 
 
 def test_ss2d_bwd_stage1_full_size_training_path():
     """Stage-1 (B=128, 56x56, D=192, N=16, bf16) at full size in the benchmark's training launch
-    configuration (forward with keep_states, backward on its states).  Checked on what the oracle
-    can compute from slices: per-element gradients (dx, ddelta, dz) on sampled (image, channel)
-    planes; dA, dD, ddelta_bias of sampled channels from all images; dB, dC of a sampled image
-    from all its channels."""
+    configuration (forward with keep_states, backward on its states), A and D drawn per route,
+    channel and state.  Checked on what the oracle can compute from slices (rows are independent,
+    and dB/dC of an image sum over its channels only): every gradient of 8 whole images (the
+    first, the last and 6 drawn ones); dA, dD, ddelta_bias of 24 channels (the first, the last and
+    22 drawn ones) summed over all 128 images."""
     cfg = synth.STAGE1
-    inp = synth.make_config_inputs(cfg, with_dout=True)
+    inp = synth.make_config_inputs(cfg, with_dout=True, params="general")
     dt = cfg.dtype
     dev = dict(x=to_dev(inp["x"], dt), delta=to_dev(inp["delta"], dt), A=to_dev(inp["A"], "f32"),
                B=to_dev(inp["B"], dt), C=to_dev(inp["C"], dt), D=to_dev(inp["D"], "f32"),
@@ -190,20 +206,14 @@ def test_ss2d_bwd_stage1_full_size_training_path():
                                z=f(inp["z"][bs][:, ds]), dout=f(inp["dout"][bs][:, ds]))
 
     rng = np.random.default_rng(21)
-    tol = TOL["bf16"]
-    for b, d in [(0, 0), (cfg.batch - 1, cfg.dim - 1), (int(rng.integers(cfg.batch)), int(rng.integers(cfg.dim)))]:
-        r = ref(slice(b, b + 1), slice(d, d + 1))
-        for k, gk in (("dx", g["dx"][b:b + 1, d:d + 1]), ("ddelta", g["ddelta"][b:b + 1, :, d:d + 1]),
-                      ("dz", g["dz"][b:b + 1, d:d + 1])):
-            e = rel_err(to_f64(gk), r[k])
-            assert e <= tol, (k, b, d, e)
-    d = int(rng.integers(cfg.dim))
-    r = ref(slice(0, cfg.batch), slice(d, d + 1))
-    for k, gk in (("dA", g["dA"][:, d:d + 1]), ("dD", g["dD"][:, d:d + 1]), ("ddelta_bias", g["ddelta_bias"][:, d:d + 1])):
-        e = rel_err(to_f64(gk), r[k])
-        assert e <= tol, (k, d, e)
-    b = int(rng.integers(cfg.batch))
-    r = ref(slice(b, b + 1), slice(0, cfg.dim))
-    for k in ("dB", "dC"):
-        e = rel_err(to_f64(g[k][b:b + 1]), r[k])
-        assert e <= tol, (k, b, e)
+    images = np.unique(np.concatenate([[0, cfg.batch - 1], rng.choice(np.arange(1, cfg.batch - 1), 6, replace=False)]))
+    r = ref(images, slice(0, cfg.dim))
+    for k in ("dx", "ddelta", "dz", "dB", "dC"):
+        e = rel_err(to_f64(g[k][torch.from_numpy(images).cuda()]), r[k])
+        assert e <= _tol(dt, k), (k, e)
+    chans = np.unique(np.concatenate([[0, cfg.dim - 1], rng.choice(np.arange(1, cfg.dim - 1), 22, replace=False)]))
+    r = ref(slice(0, cfg.batch), chans)
+    ci = torch.from_numpy(chans).cuda()
+    for k in ("dA", "dD", "ddelta_bias"):
+        e = rel_err(to_f64(g[k][:, ci]), r[k])
+        assert e <= _tol(dt, k), (k, e)

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import selective_scan_amd as ss
-from gpu_util import TOL, TOL_GRAD, f64, rel_err, to_dev, to_f64
+from gpu_util import TOL, TOL_GRAD, f64, grad_tol, rel_err, to_dev, to_f64
 from selective_scan_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -59,13 +59,12 @@ def test_ss2d_front_bwd(case):
     dev, ref, dout, dout64 = _case(batch, H, W, dim, N, dtype, z, k, bias, seed=600 + H * W + k)
     g = ss.ss2d_bwd(**dev, dout=dout)
     r = oracle.ss2d_front_bwd(**ref, dout=dout64)
-    tol = TOL_GRAD if dtype == "f32" else TOL["bf16"]
     for key in GRADS:
         if r[key] is None:
             assert g[key] is None, key
             continue
         e = rel_err(to_f64(g[key]), r[key])
-        assert e <= tol, (key, e)
+        assert e <= grad_tol(dtype, key), (key, e)
 
 
 @pytest.mark.parametrize("case", [CASES[1], CASES[2], CASES[3]], ids=str)
@@ -103,7 +102,7 @@ def test_ss2d_front_stage1_full_size_sampled():
     configuration.  The front is per channel, so the oracle checks (image, channel) planes of the
     output and of dx, ddelta, dz, and one channel's filter gradients over all images."""
     cfg = synth.STAGE1
-    inp = synth.make_config_inputs(cfg, with_dout=True)
+    inp = synth.make_config_inputs(cfg, with_dout=True, params="general")
     fp = synth.make_front_params(cfg.dim, 3, seed_base=cfg.index)
     dt = cfg.dtype
     dev = dict(x=to_dev(inp["x"], dt), delta=to_dev(inp["delta"], dt), A=to_dev(inp["A"], "f32"),
@@ -139,4 +138,4 @@ def test_ss2d_front_stage1_full_size_sampled():
     for key in ("dconv_w", "dconv_b", "dA", "dD", "ddelta_bias"):
         gk = g[key][d:d + 1] if key in ("dconv_w", "dconv_b") else g[key][:, d:d + 1]
         e = rel_err(to_f64(gk), r[key])
-        assert e <= tol, (key, d, e)
+        assert e <= grad_tol(dt, key), (key, d, e)

@@ -186,41 +186,27 @@ def test_ss2d_fwd_single_kernel(case):
     assert rel_err(to_f64(out), to_f64(plan.out)) <= (1e-5 if dtype == "f32" else 8e-3)
 
 
-def test_ss2d_fwd_tiny_config():
+@pytest.mark.parametrize("params", synth.PARAMS)
+def test_ss2d_fwd_tiny_config(params):
     cfg = synth.TINY
-    inp = synth.make_config_inputs(cfg)
+    inp = synth.make_config_inputs(cfg, params=params)
     dev, ref = _ss2d_dev_ref(inp, cfg.dtype, cfg.has_z)
     out = ss.ss2d_fwd(**dev)
     assert rel_err(to_f64(out), oracle.ss2d_fwd(**ref)) <= TOL[cfg.dtype]
 
 
-def _slice_ref(ref, b, d):
-    """Inputs of the single plane (b, d): rows are independent, so this is itself a valid SS2D input."""
-    return dict(x=ref["x"][b:b + 1, d:d + 1], delta=ref["delta"][b:b + 1, :, d:d + 1], A=ref["A"][:, d:d + 1],
-                B=ref["B"][b:b + 1], C=ref["C"][b:b + 1], D=ref["D"][:, d:d + 1],
-                delta_bias=ref["delta_bias"][:, d:d + 1],
-                z=None if ref["z"] is None else ref["z"][b:b + 1, d:d + 1])
-
-
 @pytest.mark.parametrize("cfg", [synth.STAGE1, synth.STAGE3, synth.LOWSTATE, synth.HIGHRES], ids=lambda c: c.name)
-def test_ss2d_fwd_full_config_sampled(cfg):
-    """Full-size run in the benchmark's launch configuration; oracle on sampled planes."""
-    inp = synth.make_config_inputs(cfg, with_dout=False)
-    dev = dict(x=to_dev(inp["x"], cfg.dtype), delta=to_dev(inp["delta"], cfg.dtype), A=to_dev(inp["A"], "f32"),
-               B=to_dev(inp["B"], cfg.dtype), C=to_dev(inp["C"], cfg.dtype), D=to_dev(inp["D"], "f32"),
-               delta_bias=to_dev(inp["delta_bias"], "f32"), z=to_dev(inp["z"], cfg.dtype) if cfg.has_z else None)
+def test_ss2d_fwd_full_config(cfg):
+    """Full-size run in the benchmark's launch configuration (the same shapes, so the same kernels,
+    grids and chunk plans), compared element by element with the oracle over the whole output.
+    A and D are drawn per route, channel and state (the kernels must not assume the workload's
+    structured initialisation)."""
+    inp = synth.make_config_inputs(cfg, with_dout=False, params="general")
+    dev, ref = _ss2d_dev_ref(inp, cfg.dtype, cfg.has_z)
+    print(f"full-config forward {cfg.name}", flush=True)
     out = ss.ss2d_fwd(**dev)
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(cfg.index)
-    planes = [(0, 0), (cfg.batch - 1, cfg.dim - 1)] + [
-        (int(rng.integers(cfg.batch)), int(rng.integers(cfg.dim))) for _ in range(4)]
-    ref_full = dict(x=inp["x"], delta=inp["delta"], A=inp["A"], B=inp["B"], C=inp["C"], D=inp["D"],
-                    delta_bias=inp["delta_bias"], z=inp["z"])
-    for b, d in planes:
-        sl = _slice_ref(ref_full, b, d)
-        sl = {k: (None if v is None else (v.astype(np.float64) if k in ("A", "D", "delta_bias")
-                                         else synth.storage_to_f64(v, cfg.dtype))) for k, v in sl.items()}
-        r = oracle.ss2d_fwd(**sl)
-        g = to_f64(out[b:b + 1, d:d + 1])
-        assert rel_err(g, r) <= TOL[cfg.dtype], (b, d)
-    assert torch.isfinite(out.float()).all()
+    got = to_f64(out)
+    del out, dev
+    torch.cuda.empty_cache()
+    e = rel_err(got, oracle.ss2d_fwd(**ref))
+    assert e <= TOL[cfg.dtype], e

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import selective_scan_amd as ss
-from gpu_util import TOL, TOL_GRAD, f64, rel_err, to_dev, to_f64
+from gpu_util import TOL, TOL_GRAD, f64, grad_tol, rel_err, to_dev, to_f64
 from selective_scan_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -70,13 +70,12 @@ def test_ss2d_proj_bwd(case):
     g = ss.ss2d_bwd(**dev, dout=dout)
     r = oracle.ss2d_proj_bwd(**ref, dout=dout64)
     assert g["ddelta"] is None and g["dB"] is None and g["dC"] is None
-    tol = TOL_GRAD if dtype == "f32" else TOL["bf16"]
     for key in GRADS:
         if r.get(key) is None:
             assert g.get(key) is None, key
             continue
         e = rel_err(to_f64(g[key]), r[key])
-        assert e <= tol, (key, e)
+        assert e <= grad_tol(dtype, key), (key, e)
 
 
 @pytest.mark.parametrize("case", [CASES[1], CASES[3]], ids=str)
@@ -103,7 +102,7 @@ def test_ss2d_proj_stage1_full_size_image_slices():
     LayerNorm at full size, training launch configuration.  The projections mix a pixel's channels,
     so the oracle checks whole images: the output, dx and dz of sampled images."""
     cfg = synth.STAGE1
-    inp = synth.make_config_inputs(cfg, with_dout=True)
+    inp = synth.make_config_inputs(cfg, with_dout=True, params="general")
     R = 6
     pw = synth.make_proj_params(cfg.dim, cfg.dstate, R, seed_base=cfg.index)
     fp = synth.make_front_params(cfg.dim, 3, seed_base=cfg.index)
@@ -143,7 +142,7 @@ def test_ss2d_proj_stage3_full_size_rank24():
     against the oracle; the weight gradients, sums over all images, equal the sums of those of
     the two half batches (whose slices group the images' steps differently), to fp32 rounding."""
     cfg = synth.STAGE3
-    inp = synth.make_config_inputs(cfg, with_dout=True)
+    inp = synth.make_config_inputs(cfg, with_dout=True, params="general")
     R = 24
     pw = synth.make_proj_params(cfg.dim, cfg.dstate, R, seed_base=cfg.index)
     dt = cfg.dtype

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import selective_scan_amd as ss
-from gpu_util import TOL, TOL_GRAD, f64, rel_err, to_dev, to_f64
+from gpu_util import TOL, TOL_GRAD, f64, grad_tol, rel_err, to_dev, to_f64
 from selective_scan_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -68,7 +68,7 @@ def test_vim_bidir_fwd_full_config_sampled():
     """Full Vim-Tiny size in the benchmark's launch configuration; oracle on sampled (batch, channel)
     rows (each takes both directions of its channel)."""
     cfg = synth.VIM_TINY
-    inp = synth.make_vim_config_inputs(cfg, with_dout=False)
+    inp = synth.make_vim_config_inputs(cfg, with_dout=False, params="general")
     dev = dict(u=to_dev(inp["u"], cfg.dtype), delta=to_dev(inp["delta"], cfg.dtype), A=to_dev(inp["A"], "f32"),
                B=to_dev(inp["B"], cfg.dtype), C=to_dev(inp["C"], cfg.dtype), D=to_dev(inp["D"], "f32"),
                delta_bias=to_dev(inp["delta_bias"], "f32"), z=to_dev(inp["z"], cfg.dtype))
@@ -105,13 +105,12 @@ def test_vim_bidir_bwd(case):
     dev, ref, dout, dout64 = _vim(batch, L, dim, N, dtype, z, seed=90 + L + dim, with_D=D, with_bias=bias, dout=True)
     g = ss.vim_bidir_bwd(**dev, dout=dout)
     r = oracle.vim_bidir_bwd(**ref, dout=dout64)
-    tol = TOL_GRAD if dtype == "f32" else TOL["bf16"]
     for k in GRADS:
         if r[k] is None:
             assert g[k] is None, k
             continue
         e = rel_err(to_f64(g[k]), r[k])
-        assert e <= tol, (k, e)
+        assert e <= grad_tol(dtype, k), (k, e)
 
 
 @pytest.mark.parametrize("case", [(2, 197, 40, 16, "bf16", True, True, True), (1, 1024, 32, 16, "f32", True, True, True),
@@ -139,7 +138,7 @@ def test_vim_bidir_bwd_full_config_sliced():
     slices: per-element gradients of sampled (batch, channel) rows; dA, dD, ddelta_bias of a
     sampled channel from all sequences; dB, dC of a sampled sequence from all its channels."""
     cfg = synth.VIM_TINY
-    inp = synth.make_vim_config_inputs(cfg, with_dout=True)
+    inp = synth.make_vim_config_inputs(cfg, with_dout=True, params="general")
     dt = cfg.dtype
     dev = dict(u=to_dev(inp["u"], dt), delta=to_dev(inp["delta"], dt), A=to_dev(inp["A"], "f32"),
                B=to_dev(inp["B"], dt), C=to_dev(inp["C"], dt), D=to_dev(inp["D"], "f32"),
@@ -165,7 +164,7 @@ def test_vim_bidir_bwd_full_config_sliced():
     d = int(rng.integers(cfg.dim))
     r = ref(slice(0, cfg.batch), slice(d, d + 1))
     for k, gk in (("dA", g["dA"][:, d:d + 1]), ("dD", g["dD"][:, d:d + 1]), ("ddelta_bias", g["ddelta_bias"][:, d:d + 1])):
-        assert rel_err(to_f64(gk), r[k]) <= tol, (k, d)
+        assert rel_err(to_f64(gk), r[k]) <= grad_tol(dt, k), (k, d)
     b = int(rng.integers(cfg.batch))
     r = ref(slice(b, b + 1), slice(0, cfg.dim))
     for k in ("dB", "dC"):
