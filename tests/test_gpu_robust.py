@@ -238,7 +238,7 @@ def test_guard_vim_bidir(case):
     _check_all(g, ref_g)
 
 
-@pytest.mark.parametrize("case", [(3, 37, 16, 2, "bf16"), (2, 5, 3, 1, "f32")], ids=str)
+@pytest.mark.parametrize("case", [(3, 38, 16, 2, "bf16"), (2, 5, 3, 1, "f32")], ids=str)
 def test_guard_selective_scan_step(case):
     batch, dim, N, G, dtype = case
     inp = synth.make_ss_inputs(batch, dim, N, 1, G, dtype, has_z=True, seed_base=2400 + dim)
