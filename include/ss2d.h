@@ -26,8 +26,9 @@
  *    and all accumulation are fp32.
  *  * Sizes of 0 (empty batch, no channels, empty sequence) are valid and do nothing
  *    except write zeros to gradients that are sums over an empty set.
- *  * The library keeps no global state; calls on different streams may run
- *    concurrently as long as their workspaces do not overlap.
+ *  * Apart from the scratch of ss2d_fwd_noalloc (one fixed array per GPU), the library keeps
+ *    no global state; calls on different streams may run concurrently as long as their
+ *    workspaces do not overlap.
  */
 #ifndef SS2D_H_
 #define SS2D_H_
@@ -41,7 +42,7 @@
 extern "C" {
 #endif
 
-#define SS2D_ABI_VERSION 7
+#define SS2D_ABI_VERSION 8
 
 /* Status codes returned by every entry point. */
 enum {
@@ -49,7 +50,9 @@ enum {
   SS2D_ERR_INVALID_ARGUMENT = 1, /* null required pointer, negative size, dim % ngroups != 0,
                                     workspace missing or too small, misaligned pointer */
   SS2D_ERR_UNSUPPORTED = 2,      /* dtype not F32/BF16, dstate outside [1, 64] */
-  SS2D_ERR_HIP = 3               /* a kernel launch reported an error */
+  SS2D_ERR_HIP = 3,              /* a kernel launch reported an error */
+  SS2D_ERR_TOO_LARGE = 4         /* ss2d_fwd_noalloc: the problem needs more scratch than the
+                                    library holds (ss2d_fwd_noalloc_max_workspace_bytes) */
 };
 
 /* I/O element types. */
@@ -276,6 +279,26 @@ int ss2d_fwd(const ss2d_fwd_args* args, hipStream_t stream);
  * result equals the staged one up to the order of the scan's roundings (the single kernel
  * scans each route in parallel segments, the stages step by step).  Enqueues nothing. */
 int ss2d_fwd_single_kernel(const ss2d_fwd_args* args);
+
+/* ---------------------------------------------------------------------------------
+ * Allocation-free ss2d_fwd, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same forward as
+ * ss2d_fwd(args), bit for bit, with its workspace taken from a fixed scratch array that the
+ * library holds on each GPU (ss2d_fwd_noalloc_max_workspace_bytes() bytes, 128 MiB, allocated
+ * with the library's code object on every GPU it is loaded on and kept until the process ends).
+ * `workspace` and `workspace_bytes` are ignored; the caller still passes every input and `out`.
+ * Nothing is allocated or freed.  The scratch of the current device is used, so `stream` must
+ * belong to the current device.
+ *   * Returns SS2D_ERR_TOO_LARGE, with nothing enqueued, when the call needs more than that
+ *     (ss2d_workspace_bytes(...) or ss2d_proj_workspace_bytes(...) of its shape; calls that run
+ *     as one kernel per plane, see ss2d_fwd_single_kernel, need none), and
+ *     SS2D_ERR_INVALID_ARGUMENT for keep_states != 0 (no backward can reach the scratch).
+ *   * Every call on one GPU shares that GPU's scratch, which keeps what the last call left
+ *     there (no call relies on its contents): calls that may overlap in time on one GPU (on
+ *     different streams, or from different threads) race and must be serialised by the caller.
+ * ------------------------------------------------------------------------------- */
+size_t ss2d_fwd_noalloc_max_workspace_bytes(void);
+int ss2d_fwd_noalloc(const ss2d_fwd_args* args, hipStream_t stream);
 
 /* One stage of ss2d_fwd, for callers that time or overlap the stages separately.
  * ss2d_fwd(args) == stage 0, then 1, then 2 on the same workspace (where

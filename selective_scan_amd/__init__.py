@@ -17,6 +17,8 @@ from ._binding import (  # noqa: F401
     ss2d_cross_merge,
     ss2d_cross_scan,
     ss2d_fwd,
+    ss2d_fwd_noalloc,
+    ss2d_fwd_noalloc_max_workspace_bytes,
     ss2d_workspace_bytes,
     VimForwardPlan,
     vim_bidir_bwd,

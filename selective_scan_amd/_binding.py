@@ -15,9 +15,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libss2d.so")
 
-SS2D_OK, SS2D_ERR_INVALID_ARGUMENT, SS2D_ERR_UNSUPPORTED, SS2D_ERR_HIP = 0, 1, 2, 3
+SS2D_OK, SS2D_ERR_INVALID_ARGUMENT, SS2D_ERR_UNSUPPORTED, SS2D_ERR_HIP, SS2D_ERR_TOO_LARGE = 0, 1, 2, 3, 4
 DTYPE_F32, DTYPE_BF16 = 0, 1
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -111,8 +111,10 @@ def lib():
         L.vim_bidir_workspace_bytes.argtypes = [_i64] * 4 + [_int]
         L.vim_bidir_fwd_stage.restype = _int
         L.vim_bidir_fwd_stage.argtypes = [ctypes.POINTER(VimFwdArgs), _int, _p]
+        L.ss2d_fwd_noalloc_max_workspace_bytes.restype = _sz
+        L.ss2d_fwd_noalloc_max_workspace_bytes.argtypes = []
         for name, st in (("selective_scan_fwd", SsFwdArgs), ("selective_scan_bwd", SsBwdArgs),
-                         ("ss2d_fwd", SS2DFwdArgs), ("ss2d_bwd", SS2DBwdArgs),
+                         ("ss2d_fwd", SS2DFwdArgs), ("ss2d_fwd_noalloc", SS2DFwdArgs), ("ss2d_bwd", SS2DBwdArgs),
                          ("vim_bidir_fwd", VimFwdArgs), ("vim_bidir_bwd", VimBwdArgs),
                          ("selective_scan_step", SsStepArgs)):
             f = getattr(L, name)
@@ -334,6 +336,41 @@ def ss2d_fwd(x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=
                     ln_b=_ptr(ln_b), ln_eps=float(ln_eps), x_proj_w=_ptr(x_proj_w), dt_proj_w=_ptr(dt_proj_w),
                     dt_rank=R)
     _check(lib().ss2d_fwd(ctypes.byref(a), _stream(dev)), "ss2d_fwd")
+    return out
+
+
+def ss2d_fwd_noalloc_max_workspace_bytes() -> int:
+    return int(lib().ss2d_fwd_noalloc_max_workspace_bytes())
+
+
+def ss2d_fwd_noalloc(x, delta, A, B, C, D=None, delta_bias=None, z=None, delta_softplus=True, out=None,
+                     conv_w=None, conv_b=None, layer_norm=False, ln_w=None, ln_b=None, ln_eps=1e-5, x_proj_w=None,
+                     dt_proj_w=None):
+    """ss2d_fwd without a workspace: the library's fixed per-GPU scratch serves instead (calls
+    that may overlap in time on one GPU race on it).  With `out` given and contiguous inputs of
+    the right types, nothing is allocated.  Raises SS2DError (status SS2D_ERR_TOO_LARGE) when the
+    call needs more scratch than ss2d_fwd_noalloc_max_workspace_bytes()."""
+    x, delta = _c(x), _c(delta)
+    dev = _dev(x)
+    B, C, z = _c(B), _c(C), _c(z)
+    A = _c(A, torch.float32)
+    D = _c(D, torch.float32)
+    delta_bias = _c(delta_bias, torch.float32)
+    conv_w, conv_b = _c(conv_w, torch.float32), _c(conv_b, torch.float32)
+    ln_w, ln_b = _c(ln_w, torch.float32), _c(ln_b, torch.float32)
+    batch, dim, H, W = x.shape
+    N = A.shape[-1]
+    x_proj_w, dt_proj_w, R = _proj(x_proj_w, dt_proj_w, dim)
+    if out is None:
+        out = torch.empty_like(x)
+    a = SS2DFwdArgs(x=_ptr(x), delta=_ptr(delta), A=_ptr(A), Bm=_ptr(B), Cm=_ptr(C), Dskip=_ptr(D),
+                    delta_bias=_ptr(delta_bias), z=_ptr(z), out=_ptr(out), workspace=None, workspace_bytes=0,
+                    batch=batch, dim=dim, height=H, width=W, dstate=N, dtype=_dtype_code(x.dtype),
+                    delta_softplus=int(bool(delta_softplus)), keep_states=0, conv_w=_ptr(conv_w), conv_b=_ptr(conv_b),
+                    conv_k=_conv_k(conv_w, dim), layer_norm=_ln_on(layer_norm, ln_w, ln_b), ln_w=_ptr(ln_w),
+                    ln_b=_ptr(ln_b), ln_eps=float(ln_eps), x_proj_w=_ptr(x_proj_w), dt_proj_w=_ptr(dt_proj_w),
+                    dt_rank=R)
+    _check(lib().ss2d_fwd_noalloc(ctypes.byref(a), _stream(dev)), "ss2d_fwd_noalloc")
     return out
 
 

@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/ss2d.h"
 #include "device_common.h"
 #include "internal.h"
@@ -176,6 +178,7 @@ const char* ss2d_status_string(int status) {
     case SS2D_ERR_INVALID_ARGUMENT: return "invalid argument";
     case SS2D_ERR_UNSUPPORTED: return "unsupported dtype or state size";
     case SS2D_ERR_HIP: return "HIP launch error";
+    case SS2D_ERR_TOO_LARGE: return "problem too large for the allocation-free scratch";
     default: return "unknown status";
   }
 }
@@ -553,7 +556,7 @@ static int check_front(const float* w, const float* b, int k) {
 
 // Validation shared by ss2d_fwd and ss2d_fwd_stage.  Returns SS2D_OK with *empty set when there
 // is nothing to compute.
-static int validate_ss2d_fwd(const ss2d_fwd_args* a, SS2DLayout* lay, bool* empty) {
+static int validate_ss2d_fwd(const ss2d_fwd_args* a, SS2DLayout* lay, bool* empty, bool check_ws = true) {
   *empty = false;
   if (!a) return SS2D_ERR_INVALID_ARGUMENT;
   int st = check_ss2d(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype);
@@ -566,7 +569,7 @@ static int validate_ss2d_fwd(const ss2d_fwd_args* a, SS2DLayout* lay, bool* empt
     return SS2D_OK;
   }
   const bool proj = a->x_proj_w != nullptr;  // delta, Bm, Cm come from the producer
-  if (!a->x || (!proj && (!a->delta || !a->Bm || !a->Cm)) || !a->A || !a->out || !a->workspace)
+  if (!a->x || (!proj && (!a->delta || !a->Bm || !a->Cm)) || !a->A || !a->out || (check_ws && !a->workspace))
     return SS2D_ERR_INVALID_ARGUMENT;
   if (!elem_aligned(a->dtype, {a->x, proj ? nullptr : a->delta, proj ? nullptr : a->Bm, proj ? nullptr : a->Cm, a->z,
                                a->out}))
@@ -574,7 +577,8 @@ static int validate_ss2d_fwd(const ss2d_fwd_args* a, SS2DLayout* lay, bool* empt
   if (!aligned(a->A, 4) || (a->Dskip && !aligned(a->Dskip, 4)) || (a->delta_bias && !aligned(a->delta_bias, 4)))
     return SS2D_ERR_INVALID_ARGUMENT;
   *lay = ss2d_layout(a->batch, a->dim, a->height, a->width, a->dstate, a->dtype, proj ? a->dt_rank : 0);
-  if (a->workspace_bytes < size_t(lay->total) || !aligned(a->workspace, kAlign)) return SS2D_ERR_INVALID_ARGUMENT;
+  if (check_ws && (a->workspace_bytes < size_t(lay->total) || !aligned(a->workspace, kAlign)))
+    return SS2D_ERR_INVALID_ARGUMENT;
   if (a->batch * a->dim * cdiv(a->height, 32) * cdiv(a->width, 32) > kMaxBlocks) return SS2D_ERR_INVALID_ARGUMENT;
   return SS2D_OK;
 }
@@ -620,6 +624,56 @@ int ss2d_fwd(const ss2d_fwd_args* a, hipStream_t stream) {
   st = ss2d_transpose_stage(a, lay, stream);
   if (st == SS2D_OK) st = ss2d_scan_stage(a, lay, a->keep_states != 0, stream);
   if (st == SS2D_OK) st = ss2d_merge_stage(a, lay, stream);
+  return st;
+}
+
+// ---- the allocation-free forward ------------------------------------------------------
+// Its scratch: one array per GPU, allocated with the library's code object when the library
+// is loaded on that GPU and held until the process ends.  Host code never uses the array's
+// name as an address (on the host it is only a stand-in for the device symbol): the device
+// address comes from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// The device address of the current device's scratch (looked up on its first use there).
+static int scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SS2D_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SS2D_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SS2D_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return SS2D_OK;
+}
+
+size_t ss2d_fwd_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
+
+int ss2d_fwd_noalloc(const ss2d_fwd_args* a, hipStream_t stream) {
+  SS2DLayout lay;
+  bool empty;
+  int st = validate_ss2d_fwd(a, &lay, &empty, /*check_ws=*/false);
+  if (st != SS2D_OK || empty) return st;
+  if (a->keep_states) return SS2D_ERR_INVALID_ARGUMENT;  // no backward can reach the scratch
+  PlaneFwdArgs pa{};
+  if (plane_path(a, &pa)) return status_from(launch_plane_fwd(pa, stream));  // needs no scratch
+  if (size_t(lay.total) > kScratchBytes) return SS2D_ERR_TOO_LARGE;
+  void* ptr = nullptr;
+  st = scratch_of_current_device(&ptr);
+  if (st != SS2D_OK) return st;
+  ss2d_fwd_args c = *a;
+  c.workspace = ptr;
+  c.workspace_bytes = kScratchBytes;
+  st = ss2d_transpose_stage(&c, lay, stream);
+  if (st == SS2D_OK) st = ss2d_scan_stage(&c, lay, false, stream);
+  if (st == SS2D_OK) st = ss2d_merge_stage(&c, lay, stream);
   return st;
 }
 

@@ -34,7 +34,8 @@ def test_every_declared_symbol_is_exported(lib):
             "ss2d_bwd", "ss2d_fwd_stage", "selective_scan_workspace_bytes", "ss2d_workspace_bytes",
             "ss2d_abi_version", "ss2d_status_string", "vim_bidir_workspace_bytes", "vim_bidir_fwd",
             "ss2d_proj_workspace_bytes",
-            "vim_bidir_fwd_stage", "vim_bidir_bwd", "selective_scan_step", "ss2d_fwd_single_kernel"} <= set(names)
+            "vim_bidir_fwd_stage", "vim_bidir_bwd", "selective_scan_step", "ss2d_fwd_single_kernel",
+            "ss2d_fwd_noalloc", "ss2d_fwd_noalloc_max_workspace_bytes"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
     missing = [n for n in names if n not in exported]
@@ -44,8 +45,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ss2d_abi_version() == 7
+    assert lib.ss2d_abi_version() == 8
     assert lib.ss2d_status_string(0) == b"ok"
+    assert b"too large" in lib.ss2d_status_string(4)
     assert b"invalid" in lib.ss2d_status_string(1)
     assert b"unsupported" in lib.ss2d_status_string(2)
     assert lib.ss2d_status_string(99) == b"unknown status"
@@ -252,3 +254,20 @@ def test_workspace_queries(lib):
     assert lib.vim_bidir_workspace_bytes(2, 8, 197, 0, 1) == 0
     assert lib.vim_bidir_workspace_bytes(2, 8, 197, 16, 4) == 0
     assert all(v % 256 == 0 for v in (a, b, s1, s2, v1, v2))
+
+
+def test_ss2d_fwd_noalloc_host_checks(lib):
+    """The allocation-free forward: its scratch size, and what it rejects before touching the GPU
+    (invalid arguments, kept states, problems larger than the scratch)."""
+    from selective_scan_amd._binding import SS2DFwdArgs
+    cap = lib.ss2d_fwd_noalloc_max_workspace_bytes()
+    assert cap == 128 << 20
+    f = dict(x=0x1000, delta=0x2000, A=0x3000, Bm=0x4000, Cm=0x5000, out=0x6000, batch=4, dim=192, height=56,
+             width=56, dstate=16, dtype=1, delta_softplus=1)
+    assert lib.ss2d_workspace_bytes(4, 192, 56, 56, 16, 1) > cap
+    assert lib.ss2d_fwd_noalloc(ctypes.byref(SS2DFwdArgs(**f)), None) == 4              # too large
+    assert lib.ss2d_fwd_noalloc(ctypes.byref(SS2DFwdArgs(**{**f, "keep_states": 1})), None) == 1
+    assert lib.ss2d_fwd_noalloc(ctypes.byref(SS2DFwdArgs(**{**f, "x": 0})), None) == 1
+    assert lib.ss2d_fwd_noalloc(ctypes.byref(SS2DFwdArgs(**{**f, "dtype": 5})), None) == 2
+    assert lib.ss2d_fwd_noalloc(ctypes.byref(SS2DFwdArgs(**{**f, "batch": 0})), None) == 0  # empty
+    assert lib.ss2d_fwd_noalloc(None, None) == 1
