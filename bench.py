@@ -42,17 +42,24 @@ METRIC = "SS2D scan elements/s (B·K·D·L) + achieved HBM GB/s vs peak, 56×56 
 HBM_PEAK_GBPS = 8000.0
 CLOCK_HZ = 2.4e9
 SIMDS = 256 * 4  # 256 CUs x 4 SIMDs, 16 fp32 lanes each
-# fp32 vector peak without packed math: 1024 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz
-VALU_PEAK_TFLOPS = SIMDS * 16 * 2 * CLOCK_HZ / 1e12
-# the published fp32 vector peak counts packed-FP32 instructions (two lanes' FMAs in one), which
-# this library does not issue; reported beside the peak above for reference
+# The published fp32 vector peak of the MI355X: the roofline's peak.  It counts packed-FP32
+# instructions (two lanes' FMAs in one), which this library does not issue (packed fp32 is
+# disabled in its build), so the scan kernels cannot reach more than half of it.
 PUBLISHED_FP32_VECTOR_TFLOPS = 157.3
-# Per (element, state) the scan issues 4 full-rate VALU ops (Lam*A, (Lam*u)*B, the FMA into
+# fp32 vector peak without packed math: 1024 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz (extra)
+VALU_PEAK_TFLOPS = SIMDS * 16 * 2 * CLOCK_HZ / 1e12
+# Per (element, state) the forward scan issues 4 full-rate VALU ops (Lam*A, (Lam*u)*B, the FMA into
 # h, the FMA into y: 7 flops counting the exp as one) and one v_exp_f32.  A wave64 VALU op
-# occupies a 16-lane SIMD for 4 cycles, a transcendental for 8, so 64 state-steps cost
-# 4*4 + 8 = 24 SIMD cycles: the issue-limited peak for this instruction mix.
+# occupies a 16-lane SIMD for 4 cycles and a v_exp_f32 8 (`bench.py --valu-probe`, summarised in
+# profiles/valu_issue_rates_probe.txt: the mix itself runs at ~24 cycles per 64 units), so 64
+# units cost 4*4 + 8 = 24 SIMD cycles: the issue-limited peak of this instruction mix (extra).
 FLOPS_PER_STATE_STEP = 7
 MIX_PEAK_TFLOPS = SIMDS * CLOCK_HZ * 64 / 24 * FLOPS_PER_STATE_STEP / 1e12
+# The backward scan per (element, state), from the gradient formulas: the forward recompute
+# (mul, exp, mul, fma: 5 flops), the adjoint (mul + exp for the decay, fma into lambda, two
+# muls for lambda a h, fmas into dA, ddelta and <lambda, B>, the decayed adjoint: 13 flops),
+# the dB and dC terms (2 muls) and their sums over the channels (2 adds): 22 flops.
+BWD_FLOPS_PER_STATE_STEP = 22
 FP32_MFMA_PEAK_TFLOPS = 157.3  # dense fp32 matrix-core peak of the MI355X
 MALL_BYTES = 256 << 20
 COPY_BYTES = 1 << 30
@@ -72,8 +79,17 @@ def parse():
                     help="SS2D only: LayerNorm over the channels of the merged map before the gate")
     ap.add_argument("--proj", type=int, default=0,
                     help="SS2D only: R > 0 produces delta/B/C from per-route x_proj/dt_proj (dt_rank R)")
+    ap.add_argument("--valu-probe", action="store_true",
+                    help="instead of the benchmark: measure the SIMD cycles of a wave64 FMA, a v_exp_f32 and the "
+                         "scan's per-(element, state) instruction mix (libss2d_probe.so) and print them as JSON")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="instead of the benchmark: render the rocprofv3 CSV output under DIR (kernel stats and/or "
+                         "counter collection) as the text summaries kept in profiles/")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time for the sample")
+    ap.add_argument("--cpu-seconds", type=float, default=30.0,
+                    help="oracle wall-time budget: the whole batch when its estimate fits, else the first images")
+    ap.add_argument("--no-train-step", action="store_true",
+                    help="SS2D forward workloads: skip the training-step record (forward with states + backward)")
     return ap.parse_args()
 
 
@@ -216,21 +232,13 @@ def cpu_baseline(cfg, inp, target_s, bwd=False, front=None, ln=None, proj=None):
         return time.perf_counter() - t0
 
     t1 = run(1)
-    nb = int(max(1, min(cfg.batch, round(target_s / max(t1, 1e-3)))))
+    # the whole batch when it fits the time target (the default covers every workload's forward)
+    nb = int(max(1, min(cfg.batch, math.floor(target_s / max(t1, 1e-3)))))
     t = run(nb) if nb > 1 else t1
     routes = 2 if vim else 4
     elems = nb * routes * cfg.dim * cfg.seqlen
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    single = None
-    if not vim and cfg.index in (0, 2) and proj is None and front is None and ln is None:
-        # the tiny and stage-3 workloads also on one core (one image)
-        prev = oracle.set_num_threads(1)
-        try:
-            ts = run(1)
-        finally:
-            oracle.set_num_threads(prev)
-        single = {"value": routes * cfg.dim * cfg.seqlen / ts, "unit": "elements/s", "cores": 1,
-                  "sample": f"first image, {'forward + backward' if bwd else 'forward'}, {ts * 1e3:.2f} ms wall"}
+    single = single_thread_runs() if proj is None and front is None and ln is None and not bwd else None
     return {"value": elems / t, "unit": "elements/s", "cores": threads, "kind": "oracle", "single_thread": single,
             "sample": f"first {nb} of {cfg.batch} {'sequences' if vim else 'images'} (all {cfg.dim} channels, "
                       f"{routes} {'directions' if vim else 'routes'}, L={cfg.seqlen}, N={cfg.dstate}), fp64 C "
@@ -239,6 +247,84 @@ def cpu_baseline(cfg, inp, target_s, bwd=False, front=None, ln=None, proj=None):
                       f"{', with the delta/B/C producer' if proj is not None else ''}, "
                       f"{'forward + backward' if bwd else 'forward'}, {t:.2f} s wall",
             "cpu_model": cpu_model()}
+
+
+def single_thread_runs():
+    """The oracle's SS2D forward on one core: the tiny workload whole, and the first image of the
+    stage-3 workload (the first image of each seeded tensor is the start of its stream, so a
+    one-image draw is that image)."""
+    import oracle
+    from selective_scan_amd import synth
+
+    out = []
+    prev = oracle.set_num_threads(1)
+    try:
+        for cfg in (synth.TINY, synth.STAGE3):
+            inp = synth.make_ss2d_inputs(1, cfg.height, cfg.width, cfg.dim, cfg.dstate, cfg.dtype, cfg.has_z,
+                                         cfg.index, params="s4d")
+            f = lambda a: None if a is None else synth.storage_to_f64(a, cfg.dtype)
+            args = (f(inp["x"]), f(inp["delta"]), inp["A"].astype(np.float64), f(inp["B"]), f(inp["C"]),
+                    inp["D"].astype(np.float64), inp["delta_bias"].astype(np.float64), f(inp["z"]))
+            t0 = time.perf_counter()
+            oracle.ss2d_fwd(*args)
+            ts = time.perf_counter() - t0
+            out.append({"workload": cfg.name, "value": 4 * cfg.dim * cfg.seqlen / ts, "unit": "elements/s",
+                        "cores": 1, "sample": f"{'the whole batch' if cfg.batch == 1 else 'first image'}, forward, "
+                                              f"{ts * 1e3:.2f} ms wall"})
+    finally:
+        oracle.set_num_threads(prev)
+    return out
+
+
+def train_step_record(cfg, ss, synth, d0, stream, steps, warmup):
+    """One training step of the SS2D op: ss2d_fwd keeping its checkpoint states, then ss2d_bwd on
+    them (seeded dout ~ N(0, 1)); HIP events on the launch stream around each half.  The backward's
+    arithmetic roofline counts BWD_FLOPS_PER_STATE_STEP per (element, state) over the whole
+    ss2d_bwd call (its scan kernel and the small gate, reduce and merge kernels around it)."""
+    import torch
+
+    rng = np.random.Generator(np.random.PCG64(1000 * cfg.index + synth.T_DOUT))
+    g = rng.standard_normal(size=(cfg.batch, cfg.dim, cfg.height, cfg.width), dtype=np.float32)
+    if cfg.dtype == "bf16":
+        dout = torch.from_numpy(synth.f32_to_bf16_bits(g).view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        dout = torch.from_numpy(g).cuda()
+    del g
+    plan = ss.SS2DForwardPlan(**d0, keep_states=True)
+
+    def one(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        for stage in (0, 1, 2):
+            plan.run_stage(stage)
+        if ev is not None:
+            ev[1].record(stream)
+        ss.ss2d_bwd(**d0, dout=dout, workspace=plan.workspace, workspace_has_states=True)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        one(evs[i])
+    torch.cuda.synchronize()
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    del plan, dout
+    torch.cuda.empty_cache()
+    bflops = cfg.elements * cfg.dstate * BWD_FLOPS_PER_STATE_STEP
+    b_ms = float(np.median(bwd_ms))
+    return {"what": "ss2d_fwd with keep_states + ss2d_bwd on its states, same inputs, dout ~ N(0,1)",
+            "ms": stats(step_ms), "elements_per_s": cfg.elements / (float(np.median(step_ms)) * 1e-3),
+            "fwd_keep_states_ms": stats(fwd_ms), "bwd_ms": stats(bwd_ms),
+            "bwd_roofline": {"kernel": "ss2d_bwd (scan_bwd_kernel with its gate, reduce and merge kernels)",
+                             "bound": "alu", "achieved": bflops / (b_ms * 1e-3) / 1e12,
+                             "peak": PUBLISHED_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
+                             "frac": bflops / (b_ms * 1e-3) / 1e12 / PUBLISHED_FP32_VECTOR_TFLOPS,
+                             "flops_per_unit": BWD_FLOPS_PER_STATE_STEP, "units": cfg.elements * cfg.dstate}}
 
 
 def config_record(cfg, vim, bwd, n_sets, front_k=0, ln=False, proj_r=0):
@@ -266,8 +352,141 @@ def stats(ms):
             "mean": float(np.mean(ms))}
 
 
+SES = 32  # shader engines (8 XCDs x 4); SQ_BUSY_CYCLES sums one count per engine
+CALIB_COPY_BYTES = 1 << 30  # the device copy bench.py runs after its timed steps
+
+
+def summarize(dirname):
+    """Text summary of rocprofv3 CSV output (the rule profiles/ is rendered by).
+
+    *_kernel_stats.csv (--kernel-trace --stats): calls and average / min / max duration per kernel.
+    *_counter_collection.csv (--pmc): per kernel, the mean over its dispatches of each counter (the
+    CSV holds one row per dispatch and counter; values summed over the device).  Derived, when the
+    counters are present:
+      * kernel cycles = SQ_BUSY_CYCLES / 32 (one count per shader engine while the kernel runs);
+      * VALU busy per SIMD = 4 SQ_ACTIVE_INST_VALU / (1024 x kernel cycles): SQ_ACTIVE_INST_VALU
+        counts quad-cycles of VALU issue (one per wave64 instruction, two per transcendental:
+        SQ_INSTS_VALU + SQ_INSTS_VALU_TRANS_F32 equals it), summed over all wavefronts;
+      * VALU instructions per wavefront = SQ_INSTS_VALU / SQ_WAVES;
+      * LDS bank conflicts per LDS instruction = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS (both in
+        cycles of the LDS pipe);
+      * HBM bytes = FETCH_SIZE and WRITE_SIZE (KiB per dispatch) times the factors that make the
+        1 GiB device copy of the same run read and write 1 GiB."""
+    import csv
+    import glob as _glob
+
+    out = []
+    for path in sorted(_glob.glob(os.path.join(dirname, "**", "*kernel_stats.csv"), recursive=True)):
+        out.append(f"# kernel stats: {os.path.relpath(path, dirname)}")
+        out.append(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}  kernel")
+        with open(path) as f:
+            rows = list(csv.DictReader(f))
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+            out.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} {float(r['MinNs']) / 1e3:10.1f} "
+                       f"{float(r['MaxNs']) / 1e3:10.1f}  {r['Name'][:160]}")
+    for path in sorted(_glob.glob(os.path.join(dirname, "**", "*counter_collection.csv"), recursive=True)):
+        out.append(f"# counters: {os.path.relpath(path, dirname)}")
+        per = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                k = (r["Kernel_Name"], r["Counter_Name"])
+                per.setdefault(k, {}).setdefault(r["Dispatch_Id"], 0.0)
+                per[k][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        kernels = {}
+        for (kn, cn), d in per.items():
+            kernels.setdefault(kn, {})[cn] = sum(d.values()) / len(d)
+        copy_name = next((k for k in kernels if "copy" in k.lower() or "Copy" in k), None)
+        fr = wr = None
+        if copy_name:
+            c = kernels[copy_name]
+            if c.get("FETCH_SIZE"):
+                fr = CALIB_COPY_BYTES / (c["FETCH_SIZE"] * 1024)
+            if c.get("WRITE_SIZE"):
+                wr = CALIB_COPY_BYTES / (c["WRITE_SIZE"] * 1024)
+            out.append(f"calibration ({copy_name[:60]}): FETCH_SIZE x {fr if fr else float('nan'):.3f}, "
+                       f"WRITE_SIZE x {wr if wr else float('nan'):.3f}")
+        for kn, c in sorted(kernels.items()):
+            out.append(kn[:200])
+            for cn in sorted(c):
+                out.append(f"  {cn:30s} {c[cn]:12.4g}")
+            if "SQ_BUSY_CYCLES" in c:
+                cyc = c["SQ_BUSY_CYCLES"] / SES
+                out.append(f"  {'kernel cycles (derived)':30s} {cyc:12.4g}")
+                if "SQ_ACTIVE_INST_VALU" in c:
+                    out.append(f"  {'VALU busy per SIMD (derived)':30s} {4 * c['SQ_ACTIVE_INST_VALU'] / (SIMDS * cyc):12.3f}")
+            if "SQ_INSTS_VALU" in c and c.get("SQ_WAVES"):
+                out.append(f"  {'VALU instr per wave (derived)':30s} {c['SQ_INSTS_VALU'] / c['SQ_WAVES']:12.4g}")
+            if "SQ_LDS_BANK_CONFLICT" in c and c.get("SQ_ACTIVE_INST_LDS"):
+                out.append(f"  {'bank conflict / LDS (derived)':30s} {c['SQ_LDS_BANK_CONFLICT'] / c['SQ_ACTIVE_INST_LDS']:12.3f}")
+            if fr and "FETCH_SIZE" in c:
+                out.append(f"  {'HBM read bytes (derived)':30s} {c['FETCH_SIZE'] * 1024 * fr:12.4g}")
+            if wr and "WRITE_SIZE" in c:
+                out.append(f"  {'HBM write bytes (derived)':30s} {c['WRITE_SIZE'] * 1024 * wr:12.4g}")
+    print("\n".join(out))
+
+
+def valu_probe():
+    """Issue rates of the vector unit, from the probe kernels' own clock stamps: per wavefront the
+    shader-clock and 100 MHz real-time counters around a loop of independent chains; with k
+    wavefronts per SIMD, cycles per instruction (one SIMD) = wavefront cycles / (k x instructions of
+    the wavefront).  Kinds: 0 FMA, 1 v_exp_f32, 2 the scan's mix per (element, state)."""
+    import ctypes
+
+    import torch
+
+    path = os.path.join(ROOT, "selective_scan_amd", "libss2d_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    lib.valu_probe_run.restype = ctypes.c_int
+    lib.valu_probe_run.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lib.valu_probe_insts_per_iter.restype = ctypes.c_int
+    lib.valu_probe_insts_per_iter.argtypes = [ctypes.c_int]
+    stream = torch.cuda.current_stream()
+    res = {"what": "SIMD cycles per wave64 instruction (FMA, v_exp_f32) and per 64 (element, state) units of "
+                   "the scan's mix (v_mul, v_exp_f32, v_mul, v_fma, v_fma per unit, plus one v_fma per 8 units), "
+                   "median over wavefronts, k wavefronts per SIMD", "runs": []}
+    names = {0: "fma", 1: "exp", 2: "scan_mix"}
+    for kind in (0, 1, 2):
+        ipi = lib.valu_probe_insts_per_iter(kind)
+        for k in (1, 2, 3):
+            waves = SIMDS * k
+            iters = 20000 if kind != 1 else 10000
+            stamps = torch.zeros(4 * waves, dtype=torch.int64, device="cuda")
+            sink = torch.empty(64 * waves, dtype=torch.float32, device="cuda")
+            for _ in range(2):  # the first launch warms the clocks up
+                st = lib.valu_probe_run(kind, waves, iters, ctypes.c_void_p(stamps.data_ptr()),
+                                        ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+                if st != 0:
+                    raise RuntimeError(f"valu_probe_run status {st}")
+                torch.cuda.synchronize()
+            t = stamps.view(-1, 4).cpu().numpy().astype(np.float64)
+            cyc = t[:, 1] - t[:, 0]
+            sec = (t[:, 3] - t[:, 2]) / 100e6
+            clock = float(np.median(cyc / sec))
+            # the whole launch, first wavefront start to last wavefront end (real-time counter),
+            # in cycles of the median clock: SIMD cycles for k * iters * ipi instructions per SIMD
+            span = (t[:, 3].max() - t[:, 2].min()) / 100e6 * clock
+            rec = {"kind": names[kind], "waves_per_simd": k, "clock_GHz": clock / 1e9,
+                   "launch_us": float((t[:, 3].max() - t[:, 2].min()) / 100.0),
+                   "cycles_per_instruction": float(span / (k * iters * ipi)),
+                   "wave_cycles_per_instruction": float(np.median(cyc) / (iters * ipi))}
+            if kind == 2:
+                units = iters * 64  # (element, state) units per lane and wavefront
+                rec["cycles_per_64_units"] = float(span / (k * units))
+            res["runs"].append(rec)
+    print(json.dumps(res))
+
+
 def main():
     args = parse()
+    if args.valu_probe:
+        valu_probe()
+        return
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every box here has a single "
               f"MI355X and no multi-GPU path is part of this library.", file=sys.stderr)
@@ -369,6 +588,10 @@ def main():
     scan_ms = [e[1].elapsed_time(e[2]) for e in evs]
     stage0_ms = [e[0].elapsed_time(e[1]) for e in evs]
 
+    # the training step on the same inputs (forward keeping its states, then the backward on them)
+    train = None
+    if not vim and not args.bwd and not args.no_train_step and proj is None and front is None and ln is None:
+        train = train_step_record(cfg, ss, synth, d0, stream, max(3, args.steps // 2), 2)
     # a plain device copy of known size in the same run: the practical HBM ceiling (its three
     # dispatches also calibrate the byte counters of a profiler run of this program)
     del sets, d0, plan0, dout0
@@ -412,11 +635,11 @@ def main():
                 "copy_ceiling_GBps": copy_gbps,
                 "frac_of_copy": hbm_gbps / copy_gbps},
         "roofline": {"kernel": ("direction" if vim else "route") + " scan (scan_fwd_kernel)", "bound": "alu",
-                     "achieved": achieved_tflops, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved_tflops / VALU_PEAK_TFLOPS, "traffic": traffic,
+                     "achieved": achieved_tflops, "peak": PUBLISHED_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved_tflops / PUBLISHED_FP32_VECTOR_TFLOPS, "traffic": traffic,
+                     "flops_per_unit": FLOPS_PER_STATE_STEP, "units_per_launch": elements * cfg.dstate,
+                     "unpacked_fp32_peak": VALU_PEAK_TFLOPS, "frac_of_unpacked_peak": achieved_tflops / VALU_PEAK_TFLOPS,
                      "mix_peak": MIX_PEAK_TFLOPS, "frac_of_mix_peak": achieved_tflops / MIX_PEAK_TFLOPS,
-                     "published_fp32_vector_peak": PUBLISHED_FP32_VECTOR_TFLOPS,
-                     "frac_of_published_peak": achieved_tflops / PUBLISHED_FP32_VECTOR_TFLOPS,
                      "ms_per_launch": scan_mean, "launch_ms": stats(scan_ms), "flops_per_launch": flops},
     }
     if single:
@@ -447,6 +670,8 @@ def main():
                            "bound": "mfma", "flops_per_step": pf, "stage0_ms": s_ms, "launch_ms": stats(stage0_ms),
                            "achieved_TFLOPs": pf / (s_ms * 1e-3) / 1e12, "peak_TFLOPs": FP32_MFMA_PEAK_TFLOPS,
                            "frac": pf / (s_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS}
+    if train is not None:
+        res["train_step"] = train
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds, args.bwd, front, ln, proj)
     print(json.dumps(res))

@@ -195,9 +195,20 @@ void scan_bwd_kernel(const ScanBwdParams p) {
   constexpr int kRW = 2 * NSL;  // per-step dB/dC values of a lane (its states' dB terms, then dC terms)
   constexpr int kLeft = reduce_left<kRW, kMinMask>();
   constexpr int kInner = (64 / NSL < kSub) ? 64 / NSL : kSub;       // steps whose states are held at once
+  // Deferred outputs (two lanes per channel, 16 states, vector rows, fp32 or SS2D dout): a
+  // sub-interval's du / ddelta stay in registers and its dB / dC sums in LDS until the next
+  // sub-interval has consumed its loads; only then are they stored, as 16-byte pieces.  A load
+  // that is waited for while stores are outstanding waits for the stores too (the wait counter
+  // covers both, and they complete out of order), so stores issued at the end of a sub-interval
+  // would be drained at the start of the next; issued after its loads, they drain while it
+  // computes.
+  constexpr bool kStage = kSplit == 2 && kVec && kPass == 0 && NS == 16 && kMode != 0 && kSub == 8 &&
+                          kInner == kSub;
+  constexpr int kRedStride = 2 * NS + 4;  // [step][dB states, dC states] (+4: no bank conflicts)
   __shared__ __align__(16) float sB[kTile * S];
   __shared__ __align__(16) float sC[kTile * S];
   __shared__ __align__(16) float sDt[kDtR > 0 ? kTile * kDtR : 4];
+  __shared__ __align__(16) float sRed[kStage ? kSub * kRedStride : 4];
 
   const int lane = threadIdx.x;
   const int part = lane % kSplit;
@@ -264,6 +275,40 @@ void scan_bwd_kernel(const ScanBwdParams p) {
   for (int n = 0; n < NSL; ++n) dA_acc[n] = 0.0f;
   float dD_acc = 0.0f, dbias_acc = 0.0f, lam_sum = 0.0f;
 
+  // deferred outputs of the last sub-interval (kStage): this lane's half of its channel's steps
+  float pd_du[4], pd_dd[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pd_du[k] = pd_dd[k] = 0.0f;
+  int64_t pd_s0 = -1;
+  auto flush = [&]() {
+    if constexpr (kStage) {
+      if (pd_s0 < 0) return;
+      const int64_t th = pd_s0 + 4 * part;  // this lane stores steps th .. th + 3 of its channel
+      if (active && th < t_end) {
+        Elem<T>::store4(static_cast<T*>(p.ddelta), row * L + th, make_float4(pd_dd[0], pd_dd[1], pd_dd[2], pd_dd[3]));
+        const float4 v = make_float4(pd_du[0], pd_du[1], pd_du[2], pd_du[3]);
+        if (kSS2D)
+          Elem<float>::store4(static_cast<float*>(p.du), row * L + th, v);
+        else
+          Elem<T>::store4(static_cast<T*>(p.du), row * L + th, v);
+      }
+      // dB / dC block sums: lane pair (2 r, 2 r + 1) stores the two halves of row r (dB state r
+      // for r < NS, else dC state r - NS)
+      const int r = lane >> 1, h = lane & 1, n = r % NS;
+      const int64_t t = pd_s0 + 4 * h;
+      if (n < N && t < t_end) {
+        float4 v;
+        v.x = sRed[(4 * h) * kRedStride + r];
+        v.y = sRed[(4 * h + 1) * kRedStride + r];
+        v.z = sRed[(4 * h + 2) * kRedStride + r];
+        v.w = sRed[(4 * h + 3) * kRedStride + r];
+        float* dst = (r < NS) ? p.dB_part : p.dC_part;
+        *reinterpret_cast<float4*>(dst + (((dblk * p.batch + b) * p.G + g) * N + n) * L + t) = v;
+      }
+      pd_s0 = -1;
+    }
+  };
+
   auto pair_sum = [&](float x) {
     if (kSplit == 2)
       x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
@@ -319,6 +364,13 @@ void scan_bwd_kernel(const ScanBwdParams p) {
         float h0[NSL];
 #pragma unroll
         for (int n = 0; n < NSL; ++n) h0[n] = h0_of(n);
+        if constexpr (kStage) {
+          // the previous sub-interval's outputs, now that this one's loads are in: the empty asm
+          // reads the loaded start state (so the loads are waited for here) and clobbers memory
+          // (so the stores below are not moved above it, into the wait)
+          asm volatile("" ::"v"(h0[0]), "v"(h0[NSL - 1]), "v"(lam[0]), "v"(dy[kSub - 1]) : "memory");
+          flush();
+        }
 #pragma unroll
         for (int pc = kSub / kInner - 1; pc >= 0; --pc) {
           float hstart[NSL];
@@ -385,7 +437,13 @@ void scan_bwd_kernel(const ScanBwdParams p) {
             }
             // dB / dC for (this step, this lane's states): sum over the channels of the block
             lane_transpose_reduce<kRW, kMinMask>(red, lane);
-            if (i < ns && reduce_writer<kRW, kMinMask>(lane)) {
+            if constexpr (kStage) {
+              static_assert(kLeft == 1, "one block total per writer lane");
+              if (i < ns && reduce_writer<kRW, kMinMask>(lane)) {
+                const int e = reduce_index<kRW, kMinMask>(lane, 0);  // e < NSL: dB, else dC (state n0 + e % NSL)
+                sRed[i * kRedStride + (e < NSL ? n0 + e : NS + n0 + e - NSL)] = red[0];
+              }
+            } else if (i < ns && reduce_writer<kRW, kMinMask>(lane)) {
               const int64_t t = s0 + i;
 #pragma unroll
               for (int r = 0; r < kLeft; ++r) {
@@ -398,7 +456,16 @@ void scan_bwd_kernel(const ScanBwdParams p) {
               }
             }
           }
-          if (active && part == 0) {
+          if constexpr (kStage) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              pd_du[k] = part ? o_du[4 + k] : o_du[k];
+              pd_dd[k] = part ? o_dd[4 + k] : o_dd[k];
+            }
+            pd_s0 = s0;
+            if (has_z && active && part == 0)
+              store_seg<T, kVec, kInner>(static_cast<T*>(p.dz) + row * L, o_dz, s0 + pc * kInner, t_end);
+          } else if (active && part == 0) {
             const int64_t sp = s0 + pc * kInner;
             store_seg<T, kVec, kInner>(static_cast<T*>(p.ddelta) + row * L, o_dd, sp, t_end);
             if (kSS2D)
@@ -520,13 +587,15 @@ void scan_bwd_kernel(const ScanBwdParams p) {
         load_seg<DT, kVec, kSub>(gv, dout_row, s0, t_end, L, rev);
         if (has_z) load_seg<T, kVec, kSub>(zv, z_row, s0, t_end, L, false);
         const float* ck = p.ckpt + ((s0 / kSub) * p.batch * p.dim + row) * N + n0;
-        // unconditional load (a state past N re-reads state n0, zeroed by a select)
-        seg_body(s0, q, dv, uv, gv, zv, [&](int n) {
-          const float v = ck[n < nvalid ? n : 0];
-          return (n < nvalid) ? v : 0.0f;
-        });
+        // unconditional loads (a state past N re-reads state n0, zeroed by a select), issued with
+        // the row loads so that one wait covers both
+        float ckv[NSL];
+#pragma unroll
+        for (int n = 0; n < NSL; ++n) ckv[n] = ck[n < nvalid ? n : 0];
+        seg_body(s0, q, dv, uv, gv, zv, [&](int n) { return (n < nvalid) ? ckv[n] : 0.0f; });
       }
     }
+    flush();  // the last sub-interval's outputs
   }
 
   if (!active) return;
