@@ -371,7 +371,7 @@ def summarize(dirname):
       * LDS bank conflicts per LDS instruction = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS (both in
         cycles of the LDS pipe);
       * HBM bytes = FETCH_SIZE and WRITE_SIZE (KiB per dispatch) times the factors that make the
-        1 GiB device copy of the same run read and write 1 GiB."""
+        1 GiB device copy of the same run (the copy kernel's largest dispatch) read and write 1 GiB."""
     import csv
     import glob as _glob
 
@@ -395,14 +395,16 @@ def summarize(dirname):
         kernels = {}
         for (kn, cn), d in per.items():
             kernels.setdefault(kn, {})[cn] = sum(d.values()) / len(d)
-        copy_name = next((k for k in kernels if "copy" in k.lower() or "Copy" in k), None)
+        copy_name = next((k for k in kernels if "copy" in k.lower()), None)
         fr = wr = None
         if copy_name:
-            c = kernels[copy_name]
-            if c.get("FETCH_SIZE"):
-                fr = CALIB_COPY_BYTES / (c["FETCH_SIZE"] * 1024)
-            if c.get("WRITE_SIZE"):
-                wr = CALIB_COPY_BYTES / (c["WRITE_SIZE"] * 1024)
+            # the 1 GiB copies are the copy kernel's largest dispatches (the program makes small
+            # device copies too)
+            big = lambda cn: max(per[(copy_name, cn)].values()) if (copy_name, cn) in per else 0.0
+            if big("FETCH_SIZE"):
+                fr = CALIB_COPY_BYTES / (big("FETCH_SIZE") * 1024)
+            if big("WRITE_SIZE"):
+                wr = CALIB_COPY_BYTES / (big("WRITE_SIZE") * 1024)
             out.append(f"calibration ({copy_name[:60]}): FETCH_SIZE x {fr if fr else float('nan'):.3f}, "
                        f"WRITE_SIZE x {wr if wr else float('nan'):.3f}")
         for kn, c in sorted(kernels.items()):

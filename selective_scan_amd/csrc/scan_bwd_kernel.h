@@ -569,11 +569,23 @@ void scan_bwd_kernel(const ScanBwdParams p) {
     }
   } else {
     // Two lanes per channel (full occupancy): each sub-interval loads its own values; the
-    // other resident wavefronts cover the latency.
+    // other resident wavefronts cover the latency.  SS2D rows with vector loads (the register
+    // budget allows it there) load the B/C words of the next tile (backwards) while this one
+    // computes.
+    constexpr bool kBCAhead = kSS2D && kVec && kDtR == 0 && kStage;
     const int64_t n_tiles = (t_end - t_begin + kTile - 1) / kTile;
+    BCStage<T, NS, kVec> nbc;
+    if (kBCAhead && n_tiles > 0) nbc.load(Bg, Cg, N, L, t_begin + (n_tiles - 1) * kTile, t_end, lane);
     for (int64_t jt = n_tiles - 1; jt >= 0; --jt) {
       const int64_t t0 = t_begin + jt * kTile;
-      stage_tile(t0);
+      if constexpr (!kBCAhead) {
+        stage_tile(t0);
+      } else {
+        __syncthreads();  // the previous tile's LDS reads are complete
+        nbc.template store<S>(sB, sC, lane);
+        __syncthreads();
+        if (jt > 0) nbc.load(Bg, Cg, N, L, t0 - kTile, t_end, lane);
+      }
 #pragma unroll 1
       for (int q = kSegsPerTile - 1; q >= 0; --q) {
         const int64_t s0 = t0 + int64_t(q) * kSub;

@@ -158,6 +158,10 @@ __device__ __forceinline__ void load_row(RowTile<T, kLen>& tile, const T* row, i
 // B/C staging: per lane, the raw values it copies into LDS for one tile.  The vector path keeps
 // the loaded words as they are (bf16 pairs, or fp32) and converts them only in store(), at the
 // next tile: converting at load time would make the prefetch wait for its own loads.
+// Work item j (a 4-step vector, or one element) covers state n = j % NS: consecutive lanes take
+// consecutive states, so that the LDS stores of a half-wavefront, at [step][state] with a row
+// stride of NS + 4 floats, fall on distinct banks from 16 states up (stepping through the steps
+// first put a half-wavefront's stores on 8 banks, four to a bank).
 template <typename T, int NS, bool kVec>
 struct BCStage {
   using Raw = typename std::conditional<sizeof(T) == 2, uint2, float4>::type;  // 4 steps of one state
@@ -188,7 +192,7 @@ struct BCStage {
 #pragma unroll
       for (int k = 0; k < kVecs; ++k) {
         const int j = lane + k * kWave;
-        const int n = j / (kTile / 4), q = j % (kTile / 4);
+        const int n = j % NS, q = j / NS;
         const int64_t off = int64_t(n < N ? n : N - 1) * L + t0 + 4 * q;
         Raw vb = *reinterpret_cast<const Raw*>(Bg + off), vc = *reinterpret_cast<const Raw*>(Cg + off);
         if (n >= N) vb = vc = raw_zero();
@@ -200,8 +204,8 @@ struct BCStage {
     if (kVec) {
 #pragma unroll
       for (int k = 0; k < kVecs; ++k) {
-        const int j = lane + k * kWave;            // vector id: n = j / (kTile/4), q = j % (kTile/4)
-        const int n = j / (kTile / 4), q = j % (kTile / 4);
+        const int j = lane + k * kWave;            // vector id: n = j % NS, q = j / NS
+        const int n = j % NS, q = j / NS;
         Raw vb = raw_zero(), vc = raw_zero();
         if (n < N && j < NS * kTile / 4 && t0 + 4 * q < t_end) {
           vb = *reinterpret_cast<const Raw*>(Bg + int64_t(n) * L + t0 + 4 * q);
@@ -213,8 +217,8 @@ struct BCStage {
     } else {
 #pragma unroll
       for (int k = 0; k < kElems; ++k) {
-        const int e = lane + k * kWave;            // element id: n = e / kTile, i = e % kTile
-        const int n = e / kTile, i = e % kTile;
+        const int e = lane + k * kWave;            // element id: n = e % NS, i = e / NS
+        const int n = e % NS, i = e / NS;
         float vb = 0.f, vc = 0.f;
         if (n < N && e < NS * kTile && t0 + i < t_end) {
           vb = Elem<T>::load(Bg, int64_t(n) * L + t0 + i);
@@ -234,7 +238,7 @@ struct BCStage {
       for (int k = 0; k < kVecs; ++k) {
         const int j = lane + k * kWave;
         if (j < NS * kTile / 4) {
-          const int n = j / (kTile / 4), q = j % (kTile / 4);
+          const int n = j % NS, q = j / NS;
           const float4 vb = to_f32(rb[k]), vc = to_f32(rc[k]);
           const float bb[4] = {vb.x, vb.y, vb.z, vb.w}, cc[4] = {vc.x, vc.y, vc.z, vc.w};
 #pragma unroll
@@ -249,7 +253,7 @@ struct BCStage {
       for (int k = 0; k < kElems; ++k) {
         const int e = lane + k * kWave;
         if (e < NS * kTile) {
-          const int n = e / kTile, i = e % kTile;
+          const int n = e % NS, i = e / NS;
           sB[i * S + n] = b[k] * kLn2;
           sC[i * S + n] = c[k];
         }
@@ -356,7 +360,10 @@ __device__ __forceinline__ void store_out(O* row, const float* y, int64_t t0, in
 // Store the first `count` (<= NS) of NS state values; 16-byte stores when NS and count allow.
 template <int NS>
 __device__ __forceinline__ void store_state(float* dst, const float* h, int count) {
-  if (NS % 4 == 0 && (count % 4) == 0) {
+  if (NS % 4 == 0 && count == NS) {  // every state real (the common case): 16-byte stores
+#pragma unroll
+    for (int n = 0; n < NS; n += 4) *reinterpret_cast<float4*>(dst + n) = make_float4(h[n], h[n + 1], h[n + 2], h[n + 3]);
+  } else if (NS % 4 == 0 && (count % 4) == 0) {
 #pragma unroll
     for (int n = 0; n < NS; n += 4)
       if (n < count) *reinterpret_cast<float4*>(dst + n) = make_float4(h[n], h[n + 1], h[n + 2], h[n + 3]);

@@ -268,8 +268,7 @@ void scan_fwd_kernel(const ScanFwdParams p) {
     // the state is complete here: keeps the next tile's arithmetic from being interleaved with
     // this one's (which would hold both tiles' temporaries at once).  A scheduling barrier, not an
     // inline-asm pin of h: the compiler waits for every outstanding global store (vmcnt(0)) before
-    // an inline-asm statement that redefines registers, which drained the tile's output and
-    // checkpoint stores here once per tile.
+    // an inline-asm statement that redefines registers.
     __builtin_amdgcn_sched_barrier(0);
   };
   for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * kTile) {

@@ -271,3 +271,56 @@ def test_ss2d_fwd_noalloc_host_checks(lib):
     assert lib.ss2d_fwd_noalloc(ctypes.byref(SS2DFwdArgs(**{**f, "dtype": 5})), None) == 2
     assert lib.ss2d_fwd_noalloc(ctypes.byref(SS2DFwdArgs(**{**f, "batch": 0})), None) == 0  # empty
     assert lib.ss2d_fwd_noalloc(None, None) == 1
+
+
+# Every exported prototype of include/ss2d.h: name -> parameter types (names dropped, whitespace
+# normalised).  A change to the boundary must change this table too.
+SIGNATURES = {
+    "ss2d_abi_version": ("int", ("void",)),
+    "ss2d_status_string": ("const char*", ("int",)),
+    "ss2d_cross_scan": ("int", ("const void*", "void*", "int64_t", "int64_t", "int64_t", "int64_t", "int",
+                                "hipStream_t")),
+    "ss2d_cross_merge": ("int", ("const void*", "void*", "int64_t", "int64_t", "int64_t", "int64_t", "int",
+                                 "hipStream_t")),
+    "selective_scan_workspace_bytes": ("size_t", ("int64_t",) * 5),
+    "selective_scan_fwd": ("int", ("const ss_fwd_args*", "hipStream_t")),
+    "selective_scan_bwd": ("int", ("const ss_bwd_args*", "hipStream_t")),
+    "selective_scan_step": ("int", ("const ss_step_args*", "hipStream_t")),
+    "ss2d_proj_workspace_bytes": ("size_t", ("int64_t",) * 6 + ("int",)),
+    "ss2d_workspace_bytes": ("size_t", ("int64_t",) * 5 + ("int",)),
+    "ss2d_fwd": ("int", ("const ss2d_fwd_args*", "hipStream_t")),
+    "ss2d_fwd_single_kernel": ("int", ("const ss2d_fwd_args*",)),
+    "ss2d_fwd_noalloc_max_workspace_bytes": ("size_t", ("void",)),
+    "ss2d_fwd_noalloc": ("int", ("const ss2d_fwd_args*", "hipStream_t")),
+    "ss2d_fwd_stage": ("int", ("const ss2d_fwd_args*", "int", "hipStream_t")),
+    "ss2d_bwd": ("int", ("const ss2d_bwd_args*", "hipStream_t")),
+    "vim_bidir_workspace_bytes": ("size_t", ("int64_t",) * 4 + ("int",)),
+    "vim_bidir_fwd": ("int", ("const vim_bidir_fwd_args*", "hipStream_t")),
+    "vim_bidir_fwd_stage": ("int", ("const vim_bidir_fwd_args*", "int", "hipStream_t")),
+    "vim_bidir_bwd": ("int", ("const vim_bidir_bwd_args*", "hipStream_t")),
+}
+
+
+def _prototypes():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"^\s*((?:const\s+)?\w+\s*\**)\s*(\w+)\s*\(([^)]*)\)\s*;", text, flags=re.M):
+        ret, name, params = re.sub(r"\s+", "", m.group(1)), m.group(2), m.group(3)
+        types = []
+        for prm in params.split(","):
+            prm = " ".join(prm.split())
+            if prm == "void":
+                types.append("void")
+                continue
+            # drop the parameter name: the last identifier
+            t = re.sub(r"\s*\b\w+$", "", prm).replace(" *", "*")
+            types.append(t)
+        out[name] = (ret.replace("constchar", "const char"), tuple(types))
+    return out
+
+
+def test_exported_signatures():
+    got = _prototypes()
+    assert set(got) == set(SIGNATURES), sorted(set(got) ^ set(SIGNATURES))
+    for name, want in SIGNATURES.items():
+        assert got[name] == want, (name, got[name])

@@ -160,6 +160,9 @@ PLANE_CASES = [
     (3, 8, 8, 5, 4, "f32", False, True, True),       # 15 planes (not a multiple of the 8 XCDs), L = 64
     (1, 63, 64, 3, 1, "bf16", True, True, True),     # the largest plane the LDS holds (L = 4032): 252 threads
     (1, 64, 63, 2, 4, "f32", True, True, True),      # the same at N = 4: four segments, the last one partial
+    (1, 48, 64, 4, 1, "bf16", True, True, True),     # L = 3072: 12 steps per thread (4-step loads)
+    (1, 48, 32, 4, 2, "f32", True, True, True),      # L = 1536 at N = 2: 6 steps per thread (2-step loads)
+    (2, 56, 56, 3, 1, "f32", True, True, True),      # the low-state grid: 14 steps per thread, 224 threads
 ]
 
 
