@@ -653,7 +653,7 @@ def main():
                            "traffic": load_traffic(cfg.name + ":plane", plane_kernel_source_hash()),
                            "frac_of_copy": gbps / copy_gbps, "ms_per_launch": scan_mean,
                            "launch_ms": stats(scan_ms), "bytes_per_launch": step_bytes,
-                           # what the counters show limiting it (profiles/plane_fwd_lowstate_56x56_counters.txt):
+                           # what the counters show limiting it (profiles/sq_counters_ss2d_fwd_lowstate_56x56_b128_d96_n1_bf16_noz.txt):
                            # VALU issue (softplus, decay and the two scan passes, ~27 instructions per
                            # route step), not HBM
                            "limiter": "valu"}
