@@ -236,8 +236,9 @@ typedef struct ss2d_fwd_args {
   int64_t batch, dim, height, width, dstate;
   int dtype;
   int delta_softplus;
-  int keep_states;         /* nonzero: the workspace also keeps the checkpoint states, so that
-                              ss2d_bwd can run with workspace_has_states (a training forward) */
+  int keep_states;         /* nonzero: the workspace also keeps the checkpoint states (and, with
+                              a gate, the fp32 pre-gate merged map), so that ss2d_bwd can run
+                              with workspace_has_states (a training forward) */
   /* Optional input front [S6 page, section 1: in the VSS block the SS2D input passes through a
    * depthwise convolution and SiLU]: with conv_w != NULL the four routes scan
    *   u = silu(pre),  pre[b,c,h,w] = conv_b[c] + sum_{i,j} conv_w[c,i,j] x[b,c,h+i-r,w+j-r]
@@ -320,8 +321,9 @@ int ss2d_fwd_stage(const ss2d_fwd_args* args, int stage, hipStream_t stream);
  *   dA         : (4, dim, dstate) fp32;  dDskip, ddelta_bias : (4, dim) fp32 (iff given)
  * Everything is overwritten.  The workspace (>= ss2d_workspace_bytes(...)) is required.  With
  * workspace_has_states == 0 the forward is recomputed inside it; otherwise it must hold what
- * ss2d_fwd with keep_states wrote for the same inputs (the transposed x, the route outputs and
- * the checkpoint states), untouched since, and the forward is not run again.  ss2d_bwd itself
+ * ss2d_fwd with keep_states wrote for the same inputs (the transposed x, the route outputs, the
+ * checkpoint states and, with a gate or the LayerNorm, the fp32 pre-gate merged map), untouched
+ * since, and the forward is not run again.  ss2d_bwd itself
  * overwrites the route outputs there (with the routes' input gradients), so a second backward on
  * the same workspace must pass workspace_has_states == 0. */
 typedef struct ss2d_bwd_args {

@@ -101,7 +101,9 @@ struct MergeGateArgs {
   void* dz;             // grid dtype
   float* dM;            // (batch, C, L) fp32 grid order
   float* dMT;           // (batch, C, L) fp32 column-major order
-  float* merged;        // (batch, C, L) fp32 scratch for the two-kernel fallback
+  float* merged;        // (batch, C, L) fp32: scratch for the two-kernel fallback, or the input
+  int merged_in;        // nonzero: merged already holds the pre-gate merged map (with the skip
+                        // term; a keep_states forward wrote it) and the routes are not read
   int64_t batch, C, H, W;
   int dtype;
 };

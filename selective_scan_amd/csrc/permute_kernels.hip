@@ -344,7 +344,9 @@ __global__ __launch_bounds__(kThreads) void merge_plane_kernel(MergeArgs a) {
 // in the merge, the skip term and an fp32 x are template parameters and the loads of up to
 // kMergeBatch iterations are issued before any is used.
 // kThreads: as in the merge (one wavefront for planes of up to 1024 pixels).
-template <typename T, bool kSkip, bool kXF32, int kThreads>
+// kM: the pre-gate merged map is read from a.merged (a keep_states forward wrote it, with the
+// same sum in the same order) instead of being formed from the routes; LDS then holds only dM.
+template <typename T, bool kSkip, bool kXF32, int kThreads, bool kM = false>
 __global__ __launch_bounds__(kThreads) void merge_gate_bwd_plane_kernel(MergeGateArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int H = int(a.H), Wd = int(a.W);
@@ -352,14 +354,16 @@ __global__ __launch_bounds__(kThreads) void merge_gate_bwd_plane_kernel(MergeGat
   const int ldc = H + 1, ldr = Wd + 1;
   float* t1 = reinterpret_cast<float*>(smem);
   float* t3 = t1 + Wd * ldc;
-  float* tm = t3 + Wd * ldc;  // [h][w]
+  float* tm = kM ? t1 : t3 + Wd * ldc;  // [h][w]
   const int64_t plane = int64_t(blockIdx.x);
   const int64_t b = plane / a.C, c = plane % a.C;
   const float* r0 = a.routes + (b * 4 * a.C + c) * L;
   const float* r1 = r0 + a.C * L;
   const float* r2 = r1 + a.C * L;
   const float* r3 = r2 + a.C * L;
+  const float* mg = a.merged + plane * L;
   constexpr int kStep = 4 * kThreads;
+  if (!kM)
   for (int t0 = 4 * int(threadIdx.x); t0 < L; t0 += kStep * kMergeBatch) {
     float4 v1[kMergeBatch], v3[kMergeBatch];
 #pragma unroll
@@ -397,8 +401,13 @@ __global__ __launch_bounds__(kThreads) void merge_gate_bwd_plane_kernel(MergeGat
 #pragma unroll
     for (int e = 0; e < kMergeBatch; ++e) {
       const int p = p0 + kStep * e, pc = p < L ? p : 0;
-      v0[e] = *reinterpret_cast<const float4*>(r0 + pc);
-      v2[e] = *reinterpret_cast<const float4*>(r2 + (L - 4 - pc));
+      if constexpr (kM) {
+        v0[e] = *reinterpret_cast<const float4*>(mg + pc);
+        v2[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {
+        v0[e] = *reinterpret_cast<const float4*>(r0 + pc);
+        v2[e] = *reinterpret_cast<const float4*>(r2 + (L - 4 - pc));
+      }
       if constexpr (kSkip) xv[e] = kXF32 ? Elem<float>::load4(xf, pc) : Elem<T>::load4(xg, pc);
       zv[e] = Elem<T>::load4(zg, pc);
       gv[e] = Elem<T>::load4(gg, pc);
@@ -415,10 +424,13 @@ __global__ __launch_bounds__(kThreads) void merge_gate_bwd_plane_kernel(MergeGat
       int h = p / Wd, w = p - h * Wd;  // one division; the quad's pixels follow along the row
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float m = a0[j] + t1[w * ldc + h];
-        m = m + a2[j];
-        m = m + t3[w * ldc + h];
-        if (kSkip) m = fmaf(dsum, xs[j], m);
+        float m = a0[j];
+        if constexpr (!kM) {
+          m = m + t1[w * ldc + h];
+          m = m + a2[j];
+          m = m + t3[w * ldc + h];
+          if (kSkip) m = fmaf(dsum, xs[j], m);
+        }
         const float sz = sigmoid(zs[j]);
         dm[j] = gs[j] * zs[j] * sz;
         dz[j] = gs[j] * m * sz * (1.0f + zs[j] * (1.0f - sz));
@@ -646,7 +658,12 @@ template <int kThreads>
 static void launch_merge_gate_bwd_t(const MergeGateArgs& a, dim3 g, size_t lds, hipStream_t s) {
   const dim3 b{kThreads};
   const bool skip = a.Dskip != nullptr && a.x != nullptr;
-  if (a.dtype == 0) {
+  if (a.merged_in) {
+    if (a.dtype == 0)
+      merge_gate_bwd_plane_kernel<float, false, false, kThreads, true><<<g, b, lds, s>>>(a);
+    else
+      merge_gate_bwd_plane_kernel<bf16, false, false, kThreads, true><<<g, b, lds, s>>>(a);
+  } else if (a.dtype == 0) {
     if (skip)
       merge_gate_bwd_plane_kernel<float, true, true, kThreads><<<g, b, lds, s>>>(a);
     else
@@ -663,11 +680,11 @@ static void launch_merge_gate_bwd_t(const MergeGateArgs& a, dim3 g, size_t lds, 
 
 hipError_t launch_merge_gate_bwd(const MergeGateArgs& a, hipStream_t s) {
   const int64_t L = a.H * a.W;
-  const size_t lds = (size_t(2) * size_t(a.W) * size_t(a.H + 1) + size_t(a.H) * size_t(a.W + 1)) * 4;
+  const size_t lds = ((a.merged_in ? 0 : size_t(2) * size_t(a.W) * size_t(a.H + 1)) + size_t(a.H) * size_t(a.W + 1)) * 4;
   const uintptr_t io = reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.z) |
                        reinterpret_cast<uintptr_t>(a.dout) | reinterpret_cast<uintptr_t>(a.dz);
   if (a.z && lds <= 64 * 1024 && L % 4 == 0 && a.batch * a.C > 0 && aligned16(a.routes) && aligned16(a.dM) &&
-      aligned16(a.dMT) && (io & (a.dtype == 0 ? 15 : 7)) == 0 && (!a.x_f32 || aligned16(a.x))) {
+      aligned16(a.dMT) && aligned16(a.merged) && (io & (a.dtype == 0 ? 15 : 7)) == 0 && (!a.x_f32 || aligned16(a.x))) {
     const dim3 g{uint32_t(a.batch * a.C)};
     if (L <= 1024)
       launch_merge_gate_bwd_t<64>(a, g, lds, s);
@@ -675,8 +692,9 @@ hipError_t launch_merge_gate_bwd(const MergeGateArgs& a, hipStream_t s) {
       launch_merge_gate_bwd_t<kPlaneThreads>(a, g, lds, s);
     return hipGetLastError();
   }
-  // two kernels: the pre-gate merge into `merged` (only needed with a gate), then the gate
-  if (a.z) {
+  // two kernels: the pre-gate merge into `merged` (only needed with a gate, and not when the
+  // forward left it there), then the gate
+  if (a.z && !a.merged_in) {
     MergeArgs m{};
     m.routes = a.routes;
     m.routes_f32 = 1;

@@ -503,6 +503,9 @@ static int ss2d_merge_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, hipSt
   if (!a->layer_norm) {
     m.z = a->z;
     m.y = a->out;
+    // a training forward with a gate keeps the fp32 pre-gate map: the gate's backward reads it
+    // instead of the four route outputs
+    if (a->keep_states && a->z) m.merged_f32 = reinterpret_cast<float*>(at(a->workspace, lay.off_merged));
     return status_from(launch_merge(m, stream));
   }
   // with the LayerNorm: the fp32 merged map, then the normalisation and the gate per pixel
@@ -1030,19 +1033,21 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
     // then dz, dM (grid order) and the parameter partials per pixel block, then dM transposed
     float* merged = reinterpret_cast<float*>(at(a->workspace, lay.off_merged));
     float* dM = reinterpret_cast<float*>(at(a->workspace, lay.off_dM));
-    MergeArgs m{};
-    m.routes = at(a->workspace, lay.off_ys);
-    m.routes_f32 = 1;
-    m.x = u;
-    m.x_f32 = (a->conv_w != nullptr || a->x_proj_w != nullptr);
-    m.Dskip = a->Dskip;
-    m.merged_f32 = merged;
-    m.batch = a->batch;
-    m.C = a->dim;
-    m.H = a->height;
-    m.W = a->width;
-    m.dtype = a->dtype;
-    if (launch_merge(m, stream) != hipSuccess) return SS2D_ERR_HIP;
+    if (!a->workspace_has_states) {  // (a keep_states forward left the merged map there)
+      MergeArgs m{};
+      m.routes = at(a->workspace, lay.off_ys);
+      m.routes_f32 = 1;
+      m.x = u;
+      m.x_f32 = (a->conv_w != nullptr || a->x_proj_w != nullptr);
+      m.Dskip = a->Dskip;
+      m.merged_f32 = merged;
+      m.batch = a->batch;
+      m.C = a->dim;
+      m.H = a->height;
+      m.W = a->width;
+      m.dtype = a->dtype;
+      if (launch_merge(m, stream) != hipSuccess) return SS2D_ERR_HIP;
+    }
     LnArgs l{};
     l.M = merged;
     l.w = a->ln_w;
@@ -1077,6 +1082,7 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
     gb.dM = reinterpret_cast<float*>(at(a->workspace, lay.off_dM));
     gb.dMT = reinterpret_cast<float*>(at(a->workspace, lay.off_dMT));
     gb.merged = reinterpret_cast<float*>(at(a->workspace, lay.off_merged));
+    gb.merged_in = (a->workspace_has_states && a->z) ? 1 : 0;
     gb.batch = a->batch;
     gb.C = a->dim;
     gb.H = a->height;
