@@ -53,11 +53,12 @@ struct RowTile<bf16, kLen> {
     return (i % 2 == 0) ? bf16lo(w) : bf16hi(w);
   }
   // element i + sel of an even i, sel in {0, 1} chosen per lane: both halves of one dword, the
-  // wanted one moved to the top by a per-lane shift
+  // wanted one moved to the top and the other cleared by one byte permute with a per-lane
+  // selector (bytes 1, 0 or 3, 2 of the dword into bytes 3, 2; selector byte 0x0c gives zero)
   __device__ __forceinline__ float get_pair(int i, int sel) const {
     const uint2 q = v[i / 4];
     const uint32_t w = ((i % 4) < 2) ? q.x : q.y;
-    return __uint_as_float((w << (sel ? 0 : 16)) & 0xffff0000u);
+    return __uint_as_float(__builtin_amdgcn_perm(w, w, sel ? 0x03020c0cu : 0x01000c0cu));
   }
   // every element set to the bf16 value with bit pattern `bits` (low 16 bits)
   __device__ __forceinline__ void fill(uint32_t bits) {

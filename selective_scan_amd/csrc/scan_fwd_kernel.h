@@ -259,8 +259,12 @@ void scan_fwd_kernel(const ScanFwdParams p) {
             store_seg<float, kVec, 4>(static_cast<float*>(p.out) + row * L, y, tg, t_end);
           else
             store_seg<T, kVec, 4>(static_cast<T*>(p.out) + row * L, y, tg, t_end);
+        } else if constexpr (kVec) {
+          // route outputs stay fp32 until the merge has added them: the result is rounded once.
+          // The group is in range (groups at or past the end of the range exit the tile loop
+          // above, and vector rows have L and the chunk ends a multiple of 4), so no bounds test.
+          Elem<float>::store4(static_cast<float*>(p.out) + row * L, tg, make_float4(y[0], y[1], y[2], y[3]));
         } else {
-          // route outputs stay fp32 until the merge has added them: the result is rounded once
           store_seg<float, kVec, 4>(static_cast<float*>(p.out) + row * L, y, tg, t_end);
         }
       }
