@@ -599,11 +599,23 @@ void scan_bwd_kernel(const ScanBwdParams p) {
         load_seg<DT, kVec, kSub>(gv, dout_row, s0, t_end, L, rev);
         if (has_z) load_seg<T, kVec, kSub>(zv, z_row, s0, t_end, L, false);
         const float* ck = p.ckpt + ((s0 / kSub) * p.batch * p.dim + row) * N + n0;
-        // unconditional loads (a state past N re-reads state n0, zeroed by a select), issued with
-        // the row loads so that one wait covers both
+        // issued with the row loads so that one wait covers both: 16-byte loads when every state
+        // is real (N == NS, the state rows are then 16-byte aligned pieces), else one load per
+        // state (a state past N re-reads state n0, zeroed by a select)
         float ckv[NSL];
+        if (NSL % 4 == 0 && N == NS) {
 #pragma unroll
-        for (int n = 0; n < NSL; ++n) ckv[n] = ck[n < nvalid ? n : 0];
+          for (int j = 0; j < NSL / 4; ++j) {
+            const float4 c4 = *reinterpret_cast<const float4*>(ck + 4 * j);
+            ckv[4 * j] = c4.x; ckv[4 * j + 1] = c4.y; ckv[4 * j + 2] = c4.z; ckv[4 * j + 3] = c4.w;
+          }
+        } else {
+          // (volatile: kept apart from the vector loads, which the compiler would otherwise merge
+          // with these into one set of per-state loads for both cases)
+          const volatile float* ckq = ck;
+#pragma unroll
+          for (int n = 0; n < NSL; ++n) ckv[n] = ckq[n < nvalid ? n : 0];
+        }
         seg_body(s0, q, dv, uv, gv, zv, [&](int n) { return (n < nvalid) ? ckv[n] : 0.0f; });
       }
     }
