@@ -17,7 +17,8 @@
 //   combine: the pair (S, h_loc) is the affine map h -> 2^(A S) h + h_loc of its steps; the
 //            maps compose as (S1, h1) then (S2, h2) = (S1 + S2, 2^(A S2) h1 + h2), an
 //            associative operator, scanned over the lanes with shuffles and over the four
-//            wavefronts through LDS, and applied to the state carried in from the last segment;
+//            wavefronts through LDS, and applied to the state carried in from the last segment
+//            (with one state the pair holds P = 2^(A S) instead of S: (P1 P2, P2 h1 + h2));
 //   pass 2: the thread reruns its steps from its true start state and writes y.
 // The per-step decays and inputs of pass 1 stay in registers for pass 2.  Arithmetic is in base
 // 2 as in the route scans (Lam = log2(1 + 2^(v log2 e)), decay 2^(Lam A)); the state is carried
@@ -29,8 +30,8 @@
 // 16-quad group stored at Q ^ ((Q >> 4) & 3), so that a wavefront reading or writing 16-step
 // chunks as 16-byte pieces hits distinct banks).  Routes 0 and 2 write their outputs into the
 // sum directly (their steps are pixels, forwards or backwards); routes 1 and 3 write theirs in
-// column-major order, which is then folded into the sum pixel by pixel.  Route order keeps the
-// sum ((y0 + y1) + y2) + y3.
+// column-major order, which is then folded into the sum pixel by pixel (one add per pixel, in
+// 4 x 4 blocks when H and W are multiples of 4).  Route order keeps the sum ((y0 + y1) + y2) + y3.
 #include <type_traits>
 
 #include "device_common.h"
@@ -122,7 +123,24 @@ __global__ __launch_bounds__(kPT) void plane_fwd_kernel(const PlaneFwdArgs a) {
     }
   }
   __syncthreads();
-  {  // column-major index t is pixel (h, w) = (t % H, t / H)
+  // With H and W multiples of 4 the plane is cut into 4 x 4 blocks: a block's four row quads
+  // (row-major, 16 bytes each) are its four column quads transposed (column-major index
+  // w H + h, also 16 bytes each), so a thread moves a block with eight 16-byte LDS accesses.
+  // Other shapes go element by element.
+  const bool blocks4 = (H & 3) == 0 && (Wd & 3) == 0;
+  const int Wq = Wd >> 2, nblk = (H >> 2) * Wq;
+  if (blocks4) {  // block (bh, bw): rows 4 bh .. 4 bh + 3, columns 4 bw .. 4 bw + 3
+    for (int blk = tid; blk < nblk; blk += kPT) {
+      const int bh = blk / Wq, h = 4 * bh, w = 4 * (blk - bh * Wq);
+      float4 r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = *reinterpret_cast<const float4*>(sxR + swz((h + i) * Wd + w));
+      *reinterpret_cast<float4*>(sxT + swz(w * H + h)) = make_float4(r[0].x, r[1].x, r[2].x, r[3].x);
+      *reinterpret_cast<float4*>(sxT + swz((w + 1) * H + h)) = make_float4(r[0].y, r[1].y, r[2].y, r[3].y);
+      *reinterpret_cast<float4*>(sxT + swz((w + 2) * H + h)) = make_float4(r[0].z, r[1].z, r[2].z, r[3].z);
+      *reinterpret_cast<float4*>(sxT + swz((w + 3) * H + h)) = make_float4(r[0].w, r[1].w, r[2].w, r[3].w);
+    }
+  } else {  // column-major index t is pixel (h, w) = (t % H, t / H)
     DivWalk dw(tid, kPT, H);
     for (int t = tid, st = swz(tid); t < L; t += kPT, st += kPT, dw.next()) sxT[st] = sxR[swz(dw.r * Wd + dw.q)];
   }
@@ -189,13 +207,17 @@ __global__ __launch_bounds__(kPT) void plane_fwd_kernel(const PlaneFwdArgs a) {
           }
         }
       }
-      // pass 1: this thread's map (S, h_loc)
-      float S = 0.0f, hl[NS];
+      // pass 1: this thread's map (S, h_loc).  With one state the map carries its decay
+      // P = 2^(A S) itself, the product of its steps' decays: two maps then compose with a
+      // multiply and an FMA, no exp.  With more states S is shared by all of them.
+      constexpr bool kProd = NS == 1;
+      auto decay = [&](int n, float s) { return kProd ? s : fast_exp2(Ak[n] * s); };
+      float S = kProd ? 1.0f : 0.0f, hl[NS];
 #pragma unroll
       for (int n = 0; n < NS; ++n) hl[n] = 0.0f;
 #pragma unroll
       for (int i = 0; i < kT; ++i) {
-        S += lam[i];
+        S = kProd ? S * aa[i][0] : S + lam[i];
 #pragma unroll
         for (int n = 0; n < NS; ++n) hl[n] = fmaf(aa[i][n], hl[n], bu[i][n]);
       }
@@ -208,15 +230,15 @@ __global__ __launch_bounds__(kPT) void plane_fwd_kernel(const PlaneFwdArgs a) {
         for (int n = 0; n < NS; ++n) ho[n] = __shfl_up(hl[n], off);
         if (lane >= off) {
 #pragma unroll
-          for (int n = 0; n < NS; ++n) hl[n] = fmaf(fast_exp2(Ak[n] * S), ho[n], hl[n]);
-          S += So;
+          for (int n = 0; n < NS; ++n) hl[n] = fmaf(decay(n, S), ho[n], hl[n]);
+          S = kProd ? S * So : S + So;
         }
       }
       float Se = __shfl_up(S, 1), he[NS];
 #pragma unroll
       for (int n = 0; n < NS; ++n) he[n] = __shfl_up(hl[n], 1);
       if (lane == 0) {
-        Se = 0.0f;
+        Se = kProd ? 1.0f : 0.0f;
 #pragma unroll
         for (int n = 0; n < NS; ++n) he[n] = 0.0f;
       }
@@ -238,13 +260,13 @@ __global__ __launch_bounds__(kPT) void plane_fwd_kernel(const PlaneFwdArgs a) {
         const float Sw = wt[w2 * (NS + 1)];
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
-          carry[n] = fmaf(fast_exp2(Ak[n] * Sw), carry[n], wt[w2 * (NS + 1) + 1 + n]);
+          carry[n] = fmaf(decay(n, Sw), carry[n], wt[w2 * (NS + 1) + 1 + n]);
           if (w2 + 1 == wv) st[n] = carry[n];
         }
       }
       float h[NS];
 #pragma unroll
-      for (int n = 0; n < NS; ++n) h[n] = fmaf(fast_exp2(Ak[n] * Se), st[n], he[n]);
+      for (int n = 0; n < NS; ++n) h[n] = fmaf(decay(n, Se), st[n], he[n]);
       // pass 2: outputs from the true start state
       float y[kT];
 #pragma unroll
@@ -277,8 +299,27 @@ __global__ __launch_bounds__(kPT) void plane_fwd_kernel(const PlaneFwdArgs a) {
     }
     if constexpr (kCol) {  // fold into the sum, pixel p = (h, w) <- column-major index w H + h
       __syncthreads();
-      DivWalk dw(tid, kPT, Wd);
-      for (int p = tid, sp = swz(tid); p < L; p += kPT, sp += kPT, dw.next()) sacc[sp] += syb[swz(dw.r * H + dw.q)];
+      if (blocks4) {  // one add per pixel, as below: the column quads of a block, transposed
+        for (int blk = tid; blk < nblk; blk += kPT) {
+          const int bh = blk / Wq, h = 4 * bh, w = 4 * (blk - bh * Wq);
+          float4 c[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) c[j] = *reinterpret_cast<const float4*>(syb + swz((w + j) * H + h));
+          const float cr[4][4] = {{c[0].x, c[1].x, c[2].x, c[3].x},
+                                  {c[0].y, c[1].y, c[2].y, c[3].y},
+                                  {c[0].z, c[1].z, c[2].z, c[3].z},
+                                  {c[0].w, c[1].w, c[2].w, c[3].w}};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float4* dst = reinterpret_cast<float4*>(sacc + swz((h + i) * Wd + w));
+            const float4 o = *dst;
+            *dst = make_float4(o.x + cr[i][0], o.y + cr[i][1], o.z + cr[i][2], o.w + cr[i][3]);
+          }
+        }
+      } else {
+        DivWalk dw(tid, kPT, Wd);
+        for (int p = tid, sp = swz(tid); p < L; p += kPT, sp += kPT, dw.next()) sacc[sp] += syb[swz(dw.r * H + dw.q)];
+      }
       // (the next route's segment barrier orders this fold before the sum or syb is rewritten)
     }
   };

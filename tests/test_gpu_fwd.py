@@ -149,7 +149,7 @@ def test_ss2d_fwd(case):
 PLANE_CASES = [
     # batch, H, W, dim, N, dtype, z, softplus, skip term
     (2, 8, 8, 16, 1, "f32", True, True, True),
-    (1, 6, 12, 24, 2, "bf16", True, True, True),     # H != W
+    (1, 6, 12, 24, 2, "bf16", True, True, True),     # H != W, H % 4 != 0: the element-wise transpose and fold
     (2, 40, 40, 8, 4, "f32", True, True, True),      # N = 4: two segments of 1024 steps
     (1, 56, 56, 6, 4, "bf16", True, True, True),     # four segments, the last one partial
     (1, 56, 56, 6, 2, "f32", False, True, False),    # two segments of 2048, no gate, no skip term
@@ -160,9 +160,9 @@ PLANE_CASES = [
     (3, 8, 8, 5, 4, "f32", False, True, True),       # 15 planes (not a multiple of the 8 XCDs), L = 64
     (1, 63, 64, 3, 1, "bf16", True, True, True),     # the largest plane the LDS holds (L = 4032): 252 threads
     (1, 64, 63, 2, 4, "f32", True, True, True),      # the same at N = 4: four segments, the last one partial
-    (1, 48, 64, 4, 1, "bf16", True, True, True),     # L = 3072: 12 steps per thread (4-step loads)
-    (1, 48, 32, 4, 2, "f32", True, True, True),      # L = 1536 at N = 2: 6 steps per thread (2-step loads)
-    (2, 56, 56, 3, 1, "f32", True, True, True),      # the low-state grid: 14 steps per thread, 224 threads
+    (1, 48, 64, 4, 1, "bf16", True, True, True),     # L = 3072: 192 threads of 16 steps, one idle wavefront
+    (1, 48, 32, 4, 2, "f32", True, True, True),      # L = 1536 at N = 2: 192 threads of 8 steps
+    (2, 56, 56, 3, 1, "f32", True, True, True),      # the low-state grid: 196 threads of 16 steps, 4 x 4 blocks
 ]
 
 
