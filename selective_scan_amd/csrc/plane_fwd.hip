@@ -25,8 +25,9 @@
 // as h / ln 2 (input Lam u B), so the route outputs and their sum are y / ln 2, scaled once per
 // pixel before the skip term.
 //
-// LDS (fp32, four arrays of L): x in row-major and in column-major order, the route sum in
-// row-major order and the column-major routes' outputs, all in "chunk" layout (quad Q of each
+// LDS (four arrays of L): the column-major routes' outputs and the route sum in row-major order
+// (fp32), and x in row-major and in column-major order (in the I/O type: bf16 words are exact,
+// and 12 instead of 16 bytes per pixel let four planes share a CU), all in "chunk" layout (quad Q of each
 // 16-quad group stored at Q ^ ((Q >> 4) & 3), so that a wavefront reading or writing 16-step
 // chunks as 16-byte pieces hits distinct banks).  Routes 0 and 2 write their outputs into the
 // sum directly (their steps are pixels, forwards or backwards); routes 1 and 3 write theirs in
@@ -80,6 +81,43 @@ struct Ld<bf16> {
   }
 };
 
+// x in LDS in its own type: bf16 maps keep their 16-bit words (exact), fp32 maps fp32.  A quad is
+// four consecutive elements of the chunk layout (16 or 8 bytes).
+template <typename T>
+struct XQ;
+template <>
+struct XQ<float> {
+  using E = float;
+  using Q = float4;
+  __device__ __forceinline__ static float4 get(const E* p) { return *reinterpret_cast<const float4*>(p); }
+  // the 4 x 4 block of rows r[0..3] transposed: column j of the block as a quad
+  __device__ __forceinline__ static void transpose(const Q* r, Q* c) {
+    c[0] = make_float4(r[0].x, r[1].x, r[2].x, r[3].x);
+    c[1] = make_float4(r[0].y, r[1].y, r[2].y, r[3].y);
+    c[2] = make_float4(r[0].z, r[1].z, r[2].z, r[3].z);
+    c[3] = make_float4(r[0].w, r[1].w, r[2].w, r[3].w);
+  }
+};
+template <>
+struct XQ<bf16> {
+  using E = uint16_t;
+  using Q = uint2;
+  __device__ __forceinline__ static float4 get(const E* p) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    return make_float4(bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y));
+  }
+  // words (e0 | e1 << 16, e2 | e3 << 16) per row; column j takes the same half of two rows' words
+  // (byte permute: selector 0x05040100 joins the low halves of its second and first operand,
+  // 0x07060302 the high halves)
+  __device__ __forceinline__ static void transpose(const Q* r, Q* c) {
+    constexpr uint32_t kLo = 0x05040100u, kHi = 0x07060302u;
+    c[0] = make_uint2(__builtin_amdgcn_perm(r[1].x, r[0].x, kLo), __builtin_amdgcn_perm(r[3].x, r[2].x, kLo));
+    c[1] = make_uint2(__builtin_amdgcn_perm(r[1].x, r[0].x, kHi), __builtin_amdgcn_perm(r[3].x, r[2].x, kHi));
+    c[2] = make_uint2(__builtin_amdgcn_perm(r[1].y, r[0].y, kLo), __builtin_amdgcn_perm(r[3].y, r[2].y, kLo));
+    c[3] = make_uint2(__builtin_amdgcn_perm(r[1].y, r[0].y, kHi), __builtin_amdgcn_perm(r[3].y, r[2].y, kHi));
+  }
+};
+
 // (q, r) = divmod(i, n) along i = i0, i0 + s, i0 + 2s, ... (i0, s >= 0)
 struct DivWalk {
   int q, r, dq, dr, n;
@@ -102,25 +140,24 @@ __global__ __launch_bounds__(kPT) void plane_fwd_kernel(const PlaneFwdArgs a) {
   constexpr int kG = kT < 8 ? kT : 8;  // elements per global load
   constexpr int kSeg = kPT * kT;
   extern __shared__ __align__(16) float smem[];
+  using XE = typename XQ<T>::E;
+  using XQd = typename XQ<T>::Q;
   const int H = int(a.H), Wd = int(a.W), L = H * Wd;
   const int Ls = (L + 15) & ~15;
-  float* sxR = smem;       // x, row-major (routes 0, 2), chunk layout
-  float* sxT = sxR + Ls;   // x, column-major (routes 1, 3), chunk layout
-  float* syb = sxT + Ls;   // route 1 / 3 outputs, column-major, chunk layout
-  float* sacc = syb + Ls;  // the route sum, row-major, chunk layout
+  float* syb = smem;                            // route 1 / 3 outputs, column-major, chunk layout
+  float* sacc = syb + Ls;                       // the route sum, row-major, chunk layout
+  XE* sxR = reinterpret_cast<XE*>(sacc + Ls);  // x, row-major (routes 0, 2), chunk layout
+  XE* sxT = sxR + Ls;                          // x, column-major (routes 1, 3), chunk layout
   __shared__ float wtot[2][kPWaves][NS + 1];
 
   const int tid = int(threadIdx.x), lane = tid % kWave, wv = tid / kWave;
   const int64_t plane = xcd_remap(blockIdx.x, gridDim.x);  // b * dim + d
   const int64_t b = plane / a.dim, d = plane - b * a.dim;
 
-  {  // x -> sxR
-    const T* xg = static_cast<const T*>(a.x) + plane * L;
-    for (int p = 4 * tid; p < L; p += 4 * kPT) {
-      float v[4];
-      Ld<T>::template get<4>(xg, p, v);
-      *reinterpret_cast<float4*>(sxR + swz(p)) = make_float4(v[0], v[1], v[2], v[3]);
-    }
+  {  // x -> sxR (quads copied as they are)
+    const XE* xg = reinterpret_cast<const XE*>(static_cast<const T*>(a.x) + plane * L);
+    for (int p = 4 * tid; p < L; p += 4 * kPT)
+      *reinterpret_cast<XQd*>(sxR + swz(p)) = *reinterpret_cast<const XQd*>(xg + p);
   }
   __syncthreads();
   // With H and W multiples of 4 the plane is cut into 4 x 4 blocks: a block's four row quads
@@ -132,13 +169,12 @@ __global__ __launch_bounds__(kPT) void plane_fwd_kernel(const PlaneFwdArgs a) {
   if (blocks4) {  // block (bh, bw): rows 4 bh .. 4 bh + 3, columns 4 bw .. 4 bw + 3
     for (int blk = tid; blk < nblk; blk += kPT) {
       const int bh = blk / Wq, h = 4 * bh, w = 4 * (blk - bh * Wq);
-      float4 r[4];
+      XQd r[4], cq[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = *reinterpret_cast<const float4*>(sxR + swz((h + i) * Wd + w));
-      *reinterpret_cast<float4*>(sxT + swz(w * H + h)) = make_float4(r[0].x, r[1].x, r[2].x, r[3].x);
-      *reinterpret_cast<float4*>(sxT + swz((w + 1) * H + h)) = make_float4(r[0].y, r[1].y, r[2].y, r[3].y);
-      *reinterpret_cast<float4*>(sxT + swz((w + 2) * H + h)) = make_float4(r[0].z, r[1].z, r[2].z, r[3].z);
-      *reinterpret_cast<float4*>(sxT + swz((w + 3) * H + h)) = make_float4(r[0].w, r[1].w, r[2].w, r[3].w);
+      for (int i = 0; i < 4; ++i) r[i] = *reinterpret_cast<const XQd*>(sxR + swz((h + i) * Wd + w));
+      XQ<T>::transpose(r, cq);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<XQd*>(sxT + swz((w + j) * H + h)) = cq[j];
     }
   } else {  // column-major index t is pixel (h, w) = (t % H, t / H)
     DivWalk dw(tid, kPT, H);
@@ -150,7 +186,7 @@ __global__ __launch_bounds__(kPT) void plane_fwd_kernel(const PlaneFwdArgs a) {
   auto route = [&](auto kc) {
     constexpr int k = decltype(kc)::value;
     constexpr bool kCol = (k & 1) != 0, kRev = k >= 2;
-    const float* su = kCol ? sxT : sxR;
+    const XE* su = kCol ? sxT : sxR;
     const T* dr = static_cast<const T*>(a.delta) + ((b * 4 + k) * a.dim + d) * L;
     const T* Br = static_cast<const T*>(a.Bm) + (b * 4 + k) * NS * int64_t(L);
     const T* Cr = static_cast<const T*>(a.Cm) + (b * 4 + k) * NS * int64_t(L);
@@ -185,7 +221,7 @@ __global__ __launch_bounds__(kPT) void plane_fwd_kernel(const PlaneFwdArgs a) {
         for (int q = 0; q < kT / 4; ++q) {  // u: x at the pixels of steps t .. t+3
           const int t = t0 + 4 * q;
           const int ti = t < L ? (kRev ? L - 4 - t : t) : 0;
-          const float4 f = *reinterpret_cast<const float4*>(su + swz(ti));
+          const float4 f = XQ<T>::get(su + swz(ti));
           if (kRev) {
             uv[4 * q] = f.w; uv[4 * q + 1] = f.z; uv[4 * q + 2] = f.y; uv[4 * q + 3] = f.x;
           } else {
@@ -337,7 +373,7 @@ __global__ __launch_bounds__(kPT) void plane_fwd_kernel(const PlaneFwdArgs a) {
   for (int p = 4 * tid; p < L; p += 4 * kPT) {
     float zv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (zg) Ld<T>::template get<4>(zg, p, zv);
-    const float4 xq = *reinterpret_cast<const float4*>(sxR + swz(p));
+    const float4 xq = XQ<T>::get(sxR + swz(p));
     const float4 sq = *reinterpret_cast<const float4*>(sacc + swz(p));
     const float xv[4] = {xq.x, xq.y, xq.z, xq.w};
     float v[4] = {sq.x * kLn2, sq.y * kLn2, sq.z * kLn2, sq.w * kLn2};
@@ -350,9 +386,16 @@ __global__ __launch_bounds__(kPT) void plane_fwd_kernel(const PlaneFwdArgs a) {
   }
 }
 
+// LDS a plane may take: the rule that admits a plane to the single kernel (16 bytes per pixel)
 size_t plane_lds_bytes(int64_t H, int64_t W) {
   const int64_t Ls = (H * W + 15) / 16 * 16;
   return size_t(4 * Ls) * sizeof(float);
+}
+// what a launch allocates: two fp32 arrays, and the two copies of x in the I/O type
+template <typename T>
+size_t plane_lds_alloc(int64_t H, int64_t W) {
+  const int64_t Ls = (H * W + 15) / 16 * 16;
+  return size_t(2 * Ls) * (sizeof(float) + sizeof(typename XQ<T>::E));
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -360,7 +403,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 template <typename T, int NS>
 void launch_t(const PlaneFwdArgs& a, hipStream_t s) {
   const dim3 grid{uint32_t(a.batch * a.dim)}, block{kPT};
-  const size_t lds = plane_lds_bytes(a.H, a.W);
+  const size_t lds = plane_lds_alloc<T>(a.H, a.W);
   if (a.softplus)
     plane_fwd_kernel<T, NS, true><<<grid, block, lds, s>>>(a);
   else
