@@ -38,9 +38,19 @@ hipError_t launch_transpose(const void* x, void* xT, int64_t batch, int64_t C, i
 // y[b, c, p] = (((r0 + r1) + r2) + r3)[p] (+ Dsum[c] * x[b, c, p]) (* silu(z[b, c, p])) with route
 // inputs in route order (fp32 when routes_f32, else dtype), grid outputs in dtype.
 // Optionally also writes the fp32 pre-gate sum to merged_f32.
+// Route outputs of the SS2D scans in 4-step blocks ("blocked"): route k's output at step s of
+// channel c of image b is at ((b * 4 + k) * (L / 4) + s / 4) * C * 4 + c * 4 + s % 4 (fp32).  A
+// scan wavefront's store of one 4-step group then covers whole 128-byte lines (its channels are
+// consecutive) instead of a 16-byte piece of each channel's row.  Used when H and W are
+// multiples of 4 (ss2d_routes_blocked), so that the merge can read whole 4 x 4 pixel blocks.
+inline bool ss2d_routes_blocked(int64_t H, int64_t W) {
+  return H > 0 && W > 0 && H % 4 == 0 && W % 4 == 0 && H * W < (int64_t(1) << 31);
+}
+
 struct MergeArgs {
-  const void* routes;      // (batch, 4, C, L) fp32 or dtype
+  const void* routes;      // (batch, 4, C, L) fp32 or dtype; fp32 in 4-step blocks if routes_blocked
   int routes_f32;
+  int routes_blocked;      // fp32 routes in the blocked layout above (H, W multiples of 4)
   const void* x;           // grid (batch, C, H, W) dtype (fp32 if x_f32), optional skip input
   int x_f32;
   const float* Dskip;      // (4, C) fp32, summed over routes (used with x)
@@ -92,7 +102,8 @@ hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t s);
 // One workgroup per plane when the plane's two column-major routes and dM fit in LDS; else the
 // merge writes M to `merged` (fp32 scratch) and the gate kernel reads it.
 struct MergeGateArgs {
-  const float* routes;  // (batch, 4, C, L) fp32, route order
+  const float* routes;  // (batch, 4, C, L) fp32, route order (blocked if routes_blocked)
+  int routes_blocked;   // the routes are in the blocked layout of MergeArgs
   const void* x;        // grid dtype (fp32 if x_f32) (skip input, with Dskip)
   int x_f32;
   const float* Dskip;   // (4, C) or null
@@ -273,6 +284,7 @@ struct ScanFwdParams {
   int store_states;    // pass 0 also keeps the state before every ckpt_every-th step in ckpt
   int out_f32;         // generic rows: out is fp32 instead of the I/O type
   int u_f32;           // ss2d rows, bf16 I/O: u and uT are fp32 (the input front's output)
+  int out_blocked;     // ss2d rows: out in the blocked route layout of MergeArgs (L % 4 == 0)
   int64_t bc_stride;   // elements between the (b, g) blocks of B and C (0: N * L, dense)
   // ss2d rows, fp32 I/O: raw delta formed in the kernel as dt_w[g, d, :] . dt[b, g, :, t] instead
   // of being read (dt: (b, g) blocks bc_stride apart, rows L apart; dt_w: (G, per_group, dt_rank);

@@ -339,6 +339,105 @@ __global__ __launch_bounds__(kThreads) void merge_plane_kernel(MergeArgs a) {
   }
 }
 
+// The SS2D merge from route outputs in 4-step blocks (MergeArgs: fp32, route k's step s of
+// channel c at ((b 4 + k) (L/4) + s/4) C 4 + c 4 + s % 4; H and W multiples of 4).  One thread =
+// one channel x one 4 x 4 pixel block: with W % 4 == 0 a block row is one 4-step group of the
+// row-major routes, and with H % 4 == 0 a block column is one group of the column-major ones, so
+// each route is read as four 16-byte groups and transposed in registers (no LDS).  A wavefront =
+// 8 consecutive channels (lane % 8: one 128-byte line per group and route) x 8 consecutive blocks
+// of the plane (row-major block order).  Same sum, in the same order, as merge_plane_kernel.
+// kVecIO: x, z, y and merged are aligned for 4-element accesses (else element by element).
+template <typename T, bool kSkip, bool kZ, bool kXF32, bool kVecIO>
+__global__ __launch_bounds__(64) void merge_blocked_kernel(MergeArgs a, int cblocks, int jchunks) {
+  const int lane = int(threadIdx.x);
+  int64_t bid = blockIdx.x;
+  const int jc = int(bid % jchunks);
+  bid /= jchunks;
+  const int cb = int(bid % cblocks);
+  const int64_t b = bid / cblocks;
+  const int64_t C = a.C;
+  const int64_t c = int64_t(cb) * 8 + (lane & 7);
+  const int H = int(a.H), Wd = int(a.W);
+  const int H4 = H / 4, W4 = Wd / 4;
+  const int j = jc * 8 + (lane >> 3);
+  // no LDS and no barrier in this kernel: threads past the channels or blocks leave at once
+  if (c >= C || j >= H4 * W4) return;
+  const int bh = j / W4, bw = j - bh * W4;
+  const int h0 = 4 * bh, w0 = 4 * bw;
+  const int64_t L = int64_t(H) * Wd, L4 = L / 4;
+  const float* rt = static_cast<const float*>(a.routes) + (b * 4 * L4 * C + c) * 4;
+  const int64_t kst = L4 * C * 4;  // between routes
+  float4 r0[4], r1[4], r2[4], r3[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t g0 = int64_t(h0 + i) * W4 + bw;   // row h0 + i of the block, row-major order
+    const int64_t g1 = int64_t(w0 + i) * H4 + bh;   // column w0 + i, column-major order
+    r0[i] = *reinterpret_cast<const float4*>(rt + g0 * C * 4);
+    r1[i] = *reinterpret_cast<const float4*>(rt + kst + g1 * C * 4);
+    r2[i] = *reinterpret_cast<const float4*>(rt + 2 * kst + (L4 - 1 - g0) * C * 4);
+    r3[i] = *reinterpret_cast<const float4*>(rt + 3 * kst + (L4 - 1 - g1) * C * 4);
+  }
+  const int64_t plane = (b * C + c) * L;
+  float4 xv[4], zv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t o = plane + int64_t(h0 + i) * Wd + w0;
+    if constexpr (kSkip) {
+      if constexpr (kXF32) {
+        const float* xf = static_cast<const float*>(a.x);
+        xv[i] = kVecIO ? Elem<float>::load4(xf, o) : make_float4(xf[o], xf[o + 1], xf[o + 2], xf[o + 3]);
+      } else {
+        const T* xg = static_cast<const T*>(a.x);
+        xv[i] = kVecIO ? Elem<T>::load4(xg, o)
+                       : make_float4(Elem<T>::load(xg, o), Elem<T>::load(xg, o + 1), Elem<T>::load(xg, o + 2),
+                                     Elem<T>::load(xg, o + 3));
+      }
+    }
+    if constexpr (kZ) {
+      const T* zg = static_cast<const T*>(a.z);
+      zv[i] = kVecIO ? Elem<T>::load4(zg, o)
+                     : make_float4(Elem<T>::load(zg, o), Elem<T>::load(zg, o + 1), Elem<T>::load(zg, o + 2),
+                                   Elem<T>::load(zg, o + 3));
+    }
+  }
+  float dsum = 0.0f;
+  if (kSkip) dsum = ((a.Dskip[c] + a.Dskip[C + c]) + a.Dskip[2 * C + c]) + a.Dskip[3 * C + c];
+  auto el = [](const float4& v, int e) { return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w)); };
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // block row i: pixels (h0 + i, w0 + q)
+    float v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // route 0: group row i, element q; route 1: column q, element i; route 2 runs backwards
+      // through the row (element 3 - q), route 3 backwards down the column (element 3 - i)
+      float sum = el(r0[i], q) + el(r1[q], i);
+      sum = sum + el(r2[i], 3 - q);
+      v[q] = sum + el(r3[q], 3 - i);
+    }
+    if constexpr (kSkip) {
+      v[0] = fmaf(dsum, xv[i].x, v[0]); v[1] = fmaf(dsum, xv[i].y, v[1]);
+      v[2] = fmaf(dsum, xv[i].z, v[2]); v[3] = fmaf(dsum, xv[i].w, v[3]);
+    }
+    const int64_t o = plane + int64_t(h0 + i) * Wd + w0;
+    if (a.merged_f32) {
+      if (kVecIO)
+        *reinterpret_cast<float4*>(a.merged_f32 + o) = make_float4(v[0], v[1], v[2], v[3]);
+      else
+        for (int q = 0; q < 4; ++q) a.merged_f32[o + q] = v[q];
+    }
+    if constexpr (kZ) {
+      v[0] *= silu(zv[i].x); v[1] *= silu(zv[i].y); v[2] *= silu(zv[i].z); v[3] *= silu(zv[i].w);
+    }
+    if (a.y) {
+      T* yg = static_cast<T*>(a.y);
+      if (kVecIO)
+        Elem<T>::store4(yg, o, make_float4(v[0], v[1], v[2], v[3]));
+      else
+        for (int q = 0; q < 4; ++q) Elem<T>::store(yg, o + q, v[q]);
+    }
+  }
+}
+
 // The gate backward fused with its merge (see MergeGateArgs), one plane per workgroup.  LDS:
 // routes 1 and 3 transposed to [w][h] (as in the merge), and dM as [h][w] for the dMT write.  As
 // in the merge, the skip term and an fp32 x are template parameters and the loads of up to
@@ -562,8 +661,49 @@ void launch_merge_plane(const MergeArgs& a, dim3 g, dim3 b, size_t lds, hipStrea
 }
 }  // namespace
 
+namespace {
+template <typename T, bool kSkip, bool kZ, bool kXF32>
+void launch_merge_blocked_v(const MergeArgs& a, dim3 g, int cblocks, int jchunks, bool vec_io, hipStream_t s) {
+  if (vec_io)
+    merge_blocked_kernel<T, kSkip, kZ, kXF32, true><<<g, dim3(64), 0, s>>>(a, cblocks, jchunks);
+  else
+    merge_blocked_kernel<T, kSkip, kZ, kXF32, false><<<g, dim3(64), 0, s>>>(a, cblocks, jchunks);
+}
+template <typename T>
+void launch_merge_blocked_t(const MergeArgs& a, dim3 g, int cblocks, int jchunks, bool vec_io, hipStream_t s) {
+  const bool skip = a.Dskip != nullptr && a.x != nullptr, z = a.z != nullptr;
+  if (skip && a.x_f32)
+    z ? launch_merge_blocked_v<T, true, true, true>(a, g, cblocks, jchunks, vec_io, s)
+      : launch_merge_blocked_v<T, true, false, true>(a, g, cblocks, jchunks, vec_io, s);
+  else if (skip)
+    z ? launch_merge_blocked_v<T, true, true, false>(a, g, cblocks, jchunks, vec_io, s)
+      : launch_merge_blocked_v<T, true, false, false>(a, g, cblocks, jchunks, vec_io, s);
+  else
+    z ? launch_merge_blocked_v<T, false, true, false>(a, g, cblocks, jchunks, vec_io, s)
+      : launch_merge_blocked_v<T, false, false, false>(a, g, cblocks, jchunks, vec_io, s);
+}
+}  // namespace
+
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   const int64_t L = a.H * a.W;
+  if (a.routes_blocked) {
+    // fp32 routes in 4-step blocks (written by the route scans when H and W are multiples of 4)
+    if (!a.routes_f32 || !ss2d_routes_blocked(a.H, a.W) || !aligned16(a.routes)) return hipErrorInvalidValue;
+    const int64_t cblocks = cdiv(a.C, 8), jchunks = cdiv((a.H / 4) * (a.W / 4), 8);
+    const int64_t blocks = a.batch * cblocks * jchunks;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    const uintptr_t tio = reinterpret_cast<uintptr_t>(a.y) | reinterpret_cast<uintptr_t>(a.z) |
+                          (a.x_f32 ? 0 : reinterpret_cast<uintptr_t>(a.x));
+    const bool vec_io = (tio & (a.dtype == 0 ? 15 : 7)) == 0 && (!a.x_f32 || aligned16(a.x)) &&
+                        (!a.merged_f32 || aligned16(a.merged_f32));
+    const dim3 g{uint32_t(blocks)};
+    if (a.dtype == 0)
+      launch_merge_blocked_t<float>(a, g, int(cblocks), int(jchunks), vec_io, s);
+    else
+      launch_merge_blocked_t<bf16>(a, g, int(cblocks), int(jchunks), vec_io, s);
+    return hipGetLastError();
+  }
   const size_t plane_lds = size_t(2) * size_t(a.W) * size_t(a.H + 1) * 4;
   const uintptr_t route_align = a.routes_f32 ? 15 : (a.dtype == 0 ? 15 : 7);
   if (plane_lds <= 64 * 1024 && a.batch * a.C > 0 &&
@@ -679,6 +819,29 @@ static void launch_merge_gate_bwd_t(const MergeGateArgs& a, dim3 g, size_t lds, 
 }
 
 hipError_t launch_merge_gate_bwd(const MergeGateArgs& a, hipStream_t s) {
+  if (a.routes_blocked && !a.merged_in) {
+    // the plane kernels read routes in the row layout: form the pre-gate map from the blocked
+    // routes first (the same sum in the same order), then take the path that reads it
+    MergeArgs m{};
+    m.routes = a.routes;
+    m.routes_f32 = 1;
+    m.routes_blocked = 1;
+    m.x = a.x;
+    m.x_f32 = a.x_f32;
+    m.Dskip = a.Dskip;
+    m.merged_f32 = a.merged;
+    m.batch = a.batch;
+    m.C = a.C;
+    m.H = a.H;
+    m.W = a.W;
+    m.dtype = a.dtype;
+    const hipError_t e = a.z ? launch_merge(m, s) : hipSuccess;
+    if (e != hipSuccess) return e;
+    MergeGateArgs k = a;
+    k.routes_blocked = 0;
+    k.merged_in = 1;
+    return launch_merge_gate_bwd(k, s);
+  }
   const int64_t L = a.H * a.W;
   const size_t lds = ((a.merged_in ? 0 : size_t(2) * size_t(a.W) * size_t(a.H + 1)) + size_t(a.H) * size_t(a.W + 1)) * 4;
   const uintptr_t io = reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.z) |

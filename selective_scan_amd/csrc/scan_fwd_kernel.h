@@ -98,6 +98,13 @@ void scan_fwd_kernel(const ScanFwdParams p) {
 
   const int64_t t_begin = int64_t(c) * p.chunk_len;
   const int64_t t_end = (t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L;
+  // SS2D route outputs: the 4-step group starting at step tg (tg % 4 == 0) goes to
+  // out + o_base + tg * o_step, in the row layout (row * L + tg) or in 4-step blocks
+  // (((b G + g) (L / 4) + tg / 4) per_group + dl) * 4, where the wavefront's 32 or 64 consecutive
+  // channels store one contiguous piece of whole lines per group
+  const bool blocked = kSS2D && p.out_blocked;
+  const int64_t o_base = blocked ? ((b * p.G + g) * (L / 4) * p.per_group + dl) * 4 : row * L;
+  const int64_t o_step = blocked ? p.per_group : 1;
 
   float h[NSL];
 #pragma unroll
@@ -263,9 +270,10 @@ void scan_fwd_kernel(const ScanFwdParams p) {
           // route outputs stay fp32 until the merge has added them: the result is rounded once.
           // The group is in range (groups at or past the end of the range exit the tile loop
           // above, and vector rows have L and the chunk ends a multiple of 4), so no bounds test.
-          Elem<float>::store4(static_cast<float*>(p.out) + row * L, tg, make_float4(y[0], y[1], y[2], y[3]));
+          Elem<float>::store4(static_cast<float*>(p.out) + o_base, tg * o_step, make_float4(y[0], y[1], y[2], y[3]));
         } else {
-          store_seg<float, kVec, 4>(static_cast<float*>(p.out) + row * L, y, tg, t_end);
+          // element tg + k of the group at o_base + tg * o_step + k
+          store_seg<float, kVec, 4>(static_cast<float*>(p.out) + o_base + tg * (o_step - 1), y, tg, t_end);
         }
       }
     }

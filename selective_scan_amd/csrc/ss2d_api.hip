@@ -469,6 +469,7 @@ static int ss2d_scan_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, bool k
   p.N = int(a->dstate);
   p.softplus = a->delta_softplus ? 1 : 0;
   p.ss2d = 1;
+  p.out_blocked = ss2d_routes_blocked(a->height, a->width) ? 1 : 0;
   p.dtype = proj ? SS2D_DTYPE_F32 : a->dtype;
   p.vec = (L % 4 == 0) && vec_aligned(p.dtype, {p.u, p.delta, p.Bm, p.Cm});
   p.chunk_len = sl.chunk_len;
@@ -492,6 +493,7 @@ static int ss2d_merge_stage(const ss2d_fwd_args* a, const SS2DLayout& lay, hipSt
   MergeArgs m{};
   m.routes = at(a->workspace, lay.off_ys);
   m.routes_f32 = 1;  // the scan stage writes fp32 route outputs
+  m.routes_blocked = ss2d_routes_blocked(a->height, a->width) ? 1 : 0;  // in its layout
   m.x = scan_input(a->x, (a->conv_w != nullptr || a->x_proj_w != nullptr), a->workspace, lay);
   m.x_f32 = (a->conv_w != nullptr || a->x_proj_w != nullptr);
   m.Dskip = a->Dskip;
@@ -1037,6 +1039,7 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
       MergeArgs m{};
       m.routes = at(a->workspace, lay.off_ys);
       m.routes_f32 = 1;
+      m.routes_blocked = ss2d_routes_blocked(a->height, a->width) ? 1 : 0;  // as the scan stage wrote them
       m.x = u;
       m.x_f32 = (a->conv_w != nullptr || a->x_proj_w != nullptr);
       m.Dskip = a->Dskip;
@@ -1073,6 +1076,7 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
     // transposed order
     MergeGateArgs gb{};
     gb.routes = reinterpret_cast<const float*>(at(a->workspace, lay.off_ys));
+    gb.routes_blocked = ss2d_routes_blocked(a->height, a->width) ? 1 : 0;
     gb.x = u;
     gb.x_f32 = (a->conv_w != nullptr || a->x_proj_w != nullptr);
     gb.Dskip = a->Dskip;

@@ -93,6 +93,8 @@ SS2D_BWD_CASES = [
     (1, 3, 40, 64, 8, "bf16", True),
     (1, 64, 64, 64, 16, "f32", True),   # few rows: chunked
     (1, 1, 1, 8, 4, "f32", True),
+    (2, 12, 8, 13, 16, "bf16", True),   # route outputs in 4-step blocks (H, W multiples of 4)
+    (1, 8, 12, 9, 16, "f32", False),    # the same without the gate
 ]
 
 
@@ -112,7 +114,8 @@ def test_ss2d_bwd(case):
 
 @pytest.mark.parametrize("case", [(1, 8, 8, 16, 4, "f32", True), (2, 7, 9, 20, 16, "f32", True),
                                   (1, 3, 40, 64, 8, "bf16", True), (1, 64, 64, 64, 16, "f32", True),
-                                  (2, 14, 14, 70, 16, "f32", False)], ids=str)
+                                  (2, 14, 14, 70, 16, "f32", False), (2, 12, 8, 13, 16, "bf16", True),
+                                  (1, 8, 12, 9, 16, "f32", False)], ids=str)
 def test_ss2d_bwd_reuses_forward_states(case):
     """A training forward (keep_states) then the backward on its workspace: the oracle's gradients,
     and bit for bit what the backward that recomputes the forward gives."""

@@ -134,6 +134,9 @@ SS2D_CASES = [
     (1, 64, 64, 64, 16, "f32", True),   # few rows: chunked
     (1, 12, 12, 13, 16, "bf16", True),  # small planes, several per transpose workgroup (a partial one)
     (2, 6, 10, 9, 16, "f32", True),     # the same in fp32: 16 planes per workgroup, then 2
+    (2, 12, 8, 13, 16, "bf16", True),   # H, W multiples of 4: route outputs in 4-step blocks, merged
+                                        # by 4 x 4 pixel blocks; 13 channels = a partial block of 8
+    (1, 16, 4, 9, 8, "f32", False),     # the same without the gate, one lane per channel
 ]
 
 

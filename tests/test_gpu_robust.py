@@ -144,6 +144,8 @@ SS2D_GUARD_CASES = [
     (1, 9, 11, 24, 16, "bf16", 3, True, 0),   # front and LayerNorm
     (2, 7, 8, 16, 4, "f32", 3, True, 3),      # the producer with front and LayerNorm
     (1, 13, 15, 12, 8, "bf16", 0, False, 2),  # the producer alone, bf16
+    (2, 12, 8, 13, 16, "bf16", 0, False, 0),  # route outputs in 4-step blocks, a partial channel block
+    (1, 8, 12, 9, 16, "f32", 3, True, 0),     # the same layout with front and LayerNorm
 ]
 
 
@@ -207,6 +209,42 @@ def test_guard_ss2d(case):
                         ddt_proj_w=gp("ddt_proj_w"))
     assert bnd.lib().ss2d_bwd(ctypes.byref(b), _stream()) == 0
     _check_all(g, ref_g)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ss2d_misaligned_io(dtype):
+    """x, z and out one element past an aligned address (H, W multiples of 4, N = 16): the route
+    scans then load and store element by element, still in the 4-step route blocks, and the merge
+    reads and writes the map element by element; the result equals, bit for bit, that of the same
+    call on aligned buffers, and nothing around the shifted output is written."""
+    batch, H, W, dim, N = 2, 8, 12, 9, 16
+    inp = synth.make_ss2d_inputs(batch, H, W, dim, N, dtype, has_z=True, seed_base=2400)
+    t = dict(x=to_dev(inp["x"], dtype), delta=to_dev(inp["delta"], dtype), A=to_dev(inp["A"], "f32"),
+             B=to_dev(inp["B"], dtype), C=to_dev(inp["C"], dtype), D=to_dev(inp["D"], "f32"),
+             delta_bias=to_dev(inp["delta_bias"], "f32"), z=to_dev(inp["z"], dtype))
+    ref = ss.ss2d_fwd(**t)
+
+    def shifted(a):  # a copy of a that starts one element past an aligned address
+        buf = torch.empty(a.numel() + 1, dtype=a.dtype, device="cuda")
+        v = buf[1:].view(a.shape)
+        v.copy_(a)
+        return v
+
+    x1, z1 = shifted(t["x"]), shifted(t["z"])
+    out = Guarded((t["x"].numel() + 1,), t["x"].dtype, init=torch.zeros(t["x"].numel() + 1, dtype=t["x"].dtype))
+    out1 = out.t[1:].view(t["x"].shape)
+    nbytes = ss.ss2d_workspace_bytes(batch, dim, H, W, N, t["x"].dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a = bnd.SS2DFwdArgs(x=_p(x1), delta=_p(t["delta"]), A=_p(t["A"]), Bm=_p(t["B"]), Cm=_p(t["C"]),
+                        Dskip=_p(t["D"]), delta_bias=_p(t["delta_bias"]), z=_p(z1), out=_p(out1), workspace=_p(ws),
+                        workspace_bytes=nbytes, batch=batch, dim=dim, height=H, width=W, dstate=N,
+                        dtype=_dt(t["x"]), delta_softplus=1, keep_states=0, conv_k=0, layer_norm=0, ln_eps=1e-5,
+                        dt_rank=0)
+    assert bnd.lib().ss2d_fwd(ctypes.byref(a), _stream()) == 0
+    torch.cuda.synchronize()
+    assert out.intact()
+    assert float(out.t[0]) == 0.0
+    assert torch.equal(out1, ref)
 
 
 @pytest.mark.parametrize("case", [(2, 197, 40, 16, "bf16"), (1, 1024, 16, 16, "f32"), (3, 31, 9, 4, "bf16")], ids=str)
