@@ -573,6 +573,13 @@ void scan_bwd_kernel(const ScanBwdParams p) {
     // budget allows it there) load the B/C words of the next tile (backwards) while this one
     // computes.
     constexpr bool kBCAhead = kSS2D && kVec && kDtR == 0 && kStage;
+    // this lane's start states at checkpoint index s: ck_base + s * ck_step, 16-byte pieces
+    // ck_stride apart (lane-major blocks when the forward stored them so: whole wavefronts of
+    // rows, every state real; else row-major)
+    const bool ck_lanes = ckpt_lane_major<NSL, kSplit>(N, p.per_group);
+    const float* const ck_base = p.ckpt + ckpt_slot<NSL, kSplit>(ck_lanes, 0, 0, row, N, lane);
+    const int64_t ck_step = p.batch * p.dim * N;
+    const int ck_stride = ckpt_piece_stride(ck_lanes);
     const int64_t n_tiles = (t_end - t_begin + kTile - 1) / kTile;
     BCStage<T, NS, kVec> nbc;
     if (kBCAhead && n_tiles > 0) nbc.load(Bg, Cg, N, L, t_begin + (n_tiles - 1) * kTile, t_end, lane);
@@ -598,7 +605,7 @@ void scan_bwd_kernel(const ScanBwdParams p) {
         load_seg<TU, kVec, kSub>(uv, u_row, s0, t_end, L, rev);
         load_seg<DT, kVec, kSub>(gv, dout_row, s0, t_end, L, rev);
         if (has_z) load_seg<T, kVec, kSub>(zv, z_row, s0, t_end, L, false);
-        const float* ck = p.ckpt + ((s0 / kSub) * p.batch * p.dim + row) * N + n0;
+        const float* ck = ck_base + (s0 / kSub) * ck_step;
         // issued with the row loads so that one wait covers both: 16-byte loads when every state
         // is real (N == NS, the state rows are then 16-byte aligned pieces), else one load per
         // state (a state past N re-reads state n0, zeroed by a select)
@@ -606,7 +613,7 @@ void scan_bwd_kernel(const ScanBwdParams p) {
         if (NSL % 4 == 0 && N == NS) {
 #pragma unroll
           for (int j = 0; j < NSL / 4; ++j) {
-            const float4 c4 = *reinterpret_cast<const float4*>(ck + 4 * j);
+            const float4 c4 = *reinterpret_cast<const float4*>(ck + j * ck_stride);
             ckv[4 * j] = c4.x; ckv[4 * j + 1] = c4.y; ckv[4 * j + 2] = c4.z; ckv[4 * j + 3] = c4.w;
           }
         } else {

@@ -358,6 +358,35 @@ __device__ __forceinline__ void store_out(O* row, const float* y, int64_t t0, in
   }
 }
 
+// Checkpoint slots in lane-major blocks.  When every state is real (N == NS), the per-lane state
+// count is a multiple of 4 and a wavefront's rows are whole (per_group a multiple of the rows per
+// wavefront), the wavefront's slot at one checkpoint is a contiguous block of kWave x NSL floats
+// (its rows, N states each).  Row-major, lane l's states fill bytes [16 NSL l, 16 NSL (l + 1))
+// of it, so each 16-byte store instruction writes every other piece of a line.  Lane-major, the
+// 16-byte piece j of lane l sits at floats (j kWave + l) 4 of the block: one store instruction
+// writes 1 KB of whole lines.  Only the states' order inside the wavefront's own block differs.
+template <int NSL, int kSplit>
+__device__ __forceinline__ bool ckpt_lane_major(int N, int64_t per_group) {
+  return kSplit == 2 && NSL % 4 == 0 && N == NSL * kSplit && per_group % (kWave / kSplit) == 0;
+}
+// First float of this lane's slot at checkpoint index s for row `row` (lane-major or row-major);
+// its 16-byte piece j follows at + j * ckpt_piece_stride.
+template <int NSL, int kSplit>
+__device__ __forceinline__ int64_t ckpt_slot(bool lane_major, int64_t s, int64_t rows, int64_t row, int N, int lane) {
+  const int n0 = (lane % kSplit) * NSL;
+  if (lane_major) return (s * rows + row - lane / kSplit) * N + 4 * lane;
+  return (s * rows + row) * N + n0;
+}
+__device__ __forceinline__ int ckpt_piece_stride(bool lane_major) { return lane_major ? 4 * kWave : 4; }
+
+// Store NS state values (all real, NS % 4 == 0) as 16-byte pieces `stride` floats apart.
+template <int NS>
+__device__ __forceinline__ void store_state_pieces(float* dst, const float* h, int stride) {
+#pragma unroll
+  for (int j = 0; j < NS / 4; ++j)
+    *reinterpret_cast<float4*>(dst + j * stride) = make_float4(h[4 * j], h[4 * j + 1], h[4 * j + 2], h[4 * j + 3]);
+}
+
 // Store the first `count` (<= NS) of NS state values; 16-byte stores when NS and count allow.
 template <int NS>
 __device__ __forceinline__ void store_state(float* dst, const float* h, int count) {

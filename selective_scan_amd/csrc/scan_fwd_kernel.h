@@ -103,6 +103,13 @@ void scan_fwd_kernel(const ScanFwdParams p) {
   // (((b G + g) (L / 4) + tg / 4) per_group + dl) * 4, where the wavefront's 32 or 64 consecutive
   // channels store one contiguous piece of whole lines per group
   const bool blocked = kSS2D && p.out_blocked;
+  // checkpoint slots of the states kept for the backward: lane-major blocks when the wavefront's
+  // rows are whole and every state is real (whole-line stores), else row-major
+  // (this lane's slot at checkpoint index s: ck_base + s * ck_step, 16-byte pieces ck_stride apart)
+  const bool ck_lanes = kStore && ckpt_lane_major<NSL, kSplit>(N, p.per_group);
+  float* const ck_base = kStore ? p.ckpt + ckpt_slot<NSL, kSplit>(ck_lanes, 0, 0, row, N, lane) : nullptr;
+  const int64_t ck_step = p.batch * p.dim * N;
+  const int ck_stride = ckpt_piece_stride(ck_lanes);
   const int64_t o_base = blocked ? ((b * p.G + g) * (L / 4) * p.per_group + dl) * 4 : row * L;
   const int64_t o_step = blocked ? p.per_group : 1;
 
@@ -228,7 +235,13 @@ void scan_fwd_kernel(const ScanFwdParams p) {
         // several steps' values live at once and exceed the register file)
         asm volatile("" ::: "memory");
         if (kStore && (i % kSub) == 0) {
-          if (i < nt && active) store_state<NSL>(p.ckpt + (((t0 + i) / kSub) * p.batch * p.dim + row) * N + n0, h, nvalid);
+          if (i < nt && active) {
+            float* dst = ck_base + ((t0 + i) / kSub) * ck_step;
+            if (NSL % 4 == 0 && nvalid == NSL)
+              store_state_pieces<NSL>(dst, h, ck_stride);
+            else
+              store_state<NSL>(dst, h, nvalid);
+          }
         }
         const float* cb = bufb[i & 1];
         const float* cc = bufc[i & 1];
