@@ -329,13 +329,13 @@ struct ScanBwdParams {
   const float* delta_bias;
   const void* dout;        // generic: dtype (or fp32 if dout_f32) (batch, dim, L); ss2d: dM (fp32 grid) and dMT
   const void* doutT;
-  void* du;                // generic: dtype; ss2d: fp32 route order (batch, 4D, L)
+  void* du;                // generic: dtype; ss2d: fp32 route order (batch, 4D, L), blocked if du_blocked
   void* ddelta;            // dtype (batch, dim, L)
   void* dz;                // generic only, dtype
   const float* ckpt;       // (n_ckpt, rows, N) states before every ckpt_steps-th step
   float* lam_carry;        // (rows, n_chunks, N): a_{t1} * lambda_{t1} flowing into each chunk
   float* chunk_sum;        // (rows, n_chunks)
-  float* dB_part;          // (dblocks, batch, G, N, L) fp32
+  float* dB_part;          // (dblocks, batch, G, N, L) fp32; (dblocks, batch, G, L/4, N, 4) if bc_blocked
   float* dC_part;
   float* dA_part;          // (n_chunks, rows, N)
   float* dD_part;          // (n_chunks, rows)
@@ -349,6 +349,11 @@ struct ScanBwdParams {
   int pass;                // 1: chunk-local lambda pass; 0: gradients
   int dout_f32;            // generic rows: dout is fp32 instead of the I/O type
   int u_f32;               // ss2d rows, bf16 I/O: u and uT are fp32 (the input front's output)
+  // ss2d rows with L % 4 == 0: du in the blocked route layout of MergeArgs (4-step blocks of
+  // consecutive channels), and the dB / dC partial sums in 4-step blocks of all states, so that a
+  // wavefront's 16-byte stores of one 4-step group cover whole lines
+  int du_blocked;
+  int bc_blocked;
   int64_t bc_stride;       // elements between the (b, g) blocks of B and C (0: N * L, dense)
   const float* dt;         // as in ScanFwdParams: raw delta from dt_w . dt (delta unused)
   const float* dt_w;
@@ -371,6 +376,7 @@ struct BwdReduceArgs {
   int64_t batch, dim, L, G, dblocks;
   int n_chunks, N, dtype;
   int64_t bc_out_stride;  // elements between the (b, g) blocks of dB / dC (0: N * L, dense)
+  int bc_blocked;         // dB_part / dC_part in the 4-step blocks of ScanBwdParams::bc_blocked
 };
 hipError_t launch_bwd_reduce(const BwdReduceArgs& a, hipStream_t s);
 

@@ -45,6 +45,29 @@ __global__ __launch_bounds__(256) void reduce_bc_kernel(const BwdReduceArgs a) {
   Elem<T>::store(static_cast<T*>(a.dC), o, sc);
 }
 
+// The same for partial sums in 4-step blocks of all states ((b, g) block, t / 4, n, t % 4): one
+// thread per (block, 4-step group, state) adds four steps at once, so a wavefront reads whole
+// lines of every partial-sum block.
+template <typename T>
+__global__ __launch_bounds__(256) void reduce_bc_blocked_kernel(const BwdReduceArgs a) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;  // (bg, t / 4, n)
+  const int64_t per_block = a.batch * a.G * a.N * a.L;
+  if (i * 4 >= per_block) return;
+  float4 sb = make_float4(0.0f, 0.0f, 0.0f, 0.0f), sc = sb;
+  for (int64_t k = 0; k < a.dblocks; ++k) {
+    const float4 vb = *reinterpret_cast<const float4*>(a.dB_part + k * per_block + 4 * i);
+    const float4 vc = *reinterpret_cast<const float4*>(a.dC_part + k * per_block + 4 * i);
+    sb.x += vb.x; sb.y += vb.y; sb.z += vb.z; sb.w += vb.w;
+    sc.x += vc.x; sc.y += vc.y; sc.z += vc.z; sc.w += vc.w;
+  }
+  const int64_t groups = a.L / 4;
+  const int64_t n = i % a.N, t = ((i / a.N) % groups) * 4, bg = i / (a.N * groups);
+  const int64_t o = bg * (a.bc_out_stride ? a.bc_out_stride : int64_t(a.N) * a.L) + n * a.L + t;
+  // dB terms were formed with delta / ln 2
+  Elem<T>::store4(static_cast<T*>(a.dB), o, make_float4(sb.x * kLn2, sb.y * kLn2, sb.z * kLn2, sb.w * kLn2));
+  Elem<T>::store4(static_cast<T*>(a.dC), o, sc);
+}
+
 // 64 outputs per workgroup (dA entries, then (dD, dbias) pairs); its four wavefronts take every
 // fourth image, and their sums are added in a fixed order, so the result is deterministic.
 __global__ __launch_bounds__(256) void reduce_params_kernel(const BwdReduceArgs a) {
@@ -110,7 +133,15 @@ hipError_t launch_lambda_combine(const ScanBwdParams& p, hipStream_t s) {
 
 hipError_t launch_bwd_reduce(const BwdReduceArgs& a, hipStream_t s) {
   const int64_t nbc = a.batch * a.G * a.N * a.L;
-  if (nbc > 0) {
+  if (nbc > 0 && a.bc_blocked) {
+    const int64_t threads = nbc / 4;
+    if (a.dtype == 0)
+      reduce_bc_blocked_kernel<float><<<dim3(uint32_t((threads + 255) / 256)), dim3(256), 0, s>>>(a);
+    else
+      reduce_bc_blocked_kernel<bf16><<<dim3(uint32_t((threads + 255) / 256)), dim3(256), 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (nbc > 0) {
     if (a.dtype == 0)
       reduce_bc_kernel<float><<<dim3(uint32_t((nbc + 255) / 256)), dim3(256), 0, s>>>(a);
     else

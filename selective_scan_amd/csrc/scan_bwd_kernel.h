@@ -260,6 +260,17 @@ void scan_bwd_kernel(const ScanBwdParams p) {
   const int64_t t_begin = int64_t(c) * p.chunk_len;
   const int64_t t_end = (t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L;
 
+  // Output offsets.  du of step t: du_base + (t - t % 4) * du_step + t % 4 (row layout: du_step 1;
+  // blocked route layout: the 4-step group of the wavefront's consecutive channels is contiguous).
+  // dB / dC partial sum of (state n, step t): bc_base + bc_off(n, t), rows of L steps or 4-step
+  // blocks of all N states.
+  const bool du_blk = kSS2D && p.du_blocked;
+  const int64_t du_base = du_blk ? ((b * p.G + g) * (L / 4) * p.per_group + dl) * 4 : row * L;
+  const int64_t du_step = du_blk ? p.per_group : 1;
+  const bool bc_blk = p.bc_blocked != 0;
+  const int64_t bc_base = ((dblk * p.batch + b) * p.G + g) * N * L;
+  auto bc_off = [&](int n, int64_t t) { return bc_blk ? (t - (t & 3)) * N + 4 * n + (t & 3) : n * L + t; };
+
   // mu = a_{t+1} lambda_{t+1}: the adjoint flowing into step t from later steps
   float mu[NSL];
 #pragma unroll
@@ -288,7 +299,7 @@ void scan_bwd_kernel(const ScanBwdParams p) {
         Elem<T>::store4(static_cast<T*>(p.ddelta), row * L + th, make_float4(pd_dd[0], pd_dd[1], pd_dd[2], pd_dd[3]));
         const float4 v = make_float4(pd_du[0], pd_du[1], pd_du[2], pd_du[3]);
         if (kSS2D)
-          Elem<float>::store4(static_cast<float*>(p.du), row * L + th, v);
+          Elem<float>::store4(static_cast<float*>(p.du) + du_base, th * du_step, v);
         else
           Elem<T>::store4(static_cast<T*>(p.du), row * L + th, v);
       }
@@ -303,7 +314,7 @@ void scan_bwd_kernel(const ScanBwdParams p) {
         v.z = sRed[(4 * h + 2) * kRedStride + r];
         v.w = sRed[(4 * h + 3) * kRedStride + r];
         float* dst = (r < NS) ? p.dB_part : p.dC_part;
-        *reinterpret_cast<float4*>(dst + (((dblk * p.batch + b) * p.G + g) * N + n) * L + t) = v;
+        *reinterpret_cast<float4*>(dst + bc_base + bc_off(n, t)) = v;
       }
       pd_s0 = -1;
     }
@@ -451,7 +462,7 @@ void scan_bwd_kernel(const ScanBwdParams p) {
                 const int n = e < NSL ? e : e - NSL;
                 if (n < nvalid) {
                   float* dst = (e < NSL) ? p.dB_part : p.dC_part;
-                  dst[(((dblk * p.batch + b) * p.G + g) * N + n0 + n) * L + t] = red[r];
+                  dst[bc_base + bc_off(n0 + n, t)] = red[r];
                 }
               }
             }
@@ -468,7 +479,13 @@ void scan_bwd_kernel(const ScanBwdParams p) {
           } else if (active && part == 0) {
             const int64_t sp = s0 + pc * kInner;
             store_seg<T, kVec, kInner>(static_cast<T*>(p.ddelta) + row * L, o_dd, sp, t_end);
-            if (kSS2D)
+            if (kSS2D && du_blk) {
+#pragma unroll
+              for (int k = 0; k < kInner; ++k) {
+                const int64_t t = sp + k;
+                if (t < t_end) static_cast<float*>(p.du)[du_base + (t - (t & 3)) * du_step + (t & 3)] = o_du[k];
+              }
+            } else if (kSS2D)
               store_seg<float, kVec, kInner>(static_cast<float*>(p.du) + row * L, o_du, sp, t_end);
             else
               store_seg<T, kVec, kInner>(static_cast<T*>(p.du) + row * L, o_du, sp, t_end);

@@ -761,6 +761,7 @@ static int run_scan_bwd(ScanBwdParams bp, const ScanLayout& lay, void* ws, void*
   r.N = bp.N;
   r.dtype = bp.dtype;
   r.bc_out_stride = bp.bc_stride;
+  r.bc_blocked = bp.bc_blocked;
   return status_from(launch_bwd_reduce(r, stream));
 }
 
@@ -1128,8 +1129,14 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
   bp.ss2d = 1;
   bp.dtype = proj ? SS2D_DTYPE_F32 : a->dtype;
   bp.vec = (L % 4 == 0) && vec_aligned(bp.dtype, {u, bp.delta, bp.Bm, bp.Cm, bp.ddelta});
-  st = run_scan_bwd(bp, lay.scan, at(ws, lay.off_scan), proj ? wsf(ws, lay.off_pdxdbl) + a->dt_rank * L : a->dBm,
-                    proj ? wsf(ws, lay.off_pdxdbl) + (a->dt_rank + a->dstate) * L : a->dCm, a->dA, a->Dskip ? a->dDskip : nullptr,
+  void* dB_out = proj ? static_cast<void*>(wsf(ws, lay.off_pdxdbl) + a->dt_rank * L) : a->dBm;
+  void* dC_out = proj ? static_cast<void*>(wsf(ws, lay.off_pdxdbl) + (a->dt_rank + a->dstate) * L) : a->dCm;
+  // whole-line stores of du (read back only by the dx merge below; the producer's backward reads
+  // it row by row) and of the dB / dC partial sums (whose reduction stores 4 steps at once)
+  const bool blocked = ss2d_routes_blocked(a->height, a->width);
+  bp.du_blocked = (blocked && !proj) ? 1 : 0;
+  bp.bc_blocked = (blocked && vec_aligned(bp.dtype, {dB_out, dC_out})) ? 1 : 0;
+  st = run_scan_bwd(bp, lay.scan, at(ws, lay.off_scan), dB_out, dC_out, a->dA, a->Dskip ? a->dDskip : nullptr,
                     a->delta_bias ? a->ddelta_bias : nullptr, stream);
   if (st != SS2D_OK) return st;
   if (proj) {
@@ -1142,6 +1149,7 @@ int ss2d_bwd(const ss2d_bwd_args* a, hipStream_t stream) {
   MergeArgs m{};
   m.routes = at(a->workspace, lay.off_ys);
   m.routes_f32 = 1;
+  m.routes_blocked = bp.du_blocked;  // as the adjoint scans wrote du
   m.batch = a->batch;
   m.C = a->dim;
   m.H = a->height;
