@@ -247,12 +247,23 @@ def test_ss2d_misaligned_io(dtype):
     assert torch.equal(out1, ref)
 
 
+def _shifted_copy(a):
+    """A copy of `a` that starts one element past an aligned address."""
+    buf = torch.empty(a.numel() + 1, dtype=a.dtype, device="cuda")
+    v = buf[1:].view(a.shape)
+    v.copy_(a)
+    return v
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_ss2d_bwd_misaligned_dbdc(dtype):
-    """dB and dC one element past an aligned address (H, W multiples of 4, N = 16): the adjoint scans
-    still write du in 4-step route blocks, while the dB / dC partial sums keep the row layout that
-    the element-by-element reduction reads; every gradient equals, bit for bit, that of the same
-    call on aligned buffers, and nothing around the shifted dB / dC is written."""
+@pytest.mark.parametrize("shift", ["dbdc", "gate"])
+def test_ss2d_bwd_misaligned(dtype, shift):
+    """H, W multiples of 4, N = 16, with some buffers one element past an aligned address:
+    "dbdc" shifts dB and dC (the adjoint scans still write du in 4-step route blocks, while the
+    dB / dC partial sums keep the row layout that the element-by-element reduction reads); "gate"
+    shifts dout, z and dz (the gate backward then leaves the one-workgroup-per-plane kernel for
+    the tiled one, element by element).  Every gradient equals, bit for bit, that of the same call
+    on aligned buffers, and nothing around the shifted outputs is written."""
     batch, H, W, dim, N = 2, 8, 12, 9, 16
     inp = synth.make_ss2d_inputs(batch, H, W, dim, N, dtype, has_z=True, seed_base=2500, with_dout=True)
     t = dict(x=to_dev(inp["x"], dtype), delta=to_dev(inp["delta"], dtype), A=to_dev(inp["A"], "f32"),
@@ -261,27 +272,41 @@ def test_ss2d_bwd_misaligned_dbdc(dtype):
     dout = to_dev(inp["dout"], dtype)
     ref = ss.ss2d_bwd(**t, dout=dout)
     tdt = t["x"].dtype
-    shape_bc = tuple(t["B"].shape)
-    nbc = t["B"].numel()
-    gB = Guarded((nbc + 1,), tdt, init=torch.zeros(nbc + 1, dtype=tdt))
-    gC = Guarded((nbc + 1,), tdt, init=torch.zeros(nbc + 1, dtype=tdt))
-    dB1, dC1 = gB.t[1:].view(shape_bc), gC.t[1:].view(shape_bc)
-    dx, dz = torch.empty_like(t["x"]), torch.empty_like(t["x"])
+
+    def shifted_out(like):  # an output one element past an aligned address, with guard bands
+        n = like.numel()
+        gd = Guarded((n + 1,), like.dtype, init=torch.zeros(n + 1, dtype=like.dtype))
+        return gd, gd.t[1:].view(like.shape)
+
+    guards = []
+    z_in, dout_in = t["z"], dout
+    if shift == "dbdc":
+        gB, dB = shifted_out(t["B"])
+        gC, dC = shifted_out(t["C"])
+        guards += [gB, gC]
+        dz = torch.empty_like(t["x"])
+    else:
+        dB, dC = torch.empty_like(t["B"]), torch.empty_like(t["C"])
+        gz, dz = shifted_out(t["x"])
+        guards.append(gz)
+        z_in, dout_in = _shifted_copy(t["z"]), _shifted_copy(dout)
+    dx = torch.empty_like(t["x"])
     ddelta = torch.empty_like(t["delta"])
     dA, dD, dbias = torch.empty_like(t["A"]), torch.empty_like(t["D"]), torch.empty_like(t["delta_bias"])
     nbytes = ss.ss2d_workspace_bytes(batch, dim, H, W, N, tdt)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     a = bnd.SS2DBwdArgs(x=_p(t["x"]), delta=_p(t["delta"]), A=_p(t["A"]), Bm=_p(t["B"]), Cm=_p(t["C"]),
-                        Dskip=_p(t["D"]), delta_bias=_p(t["delta_bias"]), z=_p(t["z"]), dout=_p(dout), dx=_p(dx),
-                        ddelta=_p(ddelta), dA=_p(dA), dBm=_p(dB1), dCm=_p(dC1), dDskip=_p(dD), ddelta_bias=_p(dbias),
+                        Dskip=_p(t["D"]), delta_bias=_p(t["delta_bias"]), z=_p(z_in), dout=_p(dout_in), dx=_p(dx),
+                        ddelta=_p(ddelta), dA=_p(dA), dBm=_p(dB), dCm=_p(dC), dDskip=_p(dD), ddelta_bias=_p(dbias),
                         dz=_p(dz), workspace=_p(ws), workspace_bytes=nbytes, batch=batch, dim=dim, height=H, width=W,
                         dstate=N, dtype=_dt(t["x"]), delta_softplus=1, workspace_has_states=0, conv_k=0,
                         layer_norm=0, ln_eps=1e-5, dt_rank=0)
     assert bnd.lib().ss2d_bwd(ctypes.byref(a), _stream()) == 0
     torch.cuda.synchronize()
-    assert gB.intact() and gC.intact()
-    assert float(gB.t[0]) == 0.0 and float(gC.t[0]) == 0.0
-    got = {"dx": dx, "ddelta": ddelta, "dA": dA, "dB": dB1, "dC": dC1, "dD": dD, "ddelta_bias": dbias, "dz": dz}
+    for gd in guards:
+        assert gd.intact()
+        assert float(gd.t[0]) == 0.0
+    got = {"dx": dx, "ddelta": ddelta, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "ddelta_bias": dbias, "dz": dz}
     for k, v in got.items():
         assert torch.equal(v, ref[k]), k
 
