@@ -350,7 +350,9 @@ __global__ __launch_bounds__(kThreads) void merge_plane_kernel(MergeArgs a) {
 template <typename T, bool kSkip, bool kZ, bool kXF32, bool kVecIO>
 __global__ __launch_bounds__(64) void merge_blocked_kernel(MergeArgs a, int cblocks, int jchunks) {
   const int lane = int(threadIdx.x);
-  int64_t bid = blockIdx.x;
+  // neighbouring chunks of a plane share the lines of its rows (a chunk's 8 blocks cover part of
+  // a line per row and channel): consecutive ids on one XCD merge those partial lines in one L2
+  int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
   const int jc = int(bid % jchunks);
   bid /= jchunks;
   const int cb = int(bid % cblocks);
