@@ -630,7 +630,7 @@ void scan_bwd_kernel(const ScanBwdParams p) {
         if (NSL % 4 == 0 && N == NS) {
 #pragma unroll
           for (int j = 0; j < NSL / 4; ++j) {
-            const float4 c4 = *reinterpret_cast<const float4*>(ck + j * ck_stride);
+            const F4 c4 = __builtin_nontemporal_load(reinterpret_cast<const F4*>(ck + j * ck_stride));
             ckv[4 * j] = c4.x; ckv[4 * j + 1] = c4.y; ckv[4 * j + 2] = c4.z; ckv[4 * j + 3] = c4.w;
           }
         } else {

@@ -379,12 +379,16 @@ __device__ __forceinline__ int64_t ckpt_slot(bool lane_major, int64_t s, int64_t
 }
 __device__ __forceinline__ int ckpt_piece_stride(bool lane_major) { return lane_major ? 4 * kWave : 4; }
 
+// four floats as a native vector (what the nontemporal builtins accept)
+typedef float F4 __attribute__((ext_vector_type(4)));
+
 // Store NS state values (all real, NS % 4 == 0) as 16-byte pieces `stride` floats apart.
 template <int NS>
 __device__ __forceinline__ void store_state_pieces(float* dst, const float* h, int stride) {
 #pragma unroll
   for (int j = 0; j < NS / 4; ++j)
-    *reinterpret_cast<float4*>(dst + j * stride) = make_float4(h[4 * j], h[4 * j + 1], h[4 * j + 2], h[4 * j + 3]);
+    __builtin_nontemporal_store(F4{h[4 * j], h[4 * j + 1], h[4 * j + 2], h[4 * j + 3]},
+                                reinterpret_cast<F4*>(dst + j * stride));
 }
 
 // Store the first `count` (<= NS) of NS state values; 16-byte stores when NS and count allow.
