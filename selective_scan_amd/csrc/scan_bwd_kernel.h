@@ -299,7 +299,10 @@ void scan_bwd_kernel(const ScanBwdParams p) {
         Elem<T>::store4(static_cast<T*>(p.ddelta), row * L + th, make_float4(pd_dd[0], pd_dd[1], pd_dd[2], pd_dd[3]));
         const float4 v = make_float4(pd_du[0], pd_du[1], pd_du[2], pd_du[3]);
         if (kSS2D)
-          Elem<float>::store4(static_cast<float*>(p.du) + du_base, th * du_step, v);
+          if (du_blk)  // whole lines per store instruction: written past the caches
+            store4_nt(static_cast<float*>(p.du) + du_base + th * du_step, v);
+          else
+            Elem<float>::store4(static_cast<float*>(p.du) + du_base, th * du_step, v);
         else
           Elem<T>::store4(static_cast<T*>(p.du), row * L + th, v);
       }
@@ -314,7 +317,10 @@ void scan_bwd_kernel(const ScanBwdParams p) {
         v.z = sRed[(4 * h + 2) * kRedStride + r];
         v.w = sRed[(4 * h + 3) * kRedStride + r];
         float* dst = (r < NS) ? p.dB_part : p.dC_part;
-        *reinterpret_cast<float4*>(dst + bc_base + bc_off(n, t)) = v;
+        if (bc_blk)
+          store4_nt(dst + bc_base + bc_off(n, t), v);
+        else
+          *reinterpret_cast<float4*>(dst + bc_base + bc_off(n, t)) = v;
       }
       pd_s0 = -1;
     }

@@ -382,6 +382,12 @@ __device__ __forceinline__ int ckpt_piece_stride(bool lane_major) { return lane_
 // four floats as a native vector (what the nontemporal builtins accept)
 typedef float F4 __attribute__((ext_vector_type(4)));
 
+// a 16-byte store that does not keep its line in the caches (for data written once and read
+// back by a later kernel, when the store instructions of a wavefront cover whole lines)
+__device__ __forceinline__ void store4_nt(float* p, float4 v) {
+  __builtin_nontemporal_store(F4{v.x, v.y, v.z, v.w}, reinterpret_cast<F4*>(p));
+}
+
 // Store NS state values (all real, NS % 4 == 0) as 16-byte pieces `stride` floats apart.
 template <int NS>
 __device__ __forceinline__ void store_state_pieces(float* dst, const float* h, int stride) {

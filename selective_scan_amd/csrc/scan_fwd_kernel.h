@@ -283,7 +283,11 @@ void scan_fwd_kernel(const ScanFwdParams p) {
           // route outputs stay fp32 until the merge has added them: the result is rounded once.
           // The group is in range (groups at or past the end of the range exit the tile loop
           // above, and vector rows have L and the chunk ends a multiple of 4), so no bounds test.
-          Elem<float>::store4(static_cast<float*>(p.out) + o_base, tg * o_step, make_float4(y[0], y[1], y[2], y[3]));
+          // (in 4-step blocks the wavefront's stores are whole lines: written past the caches)
+          if (blocked)
+            store4_nt(static_cast<float*>(p.out) + o_base + tg * o_step, make_float4(y[0], y[1], y[2], y[3]));
+          else
+            Elem<float>::store4(static_cast<float*>(p.out) + o_base, tg * o_step, make_float4(y[0], y[1], y[2], y[3]));
         } else {
           // element tg + k of the group at o_base + tg * o_step + k
           store_seg<float, kVec, 4>(static_cast<float*>(p.out) + o_base + tg * (o_step - 1), y, tg, t_end);
