@@ -347,6 +347,13 @@ __global__ __launch_bounds__(kThreads) void merge_plane_kernel(MergeArgs a) {
 // 8 consecutive channels (lane % 8: one 128-byte line per group and route) x 8 consecutive blocks
 // of the plane (row-major block order).  Same sum, in the same order, as merge_plane_kernel.
 // kVecIO: x, z, y and merged are aligned for 4-element accesses (else element by element).
+// 16 bytes read once (whole lines across the wavefront), not kept in the caches
+__device__ __forceinline__ float4 load4_nt(const float* p) {
+  typedef float F4 __attribute__((ext_vector_type(4)));
+  const F4 v = __builtin_nontemporal_load(reinterpret_cast<const F4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 template <typename T, bool kSkip, bool kZ, bool kXF32, bool kVecIO>
 __global__ __launch_bounds__(64) void merge_blocked_kernel(MergeArgs a, int cblocks, int jchunks) {
   const int lane = int(threadIdx.x);
@@ -374,10 +381,10 @@ __global__ __launch_bounds__(64) void merge_blocked_kernel(MergeArgs a, int cblo
   for (int i = 0; i < 4; ++i) {
     const int64_t g0 = int64_t(h0 + i) * W4 + bw;   // row h0 + i of the block, row-major order
     const int64_t g1 = int64_t(w0 + i) * H4 + bh;   // column w0 + i, column-major order
-    r0[i] = *reinterpret_cast<const float4*>(rt + g0 * C * 4);
-    r1[i] = *reinterpret_cast<const float4*>(rt + kst + g1 * C * 4);
-    r2[i] = *reinterpret_cast<const float4*>(rt + 2 * kst + (L4 - 1 - g0) * C * 4);
-    r3[i] = *reinterpret_cast<const float4*>(rt + 3 * kst + (L4 - 1 - g1) * C * 4);
+    r0[i] = load4_nt(rt + g0 * C * 4);
+    r1[i] = load4_nt(rt + kst + g1 * C * 4);
+    r2[i] = load4_nt(rt + 2 * kst + (L4 - 1 - g0) * C * 4);
+    r3[i] = load4_nt(rt + 3 * kst + (L4 - 1 - g1) * C * 4);
   }
   const int64_t plane = (b * C + c) * L;
   float4 xv[4], zv[4];
