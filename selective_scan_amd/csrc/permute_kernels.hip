@@ -347,11 +347,15 @@ __global__ __launch_bounds__(kThreads) void merge_plane_kernel(MergeArgs a) {
 // 8 consecutive channels (lane % 8: one 128-byte line per group and route) x 8 consecutive blocks
 // of the plane (row-major block order).  Same sum, in the same order, as merge_plane_kernel.
 // kVecIO: x, z, y and merged are aligned for 4-element accesses (else element by element).
-// 16 bytes read once (whole lines across the wavefront), not kept in the caches
+// 16 bytes read once, or written for a later kernel (whole lines across the wavefront), not kept
+// in the caches
+typedef float F4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float4 load4_nt(const float* p) {
-  typedef float F4 __attribute__((ext_vector_type(4)));
   const F4 v = __builtin_nontemporal_load(reinterpret_cast<const F4*>(p));
   return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store4_nt(float* p, float4 v) {
+  __builtin_nontemporal_store(F4{v.x, v.y, v.z, v.w}, reinterpret_cast<F4*>(p));
 }
 
 template <typename T, bool kSkip, bool kZ, bool kXF32, bool kVecIO>
@@ -510,7 +514,7 @@ __global__ __launch_bounds__(kThreads) void merge_gate_bwd_plane_kernel(MergeGat
     for (int e = 0; e < kMergeBatch; ++e) {
       const int p = p0 + kStep * e, pc = p < L ? p : 0;
       if constexpr (kM) {
-        v0[e] = *reinterpret_cast<const float4*>(mg + pc);
+        v0[e] = load4_nt(mg + pc);  // the kept map: read once
         v2[e] = make_float4(0.f, 0.f, 0.f, 0.f);
       } else {
         v0[e] = *reinterpret_cast<const float4*>(r0 + pc);
@@ -545,7 +549,7 @@ __global__ __launch_bounds__(kThreads) void merge_gate_bwd_plane_kernel(MergeGat
         tm[h * ldr + w] = dm[j];
         if (++w == Wd) { w = 0; ++h; }
       }
-      *reinterpret_cast<float4*>(dmg + p) = make_float4(dm[0], dm[1], dm[2], dm[3]);
+      store4_nt(dmg + p, make_float4(dm[0], dm[1], dm[2], dm[3]));
       Elem<T>::store4(dzg, p, make_float4(dz[0], dz[1], dz[2], dz[3]));
     }
   }
@@ -559,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void merge_gate_bwd_plane_kernel(MergeGat
       v[j] = tm[h * ldr + w];
       if (++h == H) { h = 0; ++w; }
     }
-    *reinterpret_cast<float4*>(dmt + t) = make_float4(v[0], v[1], v[2], v[3]);
+    store4_nt(dmt + t, make_float4(v[0], v[1], v[2], v[3]));
   }
 }
 

@@ -55,8 +55,10 @@ __global__ __launch_bounds__(256) void reduce_bc_blocked_kernel(const BwdReduceA
   if (i * 4 >= per_block) return;
   float4 sb = make_float4(0.0f, 0.0f, 0.0f, 0.0f), sc = sb;
   for (int64_t k = 0; k < a.dblocks; ++k) {
-    const float4 vb = *reinterpret_cast<const float4*>(a.dB_part + k * per_block + 4 * i);
-    const float4 vc = *reinterpret_cast<const float4*>(a.dC_part + k * per_block + 4 * i);
+    // read once: past the caches
+    typedef float F4 __attribute__((ext_vector_type(4)));
+    const F4 vb = __builtin_nontemporal_load(reinterpret_cast<const F4*>(a.dB_part + k * per_block + 4 * i));
+    const F4 vc = __builtin_nontemporal_load(reinterpret_cast<const F4*>(a.dC_part + k * per_block + 4 * i));
     sb.x += vb.x; sb.y += vb.y; sb.z += vb.z; sb.w += vb.w;
     sc.x += vc.x; sc.y += vc.y; sc.z += vc.z; sc.w += vc.w;
   }
