@@ -98,6 +98,8 @@ SS2D_BWD_CASES = [
     (1, 8, 4, 10, 32, "f32", True),     # blocked du and dB / dC partials, 32 states (4-step sub-intervals)
     (1, 4, 8, 7, 64, "bf16", True),     # 64 states: 2-step sub-intervals, du stored element by element
     (2, 8, 8, 40, 8, "bf16", False),    # one lane per channel, 40 of 64 lanes active
+    (1, 16, 8, 40, 16, "bf16", True),   # dΔ rows of whole lines (L = 128): two 64-step windows, a partial channel block
+    (1, 64, 64, 40, 16, "bf16", True),  # the same, few rows: chunked, windows cut at the chunk ends
 ]
 
 
@@ -119,7 +121,8 @@ def test_ss2d_bwd(case):
                                   (1, 3, 40, 64, 8, "bf16", True), (1, 64, 64, 64, 16, "f32", True),
                                   (2, 14, 14, 70, 16, "f32", False), (2, 12, 8, 13, 16, "bf16", True),
                                   (1, 8, 12, 9, 16, "f32", False), (1, 8, 4, 10, 32, "f32", True),
-                                  (2, 8, 8, 40, 8, "bf16", False)], ids=str)
+                                  (2, 8, 8, 40, 8, "bf16", False), (1, 16, 8, 40, 16, "bf16", True),
+                                  (1, 64, 64, 40, 16, "bf16", True)], ids=str)
 def test_ss2d_bwd_reuses_forward_states(case):
     """A training forward (keep_states) then the backward on its workspace: the oracle's gradients,
     and bit for bit what the backward that recomputes the forward gives."""
