@@ -43,8 +43,12 @@ hipError_t launch_transpose(const void* x, void* xT, int64_t batch, int64_t C, i
 // scan wavefront's store of one 4-step group then covers whole 128-byte lines (its channels are
 // consecutive) instead of a 16-byte piece of each channel's row.  Used when H and W are
 // multiples of 4 (ss2d_routes_blocked), so that the merge can read whole 4 x 4 pixel blocks.
+// Small planes whose sides are not multiples of 4 (L a multiple of 4, at most 2048 pixels) use the
+// same layout; their merge gathers 8 channels' planes in LDS instead.
 inline bool ss2d_routes_blocked(int64_t H, int64_t W) {
-  return H > 0 && W > 0 && H % 4 == 0 && W % 4 == 0 && H * W < (int64_t(1) << 31);
+  if (H <= 0 || W <= 0) return false;
+  if (H % 4 == 0 && W % 4 == 0) return H * W < (int64_t(1) << 31);
+  return (H * W) % 4 == 0 && H * W <= 2048;
 }
 
 struct MergeArgs {

@@ -451,6 +451,62 @@ __global__ __launch_bounds__(64) void merge_blocked_kernel(MergeArgs a, int cblo
   }
 }
 
+// The same merge for small planes whose H or W is not a multiple of 4 (L a multiple of 4, at
+// most kSmallBlockedL pixels): one workgroup per (image, 8 consecutive channels).  Each route's
+// 4-step groups of the 8 channels (one whole line per group) are added into an LDS copy of the 8
+// planes at the pixels of their steps, route by route, so each pixel's sum is ((y0 + y1) + y2) + y3
+// as in the other merges; then every pixel of the 8 planes gets its skip term and gate and is
+// written in grid order.
+constexpr int64_t kSmallBlockedL = 2048;  // 8 planes of fp32 in 64 KB of LDS
+template <typename T, bool kSkip, bool kZ, bool kXF32>
+__global__ __launch_bounds__(256) void merge_blocked_small_kernel(MergeArgs a, int cblocks) {
+  extern __shared__ __align__(16) float acc[];  // [8][L]
+  const int tid = int(threadIdx.x);
+  const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int cb = int(bid % cblocks);
+  const int64_t b = bid / cblocks;
+  const int64_t C = a.C;
+  const int H = int(a.H), Wd = int(a.W), L = H * Wd, G = L / 4;
+  const float* rt = static_cast<const float*>(a.routes) + b * 4 * int64_t(G) * C * 4;
+#pragma unroll 1
+  for (int k = 0; k < 4; ++k) {
+    for (int idx = tid; idx < G * 8; idx += 256) {
+      const int g = idx >> 3, c8 = idx & 7;
+      const int64_t c = int64_t(cb) * 8 + c8;
+      if (c >= C) continue;
+      const float4 v = load4_nt(rt + ((int64_t(k) * G + g) * C + c) * 4);
+      const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int st = 4 * g + q;
+        if (k >= 2) st = L - 1 - st;                    // routes 2, 3 run backwards
+        const int pix = (k & 1) ? (st % H) * Wd + st / H : st;  // column-major step -> pixel
+        float* dst = acc + c8 * L + pix;
+        *dst = (k == 0) ? e[q] : *dst + e[q];
+      }
+    }
+    __syncthreads();
+  }
+  const T* xg = static_cast<const T*>(a.x);
+  const float* xf = static_cast<const float*>(a.x);
+  const T* zg = static_cast<const T*>(a.z);
+  T* yg = static_cast<T*>(a.y);
+  for (int idx = tid; idx < 8 * L; idx += 256) {
+    const int c8 = idx / L, pix = idx - c8 * L;
+    const int64_t c = int64_t(cb) * 8 + c8;
+    if (c >= C) continue;
+    const int64_t o = (b * C + c) * L + pix;
+    float v = acc[idx];
+    if constexpr (kSkip) {
+      const float dsum = ((a.Dskip[c] + a.Dskip[C + c]) + a.Dskip[2 * C + c]) + a.Dskip[3 * C + c];
+      v = fmaf(dsum, kXF32 ? xf[o] : Elem<T>::load(xg, o), v);
+    }
+    if (a.merged_f32) a.merged_f32[o] = v;
+    if constexpr (kZ) v *= silu(Elem<T>::load(zg, o));
+    if (yg) Elem<T>::store(yg, o, v);
+  }
+}
+
 // The gate backward fused with its merge (see MergeGateArgs), one plane per workgroup.  LDS:
 // routes 1 and 3 transposed to [w][h] (as in the merge), and dM as [h][w] for the dMT write.  As
 // in the merge, the skip term and an fp32 x are template parameters and the loads of up to
@@ -695,10 +751,43 @@ void launch_merge_blocked_t(const MergeArgs& a, dim3 g, int cblocks, int jchunks
     z ? launch_merge_blocked_v<T, false, true, false>(a, g, cblocks, jchunks, vec_io, s)
       : launch_merge_blocked_v<T, false, false, false>(a, g, cblocks, jchunks, vec_io, s);
 }
+
+template <typename T, bool kSkip, bool kZ, bool kXF32>
+void launch_merge_small_v(const MergeArgs& a, dim3 g, int cblocks, size_t lds, hipStream_t s) {
+  merge_blocked_small_kernel<T, kSkip, kZ, kXF32><<<g, dim3(256), lds, s>>>(a, cblocks);
+}
+template <typename T>
+void launch_merge_small_t(const MergeArgs& a, dim3 g, int cblocks, size_t lds, hipStream_t s) {
+  const bool skip = a.Dskip != nullptr && a.x != nullptr, z = a.z != nullptr;
+  if (skip && a.x_f32)
+    z ? launch_merge_small_v<T, true, true, true>(a, g, cblocks, lds, s)
+      : launch_merge_small_v<T, true, false, true>(a, g, cblocks, lds, s);
+  else if (skip)
+    z ? launch_merge_small_v<T, true, true, false>(a, g, cblocks, lds, s)
+      : launch_merge_small_v<T, true, false, false>(a, g, cblocks, lds, s);
+  else
+    z ? launch_merge_small_v<T, false, true, false>(a, g, cblocks, lds, s)
+      : launch_merge_small_v<T, false, false, false>(a, g, cblocks, lds, s);
+}
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   const int64_t L = a.H * a.W;
+  if (a.routes_blocked && !(a.H % 4 == 0 && a.W % 4 == 0)) {
+    // fp32 routes in 4-step blocks on a small plane whose sides are not multiples of 4
+    if (!a.routes_f32 || !ss2d_routes_blocked(a.H, a.W) || L > kSmallBlockedL || !aligned16(a.routes))
+      return hipErrorInvalidValue;
+    const int64_t cblocks = cdiv(a.C, 8), blocks = a.batch * cblocks;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    const size_t lds = size_t(8) * size_t(L) * 4;
+    const dim3 g{uint32_t(blocks)};
+    if (a.dtype == 0)
+      launch_merge_small_t<float>(a, g, int(cblocks), lds, s);
+    else
+      launch_merge_small_t<bf16>(a, g, int(cblocks), lds, s);
+    return hipGetLastError();
+  }
   if (a.routes_blocked) {
     // fp32 routes in 4-step blocks (written by the route scans when H and W are multiples of 4)
     if (!a.routes_f32 || !ss2d_routes_blocked(a.H, a.W) || !aligned16(a.routes)) return hipErrorInvalidValue;
