@@ -63,27 +63,37 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// log2(1 + 2^w) for any finite w, without overflow and without losing the low digits of
-// 1 + 2^-|w|: with e = 2^-|w| and s = fl(1 + e), log2(1 + e) = log2(s) + (e - (s - 1)) / (s ln 2)
-// to first order; (e - (s - 1)) is the exact rounding error of s.  Dropping the 1/s factor
-// changes the result by less than 1e-7 absolute for every e in (0, 1].
-// softplus(v) = ln 2 * log2(1 + 2^(v log2 e)).
+// log2(1 + 2^w) for any w (softplus(v) = ln 2 * log2(1 + 2^(v log2 e))), evaluated as
+// max(w, 0) + log2(1 + e) with e = 2^-|w| in (0, 1]: no overflow; -inf gives exactly 0 (the
+// padded steps).  Forming s = fl(1 + e) drops the digits of e below half an ulp of 1, an
+// absolute error of up to 2^-24 log2(e) < 9e-8 in the result: relative 6e-5 at delta = 1e-3.
+// kExact adds that rounding error back to first order, log2(1 + e) = log2(s) + (e - (s - 1)) /
+// (s ln 2) with (e - (s - 1)) exact, the 1/s factor dropped (< 1e-7 absolute for every e): three
+// more VALU operations, used for fp32 inputs.  bf16 inputs carry a relative error of 2^-9 in
+// delta already, so their kernels use the plain form.
+template <bool kExact = true>
 __device__ __forceinline__ float softplus_log2(float w) {
   const float m = fmaxf(w, 0.0f);
   const float e = fast_exp2(-fabsf(w));
   const float s = 1.0f + e;
+  if constexpr (!kExact) return m + fast_log2(s);
   const float corr = e - (s - 1.0f);
   return m + fast_log2(s) + corr * kLog2e;
 }
 
-// softplus_log2(w) and, from the same e = 2^-|w| and s = 1 + e, the sigmoid of the softplus
-// argument v = w ln 2 (its derivative): 1 / (1 + e^-v) = (w >= 0 ? 1 : e) / s.
+// softplus_log2<kExact>(w) and, from the same e = 2^-|w| and s = 1 + e, the sigmoid of the
+// softplus argument v = w ln 2 (its derivative): 1 / (1 + e^-v) = (w >= 0 ? 1 : e) / s.
+template <bool kExact = true>
 __device__ __forceinline__ void softplus_sigmoid_log2(float w, float& lam, float& sg) {
   const float m = fmaxf(w, 0.0f);
   const float e = fast_exp2(-fabsf(w));
   const float s = 1.0f + e;
-  const float corr = e - (s - 1.0f);
-  lam = m + fast_log2(s) + corr * kLog2e;
+  if constexpr (kExact) {
+    const float corr = e - (s - 1.0f);
+    lam = m + fast_log2(s) + corr * kLog2e;
+  } else {
+    lam = m + fast_log2(s);
+  }
   sg = (w >= 0.0f ? 1.0f : e) * fast_rcp(s);
 }
 

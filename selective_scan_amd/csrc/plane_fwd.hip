@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kPT) void plane_fwd_kernel(const PlaneFwdArgs a) {
           // steps past the row (clamped loads of real data) feed only lanes after the row's
           // end, whose results are never stored nor carried into another segment
           const float w = fmaf(dv[i], kLog2e, bias_l2);
-          const float l = kSoftplus ? softplus_log2(w) : w;
+          const float l = kSoftplus ? softplus_log2<sizeof(T) == 4>(w) : w;
           lam[i] = l;
           const float du = l * uv[i];
 #pragma unroll

@@ -343,7 +343,7 @@ void scan_bwd_kernel(const ScanBwdParams p) {
       float lam[kSub], sg[kSub], dup[kSub], dy[kSub];
       auto lam_sg = [&](float v, float& l, float& g) {
         if (p.softplus) {
-          softplus_sigmoid_log2(v * kLog2e, l, g);
+          softplus_sigmoid_log2<sizeof(T) == 4>(v * kLog2e, l, g);
         } else {
           l = v * kLog2e;
           g = 1.0f;

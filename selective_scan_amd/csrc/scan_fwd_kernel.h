@@ -208,7 +208,7 @@ void scan_fwd_kernel(const ScanFwdParams p) {
       // Lam of step i (0 past the end of the range)
       auto step_lam = [&](float d, int i) {
         const float w = fmaf(d, kLog2e, bias_l2);
-        if (kSoftplus) return softplus_log2(w);
+        if (kSoftplus) return softplus_log2<sizeof(T) == 4>(w);
         return (i < nt) ? w : 0.0f;
       };
       if (kSplit == 2) {

@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256) void scan_step_kernel(const StepParams p) {
   const bool has_n = valid && n < p.N;
   const float x = Elem<T>::load(static_cast<const T*>(p.x), r);
   const float w = (Elem<T>::load(static_cast<const T*>(p.delta), r) + (p.delta_bias ? p.delta_bias[d] : 0.0f)) * kLog2e;
-  const float lam = p.softplus ? softplus_log2(w) : w;  // delta / ln 2
+  const float lam = p.softplus ? softplus_log2<sizeof(T) == 4>(w) : w;  // delta / ln 2
   float part = 0.0f;
   if (has_n) {
     const int64_t si = r * p.N + n;
